@@ -1,0 +1,249 @@
+"""ctypes wrapper around the fp64 C oracle (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU
+baseline may import this module.  It does not import the HIP library or
+its binding, and the HIP library does not import it.
+
+Inputs are numpy arrays in the oracle's dense layouts (see pic_oracle.c):
+f32 storage as float32, bf16 storage as uint16 bit patterns, and the
+oracle-only f64 storage as float64.  Workload descriptions are read by
+attribute (dtype, n_layers, n_heads, row_dim, rope_offset, rope_dim, style,
+theta, inv_freq, has_v, pool_tokens, chunks, requests, page_size, capacity,
+n_phys_pages, n_tokens, segments) so any object with those fields works.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "liboracle.so")
+
+DTYPES = {"f32": 0, "bf16": 1, "f64": 2}
+NUMPY_STORAGE = {"f32": np.float32, "bf16": np.uint16, "f64": np.float64}
+STYLES = {"half": 0, "interleaved": 1}
+STATUS = {0: "ok", 1: "bad_arg", 2: "range", 3: "overlap"}
+
+_i32p = C.POINTER(C.c_int32)
+_i64p = C.POINTER(C.c_int64)
+_f64p = C.POINTER(C.c_double)
+
+
+class _StitchProblem(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
+                ("row_dim", C.c_int32), ("rope_offset", C.c_int32), ("rope_dim", C.c_int32),
+                ("style", C.c_int32), ("has_v", C.c_int32), ("theta", C.c_double),
+                ("inv_freq", _f64p), ("pool_tokens", C.c_int64), ("n_chunks", C.c_int32),
+                ("chunk_start", _i64p), ("chunk_base", _i64p), ("chunk_len", _i32p),
+                ("n_requests", C.c_int32), ("req_entries", _i32p), ("ent_chunk", _i32p),
+                ("ent_dst", _i64p), ("ent_len", _i32p), ("ent_k", _i32p),
+                ("page_size", C.c_int32), ("capacity", C.c_int64),
+                ("n_phys_pages", C.c_int64), ("req_pages", _i32p), ("page_table", _i32p)]
+
+
+class _InplaceProblem(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
+                ("row_dim", C.c_int32), ("rope_offset", C.c_int32), ("rope_dim", C.c_int32),
+                ("style", C.c_int32), ("pad_", C.c_int32), ("theta", C.c_double),
+                ("inv_freq", _f64p), ("n_tokens", C.c_int64), ("n_segments", C.c_int32),
+                ("pad2_", C.c_int32), ("seg_start", _i64p), ("seg_delta", _i64p),
+                ("seg_len", _i32p), ("seg_k", _i32p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            from . import build as _build
+            _build.build()
+        lib = C.CDLL(LIBRARY)
+        lib.orc_stitch.restype = C.c_int
+        lib.orc_stitch.argtypes = [C.POINTER(_StitchProblem), C.c_void_p, C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_int, C.c_int]
+        lib.orc_validate_stitch.restype = C.c_int
+        lib.orc_validate_stitch.argtypes = [C.POINTER(_StitchProblem), C.c_int, C.c_int]
+        lib.orc_rotate_inplace.restype = C.c_int
+        lib.orc_rotate_inplace.argtypes = [C.POINTER(_InplaceProblem), C.c_void_p, C.c_int,
+                                           C.c_int]
+        lib.orc_validate_inplace.restype = C.c_int
+        lib.orc_validate_inplace.argtypes = [C.POINTER(_InplaceProblem), C.c_int, C.c_int]
+        lib.orc_round_bf16.restype = C.c_uint16
+        lib.orc_round_bf16.argtypes = [C.c_double]
+        lib.orc_round_bf16_array.restype = None
+        lib.orc_round_bf16_array.argtypes = [_f64p, C.POINTER(C.c_uint16), C.c_int64]
+        lib.orc_inv_freq.restype = C.c_double
+        lib.orc_inv_freq.argtypes = [C.c_double, C.c_int, C.c_int]
+        _lib = lib
+    return _lib
+
+
+def _ptr(a, ctype):
+    return a.ctypes.data_as(C.POINTER(ctype)) if a is not None else None
+
+
+def _stitch_problem(wl, dtype=None):
+    """Build the C problem struct; returns (struct, keep-alive arrays)."""
+    dt = dtype or wl.dtype
+    keep = []
+
+    def arr(values, npdt):
+        a = np.ascontiguousarray(np.asarray(values, dtype=npdt))
+        if a.size == 0:
+            a = np.zeros(1, dtype=npdt)
+        keep.append(a)
+        return a
+
+    chunk_start = arr([c.token_start for c in wl.chunks], np.int64)
+    chunk_base = arr([c.base_pos for c in wl.chunks], np.int64)
+    chunk_len = arr([c.length for c in wl.chunks], np.int32)
+    req_entries = arr([len(r.entries) for r in wl.requests], np.int32)
+    ents = [e for r in wl.requests for e in r.entries]
+    ent_chunk = arr([e.chunk_id for e in ents], np.int32)
+    ent_dst = arr([e.dst_offset for e in ents], np.int64)
+    ent_len = arr([e.length for e in ents], np.int32)
+    ent_k = arr([e.recompute_k for e in ents], np.int32)
+    paged = wl.page_size > 0
+    req_pages = arr([len(r.page_table) if paged else 0 for r in wl.requests], np.int32)
+    page_table = arr(np.concatenate([np.asarray(r.page_table, dtype=np.int32)
+                                     for r in wl.requests]) if paged and wl.requests else [],
+                     np.int32)
+    inv = arr(wl.inv_freq, np.float64) if getattr(wl, "inv_freq", None) is not None else None
+    p = _StitchProblem(DTYPES[dt], wl.n_layers, wl.n_heads, wl.row_dim, wl.rope_offset,
+                       wl.rope_dim, STYLES[wl.style], int(bool(wl.has_v)), float(wl.theta),
+                       _ptr(inv, C.c_double), wl.pool_tokens, len(wl.chunks),
+                       _ptr(chunk_start, C.c_int64), _ptr(chunk_base, C.c_int64),
+                       _ptr(chunk_len, C.c_int32), len(wl.requests),
+                       _ptr(req_entries, C.c_int32), _ptr(ent_chunk, C.c_int32),
+                       _ptr(ent_dst, C.c_int64), _ptr(ent_len, C.c_int32),
+                       _ptr(ent_k, C.c_int32), wl.page_size, wl.capacity, wl.n_phys_pages,
+                       _ptr(req_pages, C.c_int32), _ptr(page_table, C.c_int32))
+    return p, keep
+
+
+def _inplace_problem(wl, dtype=None):
+    dt = dtype or wl.dtype
+    keep = []
+
+    def arr(values, npdt):
+        a = np.ascontiguousarray(np.asarray(values, dtype=npdt))
+        if a.size == 0:
+            a = np.zeros(1, dtype=npdt)
+        keep.append(a)
+        return a
+
+    seg_start = arr([s.token_start for s in wl.segments], np.int64)
+    seg_delta = arr([s.delta for s in wl.segments], np.int64)
+    seg_len = arr([s.length for s in wl.segments], np.int32)
+    seg_k = arr([s.recompute_k for s in wl.segments], np.int32)
+    inv = arr(wl.inv_freq, np.float64) if getattr(wl, "inv_freq", None) is not None else None
+    p = _InplaceProblem(DTYPES[dt], wl.n_layers, wl.n_heads, wl.row_dim, wl.rope_offset,
+                        wl.rope_dim, STYLES[wl.style], 0, float(wl.theta),
+                        _ptr(inv, C.c_double), wl.n_tokens, len(wl.segments), 0,
+                        _ptr(seg_start, C.c_int64), _ptr(seg_delta, C.c_int64),
+                        _ptr(seg_len, C.c_int32), _ptr(seg_k, C.c_int32))
+    return p, keep
+
+
+def _check_array(a, dt, shape, name):
+    if a is None:
+        return
+    if a.dtype != NUMPY_STORAGE[dt] or not a.flags.c_contiguous:
+        raise TypeError(f"{name}: expected C-contiguous {NUMPY_STORAGE[dt].__name__}")
+    if tuple(a.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {a.shape}, expected {shape}")
+
+
+def validate_stitch(wl, layer_begin=0, layer_end=None) -> str:
+    """The oracle's verdict on a copy-mode problem: 'ok', 'bad_arg', 'range'
+    or 'overlap'."""
+    p, keep = _stitch_problem(wl)
+    le = wl.n_layers if layer_end is None else layer_end
+    return STATUS[_load().orc_validate_stitch(C.byref(p), layer_begin, le)]
+
+
+def validate_inplace(wl, layer_begin=0, layer_end=None) -> str:
+    p, keep = _inplace_problem(wl)
+    le = wl.n_layers if layer_end is None else layer_end
+    return STATUS[_load().orc_validate_inplace(C.byref(p), layer_begin, le)]
+
+
+def stitch(wl, pool_k, pool_v, dst_k, dst_v, layer_begin=0, layer_end=None, dtype=None,
+           layer_base=0) -> str:
+    """Stitch layers [layer_begin, layer_end) into dst_k / dst_v (modified in
+    place).  The arrays hold layers [layer_base, layer_base + n) of the
+    workload, so a caller can pass one layer at a time.  Returns the
+    oracle's status string; nothing is written unless it is 'ok'."""
+    dt = dtype or wl.dtype
+    le = wl.n_layers if layer_end is None else layer_end
+    n = pool_k.shape[0]
+    if not (layer_base <= layer_begin <= le <= layer_base + n):
+        raise ValueError("layer range outside the arrays given")
+    sub = _Layers(wl, n)
+    p, keep = _stitch_problem(sub, dt)
+    _check_array(pool_k, dt, (n, wl.pool_tokens, wl.n_heads, wl.row_dim), "pool_k")
+    dshape = ((n, wl.n_phys_pages, wl.page_size, wl.n_heads, wl.row_dim) if wl.page_size
+              else (n, len(wl.requests), wl.capacity, wl.n_heads, wl.row_dim))
+    _check_array(dst_k, dt, dshape, "dst_k")
+    if wl.has_v:
+        _check_array(pool_v, dt, pool_k.shape, "pool_v")
+        _check_array(dst_v, dt, dshape, "dst_v")
+    st = _load().orc_stitch(C.byref(p), pool_k.ctypes.data,
+                            pool_v.ctypes.data if wl.has_v else None, dst_k.ctypes.data,
+                            dst_v.ctypes.data if wl.has_v else None,
+                            layer_begin - layer_base, le - layer_base)
+    return STATUS[st]
+
+
+def rotate_inplace(wl, buf_k, layer_begin=0, layer_end=None, dtype=None, layer_base=0) -> str:
+    """Rotate, in place, the segments of buf_k (layers [layer_base, ...))."""
+    dt = dtype or wl.dtype
+    le = wl.n_layers if layer_end is None else layer_end
+    n = buf_k.shape[0]
+    if not (layer_base <= layer_begin <= le <= layer_base + n):
+        raise ValueError("layer range outside the array given")
+    p, keep = _inplace_problem(_Layers(wl, n), dt)
+    _check_array(buf_k, dt, (n, wl.n_tokens, wl.n_heads, wl.row_dim), "buf_k")
+    st = _load().orc_rotate_inplace(C.byref(p), buf_k.ctypes.data, layer_begin - layer_base,
+                                    le - layer_base)
+    return STATUS[st]
+
+
+def round_bf16(x) -> np.ndarray:
+    """bf16 bit patterns of fp64 values, one round-to-nearest-even each."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_round_bf16_array(_ptr(x, C.c_double), _ptr(out, C.c_uint16), x.size)
+    return out
+
+
+def inv_freq(theta: float, rope_dim: int) -> np.ndarray:
+    """The oracle's plane frequencies theta_i = theta^(-2i/rope_dim)."""
+    lib = _load()
+    return np.array([lib.orc_inv_freq(theta, rope_dim, i) for i in range(rope_dim // 2)])
+
+
+def recompute_ranges(wl):
+    """[(request, begin, end)] positions left for the recompute pass: the first
+    recompute_k tokens of every entry (empty ranges omitted)."""
+    out = []
+    for r, req in enumerate(wl.requests):
+        for e in req.entries:
+            if e.recompute_k > 0:
+                out.append((r, e.dst_offset, e.dst_offset + e.recompute_k))
+    return out
+
+
+class _Layers:
+    """View of a workload whose arrays hold only `n` layers."""
+
+    def __init__(self, wl, n):
+        self._wl = wl
+        self.n_layers = n
+
+    def __getattr__(self, name):
+        return getattr(self._wl, name)

@@ -1,0 +1,300 @@
+"""Seeded synthetic inputs for position-independent KV stitching.
+
+This module only builds inputs: chunk pools, per-request placement tables,
+page tables, in-place segments and the random key/value contents.  It holds
+none of the stitching arithmetic (no rotation, no shift, no address
+translation), so both the HIP library and the oracle can be fed from it.
+
+Structure (lengths, orders, offsets, page permutations, shifts) is drawn
+with ``numpy.random.default_rng(seed)``; values are N(0, 1) drawn with
+torch's generator (on the CPU or the device) and rounded to the storage
+type by torch.
+
+The five named workloads follow the shapes of the pages' workloads:
+multi-document RAG with re-ordered documents after a system prompt (EPIC
+Guide, "Prefix Caching Failure in Real-World RAG" and the benchmark section),
+agentic shifted chunks on an MLA model (Irminsul, Technical Summary sections
+2.1, 2.2 and 4) and 128k-token composed prompts (EPIC Guide,
+needle-in-a-haystack up to 128k).  No benchmark data is used.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import List, Optional
+
+import numpy as np
+
+DTYPE_BYTES = {"f32": 4, "bf16": 2}
+
+# Destination fill before a stitch: quiet-NaN patterns with a payload, so an
+# untouched row is recognisable bit for bit.
+SENTINEL_BITS = {"f32": 0x7FC5A5A5, "bf16": 0x7FC5}
+
+
+@dataclass(frozen=True)
+class Chunk:
+    token_start: int  # first token of the chunk in the pool
+    length: int
+    base_pos: int = 0  # position its keys were cached at (virtual offset 0)
+
+
+@dataclass(frozen=True)
+class Entry:
+    chunk_id: int
+    dst_offset: int  # logical position of the chunk's first token
+    length: int
+    recompute_k: int = 0
+
+
+@dataclass
+class Request:
+    entries: List[Entry]
+    page_table: Optional[np.ndarray] = None  # int32 physical page per logical page
+
+
+@dataclass(frozen=True)
+class Segment:
+    token_start: int
+    length: int
+    delta: int
+    recompute_k: int = 0
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str  # "f32" | "bf16"
+    n_layers: int
+    n_heads: int
+    row_dim: int
+    rope_offset: int
+    rope_dim: int
+    style: str  # "half" | "interleaved"
+    theta: float
+    has_v: bool
+    pool_tokens: int = 0
+    chunks: List[Chunk] = field(default_factory=list)
+    requests: List[Request] = field(default_factory=list)
+    page_size: int = 0  # 0 = contiguous destination
+    capacity: int = 0  # contiguous: positions per request
+    n_phys_pages: int = 0
+    inplace: bool = False
+    n_tokens: int = 0  # in-place buffer length
+    segments: List[Segment] = field(default_factory=list)
+    inv_freq: Optional[np.ndarray] = None
+
+    @property
+    def esize(self) -> int:
+        return DTYPE_BYTES[self.dtype]
+
+    @property
+    def row_elems(self) -> int:
+        return self.n_heads * self.row_dim
+
+    def pool_shape(self):
+        return (self.n_layers, self.pool_tokens, self.n_heads, self.row_dim)
+
+    def dst_shape(self):
+        if self.page_size:
+            return (self.n_layers, self.n_phys_pages, self.page_size, self.n_heads, self.row_dim)
+        return (self.n_layers, len(self.requests), self.capacity, self.n_heads, self.row_dim)
+
+    def buf_shape(self):
+        return (self.n_layers, self.n_tokens, self.n_heads, self.row_dim)
+
+    def with_layers(self, n_layers: int) -> "Workload":
+        return replace(self, n_layers=n_layers)
+
+
+# ---------------------------------------------------------------- workloads
+
+def config1() -> Workload:
+    """One layer, 8 KV heads x 128, fp32, three chunks of 512/1024/256 tokens
+    cached at offset 0, stitched at 64, 576 and 1600 behind a 64-token
+    prefix, nothing recomputed, contiguous destination."""
+    lens = [512, 1024, 256]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    chunks = [Chunk(int(s), int(n)) for s, n in zip(starts, lens)]
+    entries = [Entry(0, 64, 512), Entry(1, 576, 1024), Entry(2, 1600, 256)]
+    return Workload("single-layer fp32 3-chunk", "f32", 1, 8, 128, 0, 128, "half", 500000.0,
+                    True, pool_tokens=int(sum(lens)), chunks=chunks,
+                    requests=[Request(entries)], capacity=1856)
+
+
+def config2(seed: int = 0, n_layers: int = 32) -> Workload:
+    """Llama-3-8B-shaped cache: 32 layers, 8 KV heads x 128, bf16; one request
+    of 8 chunks x 2048 tokens in a seeded random order behind a 128-token
+    prefix; paged destination (16-token pages, physical pages a random
+    permutation); the first 32 tokens of every chunk left for recompute."""
+    rng = np.random.default_rng(seed)
+    n, length, prefix, ps = 8, 2048, 128, 16
+    chunks = [Chunk(i * length, length) for i in range(n)]
+    order = rng.permutation(n)
+    entries = [Entry(int(c), prefix + j * length, length, 32) for j, c in enumerate(order)]
+    n_pages = (prefix + n * length) // ps
+    table = rng.permutation(n_pages).astype(np.int32)
+    return Workload("llama3-8b paged 8x2048", "bf16", n_layers, 8, 128, 0, 128, "half",
+                    500000.0, True, pool_tokens=n * length, chunks=chunks,
+                    requests=[Request(entries, table)], page_size=ps, n_phys_pages=n_pages)
+
+
+def config3(seed: int = 0, n_layers: int = 32, n_requests: int = 64,
+            n_chunks: int = 256) -> Workload:
+    """Batched RAG: a pool of 256 chunks of 128..4096 tokens, bf16, 32 layers,
+    8 KV heads x 128; 64 requests stitching 4..16 pool chunks each, drawn with
+    replacement in random order, behind prefixes of 32..512 tokens; paged
+    destination (16-token pages from one global random permutation)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(128, 4096, size=n_chunks, endpoint=True)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    chunks = [Chunk(int(s), int(n)) for s, n in zip(starts, lens)]
+    ps = 16
+    reqs_entries, reqs_pages = [], []
+    for _ in range(n_requests):
+        k = int(rng.integers(4, 16, endpoint=True))
+        ids = rng.integers(0, n_chunks, size=k)
+        pos = int(rng.integers(32, 512, endpoint=True))
+        entries = []
+        for c in ids:
+            entries.append(Entry(int(c), pos, int(lens[c]), 0))
+            pos += int(lens[c])
+        reqs_entries.append(entries)
+        reqs_pages.append(-(-pos // ps))
+    total_pages = int(sum(reqs_pages))
+    perm = rng.permutation(total_pages).astype(np.int32)
+    requests, at = [], 0
+    for entries, npg in zip(reqs_entries, reqs_pages):
+        requests.append(Request(entries, perm[at:at + npg].copy()))
+        at += npg
+    return Workload("batched RAG paged", "bf16", n_layers, 8, 128, 0, 128, "half", 500000.0,
+                    True, pool_tokens=int(lens.sum()), chunks=chunks, requests=requests,
+                    page_size=ps, n_phys_pages=total_pages)
+
+
+def config4(seed: int = 0, n_layers: int = 61) -> Workload:
+    """MLA (DeepSeek-V3 shape): 61 layers, one 576-wide latent row per token
+    (512 content dims copied, 64 rotary dims rotated, theta 1e4), bf16;
+    16 chunks x 4096 tokens in random order at random offsets (the first at
+    position 0 with its first 32 tokens left for recompute, the others
+    separated by gaps of 0..512 inline tokens); contiguous destination."""
+    rng = np.random.default_rng(seed)
+    n, length = 16, 4096
+    chunks = [Chunk(i * length, length) for i in range(n)]
+    order = rng.permutation(n)
+    gaps = rng.integers(0, 512, size=n - 1, endpoint=True)
+    entries, pos = [], 0
+    for j, c in enumerate(order):
+        entries.append(Entry(int(c), pos, length, 32 if j == 0 else 0))
+        pos += length + (int(gaps[j]) if j < n - 1 else 0)
+    return Workload("deepseek-v3 MLA 16x4096", "bf16", n_layers, 1, 576, 512, 64, "half",
+                    10000.0, False, pool_tokens=n * length, chunks=chunks,
+                    requests=[Request(entries)], capacity=pos)
+
+
+def config5(seed: int = 0, n_layers: int = 36) -> Workload:
+    """Long-context in-place mode, Qwen3-8B shape: 36 layers, 8 KV heads x 128,
+    theta 1e6, bf16; 64 chunks x 2048 tokens forming one 131072-token
+    prompt, keys rotated in place by per-chunk shifts drawn from
+    [-65536, 65536]; the first 16 tokens of each chunk left alone."""
+    rng = np.random.default_rng(seed)
+    n, length = 64, 2048
+    deltas = rng.integers(-65536, 65536, size=n, endpoint=True)
+    segs = [Segment(i * length, length, int(d), 16) for i, d in enumerate(deltas)]
+    return Workload("qwen3-8b in-place 131072", "bf16", n_layers, 8, 128, 0, 128, "half",
+                    1000000.0, False, inplace=True, n_tokens=n * length, segments=segs)
+
+
+CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def random_small(seed: int, dtype: str = "bf16", style: str = "half", paged: bool = False,
+                 mla: bool = False, n_requests: int = 2, n_layers: int = 2,
+                 max_len: int = 150, deltas=None) -> Workload:
+    """A small random stitch problem with ragged chunk lengths, gaps, shared
+    and partial chunks, several requests and varied recompute_k."""
+    rng = np.random.default_rng(seed)
+    if mla:
+        heads, row, roff, rdim, has_v, theta = 1, 576, 512, 64, False, 10000.0
+    else:
+        heads, row, roff, rdim, has_v, theta = 2, 128, 0, 128, True, 500000.0
+    n_chunks = int(rng.integers(2, 6))
+    lens = rng.integers(1, max_len, size=n_chunks, endpoint=True)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    bases = rng.integers(0, 3, size=n_chunks) * rng.integers(0, 50, size=n_chunks)
+    chunks = [Chunk(int(s), int(n), int(b)) for s, n, b in zip(starts, lens, bases)]
+    ps = int(rng.choice([4, 16])) if paged else 0
+    reqs_entries, spans = [], []
+    for _ in range(n_requests):
+        k = int(rng.integers(1, 5))
+        pos = int(rng.integers(0, 40))
+        entries = []
+        for _ in range(k):
+            c = int(rng.integers(0, n_chunks))
+            ln = int(rng.integers(1, lens[c], endpoint=True))
+            rk = int(rng.choice([0, 0, 1, ln, int(rng.integers(0, ln + 1))]))
+            if deltas is not None:
+                # a chunk record of its own, cached where this shift is wanted
+                d = int(rng.choice(deltas))
+                chunks.append(Chunk(chunks[c].token_start, chunks[c].length, pos - d))
+                c = len(chunks) - 1
+            entries.append(Entry(c, pos, ln, rk))
+            pos += ln + int(rng.integers(0, 9))
+        reqs_entries.append(entries)
+        spans.append(pos + int(rng.integers(0, 5)))
+    if paged:
+        pages = [-(-s // ps) for s in spans]
+        total = int(sum(pages)) + int(rng.integers(0, 4))
+        perm = rng.permutation(total).astype(np.int32)
+        requests, at = [], 0
+        for entries, npg in zip(reqs_entries, pages):
+            requests.append(Request(entries, perm[at:at + npg].copy()))
+            at += npg
+        return Workload(f"random{seed}", dtype, n_layers, heads, row, roff, rdim, style, theta,
+                        has_v, pool_tokens=int(lens.sum()), chunks=chunks, requests=requests,
+                        page_size=ps, n_phys_pages=total)
+    return Workload(f"random{seed}", dtype, n_layers, heads, row, roff, rdim, style, theta,
+                    has_v, pool_tokens=int(lens.sum()), chunks=chunks,
+                    requests=[Request(e) for e in reqs_entries], capacity=int(max(spans)))
+
+
+# ------------------------------------------------------------------- values
+
+def _torch():
+    import torch
+    return torch
+
+
+def storage_torch_dtype(dtype: str):
+    torch = _torch()
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def normal_values(shape, dtype: str, seed: int, device="cpu"):
+    """N(0, 1) values of `shape` rounded to the storage type (a torch tensor),
+    drawn one leading slice at a time so large tensors need no fp32 copy."""
+    torch = _torch()
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = torch.empty(shape, dtype=storage_torch_dtype(dtype), device=device)
+    for i in range(shape[0]):
+        out[i].copy_(torch.randn(shape[1:], generator=gen, device=device, dtype=torch.float32))
+    return out
+
+
+def pool_values(wl: Workload, seed: int = 0, device="cpu"):
+    """(pool_k, pool_v) for a copy-mode workload; pool_v is None without V."""
+    k = normal_values(wl.pool_shape(), wl.dtype, seed, device)
+    v = normal_values(wl.pool_shape(), wl.dtype, seed + 1, device) if wl.has_v else None
+    return k, v
+
+
+def sentinel_like(shape, dtype: str, device="cpu"):
+    """A destination tensor filled with the sentinel bit pattern."""
+    torch = _torch()
+    if dtype == "f32":
+        bits = torch.full(shape, SENTINEL_BITS["f32"] - (1 << 32), dtype=torch.int32,
+                          device=device) if SENTINEL_BITS["f32"] >= (1 << 31) else \
+            torch.full(shape, SENTINEL_BITS["f32"], dtype=torch.int32, device=device)
+        return bits.view(torch.float32)
+    bits = torch.full(shape, SENTINEL_BITS["bf16"], dtype=torch.int16, device=device)
+    return bits.view(torch.bfloat16)

@@ -1,0 +1,578 @@
+"""Pins of the fp64 oracle to what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+printed on the pages (tests/golden), closed forms of plane rotations, the
+group law and orthogonality of RoPE, an independent library (numpy complex
+arithmetic, torch's bf16 conversion), brute-force enumeration, and
+brute-force attention on tiny inputs.  A dropped term, a wrong sign, a
+swapped pair member or a wrong frequency index fails at least one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from pic_workloads import Chunk, Entry, Request, Segment, Workload, random_small
+
+SENT_F64 = np.float64(-12345.5)
+
+
+def gqa(rope_dim=8, n_heads=2, style="half", theta=10000.0, row_dim=None, rope_offset=0,
+        has_v=True, n_layers=1, inv=None):
+    return Workload("pin", "f64", n_layers, n_heads, row_dim or rope_dim, rope_offset,
+                    rope_dim, style, theta, has_v, inv_freq=inv)
+
+
+def place(wl, pool_k, pool_v, chunks, entries, capacity, dtype="f64", page_size=0,
+          page_table=None, n_phys=0, fill=None):
+    """Stitch one request with the oracle; returns (status, dst_k, dst_v)."""
+    wl.chunks = chunks
+    wl.pool_tokens = pool_k.shape[1]
+    wl.requests = [Request(entries, page_table)]
+    wl.capacity = capacity
+    wl.page_size = page_size
+    wl.n_phys_pages = n_phys
+    shape = wl.dst_shape() if page_size else (wl.n_layers, 1, capacity, wl.n_heads, wl.row_dim)
+    npdt = oracle.ref.NUMPY_STORAGE[dtype]
+    f = SENT_F64 if fill is None else fill
+    dk = np.full(shape, f, dtype=npdt)
+    dv = np.full(shape, f, dtype=npdt) if wl.has_v else None
+    st = oracle.stitch(wl, pool_k, pool_v, dk, dv, dtype=dtype)
+    return st, dk, dv
+
+
+def rope_at(raw, positions, wl):
+    """Keys of `raw` [1][T][H][D] rotated to the given absolute positions, one
+    in-place segment of length 1 per token (the oracle's own rotation)."""
+    buf = raw.copy()
+    w = Workload("seg", "f64", 1, wl.n_heads, wl.row_dim, wl.rope_offset, wl.rope_dim,
+                 wl.style, wl.theta, False, inplace=True, n_tokens=raw.shape[1],
+                 inv_freq=wl.inv_freq,
+                 segments=[Segment(t, 1, int(p), 0) for t, p in enumerate(positions)])
+    assert oracle.rotate_inplace(w, buf, dtype="f64") == "ok"
+    return buf
+
+
+def pair_index(style, rope_dim, i):
+    """The two members of plane i, as the pages pair coordinates: interleaved
+    (2i, 2i+1) as written in the RoPE section; half (i, i + d/2) as in
+    rotate-half implementations."""
+    return (2 * i, 2 * i + 1) if style == "interleaved" else (i, i + rope_dim // 2)
+
+
+# --------------------------------------------------------------- rounding
+
+def test_bf16_rounding_matches_torch_on_float_values():
+    """For doubles that are exact binary32 values, one RNE to bf16 must equal
+    torch's float32 -> bfloat16 conversion (an independent library)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(200000).astype(np.float32),
+                        (rng.standard_normal(20000) * 1e-39).astype(np.float32),
+                        (rng.standard_normal(20000) * 1e37).astype(np.float32)])
+    # exact ties: bf16 value plus half a bf16 quantum
+    base = (rng.integers(0, 0x7F00, 5000).astype(np.uint32) << 16)
+    ties = (base | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, -ties])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_rounding_brute_force_on_doubles():
+    """Doubles between bf16 neighbours round to the nearer one, ties to the even
+    pattern: checked against an enumeration of every finite positive bf16."""
+    pats = np.arange(0, 0x7F80, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32).astype(np.float64)
+    rng = np.random.default_rng(2)
+    idx = rng.integers(1, len(vals) - 1, 30000)
+    lo, hi = vals[idx], vals[idx + 1]
+    frac = rng.random(30000)
+    frac[:300] = 0.5  # exact midpoints in double
+    x = lo + (hi - lo) * frac
+    got = oracle.round_bf16(x)
+    d_lo, d_hi = x - lo, hi - x
+    want = np.where(d_lo < d_hi, idx, np.where(d_hi < d_lo, idx + 1,
+                                               np.where(idx % 2 == 0, idx, idx + 1)))
+    assert np.array_equal(got, want.astype(np.uint16))
+    # sign symmetry and specials
+    assert np.array_equal(oracle.round_bf16(-x), got | 0x8000)
+    assert oracle.round_bf16([0.0])[0] == 0 and oracle.round_bf16([-0.0])[0] == 0x8000
+    assert oracle.round_bf16([3.5e38])[0] == 0x7F80  # beyond bf16 range
+    assert oracle.round_bf16([2.0 ** -134])[0] == 0  # half the subnormal quantum: tie to 0
+    assert oracle.round_bf16([1.5 * 2.0 ** -133])[0] == 2  # tie to even
+
+
+# ------------------------------------------------------------- frequencies
+
+def test_plane_frequencies_page_values(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "rope_frequencies.json")))
+    for case in g["cases"]:
+        got = oracle.inv_freq(case["base"], case["d"])
+        assert np.allclose(got, case["theta"], rtol=1e-15, atol=0)
+    # theta_0 = b^0 = 1 exactly, for any base
+    for b in (10000.0, 500000.0, 1e6):
+        assert oracle.inv_freq(b, 128)[0] == 1.0
+
+
+def test_caller_table_equals_formula():
+    """Giving theta_i as a table reproduces the formula bit for bit."""
+    rng = np.random.default_rng(3)
+    wl = gqa(rope_dim=16, theta=500000.0)
+    pool = rng.standard_normal((1, 5, 2, 16))
+    chunks = [Chunk(0, 5)]
+    a = place(wl, pool, pool.copy(), chunks, [Entry(0, 9, 5)], 20)[1]
+    wl2 = gqa(rope_dim=16, theta=500000.0, inv=oracle.inv_freq(500000.0, 16))
+    b = place(wl2, pool, pool.copy(), chunks, [Entry(0, 9, 5)], 20)[1]
+    assert np.array_equal(a, b)
+
+
+# ----------------------------------------------------------- plane rotation
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_quarter_and_half_turns(style):
+    """With theta_i = pi/2 a shift of 1 is a quarter turn: by the page's matrix
+    [[cos, -sin], [sin, cos]] the pair (x, y) becomes (-y, x); with pi it
+    becomes (-x, -y)."""
+    D = 8
+    inv = np.array([math.pi / 2, math.pi, math.pi / 2, math.pi])
+    wl = gqa(rope_dim=D, n_heads=1, style=style, inv=inv)
+    rng = np.random.default_rng(4)
+    pool = rng.standard_normal((1, 3, 1, D))
+    st, dk, _ = place(wl, pool, pool.copy(), [Chunk(0, 3)], [Entry(0, 1, 3)], 4)
+    assert st == "ok"
+    out = dk[0, 0, 1:4, 0]
+    for i in range(D // 2):
+        a, b = pair_index(style, D, i)
+        x, y = pool[0, :, 0, a], pool[0, :, 0, b]
+        if inv[i] == math.pi / 2:
+            want_a, want_b = -y, x
+        else:
+            want_a, want_b = -x, -y
+        assert np.allclose(out[:, a], want_a, atol=1e-15)
+        assert np.allclose(out[:, b], want_b, atol=1e-15)
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_rotation_is_complex_multiplication(style):
+    """Each plane rotated by phi equals (x + iy) * exp(i phi) in numpy complex
+    arithmetic, with phi = delta * theta_i and theta_i = 10^-i (b = 1e4, d = 8)."""
+    D, H = 8, 3
+    wl = gqa(rope_dim=D, n_heads=H, style=style)
+    rng = np.random.default_rng(5)
+    pool = rng.standard_normal((1, 6, H, D))
+    theta = np.array([1.0, 0.1, 0.01, 0.001])
+    for delta in (1, -1, 7, 123456, -65536):
+        st, dk, _ = place(wl, pool, pool.copy(), [Chunk(0, 6, 70000)],
+                          [Entry(0, 70000 + delta, 6)], 70000 + delta + 6)
+        assert st == "ok"
+        out = dk[0, 0, 70000 + delta:70000 + delta + 6]
+        for i in range(D // 2):
+            a, b = pair_index(style, D, i)
+            z = (pool[0, :, :, a] + 1j * pool[0, :, :, b]) * np.exp(1j * delta * theta[i])
+            tol = 1e-15 * (1 + abs(delta * theta[i]))
+            assert np.allclose(out[:, :, a], z.real, atol=tol, rtol=0)
+            assert np.allclose(out[:, :, b], z.imag, atol=tol, rtol=0)
+
+
+def test_pair_zero_turns_by_delta_radians():
+    """theta_0 = 1, so plane 0 turns by exactly delta radians (libm cos/sin)."""
+    wl = gqa(rope_dim=128, n_heads=1, theta=500000.0)
+    e = np.zeros((1, 1, 1, 128))
+    e[0, 0, 0, 0] = 1.0  # unit vector on the first member of plane 0
+    for delta in (1, 3, 1000, 65536):
+        st, dk, _ = place(wl, e, e.copy(), [Chunk(0, 1)], [Entry(0, delta, 1)], delta + 1)
+        assert st == "ok"
+        row = dk[0, 0, delta, 0]
+        assert row[0] == pytest.approx(math.cos(delta), abs=1e-15)
+        assert row[64] == pytest.approx(math.sin(delta), abs=1e-15)
+        assert np.all(row[np.r_[1:64, 65:128]] == 0.0)
+
+
+# --------------------------------------------------------------- group law
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_group_law_and_inverse(style):
+    """R(d) R(p) = R(p + d); R(-d) R(d) = I; R(0) = I exactly; plane norms kept."""
+    D, H = 16, 2
+    wl = gqa(rope_dim=D, n_heads=H, style=style, theta=1e6)
+    rng = np.random.default_rng(6)
+    raw = rng.standard_normal((1, 4, H, D))
+    for p, d in [(5, 9), (1000, -999), (65536, 65536), (3, -3), (70000, -65536)]:
+        at_p = rope_at(raw, [p] * 4, wl)
+        # a chunk cached at p, placed at p + d
+        st, moved, _ = place(wl, at_p, at_p.copy(), [Chunk(0, 4, p)], [Entry(0, p + d, 4)],
+                             p + d + 4)
+        assert st == "ok"
+        direct = rope_at(raw, [p + d] * 4, wl)
+        scale = 1e-12 * (1 + abs(p + d))
+        assert np.allclose(moved[0, 0, p + d:p + d + 4], direct[0], atol=scale, rtol=0)
+        # inverse
+        st, back, _ = place(wl, moved[:, 0, p + d:p + d + 4].copy(),
+                            moved[:, 0, p + d:p + d + 4].copy(), [Chunk(0, 4, p + d)],
+                            [Entry(0, p, 4)], p + 4)
+        assert np.allclose(back[0, 0, p:p + 4], at_p[0], atol=scale, rtol=0)
+        # norms of every plane preserved
+        for i in range(D // 2):
+            a, b = pair_index(style, D, i)
+            n0 = np.hypot(at_p[0, :, :, a], at_p[0, :, :, b])
+            n1 = np.hypot(moved[0, 0, p + d:p + d + 4, :, a], moved[0, 0, p + d:p + d + 4, :, b])
+            assert np.allclose(n0, n1, atol=1e-13, rtol=0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_shift_is_bit_exact(dtype):
+    """A chunk placed where it was cached is copied bit for bit, signed zeros
+    and all (R(0) is the identity)."""
+    import torch
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((2, 9, 2, 128)).astype(np.float32)
+    x[0, 0, 0, :8] = -0.0
+    x[0, 0, 0, 64:72] = np.array([-1, 2, -3, 4, -0.0, 0.0, 5, -6], dtype=np.float32)
+    if dtype == "bf16":
+        pk = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        fill = np.uint16(0x7FC5)
+    else:
+        pk = x
+        fill = np.float32(7.0)
+    wl = Workload("z", dtype, 2, 2, 128, 0, 128, "half", 5e5, True)
+    st, dk, dv = place(wl, pk, pk.copy(), [Chunk(0, 9, 40)], [Entry(0, 40, 9)], 60, dtype=dtype,
+                       fill=fill)
+    assert st == "ok"
+    assert np.array_equal(dk[:, 0, 40:49].view(np.uint8), pk.view(np.uint8))
+    assert np.array_equal(dv[:, 0, 40:49].view(np.uint8), pk.view(np.uint8))
+
+
+# ------------------------------------------------ attention-level invariance
+
+def test_relative_position_invariance_of_scores():
+    """q.k after RoPE depends only on the distance n - m: shifting both by the
+    same delta leaves every score unchanged (EPIC Guide, RoPE barrier)."""
+    D = 32
+    wl = gqa(rope_dim=D, n_heads=1, theta=500000.0)
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((1, 6, 1, D))
+    k = rng.standard_normal((1, 6, 1, D))
+    m = np.array([0, 3, 10, 100, 4000, 70000])
+    n = np.array([5, 1, 10, 2000, 0, 65536])
+    base = np.einsum("td,td->t", rope_at(q, m, wl)[0, :, 0], rope_at(k, n, wl)[0, :, 0])
+    for delta in (1, 777, 65536):
+        shifted = np.einsum("td,td->t", rope_at(q, m + delta, wl)[0, :, 0],
+                            rope_at(k, n + delta, wl)[0, :, 0])
+        assert np.allclose(shifted, base, atol=1e-10, rtol=0)
+    # and the score does change when only one side moves (position matters)
+    moved = np.einsum("td,td->t", rope_at(q, m, wl)[0, :, 0], rope_at(k, n + 1, wl)[0, :, 0])
+    assert np.max(np.abs(moved - base)) > 1e-3
+
+
+def _attention(q, k, v):
+    """softmax(q k^T / sqrt(d)) v per head; q [Tq][H][D], k/v [Tk][H][D]."""
+    s = np.einsum("qhd,khd->hqk", q, k) / math.sqrt(q.shape[-1])
+    s -= s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=-1, keepdims=True)
+    return np.einsum("hqk,khd->qhd", p, v)
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_brute_force_attention_on_stitched_cache(style):
+    """Chunks of 3, 5 and 4 tokens, each prefilled alone at positions 0..L-1,
+    stitched after a 2-token prefix: attention of later queries over the
+    stitched cache equals attention over keys RoPE'd directly at their
+    absolute positions; reusing the cached keys without the shift does not."""
+    H, D = 2, 8
+    wl = gqa(rope_dim=D, n_heads=H, style=style, theta=10000.0)
+    rng = np.random.default_rng(9)
+    lens, prefix = [3, 5, 4], 2
+    raw_k = rng.standard_normal((1, sum(lens), H, D))
+    vals = rng.standard_normal((1, sum(lens), H, D))
+    local = np.concatenate([np.arange(n) for n in lens])  # positions at caching time
+    cached = rope_at(raw_k, local, wl)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    chunks = [Chunk(int(s), n) for s, n in zip(starts, lens)]
+    order = [2, 0, 1]
+    entries, pos = [], prefix
+    for c in order:
+        entries.append(Entry(c, pos, lens[c]))
+        pos += lens[c]
+    total = pos
+    st, dk, dv = place(wl, cached, vals, chunks, entries, total)
+    assert st == "ok"
+    # ground truth: the same raw keys RoPE'd at their absolute positions
+    src = np.concatenate([np.arange(starts[c], starts[c] + lens[c]) for c in order])
+    absolute = np.arange(prefix, total)
+    truth_k = rope_at(raw_k[:, src], absolute, wl)[0]
+    truth_v = vals[0, src]
+    qraw = rng.standard_normal((1, 4, H, D))
+    q = rope_at(qraw, [total + i for i in range(4)], wl)[0]
+    got = _attention(q, dk[0, 0, prefix:], dv[0, 0, prefix:])
+    want = _attention(q, truth_k, truth_v)
+    assert np.allclose(got, want, atol=1e-12, rtol=0)
+    naive = _attention(q, cached[0, src], truth_v)
+    assert np.max(np.abs(naive - want)) > 1e-3
+
+
+# ----------------------------------------------- placement, copy and masking
+
+@pytest.mark.parametrize("seed", range(12))
+def test_placement_copy_mask_brute_force(seed):
+    """Every destination row is, by brute force over (request, entry, token):
+    the source row (V and non-rotary K bits unchanged, the rotary slice equal
+    to the complex-multiplication rotation), or untouched when masked or not
+    covered.  Random ragged problems, contiguous and paged, GQA and MLA rows."""
+    paged = seed % 2 == 1
+    mla = seed % 3 == 2
+    style = "interleaved" if seed % 4 == 3 else "half"
+    wl = random_small(seed, dtype="f32", style=style, paged=paged, mla=mla, n_requests=3,
+                      n_layers=2)
+    wl.dtype = "f64"
+    rng = np.random.default_rng(100 + seed)
+    pk = rng.standard_normal(wl.pool_shape())
+    pv = rng.standard_normal(wl.pool_shape()) if wl.has_v else None
+    dk = np.full(wl.dst_shape(), SENT_F64)
+    dv = np.full(wl.dst_shape(), SENT_F64) if wl.has_v else None
+    assert oracle.stitch(wl, pk, pv, dk, dv) == "ok"
+
+    theta = oracle.inv_freq(wl.theta, wl.rope_dim)
+    rot = np.arange(wl.rope_offset, wl.rope_offset + wl.rope_dim)
+    plain = np.setdiff1d(np.arange(wl.row_dim), rot)
+    written = np.zeros(wl.dst_shape()[:-2], dtype=bool)
+    for r, req in enumerate(wl.requests):
+        for e in req.entries:
+            ch = wl.chunks[e.chunk_id]
+            delta = e.dst_offset - ch.base_pos
+            for t in range(e.recompute_k, e.length):
+                pos = e.dst_offset + t
+                if paged:
+                    at = (slice(None), int(req.page_table[pos // wl.page_size]),
+                          pos % wl.page_size)
+                else:
+                    at = (slice(None), r, pos)
+                got_k, src_k = dk[at], pk[:, ch.token_start + t]
+                written[at] = True
+                assert np.array_equal(got_k[..., plain], src_k[..., plain])
+                if wl.has_v:
+                    assert np.array_equal(dv[at], pv[:, ch.token_start + t])
+                for i in range(wl.rope_dim // 2):
+                    a, b = pair_index(style, wl.rope_dim, i)
+                    a, b = a + wl.rope_offset, b + wl.rope_offset
+                    z = (src_k[..., a] + 1j * src_k[..., b]) * np.exp(1j * delta * theta[i])
+                    tol = 1e-14 * (1 + abs(delta))
+                    assert np.allclose(got_k[..., a], z.real, atol=tol, rtol=0)
+                    assert np.allclose(got_k[..., b], z.imag, atol=tol, rtol=0)
+    assert np.all(dk[~written] == SENT_F64)
+    if wl.has_v:
+        assert np.all(dv[~written] == SENT_F64)
+
+
+# ------------------------------------------------------ the pages' examples
+
+def test_epic_block_composition(golden_dir):
+    """Blocks A(128), B(8192), C(1024) cached at offset 0 and composed as
+    A + B + C: the page's offsets are the prefix sums of the lengths, and the
+    keys of every stitched block equal the keys RoPE'd at the absolute
+    position (checked on a 1-head 8-dim row)."""
+    g = json.load(open(os.path.join(golden_dir, "epic_block_composition.json")))
+    blocks = g["blocks"]
+    lens = [b["length"] for b in blocks]
+    assert [b["offset"] for b in blocks] == [0] + list(np.cumsum(lens)[:-1])
+    wl = gqa(rope_dim=8, n_heads=1, theta=500000.0)
+    rng = np.random.default_rng(10)
+    raw = rng.standard_normal((1, sum(lens), 1, 8))
+    local = np.concatenate([np.arange(n) for n in lens])
+    cached = rope_at(raw, local, wl)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    chunks = [Chunk(int(s), n) for s, n in zip(starts, lens)]
+    entries = [Entry(i, b["offset"], b["length"]) for i, b in enumerate(blocks)]
+    total = sum(lens)
+    st, dk, _ = place(wl, cached, cached.copy(), chunks, entries, total)
+    assert st == "ok"
+    truth = rope_at(raw, np.arange(total), wl)  # composed order == pool order here
+    assert np.allclose(dk[0, 0], truth[0], atol=1e-12 * total, rtol=0)
+    # block C's first token sits at 8320 and was turned by 8320 * theta_i
+    assert entries[2].dst_offset == 8320
+
+
+def test_epic_doc_d_placement(golden_dir):
+    """Document D (10,000 tokens) cached at 0 and reused behind prompt A lands
+    on [100, 10100); the whole chunk is shifted by 100."""
+    g = json.load(open(os.path.join(golden_dir, "epic_doc_d.json")))
+    n, first, end = g["length"], g["first"], g["end"]
+    assert end - first == n
+    wl = gqa(rope_dim=4, n_heads=1, theta=10000.0)
+    rng = np.random.default_rng(11)
+    raw = rng.standard_normal((1, n, 1, 4))
+    cached = rope_at(raw, np.arange(n), wl)
+    st, dk, dv = place(wl, cached, raw.copy(), [Chunk(0, n)], [Entry(0, first, n)], end + 7)
+    assert st == "ok"
+    assert np.all(dk[0, 0, :first] == SENT_F64) and np.all(dk[0, 0, end:] == SENT_F64)
+    truth = rope_at(raw, np.arange(first, end), wl)
+    assert np.allclose(dk[0, 0, first:end], truth[0], atol=1e-12 * end, rtol=0)
+    assert np.array_equal(dv[0, 0, first:end], raw[0])
+
+
+def test_epic_chunk_references(golden_dir):
+    """Two client chunk references at offsets 128 and 4224: placed adjacent,
+    the first spans 4096 tokens; overlapping them by one token is refused."""
+    g = json.load(open(os.path.join(golden_dir, "epic_chunk_references.json")))
+    o1, o2 = [r["offset"] for r in g["references"]]
+    n1 = o2 - o1
+    assert n1 == 4096
+    wl = gqa(rope_dim=4, n_heads=1)
+    pool = np.random.default_rng(12).standard_normal((1, n1 + 64, 1, 4))
+    chunks = [Chunk(0, n1), Chunk(n1, 64)]
+    st, dk, _ = place(wl, pool, pool.copy(), chunks, [Entry(0, o1, n1), Entry(1, o2, 64)],
+                      o2 + 64)
+    assert st == "ok"
+    st, _, _ = place(wl, pool, pool.copy(), chunks, [Entry(0, o1, n1), Entry(1, o2 - 1, 64)],
+                     o2 + 64)
+    assert st == "overlap"
+
+
+def test_mla_rotary_slice_only(golden_dir):
+    """In the MLA row (512 content dims + 64 rotary dims) only the rotary slice
+    moves; the content latent is reused verbatim."""
+    g = json.load(open(os.path.join(golden_dir, "mla_row.json")))
+    ckv, kr = g["cKV"], g["k_r"]
+    assert ckv / (ckv + kr) == pytest.approx(g["content_share_approx"], abs=0.005)
+    wl = Workload("mla", "f64", 1, 1, ckv + kr, ckv, kr, "half", 10000.0, False)
+    rng = np.random.default_rng(13)
+    pool = rng.standard_normal((1, 10, 1, ckv + kr))
+    st, dk, _ = place(wl, pool, None, [Chunk(0, 10)], [Entry(0, 300, 10)], 310)
+    assert st == "ok"
+    out = dk[0, 0, 300:310, 0]
+    assert np.array_equal(out[:, :ckv], pool[0, :, 0, :ckv])
+    assert not np.allclose(out[:, ckv:], pool[0, :, 0, ckv:])
+    theta = 10000.0 ** (-2.0 * np.arange(kr // 2) / kr)
+    z = (pool[0, :, 0, ckv:ckv + kr // 2] + 1j * pool[0, :, 0, ckv + kr // 2:]) * \
+        np.exp(1j * 300 * theta)
+    assert np.allclose(out[:, ckv:ckv + kr // 2], z.real, atol=1e-13)
+    assert np.allclose(out[:, ckv + kr // 2:], z.imag, atol=1e-13)
+
+
+def test_bf16_error_below_irminsul_bound(golden_dir):
+    """The oracle's bf16 result (one rounding of the exact rotation) has a
+    relative L2 error far below the 4.7e-3 the Irminsul page reports."""
+    import torch
+    bound = json.load(open(os.path.join(golden_dir, "irminsul_bf16_error.json")))["rel_l2_bf16"]
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((1, 2000, 1, 64)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    xbits = xb.view(torch.int16).numpy().view(np.uint16)
+    xf64 = xb.to(torch.float64).numpy()
+    wl_b = Workload("e", "bf16", 1, 1, 64, 0, 64, "half", 10000.0, False)
+    wl_f = Workload("e", "f64", 1, 1, 64, 0, 64, "half", 10000.0, False)
+    _, kb, _ = place(wl_b, xbits, None, [Chunk(0, 2000)], [Entry(0, 5000, 2000)], 7000,
+                     dtype="bf16", fill=np.uint16(0))
+    _, kf, _ = place(wl_f, xf64, None, [Chunk(0, 2000)], [Entry(0, 5000, 2000)], 7000)
+    got = torch.from_numpy(kb[0, 0, 5000:].view(np.int16)).view(torch.bfloat16).double().numpy()
+    exact = kf[0, 0, 5000:]
+    rel = np.linalg.norm(got - exact) / np.linalg.norm(exact)
+    assert rel < bound / 2
+    assert rel > 1e-4  # bf16 storage does round
+
+
+# ------------------------------------------------------------- in-place mode
+
+def test_inplace_matches_copy_mode_and_leaves_the_rest():
+    """Rotating segments in place equals placing them by copy at a position
+    delta away from their cached one; tokens [0, k), other dims and other
+    tokens stay untouched."""
+    rng = np.random.default_rng(15)
+    D, H, T = 16, 2, 40
+    buf = rng.standard_normal((2, T, H, D + 8))
+    segs = [Segment(0, 10, 5, 3), Segment(10, 12, -70000, 0), Segment(25, 15, 0, 2),
+            Segment(22, 3, 1, 3)]
+    wl = Workload("ip", "f64", 2, H, D + 8, 8, D, "half", 1e6, False, inplace=True,
+                  n_tokens=T, segments=segs)
+    out = buf.copy()
+    assert oracle.rotate_inplace(wl, out) == "ok"
+    for s in segs:
+        sl = slice(s.token_start, s.token_start + s.recompute_k)
+        assert np.array_equal(out[:, sl], buf[:, sl])
+        ts = slice(s.token_start + s.recompute_k, s.token_start + s.length)
+        assert np.array_equal(out[:, ts, :, :8], buf[:, ts, :, :8])
+        cw = Workload("cp", "f64", 2, H, D + 8, 8, D, "half", 1e6, False)
+        n = s.length - s.recompute_k
+        if n == 0:
+            continue
+        src = buf[:, ts].copy()
+        st, dk, _ = place(cw, src, None, [Chunk(0, n, 80000)], [Entry(0, 80000 + s.delta, n)],
+                          80000 + s.delta + n)
+        assert st == "ok"
+        assert np.array_equal(out[:, ts], dk[:, 0, 80000 + s.delta:])
+
+
+# ------------------------------------------------------------- validation
+
+def _valid_problem():
+    wl = random_small(3, dtype="f32", paged=True, n_requests=2)
+    assert oracle.validate_stitch(wl) == "ok"
+    return wl
+
+
+@pytest.mark.parametrize("mutate,expect", [
+    (lambda w: setattr(w, "rope_dim", 7), "bad_arg"),
+    (lambda w: setattr(w, "rope_offset", w.row_dim - w.rope_dim + 1), "bad_arg"),
+    (lambda w: setattr(w, "n_heads", 0), "bad_arg"),
+    (lambda w: setattr(w, "theta", 0.0), "bad_arg"),
+    (lambda w: w.chunks.__setitem__(0, Chunk(w.pool_tokens - 1, 5)), "range"),
+    (lambda w: w.requests[0].entries.__setitem__(0, Entry(99, 0, 1)), "range"),
+    (lambda w: w.requests[0].entries.__setitem__(
+        0, Entry(w.requests[0].entries[0].chunk_id, w.requests[0].entries[0].dst_offset,
+                 w.requests[0].entries[0].length, w.requests[0].entries[0].length + 1)),
+     "range"),
+    (lambda w: w.requests[0].page_table.__setitem__(0, w.n_phys_pages), "range"),
+])
+def test_validation_single_defects(mutate, expect):
+    wl = _valid_problem()
+    wl.chunks = list(wl.chunks)
+    wl.requests[0].entries = list(wl.requests[0].entries)
+    e0 = wl.requests[0].entries[0]
+    # make sure the mutated page is one the first entry writes
+    if e0.recompute_k >= e0.length:
+        wl.requests[0].entries[0] = Entry(e0.chunk_id, e0.dst_offset, e0.length, 0)
+        e0 = wl.requests[0].entries[0]
+    first_page = (e0.dst_offset + e0.recompute_k) // wl.page_size
+    pt = wl.requests[0].page_table
+    pt[[0, first_page]] = pt[[first_page, 0]]
+    assert oracle.validate_stitch(wl) == "ok"
+    mutate(wl)
+    assert oracle.validate_stitch(wl) == expect
+
+
+def test_validation_overlaps_and_no_write_on_error():
+    wl = Workload("ov", "f32", 1, 1, 8, 0, 8, "half", 1e4, True, pool_tokens=20,
+                  chunks=[Chunk(0, 10), Chunk(10, 10)], capacity=40,
+                  requests=[Request([Entry(0, 0, 10), Entry(1, 9, 10)])])
+    assert oracle.validate_stitch(wl) == "overlap"
+    pk = np.ones((1, 20, 1, 8), np.float32)
+    dk = np.zeros((1, 1, 40, 1, 8), np.float32)
+    dv = np.zeros_like(dk)
+    assert oracle.stitch(wl, pk, pk.copy(), dk, dv) == "overlap"
+    assert not dk.any() and not dv.any()
+    # two requests writing the same physical row of a paged pool
+    wl2 = Workload("ov2", "f32", 1, 1, 8, 0, 8, "half", 1e4, True, pool_tokens=20,
+                   chunks=[Chunk(0, 10)], page_size=4, n_phys_pages=6,
+                   requests=[Request([Entry(0, 0, 4)], np.array([5], np.int32)),
+                             Request([Entry(0, 2, 2)], np.array([5], np.int32))])
+    assert oracle.validate_stitch(wl2) == "overlap"
+    # ... but disjoint rows of one shared page are fine, and masked rows do not count
+    wl2.requests[1] = Request([Entry(0, 0, 4, 4)], np.array([5], np.int32))
+    assert oracle.validate_stitch(wl2) == "ok"
+    # duplicate chunk ids and negative shifts are allowed
+    wl3 = Workload("dup", "f32", 1, 1, 8, 0, 8, "half", 1e4, True, pool_tokens=20,
+                   chunks=[Chunk(0, 10, 500)], capacity=40,
+                   requests=[Request([Entry(0, 0, 10), Entry(0, 20, 10)])])
+    assert oracle.validate_stitch(wl3) == "ok"
+    # layer range
+    assert oracle.validate_stitch(wl3, 0, 2) == "bad_arg"
+    # in-place segments overlapping
+    ip = Workload("ip", "f32", 1, 1, 8, 0, 8, "half", 1e4, False, inplace=True, n_tokens=10,
+                  segments=[Segment(0, 5, 1), Segment(4, 3, 1)])
+    assert oracle.validate_inplace(ip) == "overlap"
+    ip.segments = [Segment(0, 5, 1), Segment(5, 6, 1)]
+    assert oracle.validate_inplace(ip) == "range"
