@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Throughput of position-independent KV stitching on one MI355X.
+
+One step = one pic_stitch over the whole Llama-3-8B-shaped workload: 32
+layers, 8 KV heads x 128 dims, bf16, one request of 8 chunks x 2048 tokens
+placed in a seeded random order behind a 128-token prefix into a paged cache
+of 16-token pages, the first 32 tokens of every chunk left for recompute.
+Inputs are synthetic (N(0, 1), seed 0) and resident in HBM before timing.
+
+The value is algorithmic stitched-KV bytes (rows read + rows written) per
+second; token-layers/s and the fraction of the 8 TB/s HBM peak are reported
+beside it, with the roofline of the stitch kernel (its average launch
+duration from HIP events on the launch stream), a device-to-device copy of
+the same byte count as the practical ceiling, and the fp64 CPU oracle timed
+on the host cores over one step of the same workload.
+
+Prints one JSON line on stdout.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "stitched-KV HBM GB/s (read+write) and token-layers/s; % of HBM peak"
+PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc", "stitch.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "stitch_kernel_llama3-8b-paged_counters.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(COUNTERS):
+        return None
+    text = open(COUNTERS).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return int(t.group(1))
+
+
+def cpu_baseline(wl, pk, pv, plan_info):
+    """The oracle, as it is, over one full step of the workload: one call per
+    layer on a pool of host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle
+    from parity_util import to_host
+    from pic_workloads import sentinel_like
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    log(f"cpu baseline: copying pool to host, {cores} threads")
+    hk, hv = to_host(pk), to_host(pv)
+    sent = to_host(sentinel_like((1,) + tuple(wl.dst_shape()[1:]), wl.dtype, "cpu"))
+
+    def one(layer):
+        dk, dv = sent.copy(), sent.copy()
+        st = oracle.stitch(wl, hk[layer:layer + 1], hv[layer:layer + 1], dk, dv, layer,
+                           layer + 1, layer_base=layer)
+        assert st == "ok"
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=cores) as ex:
+        list(ex.map(one, range(wl.n_layers)))
+    dt = time.perf_counter() - t0
+    step_bytes = (plan_info["bytes_read_per_layer"] + plan_info["bytes_written_per_layer"]) * \
+        wl.n_layers
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"one full step ({wl.n_layers} layers x {plan_info['tokens_written']} "
+                      f"stitched tokens), one fp64 oracle call per layer, {dt:.2f} s wall",
+            "token_layers_per_s": round(plan_info["tokens_written"] * wl.n_layers / dt, 1)}
+
+
+def copy_ceiling(torch, nbytes, reps=20):
+    """A device-to-device copy moving the same read+write bytes."""
+    n = nbytes // 2
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return {"value": round(2 * n / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "kind": "torch copy_ (device to device)", "bytes_moved": 2 * n}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures the single-GPU path only (asked for --gpus {args.gpus}); the "
+              "stitch has no cross-GPU exchange, see the sharding notes in DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import position_independent_kv_stitch_amd as pic
+    from pic_workloads import config2, pool_values, sentinel_like
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = config2()
+    log(f"workload: {wl.name}, generating inputs on cuda:0")
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
+    dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
+    dv = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    info = plan.info
+    step_bytes = (info["bytes_read_per_layer"] + info["bytes_written_per_layer"]) * wl.n_layers
+    step_tl = info["tokens_written"] * wl.n_layers
+
+    for _ in range(args.warmup):
+        pic.stitch(plan, pk, pv, dk, dv)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        pic.stitch(plan, pk, pv, dk, dv)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
+    ms_per_step = total_ms / args.steps
+
+    value = step_bytes * args.steps / (total_ms * 1e-3) / 1e9
+    achieved = step_bytes / (avg_kernel_ms * 1e-3) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic",
+        "config": {"workload": "llama3-8b-shaped paged stitch: 32 layers, 8 kv heads x 128, "
+                               "bf16, 8 chunks x 2048 tokens after a 128-token prefix, "
+                               "16-token pages, recompute_k 32",
+                   "storage": "bf16", "layers": wl.n_layers, "kv_heads": wl.n_heads,
+                   "head_dim": wl.row_dim, "chunks": 8, "chunk_tokens": 2048, "prefix": 128,
+                   "page_size": wl.page_size, "recompute_k": 32, "rope_theta": wl.theta,
+                   "parallelism": "single-gpu"},
+        "token_layers_per_s": round(step_tl * args.steps / (total_ms * 1e-3), 1),
+        "hbm_peak_frac": round(value / PEAK_GBS, 4),
+        "bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "stitch_kernel<bf16, half>",
+                     "avg_launch_ms": round(avg_kernel_ms, 5),
+                     "median_launch_ms": round(kernel_ms[len(kernel_ms) // 2], 5),
+                     "algorithmic_bytes_per_launch": step_bytes},
+    }
+    if not args.no_copy_ceiling:
+        out["copy_ceiling"] = copy_ceiling(torch, step_bytes)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, pk, pv, info)
+    else:
+        out["cpu_baseline"] = None
+    plan.destroy()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

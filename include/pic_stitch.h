@@ -1,0 +1,270 @@
+/*
+ * pic_stitch.h -- C ABI of the position-independent KV stitching library
+ * (libpic_stitch.so, HIP for gfx950).
+ *
+ * Position-independent caching keeps the KV cache of every reusable chunk
+ * (a document, a tool schema, a system prompt) computed once at virtual
+ * offset 0 and places it at any logical offset of a later request (EPIC
+ * Guide: Position-Independent Caching for LLM Serving, "Position-Independent
+ * Caching (PIC): Formalization & Core Challenges" and "Algorithmic
+ * Architecture: The EPIC Serving Runtime").  Placing a chunk needs:
+ *   - the keys' rotary part turned by delta = p_target - p_source on every
+ *     RoPE plane i, by the angle delta * theta_i with theta_i = b^(-2i/d)
+ *     (EPIC Guide, "Mathematical Foundations", sections 1 and 2; Irminsul:
+ *     MLA-Native Position-Independent Caching for Agentic LLM Serving,
+ *     Technical Summary section 2.2, delta-rotation rule);
+ *   - the values, and for MLA the 512-dim content latent, copied unchanged
+ *     (EPIC Guide section 2, values untouched; Irminsul section 2.1);
+ *   - the first recompute_k tokens of a chunk left out, for a recompute
+ *     pass to fill (Irminsul section 2.2, first-chunk carve-out).
+ *
+ * Conventions for every call:
+ *   - All sizes, offsets and strides are in elements of the storage type
+ *     unless stated otherwise; positions and token indices are int64.
+ *   - KV memory is device memory owned by the caller.  Views are borrowed
+ *     until the work enqueued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Calls return once the work is enqueued; device faults surface at the
+ *     caller's next synchronisation.
+ *   - Every argument is validated before anything is enqueued: a call that
+ *     returns an error has written nothing.  Nothing aborts the process.
+ *   - Device pointers and every row start must be 16-byte aligned, i.e. all
+ *     strides and the rotary offset are multiples of 16 bytes' worth of
+ *     elements (4 for f32, 8 for bf16).
+ *   - pic_last_error() returns a thread-local message for the last failure
+ *     on the calling thread.
+ */
+#ifndef PIC_STITCH_H
+#define PIC_STITCH_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pic_status {
+    PIC_OK = 0,
+    PIC_ERR_INVALID_ARG = 1, /* malformed shape, rope config, view or layer range */
+    PIC_ERR_RANGE = 2,       /* index or length outside what it refers to */
+    PIC_ERR_OVERLAP = 3,     /* two placements claim one position or one row */
+    PIC_ERR_ALIGN = 4,       /* pointer, stride or slice not 16-byte aligned */
+    PIC_ERR_DEVICE = 5,      /* HIP runtime error (launch, copy, allocation) */
+    PIC_ERR_NOMEM = 6,       /* host allocation failed */
+    PIC_ERR_STATE = 7        /* plan used on another device, or destroyed */
+} pic_status;
+
+enum { PIC_DTYPE_F32 = 0, PIC_DTYPE_BF16 = 1 };
+
+/* Pairing of the rotated dimensions into planes. */
+enum {
+    PIC_ROPE_HALF = 0,       /* plane i = dims (i, i + rope_dim/2): rotate-half models */
+    PIC_ROPE_INTERLEAVED = 1 /* plane i = dims (2i, 2i + 1), as the EPIC Guide writes it */
+};
+
+/* RoPE of the model (EPIC Guide, "RoPE Mathematical Structure"). */
+typedef struct pic_rope_config {
+    int32_t rope_dim;        /* rotated dims per head row: even, >= 2 */
+    int32_t style;           /* PIC_ROPE_HALF | PIC_ROPE_INTERLEAVED */
+    double theta;            /* base b; theta_i = b^(-2i/rope_dim) */
+    const double *inv_freq;  /* optional host table of rope_dim/2 values replacing the
+                                formula (scaled RoPE variants); NULL = formula */
+} pic_rope_config;
+
+/*
+ * Per-layer KV geometry.  Every token has num_heads K rows of row_dim
+ * elements (and as many V rows when has_v); the rotary slice of each K row
+ * is [rope_offset, rope_offset + rope_dim).
+ *   GQA (Llama-style):  num_heads 8, row_dim 128, rope_offset 0, has_v 1
+ *   MLA (DeepSeek-V3):  num_heads 1, row_dim 576, rope_offset 512, has_v 0
+ *                       (Irminsul section 2.1: cKV 512 + k_r 64)
+ */
+typedef struct pic_kv_shape {
+    int32_t dtype; /* PIC_DTYPE_F32 | PIC_DTYPE_BF16 */
+    int32_t num_layers;
+    int32_t num_heads;
+    int32_t row_dim;
+    int32_t rope_offset;
+    int32_t has_v; /* 0 or 1 */
+} pic_kv_shape;
+
+/* A cached chunk in the pool: tokens [token_start, token_start + length),
+ * whose keys were rotated for positions base_pos, base_pos + 1, ...
+ * (EPIC caches at virtual offset 0, so base_pos is normally 0; Irminsul's
+ * registry stores it explicitly, section 2.2). */
+typedef struct pic_chunk {
+    int64_t token_start;
+    int64_t base_pos;
+    int32_t length;
+    int32_t reserved; /* must be 0 */
+} pic_chunk;
+
+/* One placement: chunk tokens [0, length) go to logical positions
+ * [dst_offset, dst_offset + length) of the request; tokens [0, recompute_k)
+ * are not written. */
+typedef struct pic_entry {
+    int64_t dst_offset;
+    int32_t chunk_id;
+    int32_t length;
+    int32_t recompute_k;
+    int32_t reserved; /* must be 0 */
+} pic_entry;
+
+/* A request's placement table (host memory, read during pic_plan only).
+ * page_table maps logical page j to a physical page of the destination
+ * pool; it is ignored for a contiguous destination. */
+typedef struct pic_request {
+    const pic_entry *entries;
+    const int32_t *page_table;
+    int32_t n_entries;
+    int32_t n_pages;
+} pic_request;
+
+/* Destination geometry: page_size 0 = contiguous (each request owns
+ * capacity_tokens positions), else paged with num_phys_pages pages of
+ * page_size tokens shared by all requests. */
+typedef struct pic_dst_geom {
+    int32_t page_size;
+    int32_t reserved; /* must be 0 */
+    int64_t capacity_tokens;
+    int64_t num_phys_pages;
+} pic_dst_geom;
+
+/*
+ * A device view of K (and V) memory.  Element (layer l, token row t, head
+ * h, dim d) of K is k[l*layer_stride + t*token_stride + h*head_stride + d],
+ * V the same with v; K and V share the strides.
+ *   pool / in-place buffer: t is the token index.
+ *   contiguous destination: t = r*request_stride/token_stride + position,
+ *     i.e. the row of request r's position p starts at
+ *     l*layer_stride + r*request_stride + p*token_stride.
+ *   paged destination: the row of a position p of a request starts at
+ *     l*layer_stride + page_table[p / page_size]*page_stride
+ *     + (p % page_size)*token_stride.
+ * Unused strides are ignored.  v is ignored when has_v is 0.
+ */
+typedef struct pic_kv_view {
+    void *k;
+    void *v;
+    int64_t layer_stride;
+    int64_t token_stride;
+    int64_t head_stride;
+    int64_t page_stride;
+    int64_t request_stride;
+} pic_kv_view;
+
+/* In-place mode: rotate tokens [token_start + recompute_k, token_start +
+ * length) of a buffer by delta positions. */
+typedef struct pic_segment {
+    int64_t token_start;
+    int64_t delta;
+    int32_t length;
+    int32_t recompute_k;
+} pic_segment;
+
+typedef struct pic_plan_info_t {
+    int64_t n_requests;
+    int64_t n_entries;
+    int64_t n_tiles;              /* work items of one layer */
+    int64_t tokens_written;       /* per layer */
+    int64_t tokens_masked;        /* per layer: sum of recompute_k */
+    int64_t pool_tokens_required; /* max token_start + length over chunks */
+    int64_t bytes_read_per_layer; /* algorithmic: rows read */
+    int64_t bytes_written_per_layer;
+} pic_plan_info_t;
+
+typedef struct pic_plan pic_plan_t;
+
+/*
+ * pic_plan -- validate a stitch problem and build its execution plan
+ * (EPIC Guide, "Modular Prompt Composer": the composer computes the shift of
+ * every hit chunk; SemPIC: Learning Semantic Position-Independent KV Caches,
+ * cache-hit serving: final logical positions are assigned, then keys are
+ * re-rotated).
+ *
+ * For every entry, delta = dst_offset - chunk.base_pos; cos/sin of
+ * delta*theta_i are computed in fp64 on the host; tokens [recompute_k,
+ * length) are cut into work tiles.  Host only: no HIP call is made, so the
+ * plan can be built without a GPU.  All input arrays are copied; the
+ * caller may free them on return.
+ *
+ * Valid input (else PIC_ERR_RANGE unless noted):
+ *   0 <= chunk_id < n_chunks; 1 <= length <= chunk.length;
+ *   0 <= recompute_k <= length; dst_offset >= 0;
+ *   dst_offset + length <= capacity_tokens (contiguous) or
+ *     <= n_pages * page_size (paged);
+ *   chunk.token_start >= 0, chunk.length >= 1;
+ *   every page written is in [0, num_phys_pages);
+ *   entries of one request do not overlap, and no destination row is
+ *     written twice (PIC_ERR_OVERLAP);
+ *   duplicate chunk_ids and negative deltas are allowed.
+ * Shape/rope errors are PIC_ERR_INVALID_ARG; a rotary slice or unit count
+ * that does not fit 16-byte vectors is PIC_ERR_ALIGN.
+ *
+ * On success *out owns a plan released by pic_plan_destroy.
+ */
+pic_status pic_plan(const pic_kv_shape *shape, const pic_rope_config *rope,
+                    const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
+                    int32_t n_requests, const pic_dst_geom *dst, pic_plan_t **out);
+
+/*
+ * pic_stitch -- run a plan for layers [layer_begin, layer_end) of the views:
+ * one kernel launch reads each placed chunk row once from `pool`, turns the
+ * rotary slice of every K row by its entry's delta (fp64 arithmetic, one
+ * round-to-nearest-even into the storage type; delta 0 copies the bits),
+ * copies V rows and the rest of K unchanged, and writes them to `dst`
+ * (EPIC Guide, "The In-Place Shift Transformation"; Irminsul section 2.2).
+ * Destination rows not covered (prefixes, gaps, masked tokens) are not
+ * touched.  Layer indices address the views directly (0 <= layer_begin <=
+ * layer_end <= num_layers), so a view holding a group of layers is run with
+ * a range inside that group; every layer has the plan's geometry.
+ *
+ * The first call uploads the plan's metadata to the current device,
+ * ordered on `stream`; later calls on any stream wait for that upload.
+ * A plan is bound to the device of its first call (PIC_ERR_STATE after).
+ * pool and dst must not overlap.
+ */
+pic_status pic_stitch(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *dst,
+                      int32_t layer_begin, int32_t layer_end, void *stream);
+
+/*
+ * pic_rotate_inplace -- turn the rotary slice of K, in place, for tokens
+ * [token_start + recompute_k, token_start + length) of every segment by the
+ * segment's delta, for layers [layer_begin, layer_end) of `buf` (EPIC
+ * Guide, "The In-Place Shift Transformation" and the runtime's in-place key
+ * rotation step).  V and the non-rotary dims are not touched.  Segments
+ * must lie in [0, buf_tokens) and must not overlap (PIC_ERR_RANGE,
+ * PIC_ERR_OVERLAP).  Per call, the library builds the shift tables on the
+ * host and stages them in stream-ordered device memory that it frees on
+ * the same stream.
+ */
+pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
+                              const pic_kv_view *buf, int64_t buf_tokens,
+                              const pic_segment *segments, int32_t n_segments,
+                              int32_t layer_begin, int32_t layer_end, void *stream);
+
+/* pic_plan_info -- sizes and algorithmic byte counts of a plan. */
+pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info);
+
+/*
+ * pic_plan_ranges -- chunk boundaries and recompute ranges, entry by entry
+ * in request order (EPIC Guide, the chunk boundaries a LegoLink pass
+ * consumes; Irminsul section 2.2, the recompute carve-out).  Either output
+ * may be NULL; each must hold n_entries rows:
+ *   boundaries[e] = {request, dst_offset, dst_offset + length}
+ *   recompute[e]  = {request, dst_offset, dst_offset + recompute_k}
+ */
+pic_status pic_plan_ranges(const pic_plan_t *plan, int64_t *boundaries, int64_t *recompute);
+
+/* pic_plan_destroy -- wait for the device to finish, release the plan.
+ * NULL is a no-op. */
+void pic_plan_destroy(pic_plan_t *plan);
+
+/* Thread-local message for the last failed call on this thread ("" if none). */
+const char *pic_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIC_STITCH_H */

@@ -1,0 +1,14 @@
+"""Position-independent KV-chunk stitching for MI355X (gfx950).
+
+Relocates KV chunks cached at virtual offset 0 to arbitrary logical offsets
+of a request: the rotary slice of every key is turned by the chunk's shift,
+values and non-rotary dims are copied unchanged, and the first recompute_k
+tokens of a chunk are left for a recompute pass.  All work runs in the HIP
+library libpic_stitch.so (C ABI in include/pic_stitch.h); this package is
+its thin binding.  Importing it loads the library and fails if it has not
+been built.
+"""
+from ._binding import (EXPORTS, LIBRARY, PicError, Plan, load_library,  # noqa: F401
+                       rotate_inplace, rotate_workload, stitch)
+
+load_library()

@@ -1,0 +1,334 @@
+"""ctypes binding of libpic_stitch.so (argument marshalling only).
+
+Every step of the path runs in the HIP library; this module turns torch
+tensors into views (pointer + element strides), Python placement tables
+into the C structs of ``include/pic_stitch.h``, and torch's current stream
+into the stream argument.  There is no fallback: if the library is missing
+or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libpic_stitch.so")
+
+PIC_OK, PIC_ERR_INVALID_ARG, PIC_ERR_RANGE, PIC_ERR_OVERLAP = 0, 1, 2, 3
+PIC_ERR_ALIGN, PIC_ERR_DEVICE, PIC_ERR_NOMEM, PIC_ERR_STATE = 4, 5, 6, 7
+STATUS_NAMES = {0: "ok", 1: "invalid_arg", 2: "range", 3: "overlap", 4: "align", 5: "device",
+                6: "nomem", 7: "state"}
+DTYPES = {"f32": 0, "bf16": 1}
+STYLES = {"half": 0, "interleaved": 1}
+
+# every entry point the header declares
+EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_plan_info", "pic_plan_ranges",
+           "pic_plan_destroy", "pic_last_error")
+
+
+class PicError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.name = STATUS_NAMES.get(status, str(status))
+
+
+class RopeConfig(C.Structure):
+    _fields_ = [("rope_dim", C.c_int32), ("style", C.c_int32), ("theta", C.c_double),
+                ("inv_freq", C.POINTER(C.c_double))]
+
+
+class KvShape(C.Structure):
+    _fields_ = [("dtype", C.c_int32), ("num_layers", C.c_int32), ("num_heads", C.c_int32),
+                ("row_dim", C.c_int32), ("rope_offset", C.c_int32), ("has_v", C.c_int32)]
+
+
+class ChunkC(C.Structure):
+    _fields_ = [("token_start", C.c_int64), ("base_pos", C.c_int64), ("length", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class EntryC(C.Structure):
+    _fields_ = [("dst_offset", C.c_int64), ("chunk_id", C.c_int32), ("length", C.c_int32),
+                ("recompute_k", C.c_int32), ("reserved", C.c_int32)]
+
+
+class RequestC(C.Structure):
+    _fields_ = [("entries", C.POINTER(EntryC)), ("page_table", C.POINTER(C.c_int32)),
+                ("n_entries", C.c_int32), ("n_pages", C.c_int32)]
+
+
+class DstGeom(C.Structure):
+    _fields_ = [("page_size", C.c_int32), ("reserved", C.c_int32),
+                ("capacity_tokens", C.c_int64), ("num_phys_pages", C.c_int64)]
+
+
+class KvView(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("layer_stride", C.c_int64),
+                ("token_stride", C.c_int64), ("head_stride", C.c_int64),
+                ("page_stride", C.c_int64), ("request_stride", C.c_int64)]
+
+
+class SegmentC(C.Structure):
+    _fields_ = [("token_start", C.c_int64), ("delta", C.c_int64), ("length", C.c_int32),
+                ("recompute_k", C.c_int32)]
+
+
+class PlanInfo(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in (
+        "n_requests", "n_entries", "n_tiles", "tokens_written", "tokens_masked",
+        "pool_tokens_required", "bytes_read_per_layer", "bytes_written_per_layer")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load_library():
+    """Load libpic_stitch.so; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = C.CDLL(LIBRARY)
+    P = C.POINTER
+    lib.pic_plan.restype = C.c_int
+    lib.pic_plan.argtypes = [P(KvShape), P(RopeConfig), P(ChunkC), C.c_int32, P(RequestC),
+                             C.c_int32, P(DstGeom), P(C.c_void_p)]
+    lib.pic_stitch.restype = C.c_int
+    lib.pic_stitch.argtypes = [C.c_void_p, P(KvView), P(KvView), C.c_int32, C.c_int32,
+                               C.c_void_p]
+    lib.pic_rotate_inplace.restype = C.c_int
+    lib.pic_rotate_inplace.argtypes = [P(KvShape), P(RopeConfig), P(KvView), C.c_int64,
+                                       P(SegmentC), C.c_int32, C.c_int32, C.c_int32,
+                                       C.c_void_p]
+    lib.pic_plan_info.restype = C.c_int
+    lib.pic_plan_info.argtypes = [C.c_void_p, P(PlanInfo)]
+    lib.pic_plan_ranges.restype = C.c_int
+    lib.pic_plan_ranges.argtypes = [C.c_void_p, P(C.c_int64), P(C.c_int64)]
+    lib.pic_plan_destroy.restype = None
+    lib.pic_plan_destroy.argtypes = [C.c_void_p]
+    lib.pic_last_error.restype = C.c_char_p
+    lib.pic_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != PIC_OK:
+        raise PicError(status, load_library().pic_last_error().decode())
+
+
+def _get(obj, name, idx):
+    """Field `name` of an attribute object, or position `idx` of a tuple."""
+    return getattr(obj, name) if hasattr(obj, name) else obj[idx]
+
+
+def _shape_and_rope(dtype, n_layers, n_heads, row_dim, rope_offset, rope_dim, style, theta,
+                    has_v, inv_freq):
+    keep = []
+    inv_ptr = None
+    if inv_freq is not None:
+        arr = np.ascontiguousarray(np.asarray(inv_freq, dtype=np.float64))
+        keep.append(arr)
+        inv_ptr = arr.ctypes.data_as(C.POINTER(C.c_double))
+    shape = KvShape(DTYPES[dtype], n_layers, n_heads, row_dim, rope_offset, int(bool(has_v)))
+    rope = RopeConfig(rope_dim, STYLES[style], float(theta), inv_ptr)
+    return shape, rope, keep
+
+
+class Plan:
+    """An execution plan of the stitch library (wraps pic_plan_t*)."""
+
+    def __init__(self, *, dtype: str, n_layers: int, n_heads: int, row_dim: int,
+                 rope_offset: int, rope_dim: int, style: str, theta: float, has_v: bool,
+                 chunks: Sequence, requests: Sequence, page_size: int = 0,
+                 capacity: int = 0, n_phys_pages: int = 0, inv_freq=None):
+        lib = load_library()
+        self._lib = lib
+        self._handle = C.c_void_p()
+        self.dtype, self.n_layers, self.n_heads, self.row_dim = dtype, n_layers, n_heads, row_dim
+        self.has_v, self.page_size = bool(has_v), page_size
+        self.capacity, self.n_phys_pages, self.n_requests = capacity, n_phys_pages, len(requests)
+        shape, rope, keep = _shape_and_rope(dtype, n_layers, n_heads, row_dim, rope_offset,
+                                            rope_dim, style, theta, has_v, inv_freq)
+        carr = (ChunkC * max(1, len(chunks)))()
+        for i, c in enumerate(chunks):
+            carr[i] = ChunkC(int(_get(c, "token_start", 0)), int(_get(c, "base_pos", 2)),
+                             int(_get(c, "length", 1)), 0)
+        rarr = (RequestC * max(1, len(requests)))()
+        for r, rq in enumerate(requests):
+            entries = _get(rq, "entries", 0)
+            earr = (EntryC * max(1, len(entries)))()
+            for j, e in enumerate(entries):
+                earr[j] = EntryC(int(_get(e, "dst_offset", 1)), int(_get(e, "chunk_id", 0)),
+                                 int(_get(e, "length", 2)), int(_get(e, "recompute_k", 3)), 0)
+            keep.append(earr)
+            pt = _get(rq, "page_table", 1) if page_size else None
+            pt_ptr, n_pages = None, 0
+            if pt is not None:
+                pta = np.ascontiguousarray(np.asarray(pt, dtype=np.int32))
+                keep.append(pta)
+                pt_ptr, n_pages = pta.ctypes.data_as(C.POINTER(C.c_int32)), len(pta)
+            rarr[r] = RequestC(earr, pt_ptr, len(entries), n_pages)
+        geom = DstGeom(page_size, 0, capacity, n_phys_pages)
+        _check(lib.pic_plan(C.byref(shape), C.byref(rope), carr, len(chunks), rarr,
+                            len(requests), C.byref(geom), C.byref(self._handle)))
+        self.info = self._info()
+
+    @classmethod
+    def from_workload(cls, wl) -> "Plan":
+        return cls(dtype=wl.dtype, n_layers=wl.n_layers, n_heads=wl.n_heads,
+                   row_dim=wl.row_dim, rope_offset=wl.rope_offset, rope_dim=wl.rope_dim,
+                   style=wl.style, theta=wl.theta, has_v=wl.has_v, chunks=wl.chunks,
+                   requests=wl.requests, page_size=wl.page_size, capacity=wl.capacity,
+                   n_phys_pages=wl.n_phys_pages, inv_freq=wl.inv_freq)
+
+    def _info(self) -> dict:
+        info = PlanInfo()
+        _check(self._lib.pic_plan_info(self._handle, C.byref(info)))
+        return info.as_dict()
+
+    def ranges(self):
+        """(boundaries, recompute) as int64 arrays of [request, begin, end] rows."""
+        n = self.info["n_entries"]
+        b = np.zeros((max(n, 1), 3), dtype=np.int64)
+        r = np.zeros((max(n, 1), 3), dtype=np.int64)
+        _check(self._lib.pic_plan_ranges(self._handle, b.ctypes.data_as(C.POINTER(C.c_int64)),
+                                         r.ctypes.data_as(C.POINTER(C.c_int64))))
+        return b[:n], r[:n]
+
+    @property
+    def handle(self):
+        if not self._handle:
+            raise PicError(PIC_ERR_STATE, "plan destroyed")
+        return self._handle
+
+    def destroy(self):
+        if self._handle:
+            self._lib.pic_plan_destroy(self._handle)
+            self._handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------- views
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_name(t) -> str:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return "f32"
+    if t.dtype == torch.bfloat16:
+        return "bf16"
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _view(k, v, kind: str) -> KvView:
+    """A view of 4-D [L][T][H][D] (pool, in-place buffer), 5-D [L][R][S][H][D]
+    (contiguous destination) or 5-D [L][P][page][H][D] (paged destination)."""
+    for t in (k, v):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{kind}: tensors must be on a GPU")
+        if t.stride(-1) != 1:
+            raise ValueError(f"{kind}: the last (dim) axis must be contiguous")
+    if v is not None:
+        if v.shape != k.shape or v.stride() != k.stride() or v.dtype != k.dtype:
+            raise ValueError(f"{kind}: K and V must share shape, strides and dtype")
+    st = k.stride()
+    if kind in ("pool", "buf"):
+        if k.dim() != 4:
+            raise ValueError(f"{kind}: expected [layers][tokens][heads][dim]")
+        return KvView(k.data_ptr(), v.data_ptr() if v is not None else None, st[0], st[1],
+                      st[2], 0, 0)
+    if k.dim() != 5:
+        raise ValueError(f"{kind}: expected a 5-D destination")
+    if kind == "paged":
+        return KvView(k.data_ptr(), v.data_ptr() if v is not None else None, st[0], st[2],
+                      st[3], st[1], 0)
+    return KvView(k.data_ptr(), v.data_ptr() if v is not None else None, st[0], st[2], st[3],
+                  0, st[1])
+
+
+def _stream_of(t, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def stitch(plan: Plan, pool_k, pool_v, dst_k, dst_v, layer_begin: int = 0,
+           layer_end: Optional[int] = None, stream=None):
+    """Enqueue pic_stitch for layers [layer_begin, layer_end) of the tensors.
+
+    pool_*: [L][T][H][D]; dst_*: contiguous [L][R][S][H][D] or paged
+    [L][P][page][H][D].  V tensors are None when the plan has no V."""
+    le = dst_k.shape[0] if layer_end is None else layer_end
+    if _dtype_name(pool_k) != plan.dtype or _dtype_name(dst_k) != plan.dtype:
+        raise TypeError("tensor dtype does not match the plan")
+    if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+        raise PicError(PIC_ERR_RANGE, f"pool holds {pool_k.shape[1]} tokens, plan needs "
+                       f"{plan.info['pool_tokens_required']}")
+    if tuple(pool_k.shape[2:]) != (plan.n_heads, plan.row_dim) or \
+            tuple(dst_k.shape[3:]) != (plan.n_heads, plan.row_dim):
+        raise ValueError("head/row shape does not match the plan")
+    if plan.page_size:
+        if dst_k.shape[1] < plan.n_phys_pages or dst_k.shape[2] != plan.page_size:
+            raise ValueError("paged destination smaller than the plan's page pool")
+    else:
+        if dst_k.shape[1] < plan.n_requests or dst_k.shape[2] < plan.capacity:
+            raise ValueError("contiguous destination smaller than requests x capacity")
+    if pool_k.shape[0] < le or dst_k.shape[0] < le:
+        raise ValueError("layer range beyond the tensors")
+    if pool_k.device != dst_k.device:
+        raise ValueError("pool and destination on different devices")
+    if plan.has_v and (pool_v is None or dst_v is None):
+        raise ValueError("plan has V rows: pass pool_v and dst_v")
+    pv = _view(pool_k, pool_v if plan.has_v else None, "pool")
+    dv = _view(dst_k, dst_v if plan.has_v else None, "paged" if plan.page_size else "contig")
+    lib = load_library()
+    _check(lib.pic_stitch(plan.handle, C.byref(pv), C.byref(dv), layer_begin, le,
+                          _stream_of(pool_k, stream)))
+
+
+def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
+                   style: str = "half", rope_offset: int = 0, layer_begin: int = 0,
+                   layer_end: Optional[int] = None, inv_freq=None, stream=None):
+    """Enqueue pic_rotate_inplace on buf_k [L][T][H][D]; segments are
+    (token_start, length, delta, recompute_k) tuples or objects."""
+    lib = load_library()
+    L, T, H, D = buf_k.shape
+    le = L if layer_end is None else layer_end
+    shape, rope, keep = _shape_and_rope(_dtype_name(buf_k), L, H, D, rope_offset, rope_dim,
+                                        style, theta, False, inv_freq)
+    sarr = (SegmentC * max(1, len(segments)))()
+    for i, s in enumerate(segments):
+        sarr[i] = SegmentC(int(_get(s, "token_start", 0)), int(_get(s, "delta", 2)),
+                           int(_get(s, "length", 1)), int(_get(s, "recompute_k", 3)))
+    view = _view(buf_k, None, "buf")
+    _check(lib.pic_rotate_inplace(C.byref(shape), C.byref(rope), C.byref(view), T, sarr,
+                                  len(segments), layer_begin, le, _stream_of(buf_k, stream)))
+
+
+def rotate_workload(wl, buf_k, layer_begin=0, layer_end=None, stream=None):
+    """pic_rotate_inplace for an in-place workload description."""
+    rotate_inplace(buf_k, wl.segments, rope_dim=wl.rope_dim, theta=wl.theta, style=wl.style,
+                   rope_offset=wl.rope_offset, layer_begin=layer_begin, layer_end=layer_end,
+                   inv_freq=wl.inv_freq, stream=stream)

@@ -1,0 +1,435 @@
+// plan.cpp -- host planner of the stitch library: validation, per-entry
+// shifts and fp64 cos/sin tables, work tiles, boundary and recompute
+// ranges.  No HIP call is made here, so plans can be built and inspected
+// without a GPU.
+//
+// The shift of a placed chunk is delta = p_target - p_source (Irminsul:
+// MLA-Native Position-Independent Caching for Agentic LLM Serving,
+// Technical Summary section 2.2); the composer computes it for every hit
+// chunk (EPIC Guide: Position-Independent Caching for LLM Serving,
+// "Modular Prompt Composer").  Because 2-D rotations compose by adding
+// angles (EPIC Guide, "The In-Place Shift Transformation"), one table of
+// cos/sin(delta * theta_i) per distinct delta serves every token of the
+// chunk, with theta_i = b^(-2i/d) ("RoPE Mathematical Structure").
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <unordered_map>
+
+#include "pic_internal.hpp"
+
+namespace pic {
+
+namespace {
+thread_local std::string g_error;
+
+constexpr int64_t kMaxPosition = INT32_MAX;  // positions and in-chunk offsets fit int32
+}  // namespace
+
+void clear_error() { g_error.clear(); }
+
+pic_status fail(pic_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+pic_status derive_units(const pic_kv_shape *shape, const pic_rope_config *rope, bool inplace,
+                        Units *u) {
+    if (!shape || !rope) return fail(PIC_ERR_INVALID_ARG, "shape and rope must not be NULL");
+    if (shape->dtype != PIC_DTYPE_F32 && shape->dtype != PIC_DTYPE_BF16)
+        return fail(PIC_ERR_INVALID_ARG, "unknown dtype %d", shape->dtype);
+    if (rope->style != PIC_ROPE_HALF && rope->style != PIC_ROPE_INTERLEAVED)
+        return fail(PIC_ERR_INVALID_ARG, "unknown rope style %d", rope->style);
+    if (shape->num_layers < 1 || shape->num_heads < 1 || shape->row_dim < 1)
+        return fail(PIC_ERR_INVALID_ARG, "num_layers, num_heads and row_dim must be >= 1");
+    if (rope->rope_dim < 2 || rope->rope_dim % 2 != 0)
+        return fail(PIC_ERR_INVALID_ARG, "rope_dim %d must be even and >= 2", rope->rope_dim);
+    if (shape->rope_offset < 0 || shape->rope_offset + rope->rope_dim > shape->row_dim)
+        return fail(PIC_ERR_INVALID_ARG, "rotary slice [%d, %d) outside a row of %d",
+                    shape->rope_offset, shape->rope_offset + rope->rope_dim, shape->row_dim);
+    if (rope->inv_freq) {
+        for (int i = 0; i < rope->rope_dim / 2; i++)
+            if (!std::isfinite(rope->inv_freq[i]))
+                return fail(PIC_ERR_INVALID_ARG, "inv_freq[%d] is not finite", i);
+    } else if (!(rope->theta > 0.0) || !std::isfinite(rope->theta)) {
+        return fail(PIC_ERR_INVALID_ARG, "theta must be finite and > 0");
+    }
+    if (shape->has_v != 0 && shape->has_v != 1)
+        return fail(PIC_ERR_INVALID_ARG, "has_v must be 0 or 1");
+
+    const int es = shape->dtype == PIC_DTYPE_F32 ? 4 : 2;
+    const int vec = 16 / es;
+    const int half_r = rope->rope_dim / 2;
+    if (shape->row_dim % vec || shape->rope_offset % vec)
+        return fail(PIC_ERR_ALIGN, "row_dim and rope_offset must be multiples of %d", vec);
+    int uph, ncs;
+    if (rope->style == PIC_ROPE_HALF) {
+        if (half_r % vec)
+            return fail(PIC_ERR_ALIGN, "rope_dim/2 must be a multiple of %d (half pairing)", vec);
+        uph = half_r / vec;
+        ncs = vec;
+    } else {
+        if (rope->rope_dim % vec)
+            return fail(PIC_ERR_ALIGN, "rope_dim must be a multiple of %d (interleaved)", vec);
+        uph = rope->rope_dim / vec;
+        ncs = vec / 2;
+    }
+    if (uph > 64 || (64 % uph) != 0)
+        return fail(PIC_ERR_ALIGN, "rotary slice of %d 16-byte units per head: need a power "
+                    "of two <= 64", uph);
+    u->vec = vec;
+    u->half_r = half_r;
+    u->uph = uph;
+    u->uph_shift = 0;
+    while ((1 << u->uph_shift) < uph) u->uph_shift++;
+    u->ncs = ncs;
+    u->nr = shape->num_heads * uph;
+    u->cph = (shape->row_dim - rope->rope_dim) / vec;
+    u->vph = shape->row_dim / vec;
+    u->nck = inplace ? 0 : shape->num_heads * u->cph;
+    u->nv = (inplace || !shape->has_v) ? 0 : shape->num_heads * u->vph;
+    return PIC_OK;
+}
+
+namespace {
+
+// cos/sin of delta * theta_i for i < rope_dim/2, in fp64 (libm), appended to cs.
+void append_shift_table(const pic_rope_config &rope, int64_t delta, std::vector<double> &cs) {
+    const int half_r = rope.rope_dim / 2;
+    for (int i = 0; i < half_r; i++) {
+        const double f = rope.inv_freq
+                             ? rope.inv_freq[i]
+                             : std::pow(rope.theta, -(2.0 * i) / static_cast<double>(rope.rope_dim));
+        const double phi = static_cast<double>(delta) * f;
+        cs.push_back(std::cos(phi));
+        cs.push_back(std::sin(phi));
+    }
+}
+
+struct Interval {
+    int64_t key;  // sort key (physical page or request)
+    int64_t lo, hi;
+};
+
+bool any_overlap(std::vector<Interval> &v) {
+    std::sort(v.begin(), v.end(), [](const Interval &a, const Interval &b) {
+        return a.key != b.key ? a.key < b.key : a.lo < b.lo;
+    });
+    for (size_t i = 1; i < v.size(); i++)
+        if (v[i].key == v[i - 1].key && v[i].lo < v[i - 1].hi) return true;
+    return false;
+}
+
+void fill_info(Problem *p, int64_t tokens_written, int64_t tokens_masked, int64_t pool_need) {
+    const int64_t es = p->shape.dtype == PIC_DTYPE_F32 ? 4 : 2;
+    int64_t per_token;
+    if (p->mode == kInPlace)
+        per_token = static_cast<int64_t>(p->shape.num_heads) * p->rope_dim * es;
+    else
+        per_token = static_cast<int64_t>(p->shape.num_heads) * p->shape.row_dim * es *
+                    (1 + p->shape.has_v);
+    p->info.n_requests = p->n_requests;
+    p->info.n_entries = static_cast<int64_t>(p->entries.size());
+    p->info.n_tiles = static_cast<int64_t>(p->tiles.size());
+    p->info.tokens_written = tokens_written;
+    p->info.tokens_masked = tokens_masked;
+    p->info.pool_tokens_required = pool_need;
+    p->info.bytes_read_per_layer = tokens_written * per_token;
+    p->info.bytes_written_per_layer = tokens_written * per_token;
+}
+
+void add_tiles(Problem *p, int32_t entry, int32_t from, int32_t to) {
+    for (int32_t t = from; t < to; t += kTileTokens)
+        p->tiles.push_back(DevTile{entry, t, std::min(kTileTokens, to - t), 0});
+}
+
+}  // namespace
+
+pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
+                        const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
+                        int32_t n_requests, const pic_dst_geom *dst, Problem *out) {
+    Units u{};
+    pic_status st = derive_units(shape, rope, false, &u);
+    if (st) return st;
+    if (!dst) return fail(PIC_ERR_INVALID_ARG, "dst geometry must not be NULL");
+    if (n_chunks < 0 || n_requests < 0)
+        return fail(PIC_ERR_INVALID_ARG, "negative chunk or request count");
+    if ((n_chunks > 0 && !chunks) || (n_requests > 0 && !requests))
+        return fail(PIC_ERR_INVALID_ARG, "chunk or request array is NULL");
+    if (dst->page_size < 0 || dst->reserved != 0)
+        return fail(PIC_ERR_INVALID_ARG, "bad destination geometry");
+    const bool paged = dst->page_size > 0;
+    if (!paged && dst->capacity_tokens < 0)
+        return fail(PIC_ERR_INVALID_ARG, "negative capacity");
+    if (paged && dst->num_phys_pages < 0)
+        return fail(PIC_ERR_INVALID_ARG, "negative physical page count");
+    for (int r = 0; r < n_requests; r++) {
+        const pic_request &rq = requests[r];
+        if (rq.n_entries < 0 || (rq.n_entries > 0 && !rq.entries))
+            return fail(PIC_ERR_INVALID_ARG, "request %d: bad entry array", r);
+        if (paged && (rq.n_pages < 0 || (rq.n_pages > 0 && !rq.page_table)))
+            return fail(PIC_ERR_INVALID_ARG, "request %d: bad page table", r);
+    }
+
+    // ranges
+    int64_t pool_need = 0;
+    for (int c = 0; c < n_chunks; c++) {
+        if (chunks[c].token_start < 0 || chunks[c].length < 1 || chunks[c].reserved != 0)
+            return fail(PIC_ERR_RANGE, "chunk %d: token_start %lld, length %d", c,
+                        static_cast<long long>(chunks[c].token_start), chunks[c].length);
+        pool_need = std::max(pool_need, chunks[c].token_start + chunks[c].length);
+    }
+    for (int r = 0; r < n_requests; r++) {
+        const pic_request &rq = requests[r];
+        const int64_t span =
+            paged ? static_cast<int64_t>(rq.n_pages) * dst->page_size : dst->capacity_tokens;
+        for (int j = 0; j < rq.n_entries; j++) {
+            const pic_entry &e = rq.entries[j];
+            if (e.reserved != 0) return fail(PIC_ERR_RANGE, "request %d entry %d: reserved", r, j);
+            if (e.chunk_id < 0 || e.chunk_id >= n_chunks)
+                return fail(PIC_ERR_RANGE, "request %d entry %d: chunk_id %d", r, j, e.chunk_id);
+            if (e.length < 1 || e.length > chunks[e.chunk_id].length)
+                return fail(PIC_ERR_RANGE, "request %d entry %d: length %d of a %d-token chunk", r,
+                            j, e.length, chunks[e.chunk_id].length);
+            if (e.recompute_k < 0 || e.recompute_k > e.length)
+                return fail(PIC_ERR_RANGE, "request %d entry %d: recompute_k %d", r, j,
+                            e.recompute_k);
+            if (e.dst_offset < 0 || e.dst_offset + e.length > span ||
+                e.dst_offset + e.length > kMaxPosition)
+                return fail(PIC_ERR_RANGE, "request %d entry %d: positions [%lld, %lld) outside "
+                            "[0, %lld)", r, j, static_cast<long long>(e.dst_offset),
+                            static_cast<long long>(e.dst_offset + e.length),
+                            static_cast<long long>(span));
+            if (paged && e.recompute_k < e.length) {
+                const int64_t p0 = (e.dst_offset + e.recompute_k) / dst->page_size;
+                const int64_t p1 = (e.dst_offset + e.length - 1) / dst->page_size;
+                for (int64_t pg = p0; pg <= p1; pg++) {
+                    const int32_t phys = rq.page_table[pg];
+                    if (phys < 0 || phys >= dst->num_phys_pages)
+                        return fail(PIC_ERR_RANGE, "request %d: logical page %lld maps to %d "
+                                    "(pool has %lld)", r, static_cast<long long>(pg), phys,
+                                    static_cast<long long>(dst->num_phys_pages));
+                }
+            }
+        }
+    }
+
+    // overlaps: whole entry intervals inside a request, then written rows
+    {
+        std::vector<Interval> iv;
+        for (int r = 0; r < n_requests; r++)
+            for (int j = 0; j < requests[r].n_entries; j++) {
+                const pic_entry &e = requests[r].entries[j];
+                iv.push_back(Interval{r, e.dst_offset, e.dst_offset + e.length});
+            }
+        if (any_overlap(iv)) return fail(PIC_ERR_OVERLAP, "entries of a request overlap");
+    }
+    if (paged) {
+        std::vector<Interval> iv;
+        const int64_t ps = dst->page_size;
+        for (int r = 0; r < n_requests; r++)
+            for (int j = 0; j < requests[r].n_entries; j++) {
+                const pic_entry &e = requests[r].entries[j];
+                int64_t pos = e.dst_offset + e.recompute_k;
+                const int64_t end = e.dst_offset + e.length;
+                while (pos < end) {
+                    const int64_t lp = pos / ps, slot = pos % ps;
+                    const int64_t run = std::min(ps - slot, end - pos);
+                    iv.push_back(Interval{requests[r].page_table[lp], slot, slot + run});
+                    pos += run;
+                }
+            }
+        if (any_overlap(iv))
+            return fail(PIC_ERR_OVERLAP, "two placements write the same physical row");
+    }
+
+    // the plan
+    Problem &p = *out;
+    p.shape = *shape;
+    p.rope_dim = rope->rope_dim;
+    p.style = rope->style;
+    p.mode = paged ? kPaged : kContiguous;
+    p.page_size = dst->page_size;
+    p.capacity = dst->capacity_tokens;
+    p.num_phys_pages = dst->num_phys_pages;
+    p.n_requests = n_requests;
+    p.u = u;
+    std::unordered_map<int64_t, int32_t> table_of_delta;
+    int64_t written = 0, masked = 0;
+    for (int r = 0; r < n_requests; r++) {
+        const pic_request &rq = requests[r];
+        const int32_t page_base = static_cast<int32_t>(p.pages.size());
+        if (paged) p.pages.insert(p.pages.end(), rq.page_table, rq.page_table + rq.n_pages);
+        for (int j = 0; j < rq.n_entries; j++) {
+            const pic_entry &e = rq.entries[j];
+            const pic_chunk &c = chunks[e.chunk_id];
+            const int64_t delta = e.dst_offset - c.base_pos;
+            int32_t cs_idx = -1;
+            if (delta != 0) {
+                auto it = table_of_delta.find(delta);
+                if (it == table_of_delta.end()) {
+                    cs_idx = static_cast<int32_t>(table_of_delta.size());
+                    table_of_delta.emplace(delta, cs_idx);
+                    append_shift_table(*rope, delta, p.cs);
+                } else {
+                    cs_idx = it->second;
+                }
+            }
+            const int32_t idx = static_cast<int32_t>(p.entries.size());
+            p.entries.push_back(DevEntry{c.token_start, e.dst_offset, r, page_base, cs_idx, 0});
+            add_tiles(&p, idx, e.recompute_k, e.length);
+            p.bounds.insert(p.bounds.end(), {r, e.dst_offset, e.dst_offset + e.length});
+            p.recompute.insert(p.recompute.end(), {r, e.dst_offset, e.dst_offset + e.recompute_k});
+            written += e.length - e.recompute_k;
+            masked += e.recompute_k;
+        }
+    }
+    fill_info(&p, written, masked, pool_need);
+    return PIC_OK;
+}
+
+pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
+                         int64_t buf_tokens, const pic_segment *segments, int32_t n_segments,
+                         Problem *out) {
+    Units u{};
+    pic_status st = derive_units(shape, rope, true, &u);
+    if (st) return st;
+    if (buf_tokens < 0 || n_segments < 0 || (n_segments > 0 && !segments))
+        return fail(PIC_ERR_INVALID_ARG, "bad buffer length or segment array");
+    for (int g = 0; g < n_segments; g++) {
+        const pic_segment &s = segments[g];
+        if (s.token_start < 0 || s.length < 1 || s.token_start + s.length > buf_tokens)
+            return fail(PIC_ERR_RANGE, "segment %d: tokens [%lld, %lld) outside [0, %lld)", g,
+                        static_cast<long long>(s.token_start),
+                        static_cast<long long>(s.token_start + s.length),
+                        static_cast<long long>(buf_tokens));
+        if (s.recompute_k < 0 || s.recompute_k > s.length)
+            return fail(PIC_ERR_RANGE, "segment %d: recompute_k %d", g, s.recompute_k);
+    }
+    {
+        std::vector<Interval> iv;
+        for (int g = 0; g < n_segments; g++)
+            iv.push_back(Interval{0, segments[g].token_start,
+                                  segments[g].token_start + segments[g].length});
+        if (any_overlap(iv)) return fail(PIC_ERR_OVERLAP, "segments overlap");
+    }
+    Problem &p = *out;
+    p.shape = *shape;
+    p.shape.has_v = 0;
+    p.rope_dim = rope->rope_dim;
+    p.style = rope->style;
+    p.mode = kInPlace;
+    p.capacity = buf_tokens;
+    p.n_requests = 1;
+    p.u = u;
+    std::unordered_map<int64_t, int32_t> table_of_delta;
+    int64_t written = 0, masked = 0;
+    for (int g = 0; g < n_segments; g++) {
+        const pic_segment &s = segments[g];
+        masked += s.recompute_k;
+        p.bounds.insert(p.bounds.end(), {0, s.token_start, s.token_start + s.length});
+        p.recompute.insert(p.recompute.end(), {0, s.token_start, s.token_start + s.recompute_k});
+        if (s.delta == 0) continue;  // R(0) is the identity: nothing to touch
+        int32_t cs_idx;
+        auto it = table_of_delta.find(s.delta);
+        if (it == table_of_delta.end()) {
+            cs_idx = static_cast<int32_t>(table_of_delta.size());
+            table_of_delta.emplace(s.delta, cs_idx);
+            append_shift_table(*rope, s.delta, p.cs);
+        } else {
+            cs_idx = it->second;
+        }
+        const int32_t idx = static_cast<int32_t>(p.entries.size());
+        p.entries.push_back(DevEntry{s.token_start, s.token_start, 0, 0, cs_idx, 0});
+        add_tiles(&p, idx, s.recompute_k, s.length);
+        written += s.length - s.recompute_k;
+    }
+    fill_info(&p, written, masked, buf_tokens);
+    p.info.n_entries = n_segments;
+    return PIC_OK;
+}
+
+Staged stage(const Problem &p) {
+    Staged s;
+    auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+    size_t at = 0;
+    s.off_tiles = at;
+    at = align(at + p.tiles.size() * sizeof(DevTile));
+    s.off_entries = at;
+    at = align(at + p.entries.size() * sizeof(DevEntry));
+    s.off_cs = at;
+    at = align(at + p.cs.size() * sizeof(double));
+    s.off_pages = at;
+    at = align(at + p.pages.size() * sizeof(int32_t));
+    s.bytes.assign(std::max<size_t>(at, 256), 0);
+    if (!p.tiles.empty())
+        std::memcpy(&s.bytes[s.off_tiles], p.tiles.data(), p.tiles.size() * sizeof(DevTile));
+    if (!p.entries.empty())
+        std::memcpy(&s.bytes[s.off_entries], p.entries.data(), p.entries.size() * sizeof(DevEntry));
+    if (!p.cs.empty()) std::memcpy(&s.bytes[s.off_cs], p.cs.data(), p.cs.size() * sizeof(double));
+    if (!p.pages.empty())
+        std::memcpy(&s.bytes[s.off_pages], p.pages.data(), p.pages.size() * sizeof(int32_t));
+    return s;
+}
+
+}  // namespace pic
+
+extern "C" {
+
+pic_status pic_plan(const pic_kv_shape *shape, const pic_rope_config *rope,
+                    const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
+                    int32_t n_requests, const pic_dst_geom *dst, pic_plan_t **out) {
+    pic::clear_error();
+    if (!out) return pic::fail(PIC_ERR_INVALID_ARG, "out must not be NULL");
+    *out = nullptr;
+    pic_plan_t *plan = new (std::nothrow) pic_plan_t();
+    if (!plan) return pic::fail(PIC_ERR_NOMEM, "out of host memory");
+    try {
+        pic_status st =
+            pic::build_stitch(shape, rope, chunks, n_chunks, requests, n_requests, dst, &plan->prob);
+        if (st) {
+            delete plan;
+            return st;
+        }
+        plan->staged = pic::stage(plan->prob);
+    } catch (const std::bad_alloc &) {
+        delete plan;
+        return pic::fail(PIC_ERR_NOMEM, "out of host memory");
+    }
+    *out = plan;
+    return PIC_OK;
+}
+
+pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info) {
+    pic::clear_error();
+    if (!plan || plan->magic != pic::kPlanMagic)
+        return pic::fail(PIC_ERR_STATE, "invalid or destroyed plan");
+    if (!info) return pic::fail(PIC_ERR_INVALID_ARG, "info must not be NULL");
+    *info = plan->prob.info;
+    return PIC_OK;
+}
+
+pic_status pic_plan_ranges(const pic_plan_t *plan, int64_t *boundaries, int64_t *recompute) {
+    pic::clear_error();
+    if (!plan || plan->magic != pic::kPlanMagic)
+        return pic::fail(PIC_ERR_STATE, "invalid or destroyed plan");
+    const auto &p = plan->prob;
+    if (boundaries && !p.bounds.empty())
+        std::memcpy(boundaries, p.bounds.data(), p.bounds.size() * sizeof(int64_t));
+    if (recompute && !p.recompute.empty())
+        std::memcpy(recompute, p.recompute.data(), p.recompute.size() * sizeof(int64_t));
+    return PIC_OK;
+}
+
+const char *pic_last_error(void) { return pic::g_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+"""The C-ABI library loads on a machine without a GPU, exports every entry
+point include/pic_stitch.h declares, and the binding's ctypes structs have
+the C layout (checked against a C program compiled from the header)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+import position_independent_kv_stitch_amd as pic
+from position_independent_kv_stitch_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pic_stitch.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pic_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTS)
+    lib = C.CDLL(pic.LIBRARY)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", pic.LIBRARY], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (pic_\w+)", out))
+    assert set(names) <= exported
+
+
+STRUCTS = {
+    "pic_rope_config": B.RopeConfig, "pic_kv_shape": B.KvShape, "pic_chunk": B.ChunkC,
+    "pic_entry": B.EntryC, "pic_request": B.RequestC, "pic_dst_geom": B.DstGeom,
+    "pic_kv_view": B.KvView, "pic_segment": B.SegmentC, "pic_plan_info_t": B.PlanInfo,
+}
+
+
+def test_struct_layout_matches_header(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "pic_stitch.h"',
+             "int main(void) {"]
+    for cname, cls in STRUCTS.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                               check=True).stdout.splitlines():
+        s, f, v = line.split()
+        got[(s, f)] = int(v)
+    for cname, cls in STRUCTS.items():
+        assert got[(cname, "size")] == C.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
+
+
+def test_calls_fail_cleanly_without_device_work():
+    """Invalid handles and views are refused before any device call."""
+    lib = B.load_library()
+    view = B.KvView(None, None, 0, 0, 0, 0, 0)
+    assert lib.pic_stitch(None, C.byref(view), C.byref(view), 0, 1, None) == B.PIC_ERR_STATE
+    assert b"plan" in lib.pic_last_error()
+    info = B.PlanInfo()
+    assert lib.pic_plan_info(None, C.byref(info)) == B.PIC_ERR_STATE
+    lib.pic_plan_destroy(None)  # no-op
+
+
+def test_last_error_is_thread_local():
+    import threading
+    lib = B.load_library()
+    lib.pic_plan_info(None, None)
+    seen = []
+
+    def other():
+        seen.append(lib.pic_last_error())
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [b""]
+    assert lib.pic_last_error() != b""
+
+
+@pytest.mark.parametrize("mod", ["oracle", "oracle.ref"])
+def test_product_does_not_import_oracle(mod):
+    """The library's package never imports the oracle."""
+    pkg = os.path.join(ROOT, "position_independent_kv_stitch_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text
+                assert "pic_oracle" not in text and "orc_" not in text
