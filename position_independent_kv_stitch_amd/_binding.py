@@ -87,17 +87,54 @@ class PlanInfo(C.Structure):
 
 
 _lib = None
+_runtime_checked = False
+
+
+def _hip_runtimes():
+    """Distinct HIP runtime files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def _check_single_runtime():
+    """torch ships its own HIP runtime under the same soname as the system's.
+    Tensors and streams handed to the library must belong to the runtime it
+    calls, so exactly one may be mapped."""
+    global _runtime_checked
+    if _runtime_checked:
+        return
+    paths = _hip_runtimes()
+    if len(paths) > 1:
+        raise ImportError("two HIP runtimes are loaded (" + ", ".join(sorted(paths)) +
+                          "): import torch before position_independent_kv_stitch_amd")
+    _runtime_checked = True
 
 
 def load_library():
-    """Load libpic_stitch.so; raise if it has not been built."""
+    """Load libpic_stitch.so; raise if it has not been built.
+
+    torch is imported first when it is installed, so that the library binds
+    to torch's HIP runtime (the one that owns the tensors and streams it is
+    given) rather than loading a second copy."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIBRARY):
         raise ImportError(f"{LIBRARY} is missing: build it with "
                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(LIBRARY)
+    _check_single_runtime()
     P = C.POINTER
     lib.pic_plan.restype = C.c_int
     lib.pic_plan.argtypes = [P(KvShape), P(RopeConfig), P(ChunkC), C.c_int32, P(RequestC),
@@ -269,6 +306,7 @@ def _view(k, v, kind: str) -> KvView:
 
 def _stream_of(t, stream):
     torch = _torch()
+    _check_single_runtime()
     if stream is None:
         stream = torch.cuda.current_stream(t.device)
     return C.c_void_p(stream.cuda_stream)

@@ -158,7 +158,7 @@ def test_errors_write_nothing(torch_cuda):
     mis = flat[1:1 + pk.numel()].view(pk.shape)  # 2-byte offset: misaligned
     mis.copy_(pk)
     with pytest.raises(pic.PicError) as e:
-        pic.stitch(plan, mis, pv, dk, dv)
+        pic.stitch(plan, mis, pv, dk, dv, 0, 1)
     assert e.value.name == "align"
     torch.cuda.synchronize()
     assert np.all(to_host(dk) == 0x7FC5) and np.all(to_host(dv) == 0x7FC5)
