@@ -55,6 +55,57 @@ def measured_traffic():
     return int(t.group(1))
 
 
+DEFAULT = "llama3-8b-paged"
+WORKLOADS = {
+    DEFAULT: "32 layers, 8 kv heads x 128, bf16, one request of 8 chunks x 2048 tokens after a "
+             "128-token prefix, 16-token pages, recompute_k 32 (stitch, paged)",
+    "rag-group": "batched RAG, one group of 4 of the 32 layers: 64 requests of 4..16 chunks from "
+                 "a 256-chunk pool of 128..4096 tokens, bf16, 16-token pages (stitch, paged)",
+    "mla": "DeepSeek-V3 MLA rows, 61 layers, 576-wide (512 copied + 64 rotated), bf16, 16 chunks "
+           "x 4096 tokens (stitch, contiguous)",
+    "inplace": "Qwen3-8B, 36 layers, 8 kv heads x 128, bf16, 131072 tokens, 64 segments rotated "
+               "in place by shifts in [-65536, 65536], recompute_k 16 (pic_rotate_inplace)",
+    "single-layer": "1 layer, 8 kv heads x 128, fp32, 3 chunks of 512/1024/256 tokens "
+                    "(stitch, contiguous; launch-bound)",
+}
+
+
+def setup_workload(name, torch, pic):
+    """Inputs resident on cuda:0 and a step function for one workload."""
+    from pic_workloads import (config1, config2, config3, config4, config5, normal_values,
+                               pool_values, sentinel_like)
+    log(f"workload {name}: generating inputs on cuda:0")
+    if name == "inplace":
+        wl = config5()
+        buf = normal_values(wl.buf_shape(), wl.dtype, 0, "cuda:0")
+        rot = [s for s in wl.segments if s.delta != 0]
+        tokens = sum(s.length - s.recompute_k for s in rot)
+        per_tl = wl.n_heads * wl.rope_dim * wl.esize * 2  # rotary slice read + written
+        return {"wl": wl, "step": lambda: pic.rotate_workload(wl, buf),
+                "bytes": tokens * per_tl * wl.n_layers, "token_layers": tokens * wl.n_layers,
+                "kernel": "stitch_kernel<bf16, half> (in place)", "plan": None,
+                "config": {"workload": WORKLOADS[name], "storage": "bf16",
+                           "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
+    wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
+          "rag-group": lambda: config3(n_layers=4)}[name]()
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
+    dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
+    dv = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0") if wl.has_v else None
+    plan = pic.Plan.from_workload(wl)
+    info = plan.info
+    step_bytes = (info["bytes_read_per_layer"] + info["bytes_written_per_layer"]) * wl.n_layers
+    cfg = {"workload": WORKLOADS[name], "storage": wl.dtype, "layers": wl.n_layers,
+           "kv_heads": wl.n_heads, "row_dim": wl.row_dim, "rope_dim": wl.rope_dim,
+           "rope_theta": wl.theta, "page_size": wl.page_size,
+           "requests": len(wl.requests), "entries": info["n_entries"],
+           "stitched_tokens": info["tokens_written"], "masked_tokens": info["tokens_masked"],
+           "parallelism": "single-gpu"}
+    kernel = f"stitch_kernel<{wl.dtype}, {wl.style}>"
+    return {"wl": wl, "step": lambda: pic.stitch(plan, pk, pv, dk, dv), "bytes": step_bytes,
+            "token_layers": info["tokens_written"] * wl.n_layers, "kernel": kernel,
+            "plan": plan, "info": info, "pk": pk, "pv": pv, "config": cfg}
+
+
 def cpu_baseline(wl, pk, pv, plan_info):
     """The oracle, as it is, over four full steps of the workload: one call
     per layer on a pool of host threads."""
@@ -123,6 +174,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS),
+                    help="the default is the workload the headline metric is quoted on; the "
+                         "others time the remaining paths")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures the single-GPU path only (asked for --gpus {args.gpus}); the "
@@ -133,21 +187,15 @@ def main():
     import torch
 
     import position_independent_kv_stitch_amd as pic
-    from pic_workloads import config2, pool_values, sentinel_like
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    wl = config2()
-    log(f"workload: {wl.name}, generating inputs on cuda:0")
-    pk, pv = pool_values(wl, seed=0, device="cuda:0")
-    dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
-    dv = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
-    plan = pic.Plan.from_workload(wl)
-    info = plan.info
-    step_bytes = (info["bytes_read_per_layer"] + info["bytes_written_per_layer"]) * wl.n_layers
-    step_tl = info["tokens_written"] * wl.n_layers
+    W = setup_workload(args.workload, torch, pic)
+    wl = W["wl"]
+    step = W["step"]
+    step_bytes, step_tl = W["bytes"], W["token_layers"]
 
     for _ in range(args.warmup):
-        pic.stitch(plan, pk, pv, dk, dv)
+        step()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -159,7 +207,7 @@ def main():
     t_start.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
-        pic.stitch(plan, pk, pv, dk, dv)
+        step()
         ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -183,31 +231,26 @@ def main():
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": "llama3-8b-shaped paged stitch: 32 layers, 8 kv heads x 128, "
-                               "bf16, 8 chunks x 2048 tokens after a 128-token prefix, "
-                               "16-token pages, recompute_k 32",
-                   "storage": "bf16", "layers": wl.n_layers, "kv_heads": wl.n_heads,
-                   "head_dim": wl.row_dim, "chunks": 8, "chunk_tokens": 2048, "prefix": 128,
-                   "page_size": wl.page_size, "recompute_k": 32, "rope_theta": wl.theta,
-                   "parallelism": "single-gpu"},
+        "config": W["config"],
         "token_layers_per_s": round(step_tl * args.steps / (total_ms * 1e-3), 1),
         "hbm_peak_frac": round(value / PEAK_GBS, 4),
         "bytes_per_step": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
-                     "kernel": "stitch_kernel<bf16, half>",
+                     "traffic": measured_traffic() if args.workload == DEFAULT else None,
+                     "kernel": W["kernel"],
                      "avg_launch_ms": round(avg_kernel_ms, 5),
                      "median_launch_ms": round(kernel_ms[len(kernel_ms) // 2], 5),
                      "algorithmic_bytes_per_launch": step_bytes},
     }
     if not args.no_copy_ceiling:
-        out["copy_ceiling"] = copy_ceiling(torch, step_bytes)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, pk, pv, info)
+        out["copy_ceiling"] = copy_ceiling(torch, min(step_bytes, 8 << 30))
+    if not args.no_cpu_baseline and args.workload == DEFAULT:
+        out["cpu_baseline"] = cpu_baseline(wl, W["pk"], W["pv"], W["info"])
     else:
         out["cpu_baseline"] = None
-    plan.destroy()
+    if W.get("plan") is not None:
+        W["plan"].destroy()
     print(json.dumps(out), flush=True)
 
 

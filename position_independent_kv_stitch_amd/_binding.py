@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIBRARY = os.path.join(HERE, "libpic_stitch.so")
+# PIC_STITCH_LIBRARY selects another build of the same library (same ABI).
+LIBRARY = os.environ.get("PIC_STITCH_LIBRARY") or os.path.join(HERE, "libpic_stitch.so")
 
 PIC_OK, PIC_ERR_INVALID_ARG, PIC_ERR_RANGE, PIC_ERR_OVERLAP = 0, 1, 2, 3
 PIC_ERR_ALIGN, PIC_ERR_DEVICE, PIC_ERR_NOMEM, PIC_ERR_STATE = 4, 5, 6, 7

@@ -13,8 +13,14 @@ namespace pic {
 
 constexpr uint32_t kPlanMagic = 0x50494350u;  // live plan
 constexpr uint32_t kDeadMagic = 0x44454144u;  // destroyed plan
-constexpr int kTileTokens = 64;               // tokens of one entry per work tile
-constexpr int kBlockThreads = 256;            // 4 wave64s per workgroup
+#ifndef PIC_TILE_TOKENS
+#define PIC_TILE_TOKENS 64
+#endif
+#ifndef PIC_BLOCK_THREADS
+#define PIC_BLOCK_THREADS 256
+#endif
+constexpr int kTileTokens = PIC_TILE_TOKENS;     // tokens of one entry per work tile
+constexpr int kBlockThreads = PIC_BLOCK_THREADS; // wave64s per workgroup x 64
 
 // Destination addressing of a plan.
 enum DstMode : int32_t { kContiguous = 0, kPaged = 1, kInPlace = 2 };

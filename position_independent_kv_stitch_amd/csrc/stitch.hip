@@ -177,11 +177,37 @@ __device__ __forceinline__ void rotate_interleaved(uint4 &a, const double *c, co
     a = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+#ifndef PIC_NT_LOADS
+#define PIC_NT_LOADS 0
+#endif
+#ifndef PIC_NT_STORES
+#define PIC_NT_STORES 0
+#endif
+#ifndef PIC_TOKENS_PER_STEP
+#define PIC_TOKENS_PER_STEP 1
+#endif
+
+// 16-byte global accesses; the pool is read once and the destination written
+// once per launch, so both may bypass cache retention (non-temporal hints).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint4 ld16(const void *base, int64_t elem, int esize) {
-    return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * esize);
+    const char *p = static_cast<const char *>(base) + elem * esize;
+#if PIC_NT_LOADS
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *reinterpret_cast<const uint4 *>(p);
+#endif
 }
 __device__ __forceinline__ void st16(void *base, int64_t elem, int esize, const uint4 &v) {
-    *reinterpret_cast<uint4 *>(static_cast<char *>(base) + elem * esize) = v;
+    char *p = static_cast<char *>(base) + elem * esize;
+#if PIC_NT_STORES
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(p));
+#else
+    *reinterpret_cast<uint4 *>(p) = v;
+#endif
 }
 
 // --------------------------------------------------------------- the kernel
@@ -264,57 +290,74 @@ __global__ void __launch_bounds__(kBlockThreads) stitch_kernel(const KArgs a) {
             cd[i] = h * a.d_head + inner;
         }
 
-        for (int t = tile.tok0 + wave; t < tile.tok0 + tile.ntok; t += kWaves) {
-            const int64_t srow = s_base + (ent.src_tok + t) * a.s_tok;
-            int64_t drow;
-            if (a.mode == kInPlace) {
-                drow = srow;
-            } else {
-                const int32_t pos = static_cast<int32_t>(ent.dst_pos) + t;
-                if (a.mode == kContiguous) {
-                    drow = d_base + ent.request * a.d_req + static_cast<int64_t>(pos) * a.d_tok;
+        constexpr int TPS = PIC_TOKENS_PER_STEP;
+        const int t_end = tile.tok0 + tile.ntok;
+        for (int t0 = tile.tok0 + wave * TPS; t0 < t_end; t0 += kWaves * TPS) {
+            int64_t srow[TPS], drow[TPS];
+            bool tv[TPS];
+#pragma unroll
+            for (int q = 0; q < TPS; q++) {
+                const int t = t0 + q;
+                tv[q] = t < t_end;
+                srow[q] = s_base + (ent.src_tok + t) * a.s_tok;
+                if (a.mode == kInPlace) {
+                    drow[q] = srow[q];
                 } else {
-                    int32_t lp, slot;
-                    if (a.page_shift >= 0) {
-                        lp = pos >> a.page_shift;
-                        slot = pos & (a.page_size - 1);
+                    const int32_t pos = static_cast<int32_t>(ent.dst_pos) + t;
+                    if (a.mode == kContiguous) {
+                        drow[q] = d_base + ent.request * a.d_req +
+                                  static_cast<int64_t>(pos) * a.d_tok;
                     } else {
-                        lp = pos / a.page_size;
-                        slot = pos - lp * a.page_size;
-                    }
-                    const int64_t phys = a.pages[ent.page_base + lp];
-                    drow = d_base + phys * a.d_page + static_cast<int64_t>(slot) * a.d_tok;
-                }
-            }
-
-            uint4 A[MAXR], B[MAXR], Cw[MAXC];
-#pragma unroll
-            for (int i = 0; i < MAXR; i++) {
-                if (rv[i]) {
-                    A[i] = ld16(sk, srow + rs[i], ES);
-                    if (STYLE == kHalf) B[i] = ld16(sk, srow + rs[i] + half_off, ES);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < MAXC; i++)
-                if (cv[i]) Cw[i] = ld16(isv[i] ? sv : sk, srow + cs_[i], ES);
-
-#pragma unroll
-            for (int i = 0; i < MAXR; i++) {
-                if (rv[i]) {
-                    if (STYLE == kHalf) {
-                        if (turn) rotate_half(A[i], B[i], c, s, E{});
-                        st16(dk, drow + rd[i], ES, A[i]);
-                        st16(dk, drow + rd[i] + half_off, ES, B[i]);
-                    } else {
-                        if (turn) rotate_interleaved(A[i], c, s, E{});
-                        st16(dk, drow + rd[i], ES, A[i]);
+                        int32_t lp, slot;
+                        if (a.page_shift >= 0) {
+                            lp = pos >> a.page_shift;
+                            slot = pos & (a.page_size - 1);
+                        } else {
+                            lp = pos / a.page_size;
+                            slot = pos - lp * a.page_size;
+                        }
+                        const int64_t phys = tv[q] ? a.pages[ent.page_base + lp] : 0;
+                        drow[q] = d_base + phys * a.d_page + static_cast<int64_t>(slot) * a.d_tok;
                     }
                 }
             }
+
+            uint4 A[TPS][MAXR], B[TPS][MAXR], Cw[TPS][MAXC];
 #pragma unroll
-            for (int i = 0; i < MAXC; i++)
-                if (cv[i]) st16(isv[i] ? dv : dk, drow + cd[i], ES, Cw[i]);
+            for (int q = 0; q < TPS; q++) {
+                if (!tv[q]) continue;
+#pragma unroll
+                for (int i = 0; i < MAXR; i++) {
+                    if (rv[i]) {
+                        A[q][i] = ld16(sk, srow[q] + rs[i], ES);
+                        if (STYLE == kHalf) B[q][i] = ld16(sk, srow[q] + rs[i] + half_off, ES);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < MAXC; i++)
+                    if (cv[i]) Cw[q][i] = ld16(isv[i] ? sv : sk, srow[q] + cs_[i], ES);
+            }
+
+#pragma unroll
+            for (int q = 0; q < TPS; q++) {
+                if (!tv[q]) continue;
+#pragma unroll
+                for (int i = 0; i < MAXR; i++) {
+                    if (rv[i]) {
+                        if (STYLE == kHalf) {
+                            if (turn) rotate_half(A[q][i], B[q][i], c, s, E{});
+                            st16(dk, drow[q] + rd[i], ES, A[q][i]);
+                            st16(dk, drow[q] + rd[i] + half_off, ES, B[q][i]);
+                        } else {
+                            if (turn) rotate_interleaved(A[q][i], c, s, E{});
+                            st16(dk, drow[q] + rd[i], ES, A[q][i]);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < MAXC; i++)
+                    if (cv[i]) st16(isv[i] ? dv : dk, drow[q] + cd[i], ES, Cw[q][i]);
+            }
         }
     }
 }
