@@ -171,6 +171,8 @@ typedef struct pic_plan_info_t {
     int64_t pool_tokens_required; /* max token_start + length over chunks */
     int64_t bytes_read_per_layer; /* algorithmic: rows read */
     int64_t bytes_written_per_layer;
+    int64_t tile_tokens;          /* most tokens of one work tile (paged tiles also stop at
+                                     page ends) */
 } pic_plan_info_t;
 
 typedef struct pic_plan pic_plan_t;

@@ -81,7 +81,8 @@ class SegmentC(C.Structure):
 class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "n_requests", "n_entries", "n_tiles", "tokens_written", "tokens_masked",
-        "pool_tokens_required", "bytes_read_per_layer", "bytes_written_per_layer")]
+        "pool_tokens_required", "bytes_read_per_layer", "bytes_written_per_layer",
+        "tile_tokens")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -14,33 +14,35 @@ namespace pic {
 constexpr uint32_t kPlanMagic = 0x50494350u;  // live plan
 constexpr uint32_t kDeadMagic = 0x44454144u;  // destroyed plan
 #ifndef PIC_TILE_TOKENS
-#define PIC_TILE_TOKENS 64
+#define PIC_TILE_TOKENS 16
 #endif
 #ifndef PIC_BLOCK_THREADS
 #define PIC_BLOCK_THREADS 256
 #endif
-constexpr int kTileTokens = PIC_TILE_TOKENS;     // tokens of one entry per work tile
+constexpr int kTileSteps = PIC_TILE_TOKENS / 4;  // wave steps per tile (4 waves)
 constexpr int kBlockThreads = PIC_BLOCK_THREADS; // wave64s per workgroup x 64
 
 // Destination addressing of a plan.
 enum DstMode : int32_t { kContiguous = 0, kPaged = 1, kInPlace = 2 };
 
-// One work tile: tokens [tok0, tok0 + ntok) of entry `entry`.
+// One work tile: ntok consecutive tokens of one placed chunk that land in
+// consecutive destination rows (a paged tile never crosses a page).  The
+// kernel reads it for every layer of a launch.
 struct DevTile {
-    int32_t entry;
-    int32_t tok0;
+    int64_t src_row;  // pool token of the tile's first token
+    int64_t dst_a;    // contiguous: request; paged: physical page; in place: unused
+    int32_t dst_b;    // contiguous: position; paged: slot in the page; in place: unused
     int32_t ntok;
+    int32_t cs_idx;   // shift table, -1 = delta 0 (rows copied)
     int32_t pad;
 };
 
-// One placement as the kernel reads it.  src_tok is the pool row of the
-// entry's token 0, dst_pos its logical position (in place: unused);
-// cs_idx selects the shift table (-1 = delta 0, rows are copied).
-struct DevEntry {
+// Host-side record of one placement (entry of a request, or in-place segment).
+struct HostEntry {
     int64_t src_tok;
     int64_t dst_pos;
     int32_t request;
-    int32_t page_base;  // first entry of the request's page table (paged)
+    int32_t page_base;
     int32_t cs_idx;
     int32_t pad;
 };
@@ -56,6 +58,12 @@ struct Units {
     int32_t nv, vph;    // V units per token / per head
 };
 
+// Per-lane slot shape of a launch: MAXR rotary and MAXC copy units per lane,
+// g tokens per wave step, nblk unit blocks per step.
+struct Launch {
+    int32_t maxr = 1, maxc = 2, g = 1, nblk = 1;
+};
+
 struct Problem {
     pic_kv_shape shape{};
     int32_t rope_dim = 0;
@@ -66,10 +74,11 @@ struct Problem {
     int64_t num_phys_pages = 0;
     int32_t n_requests = 0;
     Units u{};
-    std::vector<DevEntry> entries;
+    Launch launch{};
+    int32_t tile_tokens = 0;
+    std::vector<HostEntry> entries;
     std::vector<DevTile> tiles;
     std::vector<double> cs;       // [table][rope_dim/2][cos, sin]
-    std::vector<int32_t> pages;   // page tables, request after request
     std::vector<int64_t> bounds;  // [entry][request, begin, end]
     std::vector<int64_t> recompute;
     pic_plan_info_t info{};
@@ -78,7 +87,7 @@ struct Problem {
 // Everything the device needs, packed into one upload.
 struct Staged {
     std::vector<uint8_t> bytes;
-    size_t off_tiles = 0, off_entries = 0, off_cs = 0, off_pages = 0;
+    size_t off_tiles = 0, off_cs = 0;
 };
 
 // Thread-local error reporting.
@@ -88,6 +97,9 @@ pic_status fail(pic_status st, const char *fmt, ...);
 // Shape/rope validation and work-unit derivation.
 pic_status derive_units(const pic_kv_shape *shape, const pic_rope_config *rope, bool inplace,
                         Units *u);
+
+// Slot shape of the kernel for a dtype and unit counts.
+Launch launch_shape_of(int32_t dtype, const Units &u);
 
 // Copy-mode and in-place problem builders (host only).
 pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,

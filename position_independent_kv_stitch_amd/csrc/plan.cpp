@@ -100,6 +100,30 @@ pic_status derive_units(const pic_kv_shape *shape, const pic_rope_config *rope, 
     return PIC_OK;
 }
 
+// A wave step takes g consecutive tokens of a tile and deals their rotary
+// units (g * nr) and copy units (g * (nck + nv)) to its 64 lanes, MAXR and
+// MAXC per lane.  Rows with few copy units (MLA: 4 rotary + 64 copy units
+// in bf16) take the wider copy shape, so one step spans several tokens and
+// every lane still has several 16-byte words in flight.
+Launch launch_shape_of(int32_t dtype, const Units &u) {
+    Launch l;
+    const int ncv = u.nck + u.nv;
+    if (dtype == PIC_DTYPE_BF16) {
+        l.maxr = 1;
+        l.maxc = (ncv > 0 && ncv <= 64) ? 4 : 2;
+    } else {
+        l.maxr = u.nr <= 64 ? 1 : 2;
+        l.maxc = 4;
+    }
+    int g = (64 * l.maxr) / u.nr;
+    if (ncv > 0) g = std::min(g, (64 * l.maxc) / ncv);
+    l.g = std::max(1, std::min(g, 8));
+    const int rb = (l.g * u.nr + 64 * l.maxr - 1) / (64 * l.maxr);
+    const int cb = (l.g * ncv + 64 * l.maxc - 1) / (64 * l.maxc);
+    l.nblk = std::max(rb, cb);
+    return l;
+}
+
 namespace {
 
 // cos/sin of delta * theta_i for i < rope_dim/2, in fp64 (libm), appended to cs.
@@ -145,11 +169,32 @@ void fill_info(Problem *p, int64_t tokens_written, int64_t tokens_masked, int64_
     p->info.pool_tokens_required = pool_need;
     p->info.bytes_read_per_layer = tokens_written * per_token;
     p->info.bytes_written_per_layer = tokens_written * per_token;
+    p->info.tile_tokens = p->tile_tokens;
 }
 
-void add_tiles(Problem *p, int32_t entry, int32_t from, int32_t to) {
-    for (int32_t t = from; t < to; t += kTileTokens)
-        p->tiles.push_back(DevTile{entry, t, std::min(kTileTokens, to - t), 0});
+// Tiles of tokens [from, to) of one placement: at most tile_tokens tokens,
+// and in a paged destination never across a page, so each tile has one
+// destination row base and consecutive rows after it.
+void add_tiles(Problem *p, const HostEntry &e, const int32_t *page_table, int32_t from,
+               int32_t to) {
+    int32_t t = from;
+    while (t < to) {
+        int32_t n = std::min(p->tile_tokens, to - t);
+        DevTile tile{e.src_tok + t, 0, 0, 0, e.cs_idx, 0};
+        if (p->mode == kPaged) {
+            const int64_t pos = e.dst_pos + t;
+            const int32_t slot = static_cast<int32_t>(pos % p->page_size);
+            n = std::min<int32_t>(n, p->page_size - slot);
+            tile.dst_a = page_table[pos / p->page_size];
+            tile.dst_b = slot;
+        } else if (p->mode == kContiguous) {
+            tile.dst_a = e.request;
+            tile.dst_b = static_cast<int32_t>(e.dst_pos + t);
+        }
+        tile.ntok = n;
+        p->tiles.push_back(tile);
+        t += n;
+    }
 }
 
 }  // namespace
@@ -263,12 +308,12 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.num_phys_pages = dst->num_phys_pages;
     p.n_requests = n_requests;
     p.u = u;
+    p.launch = launch_shape_of(shape->dtype, u);
+    p.tile_tokens = kTileSteps * 4 * p.launch.g;
     std::unordered_map<int64_t, int32_t> table_of_delta;
     int64_t written = 0, masked = 0;
     for (int r = 0; r < n_requests; r++) {
         const pic_request &rq = requests[r];
-        const int32_t page_base = static_cast<int32_t>(p.pages.size());
-        if (paged) p.pages.insert(p.pages.end(), rq.page_table, rq.page_table + rq.n_pages);
         for (int j = 0; j < rq.n_entries; j++) {
             const pic_entry &e = rq.entries[j];
             const pic_chunk &c = chunks[e.chunk_id];
@@ -284,9 +329,9 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
                     cs_idx = it->second;
                 }
             }
-            const int32_t idx = static_cast<int32_t>(p.entries.size());
-            p.entries.push_back(DevEntry{c.token_start, e.dst_offset, r, page_base, cs_idx, 0});
-            add_tiles(&p, idx, e.recompute_k, e.length);
+            const HostEntry he{c.token_start, e.dst_offset, r, 0, cs_idx, 0};
+            p.entries.push_back(he);
+            add_tiles(&p, he, paged ? rq.page_table : nullptr, e.recompute_k, e.length);
             p.bounds.insert(p.bounds.end(), {r, e.dst_offset, e.dst_offset + e.length});
             p.recompute.insert(p.recompute.end(), {r, e.dst_offset, e.dst_offset + e.recompute_k});
             written += e.length - e.recompute_k;
@@ -331,6 +376,8 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.capacity = buf_tokens;
     p.n_requests = 1;
     p.u = u;
+    p.launch = launch_shape_of(shape->dtype, u);
+    p.tile_tokens = kTileSteps * 4 * p.launch.g;
     std::unordered_map<int64_t, int32_t> table_of_delta;
     int64_t written = 0, masked = 0;
     for (int g = 0; g < n_segments; g++) {
@@ -348,9 +395,9 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
         } else {
             cs_idx = it->second;
         }
-        const int32_t idx = static_cast<int32_t>(p.entries.size());
-        p.entries.push_back(DevEntry{s.token_start, s.token_start, 0, 0, cs_idx, 0});
-        add_tiles(&p, idx, s.recompute_k, s.length);
+        const HostEntry he{s.token_start, s.token_start, 0, 0, cs_idx, 0};
+        p.entries.push_back(he);
+        add_tiles(&p, he, nullptr, s.recompute_k, s.length);
         written += s.length - s.recompute_k;
     }
     fill_info(&p, written, masked, buf_tokens);
@@ -361,23 +408,13 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
 Staged stage(const Problem &p) {
     Staged s;
     auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-    size_t at = 0;
-    s.off_tiles = at;
-    at = align(at + p.tiles.size() * sizeof(DevTile));
-    s.off_entries = at;
-    at = align(at + p.entries.size() * sizeof(DevEntry));
-    s.off_cs = at;
-    at = align(at + p.cs.size() * sizeof(double));
-    s.off_pages = at;
-    at = align(at + p.pages.size() * sizeof(int32_t));
-    s.bytes.assign(std::max<size_t>(at, 256), 0);
+    s.off_tiles = 0;
+    s.off_cs = align(p.tiles.size() * sizeof(DevTile));
+    const size_t total = align(s.off_cs + p.cs.size() * sizeof(double));
+    s.bytes.assign(std::max<size_t>(total, 256), 0);
     if (!p.tiles.empty())
         std::memcpy(&s.bytes[s.off_tiles], p.tiles.data(), p.tiles.size() * sizeof(DevTile));
-    if (!p.entries.empty())
-        std::memcpy(&s.bytes[s.off_entries], p.entries.data(), p.entries.size() * sizeof(DevEntry));
     if (!p.cs.empty()) std::memcpy(&s.bytes[s.off_cs], p.cs.data(), p.cs.size() * sizeof(double));
-    if (!p.pages.empty())
-        std::memcpy(&s.bytes[s.off_pages], p.pages.data(), p.pages.size() * sizeof(int32_t));
     return s;
 }
 

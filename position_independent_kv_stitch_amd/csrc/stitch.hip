@@ -41,6 +41,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 #include <memory>
 
@@ -53,25 +54,22 @@ namespace {
 
 struct KArgs {
     const DevTile *tiles;
-    const DevEntry *entries;
     const double *cs;
-    const int32_t *pages;
     const void *src_k;
     const void *src_v;
     void *dst_k;
     void *dst_v;
-    int64_t s_layer, s_tok, s_head;                  // source strides
-    int64_t d_layer, d_tok, d_head, d_page, d_req;   // destination strides
+    int64_t s_layer, s_tok, s_head;                 // source strides
+    int64_t d_layer, d_tok, d_head, d_page, d_req;  // destination strides
     int32_t layer_begin;
-    int32_t mode;  // DstMode
-    int32_t page_size;
-    int32_t page_shift;  // log2(page_size) when a power of two, else -1
+    int32_t mode;         // DstMode
     int32_t rope_offset;
     int32_t half_r;
-    int32_t nr, uph_shift;  // rotary units
-    int32_t nck, cph;       // K copy units
-    int32_t nv, vph;        // V units
-    int32_t nblk;           // unit blocks per token row
+    int32_t nr, uph_shift;  // rotary units per token, log2(units per head)
+    int32_t nck, cph;       // K copy units per token / per head
+    int32_t nv, vph;        // V units per token / per head
+    int32_t g;              // tokens per wave step
+    int32_t nblk;           // unit blocks per step (1 unless a row is very wide)
 };
 
 constexpr int kHalf = PIC_ROPE_HALF;
@@ -120,23 +118,21 @@ struct Vec<uint16_t> {
     static constexpr int kElems = 8;
 };
 
-// HALF pairing: word a holds x of planes p0..p0+VEC-1, word b their y.
+// HALF pairing: word a holds x of planes p0..p0+VEC-1, word b their y;
+// c[p], s[p] = cos, sin of plane p0 + p.
 __device__ __forceinline__ void rotate_half(uint4 &a, uint4 &b, const double *c, const double *s,
                                             float) {
-    double x[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                   __uint_as_float(a.w)};
-    double y[4] = {__uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z),
-                   __uint_as_float(b.w)};
-    float xo[4], yo[4];
+    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
+    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+    uint32_t ao[4], bo[4];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
-        xo[e] = static_cast<float>(x[e] * c[e] - y[e] * s[e]);
-        yo[e] = static_cast<float>(x[e] * s[e] + y[e] * c[e]);
+        const double x = __uint_as_float(aw[e]), y = __uint_as_float(bw[e]);
+        ao[e] = __float_as_uint(static_cast<float>(x * c[e] - y * s[e]));
+        bo[e] = __float_as_uint(static_cast<float>(x * s[e] + y * c[e]));
     }
-    a = make_uint4(__float_as_uint(xo[0]), __float_as_uint(xo[1]), __float_as_uint(xo[2]),
-                   __float_as_uint(xo[3]));
-    b = make_uint4(__float_as_uint(yo[0]), __float_as_uint(yo[1]), __float_as_uint(yo[2]),
-                   __float_as_uint(yo[3]));
+    a = make_uint4(ao[0], ao[1], ao[2], ao[3]);
+    b = make_uint4(bo[0], bo[1], bo[2], bo[3]);
 }
 
 __device__ __forceinline__ void rotate_half(uint4 &a, uint4 &b, const double *c, const double *s,
@@ -183,9 +179,6 @@ __device__ __forceinline__ void rotate_interleaved(uint4 &a, const double *c, co
 #ifndef PIC_NT_STORES
 #define PIC_NT_STORES 0
 #endif
-#ifndef PIC_TOKENS_PER_STEP
-#define PIC_TOKENS_PER_STEP 1
-#endif
 
 // 16-byte global accesses; the pool is read once and the destination written
 // once per launch, so both may bypass cache retention (non-temporal hints).
@@ -212,37 +205,47 @@ __device__ __forceinline__ void st16(void *base, int64_t elem, int esize, const 
 
 // --------------------------------------------------------------- the kernel
 
-// MAXR rotary units and MAXC copy units per lane per block of units.
+#ifndef PIC_WAVES_PER_EU
+#define PIC_WAVES_PER_EU 0
+#endif
+#if PIC_WAVES_PER_EU > 0
+#define PIC_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(PIC_WAVES_PER_EU)))
+#else
+#define PIC_OCCUPANCY_HINT
+#endif
+
+// One workgroup of four wave64s per (tile, layer).  A tile is up to 16 wave
+// steps of consecutive tokens of one placed chunk landing in consecutive
+// destination rows; a wave step covers g tokens, whose rotary units (g * nr)
+// and copy units (g * (nck + nv)) are dealt to the 64 lanes, MAXR and MAXC
+// per lane.  Each lane's slot offsets and the cos/sin of its planes are set
+// up once per workgroup; all of a step's loads are issued before its stores.
 template <typename E, int STYLE, int MAXR, int MAXC>
-__global__ void __launch_bounds__(kBlockThreads) stitch_kernel(const KArgs a) {
+__global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kernel(const KArgs a) {
     constexpr int VEC = Vec<E>::kElems;
     constexpr int ES = sizeof(E);
     constexpr int NCS = STYLE == kHalf ? VEC : VEC / 2;  // planes per rotary unit
+    constexpr int kWaves = kBlockThreads / 64;
+    constexpr int kNone = 1 << 30;                       // slot token index: unused slot
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    constexpr int kWaves = kBlockThreads / 64;
+    const int ncv = a.nck + a.nv;
+    const int half_off = STYLE == kHalf ? a.half_r : 0;
 
-    const DevTile tile = a.tiles[blockIdx.x];
-    const DevEntry ent = a.entries[tile.entry];
+    const DevTile T = a.tiles[blockIdx.x];
     const int64_t layer = a.layer_begin + static_cast<int64_t>(blockIdx.y);
-    const bool turn = ent.cs_idx >= 0;
+    const bool turn = T.cs_idx >= 0;
 
-    // cos/sin of the planes this lane's rotary units cover (uph divides 64,
-    // so the plane group is the same for all of the lane's units)
+    // cos/sin of this lane's planes: the same for all of its rotary units,
+    // because the rotary units per head (a power of two) divide 64
     double c[NCS], s[NCS];
     if (turn) {
-        const int j = lane & ((1 << a.uph_shift) - 1);
-        const double *t = a.cs + (static_cast<int64_t>(ent.cs_idx) * a.half_r + j * NCS) * 2;
+        const int plane0 = (lane & ((1 << a.uph_shift) - 1)) * NCS;
+        const double *t = a.cs + (static_cast<int64_t>(T.cs_idx) * a.half_r + plane0) * 2;
 #pragma unroll
         for (int p = 0; p < NCS; p++) {
             c[p] = t[2 * p];
             s[p] = t[2 * p + 1];
-        }
-    } else {
-#pragma unroll
-        for (int p = 0; p < NCS; p++) {
-            c[p] = 1.0;
-            s[p] = 0.0;
         }
     }
 
@@ -250,147 +253,131 @@ __global__ void __launch_bounds__(kBlockThreads) stitch_kernel(const KArgs a) {
     const void *sv = a.src_v;
     void *dk = a.dst_k;
     void *dv = a.dst_v;
-    const int64_t s_base = layer * a.s_layer;
-    const int64_t d_base = layer * a.d_layer;
-    const int64_t half_off = STYLE == kHalf ? a.half_r : 0;
+    const int64_t s0 = layer * a.s_layer + T.src_row * a.s_tok;
+    int64_t d0;
+    if (a.mode == kInPlace)
+        d0 = s0;
+    else
+        d0 = layer * a.d_layer + T.dst_a * (a.mode == kPaged ? a.d_page : a.d_req) +
+             static_cast<int64_t>(T.dst_b) * a.d_tok;
 
     for (int blk = 0; blk < a.nblk; blk++) {
-        // this lane's unit offsets inside a source row (rs, cs_) and inside a
-        // destination row (rd, cd); heads may be laid out differently
-        int64_t rs[MAXR], rd[MAXR];
-        bool rv[MAXR];
+        int rs[MAXR], rd[MAXR];  // slot offsets from the step's first source/dest row
+        int rq[MAXR];            // token of the step the slot belongs to
 #pragma unroll
         for (int i = 0; i < MAXR; i++) {
-            const int u = blk * 64 * MAXR + lane + 64 * i;
-            rv[i] = u < a.nr;
-            const int h = u >> a.uph_shift;
-            const int j = u & ((1 << a.uph_shift) - 1);
-            const int inner = a.rope_offset + j * VEC;
-            rs[i] = h * a.s_head + inner;
-            rd[i] = h * a.d_head + inner;
+            const int u = (blk * MAXR + i) * 64 + lane;
+            rq[i] = kNone;
+            rs[i] = rd[i] = 0;
+            if (u < a.g * a.nr) {
+                const int q = u / a.nr;
+                const int r = u - q * a.nr;
+                const int h = r >> a.uph_shift;
+                const int inner = a.rope_offset + (r & ((1 << a.uph_shift) - 1)) * VEC;
+                rq[i] = q;
+                rs[i] = static_cast<int>(q * a.s_tok + h * a.s_head + inner);
+                rd[i] = static_cast<int>(q * a.d_tok + h * a.d_head + inner);
+            }
         }
-        int64_t cs_[MAXC], cd[MAXC];
-        bool cv[MAXC], isv[MAXC];
+        int cs_[MAXC], cd[MAXC];
+        int cq[MAXC];
+        bool isv[MAXC];
 #pragma unroll
         for (int i = 0; i < MAXC; i++) {
-            const int u = blk * 64 * MAXC + lane + 64 * i;
-            cv[i] = u < a.nck + a.nv;
-            isv[i] = u >= a.nck;
-            int h, inner;
-            if (!isv[i]) {
-                h = a.cph ? u / a.cph : 0;
-                inner = (u - h * a.cph) * VEC;
-                if (inner >= a.rope_offset) inner += 2 * a.half_r;  // skip the rotary slice
-            } else {
-                const int u2 = u - a.nck;
-                h = a.vph ? u2 / a.vph : 0;
-                inner = (u2 - h * a.vph) * VEC;
+            const int u = (blk * MAXC + i) * 64 + lane;
+            cq[i] = kNone;
+            cs_[i] = cd[i] = 0;
+            isv[i] = false;
+            if (u < a.g * ncv) {
+                const int q = u / ncv;
+                const int r = u - q * ncv;
+                int h, inner;
+                if (r < a.nck) {
+                    h = r / a.cph;
+                    inner = (r - h * a.cph) * VEC;
+                    if (inner >= a.rope_offset) inner += 2 * a.half_r;  // skip the rotary slice
+                } else {
+                    const int r2 = r - a.nck;
+                    h = r2 / a.vph;
+                    inner = (r2 - h * a.vph) * VEC;
+                    isv[i] = true;
+                }
+                cq[i] = q;
+                cs_[i] = static_cast<int>(q * a.s_tok + h * a.s_head + inner);
+                cd[i] = static_cast<int>(q * a.d_tok + h * a.d_head + inner);
             }
-            cs_[i] = h * a.s_head + inner;
-            cd[i] = h * a.d_head + inner;
         }
 
-        constexpr int TPS = PIC_TOKENS_PER_STEP;
-        const int t_end = tile.tok0 + tile.ntok;
-        for (int t0 = tile.tok0 + wave * TPS; t0 < t_end; t0 += kWaves * TPS) {
-            int64_t srow[TPS], drow[TPS];
-            bool tv[TPS];
+        for (int t0 = wave * a.g; t0 < T.ntok; t0 += kWaves * a.g) {
+            const int lim = T.ntok - t0;  // slots of tokens q < lim are live
+            const int64_t sb = s0 + t0 * a.s_tok;
+            const int64_t db = d0 + t0 * a.d_tok;
+            uint4 A[MAXR], B[MAXR], Cw[MAXC];
 #pragma unroll
-            for (int q = 0; q < TPS; q++) {
-                const int t = t0 + q;
-                tv[q] = t < t_end;
-                srow[q] = s_base + (ent.src_tok + t) * a.s_tok;
-                if (a.mode == kInPlace) {
-                    drow[q] = srow[q];
-                } else {
-                    const int32_t pos = static_cast<int32_t>(ent.dst_pos) + t;
-                    if (a.mode == kContiguous) {
-                        drow[q] = d_base + ent.request * a.d_req +
-                                  static_cast<int64_t>(pos) * a.d_tok;
+            for (int i = 0; i < MAXR; i++) {
+                if (rq[i] < lim) {
+                    A[i] = ld16(sk, sb + rs[i], ES);
+                    if (STYLE == kHalf) B[i] = ld16(sk, sb + rs[i] + half_off, ES);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MAXC; i++)
+                if (cq[i] < lim) Cw[i] = ld16(isv[i] ? sv : sk, sb + cs_[i], ES);
+#pragma unroll
+            for (int i = 0; i < MAXR; i++) {
+                if (rq[i] < lim) {
+                    if (STYLE == kHalf) {
+                        if (turn) rotate_half(A[i], B[i], c, s, E{});
+                        st16(dk, db + rd[i], ES, A[i]);
+                        st16(dk, db + rd[i] + half_off, ES, B[i]);
                     } else {
-                        int32_t lp, slot;
-                        if (a.page_shift >= 0) {
-                            lp = pos >> a.page_shift;
-                            slot = pos & (a.page_size - 1);
-                        } else {
-                            lp = pos / a.page_size;
-                            slot = pos - lp * a.page_size;
-                        }
-                        const int64_t phys = tv[q] ? a.pages[ent.page_base + lp] : 0;
-                        drow[q] = d_base + phys * a.d_page + static_cast<int64_t>(slot) * a.d_tok;
+                        if (turn) rotate_interleaved(A[i], c, s, E{});
+                        st16(dk, db + rd[i], ES, A[i]);
                     }
                 }
             }
-
-            uint4 A[TPS][MAXR], B[TPS][MAXR], Cw[TPS][MAXC];
 #pragma unroll
-            for (int q = 0; q < TPS; q++) {
-                if (!tv[q]) continue;
-#pragma unroll
-                for (int i = 0; i < MAXR; i++) {
-                    if (rv[i]) {
-                        A[q][i] = ld16(sk, srow[q] + rs[i], ES);
-                        if (STYLE == kHalf) B[q][i] = ld16(sk, srow[q] + rs[i] + half_off, ES);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < MAXC; i++)
-                    if (cv[i]) Cw[q][i] = ld16(isv[i] ? sv : sk, srow[q] + cs_[i], ES);
-            }
-
-#pragma unroll
-            for (int q = 0; q < TPS; q++) {
-                if (!tv[q]) continue;
-#pragma unroll
-                for (int i = 0; i < MAXR; i++) {
-                    if (rv[i]) {
-                        if (STYLE == kHalf) {
-                            if (turn) rotate_half(A[q][i], B[q][i], c, s, E{});
-                            st16(dk, drow[q] + rd[i], ES, A[q][i]);
-                            st16(dk, drow[q] + rd[i] + half_off, ES, B[q][i]);
-                        } else {
-                            if (turn) rotate_interleaved(A[q][i], c, s, E{});
-                            st16(dk, drow[q] + rd[i], ES, A[q][i]);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < MAXC; i++)
-                    if (cv[i]) st16(isv[i] ? dv : dk, drow[q] + cd[i], ES, Cw[q][i]);
-            }
+            for (int i = 0; i < MAXC; i++)
+                if (cq[i] < lim) st16(isv[i] ? dv : dk, db + cd[i], ES, Cw[i]);
         }
     }
 }
 
 // ----------------------------------------------------------------- launch
 
-template <typename E, int STYLE>
-hipError_t launch_typed(const KArgs &a, int n_tiles, int n_layers, hipStream_t stream) {
-    constexpr int MAXR = sizeof(E) == 2 ? 1 : 2;
-    constexpr int MAXC = sizeof(E) == 2 ? 2 : 4;
+// The kernel keeps a step's slot offsets in 32 bits: g token rows and all
+// heads of a view must span fewer than 2^31 elements.
+bool slot_offsets_fit(const Problem &p, int64_t tok, int64_t head) {
+    const int64_t span = (p.launch.g - 1) * tok +
+                         static_cast<int64_t>(p.shape.num_heads - 1) * head + p.shape.row_dim;
+    return span <= INT32_MAX;
+}
+
+template <typename E, int STYLE, int MAXR, int MAXC>
+hipError_t launch_kernel(const KArgs &a, int n_tiles, int n_layers, hipStream_t stream) {
     dim3 grid(static_cast<unsigned>(n_tiles), static_cast<unsigned>(n_layers));
     hipLaunchKernelGGL((stitch_kernel<E, STYLE, MAXR, MAXC>), grid, dim3(kBlockThreads), 0,
                        stream, a);
     return hipGetLastError();
 }
 
-int max_rot_units(int dtype) { return dtype == PIC_DTYPE_BF16 ? 1 : 2; }
-int max_copy_units(int dtype) { return dtype == PIC_DTYPE_BF16 ? 2 : 4; }
-
-hipError_t launch(const Problem &p, const KArgs &base, int n_layers, hipStream_t stream) {
-    KArgs a = base;
+template <typename E, int STYLE>
+hipError_t launch_style(const Problem &p, const KArgs &a, int n_layers, hipStream_t stream) {
     const int n_tiles = static_cast<int>(p.tiles.size());
-    const int mr = 64 * max_rot_units(p.shape.dtype);
-    const int mc = 64 * max_copy_units(p.shape.dtype);
-    const int rb = (p.u.nr + mr - 1) / mr;
-    const int cb = (p.u.nck + p.u.nv + mc - 1) / mc;
-    a.nblk = rb > cb ? rb : cb;
-    if (p.shape.dtype == PIC_DTYPE_F32) {
-        return p.style == PIC_ROPE_HALF ? launch_typed<float, PIC_ROPE_HALF>(a, n_tiles, n_layers, stream)
-                                        : launch_typed<float, PIC_ROPE_INTERLEAVED>(a, n_tiles, n_layers, stream);
-    }
-    return p.style == PIC_ROPE_HALF ? launch_typed<uint16_t, PIC_ROPE_HALF>(a, n_tiles, n_layers, stream)
-                                    : launch_typed<uint16_t, PIC_ROPE_INTERLEAVED>(a, n_tiles, n_layers, stream);
+    const Launch &l = p.launch;
+    if (l.maxr == 1 && l.maxc == 2) return launch_kernel<E, STYLE, 1, 2>(a, n_tiles, n_layers, stream);
+    if (l.maxr == 1) return launch_kernel<E, STYLE, 1, 4>(a, n_tiles, n_layers, stream);
+    return launch_kernel<E, STYLE, 2, 4>(a, n_tiles, n_layers, stream);
+}
+
+hipError_t launch(const Problem &p, KArgs a, int n_layers, hipStream_t stream) {
+    a.g = p.launch.g;
+    a.nblk = p.launch.nblk;
+    if (p.shape.dtype == PIC_DTYPE_F32)
+        return p.style == PIC_ROPE_HALF ? launch_style<float, PIC_ROPE_HALF>(p, a, n_layers, stream)
+                                        : launch_style<float, PIC_ROPE_INTERLEAVED>(p, a, n_layers, stream);
+    return p.style == PIC_ROPE_HALF ? launch_style<uint16_t, PIC_ROPE_HALF>(p, a, n_layers, stream)
+                                    : launch_style<uint16_t, PIC_ROPE_INTERLEAVED>(p, a, n_layers, stream);
 }
 
 pic_status hip_fail(hipError_t e, const char *what) {
@@ -417,22 +404,11 @@ pic_status check_view(const pic_kv_view *v, int vec, bool need_v, const char *na
     return PIC_OK;
 }
 
-int page_shift_of(int32_t ps) {
-    if (ps <= 0 || (ps & (ps - 1))) return -1;
-    int s = 0;
-    while ((1 << s) < ps) s++;
-    return s;
-}
-
 KArgs args_for(const Problem &p, const uint8_t *dmem, const Staged &stg) {
     KArgs a{};
     a.tiles = reinterpret_cast<const DevTile *>(dmem + stg.off_tiles);
-    a.entries = reinterpret_cast<const DevEntry *>(dmem + stg.off_entries);
     a.cs = reinterpret_cast<const double *>(dmem + stg.off_cs);
-    a.pages = reinterpret_cast<const int32_t *>(dmem + stg.off_pages);
     a.mode = p.mode;
-    a.page_size = p.page_size;
-    a.page_shift = page_shift_of(p.page_size);
     a.rope_offset = p.shape.rope_offset;
     a.half_r = p.u.half_r;
     a.nr = p.u.nr;
@@ -473,6 +449,10 @@ pic_status pic_stitch(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_vi
         dst->request_stride < p.capacity * dst->token_stride)
         return fail(PIC_ERR_OVERLAP, "dst view: request_stride smaller than capacity rows, "
                     "requests would alias");
+    if (!slot_offsets_fit(p, pool->token_stride, pool->head_stride) ||
+        !slot_offsets_fit(p, dst->token_stride, dst->head_stride))
+        return fail(PIC_ERR_RANGE, "a view's token/head strides span 2^31 elements or more "
+                    "within one step");
     if (p.tiles.empty() || layer_begin == layer_end) return PIC_OK;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -538,6 +518,9 @@ pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *
                     layer_end, p.shape.num_layers);
     st = check_view(buf, p.u.vec, false, "buf");
     if (st) return st;
+    if (!slot_offsets_fit(p, buf->token_stride, buf->head_stride))
+        return fail(PIC_ERR_RANGE, "the view's token/head strides span 2^31 elements or more "
+                    "within one step");
     if (p.tiles.empty() || layer_begin == layer_end) return PIC_OK;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);

@@ -139,7 +139,18 @@ def test_info_and_ranges_match_definitions(cfg):
     row_bytes = wl.n_heads * wl.row_dim * wl.esize * (2 if wl.has_v else 1)
     assert p.info["bytes_read_per_layer"] == written * row_bytes
     assert p.info["bytes_written_per_layer"] == written * row_bytes
-    assert p.info["n_tiles"] == sum(-(-(e.length - e.recompute_k) // 64) for e in ents)
+    tiles = 0  # tiles of at most tile_tokens tokens that never cross a destination page
+    tt = p.info["tile_tokens"]
+    assert tt >= 1
+    for e in ents:
+        pos, end = e.dst_offset + e.recompute_k, e.dst_offset + e.length
+        while pos < end:
+            n = min(tt, end - pos)
+            if wl.page_size:
+                n = min(n, wl.page_size - pos % wl.page_size)
+            pos += n
+            tiles += 1
+    assert p.info["n_tiles"] == tiles
     assert p.info["pool_tokens_required"] == max(c.token_start + c.length for c in wl.chunks)
     bounds, rec = p.ranges()
     want_b = [(r, e.dst_offset, e.dst_offset + e.length)
