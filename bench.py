@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "stitched-KV HBM GB/s (read+write) and token-layers/s; % of HBM peak"
 PEAK_GBS = 8000.0  # MI355X HBM3E, published
-KERNEL_SOURCE = os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc", "stitch.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc", f)
+                  for f in ("stitch.hip", "plan.cpp", "pic_internal.hpp")]
 COUNTERS = os.path.join(ROOT, "profiles", "stitch_kernel_llama3-8b-paged_counters.md")
 
 
@@ -38,8 +39,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 over the sources that decide what the stitch kernel reads and writes."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic():

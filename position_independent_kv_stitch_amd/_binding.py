@@ -119,24 +119,7 @@ def _check_single_runtime():
     _runtime_checked = True
 
 
-def load_library():
-    """Load libpic_stitch.so; raise if it has not been built.
-
-    torch is imported first when it is installed, so that the library binds
-    to torch's HIP runtime (the one that owns the tensors and streams it is
-    given) rather than loading a second copy."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIBRARY):
-        raise ImportError(f"{LIBRARY} is missing: build it with "
-                          "`python -c 'import __graft_entry__ as g; g.build()'`")
-    try:
-        import torch  # noqa: F401
-    except ImportError:
-        pass
-    lib = C.CDLL(LIBRARY)
-    _check_single_runtime()
+def _configure(lib):
     P = C.POINTER
     lib.pic_plan.restype = C.c_int
     lib.pic_plan.argtypes = [P(KvShape), P(RopeConfig), P(ChunkC), C.c_int32, P(RequestC),
@@ -156,13 +139,44 @@ def load_library():
     lib.pic_plan_destroy.argtypes = [C.c_void_p]
     lib.pic_last_error.restype = C.c_char_p
     lib.pic_last_error.argtypes = []
-    _lib = lib
     return lib
 
 
-def _check(status: int):
+_other_builds = {}
+
+
+def load_library(path: Optional[str] = None):
+    """Load libpic_stitch.so (or, with `path`, another build of the same ABI);
+    raise if it has not been built.
+
+    torch is imported first when it is installed, so that the library binds
+    to torch's HIP runtime (the one that owns the tensors and streams it is
+    given) rather than loading a second copy."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    if path is not None and path in _other_builds:
+        return _other_builds[path]
+    target = LIBRARY if path is None else path
+    if not os.path.exists(target):
+        raise ImportError(f"{target} is missing: build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = _configure(C.CDLL(target))
+    _check_single_runtime()
+    if path is None:
+        _lib = lib
+    else:
+        _other_builds[path] = lib
+    return lib
+
+
+def _check(status: int, lib=None):
     if status != PIC_OK:
-        raise PicError(status, load_library().pic_last_error().decode())
+        raise PicError(status, (lib or load_library()).pic_last_error().decode())
 
 
 def _get(obj, name, idx):
@@ -189,8 +203,8 @@ class Plan:
     def __init__(self, *, dtype: str, n_layers: int, n_heads: int, row_dim: int,
                  rope_offset: int, rope_dim: int, style: str, theta: float, has_v: bool,
                  chunks: Sequence, requests: Sequence, page_size: int = 0,
-                 capacity: int = 0, n_phys_pages: int = 0, inv_freq=None):
-        lib = load_library()
+                 capacity: int = 0, n_phys_pages: int = 0, inv_freq=None, library=None):
+        lib = load_library(library)
         self._lib = lib
         self._handle = C.c_void_p()
         self.dtype, self.n_layers, self.n_heads, self.row_dim = dtype, n_layers, n_heads, row_dim
@@ -219,20 +233,20 @@ class Plan:
             rarr[r] = RequestC(earr, pt_ptr, len(entries), n_pages)
         geom = DstGeom(page_size, 0, capacity, n_phys_pages)
         _check(lib.pic_plan(C.byref(shape), C.byref(rope), carr, len(chunks), rarr,
-                            len(requests), C.byref(geom), C.byref(self._handle)))
+                            len(requests), C.byref(geom), C.byref(self._handle)), lib)
         self.info = self._info()
 
     @classmethod
-    def from_workload(cls, wl) -> "Plan":
+    def from_workload(cls, wl, library=None) -> "Plan":
         return cls(dtype=wl.dtype, n_layers=wl.n_layers, n_heads=wl.n_heads,
                    row_dim=wl.row_dim, rope_offset=wl.rope_offset, rope_dim=wl.rope_dim,
                    style=wl.style, theta=wl.theta, has_v=wl.has_v, chunks=wl.chunks,
                    requests=wl.requests, page_size=wl.page_size, capacity=wl.capacity,
-                   n_phys_pages=wl.n_phys_pages, inv_freq=wl.inv_freq)
+                   n_phys_pages=wl.n_phys_pages, inv_freq=wl.inv_freq, library=library)
 
     def _info(self) -> dict:
         info = PlanInfo()
-        _check(self._lib.pic_plan_info(self._handle, C.byref(info)))
+        _check(self._lib.pic_plan_info(self._handle, C.byref(info)), self._lib)
         return info.as_dict()
 
     def ranges(self):
@@ -241,7 +255,7 @@ class Plan:
         b = np.zeros((max(n, 1), 3), dtype=np.int64)
         r = np.zeros((max(n, 1), 3), dtype=np.int64)
         _check(self._lib.pic_plan_ranges(self._handle, b.ctypes.data_as(C.POINTER(C.c_int64)),
-                                         r.ctypes.data_as(C.POINTER(C.c_int64))))
+                                         r.ctypes.data_as(C.POINTER(C.c_int64))), self._lib)
         return b[:n], r[:n]
 
     @property
@@ -343,17 +357,17 @@ def stitch(plan: Plan, pool_k, pool_v, dst_k, dst_v, layer_begin: int = 0,
         raise ValueError("plan has V rows: pass pool_v and dst_v")
     pv = _view(pool_k, pool_v if plan.has_v else None, "pool")
     dv = _view(dst_k, dst_v if plan.has_v else None, "paged" if plan.page_size else "contig")
-    lib = load_library()
+    lib = plan._lib  # the build that made the plan runs it
     _check(lib.pic_stitch(plan.handle, C.byref(pv), C.byref(dv), layer_begin, le,
-                          _stream_of(pool_k, stream)))
+                          _stream_of(pool_k, stream)), lib)
 
 
 def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
                    style: str = "half", rope_offset: int = 0, layer_begin: int = 0,
-                   layer_end: Optional[int] = None, inv_freq=None, stream=None):
+                   layer_end: Optional[int] = None, inv_freq=None, stream=None, library=None):
     """Enqueue pic_rotate_inplace on buf_k [L][T][H][D]; segments are
     (token_start, length, delta, recompute_k) tuples or objects."""
-    lib = load_library()
+    lib = load_library(library)
     L, T, H, D = buf_k.shape
     le = L if layer_end is None else layer_end
     shape, rope, keep = _shape_and_rope(_dtype_name(buf_k), L, H, D, rope_offset, rope_dim,
@@ -364,11 +378,12 @@ def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
                            int(_get(s, "length", 1)), int(_get(s, "recompute_k", 3)))
     view = _view(buf_k, None, "buf")
     _check(lib.pic_rotate_inplace(C.byref(shape), C.byref(rope), C.byref(view), T, sarr,
-                                  len(segments), layer_begin, le, _stream_of(buf_k, stream)))
+                                  len(segments), layer_begin, le, _stream_of(buf_k, stream)),
+           lib)
 
 
-def rotate_workload(wl, buf_k, layer_begin=0, layer_end=None, stream=None):
+def rotate_workload(wl, buf_k, layer_begin=0, layer_end=None, stream=None, library=None):
     """pic_rotate_inplace for an in-place workload description."""
     rotate_inplace(buf_k, wl.segments, rope_dim=wl.rope_dim, theta=wl.theta, style=wl.style,
                    rope_offset=wl.rope_offset, layer_begin=layer_begin, layer_end=layer_end,
-                   inv_freq=wl.inv_freq, stream=stream)
+                   inv_freq=wl.inv_freq, stream=stream, library=library)

@@ -54,14 +54,19 @@ struct Units {
     int32_t nr, uph;    // rotary units per token / per head (uph: power of two dividing 64)
     int32_t uph_shift;  // log2(uph)
     int32_t ncs;        // cos/sin pairs one rotary unit needs
+    int32_t interleaved;  // 1 for interleaved pairing
     int32_t nck, cph;   // K copy units per token / per head (non-rotary dims)
     int32_t nv, vph;    // V units per token / per head
 };
 
 // Per-lane slot shape of a launch: MAXR rotary and MAXC copy units per lane,
-// g tokens per wave step, nblk unit blocks per step.
+// g tokens per wave step, nblk unit blocks per step; rotary units are rb-byte
+// words (16, or 4 when 16-byte rotary units would leave lanes of a step idle),
+// nr of them per token, 2^uph_shift per head.
 struct Launch {
     int32_t maxr = 1, maxc = 2, g = 1, nblk = 1;
+    int32_t rb = 16, nr = 0, uph_shift = 0;
+    int32_t stream_loads = 0;  // 1: no pool row is read twice in a launch (non-temporal loads)
 };
 
 struct Problem {

@@ -92,6 +92,7 @@ pic_status derive_units(const pic_kv_shape *shape, const pic_rope_config *rope, 
     u->uph_shift = 0;
     while ((1 << u->uph_shift) < uph) u->uph_shift++;
     u->ncs = ncs;
+    u->interleaved = rope->style == PIC_ROPE_INTERLEAVED ? 1 : 0;
     u->nr = shape->num_heads * uph;
     u->cph = (shape->row_dim - rope->rope_dim) / vec;
     u->vph = shape->row_dim / vec;
@@ -115,10 +116,26 @@ Launch launch_shape_of(int32_t dtype, const Units &u) {
         l.maxr = u.nr <= 64 ? 1 : 2;
         l.maxc = 4;
     }
-    int g = (64 * l.maxr) / u.nr;
-    if (ncv > 0) g = std::min(g, (64 * l.maxc) / ncv);
-    l.g = std::max(1, std::min(g, 8));
-    const int rb = (l.g * u.nr + 64 * l.maxr - 1) / (64 * l.maxr);
+    auto tokens_per_step = [&](int nr) {
+        int g = (64 * l.maxr) / nr;
+        if (ncv > 0) g = std::min(g, (64 * l.maxc) / ncv);
+        return std::max(1, std::min(g, 8));
+    };
+    l.rb = 16;
+    l.nr = u.nr;
+    l.uph_shift = u.uph_shift;
+    l.g = tokens_per_step(l.nr);
+    // A step that leaves lanes without rotary work (narrow rotary slices, as
+    // in MLA rows) deals its planes in 4-byte words instead: four times the
+    // units, a quarter of the fp64 work per lane.  Half pairing only: a
+    // 4-byte word of an interleaved f32 row would hold half a plane.
+    if (l.g * u.nr < 64 && u.uph <= 16 && u.interleaved == 0) {
+        l.rb = 4;
+        l.nr = u.nr * 4;
+        l.uph_shift = u.uph_shift + 2;
+        l.g = tokens_per_step(l.nr);
+    }
+    const int rb = (l.g * l.nr + 64 * l.maxr - 1) / (64 * l.maxr);
     const int cb = (l.g * ncv + 64 * l.maxc - 1) / (64 * l.maxc);
     l.nblk = std::max(rb, cb);
     return l;
@@ -310,6 +327,20 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.u = u;
     p.launch = launch_shape_of(shape->dtype, u);
     p.tile_tokens = kTileSteps * 4 * p.launch.g;
+    {
+        // Pool rows read more than once per layer (a chunk placed twice, or
+        // chunks sharing tokens) may be served from cache on the second
+        // read; only a plan that reads every row once streams its loads.
+        std::vector<Interval> iv;
+        for (int r = 0; r < n_requests; r++)
+            for (int j = 0; j < requests[r].n_entries; j++) {
+                const pic_entry &e = requests[r].entries[j];
+                const int64_t t0 = chunks[e.chunk_id].token_start;
+                if (e.recompute_k < e.length)
+                    iv.push_back(Interval{0, t0 + e.recompute_k, t0 + e.length});
+            }
+        p.launch.stream_loads = any_overlap(iv) ? 0 : 1;
+    }
     std::unordered_map<int64_t, int32_t> table_of_delta;
     int64_t written = 0, masked = 0;
     for (int r = 0; r < n_requests; r++) {
@@ -378,6 +409,7 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.u = u;
     p.launch = launch_shape_of(shape->dtype, u);
     p.tile_tokens = kTileSteps * 4 * p.launch.g;
+    p.launch.stream_loads = 1;  // segments never overlap: every row is read once
     std::unordered_map<int64_t, int32_t> table_of_delta;
     int64_t written = 0, masked = 0;
     for (int g = 0; g < n_segments; g++) {

@@ -118,80 +118,70 @@ struct Vec<uint16_t> {
     static constexpr int kElems = 8;
 };
 
-// HALF pairing: word a holds x of planes p0..p0+VEC-1, word b their y;
-// c[p], s[p] = cos, sin of plane p0 + p.
-__device__ __forceinline__ void rotate_half(uint4 &a, uint4 &b, const double *c, const double *s,
-                                            float) {
-    const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-    const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-    uint32_t ao[4], bo[4];
+// Rotation of one rotary unit held in NW 32-bit words, with c[p], s[p] the
+// cosine and sine of the unit's plane p.
+//   HALF pairing: words a hold the x of the unit's planes, words b their y
+//     (bf16: two planes per word, low half first; f32: one plane per word).
+//   INTERLEAVED pairing: words a hold (x, y) of consecutive planes (bf16:
+//     one plane per word; f32: one plane per two words); b is unused.
+template <typename E, int STYLE, int NW>
+__device__ __forceinline__ void rotate_unit(uint32_t (&a)[NW], uint32_t (&b)[NW],
+                                            const double *c, const double *s) {
+    if constexpr (sizeof(E) == 2) {
+        if constexpr (STYLE == PIC_ROPE_HALF) {
 #pragma unroll
-    for (int e = 0; e < 4; e++) {
-        const double x = __uint_as_float(aw[e]), y = __uint_as_float(bw[e]);
-        ao[e] = __float_as_uint(static_cast<float>(x * c[e] - y * s[e]));
-        bo[e] = __float_as_uint(static_cast<float>(x * s[e] + y * c[e]));
-    }
-    a = make_uint4(ao[0], ao[1], ao[2], ao[3]);
-    b = make_uint4(bo[0], bo[1], bo[2], bo[3]);
-}
-
-__device__ __forceinline__ void rotate_half(uint4 &a, uint4 &b, const double *c, const double *s,
-                                            uint16_t) {
-    uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-    uint32_t bw[4] = {b.x, b.y, b.z, b.w};
+            for (int k = 0; k < NW; k++) {
+                const double x0 = bf16_lo(a[k]), x1 = bf16_hi(a[k]);
+                const double y0 = bf16_lo(b[k]), y1 = bf16_hi(b[k]);
+                const double c0 = c[2 * k], s0 = s[2 * k], c1 = c[2 * k + 1], s1 = s[2 * k + 1];
+                a[k] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
+                b[k] = pack_bf16(x0 * s0 + y0 * c0, x1 * s1 + y1 * c1);
+            }
+        } else {
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const double x0 = bf16_lo(aw[k]), x1 = bf16_hi(aw[k]);
-        const double y0 = bf16_lo(bw[k]), y1 = bf16_hi(bw[k]);
-        const double c0 = c[2 * k], s0 = s[2 * k], c1 = c[2 * k + 1], s1 = s[2 * k + 1];
-        aw[k] = pack_bf16(x0 * c0 - y0 * s0, x1 * c1 - y1 * s1);
-        bw[k] = pack_bf16(x0 * s0 + y0 * c0, x1 * s1 + y1 * c1);
-    }
-    a = make_uint4(aw[0], aw[1], aw[2], aw[3]);
-    b = make_uint4(bw[0], bw[1], bw[2], bw[3]);
-}
-
-// INTERLEAVED pairing: one word holds (x, y) of consecutive planes.
-__device__ __forceinline__ void rotate_interleaved(uint4 &a, const double *c, const double *s,
-                                                   float) {
-    const double x0 = __uint_as_float(a.x), y0 = __uint_as_float(a.y);
-    const double x1 = __uint_as_float(a.z), y1 = __uint_as_float(a.w);
-    a = make_uint4(__float_as_uint(static_cast<float>(x0 * c[0] - y0 * s[0])),
-                   __float_as_uint(static_cast<float>(x0 * s[0] + y0 * c[0])),
-                   __float_as_uint(static_cast<float>(x1 * c[1] - y1 * s[1])),
-                   __float_as_uint(static_cast<float>(x1 * s[1] + y1 * c[1])));
-}
-
-__device__ __forceinline__ void rotate_interleaved(uint4 &a, const double *c, const double *s,
-                                                   uint16_t) {
-    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+            for (int k = 0; k < NW; k++) {
+                const double x = bf16_lo(a[k]), y = bf16_hi(a[k]);
+                a[k] = pack_bf16(x * c[k] - y * s[k], x * s[k] + y * c[k]);
+            }
+        }
+    } else {
+        if constexpr (STYLE == PIC_ROPE_HALF) {
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const double x = bf16_lo(w[k]), y = bf16_hi(w[k]);
-        w[k] = pack_bf16(x * c[k] - y * s[k], x * s[k] + y * c[k]);
+            for (int k = 0; k < NW; k++) {
+                const double x = __uint_as_float(a[k]), y = __uint_as_float(b[k]);
+                a[k] = __float_as_uint(static_cast<float>(x * c[k] - y * s[k]));
+                b[k] = __float_as_uint(static_cast<float>(x * s[k] + y * c[k]));
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NW / 2; k++) {
+                const double x = __uint_as_float(a[2 * k]), y = __uint_as_float(a[2 * k + 1]);
+                a[2 * k] = __float_as_uint(static_cast<float>(x * c[k] - y * s[k]));
+                a[2 * k + 1] = __float_as_uint(static_cast<float>(x * s[k] + y * c[k]));
+            }
+        }
     }
-    a = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
-#ifndef PIC_NT_LOADS
-#define PIC_NT_LOADS 0
-#endif
 #ifndef PIC_NT_STORES
-#define PIC_NT_STORES 0
+#define PIC_NT_STORES 1
 #endif
 
-// 16-byte global accesses; the pool is read once and the destination written
-// once per launch, so both may bypass cache retention (non-temporal hints).
+// 16-byte global accesses.  The destination is written once per launch and
+// not read back by it, so stores are non-temporal; loads are non-temporal
+// (NTL) when the plan reads every pool row once, and cached otherwise, so a
+// chunk placed into several requests can be served from L2/MALL.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+template <int NTL>
 __device__ __forceinline__ uint4 ld16(const void *base, int64_t elem, int esize) {
     const char *p = static_cast<const char *>(base) + elem * esize;
-#if PIC_NT_LOADS
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-#else
-    return *reinterpret_cast<const uint4 *>(p);
-#endif
+    if constexpr (NTL) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    } else {
+        return *reinterpret_cast<const uint4 *>(p);
+    }
 }
 __device__ __forceinline__ void st16(void *base, int64_t elem, int esize, const uint4 &v) {
     char *p = static_cast<char *>(base) + elem * esize;
@@ -201,6 +191,39 @@ __device__ __forceinline__ void st16(void *base, int64_t elem, int esize, const 
 #else
     *reinterpret_cast<uint4 *>(p) = v;
 #endif
+}
+
+// NW consecutive 32-bit words (NW = 4: one 16-byte access; NW = 1: one dword).
+template <int NW, int NTL>
+__device__ __forceinline__ void ldw(const void *base, int64_t elem, int esize, uint32_t (&w)[NW]) {
+    if constexpr (NW == 4) {
+        const uint4 v = ld16<NTL>(base, elem, esize);
+        w[0] = v.x;
+        w[1] = v.y;
+        w[2] = v.z;
+        w[3] = v.w;
+    } else {
+        static_assert(NW == 1, "rotary words are 16 or 4 bytes");
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(static_cast<const char *>(base) +
+                                                               elem * esize);
+        if constexpr (NTL)
+            w[0] = __builtin_nontemporal_load(p);
+        else
+            w[0] = *p;
+    }
+}
+template <int NW>
+__device__ __forceinline__ void stw(void *base, int64_t elem, int esize, const uint32_t (&w)[NW]) {
+    if constexpr (NW == 4) {
+        st16(base, elem, esize, make_uint4(w[0], w[1], w[2], w[3]));
+    } else {
+        uint32_t *p = reinterpret_cast<uint32_t *>(static_cast<char *>(base) + elem * esize);
+#if PIC_NT_STORES
+        __builtin_nontemporal_store(w[0], p);
+#else
+        *p = w[0];
+#endif
+    }
 }
 
 // --------------------------------------------------------------- the kernel
@@ -220,11 +243,13 @@ __device__ __forceinline__ void st16(void *base, int64_t elem, int esize, const 
 // and copy units (g * (nck + nv)) are dealt to the 64 lanes, MAXR and MAXC
 // per lane.  Each lane's slot offsets and the cos/sin of its planes are set
 // up once per workgroup; all of a step's loads are issued before its stores.
-template <typename E, int STYLE, int MAXR, int MAXC>
+template <typename E, int STYLE, int MAXR, int MAXC, int RB, int NTL>
 __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kernel(const KArgs a) {
-    constexpr int VEC = Vec<E>::kElems;
+    constexpr int VEC = Vec<E>::kElems;              // elements per 16-byte copy unit
     constexpr int ES = sizeof(E);
-    constexpr int NCS = STYLE == kHalf ? VEC : VEC / 2;  // planes per rotary unit
+    constexpr int NW = RB / 4;                       // 32-bit words per rotary word
+    constexpr int RVEC = RB / ES;                    // elements per rotary word
+    constexpr int NCS = STYLE == kHalf ? RVEC : RVEC / 2;  // planes per rotary unit
     constexpr int kWaves = kBlockThreads / 64;
     constexpr int kNone = 1 << 30;                       // slot token index: unused slot
     const int lane = threadIdx.x & 63;
@@ -273,7 +298,7 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
                 const int q = u / a.nr;
                 const int r = u - q * a.nr;
                 const int h = r >> a.uph_shift;
-                const int inner = a.rope_offset + (r & ((1 << a.uph_shift) - 1)) * VEC;
+                const int inner = a.rope_offset + (r & ((1 << a.uph_shift) - 1)) * RVEC;
                 rq[i] = q;
                 rs[i] = static_cast<int>(q * a.s_tok + h * a.s_head + inner);
                 rd[i] = static_cast<int>(q * a.d_tok + h * a.d_head + inner);
@@ -312,28 +337,24 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
             const int lim = T.ntok - t0;  // slots of tokens q < lim are live
             const int64_t sb = s0 + t0 * a.s_tok;
             const int64_t db = d0 + t0 * a.d_tok;
-            uint4 A[MAXR], B[MAXR], Cw[MAXC];
+            uint32_t A[MAXR][NW], B[MAXR][NW];
+            uint4 Cw[MAXC];
 #pragma unroll
             for (int i = 0; i < MAXR; i++) {
                 if (rq[i] < lim) {
-                    A[i] = ld16(sk, sb + rs[i], ES);
-                    if (STYLE == kHalf) B[i] = ld16(sk, sb + rs[i] + half_off, ES);
+                    ldw<NW, NTL>(sk, sb + rs[i], ES, A[i]);
+                    if (STYLE == kHalf) ldw<NW, NTL>(sk, sb + rs[i] + half_off, ES, B[i]);
                 }
             }
 #pragma unroll
             for (int i = 0; i < MAXC; i++)
-                if (cq[i] < lim) Cw[i] = ld16(isv[i] ? sv : sk, sb + cs_[i], ES);
+                if (cq[i] < lim) Cw[i] = ld16<NTL>(isv[i] ? sv : sk, sb + cs_[i], ES);
 #pragma unroll
             for (int i = 0; i < MAXR; i++) {
                 if (rq[i] < lim) {
-                    if (STYLE == kHalf) {
-                        if (turn) rotate_half(A[i], B[i], c, s, E{});
-                        st16(dk, db + rd[i], ES, A[i]);
-                        st16(dk, db + rd[i] + half_off, ES, B[i]);
-                    } else {
-                        if (turn) rotate_interleaved(A[i], c, s, E{});
-                        st16(dk, db + rd[i], ES, A[i]);
-                    }
+                    if (turn) rotate_unit<E, STYLE, NW>(A[i], B[i], c, s);
+                    stw<NW>(dk, db + rd[i], ES, A[i]);
+                    if (STYLE == kHalf) stw<NW>(dk, db + rd[i] + half_off, ES, B[i]);
                 }
             }
 #pragma unroll
@@ -353,26 +374,43 @@ bool slot_offsets_fit(const Problem &p, int64_t tok, int64_t head) {
     return span <= INT32_MAX;
 }
 
-template <typename E, int STYLE, int MAXR, int MAXC>
+template <typename E, int STYLE, int MAXR, int MAXC, int RB, int NTL>
 hipError_t launch_kernel(const KArgs &a, int n_tiles, int n_layers, hipStream_t stream) {
     dim3 grid(static_cast<unsigned>(n_tiles), static_cast<unsigned>(n_layers));
-    hipLaunchKernelGGL((stitch_kernel<E, STYLE, MAXR, MAXC>), grid, dim3(kBlockThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((stitch_kernel<E, STYLE, MAXR, MAXC, RB, NTL>), grid, dim3(kBlockThreads),
+                       0, stream, a);
     return hipGetLastError();
+}
+
+template <typename E, int STYLE, int RB, int NTL>
+hipError_t launch_shape(const Problem &p, const KArgs &a, int n_layers, hipStream_t stream) {
+    const int n_tiles = static_cast<int>(p.tiles.size());
+    const Launch &l = p.launch;
+    if (l.maxr == 1 && l.maxc == 2)
+        return launch_kernel<E, STYLE, 1, 2, RB, NTL>(a, n_tiles, n_layers, stream);
+    if (l.maxr == 1) return launch_kernel<E, STYLE, 1, 4, RB, NTL>(a, n_tiles, n_layers, stream);
+    return launch_kernel<E, STYLE, 2, 4, RB, NTL>(a, n_tiles, n_layers, stream);
+}
+
+template <typename E, int STYLE, int RB>
+hipError_t launch_rb(const Problem &p, const KArgs &a, int n_layers, hipStream_t stream) {
+    if (p.launch.stream_loads) return launch_shape<E, STYLE, RB, 1>(p, a, n_layers, stream);
+    return launch_shape<E, STYLE, RB, 0>(p, a, n_layers, stream);
 }
 
 template <typename E, int STYLE>
 hipError_t launch_style(const Problem &p, const KArgs &a, int n_layers, hipStream_t stream) {
-    const int n_tiles = static_cast<int>(p.tiles.size());
-    const Launch &l = p.launch;
-    if (l.maxr == 1 && l.maxc == 2) return launch_kernel<E, STYLE, 1, 2>(a, n_tiles, n_layers, stream);
-    if (l.maxr == 1) return launch_kernel<E, STYLE, 1, 4>(a, n_tiles, n_layers, stream);
-    return launch_kernel<E, STYLE, 2, 4>(a, n_tiles, n_layers, stream);
+    if constexpr (STYLE == PIC_ROPE_HALF) {
+        if (p.launch.rb == 4) return launch_rb<E, STYLE, 4>(p, a, n_layers, stream);
+    }
+    return launch_rb<E, STYLE, 16>(p, a, n_layers, stream);
 }
 
 hipError_t launch(const Problem &p, KArgs a, int n_layers, hipStream_t stream) {
     a.g = p.launch.g;
     a.nblk = p.launch.nblk;
+    a.nr = p.launch.nr;
+    a.uph_shift = p.launch.uph_shift;
     if (p.shape.dtype == PIC_DTYPE_F32)
         return p.style == PIC_ROPE_HALF ? launch_style<float, PIC_ROPE_HALF>(p, a, n_layers, stream)
                                         : launch_style<float, PIC_ROPE_INTERLEAVED>(p, a, n_layers, stream);
