@@ -64,6 +64,8 @@ DEFAULT = "llama3-8b-paged"
 WORKLOADS = {
     DEFAULT: "32 layers, 8 kv heads x 128, bf16, one request of 8 chunks x 2048 tokens after a "
              "128-token prefix, 16-token pages, recompute_k 32 (stitch, paged)",
+    "llama3-8b-paged-pool": "the default workload with its chunks read from a paged pool of "
+                            "16-token blocks in random order (stitch, paged to paged)",
     "rag-group": "batched RAG, one group of 4 of the 32 layers: 64 requests of 4..16 chunks from "
                  "a 256-chunk pool of 128..4096 tokens, bf16, 16-token pages (stitch, paged)",
     "mla": "DeepSeek-V3 MLA rows, 61 layers, 576-wide (512 copied + 64 rotated), bf16, 16 chunks "
@@ -78,7 +80,7 @@ WORKLOADS = {
 def setup_workload(name, torch, pic):
     """Inputs resident on cuda:0 and a step function for one workload."""
     from pic_workloads import (config1, config2, config3, config4, config5, normal_values,
-                               pool_values, sentinel_like)
+                               pool_values, sentinel_like, with_paged_pool)
     log(f"workload {name}: generating inputs on cuda:0")
     if name == "inplace":
         wl = config5()
@@ -92,7 +94,8 @@ def setup_workload(name, torch, pic):
                 "config": {"workload": WORKLOADS[name], "storage": "bf16",
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
     wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
-          "rag-group": lambda: config3(n_layers=4)}[name]()
+          "rag-group": lambda: config3(n_layers=4),
+          "llama3-8b-paged-pool": lambda: with_paged_pool(config2(), page_size=16, seed=1)}[name]()
     pk, pv = pool_values(wl, seed=0, device="cuda:0")
     dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
     dv = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0") if wl.has_v else None

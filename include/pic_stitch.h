@@ -88,15 +88,26 @@ typedef struct pic_kv_shape {
     int32_t has_v; /* 0 or 1 */
 } pic_kv_shape;
 
-/* A cached chunk in the pool: tokens [token_start, token_start + length),
- * whose keys were rotated for positions base_pos, base_pos + 1, ...
- * (EPIC caches at virtual offset 0, so base_pos is normally 0; Irminsul's
- * registry stores it explicitly, section 2.2). */
+/*
+ * A cached chunk.  Its keys were rotated for positions base_pos, base_pos +
+ * 1, ... (EPIC caches at virtual offset 0, so base_pos is normally 0;
+ * Irminsul's registry stores it explicitly, section 2.2).
+ *   Contiguous pool (geometry src_page_size 0): the chunk's tokens are pool
+ *     rows [token_start, token_start + length); n_pages 0, page_table NULL.
+ *   Paged pool (src_page_size > 0: the PagedAttention block pool of the EPIC
+ *     Guide's runtime figure, chunks kept at virtual offset 0 in physical
+ *     blocks): token t of the chunk is at slot (token_start + t) %
+ *     src_page_size of physical page page_table[(token_start + t) /
+ *     src_page_size]; token_start is the chunk's offset inside its first
+ *     page (normally 0) and page_table (host memory, read during pic_plan
+ *     only) holds n_pages entries.
+ */
 typedef struct pic_chunk {
     int64_t token_start;
     int64_t base_pos;
     int32_t length;
-    int32_t reserved; /* must be 0 */
+    int32_t n_pages;
+    const int32_t *page_table;
 } pic_chunk;
 
 /* One placement: chunk tokens [0, length) go to logical positions
@@ -111,8 +122,8 @@ typedef struct pic_entry {
 } pic_entry;
 
 /* A request's placement table (host memory, read during pic_plan only).
- * page_table maps logical page j to a physical page of the destination
- * pool; it is ignored for a contiguous destination. */
+ * page_table maps logical page j to a physical page of the paged
+ * destination; it is ignored for a contiguous destination. */
 typedef struct pic_request {
     const pic_entry *entries;
     const int32_t *page_table;
@@ -120,21 +131,26 @@ typedef struct pic_request {
     int32_t n_pages;
 } pic_request;
 
-/* Destination geometry: page_size 0 = contiguous (each request owns
- * capacity_tokens positions), else paged with num_phys_pages pages of
- * page_size tokens shared by all requests. */
-typedef struct pic_dst_geom {
-    int32_t page_size;
-    int32_t reserved; /* must be 0 */
-    int64_t capacity_tokens;
-    int64_t num_phys_pages;
-} pic_dst_geom;
+/* Pool and destination geometry.  Destination: dst_page_size 0 =
+ * contiguous (each request owns dst_capacity positions), else paged with
+ * dst_num_pages pages of dst_page_size tokens shared by all requests.
+ * Pool: src_page_size 0 = contiguous rows, else src_num_pages pages of
+ * src_page_size tokens. */
+typedef struct pic_geom {
+    int32_t dst_page_size;
+    int32_t src_page_size;
+    int64_t dst_capacity;
+    int64_t dst_num_pages;
+    int64_t src_num_pages;
+} pic_geom;
 
 /*
  * A device view of K (and V) memory.  Element (layer l, token row t, head
  * h, dim d) of K is k[l*layer_stride + t*token_stride + h*head_stride + d],
  * V the same with v; K and V share the strides.
- *   pool / in-place buffer: t is the token index.
+ *   contiguous pool / in-place buffer: t is the token index.
+ *   paged pool: the row of slot s of physical page g starts at
+ *     l*layer_stride + g*page_stride + s*token_stride.
  *   contiguous destination: t = r*request_stride/token_stride + position,
  *     i.e. the row of request r's position p starts at
  *     l*layer_stride + r*request_stride + p*token_stride.
@@ -168,7 +184,8 @@ typedef struct pic_plan_info_t {
     int64_t n_tiles;              /* work items of one layer */
     int64_t tokens_written;       /* per layer */
     int64_t tokens_masked;        /* per layer: sum of recompute_k */
-    int64_t pool_tokens_required; /* max token_start + length over chunks */
+    int64_t pool_tokens_required; /* contiguous pool: max token_start + length over chunks;
+                                     paged pool: src_num_pages * src_page_size */
     int64_t bytes_read_per_layer; /* algorithmic: rows read */
     int64_t bytes_written_per_layer;
     int64_t tile_tokens;          /* most tokens of one work tile (paged tiles also stop at
@@ -193,10 +210,12 @@ typedef struct pic_plan pic_plan_t;
  * Valid input (else PIC_ERR_RANGE unless noted):
  *   0 <= chunk_id < n_chunks; 1 <= length <= chunk.length;
  *   0 <= recompute_k <= length; dst_offset >= 0;
- *   dst_offset + length <= capacity_tokens (contiguous) or
- *     <= n_pages * page_size (paged);
- *   chunk.token_start >= 0, chunk.length >= 1;
- *   every page written is in [0, num_phys_pages);
+ *   dst_offset + length <= dst_capacity (contiguous) or
+ *     <= n_pages * dst_page_size (paged);
+ *   chunk.token_start >= 0, chunk.length >= 1; in a paged pool
+ *     token_start + length <= n_pages * src_page_size;
+ *   every destination page written is in [0, dst_num_pages) and every
+ *     pool page read in [0, src_num_pages);
  *   entries of one request do not overlap, and no destination row is
  *     written twice (PIC_ERR_OVERLAP);
  *   duplicate chunk_ids and negative deltas are allowed.
@@ -207,7 +226,7 @@ typedef struct pic_plan pic_plan_t;
  */
 pic_status pic_plan(const pic_kv_shape *shape, const pic_rope_config *rope,
                     const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
-                    int32_t n_requests, const pic_dst_geom *dst, pic_plan_t **out);
+                    int32_t n_requests, const pic_geom *geom, pic_plan_t **out);
 
 /*
  * pic_stitch -- run a plan for layers [layer_begin, layer_end) of the views:

@@ -45,7 +45,8 @@
  *  - destination rows not written keep their prior contents.
  *
  * Layouts are dense and row-major (elements):
- *   pool       [n_layers][pool_tokens][n_heads][row_dim]
+ *   pool       [n_layers][pool_tokens][n_heads][row_dim], or, paged,
+ *              [n_layers][src_num_pages][src_page_size][n_heads][row_dim]
  *   contiguous [n_layers][n_requests][capacity][n_heads][row_dim]
  *   paged      [n_layers][n_phys_pages][page_size][n_heads][row_dim]
  *   in-place   [n_layers][n_tokens][n_heads][row_dim]
@@ -77,8 +78,12 @@ typedef struct {
     double theta;
     const double *inv_freq; /* optional, rope_dim/2 values; NULL = theta formula */
     int64_t pool_tokens;
+    int32_t src_page_size;      /* 0 = contiguous pool */
+    int64_t src_num_pages;      /* paged pool: pages in the pool */
+    const int32_t *chunk_pages; /* paged pool: pages per chunk */
+    const int32_t *chunk_page_table; /* paged pool: tables listed chunk by chunk */
     int32_t n_chunks;
-    const int64_t *chunk_start; /* token index of the chunk in the pool */
+    const int64_t *chunk_start; /* contiguous: first pool row; paged: offset in its pages */
     const int64_t *chunk_base;  /* position the chunk's keys were cached at */
     const int32_t *chunk_len;
     int32_t n_requests;
@@ -234,6 +239,22 @@ static int orc_check_shape(int dtype, int n_layers, int n_heads, int row_dim, in
     return ORC_OK;
 }
 
+/* paged pool: physical page holding offset `at` of chunk c's page list */
+static int32_t orc_src_page(const orc_stitch_problem *p, int c, int64_t at)
+{
+    int64_t first = 0;
+    for (int i = 0; i < c; i++) first += p->chunk_pages[i];
+    return p->chunk_page_table[first + at / p->src_page_size];
+}
+
+/* pool row (within a layer) of token t of chunk c */
+static int64_t orc_src_row(const orc_stitch_problem *p, int c, int64_t t)
+{
+    if (p->src_page_size == 0) return p->chunk_start[c] + t;
+    int64_t at = p->chunk_start[c] + t;
+    return (int64_t)orc_src_page(p, c, at) * p->src_page_size + at % p->src_page_size;
+}
+
 /*
  * A problem is valid when every chunk lies in the pool, every entry names
  * an existing chunk, places 1..chunk_len of its tokens with 0 <= k <= length
@@ -250,7 +271,11 @@ int orc_validate_stitch(const orc_stitch_problem *p, int layer_begin, int layer_
     if (st) return st;
     if (p->has_v != 0 && p->has_v != 1) return ORC_BAD_ARG;
     if (p->pool_tokens < 0 || p->n_chunks < 0 || p->n_requests < 0) return ORC_BAD_ARG;
-    if (p->page_size < 0) return ORC_BAD_ARG;
+    if (p->page_size < 0 || p->src_page_size < 0) return ORC_BAD_ARG;
+    if (p->src_page_size > 0 && p->src_num_pages < 0) return ORC_BAD_ARG;
+    if (p->src_page_size > 0)
+        for (int c = 0; c < p->n_chunks; c++)
+            if (p->chunk_pages[c] < 0) return ORC_BAD_ARG;
     if (p->page_size == 0 && p->capacity < 0) return ORC_BAD_ARG;
     if (p->page_size > 0 && p->n_phys_pages < 0) return ORC_BAD_ARG;
     for (int r = 0; r < p->n_requests; r++) {
@@ -260,7 +285,9 @@ int orc_validate_stitch(const orc_stitch_problem *p, int layer_begin, int layer_
 
     for (int c = 0; c < p->n_chunks; c++) {
         if (p->chunk_start[c] < 0 || p->chunk_len[c] < 1) return ORC_RANGE;
-        if (p->chunk_start[c] + p->chunk_len[c] > p->pool_tokens) return ORC_RANGE;
+        int64_t room = p->src_page_size > 0 ? (int64_t)p->chunk_pages[c] * p->src_page_size
+                                            : p->pool_tokens;
+        if (p->chunk_start[c] + p->chunk_len[c] > room) return ORC_RANGE;
     }
     int64_t e0 = 0, pt0 = 0;
     for (int r = 0; r < p->n_requests; r++) {
@@ -277,6 +304,12 @@ int orc_validate_stitch(const orc_stitch_problem *p, int layer_begin, int layer_
                     int64_t pos = p->ent_dst[e] + t;
                     int32_t page = p->page_table[pt0 + pos / p->page_size];
                     if (page < 0 || page >= p->n_phys_pages) return ORC_RANGE;
+                }
+            }
+            if (p->src_page_size > 0) {
+                for (int t = p->ent_k[e]; t < p->ent_len[e]; t++) {
+                    int32_t page = orc_src_page(p, c, p->chunk_start[c] + t);
+                    if (page < 0 || page >= p->src_num_pages) return ORC_RANGE;
                 }
             }
         }
@@ -389,6 +422,8 @@ int orc_stitch(const orc_stitch_problem *p, const void *pool_k, const void *pool
     const int64_t dst_rows_per_layer = p->page_size > 0
                                            ? p->n_phys_pages * p->page_size
                                            : (int64_t)p->n_requests * p->capacity;
+    const int64_t src_rows_per_layer =
+        p->src_page_size > 0 ? p->src_num_pages * p->src_page_size : p->pool_tokens;
 
     for (int layer = layer_begin; layer < layer_end; layer++) {
         int64_t e0 = 0, pt0 = 0;
@@ -400,7 +435,7 @@ int orc_stitch(const orc_stitch_problem *p, const void *pool_k, const void *pool
                 if (delta != 0)
                     orc_shift_table(p->theta, p->inv_freq, p->rope_dim, delta, c, s);
                 for (int t = p->ent_k[e]; t < p->ent_len[e]; t++) {
-                    int64_t src_tok = p->chunk_start[ch] + t;
+                    int64_t src_tok = orc_src_row(p, ch, t);
                     int64_t pos = p->ent_dst[e] + t;
                     int64_t dst_tok; /* destination row within the layer */
                     if (p->page_size > 0) {
@@ -409,7 +444,7 @@ int orc_stitch(const orc_stitch_problem *p, const void *pool_k, const void *pool
                     } else {
                         dst_tok = (int64_t)r * p->capacity + pos;
                     }
-                    int64_t src_off = ((int64_t)layer * p->pool_tokens + src_tok) * row;
+                    int64_t src_off = ((int64_t)layer * src_rows_per_layer + src_tok) * row;
                     int64_t dst_off = ((int64_t)layer * dst_rows_per_layer + dst_tok) * row;
                     /* values and the K row: bit copies */
                     if (p->has_v)

@@ -35,7 +35,9 @@ class _StitchProblem(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("n_layers", C.c_int32), ("n_heads", C.c_int32),
                 ("row_dim", C.c_int32), ("rope_offset", C.c_int32), ("rope_dim", C.c_int32),
                 ("style", C.c_int32), ("has_v", C.c_int32), ("theta", C.c_double),
-                ("inv_freq", _f64p), ("pool_tokens", C.c_int64), ("n_chunks", C.c_int32),
+                ("inv_freq", _f64p), ("pool_tokens", C.c_int64), ("src_page_size", C.c_int32),
+                ("src_num_pages", C.c_int64), ("chunk_pages", _i32p),
+                ("chunk_page_table", _i32p), ("n_chunks", C.c_int32),
                 ("chunk_start", _i64p), ("chunk_base", _i64p), ("chunk_len", _i32p),
                 ("n_requests", C.c_int32), ("req_entries", _i32p), ("ent_chunk", _i32p),
                 ("ent_dst", _i64p), ("ent_len", _i32p), ("ent_k", _i32p),
@@ -98,6 +100,11 @@ def _stitch_problem(wl, dtype=None):
         keep.append(a)
         return a
 
+    src_ps = getattr(wl, "src_page_size", 0)
+    tables = [np.asarray(c.page_table if c.page_table is not None else [], dtype=np.int32)
+              for c in wl.chunks] if src_ps else []
+    chunk_pages = arr([len(t) for t in tables] if src_ps else [0] * len(wl.chunks), np.int32)
+    chunk_page_table = arr(np.concatenate(tables) if tables else [], np.int32)
     chunk_start = arr([c.token_start for c in wl.chunks], np.int64)
     chunk_base = arr([c.base_pos for c in wl.chunks], np.int64)
     chunk_len = arr([c.length for c in wl.chunks], np.int32)
@@ -115,7 +122,9 @@ def _stitch_problem(wl, dtype=None):
     inv = arr(wl.inv_freq, np.float64) if getattr(wl, "inv_freq", None) is not None else None
     p = _StitchProblem(DTYPES[dt], wl.n_layers, wl.n_heads, wl.row_dim, wl.rope_offset,
                        wl.rope_dim, STYLES[wl.style], int(bool(wl.has_v)), float(wl.theta),
-                       _ptr(inv, C.c_double), wl.pool_tokens, len(wl.chunks),
+                       _ptr(inv, C.c_double), wl.pool_tokens, src_ps,
+                       getattr(wl, "src_n_pages", 0), _ptr(chunk_pages, C.c_int32),
+                       _ptr(chunk_page_table, C.c_int32), len(wl.chunks),
                        _ptr(chunk_start, C.c_int64), _ptr(chunk_base, C.c_int64),
                        _ptr(chunk_len, C.c_int32), len(wl.requests),
                        _ptr(req_entries, C.c_int32), _ptr(ent_chunk, C.c_int32),
@@ -185,7 +194,11 @@ def stitch(wl, pool_k, pool_v, dst_k, dst_v, layer_begin=0, layer_end=None, dtyp
         raise ValueError("layer range outside the arrays given")
     sub = _Layers(wl, n)
     p, keep = _stitch_problem(sub, dt)
-    _check_array(pool_k, dt, (n, wl.pool_tokens, wl.n_heads, wl.row_dim), "pool_k")
+    if getattr(wl, "src_page_size", 0):
+        pshape = (n, wl.src_n_pages, wl.src_page_size, wl.n_heads, wl.row_dim)
+    else:
+        pshape = (n, wl.pool_tokens, wl.n_heads, wl.row_dim)
+    _check_array(pool_k, dt, pshape, "pool_k")
     dshape = ((n, wl.n_phys_pages, wl.page_size, wl.n_heads, wl.row_dim) if wl.page_size
               else (n, len(wl.requests), wl.capacity, wl.n_heads, wl.row_dim))
     _check_array(dst_k, dt, dshape, "dst_k")

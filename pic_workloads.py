@@ -31,11 +31,12 @@ DTYPE_BYTES = {"f32": 4, "bf16": 2}
 SENTINEL_BITS = {"f32": 0x7FC5A5A5, "bf16": 0x7FC5}
 
 
-@dataclass(frozen=True)
+@dataclass(frozen=True, eq=False)
 class Chunk:
-    token_start: int  # first token of the chunk in the pool
+    token_start: int  # contiguous pool: first row; paged pool: offset in the first page
     length: int
     base_pos: int = 0  # position its keys were cached at (virtual offset 0)
+    page_table: Optional[np.ndarray] = None  # paged pool: physical pages of the chunk
 
 
 @dataclass(frozen=True)
@@ -78,6 +79,8 @@ class Workload:
     page_size: int = 0  # 0 = contiguous destination
     capacity: int = 0  # contiguous: positions per request
     n_phys_pages: int = 0
+    src_page_size: int = 0  # 0 = contiguous pool
+    src_n_pages: int = 0
     inplace: bool = False
     n_tokens: int = 0  # in-place buffer length
     segments: List[Segment] = field(default_factory=list)
@@ -92,6 +95,9 @@ class Workload:
         return self.n_heads * self.row_dim
 
     def pool_shape(self):
+        if self.src_page_size:
+            return (self.n_layers, self.src_n_pages, self.src_page_size, self.n_heads,
+                    self.row_dim)
         return (self.n_layers, self.pool_tokens, self.n_heads, self.row_dim)
 
     def dst_shape(self):
@@ -205,6 +211,25 @@ def config5(seed: int = 0, n_layers: int = 36) -> Workload:
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def with_paged_pool(wl: Workload, page_size: int = 16, seed: int = 0,
+                    first_offsets: bool = False, spare_pages: int = 0) -> Workload:
+    """The same placements with the chunks kept in a paged pool (the block
+    pool of a PagedAttention runtime): every chunk gets its own pages, drawn
+    from one random permutation of the pool's pages.  With first_offsets a
+    chunk may start part-way into its first page."""
+    rng = np.random.default_rng(seed + 7919)
+    offs = [int(rng.integers(0, page_size)) if first_offsets else 0 for _ in wl.chunks]
+    need = [-(-(o + c.length) // page_size) for o, c in zip(offs, wl.chunks)]
+    total = int(sum(need)) + spare_pages
+    perm = rng.permutation(total).astype(np.int32)
+    chunks, at = [], 0
+    for o, n, c in zip(offs, need, wl.chunks):
+        chunks.append(Chunk(o, c.length, c.base_pos, perm[at:at + n].copy()))
+        at += n
+    return replace(wl, name=wl.name + " (paged pool)", chunks=chunks, pool_tokens=0,
+                   src_page_size=page_size, src_n_pages=total)
 
 
 def random_small(seed: int, dtype: str = "bf16", style: str = "half", paged: bool = False,

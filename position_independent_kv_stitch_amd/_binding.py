@@ -49,7 +49,7 @@ class KvShape(C.Structure):
 
 class ChunkC(C.Structure):
     _fields_ = [("token_start", C.c_int64), ("base_pos", C.c_int64), ("length", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("n_pages", C.c_int32), ("page_table", C.POINTER(C.c_int32))]
 
 
 class EntryC(C.Structure):
@@ -62,9 +62,10 @@ class RequestC(C.Structure):
                 ("n_entries", C.c_int32), ("n_pages", C.c_int32)]
 
 
-class DstGeom(C.Structure):
-    _fields_ = [("page_size", C.c_int32), ("reserved", C.c_int32),
-                ("capacity_tokens", C.c_int64), ("num_phys_pages", C.c_int64)]
+class Geom(C.Structure):
+    _fields_ = [("dst_page_size", C.c_int32), ("src_page_size", C.c_int32),
+                ("dst_capacity", C.c_int64), ("dst_num_pages", C.c_int64),
+                ("src_num_pages", C.c_int64)]
 
 
 class KvView(C.Structure):
@@ -123,7 +124,7 @@ def _configure(lib):
     P = C.POINTER
     lib.pic_plan.restype = C.c_int
     lib.pic_plan.argtypes = [P(KvShape), P(RopeConfig), P(ChunkC), C.c_int32, P(RequestC),
-                             C.c_int32, P(DstGeom), P(C.c_void_p)]
+                             C.c_int32, P(Geom), P(C.c_void_p)]
     lib.pic_stitch.restype = C.c_int
     lib.pic_stitch.argtypes = [C.c_void_p, P(KvView), P(KvView), C.c_int32, C.c_int32,
                                C.c_void_p]
@@ -203,19 +204,27 @@ class Plan:
     def __init__(self, *, dtype: str, n_layers: int, n_heads: int, row_dim: int,
                  rope_offset: int, rope_dim: int, style: str, theta: float, has_v: bool,
                  chunks: Sequence, requests: Sequence, page_size: int = 0,
-                 capacity: int = 0, n_phys_pages: int = 0, inv_freq=None, library=None):
+                 capacity: int = 0, n_phys_pages: int = 0, inv_freq=None, library=None,
+                 src_page_size: int = 0, src_n_pages: int = 0):
         lib = load_library(library)
         self._lib = lib
         self._handle = C.c_void_p()
         self.dtype, self.n_layers, self.n_heads, self.row_dim = dtype, n_layers, n_heads, row_dim
         self.has_v, self.page_size = bool(has_v), page_size
         self.capacity, self.n_phys_pages, self.n_requests = capacity, n_phys_pages, len(requests)
+        self.src_page_size, self.src_n_pages = src_page_size, src_n_pages
         shape, rope, keep = _shape_and_rope(dtype, n_layers, n_heads, row_dim, rope_offset,
                                             rope_dim, style, theta, has_v, inv_freq)
         carr = (ChunkC * max(1, len(chunks)))()
         for i, c in enumerate(chunks):
+            pt = getattr(c, "page_table", None) if src_page_size else None
+            pt_ptr, n_pages = None, 0
+            if pt is not None:
+                pta = np.ascontiguousarray(np.asarray(pt, dtype=np.int32))
+                keep.append(pta)
+                pt_ptr, n_pages = pta.ctypes.data_as(C.POINTER(C.c_int32)), len(pta)
             carr[i] = ChunkC(int(_get(c, "token_start", 0)), int(_get(c, "base_pos", 2)),
-                             int(_get(c, "length", 1)), 0)
+                             int(_get(c, "length", 1)), n_pages, pt_ptr)
         rarr = (RequestC * max(1, len(requests)))()
         for r, rq in enumerate(requests):
             entries = _get(rq, "entries", 0)
@@ -231,7 +240,7 @@ class Plan:
                 keep.append(pta)
                 pt_ptr, n_pages = pta.ctypes.data_as(C.POINTER(C.c_int32)), len(pta)
             rarr[r] = RequestC(earr, pt_ptr, len(entries), n_pages)
-        geom = DstGeom(page_size, 0, capacity, n_phys_pages)
+        geom = Geom(page_size, src_page_size, capacity, n_phys_pages, src_n_pages)
         _check(lib.pic_plan(C.byref(shape), C.byref(rope), carr, len(chunks), rarr,
                             len(requests), C.byref(geom), C.byref(self._handle)), lib)
         self.info = self._info()
@@ -242,7 +251,9 @@ class Plan:
                    row_dim=wl.row_dim, rope_offset=wl.rope_offset, rope_dim=wl.rope_dim,
                    style=wl.style, theta=wl.theta, has_v=wl.has_v, chunks=wl.chunks,
                    requests=wl.requests, page_size=wl.page_size, capacity=wl.capacity,
-                   n_phys_pages=wl.n_phys_pages, inv_freq=wl.inv_freq, library=library)
+                   n_phys_pages=wl.n_phys_pages, inv_freq=wl.inv_freq, library=library,
+                   src_page_size=getattr(wl, "src_page_size", 0),
+                   src_n_pages=getattr(wl, "src_n_pages", 0))
 
     def _info(self) -> dict:
         info = PlanInfo()
@@ -311,6 +322,11 @@ def _view(k, v, kind: str) -> KvView:
             raise ValueError(f"{kind}: expected [layers][tokens][heads][dim]")
         return KvView(k.data_ptr(), v.data_ptr() if v is not None else None, st[0], st[1],
                       st[2], 0, 0)
+    if kind == "paged-pool":
+        if k.dim() != 5:
+            raise ValueError("paged pool: expected [layers][pages][page][heads][dim]")
+        return KvView(k.data_ptr(), v.data_ptr() if v is not None else None, st[0], st[2],
+                      st[3], st[1], 0)
     if k.dim() != 5:
         raise ValueError(f"{kind}: expected a 5-D destination")
     if kind == "paged":
@@ -332,15 +348,20 @@ def stitch(plan: Plan, pool_k, pool_v, dst_k, dst_v, layer_begin: int = 0,
            layer_end: Optional[int] = None, stream=None):
     """Enqueue pic_stitch for layers [layer_begin, layer_end) of the tensors.
 
-    pool_*: [L][T][H][D]; dst_*: contiguous [L][R][S][H][D] or paged
-    [L][P][page][H][D].  V tensors are None when the plan has no V."""
+    pool_*: contiguous [L][T][H][D] or paged [L][P][page][H][D]; dst_*:
+    contiguous [L][R][S][H][D] or paged [L][P][page][H][D].  V tensors are
+    None when the plan has no V."""
     le = dst_k.shape[0] if layer_end is None else layer_end
     if _dtype_name(pool_k) != plan.dtype or _dtype_name(dst_k) != plan.dtype:
         raise TypeError("tensor dtype does not match the plan")
-    if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+    if plan.src_page_size:
+        if pool_k.dim() != 5 or pool_k.shape[1] < plan.src_n_pages or \
+                pool_k.shape[2] != plan.src_page_size:
+            raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
+    elif pool_k.shape[1] < plan.info["pool_tokens_required"]:
         raise PicError(PIC_ERR_RANGE, f"pool holds {pool_k.shape[1]} tokens, plan needs "
                        f"{plan.info['pool_tokens_required']}")
-    if tuple(pool_k.shape[2:]) != (plan.n_heads, plan.row_dim) or \
+    if tuple(pool_k.shape[-2:]) != (plan.n_heads, plan.row_dim) or \
             tuple(dst_k.shape[3:]) != (plan.n_heads, plan.row_dim):
         raise ValueError("head/row shape does not match the plan")
     if plan.page_size:
@@ -355,7 +376,8 @@ def stitch(plan: Plan, pool_k, pool_v, dst_k, dst_v, layer_begin: int = 0,
         raise ValueError("pool and destination on different devices")
     if plan.has_v and (pool_v is None or dst_v is None):
         raise ValueError("plan has V rows: pass pool_v and dst_v")
-    pv = _view(pool_k, pool_v if plan.has_v else None, "pool")
+    pv = _view(pool_k, pool_v if plan.has_v else None,
+               "paged-pool" if plan.src_page_size else "pool")
     dv = _view(dst_k, dst_v if plan.has_v else None, "paged" if plan.page_size else "contig")
     lib = plan._lib  # the build that made the plan runs it
     _check(lib.pic_stitch(plan.handle, C.byref(pv), C.byref(dv), layer_begin, le,

@@ -29,12 +29,12 @@ enum DstMode : int32_t { kContiguous = 0, kPaged = 1, kInPlace = 2 };
 // consecutive destination rows (a paged tile never crosses a page).  The
 // kernel reads it for every layer of a launch.
 struct DevTile {
-    int64_t src_row;  // pool token of the tile's first token
-    int64_t dst_a;    // contiguous: request; paged: physical page; in place: unused
-    int32_t dst_b;    // contiguous: position; paged: slot in the page; in place: unused
+    int64_t src_row;   // contiguous pool: row of the first token; paged pool: its page
+    int64_t dst_a;     // contiguous: request; paged: physical page; in place: unused
+    int32_t dst_b;     // contiguous: position; paged: slot in the page; in place: unused
     int32_t ntok;
-    int32_t cs_idx;   // shift table, -1 = delta 0 (rows copied)
-    int32_t pad;
+    int32_t cs_idx;    // shift table, -1 = delta 0 (rows copied)
+    int32_t src_slot;  // paged pool: slot of the first token in its page
 };
 
 // Host-side record of one placement (entry of a request, or in-place segment).
@@ -75,6 +75,7 @@ struct Problem {
     int32_t style = 0;
     int32_t mode = kContiguous;
     int32_t page_size = 0;
+    int32_t src_page_size = 0;  // 0: contiguous pool
     int64_t capacity = 0;
     int64_t num_phys_pages = 0;
     int32_t n_requests = 0;
@@ -109,7 +110,7 @@ Launch launch_shape_of(int32_t dtype, const Units &u);
 // Copy-mode and in-place problem builders (host only).
 pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
                         const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
-                        int32_t n_requests, const pic_dst_geom *dst, Problem *out);
+                        int32_t n_requests, const pic_geom *geom, Problem *out);
 pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
                          int64_t buf_tokens, const pic_segment *segments, int32_t n_segments,
                          Problem *out);

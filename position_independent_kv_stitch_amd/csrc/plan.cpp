@@ -190,19 +190,27 @@ void fill_info(Problem *p, int64_t tokens_written, int64_t tokens_masked, int64_
 }
 
 // Tiles of tokens [from, to) of one placement: at most tile_tokens tokens,
-// and in a paged destination never across a page, so each tile has one
-// destination row base and consecutive rows after it.
-void add_tiles(Problem *p, const HostEntry &e, const int32_t *page_table, int32_t from,
-               int32_t to) {
+// and never across a page of a paged destination or a paged pool, so each
+// tile has one source and one destination row base with consecutive rows
+// after them.
+void add_tiles(Problem *p, const HostEntry &e, const int32_t *dst_pages, const int32_t *src_pages,
+               int32_t from, int32_t to) {
     int32_t t = from;
     while (t < to) {
         int32_t n = std::min(p->tile_tokens, to - t);
         DevTile tile{e.src_tok + t, 0, 0, 0, e.cs_idx, 0};
+        if (src_pages) {
+            const int64_t at = e.src_tok + t;  // offset in the chunk's page list
+            const int32_t slot = static_cast<int32_t>(at % p->src_page_size);
+            n = std::min<int32_t>(n, p->src_page_size - slot);
+            tile.src_row = src_pages[at / p->src_page_size];
+            tile.src_slot = slot;
+        }
         if (p->mode == kPaged) {
             const int64_t pos = e.dst_pos + t;
             const int32_t slot = static_cast<int32_t>(pos % p->page_size);
             n = std::min<int32_t>(n, p->page_size - slot);
-            tile.dst_a = page_table[pos / p->page_size];
+            tile.dst_a = dst_pages[pos / p->page_size];
             tile.dst_b = slot;
         } else if (p->mode == kContiguous) {
             tile.dst_a = e.request;
@@ -218,22 +226,24 @@ void add_tiles(Problem *p, const HostEntry &e, const int32_t *page_table, int32_
 
 pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
                         const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
-                        int32_t n_requests, const pic_dst_geom *dst, Problem *out) {
+                        int32_t n_requests, const pic_geom *geom, Problem *out) {
     Units u{};
     pic_status st = derive_units(shape, rope, false, &u);
     if (st) return st;
-    if (!dst) return fail(PIC_ERR_INVALID_ARG, "dst geometry must not be NULL");
+    if (!geom) return fail(PIC_ERR_INVALID_ARG, "geometry must not be NULL");
     if (n_chunks < 0 || n_requests < 0)
         return fail(PIC_ERR_INVALID_ARG, "negative chunk or request count");
     if ((n_chunks > 0 && !chunks) || (n_requests > 0 && !requests))
         return fail(PIC_ERR_INVALID_ARG, "chunk or request array is NULL");
-    if (dst->page_size < 0 || dst->reserved != 0)
-        return fail(PIC_ERR_INVALID_ARG, "bad destination geometry");
-    const bool paged = dst->page_size > 0;
-    if (!paged && dst->capacity_tokens < 0)
-        return fail(PIC_ERR_INVALID_ARG, "negative capacity");
-    if (paged && dst->num_phys_pages < 0)
-        return fail(PIC_ERR_INVALID_ARG, "negative physical page count");
+    if (geom->dst_page_size < 0 || geom->src_page_size < 0)
+        return fail(PIC_ERR_INVALID_ARG, "negative page size");
+    const bool paged = geom->dst_page_size > 0;
+    const bool src_paged = geom->src_page_size > 0;
+    if (!paged && geom->dst_capacity < 0) return fail(PIC_ERR_INVALID_ARG, "negative capacity");
+    if (paged && geom->dst_num_pages < 0)
+        return fail(PIC_ERR_INVALID_ARG, "negative destination page count");
+    if (src_paged && geom->src_num_pages < 0)
+        return fail(PIC_ERR_INVALID_ARG, "negative pool page count");
     for (int r = 0; r < n_requests; r++) {
         const pic_request &rq = requests[r];
         if (rq.n_entries < 0 || (rq.n_entries > 0 && !rq.entries))
@@ -241,27 +251,36 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
         if (paged && (rq.n_pages < 0 || (rq.n_pages > 0 && !rq.page_table)))
             return fail(PIC_ERR_INVALID_ARG, "request %d: bad page table", r);
     }
+    if (src_paged)
+        for (int c = 0; c < n_chunks; c++)
+            if (chunks[c].n_pages < 0 || (chunks[c].n_pages > 0 && !chunks[c].page_table))
+                return fail(PIC_ERR_INVALID_ARG, "chunk %d: bad page table", c);
 
     // ranges
-    int64_t pool_need = 0;
+    const int64_t sps = geom->src_page_size;
+    int64_t pool_need = src_paged ? geom->src_num_pages * sps : 0;
     for (int c = 0; c < n_chunks; c++) {
-        if (chunks[c].token_start < 0 || chunks[c].length < 1 || chunks[c].reserved != 0)
-            return fail(PIC_ERR_RANGE, "chunk %d: token_start %lld, length %d", c,
-                        static_cast<long long>(chunks[c].token_start), chunks[c].length);
-        pool_need = std::max(pool_need, chunks[c].token_start + chunks[c].length);
+        const pic_chunk &ch = chunks[c];
+        if (ch.token_start < 0 || ch.length < 1 ||
+            (src_paged && ch.token_start + ch.length > static_cast<int64_t>(ch.n_pages) * sps))
+            return fail(PIC_ERR_RANGE, "chunk %d: tokens [%lld, %lld)", c,
+                        static_cast<long long>(ch.token_start),
+                        static_cast<long long>(ch.token_start + ch.length));
+        if (!src_paged) pool_need = std::max(pool_need, ch.token_start + ch.length);
     }
     for (int r = 0; r < n_requests; r++) {
         const pic_request &rq = requests[r];
         const int64_t span =
-            paged ? static_cast<int64_t>(rq.n_pages) * dst->page_size : dst->capacity_tokens;
+            paged ? static_cast<int64_t>(rq.n_pages) * geom->dst_page_size : geom->dst_capacity;
         for (int j = 0; j < rq.n_entries; j++) {
             const pic_entry &e = rq.entries[j];
             if (e.reserved != 0) return fail(PIC_ERR_RANGE, "request %d entry %d: reserved", r, j);
             if (e.chunk_id < 0 || e.chunk_id >= n_chunks)
                 return fail(PIC_ERR_RANGE, "request %d entry %d: chunk_id %d", r, j, e.chunk_id);
-            if (e.length < 1 || e.length > chunks[e.chunk_id].length)
+            const pic_chunk &ch = chunks[e.chunk_id];
+            if (e.length < 1 || e.length > ch.length)
                 return fail(PIC_ERR_RANGE, "request %d entry %d: length %d of a %d-token chunk", r,
-                            j, e.length, chunks[e.chunk_id].length);
+                            j, e.length, ch.length);
             if (e.recompute_k < 0 || e.recompute_k > e.length)
                 return fail(PIC_ERR_RANGE, "request %d entry %d: recompute_k %d", r, j,
                             e.recompute_k);
@@ -271,15 +290,27 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
                             "[0, %lld)", r, j, static_cast<long long>(e.dst_offset),
                             static_cast<long long>(e.dst_offset + e.length),
                             static_cast<long long>(span));
-            if (paged && e.recompute_k < e.length) {
-                const int64_t p0 = (e.dst_offset + e.recompute_k) / dst->page_size;
-                const int64_t p1 = (e.dst_offset + e.length - 1) / dst->page_size;
+            if (e.recompute_k == e.length) continue;  // nothing read or written
+            if (paged) {
+                const int64_t p0 = (e.dst_offset + e.recompute_k) / geom->dst_page_size;
+                const int64_t p1 = (e.dst_offset + e.length - 1) / geom->dst_page_size;
                 for (int64_t pg = p0; pg <= p1; pg++) {
                     const int32_t phys = rq.page_table[pg];
-                    if (phys < 0 || phys >= dst->num_phys_pages)
+                    if (phys < 0 || phys >= geom->dst_num_pages)
                         return fail(PIC_ERR_RANGE, "request %d: logical page %lld maps to %d "
-                                    "(pool has %lld)", r, static_cast<long long>(pg), phys,
-                                    static_cast<long long>(dst->num_phys_pages));
+                                    "(destination has %lld)", r, static_cast<long long>(pg),
+                                    phys, static_cast<long long>(geom->dst_num_pages));
+                }
+            }
+            if (src_paged) {
+                const int64_t p0 = (ch.token_start + e.recompute_k) / sps;
+                const int64_t p1 = (ch.token_start + e.length - 1) / sps;
+                for (int64_t pg = p0; pg <= p1; pg++) {
+                    const int32_t phys = ch.page_table[pg];
+                    if (phys < 0 || phys >= geom->src_num_pages)
+                        return fail(PIC_ERR_RANGE, "chunk %d: page %lld maps to %d (pool has "
+                                    "%lld)", e.chunk_id, static_cast<long long>(pg), phys,
+                                    static_cast<long long>(geom->src_num_pages));
                 }
             }
         }
@@ -297,7 +328,7 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     }
     if (paged) {
         std::vector<Interval> iv;
-        const int64_t ps = dst->page_size;
+        const int64_t ps = geom->dst_page_size;
         for (int r = 0; r < n_requests; r++)
             for (int j = 0; j < requests[r].n_entries; j++) {
                 const pic_entry &e = requests[r].entries[j];
@@ -320,24 +351,35 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.rope_dim = rope->rope_dim;
     p.style = rope->style;
     p.mode = paged ? kPaged : kContiguous;
-    p.page_size = dst->page_size;
-    p.capacity = dst->capacity_tokens;
-    p.num_phys_pages = dst->num_phys_pages;
+    p.page_size = geom->dst_page_size;
+    p.capacity = geom->dst_capacity;
+    p.num_phys_pages = geom->dst_num_pages;
+    p.src_page_size = geom->src_page_size;
     p.n_requests = n_requests;
     p.u = u;
     p.launch = launch_shape_of(shape->dtype, u);
     p.tile_tokens = kTileSteps * 4 * p.launch.g;
     {
         // Pool rows read more than once per layer (a chunk placed twice, or
-        // chunks sharing tokens) may be served from cache on the second
-        // read; only a plan that reads every row once streams its loads.
+        // chunks sharing rows) may be served from cache on the second read;
+        // only a plan that reads every row once streams its loads.
         std::vector<Interval> iv;
         for (int r = 0; r < n_requests; r++)
             for (int j = 0; j < requests[r].n_entries; j++) {
                 const pic_entry &e = requests[r].entries[j];
-                const int64_t t0 = chunks[e.chunk_id].token_start;
-                if (e.recompute_k < e.length)
-                    iv.push_back(Interval{0, t0 + e.recompute_k, t0 + e.length});
+                const pic_chunk &ch = chunks[e.chunk_id];
+                int64_t t = ch.token_start + e.recompute_k;
+                const int64_t end = ch.token_start + e.length;
+                while (t < end) {
+                    if (!src_paged) {
+                        iv.push_back(Interval{0, t, end});
+                        break;
+                    }
+                    const int64_t slot = t % sps;
+                    const int64_t run = std::min(sps - slot, end - t);
+                    iv.push_back(Interval{ch.page_table[t / sps], slot, slot + run});
+                    t += run;
+                }
             }
         p.launch.stream_loads = any_overlap(iv) ? 0 : 1;
     }
@@ -362,7 +404,8 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             }
             const HostEntry he{c.token_start, e.dst_offset, r, 0, cs_idx, 0};
             p.entries.push_back(he);
-            add_tiles(&p, he, paged ? rq.page_table : nullptr, e.recompute_k, e.length);
+            add_tiles(&p, he, paged ? rq.page_table : nullptr,
+                      src_paged ? c.page_table : nullptr, e.recompute_k, e.length);
             p.bounds.insert(p.bounds.end(), {r, e.dst_offset, e.dst_offset + e.length});
             p.recompute.insert(p.recompute.end(), {r, e.dst_offset, e.dst_offset + e.recompute_k});
             written += e.length - e.recompute_k;
@@ -429,7 +472,7 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
         }
         const HostEntry he{s.token_start, s.token_start, 0, 0, cs_idx, 0};
         p.entries.push_back(he);
-        add_tiles(&p, he, nullptr, s.recompute_k, s.length);
+        add_tiles(&p, he, nullptr, nullptr, s.recompute_k, s.length);
         written += s.length - s.recompute_k;
     }
     fill_info(&p, written, masked, buf_tokens);
@@ -456,7 +499,7 @@ extern "C" {
 
 pic_status pic_plan(const pic_kv_shape *shape, const pic_rope_config *rope,
                     const pic_chunk *chunks, int32_t n_chunks, const pic_request *requests,
-                    int32_t n_requests, const pic_dst_geom *dst, pic_plan_t **out) {
+                    int32_t n_requests, const pic_geom *geom, pic_plan_t **out) {
     pic::clear_error();
     if (!out) return pic::fail(PIC_ERR_INVALID_ARG, "out must not be NULL");
     *out = nullptr;
@@ -464,7 +507,7 @@ pic_status pic_plan(const pic_kv_shape *shape, const pic_rope_config *rope,
     if (!plan) return pic::fail(PIC_ERR_NOMEM, "out of host memory");
     try {
         pic_status st =
-            pic::build_stitch(shape, rope, chunks, n_chunks, requests, n_requests, dst, &plan->prob);
+            pic::build_stitch(shape, rope, chunks, n_chunks, requests, n_requests, geom, &plan->prob);
         if (st) {
             delete plan;
             return st;

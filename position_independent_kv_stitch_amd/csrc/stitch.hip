@@ -59,10 +59,11 @@ struct KArgs {
     const void *src_v;
     void *dst_k;
     void *dst_v;
-    int64_t s_layer, s_tok, s_head;                 // source strides
+    int64_t s_layer, s_tok, s_head, s_page;         // source strides
     int64_t d_layer, d_tok, d_head, d_page, d_req;  // destination strides
     int32_t layer_begin;
     int32_t mode;         // DstMode
+    int32_t src_paged;    // 1: the pool is paged (tile.src_row is a page)
     int32_t rope_offset;
     int32_t half_r;
     int32_t nr, uph_shift;  // rotary units per token, log2(units per head)
@@ -278,7 +279,9 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
     const void *sv = a.src_v;
     void *dk = a.dst_k;
     void *dv = a.dst_v;
-    const int64_t s0 = layer * a.s_layer + T.src_row * a.s_tok;
+    const int64_t s0 = layer * a.s_layer +
+                       (a.src_paged ? T.src_row * a.s_page + static_cast<int64_t>(T.src_slot) * a.s_tok
+                                    : T.src_row * a.s_tok);
     int64_t d0;
     if (a.mode == kInPlace)
         d0 = s0;
@@ -531,6 +534,8 @@ pic_status pic_stitch(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_vi
     a.s_layer = pool->layer_stride;
     a.s_tok = pool->token_stride;
     a.s_head = pool->head_stride;
+    a.s_page = pool->page_stride;
+    a.src_paged = p.src_page_size > 0 ? 1 : 0;
     a.d_layer = dst->layer_stride;
     a.d_tok = dst->token_stride;
     a.d_head = dst->head_stride;

@@ -15,7 +15,8 @@ import pytest
 import oracle
 from parity_util import (check_stitch_case, compare_bits, compare_k, max_abs, to_host)
 from pic_workloads import (Chunk, Entry, Request, Segment, Workload, config1, config2, config3,
-                           config4, config5, pool_values, random_small, sentinel_like)
+                           config4, config5, pool_values, random_small, sentinel_like,
+                           with_paged_pool)
 
 pytestmark = pytest.mark.gpu
 
@@ -62,6 +63,25 @@ def test_special_shifts(torch_cuda, dt, paged):
                           max_len=300, deltas=[0, 1, -1, 65536, -65536, 123457, -98765])
         say(f"special shifts seed={50 + seed} {dt} paged={paged}")
         check_stitch_case(wl, seed=seed)
+
+
+PAGED_POOL_CASES = [(seed, dt, paged, mla, ps)
+                    for seed in range(2)
+                    for dt in ("f32", "bf16")
+                    for paged in (False, True)
+                    for mla in (False, True)
+                    for ps in (4, 16)]
+
+
+@pytest.mark.parametrize("seed,dt,paged,mla,ps", PAGED_POOL_CASES)
+def test_paged_pool_small(torch_cuda, seed, dt, paged, mla, ps):
+    """Chunks read through their pool page tables (first tokens part-way into
+    a page, pages in random order), into contiguous or paged destinations."""
+    wl = with_paged_pool(random_small(20 + seed, dtype=dt, paged=paged, mla=mla, n_requests=3,
+                                      n_layers=2, max_len=120),
+                         page_size=ps, seed=seed, first_offsets=True, spare_pages=2)
+    say(f"paged pool seed={seed} {dt} paged={paged} mla={mla} ps={ps}")
+    check_stitch_case(wl, seed=seed)
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -239,6 +259,22 @@ def test_config2_full(torch_cuda):
     say("config2: oracle on sampled layers")
     _layer_compare_stitch(wl, pk, pv, dk, dv, [0, 13, 31])
     _all_layer_properties(torch, wl, pk, pv, dk, dv)
+
+
+def test_config2_paged_pool_full(torch_cuda):
+    """The Llama-3-8B-shaped stitch reading its chunks from a paged pool of
+    16-token blocks in random order: 32 layers in one launch."""
+    torch = torch_cuda
+    import position_independent_kv_stitch_amd as pic
+    wl = with_paged_pool(config2(), page_size=16, seed=1)
+    say("config2 paged pool: generating inputs")
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
+    dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
+    dv = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    pic.stitch(plan, pk, pv, dk, dv)
+    torch.cuda.synchronize()
+    _layer_compare_stitch(wl, pk, pv, dk, dv, [0, 19, 31])
 
 
 def test_config4_mla_full(torch_cuda):

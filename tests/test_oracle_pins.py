@@ -7,6 +7,7 @@ arithmetic, torch's bf16 conversion), brute-force enumeration, and
 brute-force attention on tiny inputs.  A dropped term, a wrong sign, a
 swapped pair member or a wrong frequency index fails at least one of them.
 """
+import copy
 import json
 import math
 import os
@@ -15,7 +16,8 @@ import numpy as np
 import pytest
 
 import oracle
-from pic_workloads import Chunk, Entry, Request, Segment, Workload, random_small
+from pic_workloads import (Chunk, Entry, Request, Segment, Workload, random_small,
+                           with_paged_pool)
 
 SENT_F64 = np.float64(-12345.5)
 
@@ -317,17 +319,22 @@ def test_brute_force_attention_on_stitched_cache(style):
 
 # ----------------------------------------------- placement, copy and masking
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(16))
 def test_placement_copy_mask_brute_force(seed):
     """Every destination row is, by brute force over (request, entry, token):
     the source row (V and non-rotary K bits unchanged, the rotary slice equal
     to the complex-multiplication rotation), or untouched when masked or not
-    covered.  Random ragged problems, contiguous and paged, GQA and MLA rows."""
+    covered.  Random ragged problems, contiguous and paged destinations,
+    contiguous and paged pools, GQA and MLA rows."""
     paged = seed % 2 == 1
     mla = seed % 3 == 2
     style = "interleaved" if seed % 4 == 3 else "half"
     wl = random_small(seed, dtype="f32", style=style, paged=paged, mla=mla, n_requests=3,
                       n_layers=2)
+    paged_pool = seed >= 8
+    if paged_pool:
+        wl = with_paged_pool(wl, page_size=[4, 16, 8][seed % 3], seed=seed,
+                             first_offsets=seed % 2 == 0, spare_pages=3)
     wl.dtype = "f64"
     rng = np.random.default_rng(100 + seed)
     pk = rng.standard_normal(wl.pool_shape())
@@ -351,11 +358,17 @@ def test_placement_copy_mask_brute_force(seed):
                           pos % wl.page_size)
                 else:
                     at = (slice(None), r, pos)
-                got_k, src_k = dk[at], pk[:, ch.token_start + t]
+                if paged_pool:  # the chunk's token t through its page table
+                    off = ch.token_start + t
+                    src = (slice(None), int(ch.page_table[off // wl.src_page_size]),
+                           off % wl.src_page_size)
+                else:
+                    src = (slice(None), ch.token_start + t)
+                got_k, src_k = dk[at], pk[src]
                 written[at] = True
                 assert np.array_equal(got_k[..., plain], src_k[..., plain])
                 if wl.has_v:
-                    assert np.array_equal(dv[at], pv[:, ch.token_start + t])
+                    assert np.array_equal(dv[at], pv[src])
                 for i in range(wl.rope_dim // 2):
                     a, b = pair_index(style, wl.rope_dim, i)
                     a, b = a + wl.rope_offset, b + wl.rope_offset
@@ -576,3 +589,20 @@ def test_validation_overlaps_and_no_write_on_error():
     assert oracle.validate_inplace(ip) == "overlap"
     ip.segments = [Segment(0, 5, 1), Segment(5, 6, 1)]
     assert oracle.validate_inplace(ip) == "range"
+
+
+def test_validation_paged_pool():
+    """Paged pool: chunks must fit their page tables, pages read must exist;
+    pages of masked tokens are not read."""
+    base = Workload("pp", "f32", 1, 1, 8, 0, 8, "half", 1e4, True, capacity=40,
+                    chunks=[Chunk(2, 10, 0, np.array([5, 1, 3], np.int32))],
+                    requests=[Request([Entry(0, 0, 10, 0)])], src_page_size=4, src_n_pages=6)
+    assert oracle.validate_stitch(base) == "ok"
+    w = copy.deepcopy(base)
+    w.chunks = [Chunk(3, 10, 0, np.array([5, 1, 3], np.int32))]  # 3 + 10 > 3 pages x 4
+    assert oracle.validate_stitch(w) == "range"
+    w = copy.deepcopy(base)
+    w.chunks = [Chunk(2, 10, 0, np.array([5, 6, 3], np.int32))]  # page 6 of 6
+    assert oracle.validate_stitch(w) == "range"
+    w.requests = [Request([Entry(0, 0, 10, 6)])]  # page 6 holds tokens 2..5 only: masked
+    assert oracle.validate_stitch(w) == "ok"

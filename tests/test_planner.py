@@ -11,7 +11,7 @@ import oracle
 import position_independent_kv_stitch_amd as pic
 from position_independent_kv_stitch_amd import _binding as B
 from pic_workloads import (CONFIGS, Chunk, Entry, Request, Segment, Workload, config2,
-                           config3, random_small)
+                           config3, random_small, with_paged_pool)
 
 ORACLE_TO_LIB = {"ok": "ok", "bad_arg": "invalid_arg", "range": "range", "overlap": "overlap"}
 
@@ -47,7 +47,7 @@ def _mutations(wl, rng):
         return w
     j = int(rng.integers(0, len(req.entries)))
     e = req.entries[j]
-    kind = int(rng.integers(0, 16))
+    kind = int(rng.integers(0, 17))
     if kind == 0:
         req.entries[j] = Entry(int(rng.choice([-1, len(w.chunks), 10 ** 6])), e.dst_offset,
                                e.length, e.recompute_k)
@@ -81,7 +81,7 @@ def _mutations(wl, rng):
         c = int(rng.integers(0, len(w.chunks)))
         ch = w.chunks[c]
         w.chunks[c] = Chunk(int(rng.choice([-1, ch.token_start])), int(rng.choice([0, ch.length])),
-                            ch.base_pos)
+                            ch.base_pos, ch.page_table)
     elif kind == 10:
         w.rope_dim = int(rng.choice([0, 7, w.row_dim + 8]))
     elif kind == 11:
@@ -90,6 +90,18 @@ def _mutations(wl, rng):
         w.theta = float(rng.choice([0.0, -1.0]))
     elif kind == 13:
         w.rope_offset = w.row_dim  # slice outside the row
+    elif kind == 15 and w.src_page_size:
+        c = e.chunk_id
+        if 0 <= c < len(w.chunks):
+            ch = w.chunks[c]
+            pt = ch.page_table.copy()
+            choice = int(rng.integers(0, 3))
+            if choice == 0:
+                pt[int(rng.integers(0, len(pt)))] = int(rng.choice([-1, w.src_n_pages]))
+            elif choice == 1:
+                pt = pt[:-1]  # one page short
+            w.chunks[c] = Chunk(ch.token_start + (choice == 2) * w.src_page_size, ch.length,
+                                ch.base_pos, pt)
     elif kind == 14:  # harmless: duplicate an entry's chunk id into a new tail entry
         last = max(e.dst_offset + e.length for e in req.entries)
         req.entries.append(Entry(e.chunk_id, last, 1, 0))
@@ -107,11 +119,14 @@ def test_invalid_problems_agree_with_oracle(seed):
     rng = np.random.default_rng(1000 + seed)
     base = random_small(seed, dtype="bf16", paged=seed % 2 == 0, mla=seed % 7 == 3,
                         n_requests=1 + seed % 3)
+    if seed % 3 == 1:
+        base = with_paged_pool(base, page_size=[4, 16][seed % 2], seed=seed,
+                               first_offsets=True, spare_pages=seed % 4)
     w = _mutations(base, rng)
     if seed % 5 == 0:
         w = _mutations(w, rng)  # two defects: both sides must report the first one
     want = oracle.validate_stitch(w)
-    if want == "ok" and not pool_fits(w):
+    if want == "ok" and not w.src_page_size and not pool_fits(w):
         pytest.skip("defect only visible against the pool tensor")
     got = plan_status(w)
     if got == "align" and want == "ok":
@@ -221,3 +236,28 @@ def test_inplace_valid_reaches_the_view_check():
                   n_tokens=10, segments=[Segment(0, 5, 3), Segment(5, 5, -2, 1)])
     assert oracle.validate_inplace(wl) == "ok"
     assert _inplace_status(wl) == "invalid_arg"
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_paged_pool_plans(seed):
+    """Paged pools: tiles never cross a pool page or a destination page, and
+    the planner agrees with the oracle on valid tables."""
+    wl = with_paged_pool(random_small(seed, dtype="bf16", paged=seed % 2 == 0, n_requests=2),
+                         page_size=[4, 8, 16][seed % 3], seed=seed, first_offsets=True)
+    assert oracle.validate_stitch(wl) == "ok"
+    p = pic.Plan.from_workload(wl)
+    ents = [e for r in wl.requests for e in r.entries]
+    tt = p.info["tile_tokens"]
+    tiles = 0
+    for e in ents:
+        ch = wl.chunks[e.chunk_id]
+        t = e.recompute_k
+        while t < e.length:
+            n = min(tt, e.length - t)
+            if wl.page_size:
+                n = min(n, wl.page_size - (e.dst_offset + t) % wl.page_size)
+            n = min(n, wl.src_page_size - (ch.token_start + t) % wl.src_page_size)
+            t += n
+            tiles += 1
+    assert p.info["n_tiles"] == tiles
+    assert p.info["pool_tokens_required"] == wl.src_n_pages * wl.src_page_size
