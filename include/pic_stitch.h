@@ -123,12 +123,15 @@ typedef struct pic_entry {
 
 /* A request's placement table (host memory, read during pic_plan only).
  * page_table maps logical page j to a physical page of the paged
- * destination; it is ignored for a contiguous destination. */
+ * destination; it is ignored for a contiguous destination.  context_len is
+ * the request's context for pic_attend: positions [0, context_len); 0 means
+ * up to the end of its last entry. */
 typedef struct pic_request {
     const pic_entry *entries;
     const int32_t *page_table;
     int32_t n_entries;
     int32_t n_pages;
+    int64_t context_len;
 } pic_request;
 
 /* Pool and destination geometry.  Destination: dst_page_size 0 =
@@ -190,6 +193,8 @@ typedef struct pic_plan_info_t {
     int64_t bytes_written_per_layer;
     int64_t tile_tokens;          /* most tokens of one work tile (paged tiles also stop at
                                      page ends) */
+    int64_t context_tokens;       /* pic_attend: sum of context_len over requests */
+    int64_t attend_blocks;        /* pic_attend: (request, 256-token block) work items */
 } pic_plan_info_t;
 
 typedef struct pic_plan pic_plan_t;
@@ -263,6 +268,53 @@ pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *
                               const pic_kv_view *buf, int64_t buf_tokens,
                               const pic_segment *segments, int32_t n_segments,
                               int32_t layer_begin, int32_t layer_end, void *stream);
+
+/*
+ * Decode attention over a request's context without writing the stitched
+ * cache (Irminsul, Technical Summary sections 2.2 and 4: the delta-rotation
+ * applied in the attention kernel's HBM-to-on-chip load path).  For every
+ * request r and query head j (KV head j / (num_q_heads / num_heads)):
+ *   out[r][j] = sum_p w_p V_p / sum_p w_p,  w_p = exp(scale * q . K_p + b_p)
+ * over positions p in [0, context_len).  Positions an entry writes (tokens
+ * [recompute_k, length)) read the chunk's pool row and turn its rotary slice
+ * by the entry's delta on load (fp32); every other position (prefix, gaps,
+ * tokens left for recompute) reads the request's own cache `cache` (the
+ * plan's destination geometry) unrotated.  b_p = sink_bias for the first
+ * sink_tokens positions of every entry placed after position 0 (the EPIC
+ * Guide's LegoLink pseudo-sink damping, section "1. Identifying and
+ * Neutralizing Pseudo-Sinks" and its listing: 4 tokens, -15), else 0.
+ * Query rows are post-RoPE (rotated for the query's own position).
+ */
+typedef struct pic_attend_args {
+    const void *q;        /* device [request][q head][row_dim], the plan's dtype */
+    int64_t q_request_stride, q_head_stride;
+    float *out;           /* device [request][q head][row_dim], fp32 */
+    int64_t out_request_stride, out_head_stride;
+    int32_t num_q_heads;  /* a multiple of the plan's num_heads */
+    int32_t layer;        /* layer of the views */
+    float scale;          /* logit scale, e.g. 1/sqrt(row_dim) */
+    int32_t sink_tokens;  /* LegoLink damping: tokens per chunk start (0 = off) */
+    float sink_bias;      /* LegoLink damping: logit offset (the EPIC listing: -15) */
+    int32_t reserved;
+} pic_attend_args;
+
+/*
+ * pic_attend -- enqueue decode attention for every request of a plan at one
+ * layer (see above).  GQA rows only (has_v = 1, rope_offset 0 or any slice);
+ * row_dim / (16 / element size) must be a power of two and row_dim <= 256
+ * (else PIC_ERR_ALIGN); q rows 16-byte aligned (PIC_ERR_ALIGN);
+ * num_q_heads a multiple of num_heads, at most 8x (PIC_ERR_INVALID_ARG).
+ * Each request's context must be non-empty and, in a paged cache, every
+ * page it covers must be in [0, dst_num_pages) (PIC_ERR_RANGE).  In-place
+ * plans are refused (PIC_ERR_STATE).
+ *
+ * The first call allocates the plan's partial-result workspace on the
+ * device (freed with the plan; a call with more query heads grows it after
+ * waiting for the device).  Calls on one plan share that workspace: calls
+ * that may overlap (different streams) race; order them on one stream.
+ */
+pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
+                      const pic_attend_args *args, void *stream);
 
 /* pic_plan_info -- sizes and algorithmic byte counts of a plan. */
 pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info);

@@ -4,5 +4,5 @@ TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 benchmark's CPU-baseline leg are its only users.  The product path never
 imports it, and it shares no code with the HIP library.
 """
-from .ref import (inv_freq, recompute_ranges, rotate_inplace, round_bf16, stitch,  # noqa: F401
-                  validate_inplace, validate_stitch)
+from .ref import (attend, inv_freq, recompute_ranges, rotate_inplace, round_bf16,  # noqa: F401
+                  stitch, validate_inplace, validate_stitch)

@@ -260,3 +260,79 @@ class _Layers:
 
     def __getattr__(self, name):
         return getattr(self._wl, name)
+
+
+def _to_f64(a):
+    """Storage values (float32, or bf16 as uint16 bits) widened exactly to fp64."""
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def attend(wl, pool_k, pool_v, cache_k, cache_v, q, layer, scale=None, sink_tokens=0,
+           sink_bias=0.0, layer_base=0):
+    """Decode attention of every request at `layer`, in fp64 (returns
+    [requests][q heads][row_dim] float64).
+
+    A request's context is positions [0, context_len) (0: up to its last
+    entry's end).  Positions an entry writes take the chunk's key turned by
+    the entry's shift, computed exactly by this oracle's stitch in fp64
+    (no rounding to storage), and the chunk's value; every other position
+    takes the request's own cache row.  Query head j uses KV head
+    j // (num_q_heads / n_heads).  logit_p = scale * q . K_p, plus
+    sink_bias on the first sink_tokens positions of every entry placed after
+    position 0 (the EPIC Guide's LegoLink listing: -15 on 4 tokens); the
+    weights are softmax over the context and the output their weighted sum
+    of values (the plain definition of attention).
+    """
+    from types import SimpleNamespace as NS
+    li = layer - layer_base
+    H, D = wl.n_heads, wl.row_dim
+    R, Hq = q.shape[0], q.shape[1]
+    G = Hq // H
+    sc = D ** -0.5 if scale is None else scale
+    out = np.zeros((R, Hq, D))
+    pk64 = _to_f64(pool_k[li:li + 1])
+    pv64 = _to_f64(pool_v[li:li + 1])
+    for r, rq in enumerate(wl.requests):
+        L = rq.context_len or max([e.dst_offset + e.length for e in rq.entries] + [0])
+        if L == 0:
+            raise ValueError(f"request {r} has an empty context")
+        # the request's own cache rows
+        pos = np.arange(L)
+        if wl.page_size:
+            pt = np.asarray(rq.page_table)
+            k = _to_f64(cache_k[li][pt[pos // wl.page_size], pos % wl.page_size])
+            v = _to_f64(cache_v[li][pt[pos // wl.page_size], pos % wl.page_size])
+        else:
+            k = _to_f64(cache_k[li][r, :L])
+            v = _to_f64(cache_v[li][r, :L])
+        # chunk rows, turned exactly: the stitch oracle in fp64 into a scratch request
+        cap = max(L, max([e.dst_offset + e.length for e in rq.entries] + [0]))
+        sub = NS(dtype="f64", n_layers=1, n_heads=H, row_dim=D, rope_offset=wl.rope_offset,
+                 rope_dim=wl.rope_dim, style=wl.style, theta=wl.theta, inv_freq=wl.inv_freq,
+                 has_v=True, pool_tokens=wl.pool_tokens, chunks=wl.chunks,
+                 src_page_size=getattr(wl, "src_page_size", 0),
+                 src_n_pages=getattr(wl, "src_n_pages", 0),
+                 requests=[NS(entries=rq.entries, page_table=None)], page_size=0, capacity=cap,
+                 n_phys_pages=0)
+        sk = np.zeros((1, 1, cap, H, D))
+        sv = np.zeros((1, 1, cap, H, D))
+        st = stitch(sub, pk64, pv64, sk, sv, 0, 1, dtype="f64")
+        if st != "ok":
+            raise ValueError(f"request {r}: {st}")
+        bias = np.zeros(L)
+        for e in rq.entries:
+            lo, hi = e.dst_offset + e.recompute_k, min(e.dst_offset + e.length, L)
+            if lo < hi:
+                k[lo:hi] = sk[0, 0, lo:hi]
+                v[lo:hi] = sv[0, 0, lo:hi]
+            if e.dst_offset > 0 and sink_tokens > 0:
+                bias[e.dst_offset:min(e.dst_offset + sink_tokens, L)] = sink_bias
+        qq = _to_f64(q[r])
+        for j in range(Hq):
+            h = j // G
+            logits = sc * (k[:, h, :] @ qq[j]) + bias
+            w = np.exp(logits - logits.max())
+            out[r, j] = (w @ v[:, h, :]) / w.sum()
+    return out

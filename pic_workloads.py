@@ -51,6 +51,7 @@ class Entry:
 class Request:
     entries: List[Entry]
     page_table: Optional[np.ndarray] = None  # int32 physical page per logical page
+    context_len: int = 0  # attention context [0, context_len); 0 = up to the last entry
 
 
 @dataclass(frozen=True)

@@ -26,8 +26,8 @@ DTYPES = {"f32": 0, "bf16": 1}
 STYLES = {"half": 0, "interleaved": 1}
 
 # every entry point the header declares
-EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_plan_info", "pic_plan_ranges",
-           "pic_plan_destroy", "pic_last_error")
+EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_attend", "pic_plan_info",
+           "pic_plan_ranges", "pic_plan_destroy", "pic_last_error")
 
 
 class PicError(RuntimeError):
@@ -59,7 +59,15 @@ class EntryC(C.Structure):
 
 class RequestC(C.Structure):
     _fields_ = [("entries", C.POINTER(EntryC)), ("page_table", C.POINTER(C.c_int32)),
-                ("n_entries", C.c_int32), ("n_pages", C.c_int32)]
+                ("n_entries", C.c_int32), ("n_pages", C.c_int32), ("context_len", C.c_int64)]
+
+
+class AttendArgs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("q_request_stride", C.c_int64),
+                ("q_head_stride", C.c_int64), ("out", C.c_void_p),
+                ("out_request_stride", C.c_int64), ("out_head_stride", C.c_int64),
+                ("num_q_heads", C.c_int32), ("layer", C.c_int32), ("scale", C.c_float),
+                ("sink_tokens", C.c_int32), ("sink_bias", C.c_float), ("reserved", C.c_int32)]
 
 
 class Geom(C.Structure):
@@ -83,7 +91,7 @@ class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "n_requests", "n_entries", "n_tiles", "tokens_written", "tokens_masked",
         "pool_tokens_required", "bytes_read_per_layer", "bytes_written_per_layer",
-        "tile_tokens")]
+        "tile_tokens", "context_tokens", "attend_blocks")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -132,6 +140,8 @@ def _configure(lib):
     lib.pic_rotate_inplace.argtypes = [P(KvShape), P(RopeConfig), P(KvView), C.c_int64,
                                        P(SegmentC), C.c_int32, C.c_int32, C.c_int32,
                                        C.c_void_p]
+    lib.pic_attend.restype = C.c_int
+    lib.pic_attend.argtypes = [C.c_void_p, P(KvView), P(KvView), P(AttendArgs), C.c_void_p]
     lib.pic_plan_info.restype = C.c_int
     lib.pic_plan_info.argtypes = [C.c_void_p, P(PlanInfo)]
     lib.pic_plan_ranges.restype = C.c_int
@@ -239,7 +249,8 @@ class Plan:
                 pta = np.ascontiguousarray(np.asarray(pt, dtype=np.int32))
                 keep.append(pta)
                 pt_ptr, n_pages = pta.ctypes.data_as(C.POINTER(C.c_int32)), len(pta)
-            rarr[r] = RequestC(earr, pt_ptr, len(entries), n_pages)
+            rarr[r] = RequestC(earr, pt_ptr, len(entries), n_pages,
+                               int(getattr(rq, "context_len", 0) or 0))
         geom = Geom(page_size, src_page_size, capacity, n_phys_pages, src_n_pages)
         _check(lib.pic_plan(C.byref(shape), C.byref(rope), carr, len(chunks), rarr,
                             len(requests), C.byref(geom), C.byref(self._handle)), lib)
@@ -382,6 +393,50 @@ def stitch(plan: Plan, pool_k, pool_v, dst_k, dst_v, layer_begin: int = 0,
     lib = plan._lib  # the build that made the plan runs it
     _check(lib.pic_stitch(plan.handle, C.byref(pv), C.byref(dv), layer_begin, le,
                           _stream_of(pool_k, stream)), lib)
+
+
+def attend(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: int, out=None,
+           scale: Optional[float] = None, sink_tokens: int = 0, sink_bias: float = 0.0,
+           stream=None):
+    """Enqueue pic_attend: decode attention of every request of the plan at
+    `layer`.  q: [requests][q heads][row_dim] in the plan's dtype (post-RoPE);
+    pool_* as for stitch(); cache_*: the requests' own KV in the plan's
+    destination geometry.  Returns out, fp32 [requests][q heads][row_dim]."""
+    torch = _torch()
+    if _dtype_name(q) != plan.dtype or q.dim() != 3 or q.stride(-1) != 1:
+        raise TypeError("q must be [requests][q heads][row_dim] in the plan's dtype")
+    if q.shape[0] != plan.n_requests or q.shape[2] != plan.row_dim:
+        raise ValueError("q shape does not match the plan")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != q.shape or out.stride(-1) != 1:
+        raise TypeError("out must be fp32 with q's shape")
+    if plan.src_page_size:
+        if pool_k.dim() != 5 or pool_k.shape[1] < plan.src_n_pages:
+            raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
+        pv = _view(pool_k, pool_v, "paged-pool")
+    else:
+        if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+            raise PicError(PIC_ERR_RANGE, "pool tensor smaller than the plan needs")
+        pv = _view(pool_k, pool_v, "pool")
+    if plan.page_size:
+        if cache_k.shape[1] < plan.n_phys_pages or cache_k.shape[2] != plan.page_size:
+            raise ValueError("paged cache smaller than the plan's page pool")
+        cv = _view(cache_k, cache_v, "paged")
+    else:
+        if cache_k.shape[1] < plan.n_requests or cache_k.shape[2] < plan.capacity:
+            raise ValueError("contiguous cache smaller than requests x capacity")
+        cv = _view(cache_k, cache_v, "contig")
+    if not (0 <= layer < min(pool_k.shape[0], cache_k.shape[0])):
+        raise ValueError("layer beyond the tensors")
+    a = AttendArgs(q.data_ptr(), q.stride(0), q.stride(1), out.data_ptr(), out.stride(0),
+                   out.stride(1), q.shape[1], layer,
+                   float(plan.row_dim ** -0.5 if scale is None else scale), int(sink_tokens),
+                   float(sink_bias), 0)
+    lib = plan._lib
+    _check(lib.pic_attend(plan.handle, C.byref(pv), C.byref(cv), C.byref(a),
+                          _stream_of(q, stream)), lib)
+    return out
 
 
 def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,

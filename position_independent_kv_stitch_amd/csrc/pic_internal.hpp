@@ -37,6 +37,30 @@ struct DevTile {
     int32_t src_slot;  // paged pool: slot of the first token in its page
 };
 
+// pic_attend: a run of consecutive context positions of one request read from
+// one source with consecutive rows.
+enum AttnSrc : int32_t { kPoolRows = 0, kPoolPages = 1, kCacheRows = 2, kCachePages = 3 };
+constexpr int kAttnTileTokens = 64;    // positions per attention tile at most
+constexpr int kAttnBlockTokens = 256;  // positions per attention work item at most
+constexpr int32_t kNoSink = 1 << 30;   // sink distance of runs not after a chunk start
+
+struct AttnTile {
+    int64_t a;          // pool row | pool page | request | destination page
+    int32_t b;          // -      | pool slot | position | destination slot
+    int32_t ntok;
+    int32_t cs_idx;     // pool runs whose chunk moved: shift table; else -1
+    int32_t kind;       // AttnSrc
+    int32_t sink_dist;  // position of the first token minus the last chunk start (> 0 only)
+    int32_t pad;
+};
+
+struct AttnBlock {  // consecutive tiles [tile0, tile0 + ntiles) of one request
+    int32_t request;
+    int32_t tile0;
+    int32_t ntiles;
+    int32_t ntok;
+};
+
 // Host-side record of one placement (entry of a request, or in-place segment).
 struct HostEntry {
     int64_t src_tok;
@@ -87,13 +111,18 @@ struct Problem {
     std::vector<double> cs;       // [table][rope_dim/2][cos, sin]
     std::vector<int64_t> bounds;  // [entry][request, begin, end]
     std::vector<int64_t> recompute;
+    std::vector<AttnTile> atiles;  // pic_attend map, request after request
+    std::vector<AttnBlock> ablocks;
+    std::vector<int64_t> context;  // context_len per request
+    std::vector<int32_t> req_block0;  // first attention block of each request (+ end)
+    std::vector<int32_t> context_bad_page;  // per request: a context page out of range (-1: none)
     pic_plan_info_t info{};
 };
 
 // Everything the device needs, packed into one upload.
 struct Staged {
     std::vector<uint8_t> bytes;
-    size_t off_tiles = 0, off_cs = 0;
+    size_t off_tiles = 0, off_cs = 0, off_atiles = 0, off_ablocks = 0, off_rblock = 0;
 };
 
 // Thread-local error reporting.
@@ -117,6 +146,10 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
 
 Staged stage(const Problem &p);
 
+// Device side (stitch.hip): first-use upload of a plan's metadata, ordered on
+// `stream` (a hipStream_t); view checks shared by the launchers.
+pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream);
+pic_status check_view(const pic_kv_view *v, int vec, bool need_v, const char *name);
 }  // namespace pic
 
 // The opaque plan handle of the C ABI.
@@ -128,4 +161,6 @@ struct pic_plan {
     int device = -1;
     void *d_mem = nullptr;
     void *upload_event = nullptr;  // hipEvent_t
+    void *d_work = nullptr;        // pic_attend partial results
+    size_t work_bytes = 0;
 };

@@ -222,6 +222,94 @@ void add_tiles(Problem *p, const HostEntry &e, const int32_t *dst_pages, const i
     }
 }
 
+// The pic_attend map of one request: positions [0, L) in order, each run of
+// positions with one source (a chunk's written tokens: the pool, turned by
+// the chunk's shift; anything else: the request's own cache) cut into tiles
+// of consecutive rows that stop at pool and cache page ends and at chunk
+// starts, then grouped into blocks.
+void build_attention_map(Problem *p, const pic_chunk *chunks, const pic_request &rq, int32_t r,
+                         const std::vector<int32_t> &cs_of_entry, int32_t entry0) {
+    std::vector<int32_t> order(rq.n_entries);
+    for (int j = 0; j < rq.n_entries; j++) order[j] = j;
+    std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+        return rq.entries[x].dst_offset < rq.entries[y].dst_offset;
+    });
+    int64_t L = rq.context_len;
+    for (int j = 0; j < rq.n_entries; j++)
+        if (rq.context_len == 0) L = std::max(L, rq.entries[j].dst_offset + rq.entries[j].length);
+    p->context.push_back(L);
+
+    const bool paged = p->mode == kPaged;
+    const int32_t tile_begin = static_cast<int32_t>(p->atiles.size());
+    int32_t bad_page = -1;  // a context page no stitch writes may be unmapped; attend checks
+    int64_t last_start = -1;  // last chunk start after position 0
+    // cut [lo, hi) of one source into tiles
+    auto emit = [&](int64_t lo, int64_t hi, const pic_entry *e, const pic_chunk *ch, int32_t cs) {
+        hi = std::min(hi, L);
+        while (lo < hi) {
+            int64_t n = std::min<int64_t>(kAttnTileTokens, hi - lo);
+            AttnTile t{};
+            t.cs_idx = -1;
+            if (e) {  // pool rows of the chunk's tokens
+                const int64_t at = ch->token_start + (lo - e->dst_offset);
+                if (p->src_page_size > 0) {
+                    const int64_t slot = at % p->src_page_size;
+                    n = std::min<int64_t>(n, p->src_page_size - slot);
+                    t.kind = kPoolPages;
+                    t.a = ch->page_table[at / p->src_page_size];
+                    t.b = static_cast<int32_t>(slot);
+                } else {
+                    t.kind = kPoolRows;
+                    t.a = at;
+                }
+                t.cs_idx = cs;
+            } else if (paged) {
+                const int64_t slot = lo % p->page_size;
+                n = std::min<int64_t>(n, p->page_size - slot);
+                t.kind = kCachePages;
+                t.a = rq.page_table[lo / p->page_size];
+                t.b = static_cast<int32_t>(slot);
+                if ((t.a < 0 || t.a >= p->num_phys_pages) && bad_page < 0)
+                    bad_page = static_cast<int32_t>(lo / p->page_size);
+            } else {
+                t.kind = kCacheRows;
+                t.a = r;
+                t.b = static_cast<int32_t>(lo);
+            }
+            t.ntok = static_cast<int32_t>(n);
+            t.sink_dist = last_start >= 0 ? static_cast<int32_t>(std::min<int64_t>(lo - last_start, kNoSink)) : kNoSink;
+            p->atiles.push_back(t);
+            lo += n;
+        }
+    };
+    int64_t pos = 0;
+    for (int32_t j : order) {
+        const pic_entry &e = rq.entries[j];
+        if (pos >= L) break;
+        emit(pos, e.dst_offset, nullptr, nullptr, -1);  // gap before the chunk
+        if (e.dst_offset > 0) last_start = e.dst_offset;
+        emit(e.dst_offset, e.dst_offset + e.recompute_k, nullptr, nullptr, -1);  // recomputed
+        emit(e.dst_offset + e.recompute_k, e.dst_offset + e.length, &e, &chunks[e.chunk_id],
+             cs_of_entry[entry0 + j]);
+        pos = e.dst_offset + e.length;
+    }
+    emit(pos, L, nullptr, nullptr, -1);
+    p->context_bad_page.push_back(bad_page);
+
+    // blocks of whole tiles
+    const int32_t tile_end = static_cast<int32_t>(p->atiles.size());
+    int32_t t = tile_begin;
+    while (t < tile_end) {
+        AttnBlock b{r, t, 0, 0};
+        while (t < tile_end && b.ntok + p->atiles[t].ntok <= kAttnBlockTokens) {
+            b.ntok += p->atiles[t].ntok;
+            b.ntiles++;
+            t++;
+        }
+        p->ablocks.push_back(b);
+    }
+}
+
 }  // namespace
 
 pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
@@ -316,6 +404,15 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
         }
     }
 
+    for (int r = 0; r < n_requests; r++) {
+        const pic_request &rq = requests[r];
+        const int64_t span =
+            paged ? static_cast<int64_t>(rq.n_pages) * geom->dst_page_size : geom->dst_capacity;
+        if (rq.context_len < 0 || rq.context_len > span || rq.context_len > kMaxPosition)
+            return fail(PIC_ERR_RANGE, "request %d: context_len %lld outside [0, %lld]", r,
+                        static_cast<long long>(rq.context_len), static_cast<long long>(span));
+    }
+
     // overlaps: whole entry intervals inside a request, then written rows
     {
         std::vector<Interval> iv;
@@ -384,6 +481,7 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
         p.launch.stream_loads = any_overlap(iv) ? 0 : 1;
     }
     std::unordered_map<int64_t, int32_t> table_of_delta;
+    std::vector<int32_t> cs_of_entry;
     int64_t written = 0, masked = 0;
     for (int r = 0; r < n_requests; r++) {
         const pic_request &rq = requests[r];
@@ -404,6 +502,7 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             }
             const HostEntry he{c.token_start, e.dst_offset, r, 0, cs_idx, 0};
             p.entries.push_back(he);
+            cs_of_entry.push_back(cs_idx);
             add_tiles(&p, he, paged ? rq.page_table : nullptr,
                       src_paged ? c.page_table : nullptr, e.recompute_k, e.length);
             p.bounds.insert(p.bounds.end(), {r, e.dst_offset, e.dst_offset + e.length});
@@ -412,7 +511,18 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             masked += e.recompute_k;
         }
     }
+    int32_t entry0 = 0;
+    int64_t context_tokens = 0;
+    for (int r = 0; r < n_requests; r++) {
+        p.req_block0.push_back(static_cast<int32_t>(p.ablocks.size()));
+        build_attention_map(&p, chunks, requests[r], r, cs_of_entry, entry0);
+        entry0 += requests[r].n_entries;
+        context_tokens += p.context.back();
+    }
+    p.req_block0.push_back(static_cast<int32_t>(p.ablocks.size()));
     fill_info(&p, written, masked, pool_need);
+    p.info.context_tokens = context_tokens;
+    p.info.attend_blocks = static_cast<int64_t>(p.ablocks.size());
     return PIC_OK;
 }
 
@@ -485,11 +595,19 @@ Staged stage(const Problem &p) {
     auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     s.off_tiles = 0;
     s.off_cs = align(p.tiles.size() * sizeof(DevTile));
-    const size_t total = align(s.off_cs + p.cs.size() * sizeof(double));
+    s.off_atiles = align(s.off_cs + p.cs.size() * sizeof(double));
+    s.off_ablocks = align(s.off_atiles + p.atiles.size() * sizeof(AttnTile));
+    s.off_rblock = align(s.off_ablocks + p.ablocks.size() * sizeof(AttnBlock));
+    const size_t total = align(s.off_rblock + p.req_block0.size() * sizeof(int32_t));
     s.bytes.assign(std::max<size_t>(total, 256), 0);
-    if (!p.tiles.empty())
-        std::memcpy(&s.bytes[s.off_tiles], p.tiles.data(), p.tiles.size() * sizeof(DevTile));
-    if (!p.cs.empty()) std::memcpy(&s.bytes[s.off_cs], p.cs.data(), p.cs.size() * sizeof(double));
+    auto put = [&](size_t off, const void *src, size_t n) {
+        if (n) std::memcpy(&s.bytes[off], src, n);
+    };
+    put(s.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(DevTile));
+    put(s.off_cs, p.cs.data(), p.cs.size() * sizeof(double));
+    put(s.off_atiles, p.atiles.data(), p.atiles.size() * sizeof(AttnTile));
+    put(s.off_ablocks, p.ablocks.data(), p.ablocks.size() * sizeof(AttnBlock));
+    put(s.off_rblock, p.req_block0.data(), p.req_block0.size() * sizeof(int32_t));
     return s;
 }
 

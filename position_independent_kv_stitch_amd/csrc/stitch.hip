@@ -421,6 +421,8 @@ hipError_t launch(const Problem &p, KArgs a, int n_layers, hipStream_t stream) {
                                     : launch_style<uint16_t, PIC_ROPE_INTERLEAVED>(p, a, n_layers, stream);
 }
 
+}  // namespace
+
 pic_status hip_fail(hipError_t e, const char *what) {
     return fail(PIC_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
 }
@@ -461,6 +463,44 @@ KArgs args_for(const Problem &p, const uint8_t *dmem, const Staged &stg) {
     return a;
 }
 
+// Upload the plan's metadata to the current device on first use, ordered on
+// `stream`; later uses on any stream wait for that upload.  A plan stays on
+// the device of its first use.
+pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream_) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (!plan->d_mem) {
+        const size_t n = plan->staged.bytes.size();
+        e = hipMalloc(&plan->d_mem, n);
+        if (e != hipSuccess) {
+            plan->d_mem = nullptr;
+            return hip_fail(e, "hipMalloc (plan metadata)");
+        }
+        e = hipMemcpyAsync(plan->d_mem, plan->staged.bytes.data(), n, hipMemcpyHostToDevice,
+                           stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan metadata)");
+        hipEvent_t ev;
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        e = hipEventRecord(ev, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        plan->upload_event = ev;
+        plan->device = dev;
+        return PIC_OK;
+    }
+    if (dev != plan->device)
+        return fail(PIC_ERR_STATE, "plan was uploaded to device %d, current device is %d",
+                    plan->device, dev);
+    e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(plan->upload_event), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    return PIC_OK;
+}
+
+namespace {
+
 struct HostBytes {
     std::vector<uint8_t> bytes;
 };
@@ -497,34 +537,8 @@ pic_status pic_stitch(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_vi
     if (p.tiles.empty() || layer_begin == layer_end) return PIC_OK;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    std::lock_guard<std::mutex> lock(plan->mu);
-    int dev = -1;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    if (!plan->d_mem) {
-        const size_t n = plan->staged.bytes.size();
-        e = hipMalloc(&plan->d_mem, n);
-        if (e != hipSuccess) {
-            plan->d_mem = nullptr;
-            return hip_fail(e, "hipMalloc (plan metadata)");
-        }
-        e = hipMemcpyAsync(plan->d_mem, plan->staged.bytes.data(), n, hipMemcpyHostToDevice,
-                           stream);
-        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan metadata)");
-        hipEvent_t ev;
-        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-        e = hipEventRecord(ev, stream);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-        plan->upload_event = ev;
-        plan->device = dev;
-    } else {
-        if (dev != plan->device)
-            return fail(PIC_ERR_STATE, "plan was uploaded to device %d, current device is %d",
-                        plan->device, dev);
-        e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(plan->upload_event), 0);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
-    }
+    st = ensure_device_plan(plan, stream_);
+    if (st) return st;
 
     KArgs a = args_for(p, static_cast<const uint8_t *>(plan->d_mem), plan->staged);
     a.src_k = pool->k;
@@ -542,7 +556,7 @@ pic_status pic_stitch(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_vi
     a.d_page = dst->page_stride;
     a.d_req = dst->request_stride;
     a.layer_begin = layer_begin;
-    e = launch(p, a, layer_end - layer_begin, stream);
+    const hipError_t e = launch(p, a, layer_end - layer_begin, stream);
     if (e != hipSuccess) return hip_fail(e, "stitch kernel launch");
     return PIC_OK;
 }
@@ -616,6 +630,7 @@ void pic_plan_destroy(pic_plan_t *plan) {
         if (cur != plan->device) (void)hipSetDevice(plan->device);
         (void)hipDeviceSynchronize();
         (void)hipFree(plan->d_mem);
+        if (plan->d_work) (void)hipFree(plan->d_work);
         if (plan->upload_event)
             (void)hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
         if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);

@@ -606,3 +606,95 @@ def test_validation_paged_pool():
     assert oracle.validate_stitch(w) == "range"
     w.requests = [Request([Entry(0, 0, 10, 6)])]  # page 6 holds tokens 2..5 only: masked
     assert oracle.validate_stitch(w) == "ok"
+
+
+# ------------------------------------------------------------ decode attention
+
+def _attend_case(H=2, D=8, G=2, L=20, entries=(), chunks=(), seed=20, same_keys=False):
+    """A one-request problem whose own cache holds every context position
+    (contiguous destination), pool of the given chunks, f64 storage."""
+    rng = np.random.default_rng(seed)
+    pool_tokens = max([c.token_start + c.length for c in chunks] + [1])
+    wl = Workload("att", "f64", 1, H, D, 0, D, "half", 10000.0, True, pool_tokens=pool_tokens,
+                  chunks=list(chunks), requests=[Request(list(entries), None, L)], capacity=L)
+    pk = rng.standard_normal((1, pool_tokens, H, D))
+    pv = rng.standard_normal((1, pool_tokens, H, D))
+    ck = rng.standard_normal((1, 1, L, H, D))
+    if same_keys:
+        ck[:] = ck[0, 0, 0]
+    cv = rng.standard_normal((1, 1, L, H, D))
+    q = rng.standard_normal((1, H * G, D))
+    return wl, pk, pv, ck, cv, q
+
+
+def test_attend_uniform_keys_average_values():
+    """Equal keys give equal weights: the output is the mean value row."""
+    wl, pk, pv, ck, cv, q = _attend_case(same_keys=True)
+    out = oracle.attend(wl, pk, pv, ck, cv, q, 0)
+    for j in range(q.shape[1]):
+        assert np.allclose(out[0, j], cv[0, 0, :, j // 2].mean(axis=0), atol=1e-13)
+
+
+def test_attend_sink_bias_closed_form():
+    """With equal keys, a logit bias b on the first sink_tokens positions of a
+    chunk placed after 0 weights them by e^b against 1 for the rest."""
+    ch = [Chunk(0, 6)]
+    wl, pk, pv, ck, cv, q = _attend_case(L=20, entries=[Entry(0, 8, 6, 6)], chunks=ch,
+                                         same_keys=True)
+    for b in (-15.0, -2.0, 3.0):
+        out = oracle.attend(wl, pk, pv, ck, cv, q, 0, sink_tokens=4, sink_bias=b)
+        wts = np.ones(20)
+        wts[8:12] = np.exp(b)
+        for j in range(q.shape[1]):
+            want = (wts[:, None] * cv[0, 0, :, j // 2]).sum(0) / wts.sum()
+            assert np.allclose(out[0, j], want, atol=1e-13)
+    # an entry at position 0 carries no pseudo-sink (the global sink is real)
+    wl.requests[0].entries = [Entry(0, 0, 6, 6)]
+    out0 = oracle.attend(wl, pk, pv, ck, cv, q, 0, sink_tokens=4, sink_bias=-15.0)
+    assert np.allclose(out0[0, 0], cv[0, 0, :, 0].mean(0), atol=1e-13)
+
+
+def test_attend_single_position_and_gqa_heads():
+    """A one-position context returns that value row; query head j reads KV
+    head j // G."""
+    wl, pk, pv, ck, cv, q = _attend_case(H=3, G=2, L=1)
+    out = oracle.attend(wl, pk, pv, ck, cv, q, 0)
+    for j in range(6):
+        assert np.array_equal(out[0, j], cv[0, 0, 0, j // 2])
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_attend_rotated_chunks_equal_direct_rope(style):
+    """Chunks cached at positions 0..L-1 and placed (rotated on the way in)
+    attend exactly like keys RoPE'd directly at their absolute positions
+    sitting in the cache; reusing the cached keys unturned does not."""
+    H, D, G = 2, 8, 2
+    lens, starts = [5, 7], [0, 5]
+    rng = np.random.default_rng(21)
+    raw = rng.standard_normal((1, 12, H, D))
+    wl0 = gqa(rope_dim=D, n_heads=H, style=style)
+    cached = rope_at(raw, np.concatenate([np.arange(5), np.arange(7)]), wl0)
+    vals = rng.standard_normal((1, 12, H, D))
+    chunks = [Chunk(starts[0], lens[0]), Chunk(starts[1], lens[1])]
+    entries = [Entry(1, 3, 7), Entry(0, 12, 5, 2)]  # chunk 1 at 3, chunk 0 at 12 (2 recomputed)
+    L = 18
+    wl = Workload("att", "f64", 1, H, D, 0, D, style, 10000.0, True, pool_tokens=12,
+                  chunks=chunks, requests=[Request(entries, None, L)], capacity=L)
+    ck = rng.standard_normal((1, 1, L, H, D))
+    cv = rng.standard_normal((1, 1, L, H, D))
+    q = rng.standard_normal((1, H * G, D))
+    got = oracle.attend(wl, cached, vals, ck, cv, q, 0)
+    # the same context written out: direct RoPE at absolute positions
+    dk, dv = ck.copy(), cv.copy()
+    dk[0, 0, 3:10] = rope_at(raw[:, 5:12], np.arange(3, 10), wl0)[0]
+    dv[0, 0, 3:10] = vals[0, 5:12]
+    dk[0, 0, 14:17] = rope_at(raw[:, 2:5], np.arange(14, 17), wl0)[0]
+    dv[0, 0, 14:17] = vals[0, 2:5]
+    plain = Workload("att", "f64", 1, H, D, 0, D, style, 10000.0, True, pool_tokens=12,
+                     chunks=chunks, requests=[Request([], None, L)], capacity=L)
+    want = oracle.attend(plain, cached, vals, dk, dv, q, 0)
+    assert np.allclose(got, want, atol=1e-12)
+    naive_k = dk.copy()
+    naive_k[0, 0, 3:10] = cached[0, 5:12]
+    naive = oracle.attend(plain, cached, vals, naive_k, dv, q, 0)
+    assert np.max(np.abs(naive - want)) > 1e-3

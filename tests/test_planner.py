@@ -261,3 +261,32 @@ def test_paged_pool_plans(seed):
             tiles += 1
     assert p.info["n_tiles"] == tiles
     assert p.info["pool_tokens_required"] == wl.src_n_pages * wl.src_page_size
+
+
+def test_attention_map_counts_and_validation():
+    """The pic_attend map covers every context position once, in blocks of at
+    most 256; a context beyond the request's span is refused."""
+    wl = config2()
+    wl.requests[0].context_len = 128 + 8 * 2048
+    p = pic.Plan.from_workload(wl)
+    assert p.info["context_tokens"] == 16512
+    assert p.info["attend_blocks"] >= -(-16512 // 256)
+    wl.requests[0].context_len = 16513
+    assert plan_status(wl) == "range"
+    wl.requests[0].context_len = 0  # default: up to the last entry
+    p = pic.Plan.from_workload(wl)
+    assert p.info["context_tokens"] == max(e.dst_offset + e.length for e in wl.requests[0].entries)
+
+
+def test_attend_refuses_unmapped_context_pages():
+    """A prefix page no stitch writes may be unmapped for pic_stitch, but
+    pic_attend reads it: refused before any device work."""
+    lib = B.load_library()
+    wl = config2()
+    wl.requests[0].page_table = wl.requests[0].page_table.copy()
+    wl.requests[0].page_table[0] = -1  # the 128-token prefix's first page
+    p = pic.Plan.from_workload(wl)  # the stitch never touches it
+    view = B.KvView(16, 16, 0, 1024, 128, 16384, 0)
+    args = B.AttendArgs(16, 4096, 128, 16, 4096, 128, 32, 0, 0.1, 0, 0.0, 0)
+    st = lib.pic_attend(p.handle, C.byref(view), C.byref(view), C.byref(args), None)
+    assert B.STATUS_NAMES[st] == "range" and b"context page" in lib.pic_last_error()
