@@ -74,6 +74,10 @@ WORKLOADS = {
                "in place by shifts in [-65536, 65536], recompute_k 16 (pic_rotate_inplace)",
     "single-layer": "1 layer, 8 kv heads x 128, fp32, 3 chunks of 512/1024/256 tokens "
                     "(stitch, contiguous; launch-bound)",
+    "attend-decode": "decode attention over stitched contexts, chunk keys turned on load: 16 "
+                     "requests x 16512 positions (8 own chunks x 2048 behind a 128-token prefix, "
+                     "recompute_k 32), 32 query heads over 8 kv heads x 128, bf16, 16-token "
+                     "pages; one pic_attend per layer, 32 layers per step",
 }
 
 
@@ -93,6 +97,8 @@ def setup_workload(name, torch, pic):
                 "kernel": "stitch_kernel<bf16, half> (in place)", "plan": None,
                 "config": {"workload": WORKLOADS[name], "storage": "bf16",
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
+    if name == "attend-decode":
+        return setup_attend(name, torch, pic)
     wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
           "rag-group": lambda: config3(n_layers=4),
           "llama3-8b-paged-pool": lambda: with_paged_pool(config2(), page_size=16, seed=1)}[name]()
@@ -112,6 +118,61 @@ def setup_workload(name, torch, pic):
     return {"wl": wl, "step": lambda: pic.stitch(plan, pk, pv, dk, dv), "bytes": step_bytes,
             "token_layers": info["tokens_written"] * wl.n_layers, "kernel": kernel,
             "plan": plan, "info": info, "pk": pk, "pv": pv, "config": cfg}
+
+
+def setup_attend(name, torch, pic):
+    """The decode-attention workload: one step is a pic_attend per layer."""
+    from pic_workloads import Request, Workload, decode_batch, normal_values, pool_values
+    wl = decode_batch()
+    group = 4
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, 2, "cuda:0")
+    cv = normal_values(wl.dst_shape(), wl.dtype, 3, "cuda:0")
+    R, L = len(wl.requests), wl.n_layers
+    q = normal_values((L, R, wl.n_heads * group, wl.row_dim), wl.dtype, 4, "cuda:0")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    info = plan.info
+    # the same contexts with no placed chunks: every position read from the cache
+    plain_wl = Workload(wl.name, wl.dtype, L, wl.n_heads, wl.row_dim, wl.rope_offset,
+                        wl.rope_dim, wl.style, wl.theta, True, pool_tokens=wl.pool_tokens,
+                        chunks=wl.chunks,
+                        requests=[Request([], rq.page_table, rq.context_len)
+                                  for rq in wl.requests],
+                        page_size=wl.page_size, n_phys_pages=wl.n_phys_pages)
+    plain = pic.Plan.from_workload(plain_wl)
+
+    def run(p):
+        def step():
+            for layer in range(L):
+                pic.attend(p, pk, pv, ck, cv, q[layer], layer=layer, out=out[layer],
+                           sink_tokens=4, sink_bias=-15.0)
+        return step
+
+    row = wl.n_heads * wl.row_dim * 2  # one bf16 K (or V) row of all kv heads
+    cfg = {"workload": WORKLOADS[name], "storage": wl.dtype, "layers": L,
+           "kv_heads": wl.n_heads, "q_heads": wl.n_heads * group, "row_dim": wl.row_dim,
+           "requests": R, "context_tokens": info["context_tokens"],
+           "chunk_positions": info["tokens_written"], "page_size": wl.page_size,
+           "sink_tokens": 4, "sink_bias": -15.0, "parallelism": "single-gpu"}
+    return {"wl": wl, "step": run(plan), "plain_step": run(plain),
+            "bytes": info["context_tokens"] * 2 * row * L,
+            "token_layers": info["context_tokens"] * L, "launches": L,
+            "kernel": "attend_block_kernel<bf16, half> + attend_combine_kernel (one pic_attend)",
+            "plan": plan, "plans": [plain], "info": info, "config": cfg}
+
+
+def time_steps(torch, step, steps):
+    """Average ms per step over `steps` back-to-back steps (HIP events on the
+    current stream)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        step()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
 
 
 def cpu_baseline(wl, pk, pv, plan_info):
@@ -182,6 +243,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-plain-attention", action="store_true",
+                    help="attend-decode: skip timing attention over the cache alone")
     ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS),
                     help="the default is the workload the headline metric is quoted on; the "
                          "others time the remaining paths")
@@ -220,12 +283,13 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
-    kernel_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    launches = W.get("launches", 1)
+    kernel_ms = sorted(s.elapsed_time(e) / launches for s, e in zip(starts, ends))
     avg_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     ms_per_step = total_ms / args.steps
 
     value = step_bytes * args.steps / (total_ms * 1e-3) / 1e9
-    achieved = step_bytes / (avg_kernel_ms * 1e-3) / 1e9
+    achieved = step_bytes / launches / (avg_kernel_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -249,16 +313,28 @@ def main():
                      "kernel": W["kernel"],
                      "avg_launch_ms": round(avg_kernel_ms, 5),
                      "median_launch_ms": round(kernel_ms[len(kernel_ms) // 2], 5),
-                     "algorithmic_bytes_per_launch": step_bytes},
+                     "algorithmic_bytes_per_launch": step_bytes // launches},
     }
+    if launches > 1:
+        out["roofline"]["launches_per_step"] = launches
+    if "plain_step" in W and not args.no_plain_attention:
+        for _ in range(3):
+            W["plain_step"]()
+        plain_ms = time_steps(torch, W["plain_step"], max(5, args.steps // 4))
+        out["attention_over_cache"] = {
+            "ms_per_step": round(plain_ms, 5),
+            "value": round(step_bytes / (plain_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "what": "the same contexts with no placed chunks (every row from the cache, "
+                    "no rotation): the cost of attention alone"}
     if not args.no_copy_ceiling:
         out["copy_ceiling"] = copy_ceiling(torch, min(step_bytes, 8 << 30))
     if not args.no_cpu_baseline and args.workload == DEFAULT:
         out["cpu_baseline"] = cpu_baseline(wl, W["pk"], W["pv"], W["info"])
     else:
         out["cpu_baseline"] = None
-    if W.get("plan") is not None:
-        W["plan"].destroy()
+    for p in [W.get("plan")] + W.get("plans", []):
+        if p is not None:
+            p.destroy()
     print(json.dumps(out), flush=True)
 
 

@@ -194,7 +194,9 @@ typedef struct pic_plan_info_t {
     int64_t tile_tokens;          /* most tokens of one work tile (paged tiles also stop at
                                      page ends) */
     int64_t context_tokens;       /* pic_attend: sum of context_len over requests */
-    int64_t attend_blocks;        /* pic_attend: (request, 256-token block) work items */
+    int64_t attend_blocks;        /* pic_attend: (request, block of positions) work items */
+    int64_t attend_block_tokens;  /* pic_attend: positions per block at most (256, 128 or 64:
+                                     shorter when few blocks would leave the GPU idle) */
 } pic_plan_info_t;
 
 typedef struct pic_plan pic_plan_t;

@@ -214,6 +214,29 @@ def config5(seed: int = 0, n_layers: int = 36) -> Workload:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def decode_batch(seed: int = 0, n_requests: int = 16, n_layers: int = 32) -> Workload:
+    """A decode batch over stitched contexts, Llama-3-8B shape: n_requests
+    requests, each built like the 8 x 2048 paged request (its own 8 chunks
+    in a seeded random order behind a 128-token prefix, the first 32 tokens
+    of every chunk left for recompute), whose whole 16,512-position context
+    is attended; 16-token pages from one global random permutation.  The
+    chunks are distinct per request, so no pool row is read twice."""
+    rng = np.random.default_rng(seed)
+    n, length, prefix, ps = 8, 2048, 128, 16
+    chunks = [Chunk(i * length, length) for i in range(n * n_requests)]
+    per = (prefix + n * length) // ps
+    perm = rng.permutation(per * n_requests).astype(np.int32)
+    requests = []
+    for r in range(n_requests):
+        order = rng.permutation(n) + n * r
+        entries = [Entry(int(c), prefix + j * length, length, 32) for j, c in enumerate(order)]
+        requests.append(Request(entries, perm[r * per:(r + 1) * per].copy(),
+                                prefix + n * length))
+    return Workload("llama3-8b decode batch", "bf16", n_layers, 8, 128, 0, 128, "half",
+                    500000.0, True, pool_tokens=n * length * n_requests, chunks=chunks,
+                    requests=requests, page_size=ps, n_phys_pages=per * n_requests)
+
+
 def with_paged_pool(wl: Workload, page_size: int = 16, seed: int = 0,
                     first_offsets: bool = False, spare_pages: int = 0) -> Workload:
     """The same placements with the chunks kept in a paged pool (the block
@@ -235,14 +258,17 @@ def with_paged_pool(wl: Workload, page_size: int = 16, seed: int = 0,
 
 def random_small(seed: int, dtype: str = "bf16", style: str = "half", paged: bool = False,
                  mla: bool = False, n_requests: int = 2, n_layers: int = 2,
-                 max_len: int = 150, deltas=None) -> Workload:
+                 max_len: int = 150, deltas=None, dims=None) -> Workload:
     """A small random stitch problem with ragged chunk lengths, gaps, shared
-    and partial chunks, several requests and varied recompute_k."""
+    and partial chunks, several requests and varied recompute_k.  dims =
+    (heads, row_dim, rope_offset, rope_dim) overrides the GQA row shape."""
     rng = np.random.default_rng(seed)
     if mla:
         heads, row, roff, rdim, has_v, theta = 1, 576, 512, 64, False, 10000.0
     else:
         heads, row, roff, rdim, has_v, theta = 2, 128, 0, 128, True, 500000.0
+    if dims is not None:
+        heads, row, roff, rdim = dims
     n_chunks = int(rng.integers(2, 6))
     lens = rng.integers(1, max_len, size=n_chunks, endpoint=True)
     starts = np.concatenate([[0], np.cumsum(lens)[:-1]])

@@ -91,7 +91,8 @@ class PlanInfo(C.Structure):
     _fields_ = [(n, C.c_int64) for n in (
         "n_requests", "n_entries", "n_tiles", "tokens_written", "tokens_masked",
         "pool_tokens_required", "bytes_read_per_layer", "bytes_written_per_layer",
-        "tile_tokens", "context_tokens", "attend_blocks")]
+        "tile_tokens", "context_tokens", "attend_blocks",
+        "attend_block_tokens")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}

@@ -8,20 +8,25 @@
 // Pseudo-Sinks" and its listing).
 //
 // Two kernels:
-//   attend_block_kernel: one workgroup per (256-position block of a request,
-//     KV head).  Pass 1 reads every key row of the block once (pool rows of
-//     placed chunks turned by the chunk's shift on load; other positions from
-//     the request's own cache), scores it against the GQA group's query
-//     heads and keeps the logits in LDS; the block's softmax max and sum are
-//     taken in LDS; pass 2 reads every value row once and accumulates the
-//     weighted sum.  Partial (max, sum, accumulator) per (block, query head)
-//     go to the plan's workspace.
+//   attend_block_kernel: one workgroup per (block of at most 256 positions
+//     of a request, KV head).  The block's rows are first resolved into an
+//     LDS table (element offset and source per position), so both passes
+//     run one flat loop over positions whatever the mix of pool rows, pool
+//     pages and cache pages.  Pass 1 reads every key row once (pool rows of
+//     placed chunks turned by the chunk's shift on load), scores it against
+//     the GQA group's query heads and keeps the logits in LDS; the block's
+//     softmax max and sum are taken in LDS; pass 2 reads every value row
+//     once and accumulates the weighted sum.  Partial (max, sum,
+//     accumulator) per (block, query head) go to the plan's workspace.
 //   attend_combine_kernel: one workgroup per (request, query head) merges
 //     the request's blocks (flash-decoding style rescaling).
-// A token's head row is split over LPT lanes, 16 bytes each; a wave step
-// takes 64 / LPT tokens.  Arithmetic is fp32 (the rotation with fp32
-// cos/sin rounded from the plan's fp64 tables).  Decode attention reads
-// each K and V row once, so it is HBM-bound like the stitch.
+// Lanes: a token's head row is split over LPT = row_dim / (16 / element
+// size) lanes; a wave step covers 64 / LPT tokens.  For keys a lane holds
+// two 8-byte pieces chosen so that, with half pairing, the x and y halves
+// of its planes are both in the lane (the rotation needs no lane exchange).
+// Arithmetic is fp32 (the rotation with cos/sin rounded from the plan's
+// fp64 tables).  Decode attention reads each K and V row once, so it is
+// HBM-bound like the stitch.
 
 #include <hip/hip_runtime.h>
 
@@ -37,7 +42,22 @@ pic_status hip_fail(hipError_t e, const char *what);  // stitch.hip
 namespace {
 
 constexpr int kAttnThreads = 256;  // four wave64s
-constexpr int kMaxDim = 256;       // head dims supported by the workspace layout
+constexpr int kWaves = kAttnThreads / 64;
+constexpr int kMaxDim = 256;  // head dims supported by the LDS layout
+#ifndef PIC_ATTN_UNROLL
+#define PIC_ATTN_UNROLL 4
+#endif
+#ifndef PIC_ATTN_UNROLL_V
+#define PIC_ATTN_UNROLL_V PIC_ATTN_UNROLL
+#endif
+// wave steps whose loads are issued together (keys, values)
+constexpr int kUnroll = PIC_ATTN_UNROLL;
+constexpr int kUnrollV = PIC_ATTN_UNROLL_V;
+
+// Per-position flags of the block's row table.
+constexpr uint32_t kMetaPool = 1u << 31;      // row read from the pool (else the cache)
+constexpr uint32_t kMetaDamp = 1u << 30;      // LegoLink bias applies
+constexpr uint32_t kMetaCs = (1u << 30) - 1;  // shift table + 1 (0: row not turned)
 
 struct AttnArgs {
     const AttnTile *tiles;
@@ -60,184 +80,244 @@ struct AttnArgs {
     float sink_bias;
 };
 
+// Element i of packed 32-bit words, widened to fp32.
 template <typename E>
 struct Elems;
 template <>
 struct Elems<float> {
-    static constexpr int kVec = 4;
-    __device__ static void widen(const uint4 &w, float (&x)[4]) {
-        x[0] = __uint_as_float(w.x);
-        x[1] = __uint_as_float(w.y);
-        x[2] = __uint_as_float(w.z);
-        x[3] = __uint_as_float(w.w);
-    }
+    static constexpr int kVec = 4;  // elements per 16 bytes
+    __device__ static float get(const uint32_t *w, int i) { return __uint_as_float(w[i]); }
 };
 template <>
 struct Elems<uint16_t> {
     static constexpr int kVec = 8;
-    __device__ static void widen(const uint4 &w, float (&x)[8]) {
-        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            x[2 * k] = __uint_as_float(u[k] << 16);
-            x[2 * k + 1] = __uint_as_float(u[k] & 0xFFFF0000u);
-        }
+    __device__ static float get(const uint32_t *w, int i) {
+        return __uint_as_float((i & 1) ? (w[i >> 1] & 0xFFFF0000u) : (w[i >> 1] << 16));
     }
 };
 
-__device__ __forceinline__ uint4 load16(const void *base, int64_t elem, int esize) {
-    return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * esize);
+__device__ __forceinline__ void load8(const void *base, int64_t elem, int esize, uint32_t (&w)[2]) {
+    const uint2 v =
+        *reinterpret_cast<const uint2 *>(static_cast<const char *>(base) + elem * esize);
+    w[0] = v.x;
+    w[1] = v.y;
+}
+
+__device__ __forceinline__ void load16(const void *base, int64_t elem, int esize,
+                                       uint32_t (&w)[4]) {
+    const uint4 v =
+        *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + elem * esize);
+    w[0] = v.x;
+    w[1] = v.y;
+    w[2] = v.z;
+    w[3] = v.w;
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
-// Element offset of the row of position `t` of a tile, at one layer.
-__device__ __forceinline__ int64_t row_base(const AttnArgs &a, const AttnTile &T, int64_t layer,
-                                            bool &from_pool) {
-    switch (T.kind) {
-        case kPoolRows:
-            from_pool = true;
-            return layer * a.s_layer + T.a * a.s_tok;
-        case kPoolPages:
-            from_pool = true;
-            return layer * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b) * a.s_tok;
-        case kCacheRows:
-            from_pool = false;
-            return layer * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b) * a.c_tok;
-        default:
-            from_pool = false;
-            return layer * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b) * a.c_tok;
-    }
-}
+template <int N>
+struct Log2 {
+    static constexpr int value = 1 + Log2<N / 2>::value;
+};
+template <>
+struct Log2<1> {
+    static constexpr int value = 0;
+};
 
 template <typename E, int STYLE, int GMAX>
 __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnArgs a, int32_t layer) {
     constexpr int VEC = Elems<E>::kVec;
+    constexpr int HV = VEC / 2;  // elements of one 8-byte piece
     constexpr int ES = sizeof(E);
-    constexpr int kWaves = kAttnThreads / 64;
-    __shared__ float s_w[kAttnBlockTokens * GMAX];   // logits, then weights
-    __shared__ float s_acc[kWaves * GMAX * kMaxDim];  // per-wave accumulators
+    constexpr int NH = Log2<GMAX>::value;
+    __shared__ AttnTile s_tiles[kAttnBlockTiles];
+    __shared__ int64_t s_off[kAttnBlockTokens];
+    __shared__ uint32_t s_meta[kAttnBlockTokens];
+    // logits, then weights; after pass 2 the cross-wave sums
+    __shared__ __attribute__((aligned(16))) float s_w[kAttnBlockTokens * GMAX];
     __shared__ float s_ml[2 * GMAX];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int LPT = 1 << a.lpt_shift;      // lanes per token row
-    const int TPW = 64 >> a.lpt_shift;     // tokens per wave step
-    const int lj = lane & (LPT - 1);       // this lane's 16-byte piece of the row
-    const int tg = lane >> a.lpt_shift;    // this lane's token in the step
+    const int LPT = 1 << a.lpt_shift;   // lanes per token row
+    const int TPW = 64 >> a.lpt_shift;  // tokens per wave step
+    const int lj = lane & (LPT - 1);
+    const int tg = lane >> a.lpt_shift;
     const int G = a.group;
     const int block = blockIdx.x / a.n_kv_heads;
     const int h = blockIdx.x - block * a.n_kv_heads;
     const AttnBlock B = a.blocks[block];
-    const int d0 = lj * VEC;                // first dim of this lane's piece
 
-    // this lane's piece of each query head of the group
-    float q[GMAX][VEC];
+    // ---- the block's row table
+    if (threadIdx.x < B.ntiles) s_tiles[threadIdx.x] = a.tiles[B.tile0 + threadIdx.x];
+    __syncthreads();
+    for (int pi = threadIdx.x; pi < B.ntok; pi += kAttnThreads) {
+        int lo = 0, hi = B.ntiles - 1;  // the last tile starting at or before pi
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_tiles[mid].tok0 <= pi) lo = mid;
+            else hi = mid - 1;
+        }
+        const AttnTile &T = s_tiles[lo];
+        const int t = pi - T.tok0;
+        const int64_t L = layer;
+        int64_t off;
+        uint32_t meta = 0;
+        switch (T.kind) {
+            case kPoolRows:
+                off = L * a.s_layer + (T.a + t) * a.s_tok + h * a.s_head;
+                meta = kMetaPool;
+                break;
+            case kPoolPages:
+                off = L * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b + t) * a.s_tok +
+                      h * a.s_head;
+                meta = kMetaPool;
+                break;
+            case kCacheRows:
+                off = L * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b + t) * a.c_tok +
+                      h * a.c_head;
+                break;
+            default:
+                off = L * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b + t) * a.c_tok +
+                      h * a.c_head;
+                break;
+        }
+        if (T.cs_idx >= 0) meta |= static_cast<uint32_t>(T.cs_idx + 1);
+        if (T.sink_dist + t < a.sink_tokens) meta |= kMetaDamp;
+        s_off[pi] = off;
+        s_meta[pi] = meta;
+    }
+
+    // ---- this lane's two key pieces: first elements e0, e1 of the head row
+    const int ro = a.rope_offset, hr = a.half_r;
+    int e0, e1, plane0 = 0;
+    bool rot = false;
+    if (STYLE == PIC_ROPE_HALF) {
+        const int nrl = hr / HV;  // lanes holding rotary planes
+        if (lj < nrl) {
+            rot = true;
+            plane0 = lj * HV;
+            e0 = ro + plane0;  // x of planes plane0 .. plane0 + HV - 1
+            e1 = e0 + hr;      // their y
+        } else {
+            const int x = (lj - nrl) * VEC;  // index among the non-rotary dims
+            e0 = x < ro ? x : x + 2 * hr;
+            e1 = e0 + HV;
+        }
+    } else {
+        e0 = lj * VEC;
+        e1 = e0 + HV;
+        rot = e0 >= ro && e0 < ro + 2 * hr;
+        plane0 = (e0 - ro) / 2;
+    }
+    float q0[GMAX][HV], q1[GMAX][HV];
 #pragma unroll
     for (int g = 0; g < GMAX; g++) {
+        uint32_t w0[2] = {0u, 0u}, w1[2] = {0u, 0u};
         if (g < G) {
-            const int64_t qo = B.request * a.q_req + (h * G + g) * a.q_head + d0;
-            Elems<E>::widen(load16(a.q, qo, ES), q[g]);
-        } else {
+            const int64_t qo = B.request * a.q_req + (h * G + g) * a.q_head;
+            load8(a.q, qo + e0, ES, w0);
+            load8(a.q, qo + e1, ES, w1);
+        }
 #pragma unroll
-            for (int e = 0; e < VEC; e++) q[g][e] = 0.f;
+        for (int e = 0; e < HV; e++) {
+            q0[g][e] = Elems<E>::get(w0, e);
+            q1[g][e] = Elems<E>::get(w1, e);
         }
     }
-
-    // where this lane's piece sits in the rotary slice
-    const int ro = a.rope_offset, hr = a.half_r;
-    int role = 0;  // 0: not rotary, 1: x of (half) planes, 2: y of (half) planes, 3: interleaved
-    int plane0 = 0, partner = lane;
-    if (d0 >= ro && d0 < ro + 2 * hr) {
-        if (STYLE == PIC_ROPE_HALF) {
-            if (d0 < ro + hr) {
-                role = 1;
-                plane0 = d0 - ro;
-                partner = lane + hr / VEC;
-            } else {
-                role = 2;
-                plane0 = d0 - ro - hr;
-                partner = lane - hr / VEC;
-            }
-        } else {
-            role = 3;
-            plane0 = (d0 - ro) / 2;
-        }
-    }
-    constexpr int NCS = STYLE == PIC_ROPE_HALF ? VEC : VEC / 2;
-    float c[NCS], s[NCS];
-    int cur = -2;
+    __syncthreads();
 
     // ---- pass 1: logits
-    int tok0 = 0;  // block position of the tile's first token
-    for (int ti = 0; ti < B.ntiles; ti++) {
-        const AttnTile T = a.tiles[B.tile0 + ti];
-        bool from_pool;
-        const int64_t base = row_base(a, T, layer, from_pool);
-        const void *kbase = from_pool ? a.pool_k : a.cache_k;
-        const int64_t tstride = from_pool ? a.s_tok : a.c_tok;
-        const int64_t hstride = from_pool ? a.s_head : a.c_head;
-        const bool turn = from_pool && T.cs_idx >= 0;
-        if (turn && T.cs_idx != cur) {
-            cur = T.cs_idx;
-            if (role) {
-                const double *t = a.cs + (static_cast<int64_t>(cur) * hr + plane0) * 2;
+    const int sub = LPT >> NH;  // lanes that end up holding one head's sum
+    const bool writer = (lj & (sub - 1)) == 0;
+    const int my_g = lj / sub;
+    const int steps = (B.ntok + kWaves * TPW - 1) / (kWaves * TPW);
+    uint32_t cur = 0;  // shift table (+1) whose cos/sin sit in c, s
+    float c[HV], s[HV];
 #pragma unroll
-                for (int p = 0; p < NCS; p++) {
-                    c[p] = static_cast<float>(t[2 * p]);
-                    s[p] = static_cast<float>(t[2 * p + 1]);
-                }
+    for (int p = 0; p < HV; p++) c[p] = 1.f, s[p] = 0.f;
+    for (int s0 = 0; s0 < steps; s0 += kUnroll) {
+        uint32_t w0[kUnroll][2], w1[kUnroll][2], mt[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; u++) {
+            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
+            w0[u][0] = w0[u][1] = w1[u][0] = w1[u][1] = 0u;
+            mt[u] = 0u;
+            if (pi < B.ntok) {
+                mt[u] = s_meta[pi];
+                const int64_t off = s_off[pi];
+                const void *base = (mt[u] & kMetaPool) ? a.pool_k : a.cache_k;
+                load8(base, off + e0, ES, w0[u]);
+                load8(base, off + e1, ES, w1[u]);
             }
         }
-        for (int t0 = wave * TPW; t0 < T.ntok; t0 += kWaves * TPW) {
-            const int t = t0 + tg;
-            const bool live = t < T.ntok;
-            uint4 w = make_uint4(0u, 0u, 0u, 0u);
-            if (live) w = load16(kbase, base + t * tstride + h * hstride + d0, ES);
-            float k[VEC];
-            Elems<E>::widen(w, k);
-            if (turn) {
-                if (STYLE == PIC_ROPE_HALF) {
-                    float o[VEC];
 #pragma unroll
-                    for (int e = 0; e < VEC; e++) o[e] = __shfl(k[e], partner, 64);
-                    if (role == 1) {
+        for (int u = 0; u < kUnroll; u++) {
+            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
+            float k0[HV], k1[HV];
 #pragma unroll
-                        for (int e = 0; e < VEC; e++) k[e] = k[e] * c[e] - o[e] * s[e];
-                    } else if (role == 2) {
+            for (int e = 0; e < HV; e++) {
+                k0[e] = Elems<E>::get(w0[u], e);
+                k1[e] = Elems<E>::get(w1[u], e);
+            }
+            const uint32_t cs1 = mt[u] & kMetaCs;
+            if (rot && cs1 != 0u) {
+                if (cs1 != cur) {
+                    cur = cs1;
+                    const double *t =
+                        a.cs + (static_cast<int64_t>(cs1 - 1) * hr + plane0) * 2;
 #pragma unroll
-                        for (int e = 0; e < VEC; e++) k[e] = o[e] * s[e] + k[e] * c[e];
+                    for (int p = 0; p < HV; p++) {
+                        c[p] = static_cast<float>(t[2 * p]);
+                        s[p] = static_cast<float>(t[2 * p + 1]);
                     }
-                } else if (role == 3) {
+                }
+                if (STYLE == PIC_ROPE_HALF) {
 #pragma unroll
-                    for (int e = 0; e < VEC / 2; e++) {
-                        const float x = k[2 * e], y = k[2 * e + 1];
-                        k[2 * e] = x * c[e] - y * s[e];
-                        k[2 * e + 1] = x * s[e] + y * c[e];
+                    for (int p = 0; p < HV; p++) {
+                        const float x = k0[p], y = k1[p];
+                        k0[p] = x * c[p] - y * s[p];
+                        k1[p] = x * s[p] + y * c[p];
+                    }
+                } else {
+#pragma unroll
+                    for (int p = 0; p < HV / 2; p++) {
+                        float x = k0[2 * p], y = k0[2 * p + 1];
+                        k0[2 * p] = x * c[p] - y * s[p];
+                        k0[2 * p + 1] = x * s[p] + y * c[p];
+                        x = k1[2 * p];
+                        y = k1[2 * p + 1];
+                        k1[2 * p] = x * c[HV / 2 + p] - y * s[HV / 2 + p];
+                        k1[2 * p + 1] = x * s[HV / 2 + p] + y * c[HV / 2 + p];
                     }
                 }
             }
-            float dot[GMAX];
+            float v[GMAX];
 #pragma unroll
             for (int g = 0; g < GMAX; g++) {
                 float acc = 0.f;
 #pragma unroll
-                for (int e = 0; e < VEC; e++) acc += q[g][e] * k[e];
-                dot[g] = acc;
+                for (int e = 0; e < HV; e++) acc += q0[g][e] * k0[e] + q1[g][e] * k1[e];
+                v[g] = acc;
             }
-            for (int m = 1; m < LPT; m <<= 1) {
+            // reduce-scatter over the token's lanes: each halving round keeps
+            // half of the heads, so lane lj ends with head lj / sub
 #pragma unroll
-                for (int g = 0; g < GMAX; g++) dot[g] += shfl_xor_f(dot[g], m);
-            }
-            if (live && lj == 0) {
-                const int dist = T.sink_dist + t;
-                const float bias = (dist < a.sink_tokens) ? a.sink_bias : 0.f;
+            for (int r = 0; r < NH; r++) {
+                const int n = GMAX >> r;
+                const int m = LPT >> (r + 1);
+                const bool upper = (lane & m) != 0;
 #pragma unroll
-                for (int g = 0; g < GMAX; g++)
-                    if (g < G) s_w[(tok0 + t) * GMAX + g] = dot[g] * a.scale + bias;
+                for (int i = 0; i < n / 2; i++) {
+                    const float send = upper ? v[i] : v[i + n / 2];
+                    const float keep = upper ? v[i + n / 2] : v[i];
+                    v[i] = keep + shfl_xor_f(send, m);
+                }
             }
+            for (int m = sub >> 1; m >= 1; m >>= 1) v[0] += shfl_xor_f(v[0], m);
+            if (pi < B.ntok && writer && my_g < G)
+                s_w[pi * GMAX + my_g] = v[0] * a.scale + ((mt[u] & kMetaDamp) ? a.sink_bias : 0.f);
         }
-        tok0 += T.ntok;
     }
     __syncthreads();
 
@@ -260,59 +340,66 @@ __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnAr
     }
     __syncthreads();
 
-    // ---- pass 2: weighted values
+    // ---- pass 2: weighted values; this lane's 16-byte piece of the row
+    const int dv = lj * VEC;
     float acc[GMAX][VEC];
 #pragma unroll
     for (int g = 0; g < GMAX; g++)
 #pragma unroll
         for (int e = 0; e < VEC; e++) acc[g][e] = 0.f;
-    tok0 = 0;
-    for (int ti = 0; ti < B.ntiles; ti++) {
-        const AttnTile T = a.tiles[B.tile0 + ti];
-        bool from_pool;
-        const int64_t base = row_base(a, T, layer, from_pool);
-        const void *vbase = from_pool ? a.pool_v : a.cache_v;
-        const int64_t tstride = from_pool ? a.s_tok : a.c_tok;
-        const int64_t hstride = from_pool ? a.s_head : a.c_head;
-        for (int t0 = wave * TPW; t0 < T.ntok; t0 += kWaves * TPW) {
-            const int t = t0 + tg;
-            if (t < T.ntok) {
-                float v[VEC];
-                Elems<E>::widen(load16(vbase, base + t * tstride + h * hstride + d0, ES), v);
+    for (int s0 = 0; s0 < steps; s0 += kUnrollV) {
+        uint32_t w[kUnrollV][4];
 #pragma unroll
-                for (int g = 0; g < GMAX; g++) {
-                    if (g < G) {
-                        const float p = s_w[(tok0 + t) * GMAX + g];
+        for (int u = 0; u < kUnrollV; u++) {
+            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
+            w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0u;
+            if (pi < B.ntok) {
+                const void *base = (s_meta[pi] & kMetaPool) ? a.pool_v : a.cache_v;
+                load16(base, s_off[pi] + dv, ES, w[u]);
+            }
+        }
 #pragma unroll
-                        for (int e = 0; e < VEC; e++) acc[g][e] += p * v[e];
-                    }
+        for (int u = 0; u < kUnrollV; u++) {
+            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
+            if (pi < B.ntok) {
+                float p[GMAX];
+#pragma unroll
+                for (int g = 0; g < GMAX; g++) p[g] = s_w[pi * GMAX + g];
+#pragma unroll
+                for (int e = 0; e < VEC; e++) {
+                    const float x = Elems<E>::get(w[u], e);
+#pragma unroll
+                    for (int g = 0; g < GMAX; g++) acc[g][e] += p[g] * x;
                 }
             }
         }
-        tok0 += T.ntok;
     }
-    // sum the wave's token groups, then the waves
+    // sum the wave's token groups, then the waves in order (wave 0 first)
     for (int m = LPT; m < 64; m <<= 1) {
 #pragma unroll
         for (int g = 0; g < GMAX; g++)
 #pragma unroll
             for (int e = 0; e < VEC; e++) acc[g][e] += shfl_xor_f(acc[g][e], m);
     }
-    if (tg == 0) {
+    const int D = a.row_dim;
+    float *s_sum = s_w;  // [g][row_dim]; G * D <= GMAX * kMaxDim fits
+    for (int w = 0; w < kWaves; w++) {
+        __syncthreads();
+        if (wave == w && tg == 0) {
 #pragma unroll
-        for (int g = 0; g < GMAX; g++)
-            if (g < G)
+            for (int g = 0; g < GMAX; g++)
+                if (g < G)
 #pragma unroll
-                for (int e = 0; e < VEC; e++) s_acc[(wave * GMAX + g) * kMaxDim + d0 + e] = acc[g][e];
+                    for (int e = 0; e < VEC; e++) {
+                        float *x = s_sum + g * D + dv + e;
+                        *x = (w == 0 ? 0.f : *x) + acc[g][e];
+                    }
+        }
     }
     __syncthreads();
-    const int D = a.row_dim;
     for (int idx = threadIdx.x; idx < G * D; idx += kAttnThreads) {
         const int g = idx / D, d = idx - g * D;
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWaves; w++) sum += s_acc[(w * GMAX + g) * kMaxDim + d];
-        a.part_acc[(static_cast<int64_t>(block) * a.num_q_heads + h * G + g) * D + d] = sum;
+        a.part_acc[(static_cast<int64_t>(block) * a.num_q_heads + h * G + g) * D + d] = s_sum[idx];
     }
     if (threadIdx.x < G) {
         const int g = threadIdx.x;
@@ -322,22 +409,42 @@ __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnAr
     }
 }
 
-// out[r][j][d] = sum_b acc_b[d] e^{m_b - M} / sum_b l_b e^{m_b - M}
+// out[r][j][d] = sum_b acc_b[d] e^{m_b - M} / sum_b l_b e^{m_b - M}, the
+// blocks taken in order, 256 at a time.
 __global__ void __launch_bounds__(kMaxDim) attend_combine_kernel(const AttnArgs a) {
+    __shared__ float s_f[kMaxDim];   // e^{m_b - M} of a batch of blocks
+    __shared__ float s_lf[kMaxDim];  // l_b e^{m_b - M}
+    __shared__ float s_red[kMaxDim / 64];
     const int r = blockIdx.x;
     const int j = blockIdx.y;
     const int d = threadIdx.x;
     const int b0 = a.req_block0[r], b1 = a.req_block0[r + 1];
+    const int64_t hq = a.num_q_heads;
     float M = -INFINITY;
-    for (int b = b0; b < b1; b++)
-        M = fmaxf(M, a.part_ml[(static_cast<int64_t>(b) * a.num_q_heads + j) * 2]);
+    for (int b = b0 + d; b < b1; b += kMaxDim) M = fmaxf(M, a.part_ml[(b * hq + j) * 2]);
+    for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, shfl_xor_f(M, x));
+    if ((d & 63) == 0) s_red[d >> 6] = M;
+    __syncthreads();
+    M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kMaxDim / 64; w++) M = fmaxf(M, s_red[w]);
     float L = 0.f, O = 0.f;
-    for (int b = b0; b < b1; b++) {
-        const float *ml = a.part_ml + (static_cast<int64_t>(b) * a.num_q_heads + j) * 2;
-        const float f = __expf(ml[0] - M);
-        L += ml[1] * f;
-        if (d < a.row_dim)
-            O += a.part_acc[(static_cast<int64_t>(b) * a.num_q_heads + j) * a.row_dim + d] * f;
+    for (int base = b0; base < b1; base += kMaxDim) {
+        const int nb = min(kMaxDim, b1 - base);
+        __syncthreads();
+        if (d < nb) {
+            const float *ml = a.part_ml + ((base + d) * hq + j) * 2;
+            const float f = __expf(ml[0] - M);
+            s_f[d] = f;
+            s_lf[d] = ml[1] * f;
+        }
+        __syncthreads();
+        for (int i = 0; i < nb; i++) L += s_lf[i];
+        if (d < a.row_dim) {
+            const float *acc = a.part_acc + (base * hq + j) * a.row_dim + d;
+#pragma unroll 8
+            for (int i = 0; i < nb; i++) O += acc[i * hq * a.row_dim] * s_f[i];
+        }
     }
     if (d < a.row_dim) a.out[r * a.o_req + j * a.o_head + d] = O / L;
 }
@@ -386,6 +493,10 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     if (D > kMaxDim || lpt > 64 || (lpt & (lpt - 1)) != 0)
         return fail(PIC_ERR_ALIGN, "pic_attend needs row_dim / %d a power of two, row_dim <= %d",
                     vec, kMaxDim);
+    const int gmax = args->num_q_heads / H <= 4 ? 4 : 8;  // query heads per kernel instance
+    if (lpt < gmax)
+        return fail(PIC_ERR_ALIGN, "pic_attend needs row_dim >= %d for %d query heads per KV head",
+                    gmax * vec, args->num_q_heads / H);
     if (args->q_request_stride % vec || args->q_head_stride % vec ||
         (reinterpret_cast<uintptr_t>(args->q) & 15u))
         return fail(PIC_ERR_ALIGN, "q rows must be 16-byte aligned");

@@ -42,7 +42,14 @@ struct DevTile {
 enum AttnSrc : int32_t { kPoolRows = 0, kPoolPages = 1, kCacheRows = 2, kCachePages = 3 };
 constexpr int kAttnTileTokens = 64;    // positions per attention tile at most
 constexpr int kAttnBlockTokens = 256;  // positions per attention work item at most
+constexpr int kAttnBlockTiles = 32;    // tiles per attention work item at most
 constexpr int32_t kNoSink = 1 << 30;   // sink distance of runs not after a chunk start
+#ifndef PIC_ATTN_MIN_ITEMS
+#define PIC_ATTN_MIN_ITEMS 1024
+#endif
+// Work items (blocks x KV heads) below which the planner halves the block
+// length, down to kAttnTileTokens positions, so that a launch fills the chip.
+constexpr int64_t kAttnMinItems = PIC_ATTN_MIN_ITEMS;
 
 struct AttnTile {
     int64_t a;          // pool row | pool page | request | destination page
@@ -51,7 +58,7 @@ struct AttnTile {
     int32_t cs_idx;     // pool runs whose chunk moved: shift table; else -1
     int32_t kind;       // AttnSrc
     int32_t sink_dist;  // position of the first token minus the last chunk start (> 0 only)
-    int32_t pad;
+    int32_t tok0;       // position of the first token within its block
 };
 
 struct AttnBlock {  // consecutive tiles [tile0, tile0 + ntiles) of one request
@@ -115,6 +122,8 @@ struct Problem {
     std::vector<AttnBlock> ablocks;
     std::vector<int64_t> context;  // context_len per request
     std::vector<int32_t> req_block0;  // first attention block of each request (+ end)
+    std::vector<int32_t> req_tile0;   // first attention tile of each request (+ end)
+    int32_t attn_block_tokens = 0;    // positions per attention block at most
     std::vector<int32_t> context_bad_page;  // per request: a context page out of range (-1: none)
     pic_plan_info_t info{};
 };

@@ -295,19 +295,40 @@ void build_attention_map(Problem *p, const pic_chunk *chunks, const pic_request 
     }
     emit(pos, L, nullptr, nullptr, -1);
     p->context_bad_page.push_back(bad_page);
+    p->req_tile0.push_back(tile_begin);
+}
 
-    // blocks of whole tiles
-    const int32_t tile_end = static_cast<int32_t>(p->atiles.size());
-    int32_t t = tile_begin;
-    while (t < tile_end) {
-        AttnBlock b{r, t, 0, 0};
-        while (t < tile_end && b.ntok + p->atiles[t].ntok <= kAttnBlockTokens) {
-            b.ntok += p->atiles[t].ntok;
-            b.ntiles++;
-            t++;
+// Group every request's attention tiles into work blocks of whole tiles, at
+// most `bt` positions and kAttnBlockTiles tiles each.  bt is the longest of
+// 256, 128, 64 positions that still gives kAttnMinItems (block, KV head)
+// work items, so that small batches are split finer.
+void build_attention_blocks(Problem *p) {
+    const int32_t n_req = static_cast<int32_t>(p->context.size());
+    p->req_tile0.push_back(static_cast<int32_t>(p->atiles.size()));
+    int64_t ctx_blocks_256 = 0;
+    for (int64_t L : p->context) ctx_blocks_256 += (L + kAttnBlockTokens - 1) / kAttnBlockTokens;
+    int32_t bt = kAttnBlockTokens;
+    while (bt > kAttnTileTokens && ctx_blocks_256 * (kAttnBlockTokens / bt) *
+                                           p->shape.num_heads < kAttnMinItems)
+        bt /= 2;
+    p->attn_block_tokens = bt;
+    for (int32_t r = 0; r < n_req; r++) {
+        p->req_block0.push_back(static_cast<int32_t>(p->ablocks.size()));
+        int32_t t = p->req_tile0[r];
+        const int32_t tile_end = p->req_tile0[r + 1];
+        while (t < tile_end) {
+            AttnBlock b{r, t, 0, 0};
+            while (t < tile_end && b.ntiles < kAttnBlockTiles &&
+                   b.ntok + p->atiles[t].ntok <= bt) {
+                p->atiles[t].tok0 = b.ntok;
+                b.ntok += p->atiles[t].ntok;
+                b.ntiles++;
+                t++;
+            }
+            p->ablocks.push_back(b);
         }
-        p->ablocks.push_back(b);
     }
+    p->req_block0.push_back(static_cast<int32_t>(p->ablocks.size()));
 }
 
 }  // namespace
@@ -514,15 +535,15 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     int32_t entry0 = 0;
     int64_t context_tokens = 0;
     for (int r = 0; r < n_requests; r++) {
-        p.req_block0.push_back(static_cast<int32_t>(p.ablocks.size()));
         build_attention_map(&p, chunks, requests[r], r, cs_of_entry, entry0);
         entry0 += requests[r].n_entries;
         context_tokens += p.context.back();
     }
-    p.req_block0.push_back(static_cast<int32_t>(p.ablocks.size()));
+    build_attention_blocks(&p);
     fill_info(&p, written, masked, pool_need);
     p.info.context_tokens = context_tokens;
     p.info.attend_blocks = static_cast<int64_t>(p.ablocks.size());
+    p.info.attend_block_tokens = p.attn_block_tokens;
     return PIC_OK;
 }
 

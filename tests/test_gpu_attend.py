@@ -96,6 +96,42 @@ def test_attend_small(torch_cuda, seed, dt, paged, group, pp):
     assert err <= TOL * vmax, (err, vmax)
 
 
+SHAPES = [  # (storage, pairing, (kv heads, row_dim, rope_offset, rope_dim), group)
+    ("bf16", "half", (4, 64, 0, 64), 2),
+    ("bf16", "half", (4, 64, 0, 64), 8),
+    ("bf16", "half", (2, 128, 64, 64), 4),
+    ("bf16", "half", (2, 128, 0, 64), 3),
+    ("bf16", "interleaved", (2, 128, 32, 64), 6),
+    ("f32", "half", (2, 64, 0, 32), 8),
+    ("bf16", "half", (1, 256, 0, 128), 4),
+    ("f32", "interleaved", (2, 256, 128, 128), 1),
+]
+
+
+@pytest.mark.parametrize("dt,style,dims,group", SHAPES)
+def test_attend_shapes(torch_cuda, dt, style, dims, group):
+    """Partial rotary slices at an offset, narrow and wide rows, groups that
+    do not fill the kernel's head slots."""
+    rng = np.random.default_rng(11)
+    wl = with_context(random_small(50, dtype=dt, style=style, paged=True, n_requests=2,
+                                   n_layers=1, max_len=200, deltas=[0, 3, -4096, 70000],
+                                   dims=dims), rng)
+    say(f"attend shape {dt} {style} {dims} group={group}")
+    err, vmax = run_case(torch_cuda, wl, group, 5, layer=0, sink_tokens=4, sink_bias=-15.0)
+    assert err <= TOL * vmax, (err, vmax)
+
+
+def test_attend_one_token_pool_pages(torch_cuda):
+    """A pool of 1-token pages: every pool position is its own tile, so blocks
+    stop at the per-block tile limit rather than at their length."""
+    rng = np.random.default_rng(12)
+    wl = with_paged_pool(random_small(51, dtype="bf16", n_requests=2, n_layers=1, max_len=120),
+                         page_size=1, seed=3)
+    wl = with_context(wl, rng)
+    err, vmax = run_case(torch_cuda, wl, 4, 6)
+    assert err <= TOL * vmax, (err, vmax)
+
+
 @pytest.mark.parametrize("style", ["half", "interleaved"])
 def test_attend_sink_damping(torch_cuda, style):
     """LegoLink pseudo-sink damping (-15 on 4 tokens) on chunks placed after
@@ -122,6 +158,17 @@ def test_attend_llama3_decode_full(torch_cuda):
                              sink_bias=-15.0)
         say(f"  max err {err:.3g} (tol {TOL * vmax:.3g})")
         assert err <= TOL * vmax
+
+
+def test_attend_decode_batch(torch_cuda):
+    """Sixteen Llama-3-shaped decode requests of 16,512 positions each (each
+    request's own 8 chunks of 2048): 256-position blocks, one layer."""
+    from pic_workloads import decode_batch
+    wl = decode_batch(n_requests=16, n_layers=1)
+    say("decode batch 16 x 16512")
+    err, vmax = run_case(torch_cuda, wl, 4, 8, layer=0, sink_tokens=4, sink_bias=-15.0)
+    say(f"  max err {err:.3g} (tol {TOL * vmax:.3g})")
+    assert err <= TOL * vmax
 
 
 def test_attend_matches_stitch_then_attend(torch_cuda):

@@ -11,7 +11,7 @@ import oracle
 import position_independent_kv_stitch_amd as pic
 from position_independent_kv_stitch_amd import _binding as B
 from pic_workloads import (CONFIGS, Chunk, Entry, Request, Segment, Workload, config2,
-                           config3, random_small, with_paged_pool)
+                           config3, decode_batch, random_small, with_paged_pool)
 
 ORACLE_TO_LIB = {"ok": "ok", "bad_arg": "invalid_arg", "range": "range", "overlap": "overlap"}
 
@@ -265,12 +265,20 @@ def test_paged_pool_plans(seed):
 
 def test_attention_map_counts_and_validation():
     """The pic_attend map covers every context position once, in blocks of at
-    most 256; a context beyond the request's span is refused."""
+    most 256 positions, shortened (to 128, then 64) while fewer than 1024
+    (block, KV head) items would result; a context beyond the request's span
+    is refused."""
     wl = config2()
     wl.requests[0].context_len = 128 + 8 * 2048
     p = pic.Plan.from_workload(wl)
     assert p.info["context_tokens"] == 16512
-    assert p.info["attend_blocks"] >= -(-16512 // 256)
+    # 65 blocks of 256 x 8 heads = 520 < 1024 -> 128-position blocks
+    assert p.info["attend_block_tokens"] == 128
+    assert p.info["attend_blocks"] >= -(-16512 // 128)
+    wide = decode_batch(n_requests=16)
+    assert pic.Plan.from_workload(wide).info["attend_block_tokens"] == 256
+    small = random_small(3, n_requests=1)
+    assert pic.Plan.from_workload(small).info["attend_block_tokens"] == 64
     wl.requests[0].context_len = 16513
     assert plan_status(wl) == "range"
     wl.requests[0].context_len = 0  # default: up to the last entry
@@ -290,3 +298,15 @@ def test_attend_refuses_unmapped_context_pages():
     args = B.AttendArgs(16, 4096, 128, 16, 4096, 128, 32, 0, 0.1, 0, 0.0, 0)
     st = lib.pic_attend(p.handle, C.byref(view), C.byref(view), C.byref(args), None)
     assert B.STATUS_NAMES[st] == "range" and b"context page" in lib.pic_last_error()
+
+
+def test_attend_refuses_rows_too_narrow_for_the_group():
+    """Query heads per KV head are reduced over the lanes of one row: a
+    16-dim bf16 row (2 lanes) cannot carry 8 query heads."""
+    lib = B.load_library()
+    wl = random_small(2, dtype="bf16", dims=(2, 16, 0, 16))
+    p = pic.Plan.from_workload(wl)
+    view = B.KvView(16, 16, 0, 32, 16, 0, 0)
+    args = B.AttendArgs(16, 256, 16, 16, 256, 16, 16, 0, 0.25, 0, 0.0, 0)
+    st = lib.pic_attend(p.handle, C.byref(view), C.byref(view), C.byref(args), None)
+    assert B.STATUS_NAMES[st] == "align" and b"row_dim" in lib.pic_last_error()
