@@ -78,6 +78,8 @@ WORKLOADS = {
                      "requests x 16512 positions (8 own chunks x 2048 behind a 128-token prefix, "
                      "recompute_k 32), 32 query heads over 8 kv heads x 128, bf16, 16-token "
                      "pages; one pic_attend per layer, 32 layers per step",
+    "attend-decode-single": "the attend-decode workload with one request (16512 positions): "
+                            "a latency-bound decode step",
 }
 
 
@@ -97,7 +99,7 @@ def setup_workload(name, torch, pic):
                 "kernel": "stitch_kernel<bf16, half> (in place)", "plan": None,
                 "config": {"workload": WORKLOADS[name], "storage": "bf16",
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
-    if name == "attend-decode":
+    if name.startswith("attend-decode"):
         return setup_attend(name, torch, pic)
     wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
           "rag-group": lambda: config3(n_layers=4),
@@ -123,7 +125,7 @@ def setup_workload(name, torch, pic):
 def setup_attend(name, torch, pic):
     """The decode-attention workload: one step is a pic_attend per layer."""
     from pic_workloads import Request, Workload, decode_batch, normal_values, pool_values
-    wl = decode_batch()
+    wl = decode_batch(n_requests=1 if name == "attend-decode-single" else 16)
     group = 4
     pk, pv = pool_values(wl, seed=0, device="cuda:0")
     ck = normal_values(wl.dst_shape(), wl.dtype, 2, "cuda:0")

@@ -53,6 +53,10 @@ constexpr int kMaxDim = 256;  // head dims supported by the LDS layout
 // wave steps whose loads are issued together (keys, values)
 constexpr int kUnroll = PIC_ATTN_UNROLL;
 constexpr int kUnrollV = PIC_ATTN_UNROLL_V;
+#ifndef PIC_ATTN_PIPE
+#define PIC_ATTN_PIPE 0
+#endif
+constexpr bool kPipe = PIC_ATTN_PIPE != 0;  // next batch's loads issued before this one is used
 
 // Per-position flags of the block's row table.
 constexpr uint32_t kMetaPool = 1u << 31;      // row read from the pool (else the cache)
@@ -227,7 +231,6 @@ __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnAr
     }
     __syncthreads();
 
-    // ---- pass 1: logits
     const int sub = LPT >> NH;  // lanes that end up holding one head's sum
     const bool writer = (lj & (sub - 1)) == 0;
     const int my_g = lj / sub;
@@ -236,31 +239,37 @@ __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnAr
     float c[HV], s[HV];
 #pragma unroll
     for (int p = 0; p < HV; p++) c[p] = 1.f, s[p] = 0.f;
-    for (int s0 = 0; s0 < steps; s0 += kUnroll) {
+
+    // key loads of kUnroll wave steps starting at step s0
+    struct KBatch {
         uint32_t w0[kUnroll][2], w1[kUnroll][2], mt[kUnroll];
+    };
+    auto issue_k = [&](KBatch &b, int s0) {
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
-            w0[u][0] = w0[u][1] = w1[u][0] = w1[u][1] = 0u;
-            mt[u] = 0u;
+            b.w0[u][0] = b.w0[u][1] = b.w1[u][0] = b.w1[u][1] = 0u;
+            b.mt[u] = 0u;
             if (pi < B.ntok) {
-                mt[u] = s_meta[pi];
+                b.mt[u] = s_meta[pi];
                 const int64_t off = s_off[pi];
-                const void *base = (mt[u] & kMetaPool) ? a.pool_k : a.cache_k;
-                load8(base, off + e0, ES, w0[u]);
-                load8(base, off + e1, ES, w1[u]);
+                const void *base = (b.mt[u] & kMetaPool) ? a.pool_k : a.cache_k;
+                load8(base, off + e0, ES, b.w0[u]);
+                load8(base, off + e1, ES, b.w1[u]);
             }
         }
+    };
+    auto score = [&](const KBatch &b, int s0) {
 #pragma unroll
         for (int u = 0; u < kUnroll; u++) {
             const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
             float k0[HV], k1[HV];
 #pragma unroll
             for (int e = 0; e < HV; e++) {
-                k0[e] = Elems<E>::get(w0[u], e);
-                k1[e] = Elems<E>::get(w1[u], e);
+                k0[e] = Elems<E>::get(b.w0[u], e);
+                k1[e] = Elems<E>::get(b.w1[u], e);
             }
-            const uint32_t cs1 = mt[u] & kMetaCs;
+            const uint32_t cs1 = b.mt[u] & kMetaCs;
             if (rot && cs1 != 0u) {
                 if (cs1 != cur) {
                     cur = cs1;
@@ -316,9 +325,71 @@ __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnAr
             }
             for (int m = sub >> 1; m >= 1; m >>= 1) v[0] += shfl_xor_f(v[0], m);
             if (pi < B.ntok && writer && my_g < G)
-                s_w[pi * GMAX + my_g] = v[0] * a.scale + ((mt[u] & kMetaDamp) ? a.sink_bias : 0.f);
+                s_w[pi * GMAX + my_g] =
+                    v[0] * a.scale + ((b.mt[u] & kMetaDamp) ? a.sink_bias : 0.f);
+        }
+    };
+
+    // value loads of kUnrollV wave steps starting at step s0; this lane's
+    // 16-byte piece of the row
+    const int dv = lj * VEC;
+    struct VBatch {
+        uint32_t w[kUnrollV][4];
+    };
+    auto issue_v = [&](VBatch &b, int s0) {
+#pragma unroll
+        for (int u = 0; u < kUnrollV; u++) {
+            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
+            b.w[u][0] = b.w[u][1] = b.w[u][2] = b.w[u][3] = 0u;
+            if (pi < B.ntok) {
+                const void *base = (s_meta[pi] & kMetaPool) ? a.pool_v : a.cache_v;
+                load16(base, s_off[pi] + dv, ES, b.w[u]);
+            }
+        }
+    };
+    float acc[GMAX][VEC];
+#pragma unroll
+    for (int g = 0; g < GMAX; g++)
+#pragma unroll
+        for (int e = 0; e < VEC; e++) acc[g][e] = 0.f;
+    auto accumulate = [&](const VBatch &b, int s0) {
+#pragma unroll
+        for (int u = 0; u < kUnrollV; u++) {
+            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
+            if (pi < B.ntok) {
+                float p[GMAX];
+#pragma unroll
+                for (int g = 0; g < GMAX; g++) p[g] = s_w[pi * GMAX + g];
+#pragma unroll
+                for (int e = 0; e < VEC; e++) {
+                    const float x = Elems<E>::get(b.w[u], e);
+#pragma unroll
+                    for (int g = 0; g < GMAX; g++) acc[g][e] += p[g] * x;
+                }
+            }
+        }
+    };
+
+    // ---- pass 1: logits.  With kPipe the next batch's loads are in flight
+    // while the current one is scored.
+    {
+        KBatch kb;
+        issue_k(kb, 0);
+        for (int s0 = 0; s0 < steps; s0 += kUnroll) {
+            if (kPipe) {
+                KBatch next;
+                if (s0 + kUnroll < steps) issue_k(next, s0 + kUnroll);
+                score(kb, s0);
+                kb = next;
+            } else {
+                score(kb, s0);
+                if (s0 + kUnroll < steps) issue_k(kb, s0 + kUnroll);
+            }
         }
     }
+    // the first values are loaded while the softmax runs
+    VBatch vb;
+    issue_v(vb, 0);
     __syncthreads();
 
     // ---- block softmax: max and sum per query head
@@ -340,38 +411,16 @@ __global__ void __launch_bounds__(kAttnThreads) attend_block_kernel(const AttnAr
     }
     __syncthreads();
 
-    // ---- pass 2: weighted values; this lane's 16-byte piece of the row
-    const int dv = lj * VEC;
-    float acc[GMAX][VEC];
-#pragma unroll
-    for (int g = 0; g < GMAX; g++)
-#pragma unroll
-        for (int e = 0; e < VEC; e++) acc[g][e] = 0.f;
+    // ---- pass 2: weighted values
     for (int s0 = 0; s0 < steps; s0 += kUnrollV) {
-        uint32_t w[kUnrollV][4];
-#pragma unroll
-        for (int u = 0; u < kUnrollV; u++) {
-            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
-            w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0u;
-            if (pi < B.ntok) {
-                const void *base = (s_meta[pi] & kMetaPool) ? a.pool_v : a.cache_v;
-                load16(base, s_off[pi] + dv, ES, w[u]);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kUnrollV; u++) {
-            const int pi = ((s0 + u) * kWaves + wave) * TPW + tg;
-            if (pi < B.ntok) {
-                float p[GMAX];
-#pragma unroll
-                for (int g = 0; g < GMAX; g++) p[g] = s_w[pi * GMAX + g];
-#pragma unroll
-                for (int e = 0; e < VEC; e++) {
-                    const float x = Elems<E>::get(w[u], e);
-#pragma unroll
-                    for (int g = 0; g < GMAX; g++) acc[g][e] += p[g] * x;
-                }
-            }
+        if (kPipe) {
+            VBatch next;
+            if (s0 + kUnrollV < steps) issue_v(next, s0 + kUnrollV);
+            accumulate(vb, s0);
+            vb = next;
+        } else {
+            accumulate(vb, s0);
+            if (s0 + kUnrollV < steps) issue_v(vb, s0 + kUnrollV);
         }
     }
     // sum the wave's token groups, then the waves in order (wave 0 first)
