@@ -7,15 +7,15 @@ import os
 import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCE = os.path.join(HERE, "pic_oracle.c")
+SOURCES = [os.path.join(HERE, "pic_oracle.c"), os.path.join(HERE, "cdc_oracle.c")]
 LIBRARY = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    """Compile pic_oracle.c into liboracle.so next to it; return its path."""
+    """Compile the oracle's C sources into liboracle.so next to them; return its path."""
     tmp = LIBRARY + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-           "-shared", "-Wall", "-Wextra", "-o", tmp, SOURCE, "-lm"]
+           "-shared", "-Wall", "-Wextra", "-o", tmp, *SOURCES, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
