@@ -80,6 +80,11 @@ WORKLOADS = {
                      "pages; one pic_attend per layer, 32 layers per step",
     "attend-decode-single": "the attend-decode workload with one request (16512 positions): "
                             "a latency-bound decode step",
+    "cdc-rag": "content-defined chunking + xxHash64 fingerprints + registry lookup + 128-token "
+               "fallback windows (pic_match) over the batched-RAG prompt stream: 64 requests, "
+               "~1.44 M tokens, 10% of placed documents edited, registry of the 256 pool "
+               "documents' chunks and windows; mean chunk 256 tokens",
+    "cdc-rag-sha256": "the cdc-rag workload with SHA-256 fingerprints (the EPIC registry's key)",
 }
 
 
@@ -101,6 +106,8 @@ def setup_workload(name, torch, pic):
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
     if name.startswith("attend-decode"):
         return setup_attend(name, torch, pic)
+    if name.startswith("cdc-rag"):
+        return setup_cdc(name, torch, pic)
     wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
           "rag-group": lambda: config3(n_layers=4),
           "llama3-8b-paged-pool": lambda: with_paged_pool(config2(), page_size=16, seed=1)}[name]()
@@ -162,6 +169,48 @@ def setup_attend(name, torch, pic):
             "token_layers": info["context_tokens"] * L, "launches": L,
             "kernel": "attend_block_kernel<bf16, half> + attend_combine_kernel (one pic_attend)",
             "plan": plan, "plans": [plain], "info": info, "config": cfg}
+
+
+def setup_cdc(name, torch, pic):
+    """The chunking workload: one step is one pic_match over the whole stream.
+    The registry is filled the way a serving system would fill it, from the
+    library's own chunking of every pool document on its own (its chunks, and
+    the 128-token windows of each chunk)."""
+    from pic_workloads import CDC_THRESHOLD, rag_token_stream
+    kind = "sha256" if name.endswith("sha256") else "xxh64"
+    ts = rag_token_stream(0, edit_prob=0.1)
+    reg = pic.Registry(kind)
+    seen = set()
+    for doc in ts.docs:
+        d = torch.from_numpy(doc).to("cuda:0")
+        for window in (0, 128):  # empty registry: window 0 gives chunks, 128 their windows
+            out, n_out = pic.match(d, CDC_THRESHOLD, None, kind=kind, window=window)
+            recs, m = pic.match_records(out, n_out)
+            for r in recs[:m]:
+                key = (bytes(r["fp"]), int(r["length"]))
+                if key not in seen:
+                    seen.add(key)
+                    reg.add(key[0], key[1], len(seen) - 1)
+    tokens = torch.from_numpy(ts.tokens).to("cuda:0")
+    n = len(ts.tokens)
+    out = torch.empty((n, 56), dtype=torch.uint8, device="cuda:0")
+    n_out = torch.empty(1, dtype=torch.int64, device="cuda:0")
+
+    def step():
+        pic.match(tokens, CDC_THRESHOLD, reg, kind=kind, window=128, out=out, n_out=n_out)
+
+    step()
+    recs, m = pic.match_records(out, n_out)
+    hits = recs[:m]["chunk_id"] >= 0
+    cfg = {"workload": WORKLOADS[name], "tokens": n, "requests": len(ts.request_starts),
+           "registry_entries": len(seen), "segments": int(m),
+           "registered_segments": int(hits.sum()),
+           "registered_tokens": int(recs[:m]["length"][hits].sum()),
+           "fingerprint": kind, "window": 128, "threshold": "2^56",
+           "parallelism": "single-gpu"}
+    return {"wl": None, "step": step, "bytes": 4 * n, "token_layers": n,
+            "kernel": "pic_match (8 kernels: Gear flags, scans, ends, chunk hashes, emit)",
+            "plan": None, "registry": reg, "config": cfg, "bound": "alu"}
 
 
 def time_steps(torch, step, steps):

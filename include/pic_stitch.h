@@ -335,6 +335,92 @@ pic_status pic_plan_ranges(const pic_plan_t *plan, int64_t *boundaries, int64_t 
  * NULL is a no-op. */
 void pic_plan_destroy(pic_plan_t *plan);
 
+/* ------------------------------------------------------------------------
+ * Content-defined chunking of a token stream and the chunk registry: how a
+ * request's prompt is cut into chunks whose caches can be found again
+ * (Irminsul, Technical Summary, "Content-Hash Keying with CDC" and the S1
+ * "detect and recover" strategy; EPIC Guide, the content hash registry of
+ * the serving runtime, SHA-256 keyed).
+ *
+ * Definitions (every one of them is computed on the GPU by pic_match):
+ *   G(t)   = xxHash64 of token t's 4 little-endian bytes, seed gear_seed
+ *            (the Gear value of a token; the pages give no Gear table);
+ *   h_i    = 2 h_{i-1} + G(t_i) mod 2^64, h_{-1} = 0: a rolling hash whose
+ *            value depends on tokens i-63 .. i only (a 64-token window);
+ *   a chunk ends after token i when h_i < threshold, and at the stream end;
+ *   fingerprint of tokens [s, s+len) = SHA-256 of their little-endian int32
+ *            bytes, or their xxHash64 (seed fp_seed) as 8 little-endian bytes
+ *            followed by 24 zero bytes;
+ *   a segment is registered when the registry holds an entry with the
+ *            same fingerprint and the same length.
+ * ------------------------------------------------------------------------ */
+enum { PIC_FP_XXH64 = 0, PIC_FP_SHA256 = 1 };
+
+typedef struct pic_cdc_config {
+    uint64_t threshold;   /* chunk ends after token i when h_i < threshold; the mean chunk
+                             length of random text is about 2^64 / threshold */
+    uint64_t gear_seed;   /* seed of the Gear values */
+    uint64_t fp_seed;     /* xxHash64 seed of the fingerprints (unused for SHA-256) */
+    int32_t fingerprint;  /* PIC_FP_XXH64 | PIC_FP_SHA256 */
+    int32_t window;       /* fallback window (Irminsul S1: 128 tokens); 0 = no fallback */
+} pic_cdc_config;
+
+/* One segment of a stream.  level 0: a content-defined chunk; level 1: a
+ * window of a chunk the registry does not hold (consecutive windows of
+ * `window` tokens from the chunk start, the last one shorter). */
+typedef struct pic_match_t {
+    int64_t start;      /* first token */
+    int32_t length;
+    int32_t level;
+    int32_t chunk_id;   /* id of the registered entry, -1: not registered */
+    int32_t reserved;
+    uint8_t fp[32];     /* fingerprint */
+} pic_match_t;
+
+typedef struct pic_registry pic_registry_t;
+
+/* pic_registry_create -- an empty registry for one fingerprint kind. */
+pic_status pic_registry_create(int32_t fingerprint, pic_registry_t **out);
+
+/* pic_registry_add -- register a segment (host call; fp is 32 host bytes).
+ * length >= 1, chunk_id >= 0 (PIC_ERR_RANGE); an entry with the same
+ * fingerprint and length is refused (PIC_ERR_OVERLAP).  The registry's
+ * device table is rebuilt at the next pic_match: that call first waits for
+ * the whole device (earlier pic_match calls on any stream may still read the
+ * old table), then uploads the new table ordered on its stream.  A registry
+ * is bound to the device of its first pic_match (PIC_ERR_STATE after).
+ * Adding while a pic_match runs on another host thread is serialised by the
+ * registry's lock. */
+pic_status pic_registry_add(pic_registry_t *reg, const uint8_t *fp, int32_t length,
+                            int32_t chunk_id);
+
+/* pic_registry_destroy -- wait for the device, release. NULL is a no-op. */
+void pic_registry_destroy(pic_registry_t *reg);
+
+/*
+ * pic_match -- cut tokens[0, n_tokens) (device, int32) into content-defined
+ * chunks, fingerprint every chunk and look it up in `reg` (NULL: an empty
+ * registry).  A chunk that is not registered is replaced, when window > 0,
+ * by its windows, each fingerprinted and looked up.  The segments, in
+ * stream order, tile the stream; the first max_out are written to `out`
+ * (device, max_out records) and their total count to *n_out (device int64),
+ * so a count above max_out means the output was cut short (a stream of n
+ * tokens never yields more than n segments).
+ * n_tokens in [0, 2^31) and window >= 0 and max_out >= 0 (PIC_ERR_RANGE);
+ * tokens (when n_tokens > 0), out (when max_out > 0) and n_out non-NULL
+ * (PIC_ERR_INVALID_ARG); tokens 4-byte, out and n_out 8-byte aligned
+ * (PIC_ERR_ALIGN).  The registry's fingerprint kind must equal
+ * cfg->fingerprint (PIC_ERR_INVALID_ARG).
+ * Work is enqueued on `stream` and the call does not wait for it (except
+ * to replace a changed registry's table, see pic_registry_add): counts
+ * stay on the device.  Temporary device memory of about 8 bytes per token
+ * plus 36 bytes per kept record (min(n_tokens, max_out)) is allocated and
+ * freed on `stream` (stream-ordered).
+ */
+pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32_t *tokens,
+                     int64_t n_tokens, pic_match_t *out, int64_t max_out, int64_t *n_out,
+                     void *stream);
+
 /* Thread-local message for the last failed call on this thread ("" if none). */
 const char *pic_last_error(void);
 

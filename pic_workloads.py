@@ -309,6 +309,64 @@ def random_small(seed: int, dtype: str = "bf16", style: str = "half", paged: boo
                     requests=[Request(e) for e in reqs_entries], capacity=int(max(spans)))
 
 
+# ------------------------------------------------------------ token streams
+
+# Mean content-defined chunk length of the chunking workloads: a boundary
+# wherever the rolling hash falls below 2^64 / 256 (the pages give no value).
+CDC_THRESHOLD = 1 << 56
+LLAMA3_VOCAB = 128256
+
+
+@dataclass
+class TokenStream:
+    tokens: np.ndarray          # int32: every request's prompt, back to back
+    docs: List[np.ndarray]      # the document pool (int32 token ids)
+    request_starts: np.ndarray  # first token of each request in `tokens`
+    placements: List[tuple]     # (doc id, first token in `tokens`, edited position or -1)
+
+
+def rag_token_stream(seed: int = 0, n_docs: int = 256, doc_len=(128, 4096), n_requests: int = 64,
+                     per_request=(4, 16), prefix=(32, 512), vocab: int = LLAMA3_VOCAB,
+                     edit_prob: float = 0.0) -> TokenStream:
+    """Prompts of batched RAG requests as one token stream: a pool of
+    documents with lengths uniform in doc_len, and per request a fresh
+    prefix (system prompt and query) of U{prefix} tokens followed by U{per_request}
+    documents drawn with replacement in random order (the shape of the
+    batched-RAG stitch workload).  With edit_prob > 0 a placed document has,
+    with that probability, one token replaced (the uncontrolled traffic the
+    fixed-window fallback recovers from).  Token ids are uniform in [0, vocab)."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(doc_len[0], doc_len[1], n_docs, endpoint=True)
+    docs = [rng.integers(0, vocab, int(n)).astype(np.int32) for n in lens]
+    parts, starts, placements, at = [], [], [], 0
+    for _ in range(n_requests):
+        starts.append(at)
+        pre = rng.integers(0, vocab, int(rng.integers(prefix[0], prefix[1], endpoint=True)))
+        parts.append(pre.astype(np.int32))
+        at += len(pre)
+        for d in rng.integers(0, n_docs, int(rng.integers(per_request[0], per_request[1],
+                                                           endpoint=True))):
+            doc = docs[int(d)]
+            edit = -1
+            if edit_prob > 0 and rng.random() < edit_prob:
+                doc = doc.copy()
+                edit = int(rng.integers(0, len(doc)))
+                doc[edit] = (int(doc[edit]) + 1 + int(rng.integers(0, vocab - 1))) % vocab
+            placements.append((int(d), at, edit))
+            parts.append(doc)
+            at += len(doc)
+    tokens = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    return TokenStream(tokens, docs, np.asarray(starts, np.int64), placements)
+
+
+def random_tokens(n: int, seed: int, vocab: int = LLAMA3_VOCAB, signed: bool = False) -> np.ndarray:
+    """n uniform token ids (or, signed, uniform over all int32 values)."""
+    rng = np.random.default_rng(seed)
+    if signed:
+        return rng.integers(-2 ** 31, 2 ** 31, n, dtype=np.int64).astype(np.int32)
+    return rng.integers(0, vocab, n).astype(np.int32)
+
+
 # ------------------------------------------------------------------- values
 
 def _torch():

@@ -8,7 +8,8 @@ library libpic_stitch.so (C ABI in include/pic_stitch.h); this package is
 its thin binding.  Importing it loads the library and fails if it has not
 been built.
 """
-from ._binding import (EXPORTS, LIBRARY, PicError, Plan, attend, load_library,  # noqa: F401
-                       rotate_inplace, rotate_workload, stitch)
+from ._binding import (EXPORTS, LIBRARY, PicError, Plan, Registry, attend,  # noqa: F401
+                       load_library, match, match_records, rotate_inplace, rotate_workload,
+                       stitch)
 
 load_library()

@@ -27,7 +27,9 @@ STYLES = {"half": 0, "interleaved": 1}
 
 # every entry point the header declares
 EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_attend", "pic_plan_info",
-           "pic_plan_ranges", "pic_plan_destroy", "pic_last_error")
+           "pic_plan_ranges", "pic_plan_destroy", "pic_registry_create", "pic_registry_add",
+           "pic_registry_destroy", "pic_match", "pic_last_error")
+FP_KINDS = {"xxh64": 0, "sha256": 1}
 
 
 class PicError(RuntimeError):
@@ -85,6 +87,21 @@ class KvView(C.Structure):
 class SegmentC(C.Structure):
     _fields_ = [("token_start", C.c_int64), ("delta", C.c_int64), ("length", C.c_int32),
                 ("recompute_k", C.c_int32)]
+
+
+class CdcConfig(C.Structure):
+    _fields_ = [("threshold", C.c_uint64), ("gear_seed", C.c_uint64), ("fp_seed", C.c_uint64),
+                ("fingerprint", C.c_int32), ("window", C.c_int32)]
+
+
+class MatchRecord(C.Structure):
+    _fields_ = [("start", C.c_int64), ("length", C.c_int32), ("level", C.c_int32),
+                ("chunk_id", C.c_int32), ("reserved", C.c_int32), ("fp", C.c_uint8 * 32)]
+
+
+# numpy view of pic_match_t records
+MATCH_DTYPE = np.dtype([("start", "<i8"), ("length", "<i4"), ("level", "<i4"),
+                        ("chunk_id", "<i4"), ("reserved", "<i4"), ("fp", "u1", (32,))])
 
 
 class PlanInfo(C.Structure):
@@ -149,6 +166,15 @@ def _configure(lib):
     lib.pic_plan_ranges.argtypes = [C.c_void_p, P(C.c_int64), P(C.c_int64)]
     lib.pic_plan_destroy.restype = None
     lib.pic_plan_destroy.argtypes = [C.c_void_p]
+    lib.pic_registry_create.restype = C.c_int
+    lib.pic_registry_create.argtypes = [C.c_int32, P(C.c_void_p)]
+    lib.pic_registry_add.restype = C.c_int
+    lib.pic_registry_add.argtypes = [C.c_void_p, P(C.c_uint8), C.c_int32, C.c_int32]
+    lib.pic_registry_destroy.restype = None
+    lib.pic_registry_destroy.argtypes = [C.c_void_p]
+    lib.pic_match.restype = C.c_int
+    lib.pic_match.argtypes = [C.c_void_p, P(CdcConfig), C.c_void_p, C.c_int64, C.c_void_p,
+                              C.c_int64, C.c_void_p, C.c_void_p]
     lib.pic_last_error.restype = C.c_char_p
     lib.pic_last_error.argtypes = []
     return lib
@@ -465,3 +491,83 @@ def rotate_workload(wl, buf_k, layer_begin=0, layer_end=None, stream=None, libra
     rotate_inplace(buf_k, wl.segments, rope_dim=wl.rope_dim, theta=wl.theta, style=wl.style,
                    rope_offset=wl.rope_offset, layer_begin=layer_begin, layer_end=layer_end,
                    inv_freq=wl.inv_freq, stream=stream, library=library)
+
+
+# ------------------------------------------------------- chunking, registry
+
+class Registry:
+    """A chunk registry of the library (wraps pic_registry_t*): entries are
+    (32-byte fingerprint, length, chunk id)."""
+
+    def __init__(self, kind: str = "xxh64", entries: Sequence = (), library=None):
+        lib = load_library(library)
+        self._lib = lib
+        self.kind = kind
+        self._handle = C.c_void_p()
+        _check(lib.pic_registry_create(FP_KINDS[kind], C.byref(self._handle)), lib)
+        for fp, length, chunk_id in entries:
+            self.add(fp, length, chunk_id)
+
+    def add(self, fp: bytes, length: int, chunk_id: int):
+        if len(fp) != 32:
+            raise ValueError("a fingerprint is 32 bytes")
+        buf = (C.c_uint8 * 32).from_buffer_copy(bytes(fp))
+        _check(self._lib.pic_registry_add(self.handle, buf, int(length), int(chunk_id)),
+               self._lib)
+
+    @property
+    def handle(self):
+        if not self._handle:
+            raise PicError(PIC_ERR_STATE, "registry destroyed")
+        return self._handle
+
+    def destroy(self):
+        if self._handle:
+            self._lib.pic_registry_destroy(self._handle)
+            self._handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def match(tokens, threshold: int, registry: Optional[Registry] = None, *, gear_seed: int = 0,
+          kind: str = "xxh64", fp_seed: int = 0, window: int = 128,
+          max_out: Optional[int] = None, out=None, n_out=None, stream=None, library=None):
+    """Enqueue pic_match on a device int32 token tensor.  Returns (out, n_out):
+    a uint8 device tensor of max_out 56-byte pic_match_t records (default
+    max_out: one per token, the most a stream can produce) and a one-element
+    int64 device tensor holding the segment count."""
+    torch = _torch()
+    if tokens.dtype != torch.int32 or tokens.dim() != 1 or not tokens.is_cuda:
+        raise TypeError("tokens must be a 1-D int32 GPU tensor")
+    if tokens.numel() and tokens.stride(0) != 1:
+        raise ValueError("tokens must be contiguous")
+    lib = registry._lib if registry is not None else load_library(library)
+    n = tokens.numel()
+    cap = n if max_out is None else int(max_out)
+    rec = C.sizeof(MatchRecord)
+    if out is None:
+        out = torch.empty((max(cap, 1), rec), dtype=torch.uint8, device=tokens.device)
+    elif out.dtype != torch.uint8 or out.numel() < cap * rec or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous uint8 tensor of at least {cap} records")
+    if n_out is None:
+        n_out = torch.empty(1, dtype=torch.int64, device=tokens.device)
+    cfg = CdcConfig(int(threshold) & (2 ** 64 - 1), int(gear_seed) & (2 ** 64 - 1),
+                    int(fp_seed) & (2 ** 64 - 1), FP_KINDS[kind], int(window))
+    _check(lib.pic_match(registry.handle if registry is not None else None, C.byref(cfg),
+                         C.c_void_p(tokens.data_ptr() if n else None), n,
+                         C.c_void_p(out.data_ptr()), cap, C.c_void_p(n_out.data_ptr()),
+                         _stream_of(tokens, stream)), lib)
+    return out, n_out
+
+
+def match_records(out, n_out) -> np.ndarray:
+    """Host copy of the written records as a MATCH_DTYPE array (waits for the
+    device)."""
+    m = int(n_out.cpu()[0])
+    raw = out.cpu().numpy().reshape(-1)
+    k = min(m, raw.size // MATCH_DTYPE.itemsize)
+    return raw[:k * MATCH_DTYPE.itemsize].view(MATCH_DTYPE), m

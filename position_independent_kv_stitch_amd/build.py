@@ -9,7 +9,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libpic_stitch.so")
 SOURCES = [os.path.join(CSRC, "stitch.hip"), os.path.join(CSRC, "attend.hip"),
-           os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "attend_plan.cpp")]
+           os.path.join(CSRC, "cdc.hip"), os.path.join(CSRC, "plan.cpp"),
+           os.path.join(CSRC, "attend_plan.cpp")]
 
 # Packed-fp32 instructions are kept out of the device code on purpose.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

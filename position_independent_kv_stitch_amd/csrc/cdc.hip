@@ -1,0 +1,822 @@
+// cdc.hip -- content-defined chunking of token streams, chunk fingerprints
+// and the chunk-registry lookup, on the GPU (pic_match and the registry
+// calls of the C ABI).
+//
+// What is computed (Irminsul: MLA-Native Position-Independent Caching for
+// Agentic LLM Serving, Technical Summary, "Content-Hash Keying with CDC" and
+// the S1 "detect and recover" strategy; EPIC Guide: Position-Independent
+// Caching for LLM Serving, the runtime's content hash registry):
+//   - the Gear value of a token is the xxHash64 of its 4 little-endian bytes
+//     under a gear seed; the rolling hash is h_i = 2 h_{i-1} + G(t_i) mod
+//     2^64, so h_i is a weighted sum over the 64-token window ending at i;
+//   - a chunk ends after token i when h_i < threshold, and at the stream end;
+//   - a chunk's fingerprint is the SHA-256 of its tokens' little-endian
+//     int32 bytes, or their xxHash64 as 8 little-endian bytes and 24 zeros;
+//   - a chunk is a hit when the registry holds the same fingerprint with the
+//     same length; a missed chunk is replaced, when a fallback window W > 0
+//     is given, by its consecutive W-token windows, each looked up again.
+//
+// GPU decomposition (integer work on a few bytes per token: no MFMA, no
+// HBM pressure; the cost is ALU work and its balance over lanes):
+//   1. cdc_flag_kernel: a workgroup takes 4096 positions, computes the Gear
+//      values of those positions and of the 64 before them into LDS, and
+//      every lane rolls the hash over 16 consecutive positions (64 steps to
+//      enter the window, then one shift-add per position).  Boundaries
+//      become a bit mask and a count per workgroup.
+//   2. scan_top_kernel: exclusive scan of the per-workgroup counts.
+//   3. cdc_ends_kernel: every boundary writes its chunk's end position.
+//   4. cdc_chunk_kernel: one lane per chunk hashes it, looks it up and counts
+//      the segments it becomes (1, or its number of windows).
+//   5. scan of the segment counts (reduce, top, apply) gives every chunk's
+//      first output slot and the total, which is written to *n_out.
+//   6. cdc_emit_kernel: one lane per output segment finds its chunk by
+//      binary search and writes the record, hashing and looking up a window.
+// The stream length and every count stay on the device: no call waits for
+// the GPU, and later kernels run grid-stride loops bounded by counts they
+// read from device memory.
+//
+// Hashes follow their published definitions: xxHash64 (Y. Collet's xxHash
+// specification) and SHA-256 (FIPS 180-4).  SHA-256's round constants and
+// initial state are the first 32 fractional bits of the cube roots of the
+// first 64 primes and of the square roots of the first 8; they are computed
+// at compile time below as exact integer roots.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "pic_internal.hpp"
+
+namespace pic {
+pic_status hip_fail(hipError_t e, const char *what);  // stitch.hip
+
+// Registry table (device and host).
+
+// Open-addressing table, linear probing, at most half full; an empty slot
+// has chunk_id -1.
+struct RegSlot {
+    uint64_t fp[4];
+    int32_t length;
+    int32_t chunk_id;
+};
+static_assert(sizeof(RegSlot) == 40, "slot layout");
+
+__host__ __device__ __forceinline__ uint64_t slot_hash(uint64_t fp0, int32_t length) {
+    uint64_t x = fp0 ^ (static_cast<uint64_t>(static_cast<uint32_t>(length)) * 0x9E3779B97F4A7C15ull);
+    x ^= x >> 31;
+    x *= 0xD6E8FEB86659FD93ull;
+    return x ^ (x >> 32);
+}
+
+namespace {
+
+constexpr int kThreads = 256;                  // workgroup of the block kernels
+constexpr int kPerThread = 16;                 // positions (or items) per lane
+constexpr int kBlockItems = kThreads * kPerThread;  // 4096
+constexpr int kWindow = 64;                    // Gear window
+constexpr int kWordsPerBlock = kBlockItems / 64;
+constexpr int kLaneThreads = 64;               // workgroup of the lane-per-item kernels
+
+// ------------------------------------------------------------- xxHash64
+
+constexpr uint64_t kP1 = 0x9E3779B185EBCA87ull;
+constexpr uint64_t kP2 = 0xC2B2AE3D27D4EB4Full;
+constexpr uint64_t kP3 = 0x165667B19E3779F9ull;
+constexpr uint64_t kP4 = 0x85EBCA77C2B2AE63ull;
+constexpr uint64_t kP5 = 0x27D4EB2F165667C5ull;
+
+__device__ __forceinline__ uint64_t rotl64(uint64_t x, int r) { return (x << r) | (x >> (64 - r)); }
+
+__device__ __forceinline__ uint64_t xx_round(uint64_t acc, uint64_t lane) {
+    return rotl64(acc + lane * kP2, 31) * kP1;
+}
+
+__device__ __forceinline__ uint64_t xx_avalanche(uint64_t h) {
+    h = (h ^ (h >> 33)) * kP2;
+    h = (h ^ (h >> 29)) * kP3;
+    return h ^ (h >> 32);
+}
+
+// Two consecutive tokens as one little-endian 64-bit word.
+__device__ __forceinline__ uint64_t tok_pair(const int32_t *t) {
+    return static_cast<uint64_t>(static_cast<uint32_t>(t[0])) |
+           (static_cast<uint64_t>(static_cast<uint32_t>(t[1])) << 32);
+}
+
+// xxHash64 of the 4 n bytes of tokens t[0, n).  The input is a whole number
+// of 4-byte words, so the specification's single-byte tail never occurs.
+// Stripes are read four at a time (128 bytes), the next group while the
+// current one is mixed.
+__device__ uint64_t xxh64_tokens(const int32_t *t, int64_t n, uint64_t seed) {
+    int64_t i = 0;
+    uint64_t h;
+    if (n >= 8) {  // 32-byte stripes into four accumulators
+        uint64_t a1 = seed + kP1 + kP2, a2 = seed + kP2, a3 = seed, a4 = seed - kP1;
+        const int64_t stripes = n / 8;
+        uint32_t nxt[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j) nxt[j] = j < 8 * stripes ? static_cast<uint32_t>(t[j]) : 0u;
+        for (int64_t g = 0; g < stripes; g += 4) {
+            uint32_t cur[32];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) cur[j] = nxt[j];
+            const int64_t q1 = 8 * (g + 4);
+            if (q1 + 32 <= 8 * stripes) {
+#pragma unroll
+                for (int j = 0; j < 32; ++j) nxt[j] = static_cast<uint32_t>(t[q1 + j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 32; ++j)
+                    nxt[j] = q1 + j < 8 * stripes ? static_cast<uint32_t>(t[q1 + j]) : 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if (g + k < stripes) {
+                    const uint32_t *c = cur + 8 * k;
+                    a1 = xx_round(a1, c[0] | (static_cast<uint64_t>(c[1]) << 32));
+                    a2 = xx_round(a2, c[2] | (static_cast<uint64_t>(c[3]) << 32));
+                    a3 = xx_round(a3, c[4] | (static_cast<uint64_t>(c[5]) << 32));
+                    a4 = xx_round(a4, c[6] | (static_cast<uint64_t>(c[7]) << 32));
+                }
+            }
+        }
+        i = 8 * stripes;
+        h = rotl64(a1, 1) + rotl64(a2, 7) + rotl64(a3, 12) + rotl64(a4, 18);
+        h = (h ^ xx_round(0, a1)) * kP1 + kP4;
+        h = (h ^ xx_round(0, a2)) * kP1 + kP4;
+        h = (h ^ xx_round(0, a3)) * kP1 + kP4;
+        h = (h ^ xx_round(0, a4)) * kP1 + kP4;
+    } else {
+        h = seed + kP5;
+    }
+    h += static_cast<uint64_t>(n) * 4u;
+    for (; i + 2 <= n; i += 2) h = rotl64(h ^ xx_round(0, tok_pair(t + i)), 27) * kP1 + kP4;
+    if (i < n) h = rotl64(h ^ (static_cast<uint64_t>(static_cast<uint32_t>(t[i])) * kP1), 23) * kP2 + kP3;
+    return xx_avalanche(h);
+}
+
+// Gear value: xxHash64 of one token's 4 bytes (the short-input form).
+__device__ __forceinline__ uint64_t gear_value(int32_t token, uint64_t seed) {
+    uint64_t h = seed + kP5 + 4u;
+    h = rotl64(h ^ (static_cast<uint64_t>(static_cast<uint32_t>(token)) * kP1), 23) * kP2 + kP3;
+    return xx_avalanche(h);
+}
+
+// -------------------------------------------------------------- SHA-256
+
+struct ShaConstants {
+    uint32_t k[64];
+    uint32_t h0[8];
+};
+
+constexpr bool is_prime(uint32_t v) {
+    if (v < 2) return false;
+    for (uint32_t d = 2; d * d <= v; ++d)
+        if (v % d == 0) return false;
+    return true;
+}
+
+// Largest r with r^e <= x (e = 2 or 3), by bisection on exact integers.
+constexpr uint64_t iroot(unsigned __int128 x, int e) {
+    uint64_t lo = 0, hi = 1ull << 40;
+    while (hi - lo > 1) {
+        const uint64_t mid = lo + (hi - lo) / 2;
+        unsigned __int128 p = mid;
+        p *= mid;
+        if (e == 3) p *= mid;
+        if (p <= x) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+// floor(root(p) * 2^32) = floor(root(p * 2^(32 e))); its low 32 bits are the
+// first 32 fractional bits of root(p).
+constexpr ShaConstants make_sha_constants() {
+    ShaConstants c{};
+    int n = 0;
+    for (uint32_t p = 2; n < 64; ++p) {
+        if (!is_prime(p)) continue;
+        c.k[n] = static_cast<uint32_t>(iroot(static_cast<unsigned __int128>(p) << 96, 3));
+        if (n < 8) c.h0[n] = static_cast<uint32_t>(iroot(static_cast<unsigned __int128>(p) << 64, 2));
+        ++n;
+    }
+    return c;
+}
+
+constexpr ShaConstants kSha = make_sha_constants();
+
+__device__ __forceinline__ uint32_t rotr32(uint32_t x, int r) { return (x >> r) | (x << (32 - r)); }
+
+__device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
+
+// One compression of a 16-word block; w is consumed as the schedule's ring.
+__device__ __forceinline__ void sha_compress(uint32_t st[8], uint32_t w[16]) {
+    uint32_t a = st[0], b = st[1], c = st[2], d = st[3], e = st[4], f = st[5], g = st[6],
+             h = st[7];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        if (t >= 16) {
+            const uint32_t x = w[(t + 1) & 15], y = w[(t + 14) & 15];
+            const uint32_t s0 = rotr32(x, 7) ^ rotr32(x, 18) ^ (x >> 3);
+            const uint32_t s1 = rotr32(y, 17) ^ rotr32(y, 19) ^ (y >> 10);
+            w[t & 15] += s0 + w[(t + 9) & 15] + s1;
+        }
+        const uint32_t t1 = h + (rotr32(e, 6) ^ rotr32(e, 11) ^ rotr32(e, 25)) +
+                            ((e & f) ^ (~e & g)) + kSha.k[t] + w[t & 15];
+        const uint32_t t2 = (rotr32(a, 2) ^ rotr32(a, 13) ^ rotr32(a, 22)) +
+                            ((a & b) ^ (a & c) ^ (b & c));
+        h = g;
+        g = f;
+        f = e;
+        e = d + t1;
+        d = c;
+        c = b;
+        b = a;
+        a = t1 + t2;
+    }
+    st[0] += a;
+    st[1] += b;
+    st[2] += c;
+    st[3] += d;
+    st[4] += e;
+    st[5] += f;
+    st[6] += g;
+    st[7] += h;
+}
+
+// SHA-256 of the 4 n bytes of tokens t[0, n).  The message is word-aligned,
+// so message word q is the byte swap of token q, the 0x80 padding byte
+// starts word n, and the bit length fills words 14 and 15 of the last block.
+// The next block's words are loaded before the current block is compressed,
+// so a lane's loads overlap its rounds instead of stalling every block.
+__device__ void sha256_tokens(const int32_t *t, int64_t n, uint32_t st[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st[j] = kSha.h0[j];
+    const int64_t blocks = (n + 3 + 15) / 16;
+    const uint64_t bits = static_cast<uint64_t>(n) * 32u;
+    uint32_t nxt[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) nxt[j] = j < n ? static_cast<uint32_t>(t[j]) : 0u;
+    for (int64_t b = 0; b < blocks; ++b) {
+        const int64_t q0 = 16 * b;
+        uint32_t w[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int64_t q = q0 + j;
+            w[j] = q < n ? bswap32(nxt[j]) : (q == n ? 0x80000000u : 0u);
+        }
+        if (b == blocks - 1) {
+            w[14] = static_cast<uint32_t>(bits >> 32);
+            w[15] = static_cast<uint32_t>(bits);
+        }
+        const int64_t q1 = q0 + 16;
+        if (q1 + 16 <= n) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) nxt[j] = static_cast<uint32_t>(t[q1 + j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) nxt[j] = q1 + j < n ? static_cast<uint32_t>(t[q1 + j]) : 0u;
+        }
+        sha_compress(st, w);
+    }
+}
+
+// Fingerprint as four little-endian 64-bit words of its 32 bytes.
+__device__ void fingerprint(const int32_t *t, int64_t n, int32_t kind, uint64_t seed,
+                            uint64_t fp[4]) {
+    if (kind == PIC_FP_SHA256) {
+        uint32_t st[8];
+        sha256_tokens(t, n, st);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)  // digest bytes are the state words, big-endian
+            fp[j] = static_cast<uint64_t>(bswap32(st[2 * j])) |
+                    (static_cast<uint64_t>(bswap32(st[2 * j + 1])) << 32);
+    } else {
+        fp[0] = xxh64_tokens(t, n, seed);
+        fp[1] = fp[2] = fp[3] = 0;
+    }
+}
+
+// ------------------------------------------------------- registry lookup
+
+__device__ int32_t reg_lookup(const RegSlot *tab, uint32_t mask, const uint64_t fp[4],
+                              int32_t length) {
+    if (!tab) return -1;
+    uint32_t i = static_cast<uint32_t>(slot_hash(fp[0], length)) & mask;
+    for (uint32_t probe = 0; probe <= mask; ++probe) {
+        const RegSlot &s = tab[i];
+        if (s.chunk_id < 0) return -1;
+        if (s.length == length && s.fp[0] == fp[0] && s.fp[1] == fp[1] && s.fp[2] == fp[2] &&
+            s.fp[3] == fp[3])
+            return s.chunk_id;
+        i = (i + 1) & mask;
+    }
+    return -1;
+}
+
+// ------------------------------------------------------------ scan helper
+
+// Exclusive scan of one int32 per lane over a workgroup of kThreads lanes;
+// *total receives the sum.  `lds` holds kThreads / 64 + 1 ints.
+__device__ int32_t block_exclusive_scan(int32_t v, int32_t *lds, int32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) lds[wave] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int32_t run = 0;
+        for (int w = 0; w < kThreads / 64; ++w) {
+            const int32_t s = lds[w];
+            lds[w] = run;
+            run += s;
+        }
+        lds[kThreads / 64] = run;
+    }
+    __syncthreads();
+    const int32_t r = lds[wave] + x - v;
+    *total = lds[kThreads / 64];
+    __syncthreads();
+    return r;
+}
+
+// --------------------------------------------------------------- kernels
+
+// Padded LDS index of Gear slot j (slots 0..63 are the 64 positions before
+// the workgroup's first): one 8-byte pad per 16 slots puts the 16-position
+// runs of consecutive lanes in different banks.
+__device__ __forceinline__ int gpad(int j) { return j + (j >> 4); }
+
+__global__ __launch_bounds__(kThreads) void cdc_flag_kernel(const int32_t *__restrict__ tok,
+                                                            int64_t n, uint64_t gear_seed,
+                                                            uint64_t threshold,
+                                                            uint64_t *__restrict__ flags,
+                                                            int32_t *__restrict__ bcnt) {
+    constexpr int kSlots = kBlockItems + kWindow;
+    __shared__ uint64_t g[kSlots + kSlots / 16];
+    __shared__ uint32_t bits[kThreads];
+    __shared__ int32_t cnt;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kBlockItems;
+    for (int j = threadIdx.x; j < kSlots; j += kThreads) {
+        const int64_t pos = base - kWindow + j;
+        g[gpad(j)] = (pos >= 0 && pos < n) ? gear_value(tok[pos], gear_seed) : 0;
+    }
+    if (threadIdx.x == 0) cnt = 0;
+    __syncthreads();
+    const int first = threadIdx.x * kPerThread;
+    uint64_t h = 0;  // after this loop: h at the position before the lane's first
+    for (int j = 0; j < kWindow; ++j) h = (h << 1) + g[gpad(first + j)];
+    uint32_t b = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+        const int64_t pos = base + first + j;
+        h = (h << 1) + g[gpad(first + kWindow + j)];
+        if (pos < n && (h < threshold || pos == n - 1)) b |= 1u << j;
+    }
+    bits[threadIdx.x] = b;
+    atomicAdd(&cnt, __popc(b));
+    __syncthreads();
+    if (threadIdx.x < kWordsPerBlock) {
+        const int t = 4 * threadIdx.x;
+        flags[static_cast<int64_t>(blockIdx.x) * kWordsPerBlock + threadIdx.x] =
+            static_cast<uint64_t>(bits[t]) | (static_cast<uint64_t>(bits[t + 1]) << 16) |
+            (static_cast<uint64_t>(bits[t + 2]) << 32) | (static_cast<uint64_t>(bits[t + 3]) << 48);
+    }
+    if (threadIdx.x == 0) bcnt[blockIdx.x] = cnt;
+}
+
+// Exclusive scan, in place, of v[0, len) where len = n_host, or, when
+// items_dev is given, the number of kBlockItems-blocks covering *items_dev
+// items.  The sum goes to *total (and to *total64 when given).  One
+// workgroup of 1024 lanes; lane l scans a contiguous slice.
+__global__ __launch_bounds__(1024) void scan_top_kernel(int32_t *__restrict__ v, int64_t n_host,
+                                                        const int32_t *__restrict__ items_dev,
+                                                        int32_t *__restrict__ total,
+                                                        int64_t *__restrict__ total64) {
+    __shared__ int32_t part[1024];
+    const int64_t len =
+        items_dev ? (static_cast<int64_t>(*items_dev) + kBlockItems - 1) / kBlockItems : n_host;
+    const int64_t per = (len + 1023) / 1024;
+    const int64_t lo = min(len, per * threadIdx.x), hi = min(len, lo + per);
+    int32_t s = 0;
+    for (int64_t i = lo; i < hi; ++i) s += v[i];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int d = 1; d < 1024; d <<= 1) {  // inclusive Hillis-Steele scan of the slices
+        const int32_t y = threadIdx.x >= d ? part[threadIdx.x - d] : 0;
+        __syncthreads();
+        part[threadIdx.x] += y;
+        __syncthreads();
+    }
+    int32_t run = part[threadIdx.x] - s;
+    for (int64_t i = lo; i < hi; ++i) {
+        const int32_t x = v[i];
+        v[i] = run;
+        run += x;
+    }
+    if (threadIdx.x == 1023) {
+        *total = part[1023];
+        if (total64) *total64 = part[1023];
+    }
+}
+
+// End position (exclusive) of every chunk, in stream order.
+__global__ __launch_bounds__(kThreads) void cdc_ends_kernel(const uint64_t *__restrict__ flags,
+                                                            const int32_t *__restrict__ boff,
+                                                            int32_t *__restrict__ ends) {
+    __shared__ int32_t lds[kThreads / 64 + 1];
+    const uint64_t word =
+        flags[static_cast<int64_t>(blockIdx.x) * kWordsPerBlock + (threadIdx.x >> 2)];
+    uint32_t b = static_cast<uint32_t>(word >> (16 * (threadIdx.x & 3))) & 0xFFFFu;
+    int32_t total;
+    int32_t slot = boff[blockIdx.x] + block_exclusive_scan(__popc(b), lds, &total);
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kBlockItems + threadIdx.x * kPerThread;
+    while (b) {
+        const int j = __ffs(b) - 1;
+        ends[slot++] = static_cast<int32_t>(first + j + 1);
+        b &= b - 1;
+    }
+}
+
+struct MatchArgs {
+    const int32_t *tok;
+    const int32_t *ends;    // [nc]
+    int32_t *seg;           // [nc]: segment count, then first output slot
+    const int32_t *counts;  // [0] chunks nc, [1] segments m
+    uint64_t *cfp;          // [keep][4] chunk fingerprints
+    int32_t *cid;           // [keep] chunk registry ids
+    const RegSlot *tab;
+    uint32_t mask;
+    int32_t kind;
+    uint64_t fp_seed;
+    int32_t window;
+    int32_t keep;           // chunks whose fingerprint is kept: min(n, max_out)
+    pic_match_t *out;
+    int64_t max_out;
+    int64_t n;              // stream length: bounds every count read back
+};
+
+__device__ __forceinline__ int64_t chunk_start(const int32_t *ends, int64_t c) {
+    return c ? ends[c - 1] : 0;
+}
+
+// One lane per chunk: fingerprint, lookup, number of output segments.
+__global__ __launch_bounds__(kLaneThreads) void cdc_chunk_kernel(MatchArgs a) {
+    const int64_t nc = min(static_cast<int64_t>(a.counts[0]), a.n);
+    for (int64_t c = static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x; c < nc;
+         c += static_cast<int64_t>(gridDim.x) * kLaneThreads) {
+        const int64_t s = chunk_start(a.ends, c), len = a.ends[c] - s;
+        uint64_t fp[4];
+        fingerprint(a.tok + s, len, a.kind, a.fp_seed, fp);
+        const int32_t id = reg_lookup(a.tab, a.mask, fp, static_cast<int32_t>(len));
+        a.seg[c] = (id >= 0 || a.window <= 0) ? 1
+                                              : static_cast<int32_t>((len + a.window - 1) / a.window);
+        if (c < a.keep) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.cfp[4 * c + j] = fp[j];
+            a.cid[c] = id;
+        }
+    }
+}
+
+// Per-block sums of v[0, *len_dev) (blocks past the end write nothing).
+__global__ __launch_bounds__(kThreads) void scan_reduce_kernel(const int32_t *__restrict__ v,
+                                                               const int32_t *__restrict__ len_dev,
+                                                               int32_t *__restrict__ bsum) {
+    __shared__ int32_t cnt;
+    const int64_t len = *len_dev, base = static_cast<int64_t>(blockIdx.x) * kBlockItems;
+    if (base >= len) return;
+    if (threadIdx.x == 0) cnt = 0;
+    __syncthreads();
+    int32_t s = 0;
+    for (int j = 0; j < kPerThread; ++j) {
+        const int64_t i = base + j * kThreads + threadIdx.x;
+        if (i < len) s += v[i];
+    }
+    atomicAdd(&cnt, s);
+    __syncthreads();
+    if (threadIdx.x == 0) bsum[blockIdx.x] = cnt;
+}
+
+// In-place exclusive scan of v[0, *len_dev), block b offset by boff[b].
+__global__ __launch_bounds__(kThreads) void scan_apply_kernel(int32_t *__restrict__ v,
+                                                              const int32_t *__restrict__ len_dev,
+                                                              const int32_t *__restrict__ boff) {
+    __shared__ int32_t lds[kThreads / 64 + 1];
+    const int64_t len = *len_dev, base = static_cast<int64_t>(blockIdx.x) * kBlockItems;
+    if (base >= len) return;  // uniform over the workgroup
+    const int64_t first = base + threadIdx.x * kPerThread;
+    int32_t x[kPerThread];
+    int32_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+        x[j] = first + j < len ? v[first + j] : 0;
+        s += x[j];
+    }
+    int32_t total;
+    int32_t run = boff[blockIdx.x] + block_exclusive_scan(s, lds, &total);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) {
+        if (first + j < len) v[first + j] = run;
+        run += x[j];
+    }
+}
+
+// One lane per output record (the first max_out segments).
+__global__ __launch_bounds__(kLaneThreads) void cdc_emit_kernel(MatchArgs a) {
+    const int64_t nc = min(static_cast<int64_t>(a.counts[0]), a.n);
+    const int64_t m = min(static_cast<int64_t>(a.counts[1]), a.n);
+    const int64_t lim = m < a.max_out ? m : a.max_out;
+    for (int64_t s = static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x; s < lim;
+         s += static_cast<int64_t>(gridDim.x) * kLaneThreads) {
+        int64_t lo = 0, hi = nc;  // last chunk whose first slot is <= s
+        while (hi - lo > 1) {
+            const int64_t mid = (lo + hi) >> 1;
+            if (a.seg[mid] <= s) lo = mid; else hi = mid;
+        }
+        const int64_t c = lo, k = s - a.seg[c];
+        const int64_t cs = chunk_start(a.ends, c), ce = a.ends[c];
+        pic_match_t r;
+        uint64_t fp[4];
+        if (a.cid[c] >= 0 || a.window <= 0) {
+            r.start = cs;
+            r.length = static_cast<int32_t>(ce - cs);
+            r.level = 0;
+            r.chunk_id = a.cid[c];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fp[j] = a.cfp[4 * c + j];
+        } else {
+            const int64_t ws = cs + k * a.window;
+            const int64_t wl = ce - ws < a.window ? ce - ws : a.window;
+            fingerprint(a.tok + ws, wl, a.kind, a.fp_seed, fp);
+            r.start = ws;
+            r.length = static_cast<int32_t>(wl);
+            r.level = 1;
+            r.chunk_id = reg_lookup(a.tab, a.mask, fp, static_cast<int32_t>(wl));
+        }
+        r.reserved = 0;
+        memcpy(r.fp, fp, 32);
+        a.out[s] = r;
+    }
+}
+
+__global__ void write_zero_kernel(int64_t *p) { *p = 0; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+}  // namespace
+}  // namespace pic
+
+// The opaque registry handle of the C ABI.
+struct pic_registry {
+    uint32_t magic = 0x52454753u;
+    int32_t kind = 0;
+    std::mutex mu;
+    std::vector<pic::RegSlot> entries;    // in registration order
+    std::unordered_set<std::string> keys;  // fingerprint bytes + length, for duplicates
+    bool dirty = true;
+    int device = -1;
+    std::vector<pic::RegSlot> host_table;  // last uploaded table (kept alive for the copy)
+    pic::RegSlot *d_table = nullptr;
+    size_t d_slots = 0;
+    uint32_t mask = 0;
+    hipEvent_t upload_event = nullptr;
+};
+
+namespace pic {
+namespace {
+
+constexpr uint32_t kRegMagic = 0x52454753u;
+
+std::string reg_key(const uint64_t fp[4], int32_t length) {
+    std::string k(reinterpret_cast<const char *>(fp), 32);
+    k.append(reinterpret_cast<const char *>(&length), 4);
+    return k;
+}
+
+// Bring the device table up to date on the current device, ordered on
+// `stream`.  A changed registry waits for the device first, since kernels of
+// earlier calls may still read the old table.
+pic_status sync_registry(pic_registry *reg, hipStream_t stream, const RegSlot **tab,
+                         uint32_t *mask) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (reg->device >= 0 && dev != reg->device)
+        return fail(PIC_ERR_STATE, "registry lives on device %d, current device is %d",
+                    reg->device, dev);
+    if (reg->dirty) {
+        if (reg->d_table) {
+            e = hipDeviceSynchronize();
+            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize (registry update)");
+        }
+        size_t slots = 16;
+        while (slots < 2 * reg->entries.size()) slots *= 2;
+        reg->host_table.assign(slots, RegSlot{{0, 0, 0, 0}, 0, -1});
+        const uint32_t m = static_cast<uint32_t>(slots - 1);
+        for (const RegSlot &s : reg->entries) {
+            uint32_t i = static_cast<uint32_t>(slot_hash(s.fp[0], s.length)) & m;
+            while (reg->host_table[i].chunk_id >= 0) i = (i + 1) & m;
+            reg->host_table[i] = s;
+        }
+        if (slots > reg->d_slots) {
+            if (reg->d_table) (void)hipFree(reg->d_table);
+            reg->d_table = nullptr;
+            reg->d_slots = 0;
+            e = hipMalloc(&reg->d_table, slots * sizeof(RegSlot));
+            if (e != hipSuccess) {
+                reg->d_table = nullptr;
+                return hip_fail(e, "hipMalloc (registry table)");
+            }
+            reg->d_slots = slots;
+        }
+        e = hipMemcpyAsync(reg->d_table, reg->host_table.data(), slots * sizeof(RegSlot),
+                           hipMemcpyHostToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (registry table)");
+        if (!reg->upload_event) {
+            e = hipEventCreateWithFlags(&reg->upload_event, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                reg->upload_event = nullptr;
+                return hip_fail(e, "hipEventCreate");
+            }
+        }
+        e = hipEventRecord(reg->upload_event, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        reg->mask = m;
+        reg->device = dev;
+        reg->dirty = false;
+    } else {
+        e = hipStreamWaitEvent(stream, reg->upload_event, 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    }
+    *tab = reg->d_table;
+    *mask = reg->mask;
+    return PIC_OK;
+}
+
+}  // namespace
+}  // namespace pic
+
+extern "C" {
+
+pic_status pic_registry_create(int32_t fingerprint, pic_registry_t **out) {
+    pic::clear_error();
+    if (!out) return pic::fail(PIC_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (fingerprint != PIC_FP_XXH64 && fingerprint != PIC_FP_SHA256)
+        return pic::fail(PIC_ERR_INVALID_ARG, "unknown fingerprint kind %d", fingerprint);
+    pic_registry *r = new (std::nothrow) pic_registry;
+    if (!r) return pic::fail(PIC_ERR_NOMEM, "out of host memory");
+    r->kind = fingerprint;
+    *out = r;
+    return PIC_OK;
+}
+
+pic_status pic_registry_add(pic_registry_t *reg, const uint8_t *fp, int32_t length,
+                            int32_t chunk_id) {
+    pic::clear_error();
+    if (!reg || reg->magic != pic::kRegMagic)
+        return pic::fail(PIC_ERR_STATE, "invalid or destroyed registry");
+    if (!fp) return pic::fail(PIC_ERR_INVALID_ARG, "fingerprint is NULL");
+    if (length < 1) return pic::fail(PIC_ERR_RANGE, "length %d < 1", length);
+    if (chunk_id < 0) return pic::fail(PIC_ERR_RANGE, "chunk_id %d < 0", chunk_id);
+    pic::RegSlot s{};
+    std::memcpy(s.fp, fp, 32);
+    s.length = length;
+    s.chunk_id = chunk_id;
+    std::lock_guard<std::mutex> lock(reg->mu);
+    try {
+        if (!reg->keys.insert(pic::reg_key(s.fp, length)).second)
+            return pic::fail(PIC_ERR_OVERLAP, "a segment with this fingerprint and length %d "
+                             "is already registered", length);
+        reg->entries.push_back(s);
+    } catch (const std::bad_alloc &) {
+        return pic::fail(PIC_ERR_NOMEM, "out of host memory");
+    }
+    reg->dirty = true;
+    return PIC_OK;
+}
+
+void pic_registry_destroy(pic_registry_t *reg) {
+    if (!reg || reg->magic != pic::kRegMagic) return;
+    reg->magic = 0;
+    if (reg->d_table) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(reg->d_table);
+    }
+    if (reg->upload_event) (void)hipEventDestroy(reg->upload_event);
+    delete reg;
+}
+
+pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32_t *tokens,
+                     int64_t n_tokens, pic_match_t *out, int64_t max_out, int64_t *n_out,
+                     void *stream_) {
+    using namespace pic;
+    clear_error();
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    if (!cfg) return fail(PIC_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->fingerprint != PIC_FP_XXH64 && cfg->fingerprint != PIC_FP_SHA256)
+        return fail(PIC_ERR_INVALID_ARG, "unknown fingerprint kind %d", cfg->fingerprint);
+    if (reg && reg->magic != kRegMagic) return fail(PIC_ERR_STATE, "invalid or destroyed registry");
+    if (reg && reg->kind != cfg->fingerprint)
+        return fail(PIC_ERR_INVALID_ARG, "registry holds fingerprint kind %d, cfg asks for %d",
+                    reg->kind, cfg->fingerprint);
+    if (n_tokens < 0 || n_tokens >= (int64_t{1} << 31))
+        return fail(PIC_ERR_RANGE, "n_tokens %lld outside [0, 2^31)",
+                    static_cast<long long>(n_tokens));
+    if (cfg->window < 0) return fail(PIC_ERR_RANGE, "window %d < 0", cfg->window);
+    if (max_out < 0) return fail(PIC_ERR_RANGE, "max_out < 0");
+    if (!n_out) return fail(PIC_ERR_INVALID_ARG, "n_out is NULL");
+    if (n_tokens > 0 && !tokens) return fail(PIC_ERR_INVALID_ARG, "tokens is NULL");
+    if (max_out > 0 && !out) return fail(PIC_ERR_INVALID_ARG, "out is NULL");
+    if ((reinterpret_cast<uintptr_t>(tokens) & 3u) || (reinterpret_cast<uintptr_t>(out) & 7u) ||
+        (reinterpret_cast<uintptr_t>(n_out) & 7u))
+        return fail(PIC_ERR_ALIGN, "tokens must be 4-byte, out and n_out 8-byte aligned");
+
+    const RegSlot *tab = nullptr;
+    uint32_t mask = 0;
+    std::unique_lock<std::mutex> lock;
+    if (reg) {
+        lock = std::unique_lock<std::mutex>(reg->mu);
+        pic_status st = sync_registry(reg, stream, &tab, &mask);
+        if (st != PIC_OK) return st;
+    }
+    hipError_t e;
+    if (n_tokens == 0) {
+        write_zero_kernel<<<1, 1, 0, stream>>>(n_out);
+        e = hipGetLastError();
+        return e == hipSuccess ? PIC_OK : hip_fail(e, "pic_match launch");
+    }
+
+    // Temporary device memory (stream-ordered).
+    const int64_t n = n_tokens;
+    const int64_t nb = (n + kBlockItems - 1) / kBlockItems;
+    const int64_t keep = max_out < n ? max_out : n;
+    size_t off = 0;
+    const size_t o_flags = off; off = align256(off + sizeof(uint64_t) * nb * kWordsPerBlock);
+    const size_t o_bcnt = off;  off = align256(off + sizeof(int32_t) * (nb + 1));
+    const size_t o_ends = off;  off = align256(off + sizeof(int32_t) * n);
+    const size_t o_seg = off;   off = align256(off + sizeof(int32_t) * n);
+    const size_t o_ssum = off;  off = align256(off + sizeof(int32_t) * (nb + 1));
+    const size_t o_cnt = off;   off = align256(off + sizeof(int32_t) * 2);
+    const size_t o_cfp = off;   off = align256(off + sizeof(uint64_t) * 4 * keep);
+    const size_t o_cid = off;   off = align256(off + sizeof(int32_t) * keep);
+    void *mem = nullptr;
+    e = hipMallocAsync(&mem, off, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync (pic_match temporaries)");
+    uint8_t *base = static_cast<uint8_t *>(mem);
+    auto *flags = reinterpret_cast<uint64_t *>(base + o_flags);
+    auto *bcnt = reinterpret_cast<int32_t *>(base + o_bcnt);
+    auto *ssum = reinterpret_cast<int32_t *>(base + o_ssum);
+    auto *counts = reinterpret_cast<int32_t *>(base + o_cnt);
+
+    MatchArgs a{};
+    a.tok = tokens;
+    a.ends = reinterpret_cast<int32_t *>(base + o_ends);
+    a.seg = reinterpret_cast<int32_t *>(base + o_seg);
+    a.counts = counts;
+    a.cfp = reinterpret_cast<uint64_t *>(base + o_cfp);
+    a.cid = reinterpret_cast<int32_t *>(base + o_cid);
+    a.tab = tab;
+    a.mask = mask;
+    a.kind = cfg->fingerprint;
+    a.fp_seed = cfg->fp_seed;
+    a.window = cfg->window;
+    a.keep = static_cast<int32_t>(keep);
+    a.out = out;
+    a.max_out = max_out;
+    a.n = n;
+
+    // Lane-per-item kernels stride over at most this many workgroups.
+    auto lane_grid = [](int64_t bound) {
+        const int64_t g = (bound + kLaneThreads - 1) / kLaneThreads;
+        return static_cast<unsigned>(g < 1 ? 1 : (g > 16384 ? 16384 : g));
+    };
+    const unsigned gb = static_cast<unsigned>(nb);
+    cdc_flag_kernel<<<gb, kThreads, 0, stream>>>(tokens, n, cfg->gear_seed, cfg->threshold, flags,
+                                                bcnt);
+    scan_top_kernel<<<1, 1024, 0, stream>>>(bcnt, nb, nullptr, &counts[0], nullptr);
+    cdc_ends_kernel<<<gb, kThreads, 0, stream>>>(flags, bcnt, const_cast<int32_t *>(a.ends));
+    cdc_chunk_kernel<<<lane_grid(n), kLaneThreads, 0, stream>>>(a);
+    scan_reduce_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum);
+    scan_top_kernel<<<1, 1024, 0, stream>>>(ssum, 0, &counts[0], &counts[1], n_out);
+    scan_apply_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum);
+    if (keep > 0) cdc_emit_kernel<<<lane_grid(keep), kLaneThreads, 0, stream>>>(a);
+    e = hipGetLastError();
+    const hipError_t e2 = hipFreeAsync(mem, stream);
+    if (e != hipSuccess) return hip_fail(e, "pic_match launch");
+    if (e2 != hipSuccess) return hip_fail(e2, "hipFreeAsync (pic_match temporaries)");
+    return PIC_OK;
+}
+
+}  // extern "C"

@@ -37,6 +37,7 @@ STRUCTS = {
     "pic_rope_config": B.RopeConfig, "pic_kv_shape": B.KvShape, "pic_chunk": B.ChunkC,
     "pic_entry": B.EntryC, "pic_request": B.RequestC, "pic_geom": B.Geom, "pic_attend_args": B.AttendArgs,
     "pic_kv_view": B.KvView, "pic_segment": B.SegmentC, "pic_plan_info_t": B.PlanInfo,
+    "pic_cdc_config": B.CdcConfig, "pic_match_t": B.MatchRecord,
 }
 
 
@@ -101,3 +102,44 @@ def test_product_does_not_import_oracle(mod):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text
                 assert "pic_oracle" not in text and "orc_" not in text
+
+
+def test_match_and_registry_errors_before_device_work():
+    """pic_match and the registry calls refuse bad arguments before any
+    device call (so these run without a GPU)."""
+    lib = B.load_library()
+    reg = C.c_void_p()
+    assert lib.pic_registry_create(7, C.byref(reg)) == B.PIC_ERR_INVALID_ARG
+    assert lib.pic_registry_create(B.FP_KINDS["sha256"], C.byref(reg)) == B.PIC_OK
+    fp = (C.c_uint8 * 32)(*range(32))
+    assert lib.pic_registry_add(reg, fp, 0, 1) == B.PIC_ERR_RANGE
+    assert lib.pic_registry_add(reg, fp, 5, -1) == B.PIC_ERR_RANGE
+    assert lib.pic_registry_add(reg, None, 5, 1) == B.PIC_ERR_INVALID_ARG
+    assert lib.pic_registry_add(reg, fp, 5, 1) == B.PIC_OK
+    assert lib.pic_registry_add(reg, fp, 5, 2) == B.PIC_ERR_OVERLAP
+    assert lib.pic_registry_add(reg, fp, 6, 2) == B.PIC_OK
+    assert lib.pic_registry_add(None, fp, 6, 2) == B.PIC_ERR_STATE
+
+    tok, out, n_out = C.c_void_p(0x10000), C.c_void_p(0x20000), C.c_void_p(0x30000)
+
+    def call(cfg, n=100, max_out=10, r=None, t=tok, o=out, no=n_out):
+        return lib.pic_match(r, C.byref(cfg) if cfg is not None else None, t, n, o, max_out,
+                             no, None)
+
+    good = B.CdcConfig(1 << 56, 0, 0, B.FP_KINDS["xxh64"], 128)
+    assert call(None) == B.PIC_ERR_INVALID_ARG
+    assert call(B.CdcConfig(1 << 56, 0, 0, 9, 128)) == B.PIC_ERR_INVALID_ARG
+    assert call(good, r=reg) == B.PIC_ERR_INVALID_ARG  # registry holds SHA-256 fingerprints
+    assert b"fingerprint kind" in lib.pic_last_error()
+    assert call(good, n=-1) == B.PIC_ERR_RANGE
+    assert call(good, n=1 << 31) == B.PIC_ERR_RANGE
+    assert call(B.CdcConfig(1 << 56, 0, 0, 0, -1)) == B.PIC_ERR_RANGE
+    assert call(good, max_out=-1) == B.PIC_ERR_RANGE
+    assert call(good, no=None) == B.PIC_ERR_INVALID_ARG
+    assert call(good, t=None) == B.PIC_ERR_INVALID_ARG
+    assert call(good, o=None) == B.PIC_ERR_INVALID_ARG
+    assert call(good, t=C.c_void_p(0x10002)) == B.PIC_ERR_ALIGN
+    assert call(good, o=C.c_void_p(0x20004)) == B.PIC_ERR_ALIGN
+    assert call(good, no=C.c_void_p(0x30004)) == B.PIC_ERR_ALIGN
+    lib.pic_registry_destroy(reg)
+    lib.pic_registry_destroy(None)
