@@ -29,6 +29,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "stitched-KV HBM GB/s (read+write) and token-layers/s; % of HBM peak"
 PEAK_GBS = 8000.0  # MI355X HBM3E, published
+# 32-bit integer vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 KERNEL_SOURCES = [os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc", f)
                   for f in ("stitch.hip", "plan.cpp", "pic_internal.hpp")]
 COUNTERS = os.path.join(ROOT, "profiles", "stitch_kernel_llama3-8b-paged_counters.md")
@@ -202,6 +204,13 @@ def setup_cdc(name, torch, pic):
     step()
     recs, m = pic.match_records(out, n_out)
     hits = recs[:m]["chunk_id"] >= 0
+    window_tokens = int(recs[:m]["length"][recs[:m]["level"] == 1].sum())
+    # Integer work of one call, in 32-bit ALU operations counted from the
+    # definitions (a 64-bit add, xor, shift or rotate counts 2, a 64-bit
+    # multiply 4): Gear value and rolling step per token, then every chunk
+    # token hashed once and every window token once more.
+    hash_ops = 6.0 if kind == "xxh64" else 2296.0 / 16  # per token: xxHash64 lane / SHA-256 block
+    alu_ops = n * 40 + (n + window_tokens) * hash_ops
     cfg = {"workload": WORKLOADS[name], "tokens": n, "requests": len(ts.request_starts),
            "registry_entries": len(seen), "segments": int(m),
            "registered_segments": int(hits.sum()),
@@ -210,7 +219,7 @@ def setup_cdc(name, torch, pic):
            "parallelism": "single-gpu"}
     return {"wl": None, "step": step, "bytes": 4 * n, "token_layers": n,
             "kernel": "pic_match (8 kernels: Gear flags, scans, ends, chunk hashes, emit)",
-            "plan": None, "registry": reg, "config": cfg, "bound": "alu"}
+            "plan": None, "registry": reg, "config": cfg, "alu_ops": alu_ops}
 
 
 def time_steps(torch, step, steps):
@@ -366,6 +375,15 @@ def main():
                      "median_launch_ms": round(kernel_ms[len(kernel_ms) // 2], 5),
                      "algorithmic_bytes_per_launch": step_bytes // launches},
     }
+    if "alu_ops" in W:  # integer hashing: priced against the chip's 32-bit vector ALU rate
+        tops = W["alu_ops"] / (avg_kernel_ms * 1e-3) / 1e12
+        out["roofline"] = {"bound": "alu", "achieved": round(tops, 4), "peak": ALU_PEAK_TOPS,
+                           "unit": "TOP/s", "frac": round(tops / ALU_PEAK_TOPS, 5),
+                           "traffic": None, "kernel": W["kernel"],
+                           "avg_launch_ms": round(avg_kernel_ms, 5),
+                           "median_launch_ms": round(kernel_ms[len(kernel_ms) // 2], 5),
+                           "algorithmic_int_ops_per_call": int(W["alu_ops"])}
+        out["tokens_per_s"] = round(W["token_layers"] * args.steps / (total_ms * 1e-3), 1)
     if launches > 1:
         out["roofline"]["launches_per_step"] = launches
     if "plain_step" in W and not args.no_plain_attention:

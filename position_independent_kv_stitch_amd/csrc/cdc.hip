@@ -18,19 +18,23 @@
 //
 // GPU decomposition (integer work on a few bytes per token: no MFMA, no
 // HBM pressure; the cost is ALU work and its balance over lanes):
-//   1. cdc_flag_kernel: a workgroup takes 4096 positions, computes the Gear
+//   1. cdc_flag_kernel: a workgroup takes 1024 positions, computes the Gear
 //      values of those positions and of the 64 before them into LDS, and
 //      every lane rolls the hash over 16 consecutive positions (64 steps to
 //      enter the window, then one shift-add per position).  Boundaries
 //      become a bit mask and a count per workgroup.
 //   2. scan_top_kernel: exclusive scan of the per-workgroup counts.
 //   3. cdc_ends_kernel: every boundary writes its chunk's end position.
-//   4. cdc_chunk_kernel: one lane per chunk hashes it, looks it up and counts
-//      the segments it becomes (1, or its number of windows).
+//   4. cdc_chunk_kernel: one lane per chunk (four for xxHash64, one per
+//      accumulator) hashes it, looks it up and counts the segments it
+//      becomes (1, or its number of windows).
 //   5. scan of the segment counts (reduce, top, apply) gives every chunk's
-//      first output slot and the total, which is written to *n_out.
-//   6. cdc_emit_kernel: one lane per output segment finds its chunk by
-//      binary search and writes the record, hashing and looking up a window.
+//      first output slot and the total, which is written to *n_out; the
+//      apply step also marks the chunk of every output slot.
+//   6. cdc_emit_kernel: one lane per output segment writes its record,
+//      hashing and looking up a window.
+// Every lane's hash is a serial chain, so the longest chunk sets the time
+// of step 4: loads are issued a block (or stripe) ahead of the arithmetic.
 // The stream length and every count stay on the device: no call waits for
 // the GPU, and later kernels run grid-stride loops bounded by counts they
 // read from device memory.
@@ -80,7 +84,9 @@ constexpr int kThreads = 256;                  // workgroup of the block kernels
 constexpr int kPerThread = 16;                 // positions (or items) per lane
 constexpr int kBlockItems = kThreads * kPerThread;  // 4096
 constexpr int kWindow = 64;                    // Gear window
-constexpr int kWordsPerBlock = kBlockItems / 64;
+constexpr int kFlagThreads = 64;              // boundary kernels: one wave per workgroup
+constexpr int kFlagItems = kFlagThreads * kPerThread;  // 1024 positions per workgroup
+constexpr int kFlagWords = kFlagItems / 64;
 constexpr int kLaneThreads = 64;               // workgroup of the lane-per-item kernels
 
 // ------------------------------------------------------------- xxHash64
@@ -103,55 +109,33 @@ __device__ __forceinline__ uint64_t xx_avalanche(uint64_t h) {
     return h ^ (h >> 32);
 }
 
+// An empty asm that claims to change x: the compiler cannot see through it,
+// so a value loaded for the next block stays a load issued in this one
+// (without it, the load is re-formed at its use, and the lane stalls on it).
+__device__ __forceinline__ void opaque(uint32_t &x) { asm volatile("" : "+v"(x)); }
+
 // Two consecutive tokens as one little-endian 64-bit word.
 __device__ __forceinline__ uint64_t tok_pair(const int32_t *t) {
     return static_cast<uint64_t>(static_cast<uint32_t>(t[0])) |
            (static_cast<uint64_t>(static_cast<uint32_t>(t[1])) << 32);
 }
 
-// xxHash64 of the 4 n bytes of tokens t[0, n).  The input is a whole number
-// of 4-byte words, so the specification's single-byte tail never occurs.
-// Stripes are read four at a time (128 bytes), the next group while the
-// current one is mixed.
-__device__ uint64_t xxh64_tokens(const int32_t *t, int64_t n, uint64_t seed) {
-    int64_t i = 0;
+// Seed of accumulator q (0..3) of xxHash64's 32-byte stripe phase.
+__device__ __forceinline__ uint64_t xx_acc_seed(uint64_t seed, int q) {
+    return q == 0 ? seed + kP1 + kP2 : q == 1 ? seed + kP2 : q == 2 ? seed : seed - kP1;
+}
+
+// The phase after the stripes: merge the accumulators (when there were
+// stripes), add the length, mix the remaining 8- and 4-byte words of
+// t[i, n) and avalanche.  The input is a whole number of 4-byte words, so
+// the specification's single-byte tail never occurs.
+__device__ uint64_t xx_finish(const int32_t *t, int64_t i, int64_t n, uint64_t seed,
+                              const uint64_t a[4]) {
     uint64_t h;
-    if (n >= 8) {  // 32-byte stripes into four accumulators
-        uint64_t a1 = seed + kP1 + kP2, a2 = seed + kP2, a3 = seed, a4 = seed - kP1;
-        const int64_t stripes = n / 8;
-        uint32_t nxt[32];
+    if (n >= 8) {
+        h = rotl64(a[0], 1) + rotl64(a[1], 7) + rotl64(a[2], 12) + rotl64(a[3], 18);
 #pragma unroll
-        for (int j = 0; j < 32; ++j) nxt[j] = j < 8 * stripes ? static_cast<uint32_t>(t[j]) : 0u;
-        for (int64_t g = 0; g < stripes; g += 4) {
-            uint32_t cur[32];
-#pragma unroll
-            for (int j = 0; j < 32; ++j) cur[j] = nxt[j];
-            const int64_t q1 = 8 * (g + 4);
-            if (q1 + 32 <= 8 * stripes) {
-#pragma unroll
-                for (int j = 0; j < 32; ++j) nxt[j] = static_cast<uint32_t>(t[q1 + j]);
-            } else {
-#pragma unroll
-                for (int j = 0; j < 32; ++j)
-                    nxt[j] = q1 + j < 8 * stripes ? static_cast<uint32_t>(t[q1 + j]) : 0u;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if (g + k < stripes) {
-                    const uint32_t *c = cur + 8 * k;
-                    a1 = xx_round(a1, c[0] | (static_cast<uint64_t>(c[1]) << 32));
-                    a2 = xx_round(a2, c[2] | (static_cast<uint64_t>(c[3]) << 32));
-                    a3 = xx_round(a3, c[4] | (static_cast<uint64_t>(c[5]) << 32));
-                    a4 = xx_round(a4, c[6] | (static_cast<uint64_t>(c[7]) << 32));
-                }
-            }
-        }
-        i = 8 * stripes;
-        h = rotl64(a1, 1) + rotl64(a2, 7) + rotl64(a3, 12) + rotl64(a4, 18);
-        h = (h ^ xx_round(0, a1)) * kP1 + kP4;
-        h = (h ^ xx_round(0, a2)) * kP1 + kP4;
-        h = (h ^ xx_round(0, a3)) * kP1 + kP4;
-        h = (h ^ xx_round(0, a4)) * kP1 + kP4;
+        for (int q = 0; q < 4; ++q) h = (h ^ xx_round(0, a[q])) * kP1 + kP4;
     } else {
         h = seed + kP5;
     }
@@ -159,6 +143,96 @@ __device__ uint64_t xxh64_tokens(const int32_t *t, int64_t n, uint64_t seed) {
     for (; i + 2 <= n; i += 2) h = rotl64(h ^ xx_round(0, tok_pair(t + i)), 27) * kP1 + kP4;
     if (i < n) h = rotl64(h ^ (static_cast<uint64_t>(static_cast<uint32_t>(t[i])) * kP1), 23) * kP2 + kP3;
     return xx_avalanche(h);
+}
+
+// xxHash64 of the 4 n bytes of tokens t[0, n), one lane.  Stripes are taken
+// four at a time; the next group is loaded (addresses clamped to the last
+// stripe, so every load is in bounds) before the current group is mixed.
+__device__ uint64_t xxh64_tokens(const int32_t *t, int64_t n, uint64_t seed) {
+    constexpr int kG = 4;
+    const int64_t stripes = n / 8;
+    uint64_t a[4] = {xx_acc_seed(seed, 0), xx_acc_seed(seed, 1), xx_acc_seed(seed, 2),
+                     xx_acc_seed(seed, 3)};
+    if (stripes > 0) {
+        uint32_t cur[8 * kG];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) {
+            const int32_t *p = t + 8 * min(static_cast<int64_t>(k), stripes - 1);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) cur[8 * k + j] = static_cast<uint32_t>(p[j]);
+        }
+        for (int64_t g = 0; g < stripes; g += kG) {
+            uint32_t nxt[8 * kG];
+#pragma unroll
+            for (int k = 0; k < kG; ++k) {
+                const int32_t *p = t + 8 * min(g + kG + k, stripes - 1);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) nxt[8 * k + j] = static_cast<uint32_t>(p[j]);
+            }
+            asm volatile("" : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]) : : "memory");
+#pragma unroll
+            for (int k = 0; k < kG; ++k) {
+                const bool live = g + k < stripes;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint64_t r = xx_round(a[q], cur[8 * k + 2 * q] |
+                                       (static_cast<uint64_t>(cur[8 * k + 2 * q + 1]) << 32));
+                    a[q] = live ? r : a[q];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 8 * kG; ++j) {
+                opaque(nxt[j]);
+                cur[j] = nxt[j];
+            }
+        }
+    }
+    return xx_finish(t, 8 * stripes, n, seed, a);
+}
+
+// xxHash64 of t[0, n) by a group of four consecutive lanes (q = lane % 4):
+// lane q runs accumulator q over the 8-byte word q of every stripe, eight
+// stripes per load group, then the group's accumulators meet in lane q = 0,
+// which alone returns the hash.  All four lanes must call it together.
+__device__ uint64_t xxh64_tokens_x4(const int32_t *t, int64_t n, uint64_t seed, int q) {
+    constexpr int kG = 8;
+    const int64_t stripes = n / 8;
+    uint64_t acc = xx_acc_seed(seed, q);
+    const int32_t *base = t + 2 * q;
+    if (stripes > 0) {
+        uint32_t cur[2 * kG];
+#pragma unroll
+        for (int k = 0; k < kG; ++k) {
+            const int32_t *p = base + 8 * min(static_cast<int64_t>(k), stripes - 1);
+            cur[2 * k] = static_cast<uint32_t>(p[0]);
+            cur[2 * k + 1] = static_cast<uint32_t>(p[1]);
+        }
+        for (int64_t g = 0; g < stripes; g += kG) {
+            uint32_t nxt[2 * kG];
+#pragma unroll
+            for (int k = 0; k < kG; ++k) {
+                const int32_t *p = base + 8 * min(g + kG + k, stripes - 1);
+                nxt[2 * k] = static_cast<uint32_t>(p[0]);
+                nxt[2 * k + 1] = static_cast<uint32_t>(p[1]);
+            }
+            asm volatile("" : "+v"(acc) : : "memory");
+#pragma unroll
+            for (int k = 0; k < kG; ++k) {
+                const uint64_t r = xx_round(acc, cur[2 * k] | (static_cast<uint64_t>(cur[2 * k + 1]) << 32));
+                acc = g + k < stripes ? r : acc;
+            }
+#pragma unroll
+            for (int j = 0; j < 2 * kG; ++j) {
+                opaque(nxt[j]);
+                cur[j] = nxt[j];
+            }
+        }
+    }
+    const int lead = (threadIdx.x & 63) & ~3;
+    uint64_t a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a[k] = __shfl(acc, lead + k, 64);
+    return q == 0 ? xx_finish(t, 8 * stripes, n, seed, a) : 0;
 }
 
 // Gear value: xxHash64 of one token's 4 bytes (the short-input form).
@@ -215,6 +289,13 @@ __device__ __forceinline__ uint32_t rotr32(uint32_t x, int r) { return (x >> r) 
 
 __device__ __forceinline__ uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
 
+// x ^ y ^ z in one instruction (gfx950's three-input bit operation; 0x96 is
+// the truth table of a three-way exclusive or).
+__device__ __forceinline__ uint32_t xor3(uint32_t x, uint32_t y, uint32_t z) {
+    return __builtin_amdgcn_bitop3_b32(x, y, z, 0x96);
+}
+
+
 // One compression of a 16-word block; w is consumed as the schedule's ring.
 __device__ __forceinline__ void sha_compress(uint32_t st[8], uint32_t w[16]) {
     uint32_t a = st[0], b = st[1], c = st[2], d = st[3], e = st[4], f = st[5], g = st[6],
@@ -223,14 +304,17 @@ __device__ __forceinline__ void sha_compress(uint32_t st[8], uint32_t w[16]) {
     for (int t = 0; t < 64; ++t) {
         if (t >= 16) {
             const uint32_t x = w[(t + 1) & 15], y = w[(t + 14) & 15];
-            const uint32_t s0 = rotr32(x, 7) ^ rotr32(x, 18) ^ (x >> 3);
-            const uint32_t s1 = rotr32(y, 17) ^ rotr32(y, 19) ^ (y >> 10);
+            const uint32_t s0 = xor3(rotr32(x, 7), rotr32(x, 18), x >> 3);
+            const uint32_t s1 = xor3(rotr32(y, 17), rotr32(y, 19), y >> 10);
             w[t & 15] += s0 + w[(t + 9) & 15] + s1;
         }
-        const uint32_t t1 = h + (rotr32(e, 6) ^ rotr32(e, 11) ^ rotr32(e, 25)) +
-                            ((e & f) ^ (~e & g)) + kSha.k[t] + w[t & 15];
-        const uint32_t t2 = (rotr32(a, 2) ^ rotr32(a, 13) ^ rotr32(a, 22)) +
-                            ((a & b) ^ (a & c) ^ (b & c));
+        // Ch picks f where e is set, else g; Maj picks c where a and b differ,
+        // else b: both written as bit selects (one v_bfi each).
+        const uint32_t ab = a ^ b;
+        const uint32_t t1 = h + xor3(rotr32(e, 6), rotr32(e, 11), rotr32(e, 25)) +
+                            ((e & f) | (~e & g)) + kSha.k[t] + w[t & 15];
+        const uint32_t t2 = xor3(rotr32(a, 2), rotr32(a, 13), rotr32(a, 22)) +
+                            ((ab & c) | (~ab & b));
         h = g;
         g = f;
         f = e;
@@ -253,35 +337,51 @@ __device__ __forceinline__ void sha_compress(uint32_t st[8], uint32_t w[16]) {
 // SHA-256 of the 4 n bytes of tokens t[0, n).  The message is word-aligned,
 // so message word q is the byte swap of token q, the 0x80 padding byte
 // starts word n, and the bit length fills words 14 and 15 of the last block.
-// The next block's words are loaded before the current block is compressed,
-// so a lane's loads overlap its rounds instead of stalling every block.
+// Over the full 16-word blocks the next block is loaded (unconditionally:
+// the last iteration reloads its own block) before the current one is
+// compressed, so a lane's loads overlap its rounds.  The one or two padded
+// blocks follow.
 __device__ void sha256_tokens(const int32_t *t, int64_t n, uint32_t st[8]) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) st[j] = kSha.h0[j];
-    const int64_t blocks = (n + 3 + 15) / 16;
-    const uint64_t bits = static_cast<uint64_t>(n) * 32u;
-    uint32_t nxt[16];
+    const int64_t full = n / 16;
+    uint32_t cur[16];
+    if (full > 0) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) nxt[j] = j < n ? static_cast<uint32_t>(t[j]) : 0u;
-    for (int64_t b = 0; b < blocks; ++b) {
-        const int64_t q0 = 16 * b;
+        for (int j = 0; j < 16; ++j) cur[j] = static_cast<uint32_t>(t[j]);
+    }
+    for (int64_t b = 0; b < full; ++b) {
+        const int32_t *p = t + 16 * (b + 1 < full ? b + 1 : b);
+        uint32_t nxt[16], w[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) nxt[j] = static_cast<uint32_t>(p[j]);
+        // The loads stay above this point, and the rounds below it: the
+        // state passes through the (empty) asm.
+        asm volatile("" : "+v"(st[0]), "+v"(st[1]), "+v"(st[2]), "+v"(st[3]), "+v"(st[4]),
+                     "+v"(st[5]), "+v"(st[6]), "+v"(st[7]) : : "memory");
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j] = bswap32(cur[j]);
+        sha_compress(st, w);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            opaque(nxt[j]);
+            cur[j] = nxt[j];
+        }
+    }
+    const int r = static_cast<int>(n - 16 * full);  // words left: 0..15
+    const int32_t *p = t + 16 * full;
+    const uint64_t bits = static_cast<uint64_t>(n) * 32u;
+    const int tail_blocks = r <= 13 ? 1 : 2;
+    for (int tb = 0; tb < tail_blocks; ++tb) {
         uint32_t w[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-            const int64_t q = q0 + j;
-            w[j] = q < n ? bswap32(nxt[j]) : (q == n ? 0x80000000u : 0u);
+            const int q = 16 * tb + j;
+            w[j] = q < r ? bswap32(static_cast<uint32_t>(p[q])) : (q == r ? 0x80000000u : 0u);
         }
-        if (b == blocks - 1) {
+        if (tb == tail_blocks - 1) {
             w[14] = static_cast<uint32_t>(bits >> 32);
             w[15] = static_cast<uint32_t>(bits);
-        }
-        const int64_t q1 = q0 + 16;
-        if (q1 + 16 <= n) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) nxt[j] = static_cast<uint32_t>(t[q1 + j]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) nxt[j] = q1 + j < n ? static_cast<uint32_t>(t[q1 + j]) : 0u;
         }
         sha_compress(st, w);
     }
@@ -357,21 +457,19 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t *lds, int32_t *total)
 // runs of consecutive lanes in different banks.
 __device__ __forceinline__ int gpad(int j) { return j + (j >> 4); }
 
-__global__ __launch_bounds__(kThreads) void cdc_flag_kernel(const int32_t *__restrict__ tok,
-                                                            int64_t n, uint64_t gear_seed,
-                                                            uint64_t threshold,
-                                                            uint64_t *__restrict__ flags,
-                                                            int32_t *__restrict__ bcnt) {
-    constexpr int kSlots = kBlockItems + kWindow;
+__global__ __launch_bounds__(kFlagThreads) void cdc_flag_kernel(const int32_t *__restrict__ tok,
+                                                                int64_t n, uint64_t gear_seed,
+                                                                uint64_t threshold,
+                                                                uint64_t *__restrict__ flags,
+                                                                int32_t *__restrict__ bcnt) {
+    constexpr int kSlots = kFlagItems + kWindow;
     __shared__ uint64_t g[kSlots + kSlots / 16];
-    __shared__ uint32_t bits[kThreads];
-    __shared__ int32_t cnt;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kBlockItems;
-    for (int j = threadIdx.x; j < kSlots; j += kThreads) {
+    __shared__ uint32_t bits[kFlagThreads];
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kFlagItems;
+    for (int j = threadIdx.x; j < kSlots; j += kFlagThreads) {
         const int64_t pos = base - kWindow + j;
         g[gpad(j)] = (pos >= 0 && pos < n) ? gear_value(tok[pos], gear_seed) : 0;
     }
-    if (threadIdx.x == 0) cnt = 0;
     __syncthreads();
     const int first = threadIdx.x * kPerThread;
     uint64_t h = 0;  // after this loop: h at the position before the lane's first
@@ -384,15 +482,17 @@ __global__ __launch_bounds__(kThreads) void cdc_flag_kernel(const int32_t *__res
         if (pos < n && (h < threshold || pos == n - 1)) b |= 1u << j;
     }
     bits[threadIdx.x] = b;
-    atomicAdd(&cnt, __popc(b));
+    int32_t c = __popc(b);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) c += __shfl_xor(c, d, 64);
     __syncthreads();
-    if (threadIdx.x < kWordsPerBlock) {
+    if (threadIdx.x < kFlagWords) {
         const int t = 4 * threadIdx.x;
-        flags[static_cast<int64_t>(blockIdx.x) * kWordsPerBlock + threadIdx.x] =
+        flags[static_cast<int64_t>(blockIdx.x) * kFlagWords + threadIdx.x] =
             static_cast<uint64_t>(bits[t]) | (static_cast<uint64_t>(bits[t + 1]) << 16) |
             (static_cast<uint64_t>(bits[t + 2]) << 32) | (static_cast<uint64_t>(bits[t + 3]) << 48);
     }
-    if (threadIdx.x == 0) bcnt[blockIdx.x] = cnt;
+    if (threadIdx.x == 0) bcnt[blockIdx.x] = c;
 }
 
 // Exclusive scan, in place, of v[0, len) where len = n_host, or, when
@@ -430,17 +530,23 @@ __global__ __launch_bounds__(1024) void scan_top_kernel(int32_t *__restrict__ v,
     }
 }
 
-// End position (exclusive) of every chunk, in stream order.
-__global__ __launch_bounds__(kThreads) void cdc_ends_kernel(const uint64_t *__restrict__ flags,
-                                                            const int32_t *__restrict__ boff,
-                                                            int32_t *__restrict__ ends) {
-    __shared__ int32_t lds[kThreads / 64 + 1];
+// End position (exclusive) of every chunk, in stream order.  One wave per
+// workgroup, the boundary kernel's partition.
+__global__ __launch_bounds__(kFlagThreads) void cdc_ends_kernel(const uint64_t *__restrict__ flags,
+                                                               const int32_t *__restrict__ boff,
+                                                               int32_t *__restrict__ ends) {
     const uint64_t word =
-        flags[static_cast<int64_t>(blockIdx.x) * kWordsPerBlock + (threadIdx.x >> 2)];
+        flags[static_cast<int64_t>(blockIdx.x) * kFlagWords + (threadIdx.x >> 2)];
     uint32_t b = static_cast<uint32_t>(word >> (16 * (threadIdx.x & 3))) & 0xFFFFu;
-    int32_t total;
-    int32_t slot = boff[blockIdx.x] + block_exclusive_scan(__popc(b), lds, &total);
-    const int64_t first = static_cast<int64_t>(blockIdx.x) * kBlockItems + threadIdx.x * kPerThread;
+    const int32_t cnt = __popc(b);
+    int32_t x = cnt;  // inclusive scan over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d, 64);
+        if (static_cast<int>(threadIdx.x) >= d) x += y;
+    }
+    int32_t slot = boff[blockIdx.x] + x - cnt;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * kFlagItems + threadIdx.x * kPerThread;
     while (b) {
         const int j = __ffs(b) - 1;
         ends[slot++] = static_cast<int32_t>(first + j + 1);
@@ -455,6 +561,7 @@ struct MatchArgs {
     const int32_t *counts;  // [0] chunks nc, [1] segments m
     uint64_t *cfp;          // [keep][4] chunk fingerprints
     int32_t *cid;           // [keep] chunk registry ids
+    int32_t *owner;         // [keep] chunk of every output slot
     const RegSlot *tab;
     uint32_t mask;
     int32_t kind;
@@ -470,14 +577,24 @@ __device__ __forceinline__ int64_t chunk_start(const int32_t *ends, int64_t c) {
     return c ? ends[c - 1] : 0;
 }
 
-// One lane per chunk: fingerprint, lookup, number of output segments.
+// G lanes per chunk (G = 4: xxHash64's four accumulators on four lanes; G =
+// 1: SHA-256, which is serial): fingerprint, lookup, number of output
+// segments.  The lanes of a group share their chunk index, so a group is
+// active or idle as a whole.
+template <int G>
 __global__ __launch_bounds__(kLaneThreads) void cdc_chunk_kernel(MatchArgs a) {
     const int64_t nc = min(static_cast<int64_t>(a.counts[0]), a.n);
-    for (int64_t c = static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x; c < nc;
-         c += static_cast<int64_t>(gridDim.x) * kLaneThreads) {
+    const int q = threadIdx.x % G;
+    for (int64_t c = (static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x) / G; c < nc;
+         c += static_cast<int64_t>(gridDim.x) * (kLaneThreads / G)) {
         const int64_t s = chunk_start(a.ends, c), len = a.ends[c] - s;
-        uint64_t fp[4];
-        fingerprint(a.tok + s, len, a.kind, a.fp_seed, fp);
+        uint64_t fp[4] = {0, 0, 0, 0};
+        if constexpr (G == 4) {
+            fp[0] = xxh64_tokens_x4(a.tok + s, len, a.fp_seed, q);
+        } else {
+            fingerprint(a.tok + s, len, a.kind, a.fp_seed, fp);
+        }
+        if (q != 0) continue;
         const int32_t id = reg_lookup(a.tab, a.mask, fp, static_cast<int32_t>(len));
         a.seg[c] = (id >= 0 || a.window <= 0) ? 1
                                               : static_cast<int32_t>((len + a.window - 1) / a.window);
@@ -509,9 +626,13 @@ __global__ __launch_bounds__(kThreads) void scan_reduce_kernel(const int32_t *__
 }
 
 // In-place exclusive scan of v[0, *len_dev), block b offset by boff[b].
+// With `owner`, item i also marks the slots [v'[i], v'[i] + v[i]) below
+// `keep` as its own (v' the scanned value): the chunk of every output slot.
 __global__ __launch_bounds__(kThreads) void scan_apply_kernel(int32_t *__restrict__ v,
                                                               const int32_t *__restrict__ len_dev,
-                                                              const int32_t *__restrict__ boff) {
+                                                              const int32_t *__restrict__ boff,
+                                                              int32_t *__restrict__ owner,
+                                                              int64_t keep) {
     __shared__ int32_t lds[kThreads / 64 + 1];
     const int64_t len = *len_dev, base = static_cast<int64_t>(blockIdx.x) * kBlockItems;
     if (base >= len) return;  // uniform over the workgroup
@@ -527,24 +648,24 @@ __global__ __launch_bounds__(kThreads) void scan_apply_kernel(int32_t *__restric
     int32_t run = boff[blockIdx.x] + block_exclusive_scan(s, lds, &total);
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
-        if (first + j < len) v[first + j] = run;
+        if (first + j < len) {
+            v[first + j] = run;
+            if (owner)
+                for (int64_t k = run; k < run + x[j] && k < keep; ++k)
+                    owner[k] = static_cast<int32_t>(first + j);
+        }
         run += x[j];
     }
 }
 
-// One lane per output record (the first max_out segments).
+// One lane per output record (the first max_out segments); the owner map
+// names each slot's chunk.
 __global__ __launch_bounds__(kLaneThreads) void cdc_emit_kernel(MatchArgs a) {
-    const int64_t nc = min(static_cast<int64_t>(a.counts[0]), a.n);
     const int64_t m = min(static_cast<int64_t>(a.counts[1]), a.n);
     const int64_t lim = m < a.max_out ? m : a.max_out;
     for (int64_t s = static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x; s < lim;
          s += static_cast<int64_t>(gridDim.x) * kLaneThreads) {
-        int64_t lo = 0, hi = nc;  // last chunk whose first slot is <= s
-        while (hi - lo > 1) {
-            const int64_t mid = (lo + hi) >> 1;
-            if (a.seg[mid] <= s) lo = mid; else hi = mid;
-        }
-        const int64_t c = lo, k = s - a.seg[c];
+        const int64_t c = a.owner[s], k = s - a.seg[c];
         const int64_t cs = chunk_start(a.ends, c), ce = a.ends[c];
         pic_match_t r;
         uint64_t fp[4];
@@ -760,17 +881,19 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
 
     // Temporary device memory (stream-ordered).
     const int64_t n = n_tokens;
-    const int64_t nb = (n + kBlockItems - 1) / kBlockItems;
+    const int64_t nb = (n + kBlockItems - 1) / kBlockItems;  // scan blocks
+    const int64_t nbf = (n + kFlagItems - 1) / kFlagItems;   // boundary workgroups
     const int64_t keep = max_out < n ? max_out : n;
     size_t off = 0;
-    const size_t o_flags = off; off = align256(off + sizeof(uint64_t) * nb * kWordsPerBlock);
-    const size_t o_bcnt = off;  off = align256(off + sizeof(int32_t) * (nb + 1));
+    const size_t o_flags = off; off = align256(off + sizeof(uint64_t) * nbf * kFlagWords);
+    const size_t o_bcnt = off;  off = align256(off + sizeof(int32_t) * (nbf + 1));
     const size_t o_ends = off;  off = align256(off + sizeof(int32_t) * n);
     const size_t o_seg = off;   off = align256(off + sizeof(int32_t) * n);
     const size_t o_ssum = off;  off = align256(off + sizeof(int32_t) * (nb + 1));
     const size_t o_cnt = off;   off = align256(off + sizeof(int32_t) * 2);
     const size_t o_cfp = off;   off = align256(off + sizeof(uint64_t) * 4 * keep);
     const size_t o_cid = off;   off = align256(off + sizeof(int32_t) * keep);
+    const size_t o_own = off;   off = align256(off + sizeof(int32_t) * keep);
     void *mem = nullptr;
     e = hipMallocAsync(&mem, off, stream);
     if (e != hipSuccess) return hip_fail(e, "hipMallocAsync (pic_match temporaries)");
@@ -787,6 +910,7 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
     a.counts = counts;
     a.cfp = reinterpret_cast<uint64_t *>(base + o_cfp);
     a.cid = reinterpret_cast<int32_t *>(base + o_cid);
+    a.owner = reinterpret_cast<int32_t *>(base + o_own);
     a.tab = tab;
     a.mask = mask;
     a.kind = cfg->fingerprint;
@@ -803,14 +927,18 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
         return static_cast<unsigned>(g < 1 ? 1 : (g > 16384 ? 16384 : g));
     };
     const unsigned gb = static_cast<unsigned>(nb);
-    cdc_flag_kernel<<<gb, kThreads, 0, stream>>>(tokens, n, cfg->gear_seed, cfg->threshold, flags,
-                                                bcnt);
-    scan_top_kernel<<<1, 1024, 0, stream>>>(bcnt, nb, nullptr, &counts[0], nullptr);
-    cdc_ends_kernel<<<gb, kThreads, 0, stream>>>(flags, bcnt, const_cast<int32_t *>(a.ends));
-    cdc_chunk_kernel<<<lane_grid(n), kLaneThreads, 0, stream>>>(a);
+    const unsigned gf = static_cast<unsigned>(nbf);
+    cdc_flag_kernel<<<gf, kFlagThreads, 0, stream>>>(tokens, n, cfg->gear_seed, cfg->threshold,
+                                                    flags, bcnt);
+    scan_top_kernel<<<1, 1024, 0, stream>>>(bcnt, nbf, nullptr, &counts[0], nullptr);
+    cdc_ends_kernel<<<gf, kFlagThreads, 0, stream>>>(flags, bcnt, const_cast<int32_t *>(a.ends));
+    if (cfg->fingerprint == PIC_FP_XXH64)
+        cdc_chunk_kernel<4><<<lane_grid(4 * n), kLaneThreads, 0, stream>>>(a);
+    else
+        cdc_chunk_kernel<1><<<lane_grid(n), kLaneThreads, 0, stream>>>(a);
     scan_reduce_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum);
     scan_top_kernel<<<1, 1024, 0, stream>>>(ssum, 0, &counts[0], &counts[1], n_out);
-    scan_apply_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum);
+    scan_apply_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum, a.owner, keep);
     if (keep > 0) cdc_emit_kernel<<<lane_grid(keep), kLaneThreads, 0, stream>>>(a);
     e = hipGetLastError();
     const hipError_t e2 = hipFreeAsync(mem, stream);
