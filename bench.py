@@ -32,7 +32,7 @@ PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # 32-bit integer vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 KERNEL_SOURCES = [os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc", f)
-                  for f in ("stitch.hip", "plan.cpp", "pic_internal.hpp")]
+                  for f in ("stitch.hip", "rotate.hpp", "plan.cpp", "pic_internal.hpp")]
 COUNTERS = os.path.join(ROOT, "profiles", "stitch_kernel_llama3-8b-paged_counters.md")
 
 
@@ -82,6 +82,13 @@ WORKLOADS = {
                      "pages; one pic_attend per layer, 32 layers per step",
     "attend-decode-single": "the attend-decode workload with one request (16512 positions): "
                             "a latency-bound decode step",
+    "attend-mla-decode": "MLA decode attention over stitched contexts, chunk rotary keys turned "
+                         "on load (pic_attend_latent): DeepSeek-V3 rows (576 = 512 latent + "
+                         "64 rotary, bf16), 128 query heads, 16 requests x 16512 positions "
+                         "(8 own chunks x 2048 behind a 128-token prefix, recompute_k 32), "
+                         "64-token pages; one call per layer, 61 layers per step",
+    "attend-mla-decode-16h": "the attend-mla-decode workload with 16 query heads (DeepSeek-V2-"
+                             "Lite's head count, or one GPU's share of 128 heads over 8)",
     "cdc-rag": "content-defined chunking + xxHash64 fingerprints + registry lookup + 128-token "
                "fallback windows (pic_match) over the batched-RAG prompt stream: 64 requests, "
                "~1.44 M tokens, 10% of placed documents edited, registry of the 256 pool "
@@ -108,6 +115,8 @@ def setup_workload(name, torch, pic):
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
     if name.startswith("attend-decode"):
         return setup_attend(name, torch, pic)
+    if name.startswith("attend-mla-decode"):
+        return setup_attend_mla(name, torch, pic)
     if name.startswith("cdc-rag"):
         return setup_cdc(name, torch, pic)
     wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
@@ -171,6 +180,38 @@ def setup_attend(name, torch, pic):
             "token_layers": info["context_tokens"] * L, "launches": L,
             "kernel": "attend_block_kernel<bf16, half> + attend_combine_kernel (one pic_attend)",
             "plan": plan, "plans": [plain], "info": info, "config": cfg}
+
+
+def setup_attend_mla(name, torch, pic):
+    """MLA decode attention: one step is a pic_attend_latent per layer."""
+    from pic_workloads import mla_decode_batch, normal_values, pool_values
+    wl = mla_decode_batch()
+    heads = 16 if name.endswith("16h") else 128
+    pk, _ = pool_values(wl, seed=0, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, 2, "cuda:0")
+    R, L = len(wl.requests), wl.n_layers
+    q = normal_values((L, R, heads, wl.row_dim), wl.dtype, 4, "cuda:0")
+    out = torch.empty((L, R, heads, 512), dtype=torch.float32, device="cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    info = plan.info
+    scale = 192 ** -0.5
+
+    def step():
+        for layer in range(L):
+            pic.attend_latent(plan, pk, ck, q[layer], layer=layer, out=out[layer], scale=scale,
+                              sink_tokens=4, sink_bias=-15.0)
+
+    row = wl.row_dim * 2
+    flops = info["context_tokens"] * heads * 2 * (wl.row_dim + 512) * L  # q.k and w.v per head
+    cfg = {"workload": WORKLOADS[name], "storage": wl.dtype, "layers": L, "q_heads": heads,
+           "row_dim": wl.row_dim, "requests": R, "context_tokens": info["context_tokens"],
+           "chunk_positions": info["tokens_written"], "page_size": wl.page_size,
+           "softmax_scale": "1/sqrt(192)", "sink_tokens": 4, "sink_bias": -15.0,
+           "parallelism": "single-gpu"}
+    return {"wl": wl, "step": step, "bytes": info["context_tokens"] * row * L,
+            "token_layers": info["context_tokens"] * L, "launches": L, "flops": flops,
+            "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)",
+            "plan": plan, "info": info, "config": cfg}
 
 
 def setup_cdc(name, torch, pic):
@@ -386,6 +427,11 @@ def main():
         out["tokens_per_s"] = round(W["token_layers"] * args.steps / (total_ms * 1e-3), 1)
     if launches > 1:
         out["roofline"]["launches_per_step"] = launches
+    if "flops" in W:  # matrix-core work beside the bytes: bf16 dense peak 2.5 PFLOP/s
+        tf = W["flops"] / launches / (avg_kernel_ms * 1e-3) / 1e12
+        out["roofline"]["mfma"] = {"achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                                   "frac": round(tf / 2500.0, 4),
+                                   "algorithmic_flops_per_launch": W["flops"] // launches}
     if "plain_step" in W and not args.no_plain_attention:
         for _ in range(3):
             W["plain_step"]()

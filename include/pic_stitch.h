@@ -318,6 +318,49 @@ typedef struct pic_attend_args {
 pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
                       const pic_attend_args *args, void *stream);
 
+/*
+ * Decode attention over MLA latent rows (Irminsul, Technical Summary
+ * sections 2.1, 2.2 and 4): the plan's rows are 576-wide bf16 latent rows
+ * (pic_kv_shape num_heads 1, row_dim 576, rope_offset 512, rope_dim 64,
+ * has_v 0).  In the absorbed form of MLA decode every query head j has a
+ * 576-wide query row (content part already in the latent space, rotary part
+ * post-RoPE); for every request r and query head j:
+ *   out[r][j] = sum_p w_p row_p[0, 512) / sum_p w_p,
+ *   w_p = exp(scale * q_j . row_p + b_p)
+ * over positions p in [0, context_len).  row_p is the row the stitch of
+ * this plan would leave at position p: for positions an entry writes, the
+ * chunk's pool row with its rotary key turned by the entry's delta (fp64,
+ * rounded to bf16 as pic_stitch stores it) while it is loaded; for every
+ * other position the request's own cache row.  b_p is the LegoLink damping
+ * of pic_attend.  Products on the matrix cores with fp32 accumulation; the
+ * softmax weights enter the value product as two bf16 terms (hi + lo).
+ */
+typedef struct pic_attend_latent_args {
+    const void *q;        /* device bf16 [request][q head][576] */
+    int64_t q_request_stride, q_head_stride;
+    float *out;           /* device fp32 [request][q head][512] */
+    int64_t out_request_stride, out_head_stride;
+    int32_t num_q_heads;  /* a multiple of 16, at most 1024 */
+    int32_t layer;        /* layer of the views */
+    float scale;          /* logit scale (DeepSeek-V2/V3: 1/sqrt(192)) */
+    int32_t sink_tokens;  /* LegoLink damping: tokens per chunk start (0 = off) */
+    float sink_bias;      /* LegoLink damping: logit offset */
+    int32_t reserved;
+} pic_attend_latent_args;
+
+/*
+ * pic_attend_latent -- enqueue latent decode attention for every request of
+ * a plan at one layer (see above).  The plan must be a bf16 MLA plan of the
+ * shape above (PIC_ERR_INVALID_ARG); q rows 16-byte aligned
+ * (PIC_ERR_ALIGN); contexts and pages as for pic_attend (PIC_ERR_RANGE);
+ * in-place plans are refused (PIC_ERR_STATE).  The partial-result
+ * workspace is the plan's, shared with pic_attend (allocated or grown on
+ * first use, freed with the plan): calls on one plan that may overlap race;
+ * order them on one stream.
+ */
+pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
+                             const pic_attend_latent_args *args, void *stream);
+
 /* pic_plan_info -- sizes and algorithmic byte counts of a plan. */
 pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info);
 

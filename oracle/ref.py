@@ -336,3 +336,69 @@ def attend(wl, pool_k, pool_v, cache_k, cache_v, q, layer, scale=None, sink_toke
             w = np.exp(logits - logits.max())
             out[r, j] = (w @ v[:, h, :]) / w.sum()
     return out
+
+
+def attend_latent(wl, pool_k, cache_k, q, layer, scale=None, sink_tokens=0, sink_bias=0.0,
+                  layer_base=0, dtype=None):
+    """Decode attention over MLA latent rows, in fp64 (returns
+    [requests][q heads][rope_offset] float64).
+
+    Irminsul (Technical Summary sections 2.1, 2.2 and 4): a latent row is the
+    content latent [0, rope_offset) followed by the rotary key; in the
+    absorbed form every query head j has a full-width query row, its logit
+    at position p is scale * q_j . row_p, and the value of position p is
+    the content latent.  row_p is the row this oracle's stitch leaves at p:
+    for positions an entry writes, the chunk's row with its rotary key
+    turned by the entry's shift and rounded to the storage type (dtype
+    'f64': not rounded); for every other position the request's own cache
+    row.  Damping as in attend().  The weights are softmax over the context
+    and the output their weighted sum of content latents (the plain
+    definition of attention).
+    """
+    from types import SimpleNamespace as NS
+    li = layer - layer_base
+    D, V = wl.row_dim, wl.rope_offset
+    R, Hq = q.shape[0], q.shape[1]
+    sc = D ** -0.5 if scale is None else scale
+    dt = dtype or wl.dtype
+    out = np.zeros((R, Hq, V))
+    pk = pool_k[li:li + 1]
+    if dt == "f64":
+        pk = _to_f64(pk)
+    for r, rq in enumerate(wl.requests):
+        L = rq.context_len or max([e.dst_offset + e.length for e in rq.entries] + [0])
+        if L == 0:
+            raise ValueError(f"request {r} has an empty context")
+        pos = np.arange(L)
+        if wl.page_size:
+            pt = np.asarray(rq.page_table)
+            k = _to_f64(cache_k[li][pt[pos // wl.page_size], pos % wl.page_size])
+        else:
+            k = _to_f64(cache_k[li][r, :L])
+        cap = max(L, max([e.dst_offset + e.length for e in rq.entries] + [0]))
+        sub = NS(dtype=dt, n_layers=1, n_heads=1, row_dim=D, rope_offset=wl.rope_offset,
+                 rope_dim=wl.rope_dim, style=wl.style, theta=wl.theta, inv_freq=wl.inv_freq,
+                 has_v=False, pool_tokens=wl.pool_tokens, chunks=wl.chunks,
+                 src_page_size=getattr(wl, "src_page_size", 0),
+                 src_n_pages=getattr(wl, "src_n_pages", 0),
+                 requests=[NS(entries=rq.entries, page_table=None)], page_size=0, capacity=cap,
+                 n_phys_pages=0)
+        sk = np.zeros((1, 1, cap, 1, D), dtype=pk.dtype)
+        st = stitch(sub, pk, None, sk, None, 0, 1, dtype=dt)
+        if st != "ok":
+            raise ValueError(f"request {r}: {st}")
+        sk = _to_f64(sk)
+        bias = np.zeros(L)
+        for e in rq.entries:
+            lo, hi = e.dst_offset + e.recompute_k, min(e.dst_offset + e.length, L)
+            if lo < hi:
+                k[lo:hi] = sk[0, 0, lo:hi]
+            if e.dst_offset > 0 and sink_tokens > 0:
+                bias[e.dst_offset:min(e.dst_offset + sink_tokens, L)] = sink_bias
+        rows = k[:, 0, :]
+        qq = _to_f64(q[r])
+        for j in range(Hq):
+            logits = sc * (rows @ qq[j]) + bias
+            w = np.exp(logits - logits.max())
+            out[r, j] = (w @ rows[:, :V]) / w.sum()
+    return out

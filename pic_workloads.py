@@ -237,6 +237,30 @@ def decode_batch(seed: int = 0, n_requests: int = 16, n_layers: int = 32) -> Wor
                     requests=requests, page_size=ps, n_phys_pages=per * n_requests)
 
 
+def mla_decode_batch(seed: int = 0, n_requests: int = 16, n_layers: int = 61,
+                     page_size: int = 64) -> Workload:
+    """A decode batch over stitched MLA contexts, DeepSeek-V3 shape (576-wide
+    latent rows: 512 content + 64 rotary dims, theta 1e4): each request
+    places its own 8 chunks x 2048 tokens in a seeded random order behind a
+    128-token prefix, the first 32 tokens of every chunk left for recompute,
+    and attends its whole 16,512-position context; pages of 64 tokens from
+    one global random permutation."""
+    rng = np.random.default_rng(seed)
+    n, length, prefix, ps = 8, 2048, 128, page_size
+    chunks = [Chunk(i * length, length) for i in range(n * n_requests)]
+    per = -(-(prefix + n * length) // ps)
+    perm = rng.permutation(per * n_requests).astype(np.int32)
+    requests = []
+    for r in range(n_requests):
+        order = rng.permutation(n) + n * r
+        entries = [Entry(int(c), prefix + j * length, length, 32) for j, c in enumerate(order)]
+        requests.append(Request(entries, perm[r * per:(r + 1) * per].copy(),
+                                prefix + n * length))
+    return Workload("deepseek-v3 MLA decode batch", "bf16", n_layers, 1, 576, 512, 64, "half",
+                    10000.0, False, pool_tokens=n * length * n_requests, chunks=chunks,
+                    requests=requests, page_size=ps, n_phys_pages=per * n_requests)
+
+
 def with_paged_pool(wl: Workload, page_size: int = 16, seed: int = 0,
                     first_offsets: bool = False, spare_pages: int = 0) -> Workload:
     """The same placements with the chunks kept in a paged pool (the block

@@ -26,7 +26,8 @@ DTYPES = {"f32": 0, "bf16": 1}
 STYLES = {"half": 0, "interleaved": 1}
 
 # every entry point the header declares
-EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_attend", "pic_plan_info",
+EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_attend", "pic_attend_latent",
+           "pic_plan_info",
            "pic_plan_ranges", "pic_plan_destroy", "pic_registry_create", "pic_registry_add",
            "pic_registry_destroy", "pic_match", "pic_last_error")
 FP_KINDS = {"xxh64": 0, "sha256": 1}
@@ -65,6 +66,14 @@ class RequestC(C.Structure):
 
 
 class AttendArgs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("q_request_stride", C.c_int64),
+                ("q_head_stride", C.c_int64), ("out", C.c_void_p),
+                ("out_request_stride", C.c_int64), ("out_head_stride", C.c_int64),
+                ("num_q_heads", C.c_int32), ("layer", C.c_int32), ("scale", C.c_float),
+                ("sink_tokens", C.c_int32), ("sink_bias", C.c_float), ("reserved", C.c_int32)]
+
+
+class LatentArgs(C.Structure):
     _fields_ = [("q", C.c_void_p), ("q_request_stride", C.c_int64),
                 ("q_head_stride", C.c_int64), ("out", C.c_void_p),
                 ("out_request_stride", C.c_int64), ("out_head_stride", C.c_int64),
@@ -160,6 +169,9 @@ def _configure(lib):
                                        C.c_void_p]
     lib.pic_attend.restype = C.c_int
     lib.pic_attend.argtypes = [C.c_void_p, P(KvView), P(KvView), P(AttendArgs), C.c_void_p]
+    lib.pic_attend_latent.restype = C.c_int
+    lib.pic_attend_latent.argtypes = [C.c_void_p, P(KvView), P(KvView), P(LatentArgs),
+                                      C.c_void_p]
     lib.pic_plan_info.restype = C.c_int
     lib.pic_plan_info.argtypes = [C.c_void_p, P(PlanInfo)]
     lib.pic_plan_ranges.restype = C.c_int
@@ -463,6 +475,53 @@ def attend(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: int, out=N
     lib = plan._lib
     _check(lib.pic_attend(plan.handle, C.byref(pv), C.byref(cv), C.byref(a),
                           _stream_of(q, stream)), lib)
+    return out
+
+
+def attend_latent(plan: Plan, pool_k, cache_k, q, *, layer: int, out=None,
+                  scale: Optional[float] = None, sink_tokens: int = 0, sink_bias: float = 0.0,
+                  stream=None):
+    """Enqueue pic_attend_latent: MLA decode attention of every request of an
+    MLA plan at `layer`.  q: bf16 [requests][q heads][576] (absorbed query,
+    rotary part post-RoPE); pool_k as for stitch(); cache_k: the requests'
+    own latent rows in the plan's destination geometry.  Returns out, fp32
+    [requests][q heads][512]."""
+    torch = _torch()
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
+        raise TypeError("q must be bf16 [requests][q heads][row_dim]")
+    if q.shape[0] != plan.n_requests or q.shape[2] != plan.row_dim:
+        raise ValueError("q shape does not match the plan")
+    vdim = 512
+    oshape = (q.shape[0], q.shape[1], vdim)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != oshape or out.stride(-1) != 1:
+        raise TypeError(f"out must be fp32 {oshape}")
+    if plan.src_page_size:
+        if pool_k.dim() != 5 or pool_k.shape[1] < plan.src_n_pages:
+            raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
+        pv = _view(pool_k, None, "paged-pool")
+    else:
+        if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+            raise PicError(PIC_ERR_RANGE, "pool tensor smaller than the plan needs")
+        pv = _view(pool_k, None, "pool")
+    if plan.page_size:
+        if cache_k.shape[1] < plan.n_phys_pages or cache_k.shape[2] != plan.page_size:
+            raise ValueError("paged cache smaller than the plan's page pool")
+        cv = _view(cache_k, None, "paged")
+    else:
+        if cache_k.shape[1] < plan.n_requests or cache_k.shape[2] < plan.capacity:
+            raise ValueError("contiguous cache smaller than requests x capacity")
+        cv = _view(cache_k, None, "contig")
+    if not (0 <= layer < min(pool_k.shape[0], cache_k.shape[0])):
+        raise ValueError("layer beyond the tensors")
+    a = LatentArgs(q.data_ptr(), q.stride(0), q.stride(1), out.data_ptr(), out.stride(0),
+                   out.stride(1), q.shape[1], layer,
+                   float(plan.row_dim ** -0.5 if scale is None else scale), int(sink_tokens),
+                   float(sink_bias), 0)
+    lib = plan._lib
+    _check(lib.pic_attend_latent(plan.handle, C.byref(pv), C.byref(cv), C.byref(a),
+                                 _stream_of(q, stream)), lib)
     return out
 
 

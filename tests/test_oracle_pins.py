@@ -698,3 +698,111 @@ def test_attend_rotated_chunks_equal_direct_rope(style):
     naive_k[0, 0, 3:10] = cached[0, 5:12]
     naive = oracle.attend(plain, cached, vals, naive_k, dv, q, 0)
     assert np.max(np.abs(naive - want)) > 1e-3
+
+
+# ------------------------------------------------------ latent (MLA) attention
+
+def _latent_case(L=20, entries=(), chunks=(), Hq=3, D=12, ro=8, seed=30, same_rows=False,
+                 style="half"):
+    """One request, MLA-shaped rows (content [0, ro), rotary [ro, D)), f64."""
+    rng = np.random.default_rng(seed)
+    pool_tokens = max([c.token_start + c.length for c in chunks] + [1])
+    wl = Workload("lat", "f64", 1, 1, D, ro, D - ro, style, 10000.0, False,
+                  pool_tokens=pool_tokens, chunks=list(chunks),
+                  requests=[Request(list(entries), None, L)], capacity=L)
+    pk = rng.standard_normal((1, pool_tokens, 1, D))
+    ck = rng.standard_normal((1, 1, L, 1, D))
+    if same_rows:
+        ck[:] = ck[0, 0, 0]
+    q = rng.standard_normal((1, Hq, D))
+    return wl, pk, ck, q
+
+
+def test_latent_attend_equal_rows_and_sink_bias():
+    """Equal rows give equal weights: every head returns the content latent;
+    a bias b on the first sink_tokens of a chunk after 0 weights them e^b."""
+    wl, pk, ck, q = _latent_case(same_rows=True)
+    out = oracle.attend_latent(wl, pk, ck, q, 0)
+    for j in range(3):
+        assert np.allclose(out[0, j], ck[0, 0, 0, 0, :8], atol=1e-13)
+    # the chunk at 8 is all recompute tokens (read from the cache); equal
+    # rotary keys and a query with no content part make every logit equal,
+    # while the content latents (the values) differ
+    wl, pk, ck, q = _latent_case(L=20, entries=[Entry(0, 8, 6, 6)], chunks=[Chunk(0, 6)])
+    ck[0, 0, :, 0, 8:] = ck[0, 0, 0, 0, 8:]
+    q[0, :, :8] = 0.0
+    for b in (-15.0, 2.5):
+        out = oracle.attend_latent(wl, pk, ck, q, 0, sink_tokens=4, sink_bias=b)
+        wts = np.ones(20)
+        wts[8:12] = np.exp(b)
+        want = (wts[:, None] * ck[0, 0, :, 0, :8]).sum(0) / wts.sum()
+        for j in range(3):
+            assert np.allclose(out[0, j], want, atol=1e-13)
+
+
+def test_latent_attend_single_position():
+    wl, pk, ck, q = _latent_case(L=1)
+    out = oracle.attend_latent(wl, pk, ck, q, 0)
+    for j in range(3):
+        assert np.array_equal(out[0, j], ck[0, 0, 0, 0, :8])
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_latent_attend_rotated_chunks_equal_direct_rope(style):
+    """MLA chunks whose rotary keys were RoPE'd at 0..L-1, placed and turned
+    (in fp64), attend exactly like rows RoPE'd directly at their absolute
+    positions; unturned reuse differs."""
+    D, ro = 12, 8
+    rng = np.random.default_rng(32)
+    raw = rng.standard_normal((1, 12, 1, D))
+    wl0 = gqa(rope_dim=D - ro, n_heads=1, style=style, row_dim=D, rope_offset=ro, has_v=False)
+    cached = rope_at(raw, np.concatenate([np.arange(5), np.arange(7)]), wl0)
+    chunks = [Chunk(0, 5), Chunk(5, 7)]
+    entries = [Entry(1, 3, 7), Entry(0, 12, 5, 2)]
+    L = 18
+    wl = Workload("lat", "f64", 1, 1, D, ro, D - ro, style, 10000.0, False, pool_tokens=12,
+                  chunks=chunks, requests=[Request(entries, None, L)], capacity=L)
+    ck = rng.standard_normal((1, 1, L, 1, D))
+    q = rng.standard_normal((1, 4, D))
+    got = oracle.attend_latent(wl, cached, ck, q, 0, dtype="f64")
+    dk = ck.copy()
+    dk[0, 0, 3:10] = rope_at(raw[:, 5:12], np.arange(3, 10), wl0)[0]
+    dk[0, 0, 14:17] = rope_at(raw[:, 2:5], np.arange(14, 17), wl0)[0]
+    plain = Workload("lat", "f64", 1, 1, D, ro, D - ro, style, 10000.0, False, pool_tokens=12,
+                     chunks=chunks, requests=[Request([], None, L)], capacity=L)
+    want = oracle.attend_latent(plain, cached, dk, q, 0, dtype="f64")
+    assert np.allclose(got, want, atol=1e-12)
+    naive_k = dk.copy()
+    naive_k[0, 0, 3:10] = cached[0, 5:12]
+    assert np.max(np.abs(oracle.attend_latent(plain, cached, naive_k, q, 0) - want)) > 1e-3
+
+
+def test_latent_attend_matches_library_attention_over_stitched_bf16_rows():
+    """bf16 storage: the oracle's latent attention equals torch's scaled dot
+    product attention (fp64, CPU) over the rows its stitch stores (rotary
+    keys rounded to bf16), with the content latent as the values."""
+    import torch
+    from parity_util import to_host
+    from pic_workloads import normal_values
+    D, ro = 576, 512
+    chunks = [Chunk(0, 40), Chunk(40, 30)]
+    entries = [Entry(1, 10, 30, 4), Entry(0, 45, 40)]
+    L = 90
+    wl = Workload("lat", "bf16", 1, 1, D, ro, 64, "half", 10000.0, False, pool_tokens=70,
+                  chunks=chunks, requests=[Request(entries, None, L)], capacity=L)
+    pk = to_host(normal_values((1, 70, 1, D), "bf16", 1))
+    ck = to_host(normal_values((1, 1, L, 1, D), "bf16", 2))
+    q = to_host(normal_values((1, 16, D), "bf16", 3))
+    sc = 192 ** -0.5
+    got = oracle.attend_latent(wl, pk, ck, q, 0, scale=sc, sink_tokens=4, sink_bias=-15.0)
+    rows = ck.copy()
+    assert oracle.stitch(wl, pk, None, rows, None) == "ok"
+    k = torch.from_numpy(oracle.ref._to_f64(rows[0, 0, :, 0]))
+    bias = torch.zeros(L, dtype=torch.float64)
+    bias[45:49] = -15.0  # the chunk placed at 45 (the one at 10 starts with recompute tokens)
+    bias[10:14] = -15.0
+    qq = torch.from_numpy(oracle.ref._to_f64(q[0]))
+    want = torch.nn.functional.scaled_dot_product_attention(
+        qq[None], k[None].contiguous(), k[None, :, :ro].contiguous(),
+        attn_mask=bias[None, None, :].expand(1, 16, L), scale=sc)[0].numpy()
+    assert np.allclose(got[0], want, rtol=0, atol=1e-12)
