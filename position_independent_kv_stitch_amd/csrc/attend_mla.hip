@@ -9,35 +9,43 @@
 // logit is scale * q_h . row_p, and the value of position p is the content
 // latent row_p[0, 512): every query head attends over the same rows.
 // Positions a placed chunk writes read the chunk's pool row, whose rotary
-// key is turned by the chunk's shift while it is loaded (Irminsul sections
+// key is turned by the chunk's shift once it is on chip (Irminsul sections
 // 2.2 and 4: the delta-rotation fused into the attention kernel's load
 // path); the turned key is rounded to bf16 exactly as the stitch would store
 // it, so the result is attention over the stitched cache.  Every other
 // position reads the request's own cache.  The EPIC Guide's LegoLink damping
 // is the same optional logit bias as in pic_attend.
 //
-// 16 query heads share one row of 1,152 bytes: ~2,200 flops per head per row
-// over 16 heads is ~30 flop/B, beyond the fp32 vector ALU at HBM speed, so
-// both products run on the matrix cores (v_mfma_f32_16x16x32_bf16):
-//   S^T = K Q^T: A = 16 positions x 32 dims of K (a lane holds one
-//     position's 8 consecutive dims: one 16-byte load), B = the head group's
-//     queries, held in registers for the whole block; D gives a lane 4
-//     positions of one head.
-//   O^T += V^T P^T: B = the weights straight from the D registers of two
-//     S^T tiles (the k order of the product is permuted to match them), in
-//     two bf16 terms (hi + lo, so the weights lose nothing to bf16); A = the
-//     values transposed, which go through LDS: each lane writes the value
-//     dims of the key fragments it loaded into a [dim][position] tile.
-// Work item: one wave per (block of <= 256 positions of a request, group of
-// 16 query heads).  The head groups of one block are mapped to the same XCD
-// (workgroups are dealt round-robin over the 8 XCDs), so its rows are read
-// from HBM once and from that XCD's L2 after.  Partial (max, sum,
-// accumulator) per (block, head) are merged by mla_combine_kernel.
+// Work: a workgroup of W waves takes one work item (a run of positions of
+// one request) for W groups of 16 query heads, one group per wave.  The
+// items are cut for the launch: each request gets a share of the CU slots in
+// proportion to its context, so every workgroup has about the same number
+// of positions and the launch is one round.  An item's positions come in
+// steps of 32:
+//   - staging: the step's 32 rows (36 KB) go from HBM straight into LDS
+//     (global_load_lds_dwordx4, no registers), spread over the W waves, into
+//     the second of two buffers while the first is computed on;
+//   - the rotary slots of moved chunk rows are turned in LDS (fp64, rounded
+//     to bf16 by the stitch's own code, rotate.hpp);
+//   - S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16
+//     positions x 32 dims of K, one contiguous 1 KB LDS read per wave (the
+//     staging layout is the A-fragment layout); B = the wave's head group's
+//     queries, in registers for the whole item;
+//   - online softmax over the wave's 16 heads;
+//   - O^T += V^T P^T: B = the weights straight from the D registers of the
+//     two S^T tiles (the product's k order is permuted to match), split into
+//     bf16 hi + lo so the weights lose nothing; A = V^T, eight 2-byte LDS
+//     reads per fragment from the same staged rows.
+// All W waves read the one staged copy of the rows, so with 128 heads the
+// rows leave HBM once.  A partial (max, sum, accumulator) per (item, head)
+// is merged by mla_combine_kernel.  Lane layouts of the MFMA and of the
+// direct-to-LDS load were checked on the GPU.
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
 
 #include "pic_internal.hpp"
 #include "rotate.hpp"
@@ -53,25 +61,26 @@ constexpr int kRopeOff = 512;
 constexpr int kRopeDim = 64;
 constexpr int kVDim = 512;                // value = the content latent
 constexpr int kKSteps = kRow / 32;        // MFMA k-steps of 32 dims
-constexpr int kVSteps = kVDim / 32;       // the k-steps holding value dims
 constexpr int kRopeStep = kRopeOff / 32;  // first rotary k-step (x half; y in the next)
 constexpr int kDTiles = kVDim / 16;       // output tiles of 16 dims
-constexpr int kGroupHeads = 16;           // query heads per work item
+constexpr int kGroupHeads = 16;           // query heads per wave
 constexpr int kStepPos = 32;              // positions per step: two 16-position tiles
-constexpr int kVtStride = kStepPos + 4;   // LDS row of the transposed value tile
+constexpr int kSlabs = 2 * kKSteps;       // 1 KB slabs of a staged step
+constexpr int kItemTiles = 64;            // map tiles per latent block at most
+constexpr int kBlockPos = 4096;           // positions per latent block at most
 constexpr int kCombineThreads = 256;
 
-constexpr uint32_t kMetaPool = 1u << 31;      // row read from the pool (else the cache)
-constexpr uint32_t kMetaDamp = 1u << 30;      // LegoLink bias applies
+constexpr uint32_t kMetaDamp = 1u << 31;      // LegoLink bias applies
 constexpr uint32_t kMetaCs = (1u << 30) - 1;  // shift table + 1 (0: row not turned)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 struct MlaArgs {
-    const AttnTile *tiles;
-    const AttnBlock *blocks;
-    const int32_t *req_block0;
+    const AttnTile *tiles;     // latent blocks' tiles (tok0: position in the block)
+    const AttnBlock *blocks;   // latent blocks (<= kBlockPos positions, <= kItemTiles tiles)
+    const int32_t *item_block0;  // first block of every item (+ end)
+    const int32_t *req_item0;    // first item of every request (+ end)
     const double *cs;
     const uint16_t *pool_k, *cache_k;
     int64_t s_layer, s_tok, s_page;
@@ -80,9 +89,9 @@ struct MlaArgs {
     int64_t q_req, q_head;
     float *out;
     int64_t o_req, o_head;
-    float *part_acc;  // [block][q head][kVDim]
-    float *part_ml;   // [block][q head][2]
-    int32_t n_blocks, n_groups, num_q_heads;
+    float *part_acc;  // [item][q head][kVDim]
+    float *part_ml;   // [item][q head][2]
+    int32_t n_items, n_sets, num_q_heads;
     float scale;
     int32_t sink_tokens;
     float sink_bias;
@@ -98,220 +107,265 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int STYLE>
-__global__ void __launch_bounds__(64) mla_block_kernel(const MlaArgs a, int32_t layer) {
-    __shared__ AttnTile s_tiles[kAttnBlockTiles];
-    __shared__ int64_t s_off[kAttnBlockTokens];
-    __shared__ uint32_t s_meta[kAttnBlockTokens];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vt[kVDim * kVtStride];  // [dim][position]
+// Row (element offset) and meta of position pi of a block whose tiles are in
+// s_tiles[0, ntiles).
+__device__ __forceinline__ int64_t row_of(const MlaArgs &a, const AttnTile *s_tiles, int ntiles,
+                                          int pi, int32_t layer, uint32_t *meta,
+                                          const uint16_t **base) {
+    int lo = 0, hi = ntiles - 1;  // the last tile starting at or before pi
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_tiles[mid].tok0 <= pi) lo = mid;
+        else hi = mid - 1;
+    }
+    const AttnTile &T = s_tiles[lo];
+    const int t = pi - T.tok0;
+    const int64_t L = layer;
+    uint32_t m = T.cs_idx >= 0 ? static_cast<uint32_t>(T.cs_idx + 1) : 0u;
+    if (T.sink_dist + t < a.sink_tokens) m |= kMetaDamp;
+    *meta = m;
+    switch (T.kind) {
+        case kPoolRows:
+            *base = a.pool_k;
+            return L * a.s_layer + (T.a + t) * a.s_tok;
+        case kPoolPages:
+            *base = a.pool_k;
+            return L * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b + t) * a.s_tok;
+        case kCacheRows:
+            *base = a.cache_k;
+            return L * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b + t) * a.c_tok;
+        default:
+            *base = a.cache_k;
+            return L * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b + t) * a.c_tok;
+    }
+}
 
-    // the head groups of a block sit on one XCD: workgroup w runs on XCD w % 8
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef const void __attribute__((address_space(1))) *gptr_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// Two waves per SIMD: the register budget is 256 per lane (72 for the
+// queries, 128 accumulators, the rest for fragments in flight); scheduling
+// barriers keep the compiler from hoisting every LDS read of a phase ahead.
+// NB staging buffers: 2 overlap a step's loads with the previous step's
+// work inside the workgroup; 1 halves the LDS so that twice as many
+// workgroups share a CU and overlap each other instead.
+template <int STYLE, int W, int NB>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+mla_block_kernel(const MlaArgs a, int32_t layer) {
+    // staged step: slab j = (k-step j >> 1, position tile j & 1); slot 16 g + p
+    // of a slab holds dims 32 s + 8 g .. + 8 of position 16 tau + p, i.e. the
+    // A fragment of lane 16 g + p
+    __shared__ __attribute__((aligned(16))) uint4 s_stage[NB][kSlabs * 64];
+    __shared__ AttnTile s_tiles[kItemTiles];
+    __shared__ uint32_t s_pmeta[NB][kStepPos];  // meta of the staged positions
+
+    // the head-group sets of an item sit on one XCD: workgroup w runs on XCD w % 8
     const int wid = blockIdx.x;
     const int slot = wid >> 3;
-    const int hg = slot % a.n_groups;
-    const int block = (slot / a.n_groups) * 8 + (wid & 7);
-    if (block >= a.n_blocks) return;  // uniform over the wave
-    const AttnBlock B = a.blocks[block];
-    const int lane = threadIdx.x;
+    const int set = slot % a.n_sets;
+    const int item = (slot / a.n_sets) * 8 + (wid & 7);
+    if (item >= a.n_items) return;  // uniform over the workgroup
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
+    const int hg = set * W + wave;
+    const int b_lo = a.item_block0[item], b_hi = a.item_block0[item + 1];
+    const int request = a.blocks[b_lo].request;
 
-    // ---- the block's row table: element offset of every position's row
-    if (lane < B.ntiles) s_tiles[lane] = a.tiles[B.tile0 + lane];
-    __syncthreads();
-    for (int pi = lane; pi < B.ntok; pi += 64) {
-        int lo = 0, hi = B.ntiles - 1;  // the last tile starting at or before pi
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (s_tiles[mid].tok0 <= pi) lo = mid;
-            else hi = mid - 1;
-        }
-        const AttnTile &T = s_tiles[lo];
-        const int t = pi - T.tok0;
-        const int64_t L = layer;
-        int64_t off;
-        uint32_t meta = 0;
-        switch (T.kind) {
-            case kPoolRows:
-                off = L * a.s_layer + (T.a + t) * a.s_tok;
-                meta = kMetaPool;
-                break;
-            case kPoolPages:
-                off = L * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b + t) * a.s_tok;
-                meta = kMetaPool;
-                break;
-            case kCacheRows:
-                off = L * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b + t) * a.c_tok;
-                break;
-            default:
-                off = L * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b + t) * a.c_tok;
-                break;
-        }
-        if (T.cs_idx >= 0) meta |= static_cast<uint32_t>(T.cs_idx + 1);
-        if (T.sink_dist + t < a.sink_tokens) meta |= kMetaDamp;
-        s_off[pi] = off;
-        s_meta[pi] = meta;
-    }
-
-    // ---- query fragments (B of S^T = K Q^T): head r16 of the group, dims
-    // 32 s + 8 g .. + 8 of k-step s
+    // ---- query fragments (B of S^T = K Q^T): head r16 of the wave's group,
+    // dims 32 s + 8 g .. + 8 of k-step s
     bf16x8 qf[kKSteps];
     {
-        const uint16_t *qrow = a.q + B.request * a.q_req + (hg * kGroupHeads + r16) * a.q_head;
+        const uint16_t *qrow = a.q + request * a.q_req + (hg * kGroupHeads + r16) * a.q_head;
 #pragma unroll
         for (int s = 0; s < kKSteps; s++)
             qf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g));
     }
-    __syncthreads();
 
     f32x4 acc[kDTiles];
 #pragma unroll
     for (int t = 0; t < kDTiles; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int p0 = 0; p0 < B.ntok; p0 += kStepPos) {
-        // ---- key fragments of the step: tile tau, position p0 + 16 tau + r16
-        uint4 kf[2][kKSteps];
-        uint32_t meta[2];
+    for (int b = b_lo; b < b_hi; b++) {
+        const AttnBlock B = a.blocks[b];
+        __syncthreads();  // the previous block's steps are done with s_tiles and s_stage
+        if (tid < B.ntiles) s_tiles[tid] = a.tiles[B.tile0 + tid];
+        __syncthreads();
+
+        // stage step p0 into buffer bf: wave w loads slabs w, w + W, ...; lanes
+        // past the block's end repeat position p0 (their weights are 0)
+        auto stage = [&](int p0, int bf) {
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++) {
-            const int pi = p0 + 16 * tau + r16;
-            const bool valid = pi < B.ntok;
-            meta[tau] = valid ? s_meta[pi] : 0u;
-            const uint16_t *row =
-                ((meta[tau] & kMetaPool) ? a.pool_k : a.cache_k) + (valid ? s_off[pi] : 0);
-#pragma unroll
-            for (int s = 0; s < kKSteps; s++)
-                kf[tau][s] = valid ? *reinterpret_cast<const uint4 *>(row + 32 * s + 8 * g)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-        }
-        // ---- turn the rotary key of pool rows whose chunk moved, rounding
-        // to bf16 as the stitch stores it
-#pragma unroll
-        for (int tau = 0; tau < 2; tau++) {
-            const uint32_t cs1 = meta[tau] & kMetaCs;
-            if (cs1 == 0u) continue;
-            const double *tab = a.cs + static_cast<int64_t>(cs1 - 1) * (kRopeDim / 2) * 2;
-            uint4 &kx = kf[tau][kRopeStep], &ky = kf[tau][kRopeStep + 1];
-            uint32_t xw[4] = {kx.x, kx.y, kx.z, kx.w}, yw[4] = {ky.x, ky.y, ky.z, ky.w};
-            if constexpr (STYLE == PIC_ROPE_HALF) {
-                // x of planes 8 g .. 8 g + 7 in the first rotary k-step, their
-                // y (32 planes later) in the second
-                double c[8], s[8];
-#pragma unroll
-                for (int p = 0; p < 8; p++) {
-                    c[p] = tab[2 * (8 * g + p)];
-                    s[p] = tab[2 * (8 * g + p) + 1];
+            for (int tau = 0; tau < 2; tau++) {
+                int pi = p0 + 16 * tau + r16;
+                const bool valid = pi < B.ntok;
+                if (!valid) pi = p0;
+                uint32_t meta;
+                const uint16_t *base;
+                const int64_t off = row_of(a, s_tiles, B.ntiles, pi, layer, &meta, &base);
+                if (wave == 0 && g == 0) s_pmeta[bf][16 * tau + r16] = valid ? meta : 0u;
+                const uint16_t *row = base + off + 8 * g;
+                for (int j = 2 * wave + tau; j < kSlabs; j += 2 * W) {
+                    const int s = j >> 1;
+                    __builtin_amdgcn_global_load_lds((gptr_t)(row + 32 * s),
+                                                     (lptr_t)(&s_stage[bf][j * 64]), 16, 0, 0);
                 }
-                rotate_unit<uint16_t, PIC_ROPE_HALF, 4>(xw, yw, c, s);
-            } else {
-                // whole pairs: planes 4 g .. 4 g + 3, then 16 + 4 g .. + 3
-                double c0[4], s0[4], c1[4], s1[4];
-#pragma unroll
-                for (int p = 0; p < 4; p++) {
-                    c0[p] = tab[2 * (4 * g + p)];
-                    s0[p] = tab[2 * (4 * g + p) + 1];
-                    c1[p] = tab[2 * (16 + 4 * g + p)];
-                    s1[p] = tab[2 * (16 + 4 * g + p) + 1];
-                }
-                rotate_unit<uint16_t, PIC_ROPE_INTERLEAVED, 4>(xw, xw, c0, s0);
-                rotate_unit<uint16_t, PIC_ROPE_INTERLEAVED, 4>(yw, yw, c1, s1);
             }
-            kx = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-            ky = make_uint4(yw[0], yw[1], yw[2], yw[3]);
-        }
-        // ---- logits S^T for the group's heads
-        f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        };
+
+        stage(0, 0);
+        int bf = 0;
+        for (int p0 = 0; p0 < B.ntok; p0 += kStepPos, bf = (bf + 1) % NB) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // the step is in LDS (every wave's share) and its meta written
+            if (NB == 2 && p0 + kStepPos < B.ntok) stage(p0 + kStepPos, bf ^ 1);
+
+            // ---- turn the rotary slots of moved chunk rows, in LDS
+            for (int t = tid; t < 4 * kStepPos; t += 64 * W) {
+                const int pos = t >> 2, gg = t & 3;
+                const uint32_t cs1 = s_pmeta[bf][pos] & kMetaCs;
+                if (cs1 == 0u) continue;
+                const double *tab = a.cs + static_cast<int64_t>(cs1 - 1) * kRopeDim;
+                const int tau = pos >> 4, pp = pos & 15;
+                uint4 &kx = s_stage[bf][(2 * kRopeStep + tau) * 64 + 16 * gg + pp];
+                uint4 &ky = s_stage[bf][(2 * kRopeStep + 2 + tau) * 64 + 16 * gg + pp];
+                uint32_t xw[4] = {kx.x, kx.y, kx.z, kx.w}, yw[4] = {ky.x, ky.y, ky.z, ky.w};
+                // one plane at a time (few registers live beside the queries
+                // and accumulators): the stitch's fp64 turn and rounding
 #pragma unroll
-        for (int s = 0; s < kKSteps; s++)
+                for (int q = 0; q < 8; q++) {
+                    if constexpr (STYLE == PIC_ROPE_HALF) {
+                        // x of plane 8 gg + q in the first rotary k-step, its y
+                        // (32 planes later) in the second
+                        const double c = tab[2 * (8 * gg + q)], sn = tab[2 * (8 * gg + q) + 1];
+                        uint32_t &wx = xw[q >> 1], &wy = yw[q >> 1];
+                        const int sh = 16 * (q & 1);
+                        const double x = static_cast<double>(__uint_as_float(((wx >> sh) & 0xFFFFu) << 16));
+                        const double y = static_cast<double>(__uint_as_float(((wy >> sh) & 0xFFFFu) << 16));
+                        const uint32_t nx = f64_to_bf16(x * c - y * sn), ny = f64_to_bf16(x * sn + y * c);
+                        wx = (wx & ~(0xFFFFu << sh)) | (nx << sh);
+                        wy = (wy & ~(0xFFFFu << sh)) | (ny << sh);
+                    } else {
+                        // a whole pair per word: planes 4 gg + q (first k-step),
+                        // 16 + 4 gg + q - 4 (second)
+                        const int plane = q < 4 ? 4 * gg + q : 16 + 4 * gg + (q - 4);
+                        const double c = tab[2 * plane], sn = tab[2 * plane + 1];
+                        uint32_t &w = q < 4 ? xw[q] : yw[q - 4];
+                        const double x = bf16_lo(w), y = bf16_hi(w);
+                        w = f64_to_bf16(x * c - y * sn) | (f64_to_bf16(x * sn + y * c) << 16);
+                    }
+                }
+                kx = make_uint4(xw[0], xw[1], xw[2], xw[3]);
+                ky = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+            }
+            __syncthreads();
+
+            // ---- logits S^T for the wave's heads
+            const uint4 *stg = s_stage[bf];
+            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < kKSteps; s++) {
+#pragma unroll
+                for (int tau = 0; tau < 2; tau++)
+                    st[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        as_bf16x8(stg[(2 * s + tau) * 64 + lane]), qf[s], st[tau], 0, 0, 0);
+                if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // ---- online softmax over head r16: this lane holds positions
+            // p0 + 16 tau + 4 g + i
+            float sc[8];
 #pragma unroll
             for (int tau = 0; tau < 2; tau++)
-                st[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[tau][s]), qf[s],
-                                                                 st[tau], 0, 0, 0);
-        // ---- the value dims into LDS, transposed: s_vt[dim][position in step]
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++)
+                for (int i = 0; i < 4; i++) {
+                    const int pos = 16 * tau + 4 * g + i;
+                    float x = st[tau][i] * a.scale;
+                    if (s_pmeta[bf][pos] & kMetaDamp) x += a.sink_bias;
+                    sc[4 * tau + i] = p0 + pos < B.ntok ? x : -INFINITY;
+                }
+            float mx = sc[0];
 #pragma unroll
-            for (int s = 0; s < kVSteps; s++) {
-                const uint32_t w[4] = {kf[tau][s].x, kf[tau][s].y, kf[tau][s].z, kf[tau][s].w};
+            for (int k = 1; k < 8; k++) mx = fmaxf(mx, sc[k]);
+            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run, mx);  // finite: position p0 is in the block
+            const float alpha = __expf(m_run - m_new);
+            float pw[8], psum = 0.f;
 #pragma unroll
-                for (int j = 0; j < 8; j++)
-                    s_vt[(32 * s + 8 * g + j) * kVtStride + 16 * tau + r16] =
-                        static_cast<uint16_t>((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+            for (int k = 0; k < 8; k++) {
+                pw[k] = __expf(sc[k] - m_new);
+                psum += pw[k];
             }
-        // ---- online softmax over head r16: this lane holds positions
-        // p0 + 16 tau + 4 g + i
-        float sc[8];
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
 #pragma unroll
-        for (int tau = 0; tau < 2; tau++)
+            for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
+            // weights as B of O^T += V^T P^T: k index 8 g + j is position
+            // 4 g + j (j < 4) or 16 + 4 g + j - 4, the order of pw; hi + lo bf16
+            uint32_t hi[4], lo[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int pos = p0 + 16 * tau + 4 * g + i;
-                float x = st[tau][i] * a.scale;
-                if (pos < B.ntok && (s_meta[pos] & kMetaDamp)) x += a.sink_bias;
-                sc[4 * tau + i] = pos < B.ntok ? x : -INFINITY;
+            for (int k = 0; k < 4; k++) {
+                const uint32_t h0 = f32_to_bf16(pw[2 * k]), h1 = f32_to_bf16(pw[2 * k + 1]);
+                const float r0 = pw[2 * k] - __uint_as_float(h0 << 16);
+                const float r1 = pw[2 * k + 1] - __uint_as_float(h1 << 16);
+                hi[k] = h0 | (h1 << 16);
+                lo[k] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
             }
-        float mx = sc[0];
+            const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+            const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+
+            // ---- A = V^T (dim d = 16 t + r16; positions 4 g .. 4 g + 3, then
+            // 16 + 4 g .. + 3) by transposing LDS reads: within each 16-lane
+            // group, lane i receives element i % 4 of the 8-byte rows that
+            // lanes 4 j + i / 4 address (j = 0..3).  So lane i of group g
+            // addresses position 4 g + i / 4 (+ 16 for the second read), dims
+            // 16 t + 4 (i % 4) .. + 4: slab (t / 2, tile), slot 16 g' + position
+            // % 16 with g' = 2 (t % 2) + (i % 4) / 2, second half when i is odd
+            const char *stg8 = reinterpret_cast<const char *>(stg);
+            const int pq = r16 >> 2, dq = r16 & 3;
 #pragma unroll
-        for (int k = 1; k < 8; k++) mx = fmaxf(mx, sc[k]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);  // finite: position p0 is in the block
-        const float alpha = __expf(m_run - m_new);
-        float pw[8], psum = 0.f;
-#pragma unroll
-        for (int k = 0; k < 8; k++) {
-            pw[k] = __expf(sc[k] - m_new);
-            psum += pw[k];
+            for (int t = 0; t < kDTiles; t++) {
+                const int gq = 2 * (t & 1) + (dq >> 1);
+                const int base = ((2 * (t >> 1)) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(stg8 + base));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(stg8 + base + 64 * 16));  // tile 1: the next slab
+                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                const uint32_t w[4] = {w0.x, w0.y, w1.x, w1.y};
+                const bf16x8 va = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+                if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+            if (NB == 1 && p0 + kStepPos < B.ntok) {
+                __syncthreads();  // every wave is done with the buffer
+                stage(p0 + kStepPos, 0);
+            }
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
-        // weights as B of O^T += V^T P^T: k index 8 g + j is position
-        // 4 g + j (j < 4) or 16 + 4 g + j - 4, the order of pw; hi + lo bf16
-        uint32_t hi[4], lo[4];
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const uint32_t h0 = f32_to_bf16(pw[2 * k]), h1 = f32_to_bf16(pw[2 * k + 1]);
-            const float r0 = pw[2 * k] - __uint_as_float(h0 << 16);
-            const float r1 = pw[2 * k + 1] - __uint_as_float(h1 << 16);
-            hi[k] = h0 | (h1 << 16);
-            lo[k] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
-        }
-        const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-        const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-        __syncthreads();  // the value tile is complete
-#pragma unroll
-        for (int t = 0; t < kDTiles; t++) {
-            // A = V^T: dim 16 t + r16, positions 4 g .. 4 g + 3 and 16 + 4 g .. + 3
-            const uint16_t *vr = s_vt + (16 * t + r16) * kVtStride;
-            const uint2 v0 = *reinterpret_cast<const uint2 *>(vr + 4 * g);
-            const uint2 v1 = *reinterpret_cast<const uint2 *>(vr + 16 + 4 * g);
-            const bf16x8 va = as_bf16x8(make_uint4(v0.x, v0.y, v1.x, v1.y));
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
-        }
-        __syncthreads();  // before the next step rewrites the tile
     }
 
     // ---- partial results: O^T D registers hold dims 16 t + 4 g + i of head r16
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
     const int head = hg * kGroupHeads + r16;
-    const int64_t item = static_cast<int64_t>(block) * a.num_q_heads + head;
-    float *pa = a.part_acc + item * kVDim;
+    const int64_t slot_id = static_cast<int64_t>(item) * a.num_q_heads + head;
+    float *pa = a.part_acc + slot_id * kVDim;
 #pragma unroll
     for (int t = 0; t < kDTiles; t++)
         *reinterpret_cast<float4 *>(pa + 16 * t + 4 * g) =
             make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
     if (g == 0) {
-        a.part_ml[2 * item] = m_run;
-        a.part_ml[2 * item + 1] = l_run;
+        a.part_ml[2 * slot_id] = m_run;
+        a.part_ml[2 * slot_id + 1] = l_run;
     }
 }
 
 // out[r][j][d] = sum_b acc_b[d] e^{m_b - M} / sum_b l_b e^{m_b - M} over the
-// request's blocks, in order, 256 at a time; a thread owns two dims.
+// request's items, in order, 256 at a time; a thread owns two dims.
 __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(const MlaArgs a) {
     __shared__ float s_f[kCombineThreads];
     __shared__ float s_lf[kCombineThreads];
@@ -319,7 +373,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(const MlaA
     const int r = blockIdx.x;
     const int j = blockIdx.y;
     const int d = threadIdx.x;
-    const int b0 = a.req_block0[r], b1 = a.req_block0[r + 1];
+    const int b0 = a.req_item0[r], b1 = a.req_item0[r + 1];
     const int64_t hq = a.num_q_heads;
     float M = -INFINITY;
     for (int b = b0 + d; b < b1; b += kCombineThreads) M = fmaxf(M, a.part_ml[(b * hq + j) * 2]);
@@ -351,6 +405,115 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(const MlaA
     float *o = a.out + r * a.o_req + j * a.o_head;
     o[d] = O0 / L;
     o[d + kCombineThreads] = O1 / L;
+}
+
+// ------------------------------------------------------------------ host
+
+// A map tile moved k positions on (its rows are consecutive in its source).
+AttnTile advance(AttnTile t, int32_t k) {
+    if (t.kind == kPoolRows) t.a += k;
+    else t.b += k;
+    if (t.sink_dist < kNoSink)
+        t.sink_dist = static_cast<int32_t>(std::min<int64_t>(int64_t{t.sink_dist} + k, kNoSink));
+    t.ntok -= k;
+    return t;
+}
+
+// Work items of one launch: request r gets a share of `target` items in
+// proportion to its context (at least one), each of ceil(L / n) positions
+// cut from its map tiles (tiles split where an item ends), stored as blocks
+// of at most kBlockPos positions and kItemTiles tiles.  Packed as
+// [tiles][blocks][item -> first block (+ end)][request -> first item (+ end)].
+struct LatentMap {
+    std::vector<uint8_t> bytes;
+    size_t off_blocks = 0, off_items = 0, off_reqs = 0;
+    int32_t n_items = 0, n_blocks = 0;
+};
+
+LatentMap build_latent_map(const Problem &p, int64_t target) {
+    std::vector<AttnTile> tiles;
+    std::vector<AttnBlock> blocks;
+    std::vector<int32_t> item0, req0;
+    int64_t total = 0;
+    for (int64_t L : p.context) total += L;
+    const int32_t n_req = static_cast<int32_t>(p.context.size());
+    for (int32_t r = 0; r < n_req; r++) {
+        req0.push_back(static_cast<int32_t>(item0.size()));
+        const int64_t L = p.context[r];
+        const int64_t n = std::max<int64_t>(1, (target * L + total / 2) / std::max<int64_t>(total, 1));
+        const int64_t S = (L + n - 1) / n;  // positions per item
+        int64_t left = L, item_left = 0;
+        AttnBlock blk{r, 0, 0, 0};
+        auto close_block = [&]() {
+            if (blk.ntiles > 0) blocks.push_back(blk);
+            blk = AttnBlock{r, static_cast<int32_t>(tiles.size()), 0, 0};
+        };
+        for (int32_t t = p.req_tile0[r]; t < p.req_tile0[r + 1] && left > 0; t++) {
+            AttnTile T = p.atiles[t];
+            while (T.ntok > 0 && left > 0) {
+                if (item_left == 0) {  // a new item starts here
+                    close_block();
+                    item0.push_back(static_cast<int32_t>(blocks.size()));
+                    item_left = std::min(S, left);
+                }
+                if (blk.ntok == kBlockPos || blk.ntiles == kItemTiles) close_block();
+                const int32_t take = static_cast<int32_t>(std::min<int64_t>(
+                    {int64_t{T.ntok}, item_left, int64_t{kBlockPos - blk.ntok}}));
+                AttnTile piece = T;
+                piece.ntok = take;
+                piece.tok0 = blk.ntok;
+                tiles.push_back(piece);
+                blk.ntiles++;
+                blk.ntok += take;
+                item_left -= take;
+                left -= take;
+                T = advance(T, take);
+                if (item_left == 0) close_block();
+            }
+        }
+        close_block();
+    }
+    req0.push_back(static_cast<int32_t>(item0.size()));
+    item0.push_back(static_cast<int32_t>(blocks.size()));
+    LatentMap m;
+    auto put = [&](const void *src, size_t n) {
+        const size_t at = (m.bytes.size() + 15) & ~size_t{15};
+        m.bytes.resize(at + n);
+        if (n) std::memcpy(m.bytes.data() + at, src, n);
+        return at;
+    };
+    put(tiles.data(), tiles.size() * sizeof(AttnTile));
+    m.off_blocks = put(blocks.data(), blocks.size() * sizeof(AttnBlock));
+    m.off_items = put(item0.data(), item0.size() * sizeof(int32_t));
+    m.off_reqs = put(req0.data(), req0.size() * sizeof(int32_t));
+    m.n_items = static_cast<int32_t>(item0.size()) - 1;
+    m.n_blocks = static_cast<int32_t>(blocks.size());
+    return m;
+}
+
+int cu_count() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return 256;
+    return n;
+}
+
+#ifndef PIC_MLA_NB1
+#define PIC_MLA_NB1 1
+#endif
+// staging buffers of the one-wave workgroup
+constexpr int kNb1 = PIC_MLA_NB1;
+
+template <int STYLE>
+hipError_t launch_block(int w, dim3 grid, hipStream_t stream, const MlaArgs &a, int32_t layer) {
+    switch (w) {
+        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 2>), grid, dim3(512), 0, stream, a, layer); break;
+        case 4: hipLaunchKernelGGL((mla_block_kernel<STYLE, 4, 2>), grid, dim3(256), 0, stream, a, layer); break;
+        case 2: hipLaunchKernelGGL((mla_block_kernel<STYLE, 2, 2>), grid, dim3(128), 0, stream, a, layer); break;
+        default: hipLaunchKernelGGL((mla_block_kernel<STYLE, 1, kNb1>), grid, dim3(64), 0, stream, a, layer); break;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -397,19 +560,62 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     st = ensure_device_plan(plan, stream_);
     if (st) return st;
-    const size_t need = p.ablocks.size() * static_cast<size_t>(args->num_q_heads) *
-                        (static_cast<size_t>(kVDim) + 2) * sizeof(float);
+
+    // head groups per workgroup (one wave each) and workgroups per item
+    const int G = args->num_q_heads / kGroupHeads;
+    const int W = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
+    const int sets = G / W;
+    // concurrent workgroups per CU: two with two 37 KB staging buffers each,
+    // four one-wave workgroups with one buffer; eight waves of up to 256
+    // registers fill a CU's register file
+    const int per_cu = W == 8 ? 1 : (W == 1 && kNb1 == 1) ? 4 : 2;
+    const int64_t slots = static_cast<int64_t>(cu_count()) * per_cu;
+    const int64_t target = std::max<int64_t>(1, slots / sets);
     {
         std::lock_guard<std::mutex> lock(plan->mu);
+        hipError_t e;
+        if (plan->latent_key != target) {
+            LatentMap m = build_latent_map(p, target);
+            if (plan->d_latent) {
+                e = hipDeviceSynchronize();  // earlier launches may read the old items
+                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+            }
+            if (m.bytes.size() > plan->latent_bytes) {
+                if (plan->d_latent) (void)hipFree(plan->d_latent);
+                plan->d_latent = nullptr;
+                plan->latent_bytes = 0;
+                e = hipMalloc(&plan->d_latent, m.bytes.size());
+                if (e != hipSuccess) {
+                    plan->d_latent = nullptr;
+                    return hip_fail(e, "hipMalloc (latent work items)");
+                }
+                plan->latent_bytes = m.bytes.size();
+            }
+            plan->latent_host = std::move(m.bytes);
+            e = hipMemcpyAsync(plan->d_latent, plan->latent_host.data(), plan->latent_host.size(),
+                               hipMemcpyHostToDevice, stream);
+            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (latent work items)");
+            e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), stream);
+            if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+            plan->latent_off_blocks = m.off_blocks;
+            plan->latent_off_items = m.off_items;
+            plan->latent_off_reqs = m.off_reqs;
+            plan->latent_n_items = m.n_items;
+            plan->latent_n_blocks = m.n_blocks;
+            plan->latent_key = target;
+        }
+        const size_t need = static_cast<size_t>(plan->latent_n_items) *
+                            static_cast<size_t>(args->num_q_heads) *
+                            (static_cast<size_t>(kVDim) + 2) * sizeof(float);
         if (plan->work_bytes < need) {
             if (plan->d_work) {
-                hipError_t e = hipDeviceSynchronize();  // earlier calls may use it
+                e = hipDeviceSynchronize();  // earlier calls may use it
                 if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
                 (void)hipFree(plan->d_work);
                 plan->d_work = nullptr;
                 plan->work_bytes = 0;
             }
-            hipError_t e = hipMalloc(&plan->d_work, need);
+            e = hipMalloc(&plan->d_work, need);
             if (e != hipSuccess) {
                 plan->d_work = nullptr;
                 return hip_fail(e, "hipMalloc (attention workspace)");
@@ -418,10 +624,12 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
         }
     }
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
+    const uint8_t *lm = static_cast<const uint8_t *>(plan->d_latent);
     MlaArgs a{};
-    a.tiles = reinterpret_cast<const AttnTile *>(dm + plan->staged.off_atiles);
-    a.blocks = reinterpret_cast<const AttnBlock *>(dm + plan->staged.off_ablocks);
-    a.req_block0 = reinterpret_cast<const int32_t *>(dm + plan->staged.off_rblock);
+    a.tiles = reinterpret_cast<const AttnTile *>(lm);
+    a.blocks = reinterpret_cast<const AttnBlock *>(lm + plan->latent_off_blocks);
+    a.item_block0 = reinterpret_cast<const int32_t *>(lm + plan->latent_off_items);
+    a.req_item0 = reinterpret_cast<const int32_t *>(lm + plan->latent_off_reqs);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = static_cast<const uint16_t *>(pool->k);
     a.cache_k = static_cast<const uint16_t *>(cache->k);
@@ -438,25 +646,21 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     a.out = args->out;
     a.o_req = args->out_request_stride;
     a.o_head = args->out_head_stride;
-    const size_t acc_elems = p.ablocks.size() * static_cast<size_t>(args->num_q_heads) * kVDim;
+    const size_t acc_elems =
+        static_cast<size_t>(plan->latent_n_items) * static_cast<size_t>(args->num_q_heads) * kVDim;
     a.part_acc = static_cast<float *>(plan->d_work);
     a.part_ml = static_cast<float *>(plan->d_work) + acc_elems;
-    a.n_blocks = static_cast<int32_t>(p.ablocks.size());
-    a.n_groups = args->num_q_heads / kGroupHeads;
+    a.n_items = plan->latent_n_items;
+    a.n_sets = sets;
     a.num_q_heads = args->num_q_heads;
     a.scale = args->scale;
     a.sink_tokens = args->sink_tokens;
     a.sink_bias = args->sink_bias;
-    // blocks rounded up to a multiple of the 8 XCDs, times the head groups
-    const unsigned grid = static_cast<unsigned>((a.n_blocks + 7) / 8 * 8) *
-                          static_cast<unsigned>(a.n_groups);
-    if (p.style == PIC_ROPE_HALF)
-        hipLaunchKernelGGL(mla_block_kernel<PIC_ROPE_HALF>, dim3(grid), dim3(64), 0, stream, a,
-                           args->layer);
-    else
-        hipLaunchKernelGGL(mla_block_kernel<PIC_ROPE_INTERLEAVED>, dim3(grid), dim3(64), 0, stream,
-                           a, args->layer);
-    hipError_t e = hipGetLastError();
+    // items rounded up to a multiple of the 8 XCDs, times the head-group sets
+    const dim3 grid(static_cast<unsigned>((a.n_items + 7) / 8 * 8) * static_cast<unsigned>(sets));
+    hipError_t e = p.style == PIC_ROPE_HALF
+                       ? launch_block<PIC_ROPE_HALF>(W, grid, stream, a, args->layer)
+                       : launch_block<PIC_ROPE_INTERLEAVED>(W, grid, stream, a, args->layer);
     if (e != hipSuccess) return hip_fail(e, "latent attention kernel launch");
     hipLaunchKernelGGL(mla_combine_kernel,
                        dim3(static_cast<unsigned>(p.context.size()),

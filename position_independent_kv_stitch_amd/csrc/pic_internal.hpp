@@ -142,4 +142,12 @@ struct pic_plan {
     void *upload_event = nullptr;  // hipEvent_t
     void *d_work = nullptr;        // pic_attend partial results
     size_t work_bytes = 0;
+    // pic_attend_latent work items (attend_mla.hip): built for one launch
+    // shape, uploaded, and rebuilt when a call needs another shape
+    void *d_latent = nullptr;
+    size_t latent_bytes = 0;
+    int64_t latent_key = -1;
+    std::vector<uint8_t> latent_host;  // the uploaded bytes (alive for the copy)
+    size_t latent_off_blocks = 0, latent_off_items = 0, latent_off_reqs = 0;
+    int32_t latent_n_items = 0, latent_n_blocks = 0;
 };
