@@ -89,6 +89,12 @@ WORKLOADS = {
                          "64-token pages; one call per layer, 61 layers per step",
     "attend-mla-decode-16h": "the attend-mla-decode workload with 16 query heads (DeepSeek-V2-"
                              "Lite's head count, or one GPU's share of 128 heads over 8)",
+    "legolink-boundary": "LegoLink boundary reconnection (pic_attend_boundary): the first 16 "
+                         "tokens of every relocated chunk attend causally over the stitched "
+                         "context, chunk keys turned on load; Llama-3-8B decode batch (16 "
+                         "requests x 8 chunks x 2048 behind a 128-token prefix, recompute_k 32, "
+                         "16-token pages), 32 query heads over 8 kv heads x 128, bf16, damping "
+                         "4 x -15; one call per layer, 32 layers per step",
     "cdc-rag": "content-defined chunking + xxHash64 fingerprints + registry lookup + 128-token "
                "fallback windows (pic_match) over the batched-RAG prompt stream: 64 requests, "
                "~1.44 M tokens, 10% of placed documents edited, registry of the 256 pool "
@@ -117,6 +123,8 @@ def setup_workload(name, torch, pic):
         return setup_attend(name, torch, pic)
     if name.startswith("attend-mla-decode"):
         return setup_attend_mla(name, torch, pic)
+    if name == "legolink-boundary":
+        return setup_boundary(name, torch, pic)
     if name.startswith("cdc-rag"):
         return setup_cdc(name, torch, pic)
     wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
@@ -212,6 +220,44 @@ def setup_attend_mla(name, torch, pic):
             "token_layers": info["context_tokens"] * L, "launches": L, "flops": flops,
             "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)",
             "plan": plan, "info": info, "config": cfg}
+
+
+def setup_boundary(name, torch, pic):
+    """Boundary reconnection: one step is a pic_attend_boundary per layer."""
+    from pic_workloads import decode_batch, normal_values, pool_values
+    wl = decode_batch()
+    k, group = 16, 4
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, 2, "cuda:0")
+    cv = normal_values(wl.dst_shape(), wl.dtype, 3, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    n = pic.boundary_row_count(plan, k)
+    L = wl.n_layers
+    q = normal_values((L, n, wl.n_heads * group, wl.row_dim), wl.dtype, 4, "cuda:0")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda:0")
+
+    def step():
+        for layer in range(L):
+            pic.attend_boundary(plan, pk, pv, ck, cv, q[layer], layer=layer, boundary_k=k,
+                                out=out[layer], scale=wl.row_dim ** -0.5, sink_tokens=4,
+                                sink_bias=-15.0)
+
+    # every relocated entry's rows read the K and V rows of context [0, d + k) once
+    bounds, _ = plan.ranges()
+    reloc = [(int(b), int(e - b)) for _, b, e in bounds if b > 0]
+    ctx = sum(d + min(k, ln) for d, ln in reloc)
+    row_bytes = 2 * wl.n_heads * wl.row_dim * 2
+    pairs = sum(sum(d + j + 1 for j in range(min(k, ln))) for d, ln in reloc)  # (row, position)
+    flops = pairs * wl.n_heads * group * 2 * 2 * wl.row_dim * L
+    cfg = {"workload": WORKLOADS[name], "storage": wl.dtype, "layers": L,
+           "kv_heads": wl.n_heads, "q_heads": wl.n_heads * group, "row_dim": wl.row_dim,
+           "requests": len(wl.requests), "relocated_entries": len(reloc), "boundary_k": k,
+           "boundary_rows": n, "context_positions_read": ctx, "page_size": wl.page_size,
+           "sink_tokens": 4, "sink_bias": -15.0, "parallelism": "single-gpu"}
+    return {"wl": wl, "step": step, "bytes": ctx * row_bytes * L, "token_layers": n * L,
+            "launches": L, "flops": flops,
+            "kernel": "bnd_block_kernel<half> + bnd_combine_kernel (one pic_attend_boundary)",
+            "plan": plan, "config": cfg}
 
 
 def setup_cdc(name, torch, pic):

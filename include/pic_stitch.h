@@ -361,6 +361,50 @@ typedef struct pic_attend_latent_args {
 pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
                              const pic_attend_latent_args *args, void *stream);
 
+/*
+ * LegoLink's boundary reconnection (EPIC Guide, "2. Sparse Cross-Block
+ * Reconnection"): the first boundary_k tokens of every chunk placed after
+ * position 0 attend across the chunk boundary.  Boundary row b is token j <
+ * min(boundary_k, length) of such an entry (entries request by request, in
+ * each request's order; pic_plan_ranges lists them); it attends causally to
+ * positions [0, dst_offset + j] of its request:
+ *   out[b][jq] = sum_p w_p V_p / sum_p w_p,  w_p = exp(scale * q[b][jq] . K_p + b_p)
+ * with the rows pic_attend reads (chunk keys turned by the entry's delta on
+ * load, rounded to bf16 as pic_stitch stores them; other positions from the
+ * request's own cache), query head jq reading KV head jq / (num_q_heads /
+ * num_heads), and b_p the LegoLink damping of pic_attend.  Products on the
+ * matrix cores with fp32 accumulation, weights as two bf16 terms.
+ */
+typedef struct pic_attend_boundary_args {
+    const void *q;          /* device bf16 [boundary row][q head][row_dim], post-RoPE */
+    int64_t q_row_stride, q_head_stride;
+    float *out;             /* device fp32 [boundary row][q head][row_dim] */
+    int64_t out_row_stride, out_head_stride;
+    int32_t num_q_heads;    /* a multiple of num_heads, at most 8x */
+    int32_t layer;
+    float scale;
+    int32_t boundary_k;     /* boundary tokens per relocated entry (the EPIC listing: 16);
+                               boundary_k x (num_q_heads / num_heads) <= 128 */
+    int32_t sink_tokens;    /* LegoLink damping (0 = off) */
+    float sink_bias;
+} pic_attend_boundary_args;
+
+/*
+ * pic_attend_boundary -- enqueue the boundary reconnection of every
+ * relocated entry of a plan at one layer (see above).  bf16 plans with K
+ * and V head rows of 128 dims and a rotary slice on 8-dim pieces
+ * (PIC_ERR_INVALID_ARG, PIC_ERR_ALIGN); q rows 16-byte aligned
+ * (PIC_ERR_ALIGN); every boundary row's positions inside its request's
+ * context and mapped pages (PIC_ERR_RANGE); in-place plans refused
+ * (PIC_ERR_STATE).  A plan without relocated entries enqueues nothing.  The
+ * work items for a launch shape are built on the host and uploaded with the
+ * plan on first use (a later call with another boundary_k waits for the
+ * device and rebuilds them); the partial-result workspace is the plan's,
+ * shared with pic_attend: calls on one plan that may overlap race.
+ */
+pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
+                               const pic_attend_boundary_args *args, void *stream);
+
 /* pic_plan_info -- sizes and algorithmic byte counts of a plan. */
 pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info);
 

@@ -4,6 +4,7 @@ TEST INFRASTRUCTURE ONLY: the test suite, the package smoke check and the
 benchmark's CPU-baseline leg are its only users.  The product path never
 imports it, and it shares no code with the HIP library.
 """
-from .ref import (attend, attend_latent, inv_freq, recompute_ranges, rotate_inplace,  # noqa: F401
+from .ref import (attend, attend_boundary, attend_latent, boundary_rows, inv_freq,  # noqa: F401
+                  recompute_ranges, rotate_inplace,
                   round_bf16,
                   stitch, validate_inplace, validate_stitch)

@@ -402,3 +402,86 @@ def attend_latent(wl, pool_k, cache_k, q, layer, scale=None, sink_tokens=0, sink
             w = np.exp(logits - logits.max())
             out[r, j] = (w @ rows[:, :V]) / w.sum()
     return out
+
+
+def boundary_rows(wl, boundary_k):
+    """The boundary rows of a plan, in order: (request, entry index, token j,
+    position) for every entry placed after position 0 and j < min(k, length),
+    requests in order, each request's entries in the order given."""
+    rows = []
+    for r, rq in enumerate(wl.requests):
+        for i, e in enumerate(rq.entries):
+            if e.dst_offset > 0:
+                for j in range(min(boundary_k, e.length)):
+                    rows.append((r, i, j, e.dst_offset + j))
+    return rows
+
+
+def attend_boundary(wl, pool_k, pool_v, cache_k, cache_v, q, layer, boundary_k, scale=None,
+                    sink_tokens=0, sink_bias=0.0, layer_base=0, dtype=None):
+    """LegoLink's boundary reconnection (EPIC Guide, "2. Sparse Cross-Block
+    Reconnection"), in fp64: boundary token j of every entry placed after
+    position 0 (its first boundary_k tokens) attends causally to every
+    position of its request up to and including its own, p = dst_offset + j:
+    the preceding chunks and prefix (the cross-chunk part) and its own
+    chunk's earlier tokens.  q: [boundary rows][q heads][row_dim] in
+    boundary_rows() order; returns [boundary rows][q heads][row_dim].
+
+    The context rows are those this oracle's stitch leaves (chunk keys turned
+    by the entry's shift and rounded to the storage type; dtype 'f64': not
+    rounded), every other position the request's own cache row; query head
+    j reads KV head j // (num_q_heads / n_heads); damping as in attend()."""
+    from types import SimpleNamespace as NS
+    li = layer - layer_base
+    H, D = wl.n_heads, wl.row_dim
+    Hq = q.shape[1]
+    G = Hq // H
+    sc = D ** -0.5 if scale is None else scale
+    dt = dtype or wl.dtype
+    rows = boundary_rows(wl, boundary_k)
+    out = np.zeros((len(rows), Hq, D))
+    pk, pv = pool_k[li:li + 1], pool_v[li:li + 1]
+    if dt == "f64":
+        pk, pv = _to_f64(pk), _to_f64(pv)
+    ctx = {}
+    for r in sorted({row[0] for row in rows}):
+        rq = wl.requests[r]
+        L = max(e.dst_offset + e.length for e in rq.entries)
+        pos = np.arange(L)
+        if wl.page_size:
+            pt = np.asarray(rq.page_table)
+            k = _to_f64(cache_k[li][pt[pos // wl.page_size], pos % wl.page_size])
+            v = _to_f64(cache_v[li][pt[pos // wl.page_size], pos % wl.page_size])
+        else:
+            k = _to_f64(cache_k[li][r, :L])
+            v = _to_f64(cache_v[li][r, :L])
+        sub = NS(dtype=dt, n_layers=1, n_heads=H, row_dim=D, rope_offset=wl.rope_offset,
+                 rope_dim=wl.rope_dim, style=wl.style, theta=wl.theta, inv_freq=wl.inv_freq,
+                 has_v=True, pool_tokens=wl.pool_tokens, chunks=wl.chunks,
+                 src_page_size=getattr(wl, "src_page_size", 0),
+                 src_n_pages=getattr(wl, "src_n_pages", 0),
+                 requests=[NS(entries=rq.entries, page_table=None)], page_size=0, capacity=L,
+                 n_phys_pages=0)
+        sk = np.zeros((1, 1, L, H, D), dtype=pk.dtype)
+        sv = np.zeros((1, 1, L, H, D), dtype=pk.dtype)
+        st = stitch(sub, pk, pv, sk, sv, 0, 1, dtype=dt)
+        if st != "ok":
+            raise ValueError(f"request {r}: {st}")
+        sk, sv = _to_f64(sk), _to_f64(sv)
+        bias = np.zeros(L)
+        for e in rq.entries:
+            lo, hi = e.dst_offset + e.recompute_k, e.dst_offset + e.length
+            if lo < hi:
+                k[lo:hi] = sk[0, 0, lo:hi]
+                v[lo:hi] = sv[0, 0, lo:hi]
+            if e.dst_offset > 0 and sink_tokens > 0:
+                bias[e.dst_offset:min(e.dst_offset + sink_tokens, L)] = sink_bias
+        ctx[r] = (k, v, bias)
+    for b, (r, _, _, p) in enumerate(rows):
+        k, v, bias = ctx[r]
+        qq = _to_f64(q[b])
+        for h in range(H):  # the G query heads of KV head h at once
+            logits = sc * (qq[h * G:(h + 1) * G] @ k[:p + 1, h, :].T) + bias[:p + 1]
+            w = np.exp(logits - logits.max(axis=1, keepdims=True))
+            out[b, h * G:(h + 1) * G] = (w @ v[:p + 1, h, :]) / w.sum(axis=1, keepdims=True)
+    return out

@@ -9,7 +9,7 @@ its thin binding.  Importing it loads the library and fails if it has not
 been built.
 """
 from ._binding import (EXPORTS, LIBRARY, PicError, Plan, Registry, attend,  # noqa: F401
-                       attend_latent,
+                       attend_boundary, attend_latent, boundary_row_count,
                        load_library, match, match_records, rotate_inplace, rotate_workload,
                        stitch)
 

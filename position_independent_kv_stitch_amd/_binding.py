@@ -27,7 +27,7 @@ STYLES = {"half": 0, "interleaved": 1}
 
 # every entry point the header declares
 EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_attend", "pic_attend_latent",
-           "pic_plan_info",
+           "pic_attend_boundary", "pic_plan_info",
            "pic_plan_ranges", "pic_plan_destroy", "pic_registry_create", "pic_registry_add",
            "pic_registry_destroy", "pic_match", "pic_last_error")
 FP_KINDS = {"xxh64": 0, "sha256": 1}
@@ -79,6 +79,14 @@ class LatentArgs(C.Structure):
                 ("out_request_stride", C.c_int64), ("out_head_stride", C.c_int64),
                 ("num_q_heads", C.c_int32), ("layer", C.c_int32), ("scale", C.c_float),
                 ("sink_tokens", C.c_int32), ("sink_bias", C.c_float), ("reserved", C.c_int32)]
+
+
+class BoundaryArgs(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("q_row_stride", C.c_int64), ("q_head_stride", C.c_int64),
+                ("out", C.c_void_p), ("out_row_stride", C.c_int64),
+                ("out_head_stride", C.c_int64), ("num_q_heads", C.c_int32),
+                ("layer", C.c_int32), ("scale", C.c_float), ("boundary_k", C.c_int32),
+                ("sink_tokens", C.c_int32), ("sink_bias", C.c_float)]
 
 
 class Geom(C.Structure):
@@ -172,6 +180,9 @@ def _configure(lib):
     lib.pic_attend_latent.restype = C.c_int
     lib.pic_attend_latent.argtypes = [C.c_void_p, P(KvView), P(KvView), P(LatentArgs),
                                       C.c_void_p]
+    lib.pic_attend_boundary.restype = C.c_int
+    lib.pic_attend_boundary.argtypes = [C.c_void_p, P(KvView), P(KvView), P(BoundaryArgs),
+                                        C.c_void_p]
     lib.pic_plan_info.restype = C.c_int
     lib.pic_plan_info.argtypes = [C.c_void_p, P(PlanInfo)]
     lib.pic_plan_ranges.restype = C.c_int
@@ -522,6 +533,57 @@ def attend_latent(plan: Plan, pool_k, cache_k, q, *, layer: int, out=None,
     lib = plan._lib
     _check(lib.pic_attend_latent(plan.handle, C.byref(pv), C.byref(cv), C.byref(a),
                                  _stream_of(q, stream)), lib)
+    return out
+
+
+def boundary_row_count(plan: Plan, boundary_k: int) -> int:
+    """Boundary rows of a plan: min(k, length) per entry placed after 0."""
+    bounds, _ = plan.ranges()
+    return int(sum(min(boundary_k, int(e - b)) for _, b, e in bounds if b > 0))
+
+
+def attend_boundary(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: int,
+                    boundary_k: int = 16, out=None, scale: Optional[float] = None,
+                    sink_tokens: int = 0, sink_bias: float = 0.0, stream=None):
+    """Enqueue pic_attend_boundary (LegoLink boundary reconnection) at `layer`.
+    q: bf16 [boundary rows][q heads][row_dim] (rows as boundary_row_count
+    enumerates them); tensors as for attend().  Returns out, fp32 with q's
+    shape."""
+    torch = _torch()
+    if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
+        raise TypeError("q must be bf16 [boundary rows][q heads][row_dim]")
+    n = boundary_row_count(plan, boundary_k)
+    if q.shape[0] != n or q.shape[2] != plan.row_dim:
+        raise ValueError(f"q must have {n} boundary rows of {plan.row_dim} dims")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != q.shape or out.stride(-1) != 1:
+        raise TypeError("out must be fp32 with q's shape")
+    if plan.src_page_size:
+        if pool_k.dim() != 5 or pool_k.shape[1] < plan.src_n_pages:
+            raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
+        pv = _view(pool_k, pool_v, "paged-pool")
+    else:
+        if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+            raise PicError(PIC_ERR_RANGE, "pool tensor smaller than the plan needs")
+        pv = _view(pool_k, pool_v, "pool")
+    if plan.page_size:
+        if cache_k.shape[1] < plan.n_phys_pages or cache_k.shape[2] != plan.page_size:
+            raise ValueError("paged cache smaller than the plan's page pool")
+        cv = _view(cache_k, cache_v, "paged")
+    else:
+        if cache_k.shape[1] < plan.n_requests or cache_k.shape[2] < plan.capacity:
+            raise ValueError("contiguous cache smaller than requests x capacity")
+        cv = _view(cache_k, cache_v, "contig")
+    if not (0 <= layer < min(pool_k.shape[0], cache_k.shape[0])):
+        raise ValueError("layer beyond the tensors")
+    a = BoundaryArgs(q.data_ptr(), q.stride(0), q.stride(1), out.data_ptr(), out.stride(0),
+                     out.stride(1), q.shape[1], layer,
+                     float(plan.row_dim ** -0.5 if scale is None else scale), int(boundary_k),
+                     int(sink_tokens), float(sink_bias))
+    lib = plan._lib
+    _check(lib.pic_attend_boundary(plan.handle, C.byref(pv), C.byref(cv), C.byref(a),
+                                   _stream_of(q, stream)), lib)
     return out
 
 

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libpic_stitch.so")
 SOURCES = [os.path.join(CSRC, "stitch.hip"), os.path.join(CSRC, "attend.hip"),
-           os.path.join(CSRC, "attend_mla.hip"),
+           os.path.join(CSRC, "attend_mla.hip"), os.path.join(CSRC, "attend_boundary.hip"),
            os.path.join(CSRC, "cdc.hip"), os.path.join(CSRC, "plan.cpp"),
            os.path.join(CSRC, "attend_plan.cpp")]
 

@@ -150,4 +150,11 @@ struct pic_plan {
     std::vector<uint8_t> latent_host;  // the uploaded bytes (alive for the copy)
     size_t latent_off_blocks = 0, latent_off_items = 0, latent_off_reqs = 0;
     int32_t latent_n_items = 0, latent_n_blocks = 0;
+    // pic_attend_boundary work items (attend_boundary.hip), the same way
+    void *d_bnd = nullptr;
+    size_t bnd_bytes = 0;
+    int64_t bnd_key = -1;
+    std::vector<uint8_t> bnd_host;
+    size_t bnd_off[4] = {0, 0, 0, 0};  // blocks, block positions, items, entries
+    int32_t bnd_n_items = 0, bnd_n_entries = 0;
 };

@@ -38,7 +38,7 @@ STRUCTS = {
     "pic_entry": B.EntryC, "pic_request": B.RequestC, "pic_geom": B.Geom, "pic_attend_args": B.AttendArgs,
     "pic_kv_view": B.KvView, "pic_segment": B.SegmentC, "pic_plan_info_t": B.PlanInfo,
     "pic_cdc_config": B.CdcConfig, "pic_match_t": B.MatchRecord,
-    "pic_attend_latent_args": B.LatentArgs,
+    "pic_attend_latent_args": B.LatentArgs, "pic_attend_boundary_args": B.BoundaryArgs,
 }
 
 

@@ -1,0 +1,143 @@
+"""GPU parity of pic_attend_boundary (LegoLink boundary reconnection: the
+first boundary_k tokens of every relocated chunk attend causally over the
+stitched context, chunk keys turned on load) against the fp64 oracle.
+
+Tolerance, from the arithmetic (as for the latent attention): bf16 query and
+row elements multiply exactly on the matrix cores and accumulate in fp32,
+so a logit carries at most scale * (D + 1) * u * S_pj error (u = 2^-24,
+D = 128, S_pj = sum_d |q_jd k_pd|; the oracle's rows hold the bits the
+kernel turns on load).  Weights differ by a factor within exp(+-2 dz),
+times the fast exponential and online rescaling (< 1e-5) and the hi + lo
+bf16 split (< 2^-16); the value product and the merge add < 300 u.  So
+|out - oracle| <= 2 (2 dz + 1e-5 + 2^-16 + 300 u) max|V|, dz from the case's
+data.  The observed error is printed.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from parity_util import to_host
+from pic_workloads import (Request, Workload, decode_batch, normal_values, pool_values,
+                           random_small, with_paged_pool)
+
+pytestmark = pytest.mark.gpu
+U = 2.0 ** -24
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import position_independent_kv_stitch_amd  # noqa: F401
+    return torch
+
+
+def f64(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_case(torch, wl, group, k, seed, layer=0, sink_tokens=0, sink_bias=0.0, scale=0.09):
+    import position_independent_kv_stitch_amd as pic
+    pk, pv = pool_values(wl, seed=seed, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, seed + 10, "cuda:0")
+    cv = normal_values(wl.dst_shape(), wl.dtype, seed + 11, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    n = pic.boundary_row_count(plan, k)
+    rows = oracle.boundary_rows(wl, k)
+    assert n == len(rows)
+    if n == 0:
+        plan.destroy()
+        return 0.0, 0.0, 0
+    q = normal_values((n, wl.n_heads * group, wl.row_dim), wl.dtype, seed + 12, "cuda:0")
+    out = pic.attend_boundary(plan, pk, pv, ck, cv, q, layer=layer, boundary_k=k, scale=scale,
+                              sink_tokens=sink_tokens, sink_bias=sink_bias)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    L1 = slice(layer, layer + 1)
+    hq = to_host(q)
+    want = oracle.attend_boundary(wl, to_host(pk[L1]), to_host(pv[L1]), to_host(ck[L1]),
+                                  to_host(cv[L1]), hq, layer, k, scale=scale,
+                                  sink_tokens=sink_tokens, sink_bias=sink_bias, layer_base=layer)
+    keys = np.concatenate([to_host(pk[L1]).reshape(-1, wl.row_dim),
+                           to_host(ck[L1]).reshape(-1, wl.row_dim)])
+    vals = np.concatenate([to_host(pv[L1]).reshape(-1, wl.row_dim),
+                           to_host(cv[L1]).reshape(-1, wl.row_dim)])
+    s = np.abs(f64(hq)).reshape(-1, wl.row_dim) @ np.abs(f64(keys)).T
+    dz = scale * (wl.row_dim + 1) * U * float(s.max())
+    tol = 2 * (2 * dz + 1e-5 + 2.0 ** -16 + 300 * U) * float(np.abs(f64(vals)).max())
+    err = float(np.abs(got - want).max())
+    plan.destroy()
+    return err, tol, n
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_small(torch_cuda, seed):
+    style = "interleaved" if seed % 4 == 3 else "half"
+    paged = seed % 2 == 1
+    wl = random_small(500 + seed, dtype="bf16", style=style, paged=paged,
+                      n_requests=1 + seed % 3, n_layers=2, max_len=60 + 30 * (seed % 4))
+    if seed % 5 == 4:
+        wl = with_paged_pool(wl, page_size=16, seed=seed)
+    group = (1, 2, 4, 8)[seed % 4]
+    k = (16, 5, 1, 16)[seed % 4] if group < 8 else 16
+    sink = (4, -15.0) if seed % 2 == 0 else (0, 0.0)
+    say(f"boundary random seed={seed} style={style} paged={paged} group={group} k={k} sink={sink}")
+    err, tol, n = run_case(torch_cuda, wl, group, k, seed, layer=seed % 2, sink_tokens=sink[0],
+                           sink_bias=sink[1])
+    say(f"  rows {n}: max err {err:.3g} (bound {tol:.3g})")
+    assert err <= tol
+
+
+def test_long_k_and_short_entries(torch_cuda):
+    """boundary_k larger than some entries (rows = their length), k x group
+    = 128 (eight row tiles)."""
+    wl = random_small(777, dtype="bf16", n_requests=2, n_layers=1, max_len=40)
+    err, tol, n = run_case(torch_cuda, wl, 4, 32, 3)
+    say(f"boundary k=32 group=4: rows {n}, max err {err:.3g} (bound {tol:.3g})")
+    assert err <= tol
+
+
+def test_llama3_decode_batch_two_requests(torch_cuda):
+    """Two requests of the Llama-3-8B decode batch (8 chunks x 2048 behind a
+    128-token prefix, recompute_k 32, 16-token pages): k = 16, 32 query
+    heads, LegoLink damping; contexts of up to 14,464 positions."""
+    base = decode_batch(n_requests=2, n_layers=2)
+    say("boundary llama3 decode batch, 2 requests")
+    err, tol, n = run_case(torch_cuda, base, 4, 16, 5, layer=1, sink_tokens=4, sink_bias=-15.0,
+                           scale=128 ** -0.5)
+    say(f"  rows {n}: max err {err:.3g} (bound {tol:.3g})")
+    assert n == 2 * 8 * 16
+    assert err <= tol
+
+
+def test_errors(torch_cuda):
+    import position_independent_kv_stitch_amd as pic
+    wl = random_small(9, dtype="bf16", n_requests=1, n_layers=1)
+    plan = pic.Plan.from_workload(wl)
+    pk, pv = pool_values(wl, seed=1, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, 2, "cuda:0")
+    n = pic.boundary_row_count(plan, 17)
+    assert n > 0
+    q = normal_values((n, 16, wl.row_dim), wl.dtype, 3, "cuda:0")
+    with pytest.raises(pic.PicError, match="invalid_arg"):  # 17 x 8 query heads > 128 rows
+        pic.attend_boundary(plan, pk, pv, ck, ck, q, layer=0, boundary_k=17)
+    with pytest.raises(pic.PicError, match="invalid_arg"):  # f32 plans are refused
+        f32 = random_small(9, dtype="f32", n_requests=1, n_layers=1)
+        fplan = pic.Plan.from_workload(f32)
+        import ctypes as C
+        from position_independent_kv_stitch_amd import _binding as B
+        fk, fv = pool_values(f32, seed=1, device="cuda:0")
+        fc = normal_values(f32.dst_shape(), f32.dtype, 2, "cuda:0")
+        a = B.BoundaryArgs(q.data_ptr(), q.stride(0), q.stride(1), q.data_ptr(), 0, 0, 4, 0,
+                           0.1, 4, 0, 0.0)
+        B._check(fplan._lib.pic_attend_boundary(
+            fplan.handle, C.byref(B._view(fk, fv, "pool")), C.byref(B._view(fc, fc, "contig")),
+            C.byref(a), None), fplan._lib)

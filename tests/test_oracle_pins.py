@@ -806,3 +806,73 @@ def test_latent_attend_matches_library_attention_over_stitched_bf16_rows():
         qq[None], k[None].contiguous(), k[None, :, :ro].contiguous(),
         attn_mask=bias[None, None, :].expand(1, 16, L), scale=sc)[0].numpy()
     assert np.allclose(got[0], want, rtol=0, atol=1e-12)
+
+
+# -------------------------------------------- LegoLink boundary reconnection
+
+def test_boundary_rows_enumerate_relocated_entries():
+    wl = Workload("b", "f64", 1, 1, 8, 0, 8, "half", 1e4, True, pool_tokens=30,
+                  chunks=[Chunk(0, 10), Chunk(10, 20)], capacity=60,
+                  requests=[Request([Entry(0, 0, 10), Entry(1, 12, 3), Entry(1, 20, 20)])])
+    rows = oracle.boundary_rows(wl, 4)
+    assert rows == [(0, 1, 0, 12), (0, 1, 1, 13), (0, 1, 2, 14),
+                    (0, 2, 0, 20), (0, 2, 1, 21), (0, 2, 2, 22), (0, 2, 3, 23)]
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_boundary_attention_equals_decode_attention_at_each_position(style):
+    """Boundary token j of an entry at d attends exactly like a decode step
+    whose context ends at d + j (the decode oracle, an independent path),
+    damping included."""
+    H, D, G, L = 2, 8, 2, 40
+    rng = np.random.default_rng(40)
+    chunks = [Chunk(0, 9), Chunk(9, 12)]
+    entries = [Entry(1, 3, 12, 2), Entry(0, 20, 9)]
+    wl = Workload("b", "f64", 1, H, D, 0, D, style, 1e4, True, pool_tokens=21, chunks=chunks,
+                  requests=[Request(entries, None, L)], capacity=L)
+    pk = rng.standard_normal((1, 21, H, D))
+    pv = rng.standard_normal((1, 21, H, D))
+    ck = rng.standard_normal((1, 1, L, H, D))
+    cv = rng.standard_normal((1, 1, L, H, D))
+    rows = oracle.boundary_rows(wl, 5)
+    q = rng.standard_normal((len(rows), H * G, D))
+    got = oracle.attend_boundary(wl, pk, pv, ck, cv, q, 0, 5, sink_tokens=3, sink_bias=-4.0,
+                                 dtype="f64")
+    for b, (_, _, _, p) in enumerate(rows):
+        dec = Workload("b", "f64", 1, H, D, 0, D, style, 1e4, True, pool_tokens=21,
+                       chunks=chunks, requests=[Request(entries, None, p + 1)], capacity=L)
+        want = oracle.attend(dec, pk, pv, ck, cv, q[b:b + 1], 0, sink_tokens=3, sink_bias=-4.0)
+        assert np.allclose(got[b], want[0], atol=1e-12)
+
+
+def test_boundary_attention_matches_library_sdpa_bf16():
+    """bf16 storage: equals torch's scaled dot product attention (fp64, CPU)
+    over the rows the oracle's stitch stores, with a causal limit per row."""
+    import torch
+    from parity_util import to_host
+    from pic_workloads import normal_values
+    H, D, G, L = 2, 128, 4, 96
+    chunks = [Chunk(0, 30), Chunk(30, 40)]
+    entries = [Entry(0, 0, 30), Entry(1, 40, 40, 3)]
+    wl = Workload("b", "bf16", 1, H, D, 0, D, "half", 5e5, True, pool_tokens=70, chunks=chunks,
+                  requests=[Request(entries, None, L)], capacity=L)
+    pk = to_host(normal_values((1, 70, H, D), "bf16", 1))
+    pv = to_host(normal_values((1, 70, H, D), "bf16", 2))
+    ck = to_host(normal_values((1, 1, L, H, D), "bf16", 3))
+    cv = to_host(normal_values((1, 1, L, H, D), "bf16", 4))
+    rows = oracle.boundary_rows(wl, 16)
+    q = to_host(normal_values((len(rows), H * G, D), "bf16", 5))
+    got = oracle.attend_boundary(wl, pk, pv, ck, cv, q, 0, 16, scale=0.09)
+    sk, sv = ck.copy(), cv.copy()
+    assert oracle.stitch(wl, pk, pv, sk, sv) == "ok"
+    K = torch.from_numpy(oracle.ref._to_f64(sk[0, 0]))  # [L][H][D]
+    V = torch.from_numpy(oracle.ref._to_f64(sv[0, 0]))
+    for b, (_, _, _, p) in enumerate(rows):
+        qq = torch.from_numpy(oracle.ref._to_f64(q[b])).view(H, G, 1, D)
+        mask = torch.full((1, 1, 1, L), float("-inf"), dtype=torch.float64)
+        mask[..., :p + 1] = 0.0
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qq, K.permute(1, 0, 2)[:, None].expand(H, G, L, D).contiguous(),
+            V.permute(1, 0, 2)[:, None].expand(H, G, L, D).contiguous(),
+            attn_mask=mask, scale=0.09).reshape(H * G, D).numpy()
+        assert np.allclose(got[b], want, rtol=0, atol=1e-12), b
