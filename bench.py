@@ -242,11 +242,18 @@ def setup_boundary(name, torch, pic):
                                 out=out[layer], scale=wl.row_dim ** -0.5, sink_tokens=4,
                                 sink_bias=-15.0)
 
-    # every relocated entry's rows read the K and V rows of context [0, d + k) once
+    # the method must read each request's K and V rows of [0, last boundary
+    # position] once (all its boundary rows share them), the queries, and
+    # write the outputs
     bounds, _ = plan.ranges()
     reloc = [(int(b), int(e - b)) for _, b, e in bounds if b > 0]
-    ctx = sum(d + min(k, ln) for d, ln in reloc)
+    last = {}
+    for r, b, e in bounds:
+        if b > 0:
+            last[int(r)] = max(last.get(int(r), 0), int(b) + min(k, int(e - b)))
+    ctx = sum(last.values())
     row_bytes = 2 * wl.n_heads * wl.row_dim * 2
+    qo_bytes = n * wl.n_heads * group * wl.row_dim * (2 + 4)
     pairs = sum(sum(d + j + 1 for j in range(min(k, ln))) for d, ln in reloc)  # (row, position)
     flops = pairs * wl.n_heads * group * 2 * 2 * wl.row_dim * L
     cfg = {"workload": WORKLOADS[name], "storage": wl.dtype, "layers": L,
@@ -254,7 +261,7 @@ def setup_boundary(name, torch, pic):
            "requests": len(wl.requests), "relocated_entries": len(reloc), "boundary_k": k,
            "boundary_rows": n, "context_positions_read": ctx, "page_size": wl.page_size,
            "sink_tokens": 4, "sink_bias": -15.0, "parallelism": "single-gpu"}
-    return {"wl": wl, "step": step, "bytes": ctx * row_bytes * L, "token_layers": n * L,
+    return {"wl": wl, "step": step, "bytes": (ctx * row_bytes + qo_bytes) * L, "token_layers": n * L,
             "launches": L, "flops": flops,
             "kernel": "bnd_block_kernel<half> + bnd_combine_kernel (one pic_attend_boundary)",
             "plan": plan, "config": cfg}

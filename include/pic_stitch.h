@@ -383,19 +383,21 @@ typedef struct pic_attend_boundary_args {
     int32_t num_q_heads;    /* a multiple of num_heads, at most 8x */
     int32_t layer;
     float scale;
-    int32_t boundary_k;     /* boundary tokens per relocated entry (the EPIC listing: 16);
-                               boundary_k x (num_q_heads / num_heads) <= 128 */
+    int32_t boundary_k;     /* boundary tokens per relocated entry, >= 1 (the EPIC
+                               listing: 16) */
     int32_t sink_tokens;    /* LegoLink damping (0 = off) */
     float sink_bias;
 } pic_attend_boundary_args;
 
 /*
  * pic_attend_boundary -- enqueue the boundary reconnection of every
- * relocated entry of a plan at one layer (see above).  bf16 plans with K
- * and V head rows of 128 dims and a rotary slice on 8-dim pieces
- * (PIC_ERR_INVALID_ARG, PIC_ERR_ALIGN); q rows 16-byte aligned
- * (PIC_ERR_ALIGN); every boundary row's positions inside its request's
- * context and mapped pages (PIC_ERR_RANGE); in-place plans refused
+ * relocated entry of a plan at one layer (see above).  All boundary rows of
+ * a request read its context together.  bf16 plans with K and V head rows
+ * of 128 dims and a rotary slice on 8-dim pieces (PIC_ERR_INVALID_ARG,
+ * PIC_ERR_ALIGN); q rows 16-byte aligned (PIC_ERR_ALIGN); every boundary
+ * row's positions inside its request's context and mapped pages
+ * (PIC_ERR_RANGE; also for more than 65535 requests with relocated entries
+ * or a launch beyond 2^31 threads); in-place plans refused
  * (PIC_ERR_STATE).  A plan without relocated entries enqueues nothing.  The
  * work items for a launch shape are built on the host and uploaded with the
  * plan on first use (a later call with another boundary_k waits for the

@@ -12,23 +12,28 @@
 // request's own cache) and its own chunk's earlier tokens.  The LegoLink
 // damping of pseudo-sinks is the same optional logit bias as in pic_attend.
 //
-// Work: per relocated entry, its boundary rows (tokens j < min(k, length) x
-// the GQA group's query heads) form up to 8 row tiles of 16; a workgroup is
-// one wave per row tile, for one KV head and one work item (a run of the
-// entry's context [0, d + k)).  Items are cut per launch so that every
-// workgroup has about the same number of positions.  Per step of 32
-// positions (the latent kernel's scheme, attend_mla.hip):
-//   - the step's K and V rows of the KV head (16 KB) go from HBM straight
+// Work: all boundary rows of a request (tokens x the GQA group's query heads)
+// share one pass over the request's context.  A workgroup of 8 waves takes
+// one KV head, one work item (a run of positions of the request, cut on the
+// host per launch shape) and up to 256 rows: each wave holds two row tiles of
+// 16 adjacent rows (more rows take more row sets, which read the same rows
+// on the same XCD at about the same time).  Per step of 64 positions:
+//   - the step's K and V rows of the KV head (32 KB) go from HBM straight
 //     into LDS (global_load_lds_dwordx4), in the MFMA A-fragment layout,
-//     double-buffered across steps;
-//   - rotary pieces of moved chunk rows are turned in LDS (fp64, rounded
-//     to bf16 by the stitch's own code, rotate.hpp);
-//   - S^T = K Q^T (v_mfma_f32_16x16x32_bf16, queries in registers), causal
-//     limit per row, online softmax per row;
-//   - O^T += V^T P^T with the weights from the S^T D registers (hi + lo
-//     bf16) and V^T by transposing LDS reads (ds_read_b64_tr_b16).
-// A partial (max, sum, accumulator) per (item, KV head, row) is merged by
-// bnd_combine_kernel.
+//     double-buffered across steps; each wave stages one 16-position tile's
+//     K or V, its row addresses from per-tile records built once per block;
+//   - rotary pieces of moved chunk rows are turned in LDS (fp64, rounded to
+//     bf16 by the stitch's own code, rotate.hpp), with the block's shift
+//     tables copied to LDS once;
+//   - S^T = K Q^T (v_mfma_f32_16x16x32_bf16): each K fragment is read once
+//     and used for both of the wave's row tiles; causal limit per row;
+//   - online softmax per row in log2 units, with a lazy running max (the
+//     accumulator is rescaled only when a logit passes the reference by
+//     2^12), weights split into hi + lo bf16;
+//   - O^T += V^T P^T with the weights taken from the S^T D registers and
+//     each V^T fragment (transposing LDS reads) used for both row tiles.
+// Steps past every row of a wave are skipped by that wave.  A partial (max,
+// sum, accumulator) per (item, KV head, row) is merged by bnd_combine_kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -48,51 +53,59 @@ namespace {
 constexpr int kDim = 128;                 // head row
 constexpr int kKSteps = kDim / 32;        // MFMA k-steps
 constexpr int kDTiles = kDim / 16;        // output tiles of 16 dims
-constexpr int kStepPos = 32;              // positions per step: two 16-position tiles
-constexpr int kKSlabs = 2 * kKSteps;      // 1 KB slabs of K per step (then as many of V)
-constexpr int kSlabs = 2 * kKSlabs;
-constexpr int kMaxWaves = 8;              // row tiles (of 16 rows) per entry at most
+#ifndef PIC_BND_POS_TILES
+#define PIC_BND_POS_TILES 4
+#endif
+constexpr int kPT = PIC_BND_POS_TILES;   // 16-position tiles per step (2 or 4)
+constexpr int kStepPos = 16 * kPT;        // positions per step
+constexpr int kSlabs = 2 * kKSteps * kPT; // 1 KB slabs per step: K, then V
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kMaxTT = 2;                 // row tiles per wave at most (registers)
 constexpr int kItemTiles = 64;            // map tiles per block at most
 constexpr int kBlockPos = 4096;           // positions per block at most
-constexpr int kCombineThreads = 128;
+constexpr int kBlockTabs = 4;             // shift tables per block at most (kept in LDS)
+constexpr int kMaxHalf = kDim / 2;        // rotary planes at most
+constexpr float kLazy = 12.f;             // running-max slack of the online softmax (log2 units)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxItems = 64;            // work items per request at most (one combine wave)
 
-constexpr uint32_t kMetaDamp = 1u << 31;      // LegoLink bias applies
-constexpr uint32_t kMetaCs = (1u << 30) - 1;  // shift table + 1 (0: row not turned)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
-// One relocated entry: its boundary rows start at row0 (n_tok tokens), its
-// token j sits at position pos0 + j of request `request`, its work items
-// are [item0, item1).
-struct BndEntry {
-    int32_t request;
+// A request with boundary rows: its boundary tokens are global rows [row0,
+// row0 + n_tok) (entry by entry, token by token), the last position each
+// sees is limit[row0 + i]; its work items are [item0, item1).
+struct BndReq {
     int32_t row0;
     int32_t n_tok;
-    int32_t pos0;
     int32_t item0;
     int32_t item1;
-    int32_t pad[2];
 };
 
-// A work item: blocks [block0, block1) of entry `entry`.
+// A work item: blocks [block0, block1) of request `req` (index into the
+// request table), covering context positions [pos_a, pos_b).
 struct BndItem {
-    int32_t entry;
+    int32_t req;
     int32_t block0;
     int32_t block1;
-    int32_t pad;
+    int32_t pos_a;
 };
 
 struct BndArgs {
     const AttnTile *tiles;    // blocks' tiles (tok0: position in the block)
     const AttnBlock *blocks;  // request, tile0, ntiles, ntok
     const int32_t *block_pos; // context position of every block's first token
+    const int32_t *block_tabs;  // [block][kBlockTabs] shift tables its tiles use (-1: none)
     const BndItem *items;
-    const BndEntry *entries;
+    const BndReq *reqs;
+    const int32_t *limit;     // last position every boundary token sees
     const double *cs;
     const uint16_t *pool_k, *pool_v, *cache_k, *cache_v;
     int64_t s_layer, s_tok, s_head, s_page;
@@ -101,9 +114,11 @@ struct BndArgs {
     int64_t q_row, q_head;
     float *out;
     int64_t o_row, o_head;
-    float *part_acc;  // [item][kv head][kMaxWaves * 16 rows][kDim]
-    float *part_ml;   // [item][kv head][kMaxWaves * 16 rows][2]
+    float *part_acc;  // [item][kv head][row slots][kDim]
+    float *part_ml;   // [item][kv head][row slots][2]
     int32_t n_items, n_kv_heads, group, num_q_heads;
+    int32_t row_slots;  // rows per (item, KV head): the most rows of a request, in tiles
+    int32_t n_sets;     // row sets per item
     int32_t rope_offset, half_r;
     float scale;
     int32_t sink_tokens;
@@ -114,111 +129,185 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// max over the four lanes of a row (lanes r, r + 16, r + 32, r + 48): the
+// 32-lane swap pairs lane i with i ^ 32, the 16-lane swap i with i ^ 16
+__device__ __forceinline__ float row_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Row offset (elements, layer and head included) and meta of position pi of
-// a block whose tiles are s_tiles[0, ntiles); *pool tells the source.
-__device__ __forceinline__ int64_t bnd_row(const BndArgs &a, const AttnTile *s_tiles, int ntiles,
-                                           int pi, int32_t layer, int h, uint32_t *meta,
-                                           bool *pool) {
-    int lo = 0, hi = ntiles - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_tiles[mid].tok0 <= pi) lo = mid;
-        else hi = mid - 1;
-    }
-    const AttnTile &T = s_tiles[lo];
-    const int t = pi - T.tok0;
+// A map tile as the staging reads it: the row of block position pi is
+// off0 + pi * token stride (elements, layer and head included) in the pool
+// (info bit kInfoPool) or the cache; info also holds the tile's shift-table
+// slot + 1 (bits 0-2, 0: rows not turned) and how many of its first
+// positions take the damping bias (bits 8-31).
+struct StageTile {
+    int64_t off0;
+    int32_t tok0;
+    uint32_t info;
+};
+constexpr uint32_t kInfoPool = 1u << 3;
+
+__device__ __forceinline__ StageTile stage_tile(const BndArgs &a, const AttnTile &T, int slot,
+                                                int32_t layer, int h) {
     const int64_t L = layer;
-    uint32_t m = T.cs_idx >= 0 ? static_cast<uint32_t>(T.cs_idx + 1) : 0u;
-    if (T.sink_dist + t < a.sink_tokens) m |= kMetaDamp;
-    *meta = m;
+    int64_t off0;
+    bool pool = true;
     switch (T.kind) {
         case kPoolRows:
-            *pool = true;
-            return L * a.s_layer + (T.a + t) * a.s_tok + h * a.s_head;
+            off0 = L * a.s_layer + h * a.s_head + (T.a - T.tok0) * a.s_tok;
+            break;
         case kPoolPages:
-            *pool = true;
-            return L * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b + t) * a.s_tok +
-                   h * a.s_head;
+            off0 = L * a.s_layer + h * a.s_head + T.a * a.s_page +
+                   static_cast<int64_t>(T.b - T.tok0) * a.s_tok;
+            break;
         case kCacheRows:
-            *pool = false;
-            return L * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b + t) * a.c_tok +
-                   h * a.c_head;
+            pool = false;
+            off0 = L * a.c_layer + h * a.c_head + T.a * a.c_req +
+                   static_cast<int64_t>(T.b - T.tok0) * a.c_tok;
+            break;
         default:
-            *pool = false;
-            return L * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b + t) * a.c_tok +
-                   h * a.c_head;
+            pool = false;
+            off0 = L * a.c_layer + h * a.c_head + T.a * a.c_page +
+                   static_cast<int64_t>(T.b - T.tok0) * a.c_tok;
+            break;
     }
+    // positions tok0 .. tok0 + damp - 1 lie within sink_tokens of their chunk's start
+    const int64_t damp = std::min<int64_t>(std::max<int64_t>(int64_t{a.sink_tokens} - T.sink_dist, 0),
+                                           (1 << 24) - 1);
+    const uint32_t info = static_cast<uint32_t>(slot + 1) | (pool ? kInfoPool : 0u) |
+                          (static_cast<uint32_t>(damp) << 8);
+    return StageTile{off0, T.tok0, info};
 }
 
-template <int STYLE>
-__global__ void __launch_bounds__(64 * kMaxWaves) bnd_block_kernel(const BndArgs a, int32_t layer) {
-    // staged step: slab j < kKSlabs is K, k-step j >> 1, position tile j & 1;
-    // slab kKSlabs + j the same for V.  Slot 16 g + p holds dims 32 s + 8 g ..
-    // + 8 of position 16 tau + p (the A fragment of lane 16 g + p).
+// Rows per workgroup: 8 waves x TT tiles x 16.
+template <int STYLE, int TT>
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2)))
+bnd_block_kernel(const BndArgs a, int32_t layer) {
+    // staged step: slab kind * kKSteps * kPT + s * kPT + tau (kind 0: K, 1:
+    // V) holds dims 32 s .. 32 s + 31 of positions 16 tau .. 16 tau + 15; its
+    // slot 16 g + p holds dims 32 s + 8 g .. + 8 of position 16 tau + p (the
+    // A fragment of lane 16 g + p)
     __shared__ __attribute__((aligned(16))) uint4 s_stage[2][kSlabs * 64];
-    __shared__ AttnTile s_tiles[kItemTiles];
-    __shared__ uint32_t s_pmeta[2][kStepPos];
+    __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kMaxHalf];  // block's shift tables
+    __shared__ StageTile s_tiles[kItemTiles];
+    __shared__ uint32_t s_pslot[2][kStepPos];                       // shift-table slot + 1 (0: not turned)
+    __shared__ __attribute__((aligned(16))) float s_pbias[2][kStepPos];  // damping, -inf past the block
 
-    const int item = blockIdx.x / a.n_kv_heads;
-    const int h = blockIdx.x - item * a.n_kv_heads;
+    // grid: runs of 8 (item, KV head) pairs c, each run once per row set;
+    // workgroup w goes to XCD w % 8, so every set of one pair shares an XCD
+    // (and its L2) and reads the same rows close together in time
+    const int w = blockIdx.x;
+    const int c = (w / (8 * a.n_sets)) * 8 + (w & 7);
+    const int set = (w >> 3) % a.n_sets;
+    if (c >= a.n_items * a.n_kv_heads) return;
+    const int h = c % a.n_kv_heads;
+    const int item = c / a.n_kv_heads;
     const BndItem I = a.items[item];
-    const BndEntry E = a.entries[I.entry];
+    const BndReq Q = a.reqs[I.req];
+    const int n_rows = Q.n_tok * a.group;  // row = token i x G + query head gh of KV head h
+    const int set_row0 = set * (kWaves * TT * 16);
+    if (set_row0 >= n_rows) return;  // uniform over the workgroup
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
-    const int W = blockDim.x >> 6;
-    const int n_rows = E.n_tok * a.group;  // rows: token j, query head h G + gh at j G + gh
-    const int my_row = 16 * wave + r16;    // this lane's row (as a D column)
-    const bool row_live = my_row < n_rows;
-    const int my_tok = row_live ? my_row / a.group : 0;
-    const int my_limit = E.pos0 + my_tok;  // last position the row sees
-    const bool wave_live = 16 * wave < n_rows;
 
-    // query fragments (B of S^T): row r16 of the wave's tile, dims 32 s + 8 g
-    bf16x8 qf[kKSteps];
-    {
-        const uint16_t *qr =
-            a.q + static_cast<int64_t>(E.row0 + my_tok) * a.q_row +
-            static_cast<int64_t>(h * a.group + (row_live ? my_row % a.group : 0)) * a.q_head;
+    // the wave's row tiles: rows set_row0 + 16 (TT wave + k) + r16, adjacent
+    // rows (mostly one entry) so that they end at about the same step
+    bf16x8 qf[TT][kKSteps];
+    int limit[TT];  // the row's last position (rows past the request's: none)
+#pragma unroll
+    for (int k = 0; k < TT; k++) {
+        const int row = set_row0 + 16 * (TT * wave + k) + r16;
+        const bool live = row < n_rows;
+        const int tok = live ? row / a.group : 0;
+        limit[k] = live ? a.limit[Q.row0 + tok] : -1;
+        const uint16_t *qr = a.q + static_cast<int64_t>(Q.row0 + tok) * a.q_row +
+                             static_cast<int64_t>(h * a.group + (live ? row % a.group : 0)) *
+                                 a.q_head;
 #pragma unroll
         for (int s = 0; s < kKSteps; s++)
-            qf[s] = as_bf16x8(row_live ? *reinterpret_cast<const uint4 *>(qr + 32 * s + 8 * g)
-                                       : make_uint4(0u, 0u, 0u, 0u));
+            qf[k][s] = as_bf16x8(live ? *reinterpret_cast<const uint4 *>(qr + 32 * s + 8 * g)
+                                      : make_uint4(0u, 0u, 0u, 0u));
     }
-    f32x4 acc[kDTiles];
+    // per tile, the latest last position of its rows: a step past it is
+    // skipped (rows past the request: -1)
+    int tile_last[TT];
 #pragma unroll
-    for (int t = 0; t < kDTiles; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int k = 0; k < TT; k++) {
+        int x = limit[k];
+        for (int m = 1; m < 16; m <<= 1) x = max(x, __shfl_xor(x, m, 64));
+        tile_last[k] = x;
+    }
+    const float scale2 = a.scale * kLog2e;  // logits in log2 units (exp2 weights)
+    const float bias2 = a.sink_bias * kLog2e;
+
+    f32x4 acc[TT][kDTiles];
+    float m_run[TT], l_run[TT];
+#pragma unroll
+    for (int k = 0; k < TT; k++) {
+#pragma unroll
+        for (int t = 0; t < kDTiles; t++) acc[k][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m_run[k] = -INFINITY;
+        l_run[k] = 0.f;
+    }
+    const int half_r = a.half_r;
+    // staging roles: the wave loads position tile my_tau of every step, the
+    // slabs my_j0 .. my_j0 + kSlabsPerWave - 1 of that tile's K then V slabs
+    constexpr int kWavesPerTau = kWaves / kPT;
+    constexpr int kSlabsPerWave = 2 * kKSteps / kWavesPerTau;
+    const int my_tau = wave / kWavesPerTau;
+    const int my_j0 = (wave % kWavesPerTau) * kSlabsPerWave;
 
     for (int b = I.block0; b < I.block1; b++) {
         const AttnBlock B = a.blocks[b];
         const int bpos = a.block_pos[b];
         __syncthreads();
-        if (tid < B.ntiles) s_tiles[tid] = a.tiles[B.tile0 + tid];
+        if (tid < B.ntiles) {
+            const AttnTile T = a.tiles[B.tile0 + tid];
+            int sl = -1;
+#pragma unroll
+            for (int j = 0; j < kBlockTabs; j++)
+                if (T.cs_idx >= 0 && a.block_tabs[kBlockTabs * b + j] == T.cs_idx) sl = j;
+            s_tiles[tid] = stage_tile(a, T, sl, layer, h);
+        }
+        for (int i = tid; i < kBlockTabs * half_r; i += 64 * kWaves) {
+            const int j = i / half_r, pl = i - j * half_r;
+            const int tab = a.block_tabs[kBlockTabs * b + j];
+            if (tab >= 0) {
+                const double *src = a.cs + (static_cast<int64_t>(tab) * half_r + pl) * 2;
+                s_cs[j][pl] = make_double2(src[0], src[1]);
+            }
+        }
         __syncthreads();
 
+        // tile holding the lane's position; positions only grow within a
+        // block, so the search moves forward
+        int cur = 0;
         auto stage = [&](int p0, int bf) {
+            int pi = p0 + 16 * my_tau + r16;
+            const bool valid = pi < B.ntok;
+            if (!valid) pi = p0;
+            while (cur + 1 < B.ntiles && s_tiles[cur + 1].tok0 <= pi) cur++;
+            const StageTile T = s_tiles[cur];
+            const bool pool = T.info & kInfoPool;
+            const int64_t off = T.off0 + static_cast<int64_t>(pi) * (pool ? a.s_tok : a.c_tok);
+            if (my_j0 == 0 && g == 0) {
+                const bool damp = static_cast<uint32_t>(pi - T.tok0) < (T.info >> 8);
+                s_pslot[bf][16 * my_tau + r16] = valid ? (T.info & 7u) : 0u;
+                s_pbias[bf][16 * my_tau + r16] = valid ? (damp ? bias2 : 0.f) : -INFINITY;
+            }
+            const uint16_t *kr = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
+            const uint16_t *vr = (pool ? a.pool_v : a.cache_v) + off + 8 * g;
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++) {
-                int pi = p0 + 16 * tau + r16;
-                const bool valid = pi < B.ntok;
-                if (!valid) pi = p0;
-                uint32_t meta;
-                bool pool;
-                const int64_t off = bnd_row(a, s_tiles, B.ntiles, pi, layer, h, &meta, &pool);
-                if (wave == 0 && g == 0) s_pmeta[bf][16 * tau + r16] = valid ? meta : 0u;
-                const uint16_t *kr = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
-                const uint16_t *vr = (pool ? a.pool_v : a.cache_v) + off + 8 * g;
-                for (int j = 2 * wave + tau; j < kSlabs; j += 2 * W) {
-                    const int s = (j % kKSlabs) >> 1;
-                    const uint16_t *src = (j < kKSlabs ? kr : vr) + 32 * s;
-                    __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&s_stage[bf][j * 64]),
-                                                     16, 0, 0);
-                }
+            for (int i = 0; i < kSlabsPerWave; i++) {
+                const int jl = my_j0 + i;  // kind * kKSteps + s
+                const int kind = jl / kKSteps, s = jl % kKSteps;
+                const uint16_t *src = (kind == 0 ? kr : vr) + 32 * s;
+                const int slab = kind * kKSteps * kPT + s * kPT + my_tau;
+                __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&s_stage[bf][slab * 64]),
+                                                 16, 0, 0);
             }
         };
 
@@ -229,167 +318,246 @@ __global__ void __launch_bounds__(64 * kMaxWaves) bnd_block_kernel(const BndArgs
             __syncthreads();
             if (p0 + kStepPos < B.ntok) stage(p0 + kStepPos, bf ^ 1);
 
-            // ---- turn the rotary pieces of moved chunk rows (K slabs)
-            const int pieces = a.half_r / 8;  // (x, y) piece pairs per position
-            for (int t = tid; t < pieces * kStepPos; t += 64 * W) {
-                const int pos = t / pieces, m = t - pos * pieces;
-                const uint32_t cs1 = s_pmeta[bf][pos] & kMetaCs;
-                if (cs1 == 0u) continue;
-                const double *tab = a.cs + static_cast<int64_t>(cs1 - 1) * a.half_r * 2;
+            // ---- turn the rotary pieces of moved chunk rows (K slabs): unit
+            // (position, 8-plane group m, half hh) turns 4 planes
+            const int units = (half_r / 4) * kStepPos;
+            for (int u = tid; u < units; u += 64 * kWaves) {
+                const int pos = u / (half_r / 4), rem = u - pos * (half_r / 4);
+                const int m = rem >> 1, hh = rem & 1;
+                const uint32_t slot1 = s_pslot[bf][pos];
+                if (slot1 == 0u) continue;
+                const double2 *tab = s_cs[slot1 - 1];
                 const int tau = pos >> 4, pp = pos & 15;
                 if constexpr (STYLE == PIC_ROPE_HALF) {
-                    // x of planes 8 m .. 8 m + 7 in piece (ro + 8 m) / 8, y in
-                    // piece (ro + half_r + 8 m) / 8
-                    const int px = (a.rope_offset + 8 * m) >> 3, py = px + (a.half_r >> 3);
-                    uint4 &kx = s_stage[bf][(2 * (px >> 2) + tau) * 64 + 16 * (px & 3) + pp];
-                    uint4 &ky = s_stage[bf][(2 * (py >> 2) + tau) * 64 + 16 * (py & 3) + pp];
-                    uint32_t xw[4] = {kx.x, kx.y, kx.z, kx.w}, yw[4] = {ky.x, ky.y, ky.z, ky.w};
+                    // x of planes 8 m + 4 hh .. + 4 in words 2 hh, 2 hh + 1 of
+                    // piece (ro + 8 m) / 8; y the same in piece (ro + half_r + 8 m) / 8
+                    const int px = (a.rope_offset + 8 * m) >> 3, py = px + (half_r >> 3);
+                    uint2 *kx = reinterpret_cast<uint2 *>(
+                                    &s_stage[bf][((px >> 2) * kPT + tau) * 64 + 16 * (px & 3) + pp]) + hh;
+                    uint2 *ky = reinterpret_cast<uint2 *>(
+                                    &s_stage[bf][((py >> 2) * kPT + tau) * 64 + 16 * (py & 3) + pp]) + hh;
+                    const uint2 xv = *kx, yv = *ky;
+                    uint32_t xw[2] = {xv.x, xv.y}, yw[2] = {yv.x, yv.y};
 #pragma unroll
-                    for (int q = 0; q < 8; q++) {
-                        const double c = tab[2 * (8 * m + q)], sn = tab[2 * (8 * m + q) + 1];
+                    for (int q = 0; q < 4; q++) {
+                        const double2 cs = tab[8 * m + 4 * hh + q];
                         uint32_t &wx = xw[q >> 1], &wy = yw[q >> 1];
                         const int sh = 16 * (q & 1);
                         const double x = static_cast<double>(__uint_as_float(((wx >> sh) & 0xFFFFu) << 16));
                         const double y = static_cast<double>(__uint_as_float(((wy >> sh) & 0xFFFFu) << 16));
-                        const uint32_t nx = f64_to_bf16(x * c - y * sn), ny = f64_to_bf16(x * sn + y * c);
+                        const uint32_t nx = f64_to_bf16(x * cs.x - y * cs.y);
+                        const uint32_t ny = f64_to_bf16(x * cs.y + y * cs.x);
                         wx = (wx & ~(0xFFFFu << sh)) | (nx << sh);
                         wy = (wy & ~(0xFFFFu << sh)) | (ny << sh);
                     }
-                    kx = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-                    ky = make_uint4(yw[0], yw[1], yw[2], yw[3]);
+                    *kx = make_uint2(xw[0], xw[1]);
+                    *ky = make_uint2(yw[0], yw[1]);
                 } else {
-                    // whole pairs: piece (ro / 8) + 2 m and the next hold
-                    // planes 8 m .. 8 m + 7
+                    // whole pairs: piece (ro / 8) + 2 m + hh holds planes
+                    // 8 m + 4 hh .. + 4
+                    const int pc = (a.rope_offset >> 3) + 2 * m + hh;
+                    uint4 &kw = s_stage[bf][((pc >> 2) * kPT + tau) * 64 + 16 * (pc & 3) + pp];
+                    uint32_t wv[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
-                    for (int half = 0; half < 2; half++) {
-                        const int pc = (a.rope_offset >> 3) + 2 * m + half;
-                        uint4 &kw = s_stage[bf][(2 * (pc >> 2) + tau) * 64 + 16 * (pc & 3) + pp];
-                        uint32_t w[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-                        for (int q = 0; q < 4; q++) {
-                            const int plane = 8 * m + 4 * half + q;
-                            const double c = tab[2 * plane], sn = tab[2 * plane + 1];
-                            const double x = bf16_lo(w[q]), y = bf16_hi(w[q]);
-                            w[q] = f64_to_bf16(x * c - y * sn) | (f64_to_bf16(x * sn + y * c) << 16);
-                        }
-                        kw = make_uint4(w[0], w[1], w[2], w[3]);
+                    for (int q = 0; q < 4; q++) {
+                        const double2 cs = tab[8 * m + 4 * hh + q];
+                        const double x = bf16_lo(wv[q]), y = bf16_hi(wv[q]);
+                        wv[q] = f64_to_bf16(x * cs.x - y * cs.y) |
+                                (f64_to_bf16(x * cs.y + y * cs.x) << 16);
                     }
+                    kw = make_uint4(wv[0], wv[1], wv[2], wv[3]);
                 }
             }
             __syncthreads();
-            if (!wave_live) continue;  // (the wave still joins every barrier)
 
-            // ---- logits S^T (16 positions x the wave's 16 rows) per tile
+            const int step_pos = bpos + p0;  // context position of the step's first row
+            bool any = false;
+#pragma unroll
+            for (int k = 0; k < TT; k++) any = any || tile_last[k] >= step_pos;
+            if (!any) continue;  // (the wave still joins every barrier)
+            // every tile of an active wave is computed, without branches, so
+            // that the matrix and vector work of its tiles interleave; rows
+            // past their last position are masked to weight 0
+
+            // ---- logits S^T: each K fragment serves every tile
             const uint4 *stg = s_stage[bf];
-            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 st[TT][kPT];
 #pragma unroll
-            for (int s = 0; s < kKSteps; s++)
+            for (int k = 0; k < TT; k++)
 #pragma unroll
-                for (int tau = 0; tau < 2; tau++)
-                    st[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(stg[(2 * s + tau) * 64 + lane]), qf[s], st[tau], 0, 0, 0);
-            float sc[8];
+                for (int tau = 0; tau < kPT; tau++) st[k][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // (K fragments read one k-step ahead of their products, fenced so
+            // that the compiler keeps two k-steps of them in registers, not four)
+            bf16x8 kf[kPT];
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++)
+            for (int tau = 0; tau < kPT; tau++) kf[tau] = as_bf16x8(stg[tau * 64 + lane]);
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int pos = 16 * tau + 4 * g + i;
-                    const int ctx = bpos + p0 + pos;  // context position
-                    float x = st[tau][i] * a.scale;
-                    if (s_pmeta[bf][pos] & kMetaDamp) x += a.sink_bias;
-                    const bool ok = row_live && p0 + pos < B.ntok && ctx <= my_limit;
-                    sc[4 * tau + i] = ok ? x : -INFINITY;
+            for (int s = 0; s < kKSteps; s++) {
+                bf16x8 kn[kPT];
+                if (s + 1 < kKSteps) {
+#pragma unroll
+                    for (int tau = 0; tau < kPT; tau++)
+                        kn[tau] = as_bf16x8(stg[((s + 1) * kPT + tau) * 64 + lane]);
                 }
-            float mx = sc[0];
 #pragma unroll
-            for (int k = 1; k < 8; k++) mx = fmaxf(mx, sc[k]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);
-            // a row may have no position yet (all masked): keep it empty
-            const float alpha = m_new == -INFINITY ? 1.f : __expf(m_run - m_new);
-            float pw[8], psum = 0.f;
+                for (int tau = 0; tau < kPT; tau++)
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
-                pw[k] = m_new == -INFINITY ? 0.f : __expf(sc[k] - m_new);
-                psum += pw[k];
+                    for (int k = 0; k < TT; k++)
+                        st[k][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[tau], qf[k][s], st[k][tau], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (s + 1 < kKSteps) {
+#pragma unroll
+                    for (int tau = 0; tau < kPT; tau++) kf[tau] = kn[tau];
+                }
             }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
+            // position terms shared by every tile (D registers: positions
+            // 16 tau + 4 g + i)
+            f32x4 pb[kPT];
 #pragma unroll
-            for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
-            uint32_t hi[4], lo[4];
+            for (int tau = 0; tau < kPT; tau++)
+                pb[tau] = *reinterpret_cast<const f32x4 *>(&s_pbias[bf][16 * tau + 4 * g]);
+            // ---- online softmax per row (log2 units).  The running max is
+            // kept until a logit passes it by kLazy (weights stay below
+            // 2^kLazy; the merge uses the same reference), so the accumulator
+            // is seldom rescaled
+            float alpha[TT], m_use[TT];
+            bool bump_any = false;
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
-                const uint32_t h0 = f32_to_bf16(pw[2 * k]), h1 = f32_to_bf16(pw[2 * k + 1]);
-                const float r0 = pw[2 * k] - __uint_as_float(h0 << 16);
-                const float r1 = pw[2 * k + 1] - __uint_as_float(h1 << 16);
-                hi[k] = h0 | (h1 << 16);
-                lo[k] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
+            for (int k = 0; k < TT; k++) {
+                const int lim = limit[k] - step_pos - 4 * g;  // position 16 tau + i must be <= lim
+                float mx = -INFINITY;
+#pragma unroll
+                for (int tau = 0; tau < kPT; tau++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const float x = fmaf(st[k][tau][i], scale2, pb[tau][i]);
+                        st[k][tau][i] = 16 * tau + i <= lim ? x : -INFINITY;
+                        mx = fmaxf(mx, st[k][tau][i]);
+                    }
+                mx = row_max(mx);
+                // (-inf + kLazy stays -inf: a row's first finite logit bumps)
+                const bool bump = mx > m_run[k] + kLazy;
+                const float m_new = bump ? mx : m_run[k];
+                alpha[k] = bump ? __builtin_amdgcn_exp2f(m_run[k] - m_new) : 1.f;
+                m_use[k] = m_new == -INFINITY ? 0.f : m_new;  // all -inf: weights 0
+                m_run[k] = m_new;
+                bump_any = bump_any || bump;
             }
-            const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-
-            // ---- A = V^T by transposing LDS reads (see attend_mla.hip): lane
-            // i of group g addresses position 4 g + i / 4 (+ 16), dims 16 t +
-            // 4 (i % 4) .. + 4 of the V slabs
-            const char *stg8 = reinterpret_cast<const char *>(stg + kKSlabs * 64);
+            if (__any(bump_any)) {
+#pragma unroll
+                for (int k = 0; k < TT; k++)
+#pragma unroll
+                    for (int t = 0; t < kDTiles; t++) acc[k][t] *= alpha[k];
+            }
+            // ---- weights as B fragments (hi + lo bf16) of the value product,
+            // 32 positions (two position tiles) per k-step kk
+            const char *stg8 = reinterpret_cast<const char *>(stg + kKSteps * kPT * 64);
             const int pq = r16 >> 2, dq = r16 & 3;
 #pragma unroll
-            for (int t = 0; t < kDTiles; t++) {
-                const int gq = 2 * (t & 1) + (dq >> 1);
-                const int base = ((2 * (t >> 1)) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
-                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base));
-                const s16x4 v1 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base + 64 * 16));
-                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
-                const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+            for (int kk = 0; kk < kPT / 2; kk++) {
+                bf16x8 phi[TT], plo[TT];
+#pragma unroll
+                for (int k = 0; k < TT; k++) {
+                    float pw[8];
+#pragma unroll
+                    for (int q = 0; q < 8; q++)
+                        pw[q] = __builtin_amdgcn_exp2f(st[k][2 * kk + (q >> 2)][q & 3] - m_use[k]);
+                    const float psum =
+                        ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+                    l_run[k] = (kk == 0 ? l_run[k] * alpha[k] : l_run[k]) + psum;
+                    uint32_t hi[4], lo[4];
+#pragma unroll
+                    for (int q = 0; q < 4; q++) {
+                        const f32x2 pr = {pw[2 * q], pw[2 * q + 1]};
+                        hi[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                        const f32x2 rr = {pw[2 * q] - __uint_as_float(hi[q] << 16),
+                                          pw[2 * q + 1] - __uint_as_float(hi[q] & 0xFFFF0000u)};
+                        lo[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
+                    }
+                    phi[k] = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                    plo[k] = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                }
+                // ---- A = V^T by transposing LDS reads (see attend_mla.hip),
+                // each fragment used for every tile
+#pragma unroll
+                for (int t = 0; t < kDTiles; t++) {
+                    const int gq = 2 * (t & 1) + (dq >> 1);
+                    const int base =
+                        (((t >> 1) * kPT + 2 * kk) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
+                    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base));
+                    const s16x4 v1 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base + 64 * 16));
+                    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                    const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+#pragma unroll
+                    for (int k = 0; k < TT; k++) {
+                        acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[k], acc[k][t], 0, 0, 0);
+                        acc[k][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[k], acc[k][t], 0, 0, 0);
+                    }
+                }
             }
         }
     }
 
-    // ---- partial results: O^T D registers hold dims 16 t + 4 g + i of row r16
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    const int64_t slot = (static_cast<int64_t>(item) * a.n_kv_heads + h) * (kMaxWaves * 16) + my_row;
-    float *pa = a.part_acc + slot * kDim;
+    // ---- partial results of the tiles with rows that reach this item:
+    // O^T D registers hold dims 16 t + 4 g + i of row r16
 #pragma unroll
-    for (int t = 0; t < kDTiles; t++)
-        *reinterpret_cast<float4 *>(pa + 16 * t + 4 * g) =
-            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-    if (g == 0) {
-        a.part_ml[2 * slot] = m_run;
-        a.part_ml[2 * slot + 1] = l_run;
+    for (int k = 0; k < TT; k++) {
+        if (tile_last[k] < I.pos_a) continue;
+        float l = l_run[k];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const int row = set_row0 + 16 * (TT * wave + k) + r16;
+        const int64_t slot = (static_cast<int64_t>(item) * a.n_kv_heads + h) * a.row_slots + row;
+        float *pa = a.part_acc + slot * kDim;
+#pragma unroll
+        for (int t = 0; t < kDTiles; t++)
+            *reinterpret_cast<float4 *>(pa + 16 * t + 4 * g) =
+                make_float4(acc[k][t][0], acc[k][t][1], acc[k][t][2], acc[k][t][3]);
+        if (g == 0) {
+            a.part_ml[2 * slot] = m_run[k];
+            a.part_ml[2 * slot + 1] = l;
+        }
     }
 }
 
-// out[row][q head] = merge of the entry's items (flash-decoding rescaling);
-// one workgroup per (entry, local row), a thread per dim.
-__global__ void __launch_bounds__(kCombineThreads) bnd_combine_kernel(const BndArgs a) {
-    const int e = blockIdx.x;
-    const int row = blockIdx.y;  // j G + gh within the KV head's rows
+// out[token][q head] = merge of the request's items that the token's row
+// reaches (flash-decoding rescaling).  One wave per (request, row, KV head):
+// lane t holds item t's max and sum (a request has at most 64 items), then
+// every lane merges two dims.
+__global__ void __launch_bounds__(64) bnd_combine_kernel(const BndArgs a) {
+    const BndReq Q = a.reqs[blockIdx.y];
+    const int row = blockIdx.x;  // token i x G + gh
     const int h = blockIdx.z;
-    const BndEntry E = a.entries[e];
-    if (row >= E.n_tok * a.group) return;
-    const int d = threadIdx.x;
-    float M = -INFINITY;
-    for (int it = E.item0; it < E.item1; it++) {
-        const int64_t slot = (static_cast<int64_t>(it) * a.n_kv_heads + h) * (kMaxWaves * 16) + row;
-        M = fmaxf(M, a.part_ml[2 * slot]);
-    }
-    float L = 0.f, O = 0.f;
-    for (int it = E.item0; it < E.item1; it++) {
-        const int64_t slot = (static_cast<int64_t>(it) * a.n_kv_heads + h) * (kMaxWaves * 16) + row;
-        const float m = a.part_ml[2 * slot];
-        if (m == -INFINITY) continue;  // the item held no position of this row
-        const float f = __expf(m - M);
-        L += a.part_ml[2 * slot + 1] * f;
-        O += a.part_acc[slot * kDim + d] * f;
-    }
+    if (row >= Q.n_tok * a.group) return;
+    const int lane = threadIdx.x;
     const int tok = row / a.group, gh = row - tok * a.group;
-    a.out[static_cast<int64_t>(E.row0 + tok) * a.o_row + (h * a.group + gh) * a.o_head + d] = O / L;
+    const int lim = a.limit[Q.row0 + tok];
+    const int it = Q.item0 + lane;
+    const int64_t slot = (static_cast<int64_t>(it) * a.n_kv_heads + h) * a.row_slots + row;
+    // items are in position order; those past the row's limit hold nothing
+    const bool mine = it < Q.item1 && a.items[it].pos_a <= lim;
+    const float m = mine ? a.part_ml[2 * slot] : -INFINITY;
+    const float lsum = mine ? a.part_ml[2 * slot + 1] : 0.f;
+    float M = m;
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float f = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);  // log2 units
+    float L = lsum * f;
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    const int n = Q.item1 - Q.item0;
+    float2 O = make_float2(0.f, 0.f);
+    for (int t = 0; t < n; t++) {
+        const float ft = __shfl(f, t, 64);
+        if (ft == 0.f) continue;  // uniform: an item the row does not reach, or empty
+        const int64_t st = (static_cast<int64_t>(Q.item0 + t) * a.n_kv_heads + h) * a.row_slots + row;
+        const float2 v = *reinterpret_cast<const float2 *>(a.part_acc + st * kDim + 2 * lane);
+        O.x += v.x * ft;
+        O.y += v.y * ft;
+    }
+    float *o = a.out + static_cast<int64_t>(Q.row0 + tok) * a.o_row +
+               static_cast<int64_t>(h * a.group + gh) * a.o_head + 2 * lane;
+    o[0] = O.x / L;
+    o[1] = O.y / L;
 }
 
 // ------------------------------------------------------------------ host
@@ -405,51 +573,73 @@ AttnTile advance(AttnTile t, int32_t k) {
 
 struct BndMap {
     std::vector<uint8_t> bytes;
-    size_t off_blocks = 0, off_bpos = 0, off_items = 0, off_entries = 0;
-    int32_t n_items = 0, n_entries = 0, n_rows = 0;
+    size_t off_blocks = 0, off_bpos = 0, off_items = 0, off_reqs = 0, off_limit = 0, off_tabs = 0;
+    int32_t n_items = 0, n_reqs = 0, n_rows = 0, max_req_rows = 0;
 };
 
-// Relocated entries (dst_offset > 0) of every request in order; entry e
-// reads context [0, d_e + n_e) of its request, cut into ceil(L_e / S) items
-// of equal length, S the total context over `target`: long prefixes are
-// split, short ones stay whole.
-// A relocated entry: request, dst_offset, length.
+// A relocated entry (dst_offset > 0): request, dst_offset, length.
 struct Reloc {
     int32_t request;
     int64_t dst;
     int32_t length;
 };
 
+// Requests with relocated entries, in order; each request's context [0, L),
+// L = the last boundary position + 1, is cut into ceil(L / S) items of
+// about equal length, S the total over `target` (at least one step, at most
+// kMaxItems items per request).  Boundary rows are numbered request by
+// request, entry by entry, token by token: the order of the caller's q.
 BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t k,
                      int64_t target) {
     std::vector<AttnTile> tiles;
     std::vector<AttnBlock> blocks;
     std::vector<int32_t> bpos;
+    std::vector<int32_t> btabs;  // kBlockTabs per block
     std::vector<BndItem> items;
-    std::vector<BndEntry> ents;
+    std::vector<BndReq> reqs;
+    std::vector<int32_t> limit;
+    // group the entries by request (they come request by request)
+    std::vector<std::pair<size_t, size_t>> groups;
+    for (size_t i = 0; i < order.size(); i++) {
+        if (groups.empty() || order[groups.back().first].request != order[i].request)
+            groups.push_back({i, i});
+        groups.back().second = i + 1;
+    }
+    auto ctx_of = [&](const std::pair<size_t, size_t> &gr) {
+        int64_t L = 0;
+        for (size_t i = gr.first; i < gr.second; i++)
+            L = std::max<int64_t>(L, order[i].dst + std::min(k, order[i].length));
+        return L;
+    };
     int64_t total = 0;
-    for (const Reloc &e : order) total += e.dst + std::min(k, e.length);
-    int32_t row0 = 0;
-    for (const Reloc &e : order) {
-        const int32_t r = e.request;
-        const int32_t nt = std::min(k, e.length);
-        const int64_t L = e.dst + nt;  // context of the entry's rows
-        const int64_t per = std::max<int64_t>(kStepPos, (total + target - 1) / target);
-        const int64_t n = (L + per - 1) / per;
+    for (const auto &gr : groups) total += ctx_of(gr);
+    const int64_t per = std::max<int64_t>(kStepPos, (total + target - 1) / target);
+    int32_t max_rows = 0;
+    for (const auto &gr : groups) {
+        const int32_t r = order[gr.first].request;
+        BndReq R{static_cast<int32_t>(limit.size()), 0, static_cast<int32_t>(items.size()), 0};
+        for (size_t i = gr.first; i < gr.second; i++)
+            for (int32_t j = 0; j < std::min(k, order[i].length); j++)
+                limit.push_back(static_cast<int32_t>(order[i].dst + j));
+        R.n_tok = static_cast<int32_t>(limit.size()) - R.row0;
+        max_rows = std::max(max_rows, R.n_tok);
+        const int64_t L = ctx_of(gr);
+        const int64_t n = std::min<int64_t>(kMaxItems, (L + per - 1) / per);
         const int64_t S = (L + n - 1) / n;
-        BndEntry E{r, row0, nt, static_cast<int32_t>(e.dst),
-                   static_cast<int32_t>(items.size()), 0, {0, 0}};
-        row0 += nt;
         int64_t pos = 0, left = L, item_left = 0;
         AttnBlock blk{r, 0, 0, 0};
         int32_t blk_pos = 0;
+        std::vector<int32_t> tabs;  // the open block's shift tables
         auto close_block = [&]() {
             if (blk.ntiles > 0) {
                 blocks.push_back(blk);
                 bpos.push_back(blk_pos);
+                for (int j = 0; j < kBlockTabs; j++)
+                    btabs.push_back(j < static_cast<int>(tabs.size()) ? tabs[j] : -1);
             }
             blk = AttnBlock{r, static_cast<int32_t>(tiles.size()), 0, 0};
             blk_pos = static_cast<int32_t>(pos);
+            tabs.clear();
         };
         for (int32_t t = p.req_tile0[r]; t < p.req_tile0[r + 1] && left > 0; t++) {
             AttnTile T = p.atiles[t];
@@ -458,11 +648,18 @@ BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t 
                     close_block();
                     if (!items.empty() && items.back().block1 < 0)
                         items.back().block1 = static_cast<int32_t>(blocks.size());
-                    items.push_back(BndItem{static_cast<int32_t>(ents.size()),
-                                            static_cast<int32_t>(blocks.size()), -1, 0});
+                    items.push_back(BndItem{static_cast<int32_t>(reqs.size()),
+                                            static_cast<int32_t>(blocks.size()), -1,
+                                            static_cast<int32_t>(pos)});
                     item_left = std::min(S, left);
                 }
-                if (blk.ntok == kBlockPos || blk.ntiles == kItemTiles) close_block();
+                const bool new_tab = T.cs_idx >= 0 &&
+                                     std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end();
+                if (blk.ntok == kBlockPos || blk.ntiles == kItemTiles ||
+                    (new_tab && static_cast<int>(tabs.size()) == kBlockTabs))
+                    close_block();
+                if (T.cs_idx >= 0 && std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end())
+                    tabs.push_back(T.cs_idx);
                 const int32_t take = static_cast<int32_t>(
                     std::min<int64_t>({int64_t{T.ntok}, item_left, int64_t{kBlockPos - blk.ntok}}));
                 AttnTile piece = T;
@@ -481,8 +678,8 @@ BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t 
         close_block();
         if (!items.empty() && items.back().block1 < 0)
             items.back().block1 = static_cast<int32_t>(blocks.size());
-        E.item1 = static_cast<int32_t>(items.size());
-        ents.push_back(E);
+        R.item1 = static_cast<int32_t>(items.size());
+        reqs.push_back(R);
     }
     BndMap m;
     auto put = [&](const void *src, size_t n) {
@@ -495,10 +692,13 @@ BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t 
     m.off_blocks = put(blocks.data(), blocks.size() * sizeof(AttnBlock));
     m.off_bpos = put(bpos.data(), bpos.size() * sizeof(int32_t));
     m.off_items = put(items.data(), items.size() * sizeof(BndItem));
-    m.off_entries = put(ents.data(), ents.size() * sizeof(BndEntry));
+    m.off_reqs = put(reqs.data(), reqs.size() * sizeof(BndReq));
+    m.off_limit = put(limit.data(), limit.size() * sizeof(int32_t));
+    m.off_tabs = put(btabs.data(), btabs.size() * sizeof(int32_t));
     m.n_items = static_cast<int32_t>(items.size());
-    m.n_entries = static_cast<int32_t>(ents.size());
-    m.n_rows = row0;
+    m.n_reqs = static_cast<int32_t>(reqs.size());
+    m.n_rows = static_cast<int32_t>(limit.size());
+    m.max_req_rows = max_rows;
     return m;
 }
 
@@ -533,9 +733,7 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
         return fail(PIC_ERR_INVALID_ARG, "num_q_heads %d: need a multiple of %d, at most 8x",
                     args->num_q_heads, H);
     const int G = args->num_q_heads / H;
-    if (args->boundary_k < 1 || args->boundary_k * G > kMaxWaves * 16)
-        return fail(PIC_ERR_INVALID_ARG, "boundary_k %d: need 1 <= boundary_k x %d <= %d",
-                    args->boundary_k, G, kMaxWaves * 16);
+    if (args->boundary_k < 1) return fail(PIC_ERR_INVALID_ARG, "boundary_k %d < 1", args->boundary_k);
     if (args->layer < 0 || args->layer >= p.shape.num_layers)
         return fail(PIC_ERR_INVALID_ARG, "layer %d outside [0, %d)", args->layer,
                     p.shape.num_layers);
@@ -570,10 +768,11 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     st = ensure_device_plan(plan, stream_);
     if (st) return st;
-    // items: about four rounds of the CU slots (four workgroups of 35 KB LDS
-    // per CU, one per KV head and item)
-    const int64_t target = std::max<int64_t>(1, 16 * static_cast<int64_t>(cu_count()) / H);
-    const int64_t key = (target << 20) | args->boundary_k;
+    // items: about two rounds of the CU slots (one workgroup of 8 waves per
+    // CU and KV head at a time)
+    const int64_t target = std::max<int64_t>(1, 2 * static_cast<int64_t>(cu_count()) / H);
+    const int64_t key = (target << 32) | static_cast<uint32_t>(args->boundary_k);
+    int TT = 1, n_sets = 1, row_slots = 0;
     {
         std::lock_guard<std::mutex> lock(plan->mu);
         hipError_t e;
@@ -603,12 +802,27 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
             plan->bnd_off[0] = m.off_blocks;
             plan->bnd_off[1] = m.off_bpos;
             plan->bnd_off[2] = m.off_items;
-            plan->bnd_off[3] = m.off_entries;
+            plan->bnd_off[3] = m.off_reqs;
+            plan->bnd_off[4] = m.off_limit;
+            plan->bnd_off[5] = m.off_tabs;
             plan->bnd_n_items = m.n_items;
-            plan->bnd_n_entries = m.n_entries;
+            plan->bnd_n_reqs = m.n_reqs;
+            plan->bnd_max_rows = m.max_req_rows;
             plan->bnd_key = key;
         }
-        const size_t need = static_cast<size_t>(plan->bnd_n_items) * H * (kMaxWaves * 16) *
+        // rows of a request's KV head: tokens x G, in as few sets of 8 waves
+        // x TT tiles as the registers allow, TT as small as they then permit
+        const int64_t rows = static_cast<int64_t>(plan->bnd_max_rows) * G;
+        const int64_t max_set = int64_t{kWaves} * kMaxTT * 16;
+        n_sets = static_cast<int>((rows + max_set - 1) / max_set);
+        TT = static_cast<int>((rows + int64_t{n_sets} * kWaves * 16 - 1) / (int64_t{n_sets} * kWaves * 16));
+        row_slots = n_sets * kWaves * TT * 16;
+        if ((static_cast<int64_t>(plan->bnd_n_items) * H + 7) / 8 * 8 * n_sets >=
+                (int64_t{1} << 31) / (64 * kWaves) ||
+            static_cast<int64_t>(plan->bnd_n_reqs) * rows * H >= (int64_t{1} << 31) / 64 ||
+            plan->bnd_n_reqs > 65535)
+            return fail(PIC_ERR_RANGE, "boundary rows x context too large for one launch");
+        const size_t need = static_cast<size_t>(plan->bnd_n_items) * H * row_slots *
                             (static_cast<size_t>(kDim) + 2) * sizeof(float);
         if (plan->work_bytes < need) {
             if (plan->d_work) {
@@ -633,7 +847,9 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     a.blocks = reinterpret_cast<const AttnBlock *>(bm + plan->bnd_off[0]);
     a.block_pos = reinterpret_cast<const int32_t *>(bm + plan->bnd_off[1]);
     a.items = reinterpret_cast<const BndItem *>(bm + plan->bnd_off[2]);
-    a.entries = reinterpret_cast<const BndEntry *>(bm + plan->bnd_off[3]);
+    a.reqs = reinterpret_cast<const BndReq *>(bm + plan->bnd_off[3]);
+    a.limit = reinterpret_cast<const int32_t *>(bm + plan->bnd_off[4]);
+    a.block_tabs = reinterpret_cast<const int32_t *>(bm + plan->bnd_off[5]);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = static_cast<const uint16_t *>(pool->k);
     a.pool_v = static_cast<const uint16_t *>(pool->v);
@@ -655,32 +871,44 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     a.o_row = args->out_row_stride;
     a.o_head = args->out_head_stride;
     const size_t acc_elems =
-        static_cast<size_t>(plan->bnd_n_items) * H * (kMaxWaves * 16) * static_cast<size_t>(kDim);
+        static_cast<size_t>(plan->bnd_n_items) * H * row_slots * static_cast<size_t>(kDim);
     a.part_acc = static_cast<float *>(plan->d_work);
     a.part_ml = static_cast<float *>(plan->d_work) + acc_elems;
     a.n_items = plan->bnd_n_items;
     a.n_kv_heads = H;
     a.group = G;
     a.num_q_heads = args->num_q_heads;
+    a.row_slots = row_slots;
+    a.n_sets = n_sets;
     a.rope_offset = p.shape.rope_offset;
     a.half_r = p.u.half_r;
     a.scale = args->scale;
     a.sink_tokens = args->sink_tokens;
     a.sink_bias = args->sink_bias;
-    const int waves = (args->boundary_k * G + 15) / 16;
-    const dim3 grid(static_cast<unsigned>(a.n_items) * static_cast<unsigned>(H));
-    if (p.style == PIC_ROPE_HALF)
-        hipLaunchKernelGGL(bnd_block_kernel<PIC_ROPE_HALF>, grid, dim3(64 * waves), 0, stream, a,
-                           args->layer);
-    else
-        hipLaunchKernelGGL(bnd_block_kernel<PIC_ROPE_INTERLEAVED>, grid, dim3(64 * waves), 0,
-                           stream, a, args->layer);
+    const dim3 grid(static_cast<unsigned>((static_cast<int64_t>(a.n_items) * H + 7) / 8 * 8 * n_sets));
+    const bool half = p.style == PIC_ROPE_HALF;
+    switch (TT) {
+#define PIC_BND_LAUNCH(T)                                                                          \
+    case T:                                                                                        \
+        if (half)                                                                                  \
+            hipLaunchKernelGGL((bnd_block_kernel<PIC_ROPE_HALF, T>), grid, dim3(64 * kWaves), 0,  \
+                               stream, a, args->layer);                                            \
+        else                                                                                       \
+            hipLaunchKernelGGL((bnd_block_kernel<PIC_ROPE_INTERLEAVED, T>), grid,                  \
+                               dim3(64 * kWaves), 0, stream, a, args->layer);                      \
+        break;
+        PIC_BND_LAUNCH(1)
+        PIC_BND_LAUNCH(2)
+#undef PIC_BND_LAUNCH
+        default:
+            return fail(PIC_ERR_INVALID_ARG, "internal: row tiles per wave %d", TT);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "boundary attention kernel launch");
     hipLaunchKernelGGL(bnd_combine_kernel,
-                       dim3(static_cast<unsigned>(plan->bnd_n_entries),
-                            static_cast<unsigned>(args->boundary_k * G), static_cast<unsigned>(H)),
-                       dim3(kCombineThreads), 0, stream, a);
+                       dim3(static_cast<unsigned>(plan->bnd_max_rows * G),
+                            static_cast<unsigned>(plan->bnd_n_reqs), static_cast<unsigned>(H)),
+                       dim3(64), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "boundary attention combine launch");
     return PIC_OK;

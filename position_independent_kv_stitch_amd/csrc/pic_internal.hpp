@@ -155,6 +155,7 @@ struct pic_plan {
     size_t bnd_bytes = 0;
     int64_t bnd_key = -1;
     std::vector<uint8_t> bnd_host;
-    size_t bnd_off[4] = {0, 0, 0, 0};  // blocks, block positions, items, entries
-    int32_t bnd_n_items = 0, bnd_n_entries = 0;
+    size_t bnd_off[6] = {0, 0, 0, 0, 0, 0};  // blocks, block positions, items, requests,
+                                             // limits, block shift tables
+    int32_t bnd_n_items = 0, bnd_n_reqs = 0, bnd_max_rows = 0;
 };

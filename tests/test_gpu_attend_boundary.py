@@ -105,6 +105,16 @@ def test_long_k_and_short_entries(torch_cuda):
     assert err <= tol
 
 
+@pytest.mark.parametrize("k,group", [(17, 8), (40, 8), (64, 3)])
+def test_many_rows_per_request(torch_cuda, k, group):
+    """More rows per request and KV head than one workgroup holds (256):
+    the rows are split over row sets that read the same context."""
+    wl = random_small(900 + k, dtype="bf16", n_requests=3, n_layers=1, max_len=120)
+    err, tol, n = run_case(torch_cuda, wl, group, k, 4, sink_tokens=4, sink_bias=-15.0)
+    say(f"boundary k={k} group={group}: rows {n}, max err {err:.3g} (bound {tol:.3g})")
+    assert err <= tol
+
+
 def test_llama3_decode_batch_two_requests(torch_cuda):
     """Two requests of the Llama-3-8B decode batch (8 chunks x 2048 behind a
     128-token prefix, recompute_k 32, 16-token pages): k = 16, 32 query
@@ -127,13 +137,18 @@ def test_errors(torch_cuda):
     n = pic.boundary_row_count(plan, 17)
     assert n > 0
     q = normal_values((n, 16, wl.row_dim), wl.dtype, 3, "cuda:0")
-    with pytest.raises(pic.PicError, match="invalid_arg"):  # 17 x 8 query heads > 128 rows
-        pic.attend_boundary(plan, pk, pv, ck, ck, q, layer=0, boundary_k=17)
+    import ctypes as C
+    from position_independent_kv_stitch_amd import _binding as B
+    out = torch_cuda.empty(q.shape, dtype=torch_cuda.float32, device="cuda:0")
+    with pytest.raises(pic.PicError, match="invalid_arg"):  # boundary_k < 1
+        a = B.BoundaryArgs(q.data_ptr(), q.stride(0), q.stride(1), out.data_ptr(), out.stride(0),
+                           out.stride(1), 16, 0, 0.1, 0, 0, 0.0)
+        B._check(plan._lib.pic_attend_boundary(
+            plan.handle, C.byref(B._view(pk, pv, "pool")), C.byref(B._view(ck, ck, "contig")),
+            C.byref(a), None), plan._lib)
     with pytest.raises(pic.PicError, match="invalid_arg"):  # f32 plans are refused
         f32 = random_small(9, dtype="f32", n_requests=1, n_layers=1)
         fplan = pic.Plan.from_workload(f32)
-        import ctypes as C
-        from position_independent_kv_stitch_amd import _binding as B
         fk, fv = pool_values(f32, seed=1, device="cuda:0")
         fc = normal_values(f32.dst_shape(), f32.dtype, 2, "cuda:0")
         a = B.BoundaryArgs(q.data_ptr(), q.stride(0), q.stride(1), q.data_ptr(), 0, 0, 4, 0,
