@@ -59,7 +59,11 @@ constexpr int kDTiles = kDim / 16;        // output tiles of 16 dims
 constexpr int kPT = PIC_BND_POS_TILES;   // 16-position tiles per step (2 or 4)
 constexpr int kStepPos = 16 * kPT;        // positions per step
 constexpr int kSlabs = 2 * kKSteps * kPT; // 1 KB slabs per step: K, then V
-constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kNBuf = 3;                  // staging buffers (computed, turned, loading)
+#ifndef PIC_BND_WAVES
+#define PIC_BND_WAVES 8
+#endif
+constexpr int kWaves = PIC_BND_WAVES;     // waves per workgroup
 constexpr int kMaxTT = 2;                 // row tiles per wave at most (registers)
 constexpr int kItemTiles = 64;            // map tiles per block at most
 constexpr int kBlockPos = 4096;           // positions per block at most
@@ -190,11 +194,11 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     // V) holds dims 32 s .. 32 s + 31 of positions 16 tau .. 16 tau + 15; its
     // slot 16 g + p holds dims 32 s + 8 g .. + 8 of position 16 tau + p (the
     // A fragment of lane 16 g + p)
-    __shared__ __attribute__((aligned(16))) uint4 s_stage[2][kSlabs * 64];
+    __shared__ __attribute__((aligned(16))) uint4 s_stage[kNBuf][kSlabs * 64];
     __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kMaxHalf];  // block's shift tables
     __shared__ StageTile s_tiles[kItemTiles];
-    __shared__ uint32_t s_pslot[2][kStepPos];                       // shift-table slot + 1 (0: not turned)
-    __shared__ __attribute__((aligned(16))) float s_pbias[2][kStepPos];  // damping, -inf past the block
+    __shared__ uint32_t s_pslot[kNBuf][kStepPos];                       // shift-table slot + 1 (0: not turned)
+    __shared__ __attribute__((aligned(16))) float s_pbias[kNBuf][kStepPos];  // damping, -inf past the block
 
     // grid: runs of 8 (item, KV head) pairs c, each run once per row set;
     // workgroup w goes to XCD w % 8, so every set of one pair shares an XCD
@@ -242,6 +246,21 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     }
     const float scale2 = a.scale * kLog2e;  // logits in log2 units (exp2 weights)
     const float bias2 = a.sink_bias * kLog2e;
+    // the last position any row of the workgroup sees: later positions are
+    // neither staged nor turned, and a workgroup whose rows all end before
+    // its item returns at once (the merge never reads its partial results)
+    __shared__ int s_last[kWaves];
+    if (lane == 0) {
+        int x = tile_last[0];
+#pragma unroll
+        for (int k = 1; k < TT; k++) x = max(x, tile_last[k]);
+        s_last[wave] = x;
+    }
+    __syncthreads();
+    int wg_last = s_last[0];
+#pragma unroll
+    for (int v = 1; v < kWaves; v++) wg_last = max(wg_last, s_last[v]);
+    if (wg_last < I.pos_a) return;  // uniform over the workgroup
 
     f32x4 acc[TT][kDTiles];
     float m_run[TT], l_run[TT];
@@ -263,6 +282,8 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     for (int b = I.block0; b < I.block1; b++) {
         const AttnBlock B = a.blocks[b];
         const int bpos = a.block_pos[b];
+        if (bpos > wg_last) break;  // uniform
+        const int ntok = min(B.ntok, wg_last + 1 - bpos);  // positions some row sees
         __syncthreads();
         if (tid < B.ntiles) {
             const AttnTile T = a.tiles[B.tile0 + tid];
@@ -287,7 +308,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
         int cur = 0;
         auto stage = [&](int p0, int bf) {
             int pi = p0 + 16 * my_tau + r16;
-            const bool valid = pi < B.ntok;
+            const bool valid = pi < ntok;
             if (!valid) pi = p0;
             while (cur + 1 < B.ntiles && s_tiles[cur + 1].tok0 <= pi) cur++;
             const StageTile T = s_tiles[cur];
@@ -311,20 +332,14 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             }
         };
 
-        stage(0, 0);
-        int bf = 0;
-        for (int p0 = 0; p0 < B.ntok; p0 += kStepPos, bf ^= 1) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();
-            if (p0 + kStepPos < B.ntok) stage(p0 + kStepPos, bf ^ 1);
-
-            // ---- turn the rotary pieces of moved chunk rows (K slabs): unit
-            // (position, 8-plane group m, half hh) turns 4 planes
+        // turn the rotary pieces of moved chunk rows (K slabs) of buffer bb:
+        // unit (position, 8-plane group m, half hh) turns 4 planes
+        auto turn = [&](int bb) {
             const int units = (half_r / 4) * kStepPos;
             for (int u = tid; u < units; u += 64 * kWaves) {
                 const int pos = u / (half_r / 4), rem = u - pos * (half_r / 4);
                 const int m = rem >> 1, hh = rem & 1;
-                const uint32_t slot1 = s_pslot[bf][pos];
+                const uint32_t slot1 = s_pslot[bb][pos];
                 if (slot1 == 0u) continue;
                 const double2 *tab = s_cs[slot1 - 1];
                 const int tau = pos >> 4, pp = pos & 15;
@@ -333,9 +348,9 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                     // piece (ro + 8 m) / 8; y the same in piece (ro + half_r + 8 m) / 8
                     const int px = (a.rope_offset + 8 * m) >> 3, py = px + (half_r >> 3);
                     uint2 *kx = reinterpret_cast<uint2 *>(
-                                    &s_stage[bf][((px >> 2) * kPT + tau) * 64 + 16 * (px & 3) + pp]) + hh;
+                                    &s_stage[bb][((px >> 2) * kPT + tau) * 64 + 16 * (px & 3) + pp]) + hh;
                     uint2 *ky = reinterpret_cast<uint2 *>(
-                                    &s_stage[bf][((py >> 2) * kPT + tau) * 64 + 16 * (py & 3) + pp]) + hh;
+                                    &s_stage[bb][((py >> 2) * kPT + tau) * 64 + 16 * (py & 3) + pp]) + hh;
                     const uint2 xv = *kx, yv = *ky;
                     uint32_t xw[2] = {xv.x, xv.y}, yw[2] = {yv.x, yv.y};
 #pragma unroll
@@ -356,7 +371,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                     // whole pairs: piece (ro / 8) + 2 m + hh holds planes
                     // 8 m + 4 hh .. + 4
                     const int pc = (a.rope_offset >> 3) + 2 * m + hh;
-                    uint4 &kw = s_stage[bf][((pc >> 2) * kPT + tau) * 64 + 16 * (pc & 3) + pp];
+                    uint4 &kw = s_stage[bb][((pc >> 2) * kPT + tau) * 64 + 16 * (pc & 3) + pp];
                     uint32_t wv[4] = {kw.x, kw.y, kw.z, kw.w};
 #pragma unroll
                     for (int q = 0; q < 4; q++) {
@@ -368,7 +383,27 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                     kw = make_uint4(wv[0], wv[1], wv[2], wv[3]);
                 }
             }
+        };
+
+        // three buffers: step i is computed while step i + 1 is turned and
+        // step i + 2 is loaded, with one barrier per step
+        stage(0, 0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (kStepPos < ntok) stage(kStepPos, 1);
+        turn(0);
+        int bf = 0;
+        for (int p0 = 0; p0 < ntok; p0 += kStepPos) {
+            // this wave's loads of step i + 1 are in; after the barrier every
+            // wave's are, step i is turned, and step i - 1's buffer is free
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            const int bn = bf == kNBuf - 1 ? 0 : bf + 1;
+            const int bnn = bn == kNBuf - 1 ? 0 : bn + 1;
+            if (p0 + 2 * kStepPos < ntok) stage(p0 + 2 * kStepPos, bnn);
+            if (p0 + kStepPos < ntok) turn(bn);
+            const int cur_bf = bf;
+            bf = bn;
 
             const int step_pos = bpos + p0;  // context position of the step's first row
             bool any = false;
@@ -380,7 +415,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             // past their last position are masked to weight 0
 
             // ---- logits S^T: each K fragment serves every tile
-            const uint4 *stg = s_stage[bf];
+            const uint4 *stg = s_stage[cur_bf];
             f32x4 st[TT][kPT];
 #pragma unroll
             for (int k = 0; k < TT; k++)
@@ -415,7 +450,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             f32x4 pb[kPT];
 #pragma unroll
             for (int tau = 0; tau < kPT; tau++)
-                pb[tau] = *reinterpret_cast<const f32x4 *>(&s_pbias[bf][16 * tau + 4 * g]);
+                pb[tau] = *reinterpret_cast<const f32x4 *>(&s_pbias[cur_bf][16 * tau + 4 * g]);
             // ---- online softmax per row (log2 units).  The running max is
             // kept until a logit passes it by kLazy (weights stay below
             // 2^kLazy; the merge uses the same reference), so the accumulator
