@@ -70,15 +70,20 @@ constexpr int kItemTiles = 64;            // map tiles per latent block at most
 constexpr int kBlockPos = 4096;           // positions per latent block at most
 constexpr int kCombineThreads = 256;
 
-constexpr uint32_t kMetaDamp = 1u << 31;      // LegoLink bias applies
-constexpr uint32_t kMetaCs = (1u << 30) - 1;  // shift table + 1 (0: row not turned)
+constexpr int kBlockTabs = 4;             // shift tables per latent block at most (kept in LDS)
+constexpr int kHalfR = kRopeDim / 2;      // rotary planes
+constexpr float kLazy = 12.f;             // running-max slack of the online softmax (log2 units)
+constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct MlaArgs {
     const AttnTile *tiles;     // latent blocks' tiles (tok0: position in the block)
     const AttnBlock *blocks;   // latent blocks (<= kBlockPos positions, <= kItemTiles tiles)
+    const int32_t *block_tabs; // [block][kBlockTabs] shift tables its tiles use (-1: none)
     const int32_t *item_block0;  // first block of every item (+ end)
     const int32_t *req_item0;    // first item of every request (+ end)
     const double *cs;
@@ -101,43 +106,53 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &v) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// max over the four lanes of a row (lanes r, r + 16, r + 32, r + 48): the
+// 32-lane swap pairs lane i with i ^ 32, the 16-lane swap i with i ^ 16
+__device__ __forceinline__ float row_max(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Row (element offset) and meta of position pi of a block whose tiles are in
-// s_tiles[0, ntiles).
-__device__ __forceinline__ int64_t row_of(const MlaArgs &a, const AttnTile *s_tiles, int ntiles,
-                                          int pi, int32_t layer, uint32_t *meta,
-                                          const uint16_t **base) {
-    int lo = 0, hi = ntiles - 1;  // the last tile starting at or before pi
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_tiles[mid].tok0 <= pi) lo = mid;
-        else hi = mid - 1;
-    }
-    const AttnTile &T = s_tiles[lo];
-    const int t = pi - T.tok0;
+// A map tile as the staging reads it: the row of block position pi starts at
+// element off0 + pi * token stride (layer included) of the pool (info bit
+// kInfoPool) or the cache; info also holds the tile's shift-table slot + 1
+// (bits 0-2, 0: rows not turned) and how many of its first positions take
+// the damping bias (bits 8-31).
+struct StageTile {
+    int64_t off0;
+    int32_t tok0;
+    uint32_t info;
+};
+constexpr uint32_t kInfoPool = 1u << 3;
+
+__device__ __forceinline__ StageTile stage_tile(const MlaArgs &a, const AttnTile &T, int slot,
+                                                int32_t layer) {
     const int64_t L = layer;
-    uint32_t m = T.cs_idx >= 0 ? static_cast<uint32_t>(T.cs_idx + 1) : 0u;
-    if (T.sink_dist + t < a.sink_tokens) m |= kMetaDamp;
-    *meta = m;
+    int64_t off0;
+    bool pool = true;
     switch (T.kind) {
         case kPoolRows:
-            *base = a.pool_k;
-            return L * a.s_layer + (T.a + t) * a.s_tok;
+            off0 = L * a.s_layer + (T.a - T.tok0) * a.s_tok;
+            break;
         case kPoolPages:
-            *base = a.pool_k;
-            return L * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b + t) * a.s_tok;
+            off0 = L * a.s_layer + T.a * a.s_page + static_cast<int64_t>(T.b - T.tok0) * a.s_tok;
+            break;
         case kCacheRows:
-            *base = a.cache_k;
-            return L * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b + t) * a.c_tok;
+            pool = false;
+            off0 = L * a.c_layer + T.a * a.c_req + static_cast<int64_t>(T.b - T.tok0) * a.c_tok;
+            break;
         default:
-            *base = a.cache_k;
-            return L * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b + t) * a.c_tok;
+            pool = false;
+            off0 = L * a.c_layer + T.a * a.c_page + static_cast<int64_t>(T.b - T.tok0) * a.c_tok;
+            break;
     }
+    const int64_t damp = std::min<int64_t>(std::max<int64_t>(int64_t{a.sink_tokens} - T.sink_dist, 0),
+                                           (1 << 24) - 1);
+    const uint32_t info = static_cast<uint32_t>(slot + 1) | (pool ? kInfoPool : 0u) |
+                          (static_cast<uint32_t>(damp) << 8);
+    return StageTile{off0, T.tok0, info};
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -158,8 +173,10 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
     // of a slab holds dims 32 s + 8 g .. + 8 of position 16 tau + p, i.e. the
     // A fragment of lane 16 g + p
     __shared__ __attribute__((aligned(16))) uint4 s_stage[NB][kSlabs * 64];
-    __shared__ AttnTile s_tiles[kItemTiles];
-    __shared__ uint32_t s_pmeta[NB][kStepPos];  // meta of the staged positions
+    __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kHalfR];  // block's shift tables
+    __shared__ StageTile s_tiles[kItemTiles];
+    __shared__ uint32_t s_pslot[NB][kStepPos];                        // table slot + 1 (0: not turned)
+    __shared__ __attribute__((aligned(16))) float s_pbias[NB][kStepPos];  // damping, -inf past the block
 
     // the head-group sets of an item sit on one XCD: workgroup w runs on XCD w % 8
     const int wid = blockIdx.x;
@@ -172,6 +189,8 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
     const int hg = set * W + wave;
     const int b_lo = a.item_block0[item], b_hi = a.item_block0[item + 1];
     const int request = a.blocks[b_lo].request;
+    const float scale2 = a.scale * kLog2e;  // logits in log2 units (exp2 weights)
+    const float bias2 = a.sink_bias * kLog2e;
 
     // ---- query fragments (B of S^T = K Q^T): head r16 of the wave's group,
     // dims 32 s + 8 g .. + 8 of k-step s
@@ -191,22 +210,45 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
     for (int b = b_lo; b < b_hi; b++) {
         const AttnBlock B = a.blocks[b];
         __syncthreads();  // the previous block's steps are done with s_tiles and s_stage
-        if (tid < B.ntiles) s_tiles[tid] = a.tiles[B.tile0 + tid];
+        if (tid < B.ntiles) {
+            const AttnTile T = a.tiles[B.tile0 + tid];
+            int sl = -1;
+#pragma unroll
+            for (int j = 0; j < kBlockTabs; j++)
+                if (T.cs_idx >= 0 && a.block_tabs[kBlockTabs * b + j] == T.cs_idx) sl = j;
+            s_tiles[tid] = stage_tile(a, T, sl, layer);
+        }
+        for (int i = tid; i < kBlockTabs * kHalfR; i += 64 * W) {
+            const int j = i / kHalfR, pl = i - j * kHalfR;
+            const int tab = a.block_tabs[kBlockTabs * b + j];
+            if (tab >= 0) {
+                const double *src = a.cs + (static_cast<int64_t>(tab) * kHalfR + pl) * 2;
+                s_cs[j][pl] = make_double2(src[0], src[1]);
+            }
+        }
         __syncthreads();
 
-        // stage step p0 into buffer bf: wave w loads slabs w, w + W, ...; lanes
-        // past the block's end repeat position p0 (their weights are 0)
+        // stage step p0 into buffer bf: wave w loads slabs w, w + W, ... of
+        // both position tiles; lanes past the block's end repeat position p0
+        // (their weights are 0).  The tile holding a lane's position is found
+        // by a forward search (positions only grow within a block).
+        int cur[2] = {0, 0};
         auto stage = [&](int p0, int bf) {
 #pragma unroll
             for (int tau = 0; tau < 2; tau++) {
                 int pi = p0 + 16 * tau + r16;
                 const bool valid = pi < B.ntok;
                 if (!valid) pi = p0;
-                uint32_t meta;
-                const uint16_t *base;
-                const int64_t off = row_of(a, s_tiles, B.ntiles, pi, layer, &meta, &base);
-                if (wave == 0 && g == 0) s_pmeta[bf][16 * tau + r16] = valid ? meta : 0u;
-                const uint16_t *row = base + off + 8 * g;
+                while (cur[tau] + 1 < B.ntiles && s_tiles[cur[tau] + 1].tok0 <= pi) cur[tau]++;
+                const StageTile T = s_tiles[cur[tau]];
+                const bool pool = T.info & kInfoPool;
+                const int64_t off = T.off0 + static_cast<int64_t>(pi) * (pool ? a.s_tok : a.c_tok);
+                if (wave == 0 && g == 0) {
+                    const bool damp = static_cast<uint32_t>(pi - T.tok0) < (T.info >> 8);
+                    s_pslot[bf][16 * tau + r16] = valid ? (T.info & 7u) : 0u;
+                    s_pbias[bf][16 * tau + r16] = valid ? (damp ? bias2 : 0.f) : -INFINITY;
+                }
+                const uint16_t *row = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
                 for (int j = 2 * wave + tau; j < kSlabs; j += 2 * W) {
                     const int s = j >> 1;
                     __builtin_amdgcn_global_load_lds((gptr_t)(row + 32 * s),
@@ -215,55 +257,83 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
             }
         };
 
-        stage(0, 0);
-        int bf = 0;
-        for (int p0 = 0; p0 < B.ntok; p0 += kStepPos, bf = (bf + 1) % NB) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();  // the step is in LDS (every wave's share) and its meta written
-            if (NB == 2 && p0 + kStepPos < B.ntok) stage(p0 + kStepPos, bf ^ 1);
-
-            // ---- turn the rotary slots of moved chunk rows, in LDS
-            for (int t = tid; t < 4 * kStepPos; t += 64 * W) {
-                const int pos = t >> 2, gg = t & 3;
-                const uint32_t cs1 = s_pmeta[bf][pos] & kMetaCs;
-                if (cs1 == 0u) continue;
-                const double *tab = a.cs + static_cast<int64_t>(cs1 - 1) * kRopeDim;
+        // turn the rotary slots of moved chunk rows of buffer bb, in LDS: unit
+        // (position, 8-plane group gg, pair qh) turns planes 2 qh, 2 qh + 1 of
+        // the group, with the stitch's fp64 turn and rounding
+        auto turn = [&](int bb) {
+            for (int u = tid; u < 16 * kStepPos; u += 64 * W) {
+                const int pos = u >> 4, gg = (u >> 2) & 3, qh = u & 3;
+                const uint32_t slot1 = s_pslot[bb][pos];
+                if (slot1 == 0u) continue;
+                const double2 *tab = s_cs[slot1 - 1];
                 const int tau = pos >> 4, pp = pos & 15;
-                uint4 &kx = s_stage[bf][(2 * kRopeStep + tau) * 64 + 16 * gg + pp];
-                uint4 &ky = s_stage[bf][(2 * kRopeStep + 2 + tau) * 64 + 16 * gg + pp];
-                uint32_t xw[4] = {kx.x, kx.y, kx.z, kx.w}, yw[4] = {ky.x, ky.y, ky.z, ky.w};
-                // one plane at a time (few registers live beside the queries
-                // and accumulators): the stitch's fp64 turn and rounding
+                uint32_t *kx = reinterpret_cast<uint32_t *>(
+                    &s_stage[bb][(2 * kRopeStep + tau) * 64 + 16 * gg + pp]);
+                uint32_t *ky = reinterpret_cast<uint32_t *>(
+                    &s_stage[bb][(2 * kRopeStep + 2 + tau) * 64 + 16 * gg + pp]);
+                if constexpr (STYLE == PIC_ROPE_HALF) {
+                    // x of planes 8 gg + 2 qh, + 1 in word qh of the first rotary
+                    // k-step's piece, their y (32 planes later) in the second's
+                    uint32_t wx = kx[qh], wy = ky[qh];
 #pragma unroll
-                for (int q = 0; q < 8; q++) {
-                    if constexpr (STYLE == PIC_ROPE_HALF) {
-                        // x of plane 8 gg + q in the first rotary k-step, its y
-                        // (32 planes later) in the second
-                        const double c = tab[2 * (8 * gg + q)], sn = tab[2 * (8 * gg + q) + 1];
-                        uint32_t &wx = xw[q >> 1], &wy = yw[q >> 1];
-                        const int sh = 16 * (q & 1);
+                    for (int h = 0; h < 2; h++) {
+                        const double2 cs = tab[8 * gg + 2 * qh + h];
+                        const int sh = 16 * h;
                         const double x = static_cast<double>(__uint_as_float(((wx >> sh) & 0xFFFFu) << 16));
                         const double y = static_cast<double>(__uint_as_float(((wy >> sh) & 0xFFFFu) << 16));
-                        const uint32_t nx = f64_to_bf16(x * c - y * sn), ny = f64_to_bf16(x * sn + y * c);
+                        const uint32_t nx = f64_to_bf16(x * cs.x - y * cs.y);
+                        const uint32_t ny = f64_to_bf16(x * cs.y + y * cs.x);
                         wx = (wx & ~(0xFFFFu << sh)) | (nx << sh);
                         wy = (wy & ~(0xFFFFu << sh)) | (ny << sh);
-                    } else {
-                        // a whole pair per word: planes 4 gg + q (first k-step),
-                        // 16 + 4 gg + q - 4 (second)
-                        const int plane = q < 4 ? 4 * gg + q : 16 + 4 * gg + (q - 4);
-                        const double c = tab[2 * plane], sn = tab[2 * plane + 1];
-                        uint32_t &w = q < 4 ? xw[q] : yw[q - 4];
+                    }
+                    kx[qh] = wx;
+                    ky[qh] = wy;
+                } else {
+                    // a whole pair per word: words 2 qh, 2 qh + 1 of the first
+                    // piece hold planes 4 gg + 2 qh, + 1 (qh < 2); of the second,
+                    // planes 16 + 4 gg + 2 qh - 4, + 1 (qh >= 2)
+                    uint32_t *wp = qh < 2 ? kx + 2 * qh : ky + 2 * qh - 4;
+                    const int plane0 = qh < 2 ? 4 * gg + 2 * qh : 16 + 4 * gg + 2 * qh - 4;
+#pragma unroll
+                    for (int h = 0; h < 2; h++) {
+                        const double2 cs = tab[plane0 + h];
+                        const uint32_t w = wp[h];
                         const double x = bf16_lo(w), y = bf16_hi(w);
-                        w = f64_to_bf16(x * c - y * sn) | (f64_to_bf16(x * sn + y * c) << 16);
+                        wp[h] = f64_to_bf16(x * cs.x - y * cs.y) | (f64_to_bf16(x * cs.y + y * cs.x) << 16);
                     }
                 }
-                kx = make_uint4(xw[0], xw[1], xw[2], xw[3]);
-                ky = make_uint4(yw[0], yw[1], yw[2], yw[3]);
             }
+        };
+
+        // NB = 3: step i is computed while step i + 1 is turned and step
+        // i + 2 loads, one barrier per step; NB = 2: the next step loads
+        // while this one is turned and computed; NB = 1: it loads after
+        stage(0, 0);
+        if constexpr (NB == 3) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
+            if (kStepPos < B.ntok) stage(kStepPos, 1);
+            turn(0);
+        }
+        int bf = 0;
+        for (int p0 = 0; p0 < B.ntok; p0 += kStepPos) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();  // the step is in LDS (every wave's share) and its meta written
+            const int cb = bf;  // the buffer computed on
+            if constexpr (NB == 3) {
+                const int bn = bf == 2 ? 0 : bf + 1, bnn = bn == 2 ? 0 : bn + 1;
+                if (p0 + 2 * kStepPos < B.ntok) stage(p0 + 2 * kStepPos, bnn);
+                if (p0 + kStepPos < B.ntok) turn(bn);
+                bf = bn;
+            } else {
+                if (NB == 2 && p0 + kStepPos < B.ntok) stage(p0 + kStepPos, bf ^ 1);
+                turn(bf);
+                __syncthreads();
+                bf = (bf + 1) % NB;
+            }
 
             // ---- logits S^T for the wave's heads
-            const uint4 *stg = s_stage[bf];
+            const uint4 *stg = s_stage[cb];
             f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int s = 0; s < kKSteps; s++) {
@@ -274,45 +344,43 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
                 if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
             }
 
-            // ---- online softmax over head r16: this lane holds positions
-            // p0 + 16 tau + 4 g + i
+            // ---- online softmax over head r16 (log2 units): this lane holds
+            // positions p0 + 16 tau + 4 g + i.  The running max is kept until a
+            // logit passes it by kLazy (weights stay below 2^kLazy; the merge
+            // uses the same reference), so the accumulator is seldom rescaled
             float sc[8];
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++)
+            for (int tau = 0; tau < 2; tau++) {
+                const f32x4 pb = *reinterpret_cast<const f32x4 *>(&s_pbias[cb][16 * tau + 4 * g]);
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int pos = 16 * tau + 4 * g + i;
-                    float x = st[tau][i] * a.scale;
-                    if (s_pmeta[bf][pos] & kMetaDamp) x += a.sink_bias;
-                    sc[4 * tau + i] = p0 + pos < B.ntok ? x : -INFINITY;
-                }
-            float mx = sc[0];
-#pragma unroll
-            for (int k = 1; k < 8; k++) mx = fmaxf(mx, sc[k]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run, mx);  // finite: position p0 is in the block
-            const float alpha = __expf(m_run - m_new);
-            float pw[8], psum = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                pw[k] = __expf(sc[k] - m_new);
-                psum += pw[k];
+                for (int i = 0; i < 4; i++) sc[4 * tau + i] = fmaf(st[tau][i], scale2, pb[i]);
             }
+            float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            mx = row_max(mx);  // finite: position p0 is in the block
+            const bool bump = mx > m_run + kLazy;  // (-inf + kLazy stays -inf)
+            const float m_new = bump ? mx : m_run;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+            float pw[8];
+#pragma unroll
+            for (int k = 0; k < 8; k++) pw[k] = __builtin_amdgcn_exp2f(sc[k] - m_new);
+            const float psum = ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
             l_run = l_run * alpha + psum;
             m_run = m_new;
+            if (__any(bump)) {
 #pragma unroll
-            for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
+                for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
+            }
             // weights as B of O^T += V^T P^T: k index 8 g + j is position
             // 4 g + j (j < 4) or 16 + 4 g + j - 4, the order of pw; hi + lo bf16
             uint32_t hi[4], lo[4];
 #pragma unroll
             for (int k = 0; k < 4; k++) {
-                const uint32_t h0 = f32_to_bf16(pw[2 * k]), h1 = f32_to_bf16(pw[2 * k + 1]);
-                const float r0 = pw[2 * k] - __uint_as_float(h0 << 16);
-                const float r1 = pw[2 * k + 1] - __uint_as_float(h1 << 16);
-                hi[k] = h0 | (h1 << 16);
-                lo[k] = f32_to_bf16(r0) | (f32_to_bf16(r1) << 16);
+                const f32x2 pr = {pw[2 * k], pw[2 * k + 1]};
+                hi[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                const f32x2 rr = {pw[2 * k] - __uint_as_float(hi[k] << 16),
+                                  pw[2 * k + 1] - __uint_as_float(hi[k] & 0xFFFF0000u)};
+                lo[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
             }
             const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
             const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
@@ -389,7 +457,7 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(const MlaA
         __syncthreads();
         if (d < nb) {
             const float *ml = a.part_ml + ((base + d) * hq + j) * 2;
-            const float f = __expf(ml[0] - M);
+            const float f = __builtin_amdgcn_exp2f(ml[0] - M);  // log2 units
             s_f[d] = f;
             s_lf[d] = ml[1] * f;
         }
@@ -426,7 +494,7 @@ AttnTile advance(AttnTile t, int32_t k) {
 // [tiles][blocks][item -> first block (+ end)][request -> first item (+ end)].
 struct LatentMap {
     std::vector<uint8_t> bytes;
-    size_t off_blocks = 0, off_items = 0, off_reqs = 0;
+    size_t off_blocks = 0, off_items = 0, off_reqs = 0, off_tabs = 0;
     int32_t n_items = 0, n_blocks = 0;
 };
 
@@ -434,6 +502,7 @@ LatentMap build_latent_map(const Problem &p, int64_t target) {
     std::vector<AttnTile> tiles;
     std::vector<AttnBlock> blocks;
     std::vector<int32_t> item0, req0;
+    std::vector<int32_t> btabs;  // kBlockTabs per block
     int64_t total = 0;
     for (int64_t L : p.context) total += L;
     const int32_t n_req = static_cast<int32_t>(p.context.size());
@@ -444,9 +513,15 @@ LatentMap build_latent_map(const Problem &p, int64_t target) {
         const int64_t S = (L + n - 1) / n;  // positions per item
         int64_t left = L, item_left = 0;
         AttnBlock blk{r, 0, 0, 0};
+        std::vector<int32_t> tabs;  // the open block's shift tables
         auto close_block = [&]() {
-            if (blk.ntiles > 0) blocks.push_back(blk);
+            if (blk.ntiles > 0) {
+                blocks.push_back(blk);
+                for (int j = 0; j < kBlockTabs; j++)
+                    btabs.push_back(j < static_cast<int>(tabs.size()) ? tabs[j] : -1);
+            }
             blk = AttnBlock{r, static_cast<int32_t>(tiles.size()), 0, 0};
+            tabs.clear();
         };
         for (int32_t t = p.req_tile0[r]; t < p.req_tile0[r + 1] && left > 0; t++) {
             AttnTile T = p.atiles[t];
@@ -456,7 +531,13 @@ LatentMap build_latent_map(const Problem &p, int64_t target) {
                     item0.push_back(static_cast<int32_t>(blocks.size()));
                     item_left = std::min(S, left);
                 }
-                if (blk.ntok == kBlockPos || blk.ntiles == kItemTiles) close_block();
+                const bool new_tab = T.cs_idx >= 0 &&
+                                     std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end();
+                if (blk.ntok == kBlockPos || blk.ntiles == kItemTiles ||
+                    (new_tab && static_cast<int>(tabs.size()) == kBlockTabs))
+                    close_block();
+                if (T.cs_idx >= 0 && std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end())
+                    tabs.push_back(T.cs_idx);
                 const int32_t take = static_cast<int32_t>(std::min<int64_t>(
                     {int64_t{T.ntok}, item_left, int64_t{kBlockPos - blk.ntok}}));
                 AttnTile piece = T;
@@ -486,6 +567,7 @@ LatentMap build_latent_map(const Problem &p, int64_t target) {
     m.off_blocks = put(blocks.data(), blocks.size() * sizeof(AttnBlock));
     m.off_items = put(item0.data(), item0.size() * sizeof(int32_t));
     m.off_reqs = put(req0.data(), req0.size() * sizeof(int32_t));
+    m.off_tabs = put(btabs.data(), btabs.size() * sizeof(int32_t));
     m.n_items = static_cast<int32_t>(item0.size()) - 1;
     m.n_blocks = static_cast<int32_t>(blocks.size());
     return m;
@@ -508,7 +590,7 @@ constexpr int kNb1 = PIC_MLA_NB1;
 template <int STYLE>
 hipError_t launch_block(int w, dim3 grid, hipStream_t stream, const MlaArgs &a, int32_t layer) {
     switch (w) {
-        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 2>), grid, dim3(512), 0, stream, a, layer); break;
+        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 3>), grid, dim3(512), 0, stream, a, layer); break;
         case 4: hipLaunchKernelGGL((mla_block_kernel<STYLE, 4, 2>), grid, dim3(256), 0, stream, a, layer); break;
         case 2: hipLaunchKernelGGL((mla_block_kernel<STYLE, 2, 2>), grid, dim3(128), 0, stream, a, layer); break;
         default: hipLaunchKernelGGL((mla_block_kernel<STYLE, 1, kNb1>), grid, dim3(64), 0, stream, a, layer); break;
@@ -600,6 +682,7 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
             plan->latent_off_blocks = m.off_blocks;
             plan->latent_off_items = m.off_items;
             plan->latent_off_reqs = m.off_reqs;
+            plan->latent_off_tabs = m.off_tabs;
             plan->latent_n_items = m.n_items;
             plan->latent_n_blocks = m.n_blocks;
             plan->latent_key = target;
@@ -630,6 +713,7 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     a.blocks = reinterpret_cast<const AttnBlock *>(lm + plan->latent_off_blocks);
     a.item_block0 = reinterpret_cast<const int32_t *>(lm + plan->latent_off_items);
     a.req_item0 = reinterpret_cast<const int32_t *>(lm + plan->latent_off_reqs);
+    a.block_tabs = reinterpret_cast<const int32_t *>(lm + plan->latent_off_tabs);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = static_cast<const uint16_t *>(pool->k);
     a.cache_k = static_cast<const uint16_t *>(cache->k);

@@ -148,7 +148,7 @@ struct pic_plan {
     size_t latent_bytes = 0;
     int64_t latent_key = -1;
     std::vector<uint8_t> latent_host;  // the uploaded bytes (alive for the copy)
-    size_t latent_off_blocks = 0, latent_off_items = 0, latent_off_reqs = 0;
+    size_t latent_off_blocks = 0, latent_off_items = 0, latent_off_reqs = 0, latent_off_tabs = 0;
     int32_t latent_n_items = 0, latent_n_blocks = 0;
     // pic_attend_boundary work items (attend_boundary.hip), the same way
     void *d_bnd = nullptr;
