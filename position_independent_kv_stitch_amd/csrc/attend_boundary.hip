@@ -41,6 +41,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "lds_load.hpp"
 #include "pic_internal.hpp"
 #include "rotate.hpp"
 
@@ -59,7 +60,7 @@ constexpr int kDTiles = kDim / 16;        // output tiles of 16 dims
 constexpr int kPT = PIC_BND_POS_TILES;   // 16-position tiles per step (2 or 4)
 constexpr int kStepPos = 16 * kPT;        // positions per step
 constexpr int kSlabs = 2 * kKSteps * kPT; // 1 KB slabs per step: K, then V
-constexpr int kNBuf = 3;                  // staging buffers (computed, turned, loading)
+constexpr int kNBuf = 4;                  // staging buffers (computed, turned, two loading)
 #ifndef PIC_BND_WAVES
 #define PIC_BND_WAVES 8
 #endif
@@ -327,8 +328,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                 const int kind = jl / kKSteps, s = jl % kKSteps;
                 const uint16_t *src = (kind == 0 ? kr : vr) + 32 * s;
                 const int slab = kind * kKSteps * kPT + s * kPT + my_tau;
-                __builtin_amdgcn_global_load_lds((gptr_t)src, (lptr_t)(&s_stage[bf][slab * 64]),
-                                                 16, 0, 0);
+                load_lds16(src, &s_stage[bf][slab * 64]);
             }
         };
 
@@ -385,25 +385,33 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             }
         };
 
-        // three buffers: step i is computed while step i + 1 is turned and
-        // step i + 2 is loaded, with one barrier per step
+        // four buffers: step i is computed while step i + 1 is turned and
+        // steps i + 2, i + 3 load, with one barrier per step.  Each stage call
+        // issues kSlabsPerWave loads per wave, and they complete in order, so
+        // waiting until at most n loads are outstanding leaves the newest n
+        // (a later step's) in flight.
+        auto wait_loads = [](int n) {
+            if (n >= 2 * kSlabsPerWave) wait_vm<2 * kSlabsPerWave>();
+            else if (n >= kSlabsPerWave) wait_vm<kSlabsPerWave>();
+            else wait_vm<0>();
+        };
+        const int nsteps = (ntok + kStepPos - 1) / kStepPos;
         stage(0, 0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (nsteps > 1) stage(kStepPos, 1);
+        if (nsteps > 2) stage(2 * kStepPos, 2);
+        wait_loads((nsteps > 1 ? kSlabsPerWave : 0) + (nsteps > 2 ? kSlabsPerWave : 0));
         __syncthreads();
-        if (kStepPos < ntok) stage(kStepPos, 1);
         turn(0);
-        int bf = 0;
-        for (int p0 = 0; p0 < ntok; p0 += kStepPos) {
-            // this wave's loads of step i + 1 are in; after the barrier every
-            // wave's are, step i is turned, and step i - 1's buffer is free
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        for (int i = 0; i < nsteps; i++) {
+            const int p0 = i * kStepPos;
+            // step i + 1's loads are in (step i + 2's may not be); after the
+            // barrier every wave's are, step i is turned, and step i - 1's
+            // buffer is free
+            wait_loads(i + 2 < nsteps ? kSlabsPerWave : 0);
             __syncthreads();
-            const int bn = bf == kNBuf - 1 ? 0 : bf + 1;
-            const int bnn = bn == kNBuf - 1 ? 0 : bn + 1;
-            if (p0 + 2 * kStepPos < ntok) stage(p0 + 2 * kStepPos, bnn);
-            if (p0 + kStepPos < ntok) turn(bn);
-            const int cur_bf = bf;
-            bf = bn;
+            const int cur_bf = i & (kNBuf - 1);
+            if (i + 3 < nsteps) stage(p0 + 3 * kStepPos, (i + 3) & (kNBuf - 1));
+            if (i + 1 < nsteps) turn((i + 1) & (kNBuf - 1));
 
             const int step_pos = bpos + p0;  // context position of the step's first row
             bool any = false;

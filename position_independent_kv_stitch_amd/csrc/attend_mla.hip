@@ -47,6 +47,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "lds_load.hpp"
 #include "pic_internal.hpp"
 #include "rotate.hpp"
 
@@ -251,8 +252,7 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
                 const uint16_t *row = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
                 for (int j = 2 * wave + tau; j < kSlabs; j += 2 * W) {
                     const int s = j >> 1;
-                    __builtin_amdgcn_global_load_lds((gptr_t)(row + 32 * s),
-                                                     (lptr_t)(&s_stage[bf][j * 64]), 16, 0, 0);
+                    load_lds16(row + 32 * s, &s_stage[bf][j * 64]);
                 }
             }
         };
@@ -305,31 +305,45 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
             }
         };
 
-        // NB = 3: step i is computed while step i + 1 is turned and step
-        // i + 2 loads, one barrier per step; NB = 2: the next step loads
-        // while this one is turned and computed; NB = 1: it loads after
+        // NB = 4: step i is computed while step i + 1 is turned and steps
+        // i + 2, i + 3 load, one barrier per step; NB = 2: the next step loads
+        // while this one is turned and computed; NB = 1: it loads after.  A
+        // stage call issues at least kMinLoads loads per wave (wave 0 may
+        // issue more), which complete in order: waiting until at most n
+        // kMinLoads are outstanding leaves the newest n stage calls in flight.
+        constexpr int kMinLoads = 2 * ((kSlabs - 2 * W) / (2 * W) + 1);
+        const int nsteps = (B.ntok + kStepPos - 1) / kStepPos;
         stage(0, 0);
-        if constexpr (NB == 3) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (NB == 4) {
+            if (nsteps > 1) stage(kStepPos, 1);
+            if (nsteps > 2) stage(2 * kStepPos, 2);
+            const int newer = (nsteps > 1) + (nsteps > 2);
+            if (newer == 2) wait_vm<2 * kMinLoads>();
+            else if (newer == 1) wait_vm<kMinLoads>();
+            else wait_vm<0>();
             __syncthreads();
-            if (kStepPos < B.ntok) stage(kStepPos, 1);
             turn(0);
         }
-        int bf = 0;
-        for (int p0 = 0; p0 < B.ntok; p0 += kStepPos) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __syncthreads();  // the step is in LDS (every wave's share) and its meta written
-            const int cb = bf;  // the buffer computed on
-            if constexpr (NB == 3) {
-                const int bn = bf == 2 ? 0 : bf + 1, bnn = bn == 2 ? 0 : bn + 1;
-                if (p0 + 2 * kStepPos < B.ntok) stage(p0 + 2 * kStepPos, bnn);
-                if (p0 + kStepPos < B.ntok) turn(bn);
-                bf = bn;
-            } else {
-                if (NB == 2 && p0 + kStepPos < B.ntok) stage(p0 + kStepPos, bf ^ 1);
-                turn(bf);
+        for (int i = 0; i < nsteps; i++) {
+            const int p0 = i * kStepPos;
+            int cb;  // the buffer computed on
+            if constexpr (NB == 4) {
+                // step i + 1's loads are in (i + 2's may not be); after the
+                // barrier every wave's are, step i is turned, step i - 1's
+                // buffer is free
+                if (i + 2 < nsteps) wait_vm<kMinLoads>();
+                else wait_vm<0>();
                 __syncthreads();
-                bf = (bf + 1) % NB;
+                cb = i & 3;
+                if (i + 3 < nsteps) stage(p0 + 3 * kStepPos, (i + 3) & 3);
+                if (i + 1 < nsteps) turn((i + 1) & 3);
+            } else {
+                wait_vm<0>();
+                __syncthreads();  // the step is in LDS (every wave's share) and its meta written
+                cb = NB == 2 ? (i & 1) : 0;
+                if (NB == 2 && i + 1 < nsteps) stage(p0 + kStepPos, cb ^ 1);
+                turn(cb);
+                __syncthreads();
             }
 
             // ---- logits S^T for the wave's heads
@@ -409,7 +423,7 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
                 if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
-            if (NB == 1 && p0 + kStepPos < B.ntok) {
+            if (NB == 1 && i + 1 < nsteps) {
                 __syncthreads();  // every wave is done with the buffer
                 stage(p0 + kStepPos, 0);
             }
@@ -590,7 +604,7 @@ constexpr int kNb1 = PIC_MLA_NB1;
 template <int STYLE>
 hipError_t launch_block(int w, dim3 grid, hipStream_t stream, const MlaArgs &a, int32_t layer) {
     switch (w) {
-        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 3>), grid, dim3(512), 0, stream, a, layer); break;
+        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 4>), grid, dim3(512), 0, stream, a, layer); break;
         case 4: hipLaunchKernelGGL((mla_block_kernel<STYLE, 4, 2>), grid, dim3(256), 0, stream, a, layer); break;
         case 2: hipLaunchKernelGGL((mla_block_kernel<STYLE, 2, 2>), grid, dim3(128), 0, stream, a, layer); break;
         default: hipLaunchKernelGGL((mla_block_kernel<STYLE, 1, kNb1>), grid, dim3(64), 0, stream, a, layer); break;
