@@ -10,6 +10,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(HERE, "libpic_stitch.so")
 SOURCES = [os.path.join(CSRC, "stitch.hip"), os.path.join(CSRC, "attend.hip"),
            os.path.join(CSRC, "attend_mla.hip"), os.path.join(CSRC, "attend_boundary.hip"),
+           os.path.join(CSRC, "attend_gqa.hip"),
            os.path.join(CSRC, "cdc.hip"), os.path.join(CSRC, "plan.cpp"),
            os.path.join(CSRC, "attend_plan.cpp")]
 

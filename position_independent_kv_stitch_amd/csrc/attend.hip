@@ -38,6 +38,8 @@
 namespace pic {
 
 pic_status hip_fail(hipError_t e, const char *what);  // stitch.hip
+pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pic_kv_view *cache,
+                      const pic_attend_args *args, hipStream_t stream);  // attend_gqa.hip
 
 namespace {
 
@@ -566,6 +568,8 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     st = ensure_device_plan(plan, stream_);
     if (st) return st;
+    // bf16 128-dim rows: the matrix-core path (attend_gqa.hip)
+    if (gqa_tile_path(p, args->num_q_heads / H)) return attend_gqa(plan, pool, cache, args, stream);
     const size_t need = p.ablocks.size() * static_cast<size_t>(args->num_q_heads) *
                         (static_cast<size_t>(D) + 2) * sizeof(float);
     {

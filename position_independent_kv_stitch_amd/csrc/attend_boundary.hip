@@ -605,15 +605,6 @@ __global__ void __launch_bounds__(64) bnd_combine_kernel(const BndArgs a) {
 
 // ------------------------------------------------------------------ host
 
-AttnTile advance(AttnTile t, int32_t k) {
-    if (t.kind == kPoolRows) t.a += k;
-    else t.b += k;
-    if (t.sink_dist < kNoSink)
-        t.sink_dist = static_cast<int32_t>(std::min<int64_t>(int64_t{t.sink_dist} + k, kNoSink));
-    t.ntok -= k;
-    return t;
-}
-
 struct BndMap {
     std::vector<uint8_t> bytes;
     size_t off_blocks = 0, off_bpos = 0, off_items = 0, off_reqs = 0, off_limit = 0, off_tabs = 0;
@@ -714,7 +705,7 @@ BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t 
                 item_left -= take;
                 left -= take;
                 pos += take;
-                T = advance(T, take);
+                T = advance_tile(T, take);
                 if (item_left == 0) close_block();
             }
         }

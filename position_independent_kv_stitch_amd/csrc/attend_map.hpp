@@ -53,4 +53,24 @@ void build_attention_map(Problem *p, const pic_chunk *chunks, const pic_request 
 // Group every request's tiles into work blocks (after the last request).
 void build_attention_blocks(Problem *p);
 
+// Work items of one launch of the latent and GQA tile kernels: request r gets
+// a share of `target` items in proportion to its context (at least one, at
+// most max_per_request), each of ceil(L / n) positions cut from its map tiles
+// (tiles split where an item ends), stored as blocks of at most
+// kItemBlockPos positions, kItemBlockTiles tiles and kItemBlockTabs shift
+// tables.  Packed as [tiles][blocks][item -> first block (+ end)]
+// [request -> first item (+ end)][block -> its shift tables, -1 padded].
+constexpr int kItemBlockPos = 4096;
+constexpr int kItemBlockTiles = 64;
+constexpr int kItemBlockTabs = 4;
+struct ItemMap {
+    std::vector<uint8_t> bytes;
+    size_t off_blocks = 0, off_items = 0, off_reqs = 0, off_tabs = 0;
+    int32_t n_items = 0, n_blocks = 0;
+};
+ItemMap build_item_map(const Problem &p, int64_t target, int64_t max_per_request);
+
+// A map tile moved k positions on (its rows are consecutive in its source).
+AttnTile advance_tile(AttnTile t, int32_t k);
+
 }  // namespace pic

@@ -67,11 +67,10 @@ constexpr int kDTiles = kVDim / 16;       // output tiles of 16 dims
 constexpr int kGroupHeads = 16;           // query heads per wave
 constexpr int kStepPos = 32;              // positions per step: two 16-position tiles
 constexpr int kSlabs = 2 * kKSteps;       // 1 KB slabs of a staged step
-constexpr int kItemTiles = 64;            // map tiles per latent block at most
-constexpr int kBlockPos = 4096;           // positions per latent block at most
+constexpr int kItemTiles = kItemBlockTiles;  // map tiles per block at most
 constexpr int kCombineThreads = 256;
 
-constexpr int kBlockTabs = 4;             // shift tables per latent block at most (kept in LDS)
+constexpr int kBlockTabs = kItemBlockTabs;  // shift tables per block at most (kept in LDS)
 constexpr int kHalfR = kRopeDim / 2;      // rotary planes
 constexpr float kLazy = 12.f;             // running-max slack of the online softmax (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -491,102 +490,6 @@ __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(const MlaA
 
 // ------------------------------------------------------------------ host
 
-// A map tile moved k positions on (its rows are consecutive in its source).
-AttnTile advance(AttnTile t, int32_t k) {
-    if (t.kind == kPoolRows) t.a += k;
-    else t.b += k;
-    if (t.sink_dist < kNoSink)
-        t.sink_dist = static_cast<int32_t>(std::min<int64_t>(int64_t{t.sink_dist} + k, kNoSink));
-    t.ntok -= k;
-    return t;
-}
-
-// Work items of one launch: request r gets a share of `target` items in
-// proportion to its context (at least one), each of ceil(L / n) positions
-// cut from its map tiles (tiles split where an item ends), stored as blocks
-// of at most kBlockPos positions and kItemTiles tiles.  Packed as
-// [tiles][blocks][item -> first block (+ end)][request -> first item (+ end)].
-struct LatentMap {
-    std::vector<uint8_t> bytes;
-    size_t off_blocks = 0, off_items = 0, off_reqs = 0, off_tabs = 0;
-    int32_t n_items = 0, n_blocks = 0;
-};
-
-LatentMap build_latent_map(const Problem &p, int64_t target) {
-    std::vector<AttnTile> tiles;
-    std::vector<AttnBlock> blocks;
-    std::vector<int32_t> item0, req0;
-    std::vector<int32_t> btabs;  // kBlockTabs per block
-    int64_t total = 0;
-    for (int64_t L : p.context) total += L;
-    const int32_t n_req = static_cast<int32_t>(p.context.size());
-    for (int32_t r = 0; r < n_req; r++) {
-        req0.push_back(static_cast<int32_t>(item0.size()));
-        const int64_t L = p.context[r];
-        const int64_t n = std::max<int64_t>(1, (target * L + total / 2) / std::max<int64_t>(total, 1));
-        const int64_t S = (L + n - 1) / n;  // positions per item
-        int64_t left = L, item_left = 0;
-        AttnBlock blk{r, 0, 0, 0};
-        std::vector<int32_t> tabs;  // the open block's shift tables
-        auto close_block = [&]() {
-            if (blk.ntiles > 0) {
-                blocks.push_back(blk);
-                for (int j = 0; j < kBlockTabs; j++)
-                    btabs.push_back(j < static_cast<int>(tabs.size()) ? tabs[j] : -1);
-            }
-            blk = AttnBlock{r, static_cast<int32_t>(tiles.size()), 0, 0};
-            tabs.clear();
-        };
-        for (int32_t t = p.req_tile0[r]; t < p.req_tile0[r + 1] && left > 0; t++) {
-            AttnTile T = p.atiles[t];
-            while (T.ntok > 0 && left > 0) {
-                if (item_left == 0) {  // a new item starts here
-                    close_block();
-                    item0.push_back(static_cast<int32_t>(blocks.size()));
-                    item_left = std::min(S, left);
-                }
-                const bool new_tab = T.cs_idx >= 0 &&
-                                     std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end();
-                if (blk.ntok == kBlockPos || blk.ntiles == kItemTiles ||
-                    (new_tab && static_cast<int>(tabs.size()) == kBlockTabs))
-                    close_block();
-                if (T.cs_idx >= 0 && std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end())
-                    tabs.push_back(T.cs_idx);
-                const int32_t take = static_cast<int32_t>(std::min<int64_t>(
-                    {int64_t{T.ntok}, item_left, int64_t{kBlockPos - blk.ntok}}));
-                AttnTile piece = T;
-                piece.ntok = take;
-                piece.tok0 = blk.ntok;
-                tiles.push_back(piece);
-                blk.ntiles++;
-                blk.ntok += take;
-                item_left -= take;
-                left -= take;
-                T = advance(T, take);
-                if (item_left == 0) close_block();
-            }
-        }
-        close_block();
-    }
-    req0.push_back(static_cast<int32_t>(item0.size()));
-    item0.push_back(static_cast<int32_t>(blocks.size()));
-    LatentMap m;
-    auto put = [&](const void *src, size_t n) {
-        const size_t at = (m.bytes.size() + 15) & ~size_t{15};
-        m.bytes.resize(at + n);
-        if (n) std::memcpy(m.bytes.data() + at, src, n);
-        return at;
-    };
-    put(tiles.data(), tiles.size() * sizeof(AttnTile));
-    m.off_blocks = put(blocks.data(), blocks.size() * sizeof(AttnBlock));
-    m.off_items = put(item0.data(), item0.size() * sizeof(int32_t));
-    m.off_reqs = put(req0.data(), req0.size() * sizeof(int32_t));
-    m.off_tabs = put(btabs.data(), btabs.size() * sizeof(int32_t));
-    m.n_items = static_cast<int32_t>(item0.size()) - 1;
-    m.n_blocks = static_cast<int32_t>(blocks.size());
-    return m;
-}
-
 int cu_count() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -671,7 +574,7 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
         std::lock_guard<std::mutex> lock(plan->mu);
         hipError_t e;
         if (plan->latent_key != target) {
-            LatentMap m = build_latent_map(p, target);
+            ItemMap m = build_item_map(p, target, int64_t{1} << 30);
             if (plan->d_latent) {
                 e = hipDeviceSynchronize();  // earlier launches may read the old items
                 if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");

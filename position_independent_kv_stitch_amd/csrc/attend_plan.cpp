@@ -10,6 +10,7 @@
 // Caching for LLM Serving, "1. Identifying and Neutralizing Pseudo-Sinks").
 
 #include <algorithm>
+#include <cstring>
 
 #include "pic_internal.hpp"
 
@@ -122,6 +123,93 @@ void build_attention_blocks(Problem *p) {
         }
     }
     p->req_block0.push_back(static_cast<int32_t>(p->ablocks.size()));
+}
+
+// A map tile moved k positions on (its rows are consecutive in its source).
+AttnTile advance_tile(AttnTile t, int32_t k) {
+    if (t.kind == kPoolRows) t.a += k;
+    else t.b += k;
+    if (t.sink_dist < kNoSink)
+        t.sink_dist = static_cast<int32_t>(std::min<int64_t>(int64_t{t.sink_dist} + k, kNoSink));
+    t.ntok -= k;
+    return t;
+}
+
+ItemMap build_item_map(const Problem &p, int64_t target, int64_t max_per_request) {
+    std::vector<AttnTile> tiles;
+    std::vector<AttnBlock> blocks;
+    std::vector<int32_t> item0, req0;
+    std::vector<int32_t> btabs;  // kItemBlockTabs per block
+    int64_t total = 0;
+    for (int64_t L : p.context) total += L;
+    const int32_t n_req = static_cast<int32_t>(p.context.size());
+    for (int32_t r = 0; r < n_req; r++) {
+        req0.push_back(static_cast<int32_t>(item0.size()));
+        const int64_t L = p.context[r];
+        const int64_t n = std::min<int64_t>(
+            max_per_request,
+            std::max<int64_t>(1, (target * L + total / 2) / std::max<int64_t>(total, 1)));
+        const int64_t S = (L + n - 1) / n;  // positions per item
+        int64_t left = L, item_left = 0;
+        AttnBlock blk{r, 0, 0, 0};
+        std::vector<int32_t> tabs;  // the open block's shift tables
+        auto close_block = [&]() {
+            if (blk.ntiles > 0) {
+                blocks.push_back(blk);
+                for (int j = 0; j < kItemBlockTabs; j++)
+                    btabs.push_back(j < static_cast<int>(tabs.size()) ? tabs[j] : -1);
+            }
+            blk = AttnBlock{r, static_cast<int32_t>(tiles.size()), 0, 0};
+            tabs.clear();
+        };
+        for (int32_t t = p.req_tile0[r]; t < p.req_tile0[r + 1] && left > 0; t++) {
+            AttnTile T = p.atiles[t];
+            while (T.ntok > 0 && left > 0) {
+                if (item_left == 0) {  // a new item starts here
+                    close_block();
+                    item0.push_back(static_cast<int32_t>(blocks.size()));
+                    item_left = std::min(S, left);
+                }
+                const bool new_tab = T.cs_idx >= 0 &&
+                                     std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end();
+                if (blk.ntok == kItemBlockPos || blk.ntiles == kItemBlockTiles ||
+                    (new_tab && static_cast<int>(tabs.size()) == kItemBlockTabs))
+                    close_block();
+                if (T.cs_idx >= 0 && std::find(tabs.begin(), tabs.end(), T.cs_idx) == tabs.end())
+                    tabs.push_back(T.cs_idx);
+                const int32_t take = static_cast<int32_t>(std::min<int64_t>(
+                    {int64_t{T.ntok}, item_left, int64_t{kItemBlockPos - blk.ntok}}));
+                AttnTile piece = T;
+                piece.ntok = take;
+                piece.tok0 = blk.ntok;
+                tiles.push_back(piece);
+                blk.ntiles++;
+                blk.ntok += take;
+                item_left -= take;
+                left -= take;
+                T = advance_tile(T, take);
+                if (item_left == 0) close_block();
+            }
+        }
+        close_block();
+    }
+    req0.push_back(static_cast<int32_t>(item0.size()));
+    item0.push_back(static_cast<int32_t>(blocks.size()));
+    ItemMap m;
+    auto put = [&](const void *src, size_t n) {
+        const size_t at = (m.bytes.size() + 15) & ~size_t{15};
+        m.bytes.resize(at + n);
+        if (n) std::memcpy(m.bytes.data() + at, src, n);
+        return at;
+    };
+    put(tiles.data(), tiles.size() * sizeof(AttnTile));
+    m.off_blocks = put(blocks.data(), blocks.size() * sizeof(AttnBlock));
+    m.off_items = put(item0.data(), item0.size() * sizeof(int32_t));
+    m.off_reqs = put(req0.data(), req0.size() * sizeof(int32_t));
+    m.off_tabs = put(btabs.data(), btabs.size() * sizeof(int32_t));
+    m.n_items = static_cast<int32_t>(item0.size()) - 1;
+    m.n_blocks = static_cast<int32_t>(blocks.size());
+    return m;
 }
 
 }  // namespace pic

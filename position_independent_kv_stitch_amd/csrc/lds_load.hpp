@@ -16,13 +16,26 @@ namespace pic {
 // in issue order with the wave's other vector memory loads) and publishes
 // them to the other waves with a barrier.  lds must be the same for every
 // lane of the wave.
+// M0 is saved and restored around the load, so the compiler's own use of it
+// (it treats M0 as reserved) is not disturbed.  OFF is a byte offset that
+// the instruction adds to src (no address arithmetic per load); it adds the
+// same offset to the LDS address, so M0 is set OFF bytes before lds (lds
+// must be at least OFF bytes into the LDS).
+template <int OFF = 0>
 __device__ __forceinline__ void load_lds16(const void *src, const void *lds) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)lds)));
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(m0)
-                 : "memory", "m0");
+    static_assert(OFF >= 0 && OFF < 4096, "the instruction's offset field");
+    const uint32_t base = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)lds))) - OFF;
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off offset:%3\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(base), "n"(OFF)
+        : "memory");
 }
 
 // Wait until at most N of the wave's vector memory loads are outstanding.

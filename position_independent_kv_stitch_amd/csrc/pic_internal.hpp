@@ -125,6 +125,10 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
 
 Staged stage(const Problem &p);
 
+// The matrix-core path of pic_attend (attend_gqa.hip): whether it takes a
+// plan at a GQA group size, and its launch (arguments checked by pic_attend).
+bool gqa_tile_path(const Problem &p, int group);
+
 // Device side (stitch.hip): first-use upload of a plan's metadata, ordered on
 // `stream` (a hipStream_t); view checks shared by the launchers.
 pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream);
@@ -157,5 +161,12 @@ struct pic_plan {
     std::vector<uint8_t> bnd_host;
     size_t bnd_off[6] = {0, 0, 0, 0, 0, 0};  // blocks, block positions, items, requests,
                                              // limits, block shift tables
+    int32_t gqa_n_items = 0;
+    // pic_attend's matrix-core work items (attend_gqa.hip), the same way
+    void *d_gqa = nullptr;
+    size_t gqa_bytes = 0;
+    int64_t gqa_key = -1;
+    std::vector<uint8_t> gqa_host;
+    size_t gqa_off[4] = {0, 0, 0, 0};  // blocks, items, requests, block shift tables
     int32_t bnd_n_items = 0, bnd_n_reqs = 0, bnd_max_rows = 0;
 };

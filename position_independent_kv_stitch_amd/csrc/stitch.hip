@@ -545,6 +545,7 @@ void pic_plan_destroy(pic_plan_t *plan) {
         if (plan->d_work) (void)hipFree(plan->d_work);
         if (plan->d_latent) (void)hipFree(plan->d_latent);
         if (plan->d_bnd) (void)hipFree(plan->d_bnd);
+        if (plan->d_gqa) (void)hipFree(plan->d_gqa);
         if (plan->upload_event)
             (void)hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
         if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);

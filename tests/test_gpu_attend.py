@@ -10,6 +10,11 @@ block sums (<= 256 terms) and the cross-block combine add <= 320u, and the
 output is a convex combination of value rows.  So
 |out - oracle| <= 2e-4 * max|V| covers the worst case with margin; the test
 asserts 5e-4 * max|V|.
+
+bf16 plans with 128-dim rows take the matrix-core path, which turns the
+query instead of the keys and keeps the turned query as three bf16 terms
+(within 2^-24 of it, so the logit bound above holds) and the weights as two
+(relative error < 2^-16, adding < 2e-5 * max|V| to the output bound).
 """
 import sys
 
