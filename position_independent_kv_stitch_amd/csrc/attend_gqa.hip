@@ -53,13 +53,18 @@ namespace {
 constexpr int kDim = 128;                  // head row
 constexpr int kKSteps = kDim / 32;         // MFMA k-steps
 constexpr int kDTiles = kDim / 16;         // output tiles of 16 dims
-constexpr int kStepPos = 32;               // positions per step: two 16-position tiles
-constexpr int kSlabs = 4 * kKSteps;        // 1 KB slabs per step: K (s, tau), then V
+#ifndef PIC_GQA_PT
+#define PIC_GQA_PT 2
+#endif
+constexpr int kPT = PIC_GQA_PT;            // 16-position tiles per step (1 or 2)
+constexpr int kStepPos = 16 * kPT;         // positions per step
+constexpr int kSlabs = 2 * kKSteps * kPT;  // 1 KB slabs per step: K (s, tau), then V
 #ifndef PIC_GQA_STAGES
 #define PIC_GQA_STAGES 3
 #endif
 constexpr int kStages = PIC_GQA_STAGES;    // LDS stages per wave (steps in flight + 1)
-constexpr int kWavesPerCu = 3;             // waves whose rings fit a CU's LDS
+// waves whose rings (and ~3 KB of tables) fit a CU's 160 KB of LDS
+constexpr int kWavesPerCu = 160 * 1024 / (kStages * kSlabs * 1024 + 3 * 1024);
 constexpr int kMaxHalf = kDim / 2;         // rotary planes at most
 constexpr int kMaxItems = 64;              // items per request (the merge keeps them in lanes)
 constexpr float kLazy = 12.f;              // running-max slack of the online softmax (log2 units)
@@ -227,6 +232,21 @@ __device__ __forceinline__ void turn_query(const bf16x8 (&qf)[kKSteps], bf16x8 (
     }
 }
 
+// Wait until the stage calls issued after the oldest one (`newer` of them,
+// kSlabs loads each) are the only ones outstanding.
+template <int N>
+__device__ __forceinline__ void wait_newer(int newer) {
+    if constexpr (N > 0) {
+        if (newer >= N) {
+            wait_vm<N * kSlabs>();
+            return;
+        }
+        wait_newer<N - 1>(newer);
+    } else {
+        wait_vm<0>();
+    }
+}
+
 template <int STYLE>
 __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t layer) {
     // stage slab (kind, s, tau) = kind * 2 kKSteps + 2 s + tau (kind 0: K,
@@ -302,7 +322,7 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
         int cur[2] = {0, 0};
         auto stage = [&](int p0, int st) {
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++) {
+            for (int tau = 0; tau < kPT; tau++) {
                 int pi = p0 + 16 * tau + r16;
                 const bool valid = pi < B.ntok;
                 if (!valid) pi = p0;
@@ -318,14 +338,14 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
                 const uint16_t *kr = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
                 const uint16_t *vr = (pool ? a.pool_v : a.cache_v) + off + 8 * g;
                 // k-step s of the row is 64 s bytes on (the load's offset field)
-                load_lds16<0>(kr, &s_stage[st][(0 + tau) * 64]);
-                load_lds16<64>(kr, &s_stage[st][(2 + tau) * 64]);
-                load_lds16<128>(kr, &s_stage[st][(4 + tau) * 64]);
-                load_lds16<192>(kr, &s_stage[st][(6 + tau) * 64]);
-                load_lds16<0>(vr, &s_stage[st][(2 * kKSteps + 0 + tau) * 64]);
-                load_lds16<64>(vr, &s_stage[st][(2 * kKSteps + 2 + tau) * 64]);
-                load_lds16<128>(vr, &s_stage[st][(2 * kKSteps + 4 + tau) * 64]);
-                load_lds16<192>(vr, &s_stage[st][(2 * kKSteps + 6 + tau) * 64]);
+                load_lds16<0>(kr, &s_stage[st][(0 * kPT + tau) * 64]);
+                load_lds16<64>(kr, &s_stage[st][(1 * kPT + tau) * 64]);
+                load_lds16<128>(kr, &s_stage[st][(2 * kPT + tau) * 64]);
+                load_lds16<192>(kr, &s_stage[st][(3 * kPT + tau) * 64]);
+                load_lds16<0>(vr, &s_stage[st][(kKSteps * kPT + 0 * kPT + tau) * 64]);
+                load_lds16<64>(vr, &s_stage[st][(kKSteps * kPT + 1 * kPT + tau) * 64]);
+                load_lds16<128>(vr, &s_stage[st][(kKSteps * kPT + 2 * kPT + tau) * 64]);
+                load_lds16<192>(vr, &s_stage[st][(kKSteps * kPT + 3 * kPT + tau) * 64]);
             }
         };
 
@@ -335,19 +355,16 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
             const int p0 = i * kStepPos;
             const int slot = i % kStages;
             // step i's loads are in; the ones of the steps after it may not be
-            const int newer = min(kStages - 2, nsteps - 1 - i);
-            if (newer >= 2) wait_vm<2 * kSlabs>();
-            else if (newer == 1) wait_vm<kSlabs>();
-            else wait_vm<0>();
+            wait_newer<kStages - 2>(min(kStages - 2, nsteps - 1 - i));
             // the slot freed by step i - 1 takes step i + kStages - 1
             if (i + kStages - 1 < nsteps) stage(p0 + (kStages - 1) * kStepPos, (i + kStages - 1) % kStages);
 
             // ---- logits S^T, position tile by tile; the positions' chunk
             // classes (0: not turned, j + 1: block table j) pick the query
             const uint4 *stg = s_stage[slot];
-            f32x4 st[2];
+            f32x4 st[kPT];
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++) {
+            for (int tau = 0; tau < kPT; tau++) {
                 const uint4 cl4 = *reinterpret_cast<const uint4 *>(&s_pslot[slot][16 * tau + 4 * g]);
                 const uint32_t cls[4] = {cl4.x, cl4.y, cl4.z, cl4.w};
                 uint32_t present = (1u << cls[0]) | (1u << cls[1]) | (1u << cls[2]) | (1u << cls[3]);
@@ -362,7 +379,7 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
 #pragma unroll
                         for (int s = 0; s < kKSteps; s++)
                             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(stg[(2 * s + tau) * 64 + lane]), qf[s], sc, 0, 0, 0);
+                                as_bf16x8(stg[(s * kPT + tau) * 64 + lane]), qf[s], sc, 0, 0, 0);
                     } else {
                         int tab = btab[0];
 #pragma unroll
@@ -374,7 +391,7 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
                         }
 #pragma unroll
                         for (int s = 0; s < kKSteps; s++) {
-                            const bf16x8 kf = as_bf16x8(stg[(2 * s + tau) * 64 + lane]);
+                            const bf16x8 kf = as_bf16x8(stg[(s * kPT + tau) * 64 + lane]);
 #pragma unroll
                             for (int term = 0; term < 3; term++)
                                 sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qt[term][s], sc, 0, 0, 0);
@@ -394,60 +411,74 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
             // 16 tau + 4 g + e.  The running max is kept until a logit passes
             // it by kLazy (weights stay below 2^kLazy; the merge uses the same
             // reference), so the accumulator is seldom rescaled
-            float x[8];
+            constexpr int NV = 4 * kPT;  // positions of this lane: 16 tau + 4 g + e
+            float x[NV];
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++) {
+            for (int tau = 0; tau < kPT; tau++) {
                 const f32x4 pb = *reinterpret_cast<const f32x4 *>(&s_pbias[slot][16 * tau + 4 * g]);
 #pragma unroll
                 for (int e = 0; e < 4; e++) x[4 * tau + e] = fmaf(st[tau][e], scale2, pb[e]);
             }
-            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+            float mx = x[0];
+#pragma unroll
+            for (int k = 1; k < NV; k++) mx = fmaxf(mx, x[k]);
             mx = row_max(mx);  // finite: position p0 is in the block
             const bool bump = mx > m_run + kLazy;  // (-inf + kLazy stays -inf)
             const float m_new = bump ? mx : m_run;
             const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-            float pw[8];
+            float pw[NV], psum = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; k++) pw[k] = __builtin_amdgcn_exp2f(x[k] - m_new);
-            l_run = l_run * alpha + (((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7])));
+            for (int k = 0; k < NV; k++) {
+                pw[k] = __builtin_amdgcn_exp2f(x[k] - m_new);
+                psum += pw[k];
+            }
+            l_run = l_run * alpha + psum;
             m_run = m_new;
             if (__any(bump)) {
 #pragma unroll
                 for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
             }
-            // weights as B of O^T += V^T P^T: k index 8 g + j is position
-            // 4 g + j (j < 4) or 16 + 4 g + j - 4, the order of pw; hi + lo bf16
-            uint32_t hi[4], lo[4];
+            // weights as B of O^T += V^T P^T (hi + lo bf16): k index 8 g + j is
+            // position 4 g + j (j < 4) or 16 + 4 g + j - 4 with two position
+            // tiles, 4 g + j with one -- the order of pw
+            uint32_t hi[NV / 2], lo[NV / 2];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
+            for (int k = 0; k < NV / 2; k++) {
                 const f32x2 pr = {pw[2 * k], pw[2 * k + 1]};
                 hi[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
                 const f32x2 rr = {pw[2 * k] - __uint_as_float(hi[k] << 16),
                                   pw[2 * k + 1] - __uint_as_float(hi[k] & 0xFFFF0000u)};
                 lo[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
             }
-            const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
 
             // ---- A = V^T by transposing LDS reads: within each 16-lane
             // group, lane i receives element i % 4 of the 8-byte rows that
             // lanes 4 j + i / 4 address (j = 0..3), so lane i of group g
-            // addresses position 4 g + i / 4 (+ 16 for the second read), dims
-            // 16 t + 4 (i % 4) .. + 4
-            const char *stg8 = reinterpret_cast<const char *>(stg + 2 * kKSteps * 64);
+            // addresses position 4 g + i / 4 of a position tile, dims
+            // 16 t + 4 (i % 4) .. + 4, and receives dim 16 t + i of positions
+            // 4 g .. 4 g + 3
+            const char *stg8 = reinterpret_cast<const char *>(stg + kKSteps * kPT * 64);
             const int pq = r16 >> 2, dq = r16 & 3;
 #pragma unroll
             for (int t = 0; t < kDTiles; t++) {
                 const int gq = 2 * (t & 1) + (dq >> 1);
-                const int base = ((2 * (t >> 1)) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
+                const int base = (((t >> 1) * kPT) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
                 const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base));
-                const s16x4 v1 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base + 64 * 16));
-                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
-                const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+                if constexpr (kPT == 2) {
+                    const s16x4 v1 =
+                        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(stg8 + base + 64 * 16));
+                    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                    const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+                    const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                    const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+                } else {
+                    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0], hi[1]));
+                    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0], lo[1]));
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, acc[t], 0, 0, 0);
+                }
             }
         }
         __syncthreads();  // (one wave) the block's LDS reads are done before the next block's writes
