@@ -197,6 +197,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     // A fragment of lane 16 g + p)
     __shared__ __attribute__((aligned(16))) uint4 s_stage[kNBuf][kSlabs * 64];
     __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kMaxHalf];  // block's shift tables
+    __shared__ __attribute__((aligned(8))) float2 s_cs32[kBlockTabs][kMaxHalf];  // the same, fp32
     __shared__ StageTile s_tiles[kItemTiles];
     __shared__ uint32_t s_pslot[kNBuf][kStepPos];                       // shift-table slot + 1 (0: not turned)
     __shared__ __attribute__((aligned(16))) float s_pbias[kNBuf][kStepPos];  // damping, -inf past the block
@@ -300,6 +301,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             if (tab >= 0) {
                 const double *src = a.cs + (static_cast<int64_t>(tab) * half_r + pl) * 2;
                 s_cs[j][pl] = make_double2(src[0], src[1]);
+                s_cs32[j][pl] = make_float2(static_cast<float>(src[0]), static_cast<float>(src[1]));
             }
         }
         __syncthreads();
@@ -335,53 +337,83 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
         // turn the rotary pieces of moved chunk rows (K slabs) of buffer bb:
         // unit (position, 8-plane group m, half hh) turns 4 planes
         auto turn = [&](int bb) {
-            const int units = (half_r / 4) * kStepPos;
+            // unit (position, 8-plane group m): the lanes of a wave take one
+            // group of consecutive positions, so their 16-byte LDS pieces are
+            // contiguous (no bank conflicts) and their cos/sin reads coincide
+            const int units = (half_r / 8) * kStepPos;
             for (int u = tid; u < units; u += 64 * kWaves) {
-                const int pos = u / (half_r / 4), rem = u - pos * (half_r / 4);
-                const int m = rem >> 1, hh = rem & 1;
+                const int pos = u % kStepPos, m = u / kStepPos;
                 const uint32_t slot1 = s_pslot[bb][pos];
                 if (slot1 == 0u) continue;
-                const double2 *tab = s_cs[slot1 - 1];
+                const double2 *tab = s_cs[slot1 - 1] + 8 * m;
+                const float2 *tab32 = s_cs32[slot1 - 1] + 8 * m;
                 const int tau = pos >> 4, pp = pos & 15;
+                // the unit's two 16-byte pieces: half pairing, x of planes
+                // 8 m .. + 8 in piece (ro + 8 m) / 8 and their y half_r dims on;
+                // interleaved, whole pairs in pieces ro / 8 + 2 m and the next
+                int pa, pb;
                 if constexpr (STYLE == PIC_ROPE_HALF) {
-                    // x of planes 8 m + 4 hh .. + 4 in words 2 hh, 2 hh + 1 of
-                    // piece (ro + 8 m) / 8; y the same in piece (ro + half_r + 8 m) / 8
-                    const int px = (a.rope_offset + 8 * m) >> 3, py = px + (half_r >> 3);
-                    uint2 *kx = reinterpret_cast<uint2 *>(
-                                    &s_stage[bb][((px >> 2) * kPT + tau) * 64 + 16 * (px & 3) + pp]) + hh;
-                    uint2 *ky = reinterpret_cast<uint2 *>(
-                                    &s_stage[bb][((py >> 2) * kPT + tau) * 64 + 16 * (py & 3) + pp]) + hh;
-                    const uint2 xv = *kx, yv = *ky;
-                    uint32_t xw[2] = {xv.x, xv.y}, yw[2] = {yv.x, yv.y};
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const double2 cs = tab[8 * m + 4 * hh + q];
-                        uint32_t &wx = xw[q >> 1], &wy = yw[q >> 1];
-                        const int sh = 16 * (q & 1);
-                        const double x = static_cast<double>(__uint_as_float(((wx >> sh) & 0xFFFFu) << 16));
-                        const double y = static_cast<double>(__uint_as_float(((wy >> sh) & 0xFFFFu) << 16));
-                        const uint32_t nx = f64_to_bf16(x * cs.x - y * cs.y);
-                        const uint32_t ny = f64_to_bf16(x * cs.y + y * cs.x);
-                        wx = (wx & ~(0xFFFFu << sh)) | (nx << sh);
-                        wy = (wy & ~(0xFFFFu << sh)) | (ny << sh);
-                    }
-                    *kx = make_uint2(xw[0], xw[1]);
-                    *ky = make_uint2(yw[0], yw[1]);
+                    pa = (a.rope_offset + 8 * m) >> 3;
+                    pb = pa + (half_r >> 3);
                 } else {
-                    // whole pairs: piece (ro / 8) + 2 m + hh holds planes
-                    // 8 m + 4 hh .. + 4
-                    const int pc = (a.rope_offset >> 3) + 2 * m + hh;
-                    uint4 &kw = s_stage[bb][((pc >> 2) * kPT + tau) * 64 + 16 * (pc & 3) + pp];
-                    uint32_t wv[4] = {kw.x, kw.y, kw.z, kw.w};
-#pragma unroll
-                    for (int q = 0; q < 4; q++) {
-                        const double2 cs = tab[8 * m + 4 * hh + q];
-                        const double x = bf16_lo(wv[q]), y = bf16_hi(wv[q]);
-                        wv[q] = f64_to_bf16(x * cs.x - y * cs.y) |
-                                (f64_to_bf16(x * cs.y + y * cs.x) << 16);
-                    }
-                    kw = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                    pa = (a.rope_offset >> 3) + 2 * m;
+                    pb = pa + 1;
                 }
+                uint4 &ka = s_stage[bb][((pa >> 2) * kPT + tau) * 64 + 16 * (pa & 3) + pp];
+                uint4 &kb = s_stage[bb][((pb >> 2) * kPT + tau) * 64 + 16 * (pb & 3) + pp];
+                const uint4 va = ka, vb = kb;
+                const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+                // fp32 first; the fp64 turn only where it could round otherwise
+                uint32_t na[4], nb[4];
+                bool redo = false;
+                if constexpr (STYLE == PIC_ROPE_HALF) {
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {  // planes 2 k, 2 k + 1: word k of each piece
+                        float rx0, ry0, rx1, ry1;
+                        const float2 c0 = tab32[2 * k], c1 = tab32[2 * k + 1];
+                        redo |= turn_f32(__uint_as_float(wa[k] << 16), __uint_as_float(wb[k] << 16),
+                                         c0.x, c0.y, &rx0, &ry0);
+                        redo |= turn_f32(__uint_as_float(wa[k] & 0xFFFF0000u),
+                                         __uint_as_float(wb[k] & 0xFFFF0000u), c1.x, c1.y, &rx1, &ry1);
+                        na[k] = pack2_bf16(rx0, rx1);
+                        nb[k] = pack2_bf16(ry0, ry1);
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; k++) {  // plane k: word k of piece a; plane 4 + k of piece b
+                        float rx, ry;
+                        const float2 ca = tab32[k], cb = tab32[4 + k];
+                        redo |= turn_f32(__uint_as_float(wa[k] << 16), __uint_as_float(wa[k] & 0xFFFF0000u),
+                                         ca.x, ca.y, &rx, &ry);
+                        na[k] = pack2_bf16(rx, ry);
+                        redo |= turn_f32(__uint_as_float(wb[k] << 16), __uint_as_float(wb[k] & 0xFFFF0000u),
+                                         cb.x, cb.y, &rx, &ry);
+                        nb[k] = pack2_bf16(rx, ry);
+                    }
+                }
+                if (redo) {
+                    if constexpr (STYLE == PIC_ROPE_HALF) {
+#pragma unroll
+                        for (int k = 0; k < 4; k++) {
+                            const double2 c0 = tab[2 * k], c1 = tab[2 * k + 1];
+                            const double x0 = bf16_lo(wa[k]), y0 = bf16_lo(wb[k]);
+                            const double x1 = bf16_hi(wa[k]), y1 = bf16_hi(wb[k]);
+                            na[k] = pack_bf16(x0 * c0.x - y0 * c0.y, x1 * c1.x - y1 * c1.y);
+                            nb[k] = pack_bf16(x0 * c0.y + y0 * c0.x, x1 * c1.y + y1 * c1.x);
+                        }
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; k++) {
+                            const double2 ca = tab[k], cb = tab[4 + k];
+                            const double xa = bf16_lo(wa[k]), ya = bf16_hi(wa[k]);
+                            const double xb = bf16_lo(wb[k]), yb = bf16_hi(wb[k]);
+                            na[k] = pack_bf16(xa * ca.x - ya * ca.y, xa * ca.y + ya * ca.x);
+                            nb[k] = pack_bf16(xb * cb.x - yb * cb.y, xb * cb.y + yb * cb.x);
+                        }
+                    }
+                }
+                ka = make_uint4(na[0], na[1], na[2], na[3]);
+                kb = make_uint4(nb[0], nb[1], nb[2], nb[3]);
             }
         };
 

@@ -47,6 +47,40 @@ __device__ __forceinline__ uint32_t pack_bf16(double lo, double hi) {
     return f64_to_bf16(lo) | (f64_to_bf16(hi) << 16);
 }
 
+// ------------------------------------------------- fp32 fast path of a turn
+//
+// A turned element r = x c - y s (or x s + y c) computed in fp32 from bf16 x,
+// y and the fp32-rounded c, s lies within 3 * 2^-24 (|x c| + |y s|) of the
+// value the fp64 turn rounds (itself within 2^-52 of that sum of the exact
+// one).  Its round-to-nearest-even bf16 is therefore the fp64 path's unless a
+// bf16 rounding midpoint lies that close to r: near_midpoint() reports that
+// case with a 2^-21 margin, and also non-finite values and products so small
+// that fp32 may have lost them, so that the caller redoes the element in
+// fp64.  The midpoint nearest r keeps r's sign, exponent and top 7 fraction
+// bits and has 0x8000 below; r and it share a binade, so r - mid is exact.
+__device__ __forceinline__ bool near_midpoint(float r, float mag) {
+    const float mid = __uint_as_float((__float_as_uint(r) & 0xFFFF0000u) | 0x8000u);
+    return !(fabsf(r - mid) > mag * 0x1p-21f) || !(mag > 0x1p-100f);
+}
+
+// Two fp32 values rounded to bf16 (nearest even), packed low first.
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+// Turn of one plane in fp32: *rx = x c - y s, *ry = x s + y c; returns true
+// when either result needs the fp64 path.
+__device__ __forceinline__ bool turn_f32(float x, float y, float c, float s, float *rx, float *ry) {
+    const float p1 = x * c, q1 = y * s, p2 = x * s, q2 = y * c;
+    *rx = p1 - q1;
+    *ry = p2 + q2;
+    const bool bx = near_midpoint(*rx, fabsf(p1) + fabsf(q1));
+    const bool by = near_midpoint(*ry, fabsf(p2) + fabsf(q2));
+    return bx || by;
+}
+
 // ----------------------------------------------------------------- rotation
 
 template <typename E>
