@@ -126,6 +126,34 @@ def test_attend_shapes(torch_cuda, dt, style, dims, group):
     assert err <= TOL * vmax, (err, vmax)
 
 
+@pytest.mark.parametrize("style,dims", [("half", (2, 128, 0, 128)), ("interleaved", (2, 128, 32, 64))])
+def test_attend_many_short_chunks(torch_cuda, style, dims):
+    """Many short chunks at distinct shifts in one request (bf16, 128-dim
+    rows: the matrix-core path): 16-position tiles that mix chunks, blocks cut
+    at their shift-table limit, a context shorter than one step in another
+    request, and a one-position context."""
+    rng = np.random.default_rng(77)
+    heads, row, roff, rdim = dims
+    lens = [int(n) for n in rng.integers(3, 24, size=14)]
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    chunks = [Chunk(int(st), n, int(rng.integers(0, 500))) for st, n in zip(starts, lens)]
+    entries, pos = [], 5
+    for c in range(len(chunks)):
+        entries.append(Entry(c, pos, lens[c], int(rng.integers(0, 2))))
+        pos += lens[c] + int(rng.integers(0, 3))
+    reqs = [Request(entries, None, pos + 3),
+            Request([Entry(0, 2, lens[0], 0)], None, lens[0] + 2 + 5),  # shorter than one step
+            Request([], None, 1)]  # one position, no chunk
+    cap = pos + 8
+    wl = Workload("short-chunks", "bf16", 2, heads, row, roff, rdim, style, 500000.0, True,
+                  pool_tokens=int(sum(lens)), chunks=chunks, requests=reqs, capacity=cap)
+    for group in (1, 4, 8):
+        say(f"attend many short chunks style={style} group={group}")
+        err, vmax = run_case(torch_cuda, wl, group, 3, layer=1, sink_tokens=2, sink_bias=-5.0)
+        say(f"  max err {err:.3g} (tol {TOL * vmax:.3g})")
+        assert err <= TOL * vmax, (err, vmax)
+
+
 def test_attend_one_token_pool_pages(torch_cuda):
     """A pool of 1-token pages: every pool position is its own tile, so blocks
     stop at the per-block tile limit rather than at their length."""
