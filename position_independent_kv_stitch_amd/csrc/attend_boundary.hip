@@ -60,6 +60,7 @@ constexpr int kDTiles = kDim / 16;        // output tiles of 16 dims
 constexpr int kPT = PIC_BND_POS_TILES;   // 16-position tiles per step (2 or 4)
 constexpr int kStepPos = 16 * kPT;        // positions per step
 constexpr int kSlabs = 2 * kKSteps * kPT; // 1 KB slabs per step: K, then V
+static_assert(kPT == 2 || kPT == 4, "position tiles per step");
 constexpr int kNBuf = 4;                  // staging buffers (computed, turned, two loading)
 #ifndef PIC_BND_WAVES
 #define PIC_BND_WAVES 8
@@ -201,6 +202,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     __shared__ StageTile s_tiles[kItemTiles];
     __shared__ uint32_t s_pslot[kNBuf][kStepPos];                       // shift-table slot + 1 (0: not turned)
     __shared__ __attribute__((aligned(16))) float s_pbias[kNBuf][kStepPos];  // damping, -inf past the block
+    __shared__ __attribute__((aligned(4))) uint8_t s_pflag[kNBuf][4];  // position tile has a nonzero bias
 
     // grid: runs of 8 (item, KV head) pairs c, each run once per row set;
     // workgroup w goes to XCD w % 8, so every set of one pair shares an XCD
@@ -240,11 +242,18 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     // per tile, the latest last position of its rows: a step past it is
     // skipped (rows past the request: -1)
     int tile_last[TT];
+    // and the earliest last position of its live rows: a step that ends by
+    // then needs no causal mask for the tile
+    int tile_first[TT];
 #pragma unroll
     for (int k = 0; k < TT; k++) {
-        int x = limit[k];
-        for (int m = 1; m < 16; m <<= 1) x = max(x, __shfl_xor(x, m, 64));
+        int x = limit[k], y = limit[k] < 0 ? INT32_MAX : limit[k];
+        for (int m = 1; m < 16; m <<= 1) {
+            x = max(x, __shfl_xor(x, m, 64));
+            y = min(y, __shfl_xor(y, m, 64));
+        }
         tile_last[k] = x;
+        tile_first[k] = y;
     }
     const float scale2 = a.scale * kLog2e;  // logits in log2 units (exp2 weights)
     const float bias2 = a.sink_bias * kLog2e;
@@ -317,10 +326,14 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             const StageTile T = s_tiles[cur];
             const bool pool = T.info & kInfoPool;
             const int64_t off = T.off0 + static_cast<int64_t>(pi) * (pool ? a.s_tok : a.c_tok);
-            if (my_j0 == 0 && g == 0) {
+            if (my_j0 == 0) {
                 const bool damp = static_cast<uint32_t>(pi - T.tok0) < (T.info >> 8);
-                s_pslot[bf][16 * my_tau + r16] = valid ? (T.info & 7u) : 0u;
-                s_pbias[bf][16 * my_tau + r16] = valid ? (damp ? bias2 : 0.f) : -INFINITY;
+                const uint64_t biased = __ballot(g == 0 && (!valid || damp));
+                if (g == 0) {
+                    s_pslot[bf][16 * my_tau + r16] = valid ? (T.info & 7u) : 0u;
+                    s_pbias[bf][16 * my_tau + r16] = valid ? (damp ? bias2 : 0.f) : -INFINITY;
+                }
+                if (lane == 0) s_pflag[bf][my_tau] = biased != 0;
             }
             const uint16_t *kr = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
             const uint16_t *vr = (pool ? a.pool_v : a.cache_v) + off + 8 * g;
@@ -363,18 +376,22 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                 uint4 &kb = s_stage[bb][((pb >> 2) * kPT + tau) * 64 + 16 * (pb & 3) + pp];
                 const uint4 va = ka, vb = kb;
                 const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
-                // fp32 first; the fp64 turn only where it could round otherwise
+                // fp32 first; the fp64 turn only for the planes where it could
+                // round otherwise (redo[p]: the lanes whose plane p needs it),
+                // each plane under its own branch so that a wave pays for the
+                // planes some lane flagged, not for the whole unit
                 uint32_t na[4], nb[4];
-                bool redo = false;
+                uint64_t redo[8];
                 if constexpr (STYLE == PIC_ROPE_HALF) {
 #pragma unroll
                     for (int k = 0; k < 4; k++) {  // planes 2 k, 2 k + 1: word k of each piece
                         float rx0, ry0, rx1, ry1;
                         const float2 c0 = tab32[2 * k], c1 = tab32[2 * k + 1];
-                        redo |= turn_f32(__uint_as_float(wa[k] << 16), __uint_as_float(wb[k] << 16),
-                                         c0.x, c0.y, &rx0, &ry0);
-                        redo |= turn_f32(__uint_as_float(wa[k] & 0xFFFF0000u),
-                                         __uint_as_float(wb[k] & 0xFFFF0000u), c1.x, c1.y, &rx1, &ry1);
+                        redo[2 * k] = __ballot(turn_f32(__uint_as_float(wa[k] << 16),
+                                                        __uint_as_float(wb[k] << 16), c0.x, c0.y, &rx0, &ry0));
+                        redo[2 * k + 1] = __ballot(turn_f32(__uint_as_float(wa[k] & 0xFFFF0000u),
+                                                            __uint_as_float(wb[k] & 0xFFFF0000u), c1.x, c1.y,
+                                                            &rx1, &ry1));
                         na[k] = pack2_bf16(rx0, rx1);
                         nb[k] = pack2_bf16(ry0, ry1);
                     }
@@ -383,32 +400,37 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                     for (int k = 0; k < 4; k++) {  // plane k: word k of piece a; plane 4 + k of piece b
                         float rx, ry;
                         const float2 ca = tab32[k], cb = tab32[4 + k];
-                        redo |= turn_f32(__uint_as_float(wa[k] << 16), __uint_as_float(wa[k] & 0xFFFF0000u),
-                                         ca.x, ca.y, &rx, &ry);
+                        redo[k] = __ballot(turn_f32(__uint_as_float(wa[k] << 16),
+                                                    __uint_as_float(wa[k] & 0xFFFF0000u), ca.x, ca.y, &rx, &ry));
                         na[k] = pack2_bf16(rx, ry);
-                        redo |= turn_f32(__uint_as_float(wb[k] << 16), __uint_as_float(wb[k] & 0xFFFF0000u),
-                                         cb.x, cb.y, &rx, &ry);
+                        redo[4 + k] = __ballot(turn_f32(__uint_as_float(wb[k] << 16),
+                                                        __uint_as_float(wb[k] & 0xFFFF0000u), cb.x, cb.y, &rx, &ry));
                         nb[k] = pack2_bf16(rx, ry);
                     }
                 }
-                if (redo) {
-                    if constexpr (STYLE == PIC_ROPE_HALF) {
+                uint64_t any_redo = 0;
 #pragma unroll
-                        for (int k = 0; k < 4; k++) {
-                            const double2 c0 = tab[2 * k], c1 = tab[2 * k + 1];
-                            const double x0 = bf16_lo(wa[k]), y0 = bf16_lo(wb[k]);
-                            const double x1 = bf16_hi(wa[k]), y1 = bf16_hi(wb[k]);
-                            na[k] = pack_bf16(x0 * c0.x - y0 * c0.y, x1 * c1.x - y1 * c1.y);
-                            nb[k] = pack_bf16(x0 * c0.y + y0 * c0.x, x1 * c1.y + y1 * c1.x);
-                        }
-                    } else {
+                for (int pl = 0; pl < 8; pl++) any_redo |= redo[pl];
+                if (any_redo != 0) {  // uniform
 #pragma unroll
-                        for (int k = 0; k < 4; k++) {
-                            const double2 ca = tab[k], cb = tab[4 + k];
-                            const double xa = bf16_lo(wa[k]), ya = bf16_hi(wa[k]);
-                            const double xb = bf16_lo(wb[k]), yb = bf16_hi(wb[k]);
-                            na[k] = pack_bf16(xa * ca.x - ya * ca.y, xa * ca.y + ya * ca.x);
-                            nb[k] = pack_bf16(xb * cb.x - yb * cb.y, xb * cb.y + yb * cb.x);
+                    for (int pl = 0; pl < 8; pl++) {
+                        if (!((redo[pl] >> lane) & 1)) continue;
+                        const double2 cs = tab[pl];
+                        if constexpr (STYLE == PIC_ROPE_HALF) {
+                            // plane pl: half pl % 2 of word pl / 2 in both pieces
+                            const int k = pl >> 1, sh = 16 * (pl & 1);
+                            const double x = (pl & 1) ? bf16_hi(wa[k]) : bf16_lo(wa[k]);
+                            const double y = (pl & 1) ? bf16_hi(wb[k]) : bf16_lo(wb[k]);
+                            const uint32_t keep = 0xFFFF0000u >> sh;
+                            na[k] = (na[k] & keep) | (f64_to_bf16(x * cs.x - y * cs.y) << sh);
+                            nb[k] = (nb[k] & keep) | (f64_to_bf16(x * cs.y + y * cs.x) << sh);
+                        } else {
+                            // plane pl: word pl % 4 of piece a (pl < 4) or b
+                            const uint32_t w = pl < 4 ? wa[pl & 3] : wb[pl & 3];
+                            const double x = bf16_lo(w), y = bf16_hi(w);
+                            const uint32_t r = pack_bf16(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
+                            if (pl < 4) na[pl & 3] = r;
+                            else nb[pl & 3] = r;
                         }
                     }
                 }
@@ -444,6 +466,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             const int cur_bf = i & (kNBuf - 1);
             if (i + 3 < nsteps) stage(p0 + 3 * kStepPos, (i + 3) & (kNBuf - 1));
             if (i + 1 < nsteps) turn((i + 1) & (kNBuf - 1));
+
 
             const int step_pos = bpos + p0;  // context position of the step's first row
             bool any = false;
@@ -485,31 +508,48 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
                     for (int tau = 0; tau < kPT; tau++) kf[tau] = kn[tau];
                 }
             }
-            // position terms shared by every tile (D registers: positions
-            // 16 tau + 4 g + i)
-            f32x4 pb[kPT];
-#pragma unroll
-            for (int tau = 0; tau < kPT; tau++)
-                pb[tau] = *reinterpret_cast<const f32x4 *>(&s_pbias[cur_bf][16 * tau + 4 * g]);
             // ---- online softmax per row (log2 units).  The running max is
             // kept until a logit passes it by kLazy (weights stay below
             // 2^kLazy; the merge uses the same reference), so the accumulator
-            // is seldom rescaled
+            // is seldom rescaled.
+            // A step with no damped or missing position that ends before
+            // every live row of the wave's tiles does (the usual case) needs
+            // neither bias nor mask: its logits stay unscaled in st, the row
+            // max is scaled after the reduction (exact: rounding is
+            // monotonic and scale2 > 0), and the weights take the scale in
+            // the exponent's fma.  Otherwise st becomes the scaled, biased,
+            // masked logits and the weights multiply by 1.
+            bool fast = (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint32_t *>(s_pflag[cur_bf])) &
+                         (0xFFFFFFFFu >> (32 - 8 * kPT))) == 0u;
+#pragma unroll
+            for (int k = 0; k < TT; k++) fast = fast && tile_first[k] >= step_pos + kStepPos - 1;
+            const float wmul = fast ? scale2 : 1.f;
             float alpha[TT], m_use[TT];
             bool bump_any = false;
 #pragma unroll
             for (int k = 0; k < TT; k++) {
-                const int lim = limit[k] - step_pos - 4 * g;  // position 16 tau + i must be <= lim
                 float mx = -INFINITY;
+                if (fast) {
 #pragma unroll
-                for (int tau = 0; tau < kPT; tau++)
+                    for (int tau = 0; tau < kPT; tau++)
 #pragma unroll
-                    for (int i = 0; i < 4; i++) {
-                        const float x = fmaf(st[k][tau][i], scale2, pb[tau][i]);
-                        st[k][tau][i] = 16 * tau + i <= lim ? x : -INFINITY;
-                        mx = fmaxf(mx, st[k][tau][i]);
+                        for (int i = 0; i < 4; i++) mx = fmaxf(mx, st[k][tau][i]);
+                    mx = row_max(mx) * scale2;
+                } else {
+                    // position terms (D registers: positions 16 tau + 4 g + i)
+                    const int lim = limit[k] - step_pos - 4 * g;  // position 16 tau + i must be <= lim
+#pragma unroll
+                    for (int tau = 0; tau < kPT; tau++) {
+                        const f32x4 pb = *reinterpret_cast<const f32x4 *>(&s_pbias[cur_bf][16 * tau + 4 * g]);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const float x = fmaf(st[k][tau][i], scale2, pb[i]);
+                            st[k][tau][i] = 16 * tau + i <= lim ? x : -INFINITY;
+                            mx = fmaxf(mx, st[k][tau][i]);
+                        }
                     }
-                mx = row_max(mx);
+                    mx = row_max(mx);
+                }
                 // (-inf + kLazy stays -inf: a row's first finite logit bumps)
                 const bool bump = mx > m_run[k] + kLazy;
                 const float m_new = bump ? mx : m_run[k];
@@ -534,9 +574,10 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
 #pragma unroll
                 for (int k = 0; k < TT; k++) {
                     float pw[8];
+                    const float neg_m = -m_use[k];
 #pragma unroll
                     for (int q = 0; q < 8; q++)
-                        pw[q] = __builtin_amdgcn_exp2f(st[k][2 * kk + (q >> 2)][q & 3] - m_use[k]);
+                        pw[q] = __builtin_amdgcn_exp2f(fmaf(st[k][2 * kk + (q >> 2)][q & 3], wmul, neg_m));
                     const float psum =
                         ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
                     l_run[k] = (kk == 0 ? l_run[k] * alpha[k] : l_run[k]) + psum;

@@ -52,15 +52,20 @@ __device__ __forceinline__ uint32_t pack_bf16(double lo, double hi) {
 // A turned element r = x c - y s (or x s + y c) computed in fp32 from bf16 x,
 // y and the fp32-rounded c, s lies within 3 * 2^-24 (|x c| + |y s|) of the
 // value the fp64 turn rounds (itself within 2^-52 of that sum of the exact
-// one).  Its round-to-nearest-even bf16 is therefore the fp64 path's unless a
-// bf16 rounding midpoint lies that close to r: near_midpoint() reports that
-// case with a 2^-21 margin, and also non-finite values and products so small
-// that fp32 may have lost them, so that the caller redoes the element in
-// fp64.  The midpoint nearest r keeps r's sign, exponent and top 7 fraction
-// bits and has 0x8000 below; r and it share a binade, so r - mid is exact.
-__device__ __forceinline__ bool near_midpoint(float r, float mag) {
+// one), plus at most 2^-123 lost to underflow or flushed subnormals; and
+// |x c| + |y s| <= |x| + |y| for either element.  Its round-to-nearest-even
+// bf16 is therefore the fp64 path's unless a rounding boundary lies that
+// close to r.  near_midpoint() takes T = 2^-21 (|x| + |y|) + 2^-120 (the
+// caller's t) and reports |r - mid| <= T, mid being the midpoint above r's
+// bf16 truncation (r's sign, exponent and top 7 fraction bits, then 0x8000;
+// r and mid share a binade, so r - mid is exact).  When it does not, the
+// error is below T / 2 and below |r - mid| / 2, and the boundary under the
+// truncation is at least |r - mid| / 2 away (a quarter of a bf16 step, where
+// the truncation is a power of two), so both round alike.  Non-finite r or T
+// also report, and the caller redoes the plane in fp64.
+__device__ __forceinline__ bool near_midpoint(float r, float t) {
     const float mid = __uint_as_float((__float_as_uint(r) & 0xFFFF0000u) | 0x8000u);
-    return !(fabsf(r - mid) > mag * 0x1p-21f) || !(mag > 0x1p-100f);
+    return !(fabsf(r - mid) > t);
 }
 
 // Two fp32 values rounded to bf16 (nearest even), packed low first.
@@ -73,12 +78,10 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
 // Turn of one plane in fp32: *rx = x c - y s, *ry = x s + y c; returns true
 // when either result needs the fp64 path.
 __device__ __forceinline__ bool turn_f32(float x, float y, float c, float s, float *rx, float *ry) {
-    const float p1 = x * c, q1 = y * s, p2 = x * s, q2 = y * c;
-    *rx = p1 - q1;
-    *ry = p2 + q2;
-    const bool bx = near_midpoint(*rx, fabsf(p1) + fabsf(q1));
-    const bool by = near_midpoint(*ry, fabsf(p2) + fabsf(q2));
-    return bx || by;
+    *rx = fmaf(x, c, -(y * s));
+    *ry = fmaf(x, s, y * c);
+    const float t = fmaf(fabsf(x) + fabsf(y), 0x1p-21f, 0x1p-120f);
+    return near_midpoint(*rx, t) || near_midpoint(*ry, t);
 }
 
 // ----------------------------------------------------------------- rotation
