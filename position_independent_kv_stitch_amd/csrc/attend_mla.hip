@@ -21,10 +21,12 @@
 // items are cut for the launch: each request gets a share of the CU slots in
 // proportion to its context, so every workgroup has about the same number
 // of positions and the launch is one round.  An item's positions come in
-// steps of 32:
-//   - staging: the step's 32 rows (36 KB) go from HBM straight into LDS
+// steps of 32 (16 for a one-wave workgroup, which then double-buffers in
+// the LDS that one 32-position step took and still shares a CU with three
+// others):
+//   - staging: the step's rows (36 KB for 32) go from HBM straight into LDS
 //     (global_load_lds_dwordx4, no registers), spread over the W waves, into
-//     the second of two buffers while the first is computed on;
+//     a later buffer while an earlier one is computed on;
 //   - the rotary slots of moved chunk rows are turned in LDS (fp64, rounded
 //     to bf16 by the stitch's own code, rotate.hpp);
 //   - S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16
@@ -65,8 +67,6 @@ constexpr int kKSteps = kRow / 32;        // MFMA k-steps of 32 dims
 constexpr int kRopeStep = kRopeOff / 32;  // first rotary k-step (x half; y in the next)
 constexpr int kDTiles = kVDim / 16;       // output tiles of 16 dims
 constexpr int kGroupHeads = 16;           // query heads per wave
-constexpr int kStepPos = 32;              // positions per step: two 16-position tiles
-constexpr int kSlabs = 2 * kKSteps;       // 1 KB slabs of a staged step
 constexpr int kItemTiles = kItemBlockTiles;  // map tiles per block at most
 constexpr int kCombineThreads = 256;
 
@@ -165,13 +165,19 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 // barriers keep the compiler from hoisting every LDS read of a phase ahead.
 // NB staging buffers: 2 overlap a step's loads with the previous step's
 // work inside the workgroup; 1 halves the LDS so that twice as many
-// workgroups share a CU and overlap each other instead.
-template <int STYLE, int W, int NB>
+// workgroups share a CU and overlap each other instead.  TPS 16-position
+// tiles per step: 2 (the value product on 16x16x32 tiles), or 1 (on
+// 16x16x16 tiles), which halves a step's LDS so that a one-wave workgroup
+// can hold two steps and still share a CU with three others.
+template <int STYLE, int W, int NB, int TPS>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
 mla_block_kernel(const MlaArgs a, int32_t layer) {
-    // staged step: slab j = (k-step j >> 1, position tile j & 1); slot 16 g + p
-    // of a slab holds dims 32 s + 8 g .. + 8 of position 16 tau + p, i.e. the
-    // A fragment of lane 16 g + p
+    static_assert(TPS == 1 || TPS == 2, "position tiles per step");
+    constexpr int kStepPos = 16 * TPS;      // positions per step
+    constexpr int kSlabs = TPS * kKSteps;   // 1 KB slabs of a staged step
+    // staged step: slab j = (k-step j / TPS, position tile j % TPS); slot
+    // 16 g + p of a slab holds dims 32 s + 8 g .. + 8 of position 16 tau + p,
+    // i.e. the A fragment of lane 16 g + p
     __shared__ __attribute__((aligned(16))) uint4 s_stage[NB][kSlabs * 64];
     __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kHalfR];  // block's shift tables
     __shared__ StageTile s_tiles[kItemTiles];
@@ -228,14 +234,14 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
         }
         __syncthreads();
 
-        // stage step p0 into buffer bf: wave w loads slabs w, w + W, ... of
-        // both position tiles; lanes past the block's end repeat position p0
+        // stage step p0 into buffer bf: wave w loads slabs TPS w + tau,
+        // + TPS W, ... of position tile tau; lanes past the block's end repeat position p0
         // (their weights are 0).  The tile holding a lane's position is found
         // by a forward search (positions only grow within a block).
         int cur[2] = {0, 0};
         auto stage = [&](int p0, int bf) {
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++) {
+            for (int tau = 0; tau < TPS; tau++) {
                 int pi = p0 + 16 * tau + r16;
                 const bool valid = pi < B.ntok;
                 if (!valid) pi = p0;
@@ -249,8 +255,8 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
                     s_pbias[bf][16 * tau + r16] = valid ? (damp ? bias2 : 0.f) : -INFINITY;
                 }
                 const uint16_t *row = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
-                for (int j = 2 * wave + tau; j < kSlabs; j += 2 * W) {
-                    const int s = j >> 1;
+                for (int j = TPS * wave + tau; j < kSlabs; j += TPS * W) {
+                    const int s = j / TPS;
                     load_lds16(row + 32 * s, &s_stage[bf][j * 64]);
                 }
             }
@@ -267,9 +273,9 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
                 const double2 *tab = s_cs[slot1 - 1];
                 const int tau = pos >> 4, pp = pos & 15;
                 uint32_t *kx = reinterpret_cast<uint32_t *>(
-                    &s_stage[bb][(2 * kRopeStep + tau) * 64 + 16 * gg + pp]);
+                    &s_stage[bb][(TPS * kRopeStep + tau) * 64 + 16 * gg + pp]);
                 uint32_t *ky = reinterpret_cast<uint32_t *>(
-                    &s_stage[bb][(2 * kRopeStep + 2 + tau) * 64 + 16 * gg + pp]);
+                    &s_stage[bb][(TPS * (kRopeStep + 1) + tau) * 64 + 16 * gg + pp]);
                 if constexpr (STYLE == PIC_ROPE_HALF) {
                     // x of planes 8 gg + 2 qh, + 1 in word qh of the first rotary
                     // k-step's piece, their y (32 planes later) in the second's
@@ -310,7 +316,7 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
         // stage call issues at least kMinLoads loads per wave (wave 0 may
         // issue more), which complete in order: waiting until at most n
         // kMinLoads are outstanding leaves the newest n stage calls in flight.
-        constexpr int kMinLoads = 2 * ((kSlabs - 2 * W) / (2 * W) + 1);
+        constexpr int kMinLoads = TPS * ((kSlabs - TPS * W) / (TPS * W) + 1);
         const int nsteps = (B.ntok + kStepPos - 1) / kStepPos;
         stage(0, 0);
         if constexpr (NB == 4) {
@@ -347,13 +353,15 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
 
             // ---- logits S^T for the wave's heads
             const uint4 *stg = s_stage[cb];
-            f32x4 st[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            f32x4 st[TPS];
+#pragma unroll
+            for (int tau = 0; tau < TPS; tau++) st[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < kKSteps; s++) {
 #pragma unroll
-                for (int tau = 0; tau < 2; tau++)
+                for (int tau = 0; tau < TPS; tau++)
                     st[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(stg[(2 * s + tau) * 64 + lane]), qf[s], st[tau], 0, 0, 0);
+                        as_bf16x8(stg[(TPS * s + tau) * 64 + lane]), qf[s], st[tau], 0, 0, 0);
                 if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
             }
 
@@ -361,23 +369,25 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
             // positions p0 + 16 tau + 4 g + i.  The running max is kept until a
             // logit passes it by kLazy (weights stay below 2^kLazy; the merge
             // uses the same reference), so the accumulator is seldom rescaled
-            float sc[8];
+            constexpr int NV = 4 * TPS;  // logits per lane
+            float sc[NV];
 #pragma unroll
-            for (int tau = 0; tau < 2; tau++) {
+            for (int tau = 0; tau < TPS; tau++) {
                 const f32x4 pb = *reinterpret_cast<const f32x4 *>(&s_pbias[cb][16 * tau + 4 * g]);
 #pragma unroll
                 for (int i = 0; i < 4; i++) sc[4 * tau + i] = fmaf(st[tau][i], scale2, pb[i]);
             }
-            float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            if constexpr (TPS == 2) mx = fmaxf(mx, fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
             mx = row_max(mx);  // finite: position p0 is in the block
             const bool bump = mx > m_run + kLazy;  // (-inf + kLazy stays -inf)
             const float m_new = bump ? mx : m_run;
             const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-            float pw[8];
+            float pw[NV];
 #pragma unroll
-            for (int k = 0; k < 8; k++) pw[k] = __builtin_amdgcn_exp2f(sc[k] - m_new);
-            const float psum = ((pw[0] + pw[1]) + (pw[2] + pw[3])) + ((pw[4] + pw[5]) + (pw[6] + pw[7]));
+            for (int k = 0; k < NV; k++) pw[k] = __builtin_amdgcn_exp2f(sc[k] - m_new);
+            float psum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
+            if constexpr (TPS == 2) psum += (pw[4] + pw[5]) + (pw[6] + pw[7]);
             l_run = l_run * alpha + psum;
             m_run = m_new;
             if (__any(bump)) {
@@ -385,24 +395,23 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
                 for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
             }
             // weights as B of O^T += V^T P^T: k index 8 g + j is position
-            // 4 g + j (j < 4) or 16 + 4 g + j - 4, the order of pw; hi + lo bf16
-            uint32_t hi[4], lo[4];
+            // 4 g + j (j < 4) or 16 + 4 g + j - 4 with two tiles, k index 4 g + j
+            // position 4 g + j with one -- the order of pw; hi + lo bf16
+            uint32_t hi[NV / 2], lo[NV / 2];
 #pragma unroll
-            for (int k = 0; k < 4; k++) {
+            for (int k = 0; k < NV / 2; k++) {
                 const f32x2 pr = {pw[2 * k], pw[2 * k + 1]};
                 hi[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
                 const f32x2 rr = {pw[2 * k] - __uint_as_float(hi[k] << 16),
                                   pw[2 * k + 1] - __uint_as_float(hi[k] & 0xFFFF0000u)};
                 lo[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
             }
-            const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-            const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
 
             // ---- A = V^T (dim d = 16 t + r16; positions 4 g .. 4 g + 3, then
             // 16 + 4 g .. + 3) by transposing LDS reads: within each 16-lane
             // group, lane i receives element i % 4 of the 8-byte rows that
             // lanes 4 j + i / 4 address (j = 0..3).  So lane i of group g
-            // addresses position 4 g + i / 4 (+ 16 for the second read), dims
+            // addresses position 4 g + i / 4 (+ 16 for the second tile), dims
             // 16 t + 4 (i % 4) .. + 4: slab (t / 2, tile), slot 16 g' + position
             // % 16 with g' = 2 (t % 2) + (i % 4) / 2, second half when i is odd
             const char *stg8 = reinterpret_cast<const char *>(stg);
@@ -410,16 +419,24 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
 #pragma unroll
             for (int t = 0; t < kDTiles; t++) {
                 const int gq = 2 * (t & 1) + (dq >> 1);
-                const int base = ((2 * (t >> 1)) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
+                const int base = ((TPS * (t >> 1)) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
                 const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                     (lds_s16x4 *)(stg8 + base));
-                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(stg8 + base + 64 * 16));  // tile 1: the next slab
-                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
-                const uint32_t w[4] = {w0.x, w0.y, w1.x, w1.y};
-                const bf16x8 va = as_bf16x8(make_uint4(w[0], w[1], w[2], w[3]));
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+                if constexpr (TPS == 2) {
+                    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4 *)(stg8 + base + 64 * 16));  // tile 1: the next slab
+                    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                    const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+                    const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
+                    const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+                } else {
+                    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0], hi[1]));
+                    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0], lo[1]));
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, acc[t], 0, 0, 0);
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, acc[t], 0, 0, 0);
+                }
                 if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
             if (NB == 1 && i + 1 < nsteps) {
@@ -499,18 +516,27 @@ int cu_count() {
 }
 
 #ifndef PIC_MLA_NB1
-#define PIC_MLA_NB1 1
+#define PIC_MLA_NB1 2
 #endif
-// staging buffers of the one-wave workgroup
+#ifndef PIC_MLA_TPS1
+#define PIC_MLA_TPS1 1
+#endif
+// staging buffers and position tiles per step of the one-wave workgroup
 constexpr int kNb1 = PIC_MLA_NB1;
+constexpr int kTps1 = PIC_MLA_TPS1;
+// one-wave workgroups per CU: LDS holds kNb1 steps of 16 kTps1 rows (18 KB a
+// tile) plus about 3 KB of tables; registers allow eight waves
+constexpr int kPerCu1 = std::min(8, 160 / (18 * kNb1 * kTps1 + 3));
 
 template <int STYLE>
 hipError_t launch_block(int w, dim3 grid, hipStream_t stream, const MlaArgs &a, int32_t layer) {
     switch (w) {
-        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 4>), grid, dim3(512), 0, stream, a, layer); break;
-        case 4: hipLaunchKernelGGL((mla_block_kernel<STYLE, 4, 2>), grid, dim3(256), 0, stream, a, layer); break;
-        case 2: hipLaunchKernelGGL((mla_block_kernel<STYLE, 2, 2>), grid, dim3(128), 0, stream, a, layer); break;
-        default: hipLaunchKernelGGL((mla_block_kernel<STYLE, 1, kNb1>), grid, dim3(64), 0, stream, a, layer); break;
+        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 4, 2>), grid, dim3(512), 0, stream, a, layer); break;
+        case 4: hipLaunchKernelGGL((mla_block_kernel<STYLE, 4, 2, 2>), grid, dim3(256), 0, stream, a, layer); break;
+        case 2: hipLaunchKernelGGL((mla_block_kernel<STYLE, 2, 2, 2>), grid, dim3(128), 0, stream, a, layer); break;
+        default:
+            hipLaunchKernelGGL((mla_block_kernel<STYLE, 1, kNb1, kTps1>), grid, dim3(64), 0, stream, a, layer);
+            break;
     }
     return hipGetLastError();
 }
@@ -564,10 +590,10 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     const int G = args->num_q_heads / kGroupHeads;
     const int W = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
     const int sets = G / W;
-    // concurrent workgroups per CU: two with two 37 KB staging buffers each,
-    // four one-wave workgroups with one buffer; eight waves of up to 256
-    // registers fill a CU's register file
-    const int per_cu = W == 8 ? 1 : (W == 1 && kNb1 == 1) ? 4 : 2;
+    // concurrent workgroups per CU: one of eight waves, two with two 37 KB
+    // staging buffers each, kPerCu1 one-wave workgroups; eight waves of up to
+    // 256 registers fill a CU's register file
+    const int per_cu = W == 8 ? 1 : W == 1 ? kPerCu1 : 2;
     const int64_t slots = static_cast<int64_t>(cu_count()) * per_cu;
     const int64_t target = std::max<int64_t>(1, slots / sets);
     {
