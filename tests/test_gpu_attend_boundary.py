@@ -96,6 +96,21 @@ def test_random_small(torch_cuda, seed):
     assert err <= tol
 
 
+@pytest.mark.parametrize("style,dims", [("half", (2, 128, 32, 64)), ("interleaved", (2, 128, 16, 64)),
+                                        ("half", (1, 128, 96, 32)), ("interleaved", (2, 128, 112, 16))])
+def test_partial_rotary_slices(torch_cuda, style, dims):
+    """Rotary slices narrower than the row and away from dim 0: only some
+    waves hold turn units, and the turned pieces sit at other offsets."""
+    seed = dims[2] + dims[3]
+    wl = random_small(1200 + seed, dtype="bf16", style=style, n_requests=2, n_layers=1,
+                      max_len=90, dims=dims)
+    say(f"boundary partial rotary style={style} dims={dims}")
+    err, tol, n = run_case(torch_cuda, wl, 4, 16, seed, sink_tokens=4, sink_bias=-15.0)
+    say(f"  rows {n}: max err {err:.3g} (bound {tol:.3g})")
+    assert n > 0
+    assert err <= tol
+
+
 def test_long_k_and_short_entries(torch_cuda):
     """boundary_k larger than some entries (rows = their length), k x group
     = 128 (eight row tiles)."""
