@@ -26,8 +26,10 @@
 //     wave's ring of LDS stages (global_load_lds_dwordx4), in the MFMA
 //     A-fragment layout, several steps ahead of their use;
 //   - S^T = K Q'^T (v_mfma_f32_16x16x32_bf16) with Q' the query of the
-//     positions' chunk: one product per term, a position tile that mixes
-//     chunks is computed once per chunk and selected per position;
+//     positions' chunk: one product per term (for groups of 1, 2 or 4 query
+//     heads the terms share one product in the spare rows and DPP row shifts
+//     add them up), a position tile that mixes chunks is computed once per
+//     chunk and selected per position;
 //   - online softmax over the query heads (rows), in log2 units with a lazy
 //     running max;
 //   - O^T += V^T P^T with the weights straight from the S^T D registers
@@ -40,6 +42,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "lds_load.hpp"
 #include "pic_internal.hpp"
@@ -119,6 +122,14 @@ __device__ __forceinline__ float row_max(float v) {
     v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// lane i of every 16-lane row takes lane i + K's value (DPP row_shl; lanes
+// whose source lies past the row take 0)
+template <int K>
+__device__ __forceinline__ float row_shl(float v) {
+    static_assert(K >= 1 && K < 16, "DPP row shift");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xF, 0xF, true));
 }
 
 // the same with bitwise or
@@ -232,6 +243,24 @@ __device__ __forceinline__ void turn_query(const bf16x8 (&qf)[kKSteps], bf16x8 (
     }
 }
 
+// The packed form for groups of PG <= 5 query heads: row n of the products
+// holds term n / PG of head n % PG (rows from 3 PG on: zero), so one product
+// per k-step computes all three terms and row_shl folds them into rows
+// 0 .. PG - 1.  qr holds the lane's raw query (head n % PG).
+template <int STYLE>
+__device__ __forceinline__ void turn_query_packed(const bf16x8 (&qr)[kKSteps], bf16x8 (&qp)[kKSteps],
+                                                  const CosSin *cs, int ro, int hr, int g, int term) {
+    bf16x8 qt[3][kKSteps];
+    turn_query<STYLE>(qr, qt, cs, ro, hr, g);
+#pragma unroll
+    for (int s = 0; s < kKSteps; s++) {
+        const uint4 t0 = __builtin_bit_cast(uint4, qt[0][s]), t1 = __builtin_bit_cast(uint4, qt[1][s]),
+                    t2 = __builtin_bit_cast(uint4, qt[2][s]);
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        qp[s] = as_bf16x8(term == 0 ? t0 : term == 1 ? t1 : term == 2 ? t2 : z);
+    }
+}
+
 // Wait until the stage calls issued after the oldest one (`newer` of them,
 // kSlabs loads each) are the only ones outstanding.
 template <int N>
@@ -247,8 +276,10 @@ __device__ __forceinline__ void wait_newer(int newer) {
     }
 }
 
-template <int STYLE>
+// PG: the group size when it is packed (1, 2 or 4 query heads), else 0.
+template <int STYLE, int PG>
 __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t layer) {
+    static_assert(PG >= 0 && 3 * PG <= 16, "packed terms fit the 16 rows");
     // stage slab (kind, s, tau) = kind * 2 kKSteps + 2 s + tau (kind 0: K,
     // 1: V) holds dims 32 s .. + 31 of positions 16 tau .. + 15; its slot
     // 16 g + p holds dims 32 s + 8 g .. + 8 of position 16 tau + p
@@ -269,17 +300,28 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
     const int ro = a.rope_offset, hr = a.half_r;
 
     // query fragments (B of S^T = K Q^T): row r16 = query head h G + r16
-    // (rows past the group are zero), dims 32 s + 8 g .. + 8
+    // (rows past the group are zero), dims 32 s + 8 g .. + 8.  Packed, the
+    // lane also keeps the raw query of its term row's head r16 % PG.
     bf16x8 qf[kKSteps];
+    bf16x8 qr[PG ? kKSteps : 1];
     {
-        const bool live = r16 < G;
-        const uint16_t *qrow = a.q + request * a.q_req + (h * G + (live ? r16 : 0)) * a.q_head;
+        const int qh = PG ? r16 % PG : r16;
+        const bool live = PG ? r16 < 3 * PG : r16 < G;
+        const uint16_t *qrow = a.q + request * a.q_req + (h * G + (live ? qh : 0)) * a.q_head;
 #pragma unroll
-        for (int s = 0; s < kKSteps; s++)
-            qf[s] = as_bf16x8(live ? *reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g)
-                                   : make_uint4(0u, 0u, 0u, 0u));
+        for (int s = 0; s < kKSteps; s++) {
+            const uint4 v = live ? *reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+            if constexpr (PG) {
+                qr[s] = as_bf16x8(v);
+                qf[s] = as_bf16x8(r16 < PG ? v : make_uint4(0u, 0u, 0u, 0u));
+            } else {
+                qf[s] = as_bf16x8(v);
+            }
+        }
     }
-    bf16x8 qt[3][kKSteps];  // the query turned for table cur_tab
+    // the query turned for table cur_tab: three terms, or packed
+    bf16x8 qt[PG ? 1 : 3][kKSteps];
     int cur_tab = -1;
 
     f32x4 acc[kDTiles];
@@ -386,15 +428,29 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
                         for (int jj = 1; jj < kItemBlockTabs; jj++)
                             if (c - 1 == jj) tab = btab[jj];
                         if (tab != cur_tab) {
-                            turn_query<STYLE>(qf, qt, s_cs[c - 1], ro, hr, g);
+                            if constexpr (PG)
+                                turn_query_packed<STYLE>(qr, qt[0], s_cs[c - 1], ro, hr, g, r16 / PG);
+                            else
+                                turn_query<STYLE>(qf, qt, s_cs[c - 1], ro, hr, g);
                             cur_tab = tab;
                         }
+                        if constexpr (PG) {
 #pragma unroll
-                        for (int s = 0; s < kKSteps; s++) {
-                            const bf16x8 kf = as_bf16x8(stg[(s * kPT + tau) * 64 + lane]);
+                            for (int s = 0; s < kKSteps; s++)
+                                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    as_bf16x8(stg[(s * kPT + tau) * 64 + lane]), qt[0][s], sc, 0, 0, 0);
+                            // rows 0 .. PG - 1 gather their terms from rows + PG, + 2 PG
 #pragma unroll
-                            for (int term = 0; term < 3; term++)
-                                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qt[term][s], sc, 0, 0, 0);
+                            for (int e = 0; e < 4; e++)
+                                sc[e] = (sc[e] + row_shl<PG>(sc[e])) + row_shl<2 * PG>(sc[e]);
+                        } else {
+#pragma unroll
+                            for (int s = 0; s < kKSteps; s++) {
+                                const bf16x8 kf = as_bf16x8(stg[(s * kPT + tau) * 64 + lane]);
+#pragma unroll
+                                for (int term = 0; term < 3; term++)
+                                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qt[term][s], sc, 0, 0, 0);
+                            }
                         }
                     }
                     if (single) {
@@ -653,11 +709,20 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
     a.sink_tokens = args->sink_tokens;
     a.sink_bias = args->sink_bias;
     const dim3 grid(static_cast<unsigned>(a.n_items) * static_cast<unsigned>(H));
-    if (p.style == PIC_ROPE_HALF)
-        hipLaunchKernelGGL(gqa_tile_kernel<PIC_ROPE_HALF>, grid, dim3(64), 0, stream, a, args->layer);
-    else
-        hipLaunchKernelGGL(gqa_tile_kernel<PIC_ROPE_INTERLEAVED>, grid, dim3(64), 0, stream, a,
-                           args->layer);
+    auto launch = [&](auto style_tag, auto pg_tag) {
+        constexpr int S = decltype(style_tag)::value, PG = decltype(pg_tag)::value;
+        hipLaunchKernelGGL((gqa_tile_kernel<S, PG>), grid, dim3(64), 0, stream, a, args->layer);
+    };
+    auto with_style = [&](auto pg_tag) {
+        if (p.style == PIC_ROPE_HALF) launch(std::integral_constant<int, PIC_ROPE_HALF>{}, pg_tag);
+        else launch(std::integral_constant<int, PIC_ROPE_INTERLEAVED>{}, pg_tag);
+    };
+    switch (a.group) {  // packed terms for groups of 1, 2 or 4 query heads
+        case 1: with_style(std::integral_constant<int, 1>{}); break;
+        case 2: with_style(std::integral_constant<int, 2>{}); break;
+        case 4: with_style(std::integral_constant<int, 4>{}); break;
+        default: with_style(std::integral_constant<int, 0>{}); break;
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     hipLaunchKernelGGL(gqa_combine_kernel,
