@@ -200,6 +200,7 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
     __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kMaxHalf];  // block's shift tables
     __shared__ __attribute__((aligned(8))) float2 s_cs32[kBlockTabs][kMaxHalf];  // the same, fp32
     __shared__ StageTile s_tiles[kItemTiles];
+    __shared__ uint8_t s_tile_of[kBlockPos];  // map tile of every block position
     __shared__ uint32_t s_pslot[kNBuf][kStepPos];                       // shift-table slot + 1 (0: not turned)
     __shared__ __attribute__((aligned(16))) float s_pbias[kNBuf][kStepPos];  // damping, -inf past the block
     __shared__ __attribute__((aligned(4))) uint8_t s_pflag[kNBuf][4];  // position tile has a nonzero bias
@@ -314,16 +315,26 @@ bnd_block_kernel(const BndArgs a, int32_t layer) {
             }
         }
         __syncthreads();
+        // the map tile of every position the block stages (the last tile
+        // starting at or before it; tiles are in position order), so that a
+        // staging lane finds its tile with one LDS read
+        static_assert(kItemTiles <= 256, "tile index in a byte");
+        for (int pp = tid; pp < ntok; pp += 64 * kWaves) {
+            int lo = 0, hi = B.ntiles - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_tiles[mid].tok0 <= pp) lo = mid;
+                else hi = mid - 1;
+            }
+            s_tile_of[pp] = static_cast<uint8_t>(lo);
+        }
+        __syncthreads();
 
-        // tile holding the lane's position; positions only grow within a
-        // block, so the search moves forward
-        int cur = 0;
         auto stage = [&](int p0, int bf) {
             int pi = p0 + 16 * my_tau + r16;
             const bool valid = pi < ntok;
             if (!valid) pi = p0;
-            while (cur + 1 < B.ntiles && s_tiles[cur + 1].tok0 <= pi) cur++;
-            const StageTile T = s_tiles[cur];
+            const StageTile T = s_tiles[s_tile_of[pi]];
             const bool pool = T.info & kInfoPool;
             const int64_t off = T.off0 + static_cast<int64_t>(pi) * (pool ? a.s_tok : a.c_tok);
             if (my_j0 == 0) {
