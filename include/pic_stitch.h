@@ -272,6 +272,57 @@ pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *
                               int32_t layer_begin, int32_t layer_end, void *stream);
 
 /*
+ * One segment of a paged KV buffer for pic_rotate_paged.  Token t of the
+ * segment (t in [0, length)) sits at logical position first + t of the
+ * segment's block table: slot (first + t) % page_size of physical page
+ * pages[(first + t) / page_size]; n_pages = ceil((first + length) /
+ * page_size).  cow, when given, holds for every logical page the physical
+ * page a shared page is copied to, or -1 for a page the caller owns.
+ */
+typedef struct pic_page_segment {
+    const int32_t *pages;  /* host, n_pages physical page ids */
+    const int32_t *cow;    /* host, n_pages entries, or NULL: every page owned */
+    int64_t delta;
+    int32_t n_pages;
+    int32_t first;         /* 0 <= first < page_size */
+    int32_t length;        /* >= 1 */
+    int32_t recompute_k;   /* tokens [0, recompute_k) are not turned */
+} pic_page_segment;
+
+/*
+ * pic_rotate_paged -- the in-place turn on a paged buffer whose physical
+ * pages (blocks) may be shared by several requests, with copy-on-write
+ * (EPIC Guide, "Algorithmic Architecture: The EPIC Serving Runtime": chunk
+ * KV kept at virtual offset 0 in physical blocks of a pool and reused
+ * through block tables, and the runtime's in-place key rotation; turning a
+ * block in place that another request maps would change that request's
+ * keys).  For every segment and token t in [recompute_k, length) the
+ * rotary slice of K is turned by the segment's delta, layers [layer_begin,
+ * layer_end):
+ *   - a page the caller owns (cow NULL or cow[i] < 0) is turned in place:
+ *     only the rotary slice of those tokens' K rows is written;
+ *   - a shared page (cow[i] >= 0) is left unchanged and its complete
+ *     content -- every slot, K and (when the shape has V) V, all dims -- is
+ *     written to physical page cow[i], with the segment's tokens on it
+ *     turned there; the caller then maps logical page i to cow[i].
+ * buf is a paged view (k, v, layer_stride, token_stride = slot stride,
+ * head_stride, page_stride) of n_phys_pages pages of page_size slots; v may
+ * be NULL when no segment copies a page or the shape has no V.
+ * Errors, all before any launch: PIC_ERR_INVALID_ARG (NULL arrays, bad
+ * counts, page_size < 1, n_pages not ceil((first + length) / page_size)),
+ * PIC_ERR_RANGE (first, length, recompute_k or a page id out of range),
+ * PIC_ERR_OVERLAP (two segments turn the same slot of a page in place; a
+ * copy target is used twice, or is also a page some segment reads or
+ * turns; a page is copied by one segment and turned in place by another).
+ * Per call the library stages the tiles and shift tables in stream-ordered
+ * device memory that it frees on the same stream.
+ */
+pic_status pic_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *rope,
+                            const pic_kv_view *buf, int32_t page_size, int64_t n_phys_pages,
+                            const pic_page_segment *segments, int32_t n_segments,
+                            int32_t layer_begin, int32_t layer_end, void *stream);
+
+/*
  * Decode attention over a request's context without writing the stitched
  * cache (Irminsul, Technical Summary sections 2.2 and 4: the delta-rotation
  * applied in the attention kernel's HBM-to-on-chip load path).  For every

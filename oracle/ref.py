@@ -226,6 +226,96 @@ def rotate_inplace(wl, buf_k, layer_begin=0, layer_end=None, dtype=None, layer_b
     return STATUS[st]
 
 
+def validate_rotate_paged(page_size, n_phys_pages, segments) -> str:
+    """The status pic_rotate_paged gives a set of paged segments, checked
+    here from its stated rules (before any shape checks): bad_arg for counts,
+    range for positions and page ids, overlap for clashing writes."""
+    if page_size < 1 or n_phys_pages < 1:
+        return "bad_arg"
+    turned_slots, targets, sources, turned_pages, all_pages = set(), [], set(), set(), set()
+    for sg in segments:
+        if not (0 <= sg.first < page_size) or sg.length < 1:
+            return "range"
+        if not (0 <= sg.recompute_k <= sg.length):
+            return "range"
+        n_pages = -(-(sg.first + sg.length) // page_size)
+        if len(sg.pages) != n_pages:
+            return "bad_arg"
+        cow = sg.cow if sg.cow is not None else [-1] * n_pages
+        if len(cow) != n_pages:
+            return "bad_arg"
+        for i, (pg, cw) in enumerate(zip(sg.pages, cow)):
+            if not (0 <= pg < n_phys_pages) or not (-1 <= cw < n_phys_pages):
+                return "range"
+            all_pages.add(pg)
+            if cw >= 0:
+                if cw in targets:
+                    return "overlap"
+                targets.append(cw)
+                sources.add(pg)
+                continue
+            # logical positions of the page's turned tokens
+            lo = max(sg.first + sg.recompute_k, i * page_size)
+            hi = min(sg.first + sg.length, (i + 1) * page_size)
+            if sg.delta == 0 or lo >= hi:
+                continue
+            turned_pages.add(pg)
+            for q in range(lo, hi):
+                key = (pg, q - i * page_size)
+                if key in turned_slots:
+                    return "overlap"
+                turned_slots.add(key)
+    if any(t in all_pages for t in targets) or sources & turned_pages:
+        return "overlap"
+    return "ok"
+
+
+def rotate_paged(shape, buf_k, buf_v, page_size, segments, layer_begin=0, layer_end=None,
+                 dtype=None) -> str:
+    """fp64 oracle of pic_rotate_paged on numpy buffers [L][pages][page][H][D]
+    (buf_v may be None): every shared page (cow[i] >= 0) is copied whole,
+    K and V, to its target page, then every segment's tokens t in
+    [recompute_k, length) have their K rotary slice turned by the segment's
+    delta where they now live (the copy for a shared page, the page itself
+    otherwise), by this oracle's in-place turn.  shape: an object with
+    n_layers, n_heads, row_dim, rope_offset, rope_dim, style, theta,
+    inv_freq; segments: objects with pages, cow, delta, first, length,
+    recompute_k.  Returns the status."""
+    from types import SimpleNamespace as NS
+    dt = dtype or shape.dtype
+    le = shape.n_layers if layer_end is None else layer_end
+    st = validate_rotate_paged(page_size, buf_k.shape[1], segments)
+    if st != "ok":
+        return st
+    L = slice(layer_begin, le)
+    for sg in segments:  # copies first: no copy source is turned, no target is read
+        for pg, cw in zip(sg.pages, sg.cow if sg.cow is not None else [-1] * len(sg.pages)):
+            if cw >= 0:
+                buf_k[L, cw] = buf_k[L, pg]
+                if buf_v is not None:
+                    buf_v[L, cw] = buf_v[L, pg]
+    for sg in segments:
+        if sg.delta == 0:
+            continue
+        cow = sg.cow if sg.cow is not None else [-1] * len(sg.pages)
+        home = [cw if cw >= 0 else pg for pg, cw in zip(sg.pages, cow)]
+        where = [(home[(sg.first + t) // page_size], (sg.first + t) % page_size)
+                 for t in range(sg.length)]
+        rows = np.stack([buf_k[L, p, s] for p, s in where], axis=1)  # [L'][length][H][D]
+        sub = NS(dtype=dt, n_layers=rows.shape[0], n_heads=shape.n_heads, row_dim=shape.row_dim,
+                 rope_offset=shape.rope_offset, rope_dim=shape.rope_dim, style=shape.style,
+                 theta=shape.theta, inv_freq=getattr(shape, "inv_freq", None), n_tokens=sg.length,
+                 segments=[NS(token_start=0, length=sg.length, delta=sg.delta,
+                              recompute_k=sg.recompute_k)])
+        rows = np.ascontiguousarray(rows)
+        res = rotate_inplace(sub, rows, 0, rows.shape[0], dtype=dt)
+        if res != "ok":
+            return res
+        for t, (p, s) in enumerate(where):
+            buf_k[L, p, s] = rows[:, t]
+    return "ok"
+
+
 def round_bf16(x) -> np.ndarray:
     """bf16 bit patterns of fp64 values, one round-to-nearest-even each."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))

@@ -62,6 +62,19 @@ class Segment:
     recompute_k: int = 0
 
 
+@dataclass(frozen=True)
+class PageSegment:
+    """A segment of a paged buffer (pic_rotate_paged): tokens [0, length) at
+    logical positions first + t of the block table `pages`; cow[i] >= 0 is
+    the page a shared page i is copied to, -1 a page the caller owns."""
+    pages: tuple
+    cow: Optional[tuple]
+    delta: int
+    first: int
+    length: int
+    recompute_k: int = 0
+
+
 @dataclass
 class Workload:
     name: str
@@ -212,6 +225,54 @@ def config5(seed: int = 0, n_layers: int = 36) -> Workload:
 
 
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
+
+
+def paged_cow_case(seed: int, dtype: str = "bf16", style: str = "half", mla: bool = False,
+                   n_layers: int = 2, page_size: int = 16, n_chunks: int = 4, max_len: int = 70,
+                   share: float = 0.5, delta_range: int = 5000):
+    """A small seeded pic_rotate_paged problem: chunks of ragged length sit
+    in physical pages of a pool (a random permutation), starting at a random
+    slot of their first page.  A chunk is shared with probability `share`:
+    then 2..3 segments (requests) map it, each copying every page to fresh
+    target pages with its own shift; a private chunk has one segment that
+    copies each page with probability 0.3 (a block some other request holds)
+    and turns the rest in place.  Returns (workload fields for the shape,
+    n_phys_pages, segments)."""
+    rng = np.random.default_rng(seed)
+    if mla:
+        heads, row, roff, rdim, has_v, theta = 1, 576, 512, 64, False, 10000.0
+    else:
+        heads, row, roff, rdim, has_v, theta = 2, 128, 0, 128, True, 500000.0
+    chunks = []
+    for _ in range(n_chunks):
+        first = int(rng.integers(0, page_size))
+        length = int(rng.integers(1, max_len + 1))
+        chunks.append((first, length, -(-(first + length) // page_size)))
+    shared = [bool(rng.random() < share) for _ in chunks]
+    n_refs = [int(rng.integers(2, 4)) if sh else 1 for sh in shared]
+    n_pages = sum(c[2] for c in chunks)
+    n_targets = sum(c[2] * k for c, k in zip(chunks, n_refs))
+    n_phys = n_pages + n_targets + int(rng.integers(0, 5))
+    perm = [int(x) for x in rng.permutation(n_phys)]
+    take = iter(perm)
+    segs = []
+    for (first, length, npg), sh, k in zip(chunks, shared, n_refs):
+        pages = tuple(next(take) for _ in range(npg))
+        for _ in range(k):
+            if sh:
+                cow = tuple(next(take) for _ in range(npg))
+            else:
+                cow = tuple(next(take) if rng.random() < 0.3 else -1 for _ in range(npg))
+                if all(c < 0 for c in cow) and rng.random() < 0.5:
+                    cow = None
+            delta = 0 if rng.random() < 0.1 else int(rng.integers(-delta_range, delta_range + 1))
+            rk = int(rng.choice([0, 0, 1, length, int(rng.integers(0, length + 1))]))
+            segs.append(PageSegment(pages, cow, delta, first, length, rk))
+    order = [int(i) for i in rng.permutation(len(segs))]
+    segs = [segs[i] for i in order]
+    wl = Workload(f"paged cow {seed}", dtype, n_layers, heads, row, roff, rdim, style, theta,
+                  has_v, page_size=page_size, n_phys_pages=n_phys)
+    return wl, n_phys, segs
 
 
 def decode_batch(seed: int = 0, n_requests: int = 16, n_layers: int = 32) -> Workload:

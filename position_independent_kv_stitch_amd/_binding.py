@@ -26,7 +26,8 @@ DTYPES = {"f32": 0, "bf16": 1}
 STYLES = {"half": 0, "interleaved": 1}
 
 # every entry point the header declares
-EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_attend", "pic_attend_latent",
+EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_rotate_paged", "pic_attend",
+           "pic_attend_latent",
            "pic_attend_boundary", "pic_plan_info",
            "pic_plan_ranges", "pic_plan_destroy", "pic_registry_create", "pic_registry_add",
            "pic_registry_destroy", "pic_match", "pic_last_error")
@@ -106,6 +107,12 @@ class SegmentC(C.Structure):
                 ("recompute_k", C.c_int32)]
 
 
+class PageSegmentC(C.Structure):
+    _fields_ = [("pages", C.POINTER(C.c_int32)), ("cow", C.POINTER(C.c_int32)),
+                ("delta", C.c_int64), ("n_pages", C.c_int32), ("first", C.c_int32),
+                ("length", C.c_int32), ("recompute_k", C.c_int32)]
+
+
 class CdcConfig(C.Structure):
     _fields_ = [("threshold", C.c_uint64), ("gear_seed", C.c_uint64), ("fp_seed", C.c_uint64),
                 ("fingerprint", C.c_int32), ("window", C.c_int32)]
@@ -175,6 +182,10 @@ def _configure(lib):
     lib.pic_rotate_inplace.argtypes = [P(KvShape), P(RopeConfig), P(KvView), C.c_int64,
                                        P(SegmentC), C.c_int32, C.c_int32, C.c_int32,
                                        C.c_void_p]
+    lib.pic_rotate_paged.restype = C.c_int
+    lib.pic_rotate_paged.argtypes = [P(KvShape), P(RopeConfig), P(KvView), C.c_int32, C.c_int64,
+                                     P(PageSegmentC), C.c_int32, C.c_int32, C.c_int32,
+                                     C.c_void_p]
     lib.pic_attend.restype = C.c_int
     lib.pic_attend.argtypes = [C.c_void_p, P(KvView), P(KvView), P(AttendArgs), C.c_void_p]
     lib.pic_attend_latent.restype = C.c_int
@@ -605,6 +616,39 @@ def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
     _check(lib.pic_rotate_inplace(C.byref(shape), C.byref(rope), C.byref(view), T, sarr,
                                   len(segments), layer_begin, le, _stream_of(buf_k, stream)),
            lib)
+
+
+def rotate_paged(buf_k, buf_v, segments: Sequence, *, rope_dim: int, theta: float,
+                 style: str = "half", rope_offset: int = 0, layer_begin: int = 0,
+                 layer_end: Optional[int] = None, inv_freq=None, stream=None, library=None):
+    """Enqueue pic_rotate_paged on a paged buffer buf_k (and buf_v, or None)
+    of shape [L][P][page][H][D].  segments are objects with fields pages and
+    cow (sequences of physical page ids, cow -1 for a page the caller owns,
+    or cow None), delta, first, length and recompute_k, or tuples in that
+    order."""
+    lib = load_library(library)
+    L, P, S, H, D = buf_k.shape
+    le = L if layer_end is None else layer_end
+    shape, rope, keep = _shape_and_rope(_dtype_name(buf_k), L, H, D, rope_offset, rope_dim,
+                                        style, theta, buf_v is not None, inv_freq)
+    sarr = (PageSegmentC * max(1, len(segments)))()
+    for i, sg in enumerate(segments):
+        pages = list(_get(sg, "pages", 0))
+        pa = (C.c_int32 * max(1, len(pages)))(*pages)
+        keep.append(pa)
+        cow = _get(sg, "cow", 1)
+        if cow is not None:
+            ca = (C.c_int32 * max(1, len(cow)))(*list(cow))
+            keep.append(ca)
+            cptr = C.cast(ca, C.POINTER(C.c_int32))
+        else:
+            cptr = C.POINTER(C.c_int32)()
+        sarr[i] = PageSegmentC(C.cast(pa, C.POINTER(C.c_int32)), cptr, int(_get(sg, "delta", 2)),
+                               len(pages), int(_get(sg, "first", 3)), int(_get(sg, "length", 4)),
+                               int(_get(sg, "recompute_k", 5)))
+    view = _view(buf_k, buf_v, "paged")
+    _check(lib.pic_rotate_paged(C.byref(shape), C.byref(rope), C.byref(view), S, P, sarr,
+                                len(segments), layer_begin, le, _stream_of(buf_k, stream)), lib)
 
 
 def rotate_workload(wl, buf_k, layer_begin=0, layer_end=None, stream=None, library=None):

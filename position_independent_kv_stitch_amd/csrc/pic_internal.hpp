@@ -123,6 +123,12 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
                          int64_t buf_tokens, const pic_segment *segments, int32_t n_segments,
                          Problem *out);
 
+// pic_rotate_paged: the in-place turns (turn) and the copies of shared pages
+// (copy) of a set of paged segments, validated.
+pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *rope,
+                              int32_t page_size, int64_t n_phys_pages,
+                              const pic_page_segment *segments, int32_t n_segments,
+                              Problem *turn, Problem *copy);
 Staged stage(const Problem &p);
 
 // The matrix-core path of pic_attend (attend_gqa.hip): whether it takes a

@@ -19,6 +19,7 @@
 #include <cstring>
 #include <new>
 #include <unordered_map>
+#include <unordered_set>
 
 #include "pic_internal.hpp"
 
@@ -500,6 +501,138 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
     }
     fill_info(&p, written, masked, buf_tokens);
     p.info.n_entries = n_segments;
+    return PIC_OK;
+}
+
+pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *rope,
+                              int32_t page_size, int64_t n_phys_pages,
+                              const pic_page_segment *segments, int32_t n_segments,
+                              Problem *turn, Problem *copy) {
+    Units ut{}, uc{};
+    pic_status st = derive_units(shape, rope, true, &ut);
+    if (st) return st;
+    st = derive_units(shape, rope, false, &uc);
+    if (st) return st;
+    if (page_size < 1 || n_phys_pages < 1 || n_phys_pages > INT32_MAX)
+        return fail(PIC_ERR_INVALID_ARG, "page_size %d and n_phys_pages %lld must be >= 1 (pages "
+                    "fit int32)", page_size, static_cast<long long>(n_phys_pages));
+    if (n_segments < 0 || (n_segments > 0 && !segments))
+        return fail(PIC_ERR_INVALID_ARG, "bad segment array");
+    // the token run [lo, hi) of segment g that page i holds, as logical
+    // positions, and the part of it that is turned
+    auto page_run = [&](const pic_page_segment &sg, int32_t i, int64_t from_t, int64_t *lo,
+                        int64_t *hi) {
+        *lo = std::max<int64_t>(int64_t{sg.first} + from_t, int64_t{i} * page_size);
+        *hi = std::min<int64_t>(int64_t{sg.first} + sg.length, int64_t{i + 1} * page_size);
+    };
+    std::unordered_set<int64_t> turned_slots, targets, sources, turned_pages, all_pages;
+    for (int g = 0; g < n_segments; g++) {
+        const pic_page_segment &sg = segments[g];
+        if (!sg.pages) return fail(PIC_ERR_INVALID_ARG, "segment %d: pages is NULL", g);
+        if (sg.first < 0 || sg.first >= page_size || sg.length < 1)
+            return fail(PIC_ERR_RANGE, "segment %d: first %d, length %d (page_size %d)", g, sg.first,
+                        sg.length, page_size);
+        if (sg.recompute_k < 0 || sg.recompute_k > sg.length)
+            return fail(PIC_ERR_RANGE, "segment %d: recompute_k %d", g, sg.recompute_k);
+        const int64_t need = (int64_t{sg.first} + sg.length + page_size - 1) / page_size;
+        if (sg.n_pages != need)
+            return fail(PIC_ERR_INVALID_ARG, "segment %d: n_pages %d, its tokens span %lld pages", g,
+                        sg.n_pages, static_cast<long long>(need));
+        for (int32_t i = 0; i < sg.n_pages; i++) {
+            if (sg.pages[i] < 0 || sg.pages[i] >= n_phys_pages)
+                return fail(PIC_ERR_RANGE, "segment %d: page %d = %d outside [0, %lld)", g, i,
+                            sg.pages[i], static_cast<long long>(n_phys_pages));
+            if (sg.cow && (sg.cow[i] < -1 || sg.cow[i] >= n_phys_pages))
+                return fail(PIC_ERR_RANGE, "segment %d: copy target %d = %d outside [-1, %lld)", g, i,
+                            sg.cow[i], static_cast<long long>(n_phys_pages));
+            all_pages.insert(sg.pages[i]);
+            if (sg.cow && sg.cow[i] >= 0) {
+                if (!targets.insert(sg.cow[i]).second)
+                    return fail(PIC_ERR_OVERLAP, "segment %d: copy target %d used twice", g, sg.cow[i]);
+                sources.insert(sg.pages[i]);
+                continue;
+            }
+            int64_t lo, hi;
+            page_run(sg, i, sg.recompute_k, &lo, &hi);
+            if (sg.delta == 0 || lo >= hi) continue;  // nothing written in place
+            turned_pages.insert(sg.pages[i]);
+            for (int64_t q = lo; q < hi; q++)
+                if (!turned_slots.insert(int64_t{sg.pages[i]} * page_size + (q - int64_t{i} * page_size))
+                         .second)
+                    return fail(PIC_ERR_OVERLAP, "segment %d: slot %lld of page %d is turned twice", g,
+                                static_cast<long long>(q - int64_t{i} * page_size), sg.pages[i]);
+        }
+    }
+    for (int64_t t : targets)
+        if (all_pages.count(t))
+            return fail(PIC_ERR_OVERLAP, "copy target %lld is also a page a segment maps",
+                        static_cast<long long>(t));
+    for (int64_t t : sources)
+        if (turned_pages.count(t))
+            return fail(PIC_ERR_OVERLAP, "page %lld is copied by one segment and turned in place by "
+                        "another", static_cast<long long>(t));
+
+    auto init = [&](Problem &p, const Units &u, int32_t mode) {
+        p.shape = *shape;
+        p.rope_dim = rope->rope_dim;
+        p.style = rope->style;
+        p.mode = mode;
+        p.page_size = page_size;
+        p.src_page_size = page_size;
+        p.capacity = n_phys_pages * page_size;
+        p.num_phys_pages = n_phys_pages;
+        p.n_requests = 1;
+        p.u = u;
+        p.launch = launch_shape_of(shape->dtype, u);
+        p.tile_tokens = kTileSteps * 4 * p.launch.g;
+    };
+    init(*turn, ut, kInPlace);
+    turn->shape.has_v = 0;
+    turn->launch.stream_loads = 1;  // every turned slot is read once
+    init(*copy, uc, kPaged);
+    copy->launch.stream_loads = 0;  // a shared page may be copied for several segments
+    std::unordered_map<int64_t, int32_t> tab_turn, tab_copy;
+    auto table = [&](Problem &p, std::unordered_map<int64_t, int32_t> &m, int64_t delta) {
+        auto it = m.find(delta);
+        if (it != m.end()) return it->second;
+        const int32_t idx = static_cast<int32_t>(m.size());
+        m.emplace(delta, idx);
+        append_shift_table(*rope, delta, p.cs);
+        return idx;
+    };
+    int64_t turned = 0, copied = 0;
+    for (int g = 0; g < n_segments; g++) {
+        const pic_page_segment &sg = segments[g];
+        for (int32_t i = 0; i < sg.n_pages; i++) {
+            const int64_t p0 = int64_t{i} * page_size;  // logical position of the page's slot 0
+            int64_t lo, hi;
+            page_run(sg, i, sg.recompute_k, &lo, &hi);
+            const bool turn_run = sg.delta != 0 && lo < hi;
+            if (sg.cow && sg.cow[i] >= 0) {
+                // the whole page to its copy: slots before and after the
+                // turned run bit for bit, the run turned
+                const int32_t cs = turn_run ? table(*copy, tab_copy, sg.delta) : -1;
+                const HostEntry plain{0, 0, 0, 0, -1, 0}, turned_e{0, 0, 0, 0, cs, 0};
+                if (turn_run) {
+                    add_tiles(copy, plain, sg.cow, sg.pages, static_cast<int32_t>(p0), static_cast<int32_t>(lo));
+                    add_tiles(copy, turned_e, sg.cow, sg.pages, static_cast<int32_t>(lo), static_cast<int32_t>(hi));
+                    add_tiles(copy, plain, sg.cow, sg.pages, static_cast<int32_t>(hi),
+                              static_cast<int32_t>(p0 + page_size));
+                    turned += hi - lo;
+                } else {
+                    add_tiles(copy, plain, sg.cow, sg.pages, static_cast<int32_t>(p0),
+                              static_cast<int32_t>(p0 + page_size));
+                }
+                copied += page_size;
+            } else if (turn_run) {
+                const HostEntry e{0, 0, 0, 0, table(*turn, tab_turn, sg.delta), 0};
+                add_tiles(turn, e, nullptr, sg.pages, static_cast<int32_t>(lo), static_cast<int32_t>(hi));
+                turned += hi - lo;
+            }
+        }
+    }
+    fill_info(turn, turned, 0, 0);
+    fill_info(copy, copied, 0, 0);
     return PIC_OK;
 }
 

@@ -419,6 +419,61 @@ struct HostBytes {
 
 void free_host_bytes(void *p) { delete static_cast<HostBytes *>(p); }
 
+// Stage a per-call problem's tiles and shift tables in stream-ordered device
+// memory (freed on the same stream once the kernel has run) and launch it
+// over n_layers layers from layer_begin; views holds the pointers and strides.
+pic_status run_staged(const Problem &p, const KArgs &views, int32_t layer_begin, int32_t n_layers,
+                      hipStream_t stream, const char *what) {
+    if (p.tiles.empty() || n_layers == 0) return PIC_OK;
+    Staged stg = stage(p);
+    auto *host = new (std::nothrow) HostBytes{std::move(stg.bytes)};
+    if (!host) return fail(PIC_ERR_NOMEM, "out of host memory");
+    void *dmem = nullptr;
+    hipError_t e = hipMallocAsync(&dmem, host->bytes.size(), stream);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();  // clear it
+        delete host;
+        return fail(PIC_ERR_DEVICE, "%s: hipMallocAsync (metadata): %s", what, hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(dmem, host->bytes.data(), host->bytes.size(), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) {
+        (void)hipFreeAsync(dmem, stream);
+        (void)hipStreamSynchronize(stream);
+        delete host;
+        return fail(PIC_ERR_DEVICE, "%s: hipMemcpyAsync (metadata): %s", what, hipGetErrorString(e));
+    }
+    // the staging bytes live until the stream has consumed them
+    e = hipLaunchHostFunc(stream, free_host_bytes, host);
+    if (e != hipSuccess) {
+        (void)hipStreamSynchronize(stream);
+        delete host;
+        (void)hipFreeAsync(dmem, stream);
+        return fail(PIC_ERR_DEVICE, "%s: hipLaunchHostFunc: %s", what, hipGetErrorString(e));
+    }
+    KArgs a = args_for(p, static_cast<const uint8_t *>(dmem), stg);
+    a.src_k = views.src_k;
+    a.src_v = views.src_v;
+    a.dst_k = views.dst_k;
+    a.dst_v = views.dst_v;
+    a.s_layer = views.s_layer;
+    a.s_tok = views.s_tok;
+    a.s_head = views.s_head;
+    a.s_page = views.s_page;
+    a.src_paged = views.src_paged;
+    a.d_layer = views.d_layer;
+    a.d_tok = views.d_tok;
+    a.d_head = views.d_head;
+    a.d_page = views.d_page;
+    a.d_req = views.d_req;
+    a.layer_begin = layer_begin;
+    e = launch(p, a, n_layers, stream);
+    const hipError_t e2 = hipFreeAsync(dmem, stream);
+    if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s kernel launch: %s", what, hipGetErrorString(e));
+    if (e2 != hipSuccess)
+        return fail(PIC_ERR_DEVICE, "%s: hipFreeAsync (metadata): %s", what, hipGetErrorString(e2));
+    return PIC_OK;
+}
+
 }  // namespace
 }  // namespace pic
 
@@ -492,45 +547,51 @@ pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *
                     "within one step");
     if (p.tiles.empty() || layer_begin == layer_end) return PIC_OK;
 
+    KArgs v{};
+    v.src_k = buf->k;
+    v.dst_k = buf->k;
+    v.s_layer = v.d_layer = buf->layer_stride;
+    v.s_tok = v.d_tok = buf->token_stride;
+    v.s_head = v.d_head = buf->head_stride;
+    return run_staged(p, v, layer_begin, layer_end - layer_begin, static_cast<hipStream_t>(stream_),
+                      "rotate");
+}
+
+pic_status pic_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *rope,
+                            const pic_kv_view *buf, int32_t page_size, int64_t n_phys_pages,
+                            const pic_page_segment *segments, int32_t n_segments,
+                            int32_t layer_begin, int32_t layer_end, void *stream_) {
+    using namespace pic;
+    clear_error();
+    Problem turn, copy;
+    pic_status st = build_rotate_paged(shape, rope, page_size, n_phys_pages, segments, n_segments,
+                                       &turn, &copy);
+    if (st) return st;
+    if (layer_begin < 0 || layer_begin > layer_end || layer_end > shape->num_layers)
+        return fail(PIC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin,
+                    layer_end, shape->num_layers);
+    const bool need_v = !copy.tiles.empty() && shape->has_v;
+    st = check_view(buf, turn.u.vec, need_v, "buf");
+    if (st) return st;
+    if (!slot_offsets_fit(copy, buf->token_stride, buf->head_stride) ||
+        !slot_offsets_fit(turn, buf->token_stride, buf->head_stride))
+        return fail(PIC_ERR_RANGE, "the view's token/head strides span 2^31 elements or more "
+                    "within one step");
+    if (layer_begin == layer_end) return PIC_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_);
-    Staged stg = stage(p);
-    auto *host = new (std::nothrow) HostBytes{std::move(stg.bytes)};
-    if (!host) return fail(PIC_ERR_NOMEM, "out of host memory");
-    void *dmem = nullptr;
-    hipError_t e = hipMallocAsync(&dmem, host->bytes.size(), stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();  // clear it
-        delete host;
-        return hip_fail(e, "hipMallocAsync (segment metadata)");
-    }
-    e = hipMemcpyAsync(dmem, host->bytes.data(), host->bytes.size(), hipMemcpyHostToDevice,
-                       stream);
-    if (e != hipSuccess) {
-        (void)hipFreeAsync(dmem, stream);
-        (void)hipStreamSynchronize(stream);
-        delete host;
-        return hip_fail(e, "hipMemcpyAsync (segment metadata)");
-    }
-    // the staging bytes live until the stream has consumed them
-    e = hipLaunchHostFunc(stream, free_host_bytes, host);
-    if (e != hipSuccess) {
-        (void)hipStreamSynchronize(stream);
-        delete host;
-        (void)hipFreeAsync(dmem, stream);
-        return hip_fail(e, "hipLaunchHostFunc");
-    }
-    KArgs a = args_for(p, static_cast<const uint8_t *>(dmem), stg);
-    a.src_k = buf->k;
-    a.dst_k = buf->k;
-    a.s_layer = a.d_layer = buf->layer_stride;
-    a.s_tok = a.d_tok = buf->token_stride;
-    a.s_head = a.d_head = buf->head_stride;
-    a.layer_begin = layer_begin;
-    e = launch(p, a, layer_end - layer_begin, stream);
-    hipError_t e2 = hipFreeAsync(dmem, stream);
-    if (e != hipSuccess) return hip_fail(e, "rotate kernel launch");
-    if (e2 != hipSuccess) return hip_fail(e2, "hipFreeAsync (segment metadata)");
-    return PIC_OK;
+    KArgs v{};
+    v.src_k = v.dst_k = buf->k;
+    v.src_v = v.dst_v = need_v ? buf->v : nullptr;
+    v.s_layer = v.d_layer = buf->layer_stride;
+    v.s_tok = v.d_tok = buf->token_stride;
+    v.s_head = v.d_head = buf->head_stride;
+    v.s_page = v.d_page = buf->page_stride;
+    v.src_paged = 1;
+    // the copies read shared pages that no turn writes, and the turns write
+    // pages that no copy reads or writes, so their order does not matter
+    st = run_staged(copy, v, layer_begin, layer_end - layer_begin, stream, "copy-on-write");
+    if (st) return st;
+    return run_staged(turn, v, layer_begin, layer_end - layer_begin, stream, "paged rotate");
 }
 
 void pic_plan_destroy(pic_plan_t *plan) {

@@ -36,7 +36,8 @@ def test_exports_every_declared_symbol():
 STRUCTS = {
     "pic_rope_config": B.RopeConfig, "pic_kv_shape": B.KvShape, "pic_chunk": B.ChunkC,
     "pic_entry": B.EntryC, "pic_request": B.RequestC, "pic_geom": B.Geom, "pic_attend_args": B.AttendArgs,
-    "pic_kv_view": B.KvView, "pic_segment": B.SegmentC, "pic_plan_info_t": B.PlanInfo,
+    "pic_kv_view": B.KvView, "pic_segment": B.SegmentC, "pic_page_segment": B.PageSegmentC,
+    "pic_plan_info_t": B.PlanInfo,
     "pic_cdc_config": B.CdcConfig, "pic_match_t": B.MatchRecord,
     "pic_attend_latent_args": B.LatentArgs, "pic_attend_boundary_args": B.BoundaryArgs,
 }
