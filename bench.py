@@ -74,6 +74,9 @@ WORKLOADS = {
            "x 4096 tokens (stitch, contiguous)",
     "inplace": "Qwen3-8B, 36 layers, 8 kv heads x 128, bf16, 131072 tokens, 64 segments rotated "
                "in place by shifts in [-65536, 65536], recompute_k 16 (pic_rotate_inplace)",
+    "inplace-paged-cow": "the inplace workload on a paged pool of 16-token pages (random physical "
+                         "order): 48 chunks turned in place, 16 shared chunks copied page by page "
+                         "(K and V) to fresh pages and turned there (pic_rotate_paged)",
     "single-layer": "1 layer, 8 kv heads x 128, fp32, 3 chunks of 512/1024/256 tokens "
                     "(stitch, contiguous; launch-bound)",
     "attend-decode": "decode attention over stitched contexts, chunk keys turned on load: 16 "
@@ -119,6 +122,30 @@ def setup_workload(name, torch, pic):
                 "kernel": "stitch_kernel<bf16, half> (in place)", "plan": None,
                 "config": {"workload": WORKLOADS[name], "storage": "bf16",
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
+    if name == "inplace-paged-cow":
+        from pic_workloads import config5_paged_cow
+        wl, n_phys, segs = config5_paged_cow()
+        shape = (wl.n_layers, n_phys, wl.page_size, wl.n_heads, wl.row_dim)
+        k = normal_values(shape, wl.dtype, 0, "cuda:0")
+        v = normal_values(shape, wl.dtype, 1, "cuda:0")
+        row = wl.n_heads * wl.row_dim * wl.esize  # one token's K (or V) row
+        rot = wl.n_heads * wl.rope_dim * wl.esize
+        turned = sum(s.length - s.recompute_k for s in segs if s.delta != 0)
+        copied = sum(len(s.pages) * wl.page_size for s in segs if s.cow is not None)
+        in_place = sum(s.length - s.recompute_k for s in segs if s.delta != 0 and s.cow is None)
+        # in place: the rotary slice read and written; copies: K and V rows read and written
+        nbytes = (in_place * rot * 2 + copied * row * 2 * 2) * wl.n_layers
+
+        def step():
+            pic.rotate_paged(k, v, segs, rope_dim=wl.rope_dim, theta=wl.theta, style=wl.style,
+                             rope_offset=wl.rope_offset)
+        return {"wl": wl, "step": step, "bytes": nbytes, "token_layers": turned * wl.n_layers,
+                "kernel": "stitch_kernel<bf16, half> (page copies, then in-place turns)",
+                "plan": None,
+                "config": {"workload": WORKLOADS[name], "storage": "bf16", "layers": wl.n_layers,
+                           "page_size": wl.page_size, "phys_pages": n_phys, "segments": len(segs),
+                           "shared_segments": sum(1 for s in segs if s.cow is not None),
+                           "copied_tokens": copied, "turned_in_place_tokens": in_place}}
     if name.startswith("attend-decode"):
         return setup_attend(name, torch, pic)
     if name.startswith("attend-mla-decode"):

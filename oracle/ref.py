@@ -228,29 +228,31 @@ def rotate_inplace(wl, buf_k, layer_begin=0, layer_end=None, dtype=None, layer_b
 
 def validate_rotate_paged(page_size, n_phys_pages, segments) -> str:
     """The status pic_rotate_paged gives a set of paged segments, checked
-    here from its stated rules (before any shape checks): bad_arg for counts,
-    range for positions and page ids, overlap for clashing writes."""
+    here from its stated rules (after the shape checks): first every
+    segment's counts (bad_arg) and positions and page ids (range), then the
+    clashes between segments (overlap)."""
     if page_size < 1 or n_phys_pages < 1:
         return "bad_arg"
-    turned_slots, targets, sources, turned_pages, all_pages = set(), [], set(), set(), set()
     for sg in segments:
         if not (0 <= sg.first < page_size) or sg.length < 1:
             return "range"
         if not (0 <= sg.recompute_k <= sg.length):
             return "range"
         n_pages = -(-(sg.first + sg.length) // page_size)
-        if len(sg.pages) != n_pages:
+        cow = sg.cow if sg.cow is not None else [-1] * len(sg.pages)
+        if len(sg.pages) != n_pages or len(cow) != n_pages:
             return "bad_arg"
-        cow = sg.cow if sg.cow is not None else [-1] * n_pages
-        if len(cow) != n_pages:
-            return "bad_arg"
-        for i, (pg, cw) in enumerate(zip(sg.pages, cow)):
+        for pg, cw in zip(sg.pages, cow):
             if not (0 <= pg < n_phys_pages) or not (-1 <= cw < n_phys_pages):
                 return "range"
+    turned_slots, targets, sources, turned_pages, all_pages = set(), [], set(), set(), set()
+    clash = False
+    for sg in segments:
+        cow = sg.cow if sg.cow is not None else [-1] * len(sg.pages)
+        for i, (pg, cw) in enumerate(zip(sg.pages, cow)):
             all_pages.add(pg)
             if cw >= 0:
-                if cw in targets:
-                    return "overlap"
+                clash |= cw in targets
                 targets.append(cw)
                 sources.add(pg)
                 continue
@@ -262,10 +264,9 @@ def validate_rotate_paged(page_size, n_phys_pages, segments) -> str:
             turned_pages.add(pg)
             for q in range(lo, hi):
                 key = (pg, q - i * page_size)
-                if key in turned_slots:
-                    return "overlap"
+                clash |= key in turned_slots
                 turned_slots.add(key)
-    if any(t in all_pages for t in targets) or sources & turned_pages:
+    if clash or any(t in all_pages for t in targets) or sources & turned_pages:
         return "overlap"
     return "ok"
 

@@ -227,6 +227,33 @@ def config5(seed: int = 0, n_layers: int = 36) -> Workload:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
+def config5_paged_cow(seed: int = 0, n_layers: int = 36, n_shared: int = 16):
+    """The long-context in-place workload on a paged pool: Qwen3-8B shape
+    (36 layers, 8 KV heads x 128, theta 1e6, bf16), 64 chunks x 2048 tokens
+    in 16-token pages placed by a random permutation of the pool, each
+    chunk one segment shifted by a draw from [-65536, 65536] with the first
+    16 tokens left alone.  n_shared chunks (a random subset) are shared with
+    other requests: their pages are copied to fresh pages and turned there;
+    the other chunks are turned in place.  Returns (workload fields,
+    n_phys_pages, segments)."""
+    rng = np.random.default_rng(seed)
+    n, length, ps = 64, 2048, 16
+    npg = length // ps
+    deltas = rng.integers(-65536, 65536, size=n, endpoint=True)
+    shared = set(int(c) for c in rng.choice(n, size=n_shared, replace=False))
+    n_phys = n * npg + n_shared * npg
+    perm = [int(x) for x in rng.permutation(n_phys)]
+    take = iter(perm)
+    segs = []
+    for c in range(n):
+        pages = tuple(next(take) for _ in range(npg))
+        cow = tuple(next(take) for _ in range(npg)) if c in shared else None
+        segs.append(PageSegment(pages, cow, int(deltas[c]), 0, length, 16))
+    wl = Workload("qwen3-8b paged in-place 131072", "bf16", n_layers, 8, 128, 0, 128, "half",
+                  1000000.0, True, page_size=ps, n_phys_pages=n_phys)
+    return wl, n_phys, segs
+
+
 def paged_cow_case(seed: int, dtype: str = "bf16", style: str = "half", mla: bool = False,
                    n_layers: int = 2, page_size: int = 16, n_chunks: int = 4, max_len: int = 70,
                    share: float = 0.5, delta_range: int = 5000):

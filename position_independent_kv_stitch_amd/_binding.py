@@ -618,6 +618,22 @@ def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
            lib)
 
 
+def _int32_array(ids):
+    """A page-id list as a C-contiguous int32 array and its length; the array
+    holds at least one element, so its pointer is never NULL.  Ids outside
+    int32 are refused here rather than wrapped."""
+    a = np.asarray(ids)
+    if a.ndim != 1:
+        raise ValueError("a page list is one-dimensional")
+    if a.size and a.dtype != np.int32:
+        if not np.issubdtype(a.dtype, np.integer):
+            raise TypeError("page ids are integers")
+        if a.min() < np.iinfo(np.int32).min or a.max() > np.iinfo(np.int32).max:
+            raise ValueError("page id outside int32")
+    n = int(a.size)
+    return (np.ascontiguousarray(a, dtype=np.int32) if n else np.zeros(1, np.int32)), n
+
+
 def rotate_paged(buf_k, buf_v, segments: Sequence, *, rope_dim: int, theta: float,
                  style: str = "half", rope_offset: int = 0, layer_begin: int = 0,
                  layer_end: Optional[int] = None, inv_freq=None, stream=None, library=None):
@@ -633,19 +649,20 @@ def rotate_paged(buf_k, buf_v, segments: Sequence, *, rope_dim: int, theta: floa
                                         style, theta, buf_v is not None, inv_freq)
     sarr = (PageSegmentC * max(1, len(segments)))()
     for i, sg in enumerate(segments):
-        pages = list(_get(sg, "pages", 0))
-        pa = (C.c_int32 * max(1, len(pages)))(*pages)
+        pa, n_pages = _int32_array(_get(sg, "pages", 0))
         keep.append(pa)
         cow = _get(sg, "cow", 1)
         if cow is not None:
-            ca = (C.c_int32 * max(1, len(cow)))(*list(cow))
+            ca, n_cow = _int32_array(cow)
+            if n_cow != n_pages:
+                raise ValueError(f"segment {i}: {n_cow} copy targets for {n_pages} pages")
             keep.append(ca)
-            cptr = C.cast(ca, C.POINTER(C.c_int32))
+            cptr = ca.ctypes.data_as(C.POINTER(C.c_int32))
         else:
             cptr = C.POINTER(C.c_int32)()
-        sarr[i] = PageSegmentC(C.cast(pa, C.POINTER(C.c_int32)), cptr, int(_get(sg, "delta", 2)),
-                               len(pages), int(_get(sg, "first", 3)), int(_get(sg, "length", 4)),
-                               int(_get(sg, "recompute_k", 5)))
+        sarr[i] = PageSegmentC(pa.ctypes.data_as(C.POINTER(C.c_int32)), cptr,
+                               int(_get(sg, "delta", 2)), n_pages, int(_get(sg, "first", 3)),
+                               int(_get(sg, "length", 4)), int(_get(sg, "recompute_k", 5)))
     view = _view(buf_k, buf_v, "paged")
     _check(lib.pic_rotate_paged(C.byref(shape), C.byref(rope), C.byref(view), S, P, sarr,
                                 len(segments), layer_begin, le, _stream_of(buf_k, stream)), lib)

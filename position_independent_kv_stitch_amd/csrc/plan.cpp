@@ -19,7 +19,6 @@
 #include <cstring>
 #include <new>
 #include <unordered_map>
-#include <unordered_set>
 
 #include "pic_internal.hpp"
 
@@ -525,7 +524,10 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
         *lo = std::max<int64_t>(int64_t{sg.first} + from_t, int64_t{i} * page_size);
         *hi = std::min<int64_t>(int64_t{sg.first} + sg.length, int64_t{i + 1} * page_size);
     };
-    std::unordered_set<int64_t> turned_slots, targets, sources, turned_pages, all_pages;
+    // writes and reads, collected as intervals and page lists and checked
+    // after sorting (no per-slot sets: a call may turn ~10^5 tokens)
+    std::vector<Interval> turned_runs;  // key = page, [lo, hi) slots turned in place
+    std::vector<int64_t> targets, sources, turned_pages, all_pages;
     for (int g = 0; g < n_segments; g++) {
         const pic_page_segment &sg = segments[g];
         if (!sg.pages) return fail(PIC_ERR_INVALID_ARG, "segment %d: pages is NULL", g);
@@ -545,30 +547,38 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
             if (sg.cow && (sg.cow[i] < -1 || sg.cow[i] >= n_phys_pages))
                 return fail(PIC_ERR_RANGE, "segment %d: copy target %d = %d outside [-1, %lld)", g, i,
                             sg.cow[i], static_cast<long long>(n_phys_pages));
-            all_pages.insert(sg.pages[i]);
+            all_pages.push_back(sg.pages[i]);
             if (sg.cow && sg.cow[i] >= 0) {
-                if (!targets.insert(sg.cow[i]).second)
-                    return fail(PIC_ERR_OVERLAP, "segment %d: copy target %d used twice", g, sg.cow[i]);
-                sources.insert(sg.pages[i]);
+                targets.push_back(sg.cow[i]);
+                sources.push_back(sg.pages[i]);
                 continue;
             }
             int64_t lo, hi;
             page_run(sg, i, sg.recompute_k, &lo, &hi);
             if (sg.delta == 0 || lo >= hi) continue;  // nothing written in place
-            turned_pages.insert(sg.pages[i]);
-            for (int64_t q = lo; q < hi; q++)
-                if (!turned_slots.insert(int64_t{sg.pages[i]} * page_size + (q - int64_t{i} * page_size))
-                         .second)
-                    return fail(PIC_ERR_OVERLAP, "segment %d: slot %lld of page %d is turned twice", g,
-                                static_cast<long long>(q - int64_t{i} * page_size), sg.pages[i]);
+            turned_pages.push_back(sg.pages[i]);
+            turned_runs.push_back(Interval{sg.pages[i], lo - int64_t{i} * page_size,
+                                           hi - int64_t{i} * page_size});
         }
     }
+    if (any_overlap(turned_runs))
+        return fail(PIC_ERR_OVERLAP, "two segments turn the same slot of a page in place");
+    auto sort_unique = [](std::vector<int64_t> &v) {
+        std::sort(v.begin(), v.end());
+        v.erase(std::unique(v.begin(), v.end()), v.end());
+    };
+    std::sort(targets.begin(), targets.end());
+    if (std::adjacent_find(targets.begin(), targets.end()) != targets.end())
+        return fail(PIC_ERR_OVERLAP, "a copy target is used twice");
+    sort_unique(all_pages);
+    sort_unique(sources);
+    sort_unique(turned_pages);
     for (int64_t t : targets)
-        if (all_pages.count(t))
+        if (std::binary_search(all_pages.begin(), all_pages.end(), t))
             return fail(PIC_ERR_OVERLAP, "copy target %lld is also a page a segment maps",
                         static_cast<long long>(t));
     for (int64_t t : sources)
-        if (turned_pages.count(t))
+        if (std::binary_search(turned_pages.begin(), turned_pages.end(), t))
             return fail(PIC_ERR_OVERLAP, "page %lld is copied by one segment and turned in place by "
                         "another", static_cast<long long>(t));
 

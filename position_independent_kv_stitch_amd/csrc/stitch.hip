@@ -43,7 +43,10 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <cstring>
+#include <map>
 #include <memory>
+#include <mutex>
 
 #include "pic_internal.hpp"
 #include "rotate.hpp"
@@ -413,11 +416,35 @@ pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream_) {
 
 namespace {
 
-struct HostBytes {
-    std::vector<uint8_t> bytes;
+// Pinned staging for per-call metadata.  A copy from pageable memory makes
+// hipMemcpyAsync wait for the stream to drain, so each call would stall its
+// caller until earlier work finished; copies from pinned memory are truly
+// asynchronous.  Each device keeps a ring of pinned slots, each guarded by
+// an event recorded after the copy that reads it: a slot is refilled only
+// once that copy has run (the wait blocks only with more calls in flight
+// than slots).  Slots grow on demand and live until the process ends.
+constexpr int kPinnedSlots = 4;
+
+struct PinnedSlot {
+    void *host = nullptr;
+    size_t cap = 0;
+    hipEvent_t done = nullptr;
 };
 
-void free_host_bytes(void *p) { delete static_cast<HostBytes *>(p); }
+struct PinnedRing {
+    std::mutex mu;
+    PinnedSlot slots[kPinnedSlots];
+    int next = 0;
+};
+
+PinnedRing *pinned_ring(int device) {
+    static std::mutex mu;
+    static std::map<int, std::unique_ptr<PinnedRing>> rings;
+    std::lock_guard<std::mutex> lock(mu);
+    std::unique_ptr<PinnedRing> &r = rings[device];
+    if (!r) r.reset(new (std::nothrow) PinnedRing);
+    return r.get();
+}
 
 // Stage a per-call problem's tiles and shift tables in stream-ordered device
 // memory (freed on the same stream once the kernel has run) and launch it
@@ -425,30 +452,55 @@ void free_host_bytes(void *p) { delete static_cast<HostBytes *>(p); }
 pic_status run_staged(const Problem &p, const KArgs &views, int32_t layer_begin, int32_t n_layers,
                       hipStream_t stream, const char *what) {
     if (p.tiles.empty() || n_layers == 0) return PIC_OK;
-    Staged stg = stage(p);
-    auto *host = new (std::nothrow) HostBytes{std::move(stg.bytes)};
-    if (!host) return fail(PIC_ERR_NOMEM, "out of host memory");
+    const Staged stg = stage(p);
+    const size_t n = stg.bytes.size();
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+    PinnedRing *ring = pinned_ring(dev);
+    if (!ring) return fail(PIC_ERR_NOMEM, "out of host memory");
     void *dmem = nullptr;
-    hipError_t e = hipMallocAsync(&dmem, host->bytes.size(), stream);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();  // clear it
-        delete host;
-        return fail(PIC_ERR_DEVICE, "%s: hipMallocAsync (metadata): %s", what, hipGetErrorString(e));
-    }
-    e = hipMemcpyAsync(dmem, host->bytes.data(), host->bytes.size(), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) {
-        (void)hipFreeAsync(dmem, stream);
-        (void)hipStreamSynchronize(stream);
-        delete host;
-        return fail(PIC_ERR_DEVICE, "%s: hipMemcpyAsync (metadata): %s", what, hipGetErrorString(e));
-    }
-    // the staging bytes live until the stream has consumed them
-    e = hipLaunchHostFunc(stream, free_host_bytes, host);
-    if (e != hipSuccess) {
-        (void)hipStreamSynchronize(stream);
-        delete host;
-        (void)hipFreeAsync(dmem, stream);
-        return fail(PIC_ERR_DEVICE, "%s: hipLaunchHostFunc: %s", what, hipGetErrorString(e));
+    {
+        std::lock_guard<std::mutex> lock(ring->mu);
+        PinnedSlot &slot = ring->slots[ring->next];
+        ring->next = (ring->next + 1) % kPinnedSlots;
+        if (slot.done) {
+            e = hipEventSynchronize(slot.done);  // the copy that last read the slot has run
+            if (e != hipSuccess)
+                return fail(PIC_ERR_DEVICE, "%s: hipEventSynchronize: %s", what, hipGetErrorString(e));
+        } else {
+            e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                slot.done = nullptr;
+                return fail(PIC_ERR_DEVICE, "%s: hipEventCreate: %s", what, hipGetErrorString(e));
+            }
+        }
+        if (slot.cap < n) {
+            if (slot.host) (void)hipHostFree(slot.host);
+            slot.host = nullptr;
+            slot.cap = 0;
+            const size_t cap = std::max<size_t>(n, size_t{1} << 20);
+            e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
+            if (e != hipSuccess) {
+                slot.host = nullptr;
+                return fail(PIC_ERR_NOMEM, "%s: hipHostMalloc (%zu bytes): %s", what, cap,
+                            hipGetErrorString(e));
+            }
+            slot.cap = cap;
+        }
+        std::memcpy(slot.host, stg.bytes.data(), n);
+        e = hipMallocAsync(&dmem, n, stream);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();  // clear it
+            return fail(PIC_ERR_DEVICE, "%s: hipMallocAsync (metadata): %s", what, hipGetErrorString(e));
+        }
+        e = hipMemcpyAsync(dmem, slot.host, n, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipEventRecord(slot.done, stream);
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(dmem, stream);
+            (void)hipStreamSynchronize(stream);
+            return fail(PIC_ERR_DEVICE, "%s: hipMemcpyAsync (metadata): %s", what, hipGetErrorString(e));
+        }
     }
     KArgs a = args_for(p, static_cast<const uint8_t *>(dmem), stg);
     a.src_k = views.src_k;

@@ -154,6 +154,9 @@ RULES = [
     ("overlap", [seg([0], 0, 2, cow=[5]), seg([1], 0, 2, cow=[5])]),  # a target used twice
     ("overlap", [seg([0], 0, 2, cow=[1]), seg([1], 0, 2)]),         # a target another maps
     ("overlap", [seg([0], 0, 2, cow=[5]), seg([0], 2, 2)]),         # shared page turned in place
+    # every segment's own checks come before clashes between segments
+    ("range", [seg([0], 0, 2, cow=[5]), seg([1], 0, 2, cow=[5]), seg([9], 0, 1)]),
+    ("bad_arg", [seg([0], 0, 3), seg([0], 2, 2), seg([1, 2], 0, 1)]),
 ]
 
 
@@ -201,3 +204,55 @@ def test_library_refuses_bad_counts():
     assert library_status([], n_phys=0)[0] == B.PIC_ERR_INVALID_ARG
     assert library_status([seg([0], 0, 2)], layers=(1, 3))[0] == B.PIC_ERR_INVALID_ARG
     assert library_status([seg([0], 0, 2)], layers=(2, 1))[0] == B.PIC_ERR_INVALID_ARG
+
+
+def mutate(segs, rng, n_phys, ps):
+    """One random defect (or none) in a valid segment set."""
+    segs = list(segs)
+    g = int(rng.integers(0, len(segs)))
+    sg = segs[g]
+    kind = int(rng.integers(0, 8))
+    pages, cow = list(sg.pages), (list(sg.cow) if sg.cow is not None else None)
+    first, length, k, delta = sg.first, sg.length, sg.recompute_k, sg.delta
+    if kind == 0:
+        pages[int(rng.integers(0, len(pages)))] = int(rng.choice([n_phys, -1, n_phys + 3]))
+    elif kind == 1:
+        k = length + int(rng.integers(1, 3))
+    elif kind == 2:
+        first = ps + int(rng.integers(0, 3))
+    elif kind == 3:
+        pages = pages + [0]
+    elif kind == 4 and len(segs) > 1:  # map another segment's page
+        other = segs[(g + 1) % len(segs)]
+        pages[int(rng.integers(0, len(pages)))] = int(rng.choice(other.pages))
+    elif kind == 5 and cow is not None:  # a copy target onto a mapped page
+        cow[int(rng.integers(0, len(cow)))] = int(rng.choice(pages))
+    elif kind == 6 and len(segs) > 1 and segs[(g + 1) % len(segs)].cow is not None:
+        oc = [c for c in segs[(g + 1) % len(segs)].cow if c >= 0]
+        if oc:  # reuse another segment's copy target
+            cow = cow or [-1] * len(pages)
+            cow[int(rng.integers(0, len(cow)))] = int(rng.choice(oc))
+    segs[g] = PageSegment(tuple(pages), tuple(cow) if cow is not None else None, delta, first,
+                          length, k)
+    return segs
+
+
+def test_library_and_oracle_agree_on_mutated_sets():
+    """Valid random sets with one random defect each: wherever the oracle
+    refuses, the library gives the same status (valid sets are not sent:
+    the library would launch)."""
+    from position_independent_kv_stitch_amd import _binding as B
+    code = {"range": B.PIC_ERR_RANGE, "bad_arg": B.PIC_ERR_INVALID_ARG,
+            "overlap": B.PIC_ERR_OVERLAP}
+    rng = np.random.default_rng(2024)
+    refused = {k: 0 for k in code}
+    for seed in range(300):
+        wl, n_phys, segs = paged_cow_case(seed, page_size=4, max_len=12, n_chunks=3)
+        bad = mutate(segs, rng, n_phys, 4)
+        want = oracle.validate_rotate_paged(4, n_phys, bad)
+        if want == "ok":
+            continue
+        refused[want] += 1
+        st, msg = library_status(bad, page_size=4, n_phys=n_phys)
+        assert st == code[want], (seed, want, msg)
+    assert all(v > 5 for v in refused.values()), refused
