@@ -88,3 +88,65 @@ def test_zero_shift_copies_are_bit_exact(torch_cuda):
     segs = [PageSegment(s.pages, s.cow, 0, s.first, s.length, s.recompute_k) for s in segs]
     stats = run(torch_cuda, wl, n_phys, segs, 5)
     assert stats["bit_diffs"] == 0
+
+
+def test_config5_paged_cow_full(torch_cuda):
+    """The bench's paged workload at full size (36 layers, 64 x 2048 tokens
+    in 16-token pages, 16 chunks shared): one call over all layers and
+    segments, then
+    - on the whole buffer: every copy target holds its source's V bit for
+      bit, owned pages keep their V, shared source pages keep K and V, and
+      the first 16 tokens (page 0) of every segment keep their K bits;
+    - at layers 0 and 35, two shared and two owned segments against the
+      oracle run on just their pages."""
+    torch = torch_cuda
+    import position_independent_kv_stitch_amd as pic
+    from pic_workloads import config5_paged_cow
+    wl, n_phys, segs = config5_paged_cow()
+    say("config5 paged: generating inputs")
+    shape = (wl.n_layers, n_phys, wl.page_size, wl.n_heads, wl.row_dim)
+    k = normal_values(shape, wl.dtype, 0, "cuda:0")
+    v = normal_values(shape, wl.dtype, 1, "cuda:0")
+    k0, v0 = k.clone(), v.clone()
+    shared = [g for g, s in enumerate(segs) if s.cow is not None]
+    owned = [g for g, s in enumerate(segs) if s.cow is None]
+    pick = shared[:2] + owned[:2]
+    mini = sorted({p for g in pick for p in segs[g].pages}
+                  | {c for g in pick for c in (segs[g].cow or ())})
+    at = {p: i for i, p in enumerate(mini)}
+    idx = torch.tensor(mini, dtype=torch.long, device="cuda:0")
+    sample = [0, wl.n_layers - 1]
+    before = {L: (to_host(k[L:L + 1, idx]), to_host(v[L:L + 1, idx])) for L in sample}
+    say(f"config5 paged: one call, {len(segs)} segments, {len(shared)} shared")
+    pic.rotate_paged(k, v, segs, rope_dim=wl.rope_dim, theta=wl.theta, style=wl.style,
+                     rope_offset=wl.rope_offset)
+    torch.cuda.synchronize()
+
+    def pages(ids):
+        return torch.tensor(list(ids), dtype=torch.long, device="cuda:0")
+
+    def same(a, b):
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+    src = pages(p for g in shared for p in segs[g].pages)
+    dst = pages(c for g in shared for c in segs[g].cow)
+    own = pages(p for g in owned for p in segs[g].pages)
+    assert same(v[:, dst], v0[:, src]), "copy targets hold their sources' V"
+    assert same(v[:, own], v0[:, own]), "owned pages keep their V"
+    assert same(k[:, src], k0[:, src]) and same(v[:, src], v0[:, src]), "shared sources unchanged"
+    first = pages(segs[g].pages[0] for g in owned)
+    assert same(k[:, first], k0[:, first]), "recompute tokens of owned segments keep their K"
+    assert same(k[:, pages(segs[g].cow[0] for g in shared)],
+                k0[:, pages(segs[g].pages[0] for g in shared)]), "recompute tokens copied as they are"
+    del k0, v0
+    msegs = [PageSegment(tuple(at[p] for p in segs[g].pages),
+                         tuple(at[c] for c in segs[g].cow) if segs[g].cow else None,
+                         segs[g].delta, segs[g].first, segs[g].length, segs[g].recompute_k)
+             for g in pick]
+    for L in sample:
+        want_k, want_v = before[L][0].copy(), before[L][1].copy()
+        assert oracle.rotate_paged(wl, want_k, want_v, wl.page_size, msegs, 0, 1) == "ok"
+        stats = compare_k(to_host(k[L:L + 1, idx]), want_k, wl.rope_offset, wl.rope_dim,
+                          max_abs(before[L][0]), what=f"paged K layer {L}")
+        compare_bits(to_host(v[L:L + 1, idx]), want_v, f"paged V layer {L}")
+        say(f"  layer {L}: {stats}")
