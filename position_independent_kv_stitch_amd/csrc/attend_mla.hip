@@ -49,6 +49,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "acc_scale.hpp"
 #include "lds_load.hpp"
 #include "pic_internal.hpp"
 #include "rotate.hpp"
@@ -391,8 +392,16 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
             l_run = l_run * alpha + psum;
             m_run = m_new;
             if (__any(bump)) {
+                // one or two waves per workgroup: the accumulators live in
+                // AGPRs, and plain code paid their copies at every step
+                if constexpr (W <= 2) {
+                    acc_read_guard();
 #pragma unroll
-                for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
+                    for (int t = 0; t < kDTiles; t++) scale_acc(acc[t], alpha);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
+                }
             }
             // weights as B of O^T += V^T P^T: k index 8 g + j is position
             // 4 g + j (j < 4) or 16 + 4 g + j - 4 with two tiles, k index 4 g + j

@@ -92,6 +92,22 @@ def test_random_small(torch_cuda, seed):
     assert err <= tol
 
 
+@pytest.mark.parametrize("heads", [16, 32, 128])
+def test_running_max_moves_late(torch_cuda, heads):
+    """Scale 0.5 over 576-dim N(0, 1) rows puts the logits' spread at about
+    17 in log2 units, so a later position passes the running maximum by more
+    than the lazy slack (2^12) many times after the first step, and the
+    accumulators are rescaled while they hold partial sums (the rescale
+    differs between one- or two-wave workgroups, 16 and 32 heads, and
+    eight-wave ones)."""
+    wl = random_small(360 + heads, dtype="bf16", style="half", paged=True, mla=True,
+                      n_requests=2, n_layers=1, max_len=700)
+    say(f"latent late max heads={heads}")
+    err, tol, vmax = run_case(torch_cuda, wl, heads, 21, scale=0.5)
+    say(f"  max err {err:.3g} (bound {tol:.3g}, max|V| {vmax:.3g})")
+    assert err <= tol
+
+
 @pytest.mark.parametrize("layer,heads", [(0, 16), (60, 128)])
 def test_deepseek_v3_request_full(torch_cuda, layer, heads):
     """The DeepSeek-V3 MLA request (16 chunks x 4096 tokens at random offsets,
