@@ -472,46 +472,57 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
 }
 
 // out[r][j][d] = sum_b acc_b[d] e^{m_b - M} / sum_b l_b e^{m_b - M} over the
-// request's items, in order, 256 at a time; a thread owns two dims.
+// request's items b.  Wave w takes items b0 + w, b0 + w + 4, ...; lane i holds
+// dims 4 i .. 4 i + 3 and 256 + 4 i .. + 3, so each item's 2 KB row is one
+// coalesced read per wave, and four items per wave are in flight.  The waves'
+// sums meet in LDS; thread t writes dims t and t + 256.
 __global__ void __launch_bounds__(kCombineThreads) mla_combine_kernel(const MlaArgs a) {
-    __shared__ float s_f[kCombineThreads];
-    __shared__ float s_lf[kCombineThreads];
-    __shared__ float s_red[kCombineThreads / 64];
+    constexpr int kWaves = kCombineThreads / 64;
+    static_assert(kVDim == 2 * kCombineThreads && kCombineThreads % 64 == 0,
+                  "a lane holds two float4 of the value row");
+    __shared__ __attribute__((aligned(16))) float s_o[kWaves][kVDim];
+    __shared__ float s_red[kWaves];
+    __shared__ float s_l[kWaves];
     const int r = blockIdx.x;
     const int j = blockIdx.y;
-    const int d = threadIdx.x;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63;
     const int b0 = a.req_item0[r], b1 = a.req_item0[r + 1];
     const int64_t hq = a.num_q_heads;
     float M = -INFINITY;
-    for (int b = b0 + d; b < b1; b += kCombineThreads) M = fmaxf(M, a.part_ml[(b * hq + j) * 2]);
+    for (int b = b0 + t; b < b1; b += kCombineThreads) M = fmaxf(M, a.part_ml[(b * hq + j) * 2]);
     for (int x = 1; x < 64; x <<= 1) M = fmaxf(M, __shfl_xor(M, x, 64));
-    if ((d & 63) == 0) s_red[d >> 6] = M;
+    if (lane == 0) s_red[w] = M;
     __syncthreads();
     M = s_red[0];
 #pragma unroll
-    for (int w = 1; w < kCombineThreads / 64; w++) M = fmaxf(M, s_red[w]);
-    float L = 0.f, O0 = 0.f, O1 = 0.f;
-    for (int base = b0; base < b1; base += kCombineThreads) {
-        const int nb = min(kCombineThreads, b1 - base);
-        __syncthreads();
-        if (d < nb) {
-            const float *ml = a.part_ml + ((base + d) * hq + j) * 2;
-            const float f = __builtin_amdgcn_exp2f(ml[0] - M);  // log2 units
-            s_f[d] = f;
-            s_lf[d] = ml[1] * f;
-        }
-        __syncthreads();
-        for (int i = 0; i < nb; i++) L += s_lf[i];
-        const float *acc = a.part_acc + (base * hq + j) * kVDim + d;
+    for (int v = 1; v < kWaves; v++) M = fmaxf(M, s_red[v]);
+    float L = 0.f;
+    float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
 #pragma unroll 4
-        for (int i = 0; i < nb; i++) {
-            O0 += acc[i * hq * kVDim] * s_f[i];
-            O1 += acc[i * hq * kVDim + kCombineThreads] * s_f[i];
-        }
+    for (int b = b0 + w; b < b1; b += kWaves) {
+        const int64_t slot = static_cast<int64_t>(b) * hq + j;
+        const float2 ml = *reinterpret_cast<const float2 *>(a.part_ml + 2 * slot);
+        const float4 *row = reinterpret_cast<const float4 *>(a.part_acc + slot * kVDim);
+        const float4 x0 = row[lane], x1 = row[64 + lane];
+        const float f = __builtin_amdgcn_exp2f(ml.x - M);  // log2 units
+        L += ml.y * f;
+        o0.x += x0.x * f; o0.y += x0.y * f; o0.z += x0.z * f; o0.w += x0.w * f;
+        o1.x += x1.x * f; o1.y += x1.y * f; o1.z += x1.z * f; o1.w += x1.w * f;
+    }
+    *reinterpret_cast<float4 *>(&s_o[w][4 * lane]) = o0;
+    *reinterpret_cast<float4 *>(&s_o[w][256 + 4 * lane]) = o1;
+    if (lane == 0) s_l[w] = L;
+    __syncthreads();
+    float Lt = s_l[0], O0 = s_o[0][t], O1 = s_o[0][t + kCombineThreads];
+#pragma unroll
+    for (int v = 1; v < kWaves; v++) {
+        Lt += s_l[v];
+        O0 += s_o[v][t];
+        O1 += s_o[v][t + kCombineThreads];
     }
     float *o = a.out + r * a.o_req + j * a.o_head;
-    o[d] = O0 / L;
-    o[d + kCombineThreads] = O1 / L;
+    o[t] = O0 / Lt;
+    o[t + kCombineThreads] = O1 / Lt;
 }
 
 // ------------------------------------------------------------------ host
