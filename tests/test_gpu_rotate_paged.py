@@ -150,3 +150,32 @@ def test_config5_paged_cow_full(torch_cuda):
                           max_abs(before[L][0]), what=f"paged K layer {L}")
         compare_bits(to_host(v[L:L + 1, idx]), want_v, f"paged V layer {L}")
         say(f"  layer {L}: {stats}")
+
+
+def test_back_to_back_calls_reuse_staging(torch_cuda):
+    """Seven calls enqueued without waiting, on separate buffers, of
+    different sizes (each call stages two launches' metadata, so the staging
+    slots are reused several times while earlier calls are still queued):
+    every call must still see its own tiles and shift tables."""
+    torch = torch_cuda
+    import position_independent_kv_stitch_amd as pic
+    cases = []
+    for i, max_len in enumerate((40, 70, 300, 900, 2000, 120, 3000)):
+        wl, n_phys, segs = paged_cow_case(60 + i, dtype="bf16", n_layers=2, max_len=max_len,
+                                          n_chunks=3 + i % 3, delta_range=65536)
+        shape = (wl.n_layers, n_phys, wl.page_size, wl.n_heads, wl.row_dim)
+        k = normal_values(shape, wl.dtype, 70 + i, "cuda:0")
+        v = normal_values(shape, wl.dtype, 80 + i, "cuda:0")
+        cases.append((wl, segs, k, v, to_host(k), to_host(v)))
+    torch.cuda.synchronize()
+    for wl, segs, k, v, _, _ in cases:
+        pic.rotate_paged(k, v, segs, rope_dim=wl.rope_dim, theta=wl.theta, style=wl.style,
+                         rope_offset=wl.rope_offset)
+    torch.cuda.synchronize()
+    for i, (wl, segs, k, v, k0, v0) in enumerate(cases):
+        want_k, want_v = k0.copy(), v0.copy()
+        assert oracle.rotate_paged(wl, want_k, want_v, wl.page_size, segs) == "ok"
+        stats = compare_k(to_host(k), want_k, wl.rope_offset, wl.rope_dim, max_abs(k0),
+                          what=f"call {i}")
+        compare_bits(to_host(v), want_v, f"call {i} V")
+        say(f"  call {i}: {len(segs)} segments, {stats}")
