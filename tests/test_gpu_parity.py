@@ -390,3 +390,34 @@ def test_config3_full_in_layer_groups(torch_cuda):
         say(f"  requests {req_ids} layer {layer}: {stats}")
         del pk, pv, dk, dv
         torch.cuda.empty_cache()
+
+
+def test_inplace_back_to_back_calls(torch_cuda):
+    """Six pic_rotate_inplace calls enqueued without waiting, on separate
+    buffers with different segment sets (the per-call staging slots are
+    reused while earlier calls are still queued), each against the oracle."""
+    torch = torch_cuda
+    import position_independent_kv_stitch_amd as pic
+    from pic_workloads import Segment, Workload, normal_values
+    rng = np.random.default_rng(90)
+    cases = []
+    for i in range(6):
+        n_seg = 2 + 3 * i
+        lens = [int(x) for x in rng.integers(1, 400, size=n_seg)]
+        segs, at = [], 0
+        for n in lens:
+            segs.append(Segment(at, n, int(rng.integers(-65536, 65537)), int(rng.integers(0, min(n, 20) + 1))))
+            at += n + int(rng.integers(0, 5))
+        wl = Workload(f"in-place back to back {i}", "bf16", 2, 8, 128, 0, 128, "half", 1e6, False,
+                      inplace=True, n_tokens=at, segments=segs)
+        buf = normal_values(wl.buf_shape(), "bf16", 100 + i, "cuda:0")
+        cases.append((wl, buf, to_host(buf)))
+    torch.cuda.synchronize()
+    for wl, buf, _ in cases:
+        pic.rotate_workload(wl, buf)
+    torch.cuda.synchronize()
+    for i, (wl, buf, ref) in enumerate(cases):
+        want = ref.copy()
+        assert oracle.rotate_inplace(wl, want) == "ok"
+        stats = compare_k(to_host(buf), want, 0, 128, max_abs(ref), what=f"call {i}")
+        say(f"  call {i}: {len(wl.segments)} segments, {stats}")
