@@ -641,7 +641,9 @@ def rotate_paged(buf_k, buf_v, segments: Sequence, *, rope_dim: int, theta: floa
     of shape [L][P][page][H][D].  segments are objects with fields pages and
     cow (sequences of physical page ids, cow -1 for a page the caller owns,
     or cow None), delta, first, length and recompute_k, or tuples in that
-    order."""
+    order.  Page lists given as C-contiguous int32 numpy arrays are passed
+    without a copy; other integer sequences are converted, and ids outside
+    int32 are refused."""
     lib = load_library(library)
     L, P, S, H, D = buf_k.shape
     le = L if layer_end is None else layer_end
