@@ -256,3 +256,26 @@ def test_library_and_oracle_agree_on_mutated_sets():
         st, msg = library_status(bad, page_size=4, n_phys=n_phys)
         assert st == code[want], (seed, want, msg)
     assert all(v > 5 for v in refused.values()), refused
+
+
+def test_binding_page_lists():
+    """The binding's page-list conversion: int32 arrays pass without a copy,
+    other integer sequences are converted, ids outside int32 and non-integer
+    ids are refused, and an empty list still gets a non-NULL pointer."""
+    from position_independent_kv_stitch_amd._binding import _int32_array
+    a = np.arange(5, dtype=np.int32)
+    got, n = _int32_array(a)
+    assert n == 5 and got is a
+    got, n = _int32_array((3, 1, 2))
+    assert n == 3 and got.dtype == np.int32 and got.tolist() == [3, 1, 2]
+    got, n = _int32_array(np.array([7, 9], dtype=np.int64))
+    assert got.dtype == np.int32 and got.tolist() == [7, 9]
+    got, n = _int32_array([])
+    assert n == 0 and got.size == 1 and got.ctypes.data != 0
+    for bad in ([2 ** 31], [-2 ** 31 - 1]):
+        with pytest.raises(ValueError):
+            _int32_array(bad)
+    with pytest.raises(TypeError):
+        _int32_array([1.5, 2.0])
+    with pytest.raises(ValueError):
+        _int32_array([[1, 2]])
