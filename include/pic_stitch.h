@@ -310,7 +310,8 @@ typedef struct pic_page_segment {
  * be NULL when no segment copies a page or the shape has no V.
  * Errors, all before any launch: PIC_ERR_INVALID_ARG (NULL arrays, bad
  * counts, page_size < 1, n_pages not ceil((first + length) / page_size)),
- * PIC_ERR_RANGE (first, length, recompute_k or a page id out of range),
+ * PIC_ERR_RANGE (first, length, recompute_k or a page id out of range, or
+ * n_pages * page_size above 2^31 - 1: logical positions are int32),
  * PIC_ERR_OVERLAP (two segments turn the same slot of a page in place; a
  * copy target is used twice, or is also a page some segment reads or
  * turns; a page is copied by one segment and turned in place by another).

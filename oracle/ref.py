@@ -229,13 +229,16 @@ def rotate_inplace(wl, buf_k, layer_begin=0, layer_end=None, dtype=None, layer_b
 def validate_rotate_paged(page_size, n_phys_pages, segments) -> str:
     """The status pic_rotate_paged gives a set of paged segments, checked
     here from its stated rules (after the shape checks): first every
-    segment's counts (bad_arg) and positions and page ids (range), then the
-    clashes between segments (overlap)."""
+    segment's counts (bad_arg) and positions and page ids (range; the
+    logical positions its pages span must stay below 2^31), then the clashes
+    between segments (overlap)."""
     if page_size < 1 or n_phys_pages < 1:
         return "bad_arg"
     for sg in segments:
         if not (0 <= sg.first < page_size) or sg.length < 1:
             return "range"
+        if -(-(sg.first + sg.length) // page_size) * page_size > 2 ** 31 - 1:
+            return "range"  # the pages' logical positions must fit int32
         if not (0 <= sg.recompute_k <= sg.length):
             return "range"
         n_pages = -(-(sg.first + sg.length) // page_size)

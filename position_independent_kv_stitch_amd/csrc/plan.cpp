@@ -534,9 +534,13 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
         if (sg.first < 0 || sg.first >= page_size || sg.length < 1)
             return fail(PIC_ERR_RANGE, "segment %d: first %d, length %d (page_size %d)", g, sg.first,
                         sg.length, page_size);
+        const int64_t need = (int64_t{sg.first} + sg.length + page_size - 1) / page_size;
+        if (need * page_size > INT32_MAX)  // logical positions of the pages fit int32
+            return fail(PIC_ERR_RANGE, "segment %d: first %d + length %d spans %lld pages of %d, "
+                        "past 2^31 - 1 positions", g, sg.first, sg.length,
+                        static_cast<long long>(need), page_size);
         if (sg.recompute_k < 0 || sg.recompute_k > sg.length)
             return fail(PIC_ERR_RANGE, "segment %d: recompute_k %d", g, sg.recompute_k);
-        const int64_t need = (int64_t{sg.first} + sg.length + page_size - 1) / page_size;
         if (sg.n_pages != need)
             return fail(PIC_ERR_INVALID_ARG, "segment %d: n_pages %d, its tokens span %lld pages", g,
                         sg.n_pages, static_cast<long long>(need));

@@ -876,3 +876,62 @@ def test_boundary_attention_matches_library_sdpa_bf16():
             V.permute(1, 0, 2)[:, None].expand(H, G, L, D).contiguous(),
             attn_mask=mask, scale=0.09).reshape(H * G, D).numpy()
         assert np.allclose(got[b], want, rtol=0, atol=1e-12), b
+
+
+# ------------------------------------------------------- recompute ranges
+
+def test_recompute_ranges_irminsul_carveout(golden_dir):
+    """The MLA workload places its first chunk at absolute position 0, the
+    only chunk the carve-out applies to: exactly one range, its first 32
+    tokens (the page's figure), and none for the chunks placed after it."""
+    from pic_workloads import config4
+    g = json.load(open(os.path.join(golden_dir, "irminsul_carveout.json")))
+    wl = config4()
+    at_zero = [e for e in wl.requests[0].entries if e.dst_offset == g["applies_at_position"]]
+    assert len(at_zero) == 1
+    assert oracle.recompute_ranges(wl) == [(0, 0, g["recompute_tokens"])]
+
+
+def test_recompute_ranges_llama_paged_workload():
+    """The Llama-3-8B paged workload: 8 chunks of 2048 tokens behind a
+    128-token prefix, each with its first 32 tokens left for recompute, give
+    the eight ranges [128 + 2048 j, 160 + 2048 j)."""
+    from pic_workloads import config2
+    want = [(0, 128 + 2048 * j, 160 + 2048 * j) for j in range(8)]
+    assert oracle.recompute_ranges(config2()) == want
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_recompute_ranges_are_the_rows_the_stitch_leaves(seed):
+    """Brute force over every position of every request: after the oracle's
+    stitch onto a sentinel-filled destination, the positions inside an
+    entry whose K row still holds the sentinel form a prefix of that entry,
+    and those prefixes are exactly the ranges recompute_ranges lists (entry
+    by entry, empty ones omitted)."""
+    paged = seed % 2 == 1
+    wl = random_small(200 + seed, dtype="f32", paged=paged, mla=seed % 3 == 2, n_requests=3,
+                      n_layers=1)
+    wl.dtype = "f64"
+    rng = np.random.default_rng(seed)
+    pk = rng.standard_normal(wl.pool_shape())
+    pv = rng.standard_normal(wl.pool_shape()) if wl.has_v else None
+    dk = np.full(wl.dst_shape(), SENT_F64)
+    dv = np.full(wl.dst_shape(), SENT_F64) if wl.has_v else None
+    assert oracle.stitch(wl, pk, pv, dk, dv) == "ok"
+
+    def untouched(r, pos):
+        if paged:
+            row = dk[0, int(wl.requests[r].page_table[pos // wl.page_size]), pos % wl.page_size]
+        else:
+            row = dk[0, r, pos]
+        return bool(np.all(row == SENT_F64))
+
+    want = []
+    for r, req in enumerate(wl.requests):
+        for e in req.entries:
+            kept = [untouched(r, p) for p in range(e.dst_offset, e.dst_offset + e.length)]
+            n = kept.index(False) if False in kept else len(kept)
+            assert not any(kept[n:])  # the untouched positions are a prefix
+            if n:
+                want.append((r, e.dst_offset, e.dst_offset + n))
+    assert oracle.recompute_ranges(wl) == want

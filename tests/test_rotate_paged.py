@@ -147,6 +147,9 @@ RULES = [
     ("range", [seg([8], 0, 2)]),                                    # page id past the pool
     ("range", [seg([0], 0, 2, cow=[8])]),                           # copy target past the pool
     ("range", [seg([0], 0, 2, cow=[-2])]),
+    ("range", [seg([0], 0, 2 ** 31 - 3)]),                          # pages span 2^31 positions
+    ("range", [seg([0], 3, 2 ** 31 - 6)]),
+    ("bad_arg", [seg([0], 3, 2 ** 31 - 7)]),                        # span 2^31 - 4 fits int32
     ("bad_arg", [seg([0, 1], 0, 4)]),                               # n_pages != ceil(.)
     ("bad_arg", [seg([0], 2, 4)]),
     ("overlap", [seg([0], 0, 3), seg([0], 2, 2)]),                  # slot 2 turned twice
