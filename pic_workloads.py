@@ -520,3 +520,13 @@ def sentinel_like(shape, dtype: str, device="cpu"):
         return bits.view(torch.float32)
     bits = torch.full(shape, SENTINEL_BITS["bf16"], dtype=torch.int16, device=device)
     return bits.view(torch.bfloat16)
+
+
+def to_host(t) -> np.ndarray:
+    """A torch tensor's storage as numpy: float32 values, or bf16 as uint16
+    bit patterns (no arithmetic; the layout the oracle reads)."""
+    torch = _torch()
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -143,30 +143,39 @@ _lib = None
 _runtime_checked = False
 
 
-def _hip_runtimes():
-    """Distinct HIP runtime files mapped into this process."""
+def hip_runtimes(maps_lines=None, resolve=os.path.realpath):
+    """Distinct HIP runtime files in a /proc/<pid>/maps listing (by default
+    this process's own): the path column of every mapping of a
+    libamdhip64 file, with symlinks resolved."""
+    if maps_lines is None:
+        try:
+            with open("/proc/self/maps") as f:
+                maps_lines = f.readlines()
+        except OSError:
+            maps_lines = []
     paths = set()
-    try:
-        with open("/proc/self/maps") as f:
-            for line in f:
-                if "libamdhip64" in line:
-                    paths.add(os.path.realpath(line.split()[-1]))
-    except OSError:
-        pass
+    for line in maps_lines:
+        fields = line.split()
+        if len(fields) >= 6 and "libamdhip64" in fields[-1]:
+            paths.add(resolve(fields[-1]))
     return paths
 
 
-def _check_single_runtime():
+def check_single_runtime(maps_lines=None, resolve=os.path.realpath):
     """torch ships its own HIP runtime under the same soname as the system's.
     Tensors and streams handed to the library must belong to the runtime it
-    calls, so exactly one may be mapped."""
-    global _runtime_checked
-    if _runtime_checked:
-        return
-    paths = _hip_runtimes()
+    calls, so exactly one may be mapped; raise ImportError otherwise."""
+    paths = hip_runtimes(maps_lines, resolve)
     if len(paths) > 1:
         raise ImportError("two HIP runtimes are loaded (" + ", ".join(sorted(paths)) +
                           "): import torch before position_independent_kv_stitch_amd")
+
+
+def _check_single_runtime():
+    global _runtime_checked
+    if _runtime_checked:
+        return
+    check_single_runtime()
     _runtime_checked = True
 
 

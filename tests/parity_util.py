@@ -11,18 +11,12 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
+from pic_workloads import to_host  # noqa: F401  (re-exported for the tests)
 
 F32_TOL = 1e-5   # x max|k|, absolute
 BF16_ULPS = 1
 
 
-def to_host(t) -> np.ndarray:
-    """A torch tensor as the oracle's numpy storage (float32 or uint16 bits)."""
-    import torch
-    t = t.detach().contiguous().cpu()
-    if t.dtype == torch.bfloat16:
-        return t.view(torch.int16).numpy().view(np.uint16)
-    return t.numpy()
 
 
 def to_device(a: np.ndarray, device):

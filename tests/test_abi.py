@@ -145,3 +145,49 @@ def test_match_and_registry_errors_before_device_work():
     assert call(good, no=C.c_void_p(0x30004)) == B.PIC_ERR_ALIGN
     lib.pic_registry_destroy(reg)
     lib.pic_registry_destroy(None)
+
+
+# ------------------------------------------------- one HIP runtime per process
+
+def _maps_line(path, addr="7f0000000000-7f0000100000"):
+    return f"{addr} r-xp 00000000 08:01 1234 {path}\n"
+
+
+def test_runtime_guard_accepts_one_runtime():
+    """Several mappings of one runtime file (text, data, bss segments), plus
+    other libraries and anonymous mappings, pass."""
+    from position_independent_kv_stitch_amd import _binding as B
+    lines = [_maps_line("/opt/rocm/lib/libamdhip64.so.7.2.0"),
+             _maps_line("/opt/rocm/lib/libamdhip64.so.7.2.0", "7f0000100000-7f0000200000"),
+             _maps_line("/usr/lib/libc.so.6"),
+             "7ffd00000000-7ffd00021000 rw-p 00000000 00:00 0 [stack]\n",
+             "7f0000300000-7f0000400000 rw-p 00000000 00:00 0\n"]
+    B.check_single_runtime(lines, resolve=lambda p: p)
+    assert B.hip_runtimes(lines, resolve=lambda p: p) == {"/opt/rocm/lib/libamdhip64.so.7.2.0"}
+    B.check_single_runtime([], resolve=lambda p: p)  # no runtime mapped yet
+
+
+def test_runtime_guard_refuses_two_runtimes():
+    """torch's bundled runtime and ROCm's, both mapped: refused, naming both."""
+    from position_independent_kv_stitch_amd import _binding as B
+    torch_rt = "/usr/lib/python3/site-packages/torch/lib/libamdhip64.so"
+    rocm_rt = "/opt/rocm/lib/libamdhip64.so.7"
+    lines = [_maps_line(torch_rt), _maps_line(rocm_rt, "7f0000500000-7f0000600000")]
+    with pytest.raises(ImportError) as e:
+        B.check_single_runtime(lines, resolve=lambda p: p)
+    assert torch_rt in str(e.value) and rocm_rt in str(e.value)
+
+
+def test_runtime_guard_resolves_links_to_one_file():
+    """Two names of one file (a soname link and its target) are one runtime."""
+    from position_independent_kv_stitch_amd import _binding as B
+    real = "/opt/rocm/lib/libamdhip64.so.7.2.0"
+    links = {"/opt/rocm/lib/libamdhip64.so": real, real: real}
+    lines = [_maps_line("/opt/rocm/lib/libamdhip64.so"), _maps_line(real)]
+    B.check_single_runtime(lines, resolve=links.get)
+
+
+def test_runtime_guard_on_this_process():
+    """The package imported here (with torch) maps at most one runtime."""
+    from position_independent_kv_stitch_amd import _binding as B
+    assert len(B.hip_runtimes()) <= 1
