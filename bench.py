@@ -1,18 +1,22 @@
 #!/usr/bin/env python3
 """Throughput of position-independent KV stitching on one MI355X.
 
-One step = one pic_stitch over the whole Llama-3-8B-shaped workload: 32
-layers, 8 KV heads x 128 dims, bf16, one request of 8 chunks x 2048 tokens
-placed in a seeded random order behind a 128-token prefix into a paged cache
-of 16-token pages, the first 32 tokens of every chunk left for recompute.
-Inputs are synthetic (N(0, 1), seed 0) and resident in HBM before timing.
+One step = the whole batched-RAG stitch: 32 layers, 8 KV heads x 128 dims,
+bf16; a pool of 256 cached chunks of 128..4096 tokens; 64 requests, each
+placing 4..16 pool chunks (drawn with replacement, in random order) behind
+a prefix of 32..512 tokens into a paged cache of 16-token pages.  Every
+layer of every request is stitched inside the step.  The pool holds all 32
+layers; the destination holds as many layers as fit beside it in HBM, and
+each layer group of the step is one pic_stitch launch into it.  Inputs are
+synthetic (N(0, 1), seed 0) and resident in HBM before timing.
 
 The value is algorithmic stitched-KV bytes (rows read + rows written) per
 second; token-layers/s and the fraction of the 8 TB/s HBM peak are reported
 beside it, with the roofline of the stitch kernel (its average launch
-duration from HIP events on the launch stream), a device-to-device copy of
-the same byte count as the practical ceiling, and the fp64 CPU oracle timed
-on the host cores over four steps of the same workload.
+duration from HIP events on the launch stream), the library's own 16-byte
+streaming copy at the same read/write mix as the practical ceiling, the
+planner's time, and the fp64 CPU oracle timed on the host cores over a
+stated sample of the same workload.  --workload selects the other paths.
 
 Prints one JSON line on stdout.
 """
@@ -31,45 +35,64 @@ METRIC = "stitched-KV HBM GB/s (read+write) and token-layers/s; % of HBM peak"
 PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # 32-bit integer vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-KERNEL_SOURCES = [os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc", f)
-                  for f in ("stitch.hip", "rotate.hpp", "plan.cpp", "pic_internal.hpp")]
-COUNTERS = os.path.join(ROOT, "profiles", "stitch_kernel_llama3-8b-paged_counters.md")
+CSRC = os.path.join(ROOT, "position_independent_kv_stitch_amd", "csrc")
+# The sources that decide what each timed kernel reads and writes: a counter
+# summary counts only while their sha256 is the one it was taken with.
+STITCH_SOURCES = ("stitch.hip", "rotate.hpp", "plan.cpp", "pic_internal.hpp")
+KERNEL_SOURCES = {
+    "stitch": STITCH_SOURCES,
+    "gqa": ("attend_gqa.hip", "attend_plan.cpp", "attend_map.hpp", "lds_load.hpp", "acc_scale.hpp",
+            "attend.hip", "pic_internal.hpp"),
+    "mla": ("attend_mla.hip", "attend_plan.cpp", "attend_map.hpp", "lds_load.hpp", "acc_scale.hpp",
+            "rotate.hpp", "pic_internal.hpp"),
+    "bnd": ("attend_boundary.hip", "attend_plan.cpp", "attend_map.hpp", "lds_load.hpp",
+            "rotate.hpp", "pic_internal.hpp"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the sources that decide what the stitch kernel reads and writes."""
+def kernel_source_hash(kind: str = "stitch") -> str:
+    """sha256 over the sources that decide what a kernel reads and writes."""
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[kind]:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if there is none or the kernel source changed since it was taken."""
-    if not os.path.exists(COUNTERS):
+def counters_file(workload: str, kernel: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+
+
+def measured_traffic(workload: str, kernel: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload, or None if there is none or the kernel's sources changed
+    since it was taken."""
+    path = counters_file(workload, kernel)
+    if not os.path.exists(path):
         return None
-    text = open(COUNTERS).read()
+    text = open(path).read()
     h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     t = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not h or not t or h.group(1) != kernel_source_hash():
+    if not h or not t or h.group(1) != kernel_source_hash(kind):
         return None
     return int(t.group(1))
 
 
-DEFAULT = "llama3-8b-paged"
+DEFAULT = "batched-rag"
 WORKLOADS = {
-    DEFAULT: "32 layers, 8 kv heads x 128, bf16, one request of 8 chunks x 2048 tokens after a "
-             "128-token prefix, 16-token pages, recompute_k 32 (stitch, paged)",
+    DEFAULT: "batched RAG, all 32 layers: 64 requests of 4..16 chunks drawn with replacement from "
+             "a pool of 256 chunks of 128..4096 tokens behind prefixes of 32..512 tokens, "
+             "8 kv heads x 128, bf16, 16-token pages, recompute_k 0 (stitch, paged); the pool "
+             "holds all 32 layers, the destination the layers of one group, written by each "
+             "layer-group launch of the step",
+    "llama3-8b-paged": "32 layers, 8 kv heads x 128, bf16, one request of 8 chunks x 2048 tokens "
+                       "after a 128-token prefix, 16-token pages, recompute_k 32 (stitch, paged)",
     "llama3-8b-paged-pool": "the default workload with its chunks read from a paged pool of "
                             "16-token blocks in random order (stitch, paged to paged)",
-    "rag-group": "batched RAG, one group of 4 of the 32 layers: 64 requests of 4..16 chunks from "
-                 "a 256-chunk pool of 128..4096 tokens, bf16, 16-token pages (stitch, paged)",
     "mla": "DeepSeek-V3 MLA rows, 61 layers, 576-wide (512 copied + 64 rotated), bf16, 16 chunks "
            "x 4096 tokens (stitch, contiguous)",
     "inplace": "Qwen3-8B, 36 layers, 8 kv heads x 128, bf16, 131072 tokens, 64 segments rotated "
@@ -120,6 +143,8 @@ def setup_workload(name, torch, pic):
         return {"wl": wl, "step": lambda: pic.rotate_workload(wl, buf),
                 "bytes": tokens * per_tl * wl.n_layers, "token_layers": tokens * wl.n_layers,
                 "kernel": "stitch_kernel<bf16, half> (in place)", "plan": None,
+                "cpu": lambda: cpu_baseline_inplace(wl, buf), "counters": "stitch",
+                "tensors": [buf],
                 "config": {"workload": WORKLOADS[name], "storage": "bf16",
                            "layers": wl.n_layers, "tokens": wl.n_tokens, "segments": 64}}
     if name == "inplace-paged-cow":
@@ -141,7 +166,7 @@ def setup_workload(name, torch, pic):
                              rope_offset=wl.rope_offset)
         return {"wl": wl, "step": step, "bytes": nbytes, "token_layers": turned * wl.n_layers,
                 "kernel": "stitch_kernel<bf16, half> (page copies, then in-place turns)",
-                "plan": None,
+                "plan": None, "counters": "stitch", "tensors": [k, v],
                 "config": {"workload": WORKLOADS[name], "storage": "bf16", "layers": wl.n_layers,
                            "page_size": wl.page_size, "phys_pages": n_phys, "segments": len(segs),
                            "shared_segments": sum(1 for s in segs if s.cow is not None),
@@ -154,8 +179,9 @@ def setup_workload(name, torch, pic):
         return setup_boundary(name, torch, pic)
     if name.startswith("cdc-rag"):
         return setup_cdc(name, torch, pic)
-    wl = {DEFAULT: config2, "mla": config4, "single-layer": config1,
-          "rag-group": lambda: config3(n_layers=4),
+    if name == DEFAULT:
+        return setup_rag(name, torch, pic)
+    wl = {"llama3-8b-paged": config2, "mla": config4, "single-layer": config1,
           "llama3-8b-paged-pool": lambda: with_paged_pool(config2(), page_size=16, seed=1)}[name]()
     pk, pv = pool_values(wl, seed=0, device="cuda:0")
     dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
@@ -172,7 +198,56 @@ def setup_workload(name, torch, pic):
     kernel = f"stitch_kernel<{wl.dtype}, {wl.style}>"
     return {"wl": wl, "step": lambda: pic.stitch(plan, pk, pv, dk, dv), "bytes": step_bytes,
             "token_layers": info["tokens_written"] * wl.n_layers, "kernel": kernel,
-            "plan": plan, "info": info, "pk": pk, "pv": pv, "config": cfg}
+            "plan": plan, "info": info, "pk": pk, "pv": pv, "config": cfg,
+            "cpu": lambda: cpu_baseline_stitch(wl, pk, pv, info), "counters": "stitch",
+            "tensors": [pk, pv, dk, dv]}
+
+
+def setup_rag(name, torch, pic):
+    """The batched-RAG stitch over all 32 layers: the pool holds every layer,
+    the destination as many layers (a divisor of 32) as fit beside it; a
+    step is one pic_stitch per layer group, each reading its own pool
+    layers and writing the destination's layers."""
+    from pic_workloads import config3, pool_values, sentinel_like
+    wl = config3()
+    row = wl.n_heads * wl.row_dim * wl.esize
+    pool_bytes = 2 * wl.n_layers * wl.pool_tokens * row
+    dst_layer = 2 * wl.n_phys_pages * wl.page_size * row
+    free, total = torch.cuda.mem_get_info()
+    margin = 6 << 30  # value generation, plan metadata, the runtime
+    group = next(g for g in (32, 16, 8, 4, 2, 1)
+                 if wl.n_layers % g == 0 and pool_bytes + g * dst_layer + margin <= free)
+    log(f"workload {name}: {free / 2**30:.1f} of {total / 2**30:.1f} GiB free; pool "
+        f"{pool_bytes / 2**30:.1f} GiB, destination {group} layers x {dst_layer / 2**30:.2f} GiB")
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
+    dk = sentinel_like((group,) + tuple(wl.dst_shape()[1:]), wl.dtype, "cuda:0")
+    dv = sentinel_like((group,) + tuple(wl.dst_shape()[1:]), wl.dtype, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    info = plan.info
+    groups = [(pk[g:g + group], pv[g:g + group]) for g in range(0, wl.n_layers, group)]
+
+    def step():
+        for gk, gv in groups:
+            pic.stitch(plan, gk, gv, dk, dv, 0, group)
+
+    step_bytes = (info["bytes_read_per_layer"] + info["bytes_written_per_layer"]) * wl.n_layers
+    cfg = {"workload": WORKLOADS[name], "storage": wl.dtype, "layers": wl.n_layers,
+           "kv_heads": wl.n_heads, "row_dim": wl.row_dim, "rope_dim": wl.rope_dim,
+           "rope_theta": wl.theta, "page_size": wl.page_size, "requests": len(wl.requests),
+           "pool_chunks": len(wl.chunks), "pool_tokens": wl.pool_tokens,
+           "entries": info["n_entries"], "stitched_tokens": info["tokens_written"],
+           "masked_tokens": info["tokens_masked"], "dst_phys_pages": wl.n_phys_pages,
+           "layers_per_launch": group, "launches_per_step": wl.n_layers // group,
+           "hbm_gib": {"total": round(total / 2**30, 1), "free_before": round(free / 2**30, 1),
+                       "pool": round(pool_bytes / 2**30, 1),
+                       "destination": round(group * dst_layer / 2**30, 1)},
+           "parallelism": "single-gpu"}
+    return {"wl": wl, "step": step, "bytes": step_bytes,
+            "token_layers": info["tokens_written"] * wl.n_layers,
+            "launches": wl.n_layers // group,
+            "kernel": f"stitch_kernel<{wl.dtype}, {wl.style}>", "plan": plan, "info": info,
+            "config": cfg, "cpu": lambda: cpu_baseline_rag(wl, pk, pv), "counters": "stitch",
+            "tensors": [pk, pv, dk, dv]}
 
 
 def setup_attend(name, torch, pic):
@@ -213,7 +288,7 @@ def setup_attend(name, torch, pic):
     return {"wl": wl, "step": run(plan), "plain_step": run(plain),
             "bytes": info["context_tokens"] * 2 * row * L,
             "token_layers": info["context_tokens"] * L, "launches": L,
-            "kernel": "attend_block_kernel<bf16, half> + attend_combine_kernel (one pic_attend)",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "gqa_tile_kernel + gqa_combine_kernel (one pic_attend)",
             "plan": plan, "plans": [plain], "info": info, "config": cfg}
 
 
@@ -245,7 +320,7 @@ def setup_attend_mla(name, torch, pic):
            "parallelism": "single-gpu"}
     return {"wl": wl, "step": step, "bytes": info["context_tokens"] * row * L,
             "token_layers": info["context_tokens"] * L, "launches": L, "flops": flops,
-            "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)",
             "plan": plan, "info": info, "config": cfg}
 
 
@@ -290,7 +365,7 @@ def setup_boundary(name, torch, pic):
            "sink_tokens": 4, "sink_bias": -15.0, "parallelism": "single-gpu"}
     return {"wl": wl, "step": step, "bytes": (ctx * row_bytes + qo_bytes) * L, "token_layers": n * L,
             "launches": L, "flops": flops,
-            "kernel": "bnd_block_kernel<half> + bnd_combine_kernel (one pic_attend_boundary)",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "bnd_block_kernel<half> + bnd_combine_kernel (one pic_attend_boundary)",
             "plan": plan, "config": cfg}
 
 
@@ -339,7 +414,7 @@ def setup_cdc(name, torch, pic):
            "fingerprint": kind, "window": 128, "threshold": "2^56",
            "parallelism": "single-gpu"}
     return {"wl": None, "step": step, "bytes": 4 * n, "token_layers": n,
-            "kernel": "pic_match (8 kernels: Gear flags, scans, ends, chunk hashes, emit)",
+            "arithmetic": "64-bit integer hashing", "kernel": "pic_match (8 kernels: Gear flags, scans, ends, chunk hashes, emit)",
             "plan": None, "registry": reg, "config": cfg, "alu_ops": alu_ops}
 
 
@@ -356,65 +431,173 @@ def time_steps(torch, step, steps):
     return s.elapsed_time(e) / steps
 
 
-def cpu_baseline(wl, pk, pv, plan_info):
-    """The oracle, as it is, over four full steps of the workload: one call
-    per layer on a pool of host threads."""
+def host_cpu():
+    """What the host offers the oracle: logical CPUs, this process's CPU
+    share (affinity) and the CPU model."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    share = len(os.sched_getaffinity(0))
+    # one GPU's share of the host: at most 16 worker threads whatever nproc shows
+    return {"nproc": os.cpu_count(), "affinity": share, "threads": min(16, share),
+            "model": model}
+
+
+def _timed_pool(fn, units, threads):
+    """Run fn over units on `threads` host threads (the oracle's C calls
+    release the GIL); returns (wall s, process CPU s)."""
     from concurrent.futures import ThreadPoolExecutor
+    c0, t0 = time.process_time(), time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        list(ex.map(fn, units))
+    return time.perf_counter() - t0, time.process_time() - c0
 
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+def _baseline(host, unit_bytes, unit_tl, all_units, one_units, fn, what):
+    """The oracle over `all_units` on the host's threads and over `one_units`
+    on one thread, as GB/s of algorithmic bytes and token-layers/s."""
+    wall, cpu_s = _timed_pool(fn, all_units, host["threads"])
+    wall1, _ = _timed_pool(fn, one_units, 1)
+    nb, nt = sum(unit_bytes(u) for u in all_units), sum(unit_tl(u) for u in all_units)
+    nb1, nt1 = sum(unit_bytes(u) for u in one_units), sum(unit_tl(u) for u in one_units)
+    return {"value": round(nb / wall / 1e9, 4), "unit": "GB/s", "cores": host["threads"],
+            "kind": "oracle",
+            "sample": f"{what}: {len(all_units)} units on {host['threads']} threads in "
+                      f"{wall:.2f} s wall ({cpu_s:.1f} s CPU); one thread: {len(one_units)} "
+                      f"units in {wall1:.2f} s",
+            "token_layers_per_s": round(nt / wall, 1),
+            "one_core": {"value": round(nb1 / wall1 / 1e9, 4), "unit": "GB/s",
+                         "token_layers_per_s": round(nt1 / wall1, 1)},
+            "process_cpu_s": round(cpu_s, 1),
+            "host": {"nproc": host["nproc"], "affinity_cpus": host["affinity"],
+                     "cpu_model": host["model"]}}
+
+
+def cpu_baseline_stitch(wl, pk, pv, plan_info, passes=4):
+    """The oracle, as it is, over `passes` full steps of a stitch workload:
+    one oracle call per layer (a unit) on the host threads; one thread runs
+    one step."""
     import oracle
-    from parity_util import to_host
-    from pic_workloads import sentinel_like
+    from pic_workloads import sentinel_like, to_host
 
-    cores = min(16, len(os.sched_getaffinity(0)))
-    log(f"cpu baseline: copying pool to host, {cores} threads")
-    hk, hv = to_host(pk), to_host(pv)
+    host = host_cpu()
+    log(f"cpu baseline: copying pool to host, {host['threads']} threads")
+    hk = to_host(pk)
+    hv = to_host(pv) if pv is not None else None
     sent = to_host(sentinel_like((1,) + tuple(wl.dst_shape()[1:]), wl.dtype, "cpu"))
 
     def one(layer):
-        dk, dv = sent.copy(), sent.copy()
-        st = oracle.stitch(wl, hk[layer:layer + 1], hv[layer:layer + 1], dk, dv, layer,
-                           layer + 1, layer_base=layer)
+        dk = sent.copy()
+        dv = sent.copy() if hv is not None else None
+        st = oracle.stitch(wl, hk[layer:layer + 1], hv[layer:layer + 1] if hv is not None else None,
+                           dk, dv, layer, layer + 1, layer_base=layer)
         assert st == "ok"
 
-    passes = 4  # about 20 s of CPU work on a 16-thread host
-    c0 = time.process_time()
-    t0 = time.perf_counter()
-    with ThreadPoolExecutor(max_workers=cores) as ex:
-        list(ex.map(one, [layer for _ in range(passes) for layer in range(wl.n_layers)]))
-    dt = time.perf_counter() - t0
-    cpu_s = time.process_time() - c0
-    step_bytes = (plan_info["bytes_read_per_layer"] + plan_info["bytes_written_per_layer"]) * \
-        wl.n_layers
-    return {"value": round(passes * step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{passes} full steps of the same workload ({wl.n_layers} layers x "
-                      f"{plan_info['tokens_written']} stitched tokens each), one fp64 oracle "
-                      f"call per layer on {cores} threads, {dt:.2f} s wall",
-            "process_cpu_s": round(cpu_s, 1),
-            "token_layers_per_s": round(passes * plan_info["tokens_written"] * wl.n_layers / dt,
-                                        1)}
+    per_layer = plan_info["bytes_read_per_layer"] + plan_info["bytes_written_per_layer"]
+    layers = list(range(wl.n_layers))
+    return _baseline(host, lambda u: per_layer, lambda u: plan_info["tokens_written"],
+                     layers * passes, layers, one,
+                     f"{passes} full steps ({wl.n_layers} layers x "
+                     f"{plan_info['tokens_written']} stitched tokens), one oracle call per layer")
 
 
-def copy_ceiling(torch, nbytes, reps=20):
-    """A device-to-device copy moving the same read+write bytes."""
-    n = nbytes // 2
+def cpu_baseline_rag(wl, pk, pv, layers=(0,), one_requests=8):
+    """The oracle on a sample of the batched-RAG step: every request of
+    `layers` (each (layer, request) a one-request problem over that layer's
+    whole pool, its pages renumbered), on the host threads; one thread runs
+    `one_requests` requests of the first layer."""
+    import numpy as np
+
+    import oracle
+    from pic_workloads import SENTINEL_BITS, Request, Workload, to_host
+
+    host = host_cpu()
+    log(f"cpu baseline: copying layers {list(layers)} of the pool to host, "
+        f"{host['threads']} threads")
+    hk = {layer: to_host(pk[layer:layer + 1]) for layer in layers}
+    hv = {layer: to_host(pv[layer:layer + 1]) for layer in layers}
+    row = wl.n_heads * wl.row_dim * wl.esize
+    subs = []
+    for rq in wl.requests:
+        n = len(rq.page_table)
+        subs.append(Workload(wl.name, wl.dtype, wl.n_layers, wl.n_heads, wl.row_dim,
+                             wl.rope_offset, wl.rope_dim, wl.style, wl.theta, wl.has_v,
+                             pool_tokens=wl.pool_tokens, chunks=wl.chunks,
+                             requests=[Request(rq.entries, np.arange(n, dtype=np.int32))],
+                             page_size=wl.page_size, n_phys_pages=n))
+    tokens = [sum(e.length - e.recompute_k for e in rq.entries) for rq in wl.requests]
+
+    def one(unit):
+        layer, r = unit
+        sub = subs[r]
+        shape = (1,) + tuple(sub.dst_shape()[1:])
+        dk = np.full(shape, SENTINEL_BITS[wl.dtype], dtype=np.uint16 if wl.dtype == "bf16"
+                     else np.uint32)
+        if wl.dtype == "f32":
+            dk = dk.view(np.float32)
+        dv = dk.copy()
+        assert oracle.stitch(sub, hk[layer], hv[layer], dk, dv, layer, layer + 1,
+                             layer_base=layer) == "ok"
+
+    units = [(layer, r) for layer in layers for r in range(len(wl.requests))]
+    return _baseline(host, lambda u: tokens[u[1]] * 2 * 2 * row, lambda u: tokens[u[1]],
+                     units, units[:one_requests], one,
+                     f"layers {list(layers)} of the step, all {len(wl.requests)} requests "
+                     f"(one unit = one request at one layer)")
+
+
+def cpu_baseline_inplace(wl, buf, n_layers=8):
+    """The oracle's in-place rotation over the first n_layers layers of the
+    in-place workload: one call per layer on the host threads; one thread
+    runs 2 layers."""
+    import oracle
+    from pic_workloads import to_host
+
+    host = host_cpu()
+    log(f"cpu baseline: copying the buffer to host, {host['threads']} threads")
+    hb = to_host(buf[:n_layers])
+    rot = [sg for sg in wl.segments if sg.delta != 0]
+    tokens = sum(sg.length - sg.recompute_k for sg in rot)
+    per_layer = tokens * wl.n_heads * wl.rope_dim * wl.esize * 2
+
+    def one(layer):
+        part = hb[layer:layer + 1].copy()
+        assert oracle.rotate_inplace(wl, part, layer, layer + 1, layer_base=layer) == "ok"
+
+    layers = list(range(n_layers))
+    return _baseline(host, lambda u: per_layer, lambda u: tokens, layers, layers[:2], one,
+                     f"{n_layers} of the step's {wl.n_layers} layers ({tokens} turned tokens "
+                     f"each), one oracle call per layer")
+
+
+def copy_ceiling(torch, pic, nbytes, reps=20):
+    """The library's 16-byte streaming copy (pic_stream_copy) moving the same
+    read+write bytes: half read, half written, as in the stitch."""
+    n = (nbytes // 2) // 16 * 16
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
     src.fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        pic.stream_copy(dst, src)
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s.record()
     for _ in range(reps):
-        dst.copy_(src)
+        pic.stream_copy(dst, src)
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / reps
+    assert torch.equal(dst[:4096], src[:4096])
     del src, dst
     return {"value": round(2 * n / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
-            "kind": "torch copy_ (device to device)", "bytes_moved": 2 * n}
+            "kind": "pic_stream_copy (16-byte non-temporal loads and stores, 1:1 read/write)",
+            "bytes_moved": 2 * n}
 
 
 def main():
@@ -442,7 +625,6 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     W = setup_workload(args.workload, torch, pic)
-    wl = W["wl"]
     step = W["step"]
     step_bytes, step_tl = W["bytes"], W["token_layers"]
 
@@ -482,7 +664,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64",
+        "dtype": W["config"].get("storage", "int32"),  # cdc workloads: int32 token ids
+        "arithmetic": W.get("arithmetic", "f64 rotation, one rounding to the storage type"),
         "data": "synthetic",
         "config": W["config"],
         "token_layers_per_s": round(step_tl * args.steps / (total_ms * 1e-3), 1),
@@ -490,7 +673,9 @@ def main():
         "bytes_per_step": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
-                     "traffic": measured_traffic() if args.workload == DEFAULT else None,
+                     "traffic": measured_traffic(args.workload, W["kernel"].split("<")[0].split()[0],
+                                                 W.get("counters", "")) if W.get("counters")
+                     else None,
                      "kernel": W["kernel"],
                      "avg_launch_ms": round(avg_kernel_ms, 5),
                      "median_launch_ms": round(kernel_ms[len(kernel_ms) // 2], 5),
@@ -521,15 +706,20 @@ def main():
             "value": round(step_bytes / (plain_ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "what": "the same contexts with no placed chunks (every row from the cache, "
                     "no rotation): the cost of attention alone"}
-    if not args.no_copy_ceiling:
-        out["copy_ceiling"] = copy_ceiling(torch, min(step_bytes, 8 << 30))
-    if not args.no_cpu_baseline and args.workload == DEFAULT:
-        out["cpu_baseline"] = cpu_baseline(wl, W["pk"], W["pv"], W["info"])
-    else:
-        out["cpu_baseline"] = None
+    if W.get("plan") is not None:
+        out["planner_ms"] = round(W["plan"].plan_seconds * 1e3, 3)
+    out["cpu_baseline"] = None
+    if not args.no_cpu_baseline and "cpu" in W:
+        out["cpu_baseline"] = W["cpu"]()
     for p in [W.get("plan")] + W.get("plans", []):
         if p is not None:
             p.destroy()
+    step = None
+    W.clear()  # the workload's tensors go before the copy ceiling allocates its own
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_copy_ceiling:
+        out["copy_ceiling"] = copy_ceiling(torch, pic, min(step_bytes // launches, 8 << 30))
     print(json.dumps(out), flush=True)
 
 

@@ -562,6 +562,18 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
                      int64_t n_tokens, pic_match_t *out, int64_t max_out, int64_t *n_out,
                      void *stream);
 
+/*
+ * pic_stream_copy -- the measurement reference of the library, not a step
+ * of the method: copy nbytes from src to dst (device memory, 16-byte
+ * aligned, nbytes a multiple of 16, else PIC_ERR_ALIGN; overlapping buffers
+ * PIC_ERR_OVERLAP; NULL pointers PIC_ERR_INVALID_ARG; nbytes < 0
+ * PIC_ERR_RANGE) with the 16-byte non-temporal loads and stores the stitch
+ * kernel uses, every byte read once and written once.  Its rate is the
+ * practical HBM ceiling of a 1:1 read/write stream, against which the
+ * stitch's rate is read.  Enqueued on `stream`; nothing is allocated.
+ */
+pic_status pic_stream_copy(void *dst, const void *src, int64_t nbytes, void *stream);
+
 /* Thread-local message for the last failed call on this thread ("" if none). */
 const char *pic_last_error(void);
 

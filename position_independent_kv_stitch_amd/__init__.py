@@ -11,6 +11,6 @@ been built.
 from ._binding import (EXPORTS, LIBRARY, PicError, Plan, Registry, attend,  # noqa: F401
                        attend_boundary, attend_latent, boundary_row_count,
                        load_library, match, match_records, rotate_inplace, rotate_paged,
-                       rotate_workload, stitch)
+                       rotate_workload, stitch, stream_copy)
 
 load_library()

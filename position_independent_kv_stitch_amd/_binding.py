@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import time
 from typing import Optional, Sequence
 
 import numpy as np
@@ -30,7 +31,7 @@ EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_rotate_paged", "
            "pic_attend_latent",
            "pic_attend_boundary", "pic_plan_info",
            "pic_plan_ranges", "pic_plan_destroy", "pic_registry_create", "pic_registry_add",
-           "pic_registry_destroy", "pic_match", "pic_last_error")
+           "pic_registry_destroy", "pic_match", "pic_stream_copy", "pic_last_error")
 FP_KINDS = {"xxh64": 0, "sha256": 1}
 
 
@@ -218,6 +219,8 @@ def _configure(lib):
     lib.pic_match.restype = C.c_int
     lib.pic_match.argtypes = [C.c_void_p, P(CdcConfig), C.c_void_p, C.c_int64, C.c_void_p,
                               C.c_int64, C.c_void_p, C.c_void_p]
+    lib.pic_stream_copy.restype = C.c_int
+    lib.pic_stream_copy.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_void_p]
     lib.pic_last_error.restype = C.c_char_p
     lib.pic_last_error.argtypes = []
     return lib
@@ -322,8 +325,11 @@ class Plan:
             rarr[r] = RequestC(earr, pt_ptr, len(entries), n_pages,
                                int(getattr(rq, "context_len", 0) or 0))
         geom = Geom(page_size, src_page_size, capacity, n_phys_pages, src_n_pages)
-        _check(lib.pic_plan(C.byref(shape), C.byref(rope), carr, len(chunks), rarr,
-                            len(requests), C.byref(geom), C.byref(self._handle)), lib)
+        t0 = time.perf_counter()
+        st = lib.pic_plan(C.byref(shape), C.byref(rope), carr, len(chunks), rarr, len(requests),
+                          C.byref(geom), C.byref(self._handle))
+        self.plan_seconds = time.perf_counter() - t0  # the C call alone, no marshalling
+        _check(st, lib)
         self.info = self._info()
 
     @classmethod
@@ -625,6 +631,20 @@ def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
     _check(lib.pic_rotate_inplace(C.byref(shape), C.byref(rope), C.byref(view), T, sarr,
                                   len(segments), layer_begin, le, _stream_of(buf_k, stream)),
            lib)
+
+
+def stream_copy(dst, src, stream=None, library=None):
+    """Enqueue pic_stream_copy of src's bytes into dst (two contiguous device
+    tensors of equal byte size): the library's 1:1 read/write bandwidth
+    reference."""
+    if not (dst.is_contiguous() and src.is_contiguous()):
+        raise ValueError("stream_copy needs contiguous tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src differ in size")
+    lib = load_library(library)
+    _check(lib.pic_stream_copy(C.c_void_p(dst.data_ptr()), C.c_void_p(src.data_ptr()), nbytes,
+                               _stream_of(src, stream)), lib)
 
 
 def _int32_array(ids):

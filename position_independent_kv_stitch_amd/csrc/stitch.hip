@@ -282,6 +282,32 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
     }
 }
 
+// The bandwidth reference of the library: a plain copy with the stitch's
+// 16-byte non-temporal loads and stores, one read and one write per byte.
+// Each thread moves kCopyUnroll words per pass, all loads of a pass issued
+// before its stores; passes stride over the whole buffer.
+constexpr int kCopyThreads = 512;
+constexpr int kCopyUnroll = 4;
+
+__global__ void __launch_bounds__(kCopyThreads)
+    stream_copy_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst, int64_t n) {
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kCopyThreads;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x; base < n;
+         base += stride * kCopyUnroll) {
+        u32x4 w[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; u++) {
+            const int64_t i = base + u * stride;
+            if (i < n) w[u] = __builtin_nontemporal_load(src + i);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; u++) {
+            const int64_t i = base + u * stride;
+            if (i < n) __builtin_nontemporal_store(w[u], dst + i);
+        }
+    }
+}
+
 // ----------------------------------------------------------------- launch
 
 // The kernel keeps a step's slot offsets in 32 bits: g token rows and all
@@ -644,6 +670,29 @@ pic_status pic_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *ro
     st = run_staged(copy, v, layer_begin, layer_end - layer_begin, stream, "copy-on-write");
     if (st) return st;
     return run_staged(turn, v, layer_begin, layer_end - layer_begin, stream, "paged rotate");
+}
+
+pic_status pic_stream_copy(void *dst, const void *src, int64_t nbytes, void *stream_) {
+    using namespace pic;
+    clear_error();
+    if (nbytes < 0) return fail(PIC_ERR_RANGE, "nbytes %lld < 0", static_cast<long long>(nbytes));
+    if (nbytes == 0) return PIC_OK;
+    if (!dst || !src) return fail(PIC_ERR_INVALID_ARG, "dst and src must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src) |
+         static_cast<uintptr_t>(nbytes)) & 15u)
+        return fail(PIC_ERR_ALIGN, "dst, src and nbytes must be multiples of 16 bytes");
+    const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), s0 = reinterpret_cast<uintptr_t>(src);
+    if (d0 < s0 + static_cast<uintptr_t>(nbytes) && s0 < d0 + static_cast<uintptr_t>(nbytes))
+        return fail(PIC_ERR_OVERLAP, "dst and src overlap");
+    const int64_t n = nbytes / 16;
+    const int64_t per_block = int64_t{kCopyThreads} * kCopyUnroll;
+    const int64_t blocks = std::min<int64_t>(16384, (n + per_block - 1) / per_block);
+    hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kCopyThreads),
+                       0, static_cast<hipStream_t>(stream_), static_cast<const u32x4 *>(src),
+                       static_cast<u32x4 *>(dst), n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "copy kernel launch");
+    return PIC_OK;
 }
 
 void pic_plan_destroy(pic_plan_t *plan) {

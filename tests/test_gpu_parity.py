@@ -357,39 +357,52 @@ def _subproblem(wl, req_ids):
 
 
 def test_config3_full_in_layer_groups(torch_cuda):
-    """Batched RAG: 64 requests over a 256-chunk pool, 32 layers run as 8
-    groups of 4 layers (one launch per group covers every request); sampled
-    requests of one layer per group compared with the oracle."""
+    """Batched RAG: 64 requests over a 256-chunk pool, all 32 layers.  As the
+    benchmark runs it, the pool holds every layer and each launch stitches
+    one layer group (8 layers here) of all requests into a destination
+    holding that group.  Every group: on every layer, unwritten rows keep
+    the sentinel, no row is written twice and every written V row is its
+    pool row; 4 sampled requests on 2 layers are compared with the oracle."""
     torch = torch_cuda
     import position_independent_kv_stitch_amd as pic
-    full = config3()
-    group = 4
-    wl = full.with_layers(group)
+    wl = config3()
+    group = 8
+    gw = wl.with_layers(group)
+    say("config3: generating the 32-layer pool")
+    pk, pv = pool_values(wl, seed=0, device="cuda:0")
     plan = pic.Plan.from_workload(wl)
     rng = np.random.default_rng(0)
-    for g in range(full.n_layers // group):
-        say(f"config3: layer group {g}")
-        pk, pv = pool_values(wl, seed=100 + g, device="cuda:0")
-        dk = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
-        dv = sentinel_like(wl.dst_shape(), wl.dtype, "cuda:0")
-        pic.stitch(plan, pk, pv, dk, dv)
+    dk = sentinel_like(gw.dst_shape(), wl.dtype, "cuda:0")
+    dv = sentinel_like(gw.dst_shape(), wl.dtype, "cuda:0")
+    for g in range(wl.n_layers // group):
+        lo = g * group
+        say(f"config3: layer group {g} (layers {lo}..{lo + group - 1})")
+        if g:
+            sent = sentinel_like((1,), wl.dtype, "cuda:0")
+            dk.copy_(sent.expand_as(dk))
+            dv.copy_(sent.expand_as(dv))
+        gk, gv = pk[lo:lo + group], pv[lo:lo + group]
+        pic.stitch(plan, gk, gv, dk, dv, 0, group)
         torch.cuda.synchronize()
-        layer = int(rng.integers(0, group))
-        req_ids = sorted(rng.choice(len(wl.requests), size=3, replace=False).tolist())
-        sub, src_tok, pages = _subproblem(wl, req_ids)
-        st = torch.from_numpy(src_tok).to("cuda:0")
-        pg = torch.from_numpy(pages.astype(np.int64)).to("cuda:0")
-        hk = to_host(pk[layer:layer + 1].index_select(1, st))
-        hv = to_host(pv[layer:layer + 1].index_select(1, st))
-        rk = to_host(sentinel_like((1,) + tuple(sub.dst_shape()[1:]), wl.dtype, "cpu"))
-        rv = rk.copy()
-        assert oracle.stitch(sub, hk, hv, rk, rv, layer, layer + 1, layer_base=layer) == "ok"
-        stats = compare_k(to_host(dk[layer:layer + 1].index_select(1, pg)), rk, 0, 128,
-                          max_abs(hk), what=f"K group {g} layer {layer}")
-        compare_bits(to_host(dv[layer:layer + 1].index_select(1, pg)), rv, f"V group {g}")
-        say(f"  requests {req_ids} layer {layer}: {stats}")
-        del pk, pv, dk, dv
-        torch.cuda.empty_cache()
+        _all_layer_properties(torch, gw, gk, gv, dk, dv)
+        for layer in sorted(rng.choice(group, size=2, replace=False).tolist()):
+            req_ids = sorted(rng.choice(len(wl.requests), size=4, replace=False).tolist())
+            sub, src_tok, pages = _subproblem(gw, req_ids)
+            st = torch.from_numpy(src_tok).to("cuda:0")
+            pg = torch.from_numpy(pages.astype(np.int64)).to("cuda:0")
+            hk = to_host(gk[layer:layer + 1].index_select(1, st))
+            hv = to_host(gv[layer:layer + 1].index_select(1, st))
+            rk = to_host(sentinel_like((1,) + tuple(sub.dst_shape()[1:]), wl.dtype, "cpu"))
+            rv = rk.copy()
+            assert oracle.stitch(sub, hk, hv, rk, rv, layer, layer + 1, layer_base=layer) == "ok"
+            stats = compare_k(to_host(dk[layer:layer + 1].index_select(1, pg)), rk, 0, 128,
+                              max_abs(hk), what=f"K layer {lo + layer}")
+            compare_bits(to_host(dv[layer:layer + 1].index_select(1, pg)), rv,
+                         f"V layer {lo + layer}")
+            say(f"  layer {lo + layer}, requests {req_ids}: {stats}")
+    plan.destroy()
+    del pk, pv, dk, dv
+    torch.cuda.empty_cache()
 
 
 def test_inplace_back_to_back_calls(torch_cuda):
