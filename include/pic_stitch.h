@@ -212,7 +212,8 @@ typedef struct pic_plan pic_plan_t;
  * delta*theta_i are computed in fp64 on the host; tokens [recompute_k,
  * length) are cut into work tiles.  Host only: no HIP call is made, so the
  * plan can be built without a GPU.  All input arrays are copied; the
- * caller may free them on return.
+ * caller may free them on return.  The attention map (pic_attend*) is not
+ * built here but by the first call that needs it.
  *
  * Valid input (else PIC_ERR_RANGE unless noted):
  *   0 <= chunk_id < n_chunks; 1 <= length <= chunk.length;
@@ -362,10 +363,13 @@ typedef struct pic_attend_args {
  * page it covers must be in [0, dst_num_pages) (PIC_ERR_RANGE).  In-place
  * plans are refused (PIC_ERR_STATE).
  *
- * The first call allocates the plan's partial-result workspace on the
- * device (freed with the plan; a call with more query heads grows it after
- * waiting for the device).  Calls on one plan share that workspace: calls
- * that may overlap (different streams) race; order them on one stream.
+ * Each call takes its partial-result workspace in stream-ordered device
+ * memory (hipMallocAsync / hipFreeAsync on `stream`), so calls on one plan
+ * from several streams may overlap.  The plan's attention map is built on
+ * the host by the first call that needs it, and its device metadata for a
+ * launch shape is uploaded once, ordered on the stream of the call that
+ * first needs it; calls on other streams wait for that upload on their own
+ * stream.  Nothing waits for the device.
  */
 pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
                       const pic_attend_args *args, void *stream);
@@ -405,10 +409,8 @@ typedef struct pic_attend_latent_args {
  * a plan at one layer (see above).  The plan must be a bf16 MLA plan of the
  * shape above (PIC_ERR_INVALID_ARG); q rows 16-byte aligned
  * (PIC_ERR_ALIGN); contexts and pages as for pic_attend (PIC_ERR_RANGE);
- * in-place plans are refused (PIC_ERR_STATE).  The partial-result
- * workspace is the plan's, shared with pic_attend (allocated or grown on
- * first use, freed with the plan): calls on one plan that may overlap race;
- * order them on one stream.
+ * in-place plans are refused (PIC_ERR_STATE).  Workspace and metadata as
+ * for pic_attend: calls on one plan from several streams may overlap.
  */
 pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
                              const pic_attend_latent_args *args, void *stream);
@@ -451,15 +453,16 @@ typedef struct pic_attend_boundary_args {
  * (PIC_ERR_RANGE; also for more than 65535 requests with relocated entries
  * or a launch beyond 2^31 threads); in-place plans refused
  * (PIC_ERR_STATE).  A plan without relocated entries enqueues nothing.  The
- * work items for a launch shape are built on the host and uploaded with the
- * plan on first use (a later call with another boundary_k waits for the
- * device and rebuilds them); the partial-result workspace is the plan's,
- * shared with pic_attend: calls on one plan that may overlap race.
+ * work items for a launch shape (boundary_k and the device's CU count) are
+ * built on the host and uploaded once per plan; workspace and metadata as
+ * for pic_attend: calls on one plan from several streams may overlap.
  */
 pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
                                const pic_attend_boundary_args *args, void *stream);
 
-/* pic_plan_info -- sizes and algorithmic byte counts of a plan. */
+/* pic_plan_info -- sizes and algorithmic byte counts of a plan.  Host only.
+ * The attention counts (attend_blocks, attend_block_tokens) need the plan's
+ * attention map: the first call builds it if no attention call has. */
 pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info);
 
 /*
@@ -472,8 +475,9 @@ pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info);
  */
 pic_status pic_plan_ranges(const pic_plan_t *plan, int64_t *boundaries, int64_t *recompute);
 
-/* pic_plan_destroy -- wait for the device to finish, release the plan.
- * NULL is a no-op. */
+/* pic_plan_destroy -- wait for the work enqueued with the plan (its last
+ * use on every stream it ran on, and its uploads; not the whole device),
+ * then release it and its device memory.  NULL is a no-op. */
 void pic_plan_destroy(pic_plan_t *plan);
 
 /* ------------------------------------------------------------------------
@@ -525,17 +529,19 @@ pic_status pic_registry_create(int32_t fingerprint, pic_registry_t **out);
 
 /* pic_registry_add -- register a segment (host call; fp is 32 host bytes).
  * length >= 1, chunk_id >= 0 (PIC_ERR_RANGE); an entry with the same
- * fingerprint and length is refused (PIC_ERR_OVERLAP).  The registry's
- * device table is rebuilt at the next pic_match: that call first waits for
- * the whole device (earlier pic_match calls on any stream may still read the
- * old table), then uploads the new table ordered on its stream.  A registry
- * is bound to the device of its first pic_match (PIC_ERR_STATE after).
+ * fingerprint and length is refused (PIC_ERR_OVERLAP).  The next pic_match
+ * uploads a new version of the registry's device table, ordered on its
+ * stream; earlier pic_match calls on any stream keep reading the version
+ * they were given, which is freed once they have run (no call waits for the
+ * device).  A registry is bound to the device of its first pic_match
+ * (PIC_ERR_STATE after).
  * Adding while a pic_match runs on another host thread is serialised by the
  * registry's lock. */
 pic_status pic_registry_add(pic_registry_t *reg, const uint8_t *fp, int32_t length,
                             int32_t chunk_id);
 
-/* pic_registry_destroy -- wait for the device, release. NULL is a no-op. */
+/* pic_registry_destroy -- wait for the pic_match calls that read the
+ * registry's tables, release it.  NULL is a no-op. */
 void pic_registry_destroy(pic_registry_t *reg);
 
 /*
@@ -552,8 +558,7 @@ void pic_registry_destroy(pic_registry_t *reg);
  * (PIC_ERR_INVALID_ARG); tokens 4-byte, out and n_out 8-byte aligned
  * (PIC_ERR_ALIGN).  The registry's fingerprint kind must equal
  * cfg->fingerprint (PIC_ERR_INVALID_ARG).
- * Work is enqueued on `stream` and the call does not wait for it (except
- * to replace a changed registry's table, see pic_registry_add): counts
+ * Work is enqueued on `stream` and the call does not wait for it: counts
  * stay on the device.  Temporary device memory of about 8 bytes per token
  * plus 36 bytes per kept record (min(n_tokens, max_out)) is allocated and
  * freed on `stream` (stream-ordered).

@@ -330,7 +330,13 @@ class Plan:
                           C.byref(geom), C.byref(self._handle))
         self.plan_seconds = time.perf_counter() - t0  # the C call alone, no marshalling
         _check(st, lib)
-        self.info = self._info()
+        self._info_cache = None
+        # what the launch wrappers check tensors against, without asking the
+        # library for the full info (whose attention counts build the map)
+        self.n_entries = sum(len(_get(rq, "entries", 0)) for rq in requests)
+        self.pool_tokens_required = (src_n_pages * src_page_size if src_page_size else
+                                     max((int(_get(c, "token_start", 0)) + int(_get(c, "length", 1))
+                                          for c in chunks), default=0))
 
     @classmethod
     def from_workload(cls, wl, library=None) -> "Plan":
@@ -342,14 +348,19 @@ class Plan:
                    src_page_size=getattr(wl, "src_page_size", 0),
                    src_n_pages=getattr(wl, "src_n_pages", 0))
 
-    def _info(self) -> dict:
-        info = PlanInfo()
-        _check(self._lib.pic_plan_info(self._handle, C.byref(info)), self._lib)
-        return info.as_dict()
+    @property
+    def info(self) -> dict:
+        """pic_plan_info as a dict (its first call on a plan builds the
+        attention map, which the attention calls would build anyway)."""
+        if self._info_cache is None:
+            info = PlanInfo()
+            _check(self._lib.pic_plan_info(self.handle, C.byref(info)), self._lib)
+            self._info_cache = info.as_dict()
+        return self._info_cache
 
     def ranges(self):
         """(boundaries, recompute) as int64 arrays of [request, begin, end] rows."""
-        n = self.info["n_entries"]
+        n = self.n_entries
         b = np.zeros((max(n, 1), 3), dtype=np.int64)
         r = np.zeros((max(n, 1), 3), dtype=np.int64)
         _check(self._lib.pic_plan_ranges(self._handle, b.ctypes.data_as(C.POINTER(C.c_int64)),
@@ -445,9 +456,9 @@ def stitch(plan: Plan, pool_k, pool_v, dst_k, dst_v, layer_begin: int = 0,
         if pool_k.dim() != 5 or pool_k.shape[1] < plan.src_n_pages or \
                 pool_k.shape[2] != plan.src_page_size:
             raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
-    elif pool_k.shape[1] < plan.info["pool_tokens_required"]:
+    elif pool_k.shape[1] < plan.pool_tokens_required:
         raise PicError(PIC_ERR_RANGE, f"pool holds {pool_k.shape[1]} tokens, plan needs "
-                       f"{plan.info['pool_tokens_required']}")
+                       f"{plan.pool_tokens_required}")
     if tuple(pool_k.shape[-2:]) != (plan.n_heads, plan.row_dim) or \
             tuple(dst_k.shape[3:]) != (plan.n_heads, plan.row_dim):
         raise ValueError("head/row shape does not match the plan")
@@ -492,7 +503,7 @@ def attend(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: int, out=N
             raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
         pv = _view(pool_k, pool_v, "paged-pool")
     else:
-        if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+        if pool_k.shape[1] < plan.pool_tokens_required:
             raise PicError(PIC_ERR_RANGE, "pool tensor smaller than the plan needs")
         pv = _view(pool_k, pool_v, "pool")
     if plan.page_size:
@@ -539,7 +550,7 @@ def attend_latent(plan: Plan, pool_k, cache_k, q, *, layer: int, out=None,
             raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
         pv = _view(pool_k, None, "paged-pool")
     else:
-        if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+        if pool_k.shape[1] < plan.pool_tokens_required:
             raise PicError(PIC_ERR_RANGE, "pool tensor smaller than the plan needs")
         pv = _view(pool_k, None, "pool")
     if plan.page_size:
@@ -590,7 +601,7 @@ def attend_boundary(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: i
             raise PicError(PIC_ERR_RANGE, "paged pool tensor smaller than the plan's pages")
         pv = _view(pool_k, pool_v, "paged-pool")
     else:
-        if pool_k.shape[1] < plan.info["pool_tokens_required"]:
+        if pool_k.shape[1] < plan.pool_tokens_required:
             raise PicError(PIC_ERR_RANGE, "pool tensor smaller than the plan needs")
         pv = _view(pool_k, pool_v, "pool")
     if plan.page_size:

@@ -30,6 +30,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstring>
+
 #include <algorithm>
 #include <cstdint>
 
@@ -531,6 +533,8 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     if (!args || !args->q || !args->out)
         return fail(PIC_ERR_INVALID_ARG, "attend arguments, q and out must not be NULL");
     if (p.mode == kInPlace) return fail(PIC_ERR_STATE, "in-place plans have no attention map");
+    pic_status st0 = ensure_attention(plan);
+    if (st0) return st0;
     if (!p.shape.has_v) return fail(PIC_ERR_INVALID_ARG, "pic_attend needs K and V rows (has_v)");
     const int H = p.shape.num_heads, D = p.shape.row_dim;
     if (args->num_q_heads < H || args->num_q_heads % H != 0 || args->num_q_heads / H > 8)
@@ -570,31 +574,31 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     if (st) return st;
     // bf16 128-dim rows: the matrix-core path (attend_gqa.hip)
     if (gqa_tile_path(p, args->num_q_heads / H)) return attend_gqa(plan, pool, cache, args, stream);
+    // the map's work blocks, uploaded once per plan
+    const DevBlob *blob = nullptr;
+    st = plan_blob(plan, blob_key(kBlobAttnMap, 0), stream_, [&](DevBlob &b) {
+        auto put = [&](const void *src, size_t n) {
+            const size_t at = (b.host.size() + 255) & ~size_t{255};
+            b.host.resize(at + n);
+            if (n) std::memcpy(b.host.data() + at, src, n);
+            return at;
+        };
+        b.off[0] = put(p.atiles.data(), p.atiles.size() * sizeof(AttnTile));
+        b.off[1] = put(p.ablocks.data(), p.ablocks.size() * sizeof(AttnBlock));
+        b.off[2] = put(p.req_block0.data(), p.req_block0.size() * sizeof(int32_t));
+    }, &blob);
+    if (st) return st;
     const size_t need = p.ablocks.size() * static_cast<size_t>(args->num_q_heads) *
                         (static_cast<size_t>(D) + 2) * sizeof(float);
-    {
-        std::lock_guard<std::mutex> lock(plan->mu);
-        if (plan->work_bytes < need) {
-            if (plan->d_work) {
-                hipError_t e = hipDeviceSynchronize();  // earlier calls may use it
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-                (void)hipFree(plan->d_work);
-                plan->d_work = nullptr;
-                plan->work_bytes = 0;
-            }
-            hipError_t e = hipMalloc(&plan->d_work, need);
-            if (e != hipSuccess) {
-                plan->d_work = nullptr;
-                return hip_fail(e, "hipMalloc (attention workspace)");
-            }
-            plan->work_bytes = need;
-        }
-    }
+    void *work = nullptr;
+    st = call_workspace(need, stream_, &work);
+    if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
+    const uint8_t *bm = static_cast<const uint8_t *>(blob->dev);
     AttnArgs a{};
-    a.tiles = reinterpret_cast<const AttnTile *>(dm + plan->staged.off_atiles);
-    a.blocks = reinterpret_cast<const AttnBlock *>(dm + plan->staged.off_ablocks);
-    a.req_block0 = reinterpret_cast<const int32_t *>(dm + plan->staged.off_rblock);
+    a.tiles = reinterpret_cast<const AttnTile *>(bm + blob->off[0]);
+    a.blocks = reinterpret_cast<const AttnBlock *>(bm + blob->off[1]);
+    a.req_block0 = reinterpret_cast<const int32_t *>(bm + blob->off[2]);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = pool->k;
     a.pool_v = pool->v;
@@ -616,8 +620,8 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     a.o_req = args->out_request_stride;
     a.o_head = args->out_head_stride;
     const size_t acc_elems = p.ablocks.size() * static_cast<size_t>(args->num_q_heads) * D;
-    a.part_acc = static_cast<float *>(plan->d_work);
-    a.part_ml = static_cast<float *>(plan->d_work) + acc_elems;
+    a.part_acc = static_cast<float *>(work);
+    a.part_ml = static_cast<float *>(work) + acc_elems;
     a.n_kv_heads = H;
     a.group = args->num_q_heads / H;
     a.row_dim = D;
@@ -638,6 +642,11 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     else
         e = p.style == PIC_ROPE_HALF ? launch_attend<uint16_t, PIC_ROPE_HALF>(a, nb, nr, args->layer, stream)
                                      : launch_attend<uint16_t, PIC_ROPE_INTERLEAVED>(a, nb, nr, args->layer, stream);
-    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    return PIC_OK;
+    if (e != hipSuccess) {
+        (void)release_workspace(work, stream_);
+        return hip_fail(e, "attention kernel launch");
+    }
+    st = release_workspace(work, stream_);
+    if (st) return st;
+    return note_use(plan, stream_);
 }

@@ -838,6 +838,10 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     clear_error();
     if (!plan || plan->magic != kPlanMagic) return fail(PIC_ERR_STATE, "invalid or destroyed plan");
     const Problem &p = plan->prob;
+    {
+        const pic_status st0 = ensure_attention(plan);
+        if (st0) return st0;
+    }
     if (!args || !args->q || !args->out)
         return fail(PIC_ERR_INVALID_ARG, "attend arguments, q and out must not be NULL");
     if (p.mode == kInPlace) return fail(PIC_ERR_STATE, "in-place plans have no attention map");
@@ -891,83 +895,47 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     const int64_t target = std::max<int64_t>(1, 2 * static_cast<int64_t>(cu_count()) / H);
     const int64_t key = (target << 32) | static_cast<uint32_t>(args->boundary_k);
     int TT = 1, n_sets = 1, row_slots = 0;
-    {
-        std::lock_guard<std::mutex> lock(plan->mu);
-        hipError_t e;
-        if (plan->bnd_key != key) {
-            BndMap m = build_bnd_map(p, order, args->boundary_k, target);
-            if (plan->d_bnd) {
-                e = hipDeviceSynchronize();  // earlier launches may read the old items
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            }
-            if (m.bytes.size() > plan->bnd_bytes) {
-                if (plan->d_bnd) (void)hipFree(plan->d_bnd);
-                plan->d_bnd = nullptr;
-                plan->bnd_bytes = 0;
-                e = hipMalloc(&plan->d_bnd, m.bytes.size());
-                if (e != hipSuccess) {
-                    plan->d_bnd = nullptr;
-                    return hip_fail(e, "hipMalloc (boundary work items)");
-                }
-                plan->bnd_bytes = m.bytes.size();
-            }
-            plan->bnd_host = std::move(m.bytes);
-            e = hipMemcpyAsync(plan->d_bnd, plan->bnd_host.data(), plan->bnd_host.size(),
-                               hipMemcpyHostToDevice, stream);
-            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (boundary work items)");
-            e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), stream);
-            if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-            plan->bnd_off[0] = m.off_blocks;
-            plan->bnd_off[1] = m.off_bpos;
-            plan->bnd_off[2] = m.off_items;
-            plan->bnd_off[3] = m.off_reqs;
-            plan->bnd_off[4] = m.off_limit;
-            plan->bnd_off[5] = m.off_tabs;
-            plan->bnd_n_items = m.n_items;
-            plan->bnd_n_reqs = m.n_reqs;
-            plan->bnd_max_rows = m.max_req_rows;
-            plan->bnd_key = key;
-        }
-        // rows of a request's KV head: tokens x G, in as few sets of 8 waves
-        // x TT tiles as the registers allow, TT as small as they then permit
-        const int64_t rows = static_cast<int64_t>(plan->bnd_max_rows) * G;
-        const int64_t max_set = int64_t{kWaves} * kMaxTT * 16;
-        n_sets = static_cast<int>((rows + max_set - 1) / max_set);
-        TT = static_cast<int>((rows + int64_t{n_sets} * kWaves * 16 - 1) / (int64_t{n_sets} * kWaves * 16));
-        row_slots = n_sets * kWaves * TT * 16;
-        if ((static_cast<int64_t>(plan->bnd_n_items) * H + 7) / 8 * 8 * n_sets >=
-                (int64_t{1} << 31) / (64 * kWaves) ||
-            static_cast<int64_t>(plan->bnd_n_reqs) * rows * H >= (int64_t{1} << 31) / 64 ||
-            plan->bnd_n_reqs > 65535)
-            return fail(PIC_ERR_RANGE, "boundary rows x context too large for one launch");
-        const size_t need = static_cast<size_t>(plan->bnd_n_items) * H * row_slots *
-                            (static_cast<size_t>(kDim) + 2) * sizeof(float);
-        if (plan->work_bytes < need) {
-            if (plan->d_work) {
-                e = hipDeviceSynchronize();
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-                (void)hipFree(plan->d_work);
-                plan->d_work = nullptr;
-                plan->work_bytes = 0;
-            }
-            e = hipMalloc(&plan->d_work, need);
-            if (e != hipSuccess) {
-                plan->d_work = nullptr;
-                return hip_fail(e, "hipMalloc (attention workspace)");
-            }
-            plan->work_bytes = need;
-        }
-    }
+    const DevBlob *blob = nullptr;
+    st = plan_blob(plan, blob_key(kBlobBoundary, key), stream_, [&](DevBlob &b) {
+        BndMap m = build_bnd_map(p, order, args->boundary_k, target);
+        b.host = std::move(m.bytes);
+        b.off[0] = m.off_blocks;
+        b.off[1] = m.off_bpos;
+        b.off[2] = m.off_items;
+        b.off[3] = m.off_reqs;
+        b.off[4] = m.off_limit;
+        b.off[5] = m.off_tabs;
+        b.n[0] = m.n_items;
+        b.n[1] = m.n_reqs;
+        b.n[2] = m.max_req_rows;
+    }, &blob);
+    if (st) return st;
+    const int32_t n_items = blob->n[0], n_reqs = blob->n[1], max_rows = blob->n[2];
+    // rows of a request's KV head: tokens x G, in as few sets of 8 waves x TT
+    // tiles as the registers allow, TT as small as they then permit
+    const int64_t rows = static_cast<int64_t>(max_rows) * G;
+    const int64_t max_set = int64_t{kWaves} * kMaxTT * 16;
+    n_sets = static_cast<int>((rows + max_set - 1) / max_set);
+    TT = static_cast<int>((rows + int64_t{n_sets} * kWaves * 16 - 1) / (int64_t{n_sets} * kWaves * 16));
+    row_slots = n_sets * kWaves * TT * 16;
+    if ((static_cast<int64_t>(n_items) * H + 7) / 8 * 8 * n_sets >= (int64_t{1} << 31) / (64 * kWaves) ||
+        static_cast<int64_t>(n_reqs) * rows * H >= (int64_t{1} << 31) / 64 || n_reqs > 65535)
+        return fail(PIC_ERR_RANGE, "boundary rows x context too large for one launch");
+    const size_t need = static_cast<size_t>(n_items) * H * row_slots *
+                        (static_cast<size_t>(kDim) + 2) * sizeof(float);
+    void *work = nullptr;
+    st = call_workspace(need, stream_, &work);
+    if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
-    const uint8_t *bm = static_cast<const uint8_t *>(plan->d_bnd);
+    const uint8_t *bm = static_cast<const uint8_t *>(blob->dev);
     BndArgs a{};
     a.tiles = reinterpret_cast<const AttnTile *>(bm);
-    a.blocks = reinterpret_cast<const AttnBlock *>(bm + plan->bnd_off[0]);
-    a.block_pos = reinterpret_cast<const int32_t *>(bm + plan->bnd_off[1]);
-    a.items = reinterpret_cast<const BndItem *>(bm + plan->bnd_off[2]);
-    a.reqs = reinterpret_cast<const BndReq *>(bm + plan->bnd_off[3]);
-    a.limit = reinterpret_cast<const int32_t *>(bm + plan->bnd_off[4]);
-    a.block_tabs = reinterpret_cast<const int32_t *>(bm + plan->bnd_off[5]);
+    a.blocks = reinterpret_cast<const AttnBlock *>(bm + blob->off[0]);
+    a.block_pos = reinterpret_cast<const int32_t *>(bm + blob->off[1]);
+    a.items = reinterpret_cast<const BndItem *>(bm + blob->off[2]);
+    a.reqs = reinterpret_cast<const BndReq *>(bm + blob->off[3]);
+    a.limit = reinterpret_cast<const int32_t *>(bm + blob->off[4]);
+    a.block_tabs = reinterpret_cast<const int32_t *>(bm + blob->off[5]);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = static_cast<const uint16_t *>(pool->k);
     a.pool_v = static_cast<const uint16_t *>(pool->v);
@@ -988,11 +956,10 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     a.out = args->out;
     a.o_row = args->out_row_stride;
     a.o_head = args->out_head_stride;
-    const size_t acc_elems =
-        static_cast<size_t>(plan->bnd_n_items) * H * row_slots * static_cast<size_t>(kDim);
-    a.part_acc = static_cast<float *>(plan->d_work);
-    a.part_ml = static_cast<float *>(plan->d_work) + acc_elems;
-    a.n_items = plan->bnd_n_items;
+    const size_t acc_elems = static_cast<size_t>(n_items) * H * row_slots * static_cast<size_t>(kDim);
+    a.part_acc = static_cast<float *>(work);
+    a.part_ml = static_cast<float *>(work) + acc_elems;
+    a.n_items = n_items;
     a.n_kv_heads = H;
     a.group = G;
     a.num_q_heads = args->num_q_heads;
@@ -1019,15 +986,19 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
         PIC_BND_LAUNCH(2)
 #undef PIC_BND_LAUNCH
         default:
+            (void)release_workspace(work, stream_);
             return fail(PIC_ERR_INVALID_ARG, "internal: row tiles per wave %d", TT);
     }
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(bnd_combine_kernel,
+                           dim3(static_cast<unsigned>(max_rows * G), static_cast<unsigned>(n_reqs),
+                                static_cast<unsigned>(H)),
+                           dim3(64), 0, stream, a);
+        e = hipGetLastError();
+    }
+    st = release_workspace(work, stream_);
     if (e != hipSuccess) return hip_fail(e, "boundary attention kernel launch");
-    hipLaunchKernelGGL(bnd_combine_kernel,
-                       dim3(static_cast<unsigned>(plan->bnd_max_rows * G),
-                            static_cast<unsigned>(plan->bnd_n_reqs), static_cast<unsigned>(H)),
-                       dim3(64), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "boundary attention combine launch");
-    return PIC_OK;
+    if (st) return st;
+    return note_use(plan, stream_);
 }

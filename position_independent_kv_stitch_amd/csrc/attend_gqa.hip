@@ -615,66 +615,31 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
     const int H = p.shape.num_heads;
     const int64_t slots = static_cast<int64_t>(cu_count()) * kWavesPerCu;
     const int64_t target = std::max<int64_t>(1, 2 * slots / H);  // about two rounds
-    {
-        std::lock_guard<std::mutex> lock(plan->mu);
-        hipError_t e;
-        if (plan->gqa_key != target) {
-            ItemMap m = build_item_map(p, target, kMaxItems);
-            if (plan->d_gqa) {
-                e = hipDeviceSynchronize();  // earlier launches may read the old items
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            }
-            if (m.bytes.size() > plan->gqa_bytes) {
-                if (plan->d_gqa) (void)hipFree(plan->d_gqa);
-                plan->d_gqa = nullptr;
-                plan->gqa_bytes = 0;
-                e = hipMalloc(&plan->d_gqa, m.bytes.size());
-                if (e != hipSuccess) {
-                    plan->d_gqa = nullptr;
-                    return hip_fail(e, "hipMalloc (attention work items)");
-                }
-                plan->gqa_bytes = m.bytes.size();
-            }
-            plan->gqa_host = std::move(m.bytes);
-            e = hipMemcpyAsync(plan->d_gqa, plan->gqa_host.data(), plan->gqa_host.size(),
-                               hipMemcpyHostToDevice, stream);
-            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (attention work items)");
-            e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), stream);
-            if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-            plan->gqa_off[0] = m.off_blocks;
-            plan->gqa_off[1] = m.off_items;
-            plan->gqa_off[2] = m.off_reqs;
-            plan->gqa_off[3] = m.off_tabs;
-            plan->gqa_n_items = m.n_items;
-            plan->gqa_key = target;
-        }
-        const size_t need = static_cast<size_t>(plan->gqa_n_items) *
-                            static_cast<size_t>(args->num_q_heads) *
-                            (static_cast<size_t>(kDim) + 2) * sizeof(float);
-        if (plan->work_bytes < need) {
-            if (plan->d_work) {
-                e = hipDeviceSynchronize();  // earlier calls may use it
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-                (void)hipFree(plan->d_work);
-                plan->d_work = nullptr;
-                plan->work_bytes = 0;
-            }
-            e = hipMalloc(&plan->d_work, need);
-            if (e != hipSuccess) {
-                plan->d_work = nullptr;
-                return hip_fail(e, "hipMalloc (attention workspace)");
-            }
-            plan->work_bytes = need;
-        }
-    }
+    const DevBlob *blob = nullptr;
+    pic_status st = plan_blob(plan, blob_key(kBlobGqa, target), stream, [&](DevBlob &b) {
+        ItemMap m = build_item_map(p, target, kMaxItems);
+        b.host = std::move(m.bytes);
+        b.off[0] = m.off_blocks;
+        b.off[1] = m.off_items;
+        b.off[2] = m.off_reqs;
+        b.off[3] = m.off_tabs;
+        b.n[0] = m.n_items;
+    }, &blob);
+    if (st) return st;
+    const int32_t n_items = blob->n[0];
+    const size_t need = static_cast<size_t>(n_items) * static_cast<size_t>(args->num_q_heads) *
+                        (static_cast<size_t>(kDim) + 2) * sizeof(float);
+    void *work = nullptr;
+    st = call_workspace(need, stream, &work);
+    if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
-    const uint8_t *gm = static_cast<const uint8_t *>(plan->d_gqa);
+    const uint8_t *gm = static_cast<const uint8_t *>(blob->dev);
     GqaArgs a{};
     a.tiles = reinterpret_cast<const AttnTile *>(gm);
-    a.blocks = reinterpret_cast<const AttnBlock *>(gm + plan->gqa_off[0]);
-    a.item_block0 = reinterpret_cast<const int32_t *>(gm + plan->gqa_off[1]);
-    a.req_item0 = reinterpret_cast<const int32_t *>(gm + plan->gqa_off[2]);
-    a.block_tabs = reinterpret_cast<const int32_t *>(gm + plan->gqa_off[3]);
+    a.blocks = reinterpret_cast<const AttnBlock *>(gm + blob->off[0]);
+    a.item_block0 = reinterpret_cast<const int32_t *>(gm + blob->off[1]);
+    a.req_item0 = reinterpret_cast<const int32_t *>(gm + blob->off[2]);
+    a.block_tabs = reinterpret_cast<const int32_t *>(gm + blob->off[3]);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = static_cast<const uint16_t *>(pool->k);
     a.pool_v = static_cast<const uint16_t *>(pool->v);
@@ -696,10 +661,10 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
     a.o_req = args->out_request_stride;
     a.o_head = args->out_head_stride;
     const size_t acc_elems =
-        static_cast<size_t>(plan->gqa_n_items) * static_cast<size_t>(args->num_q_heads) * kDim;
-    a.part_acc = static_cast<float *>(plan->d_work);
-    a.part_ml = static_cast<float *>(plan->d_work) + acc_elems;
-    a.n_items = plan->gqa_n_items;
+        static_cast<size_t>(n_items) * static_cast<size_t>(args->num_q_heads) * kDim;
+    a.part_acc = static_cast<float *>(work);
+    a.part_ml = static_cast<float *>(work) + acc_elems;
+    a.n_items = n_items;
     a.n_kv_heads = H;
     a.group = args->num_q_heads / H;
     a.num_q_heads = args->num_q_heads;
@@ -724,14 +689,17 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
         default: with_style(std::integral_constant<int, 0>{}); break;
     }
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(gqa_combine_kernel,
+                           dim3(static_cast<unsigned>(p.context.size()),
+                                static_cast<unsigned>(args->num_q_heads)),
+                           dim3(64), 0, stream, a);
+        e = hipGetLastError();
+    }
+    st = release_workspace(work, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    hipLaunchKernelGGL(gqa_combine_kernel,
-                       dim3(static_cast<unsigned>(p.context.size()),
-                            static_cast<unsigned>(args->num_q_heads)),
-                       dim3(64), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "attention combine launch");
-    return PIC_OK;
+    if (st) return st;
+    return note_use(plan, stream);
 }
 
 }  // namespace pic

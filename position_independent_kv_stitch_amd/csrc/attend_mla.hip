@@ -571,6 +571,10 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     clear_error();
     if (!plan || plan->magic != kPlanMagic) return fail(PIC_ERR_STATE, "invalid or destroyed plan");
     const Problem &p = plan->prob;
+    {
+        const pic_status st0 = ensure_attention(plan);
+        if (st0) return st0;
+    }
     if (!args || !args->q || !args->out)
         return fail(PIC_ERR_INVALID_ARG, "attend arguments, q and out must not be NULL");
     if (p.mode == kInPlace) return fail(PIC_ERR_STATE, "in-place plans have no attention map");
@@ -616,67 +620,32 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     const int per_cu = W == 8 ? 1 : W == 1 ? kPerCu1 : 2;
     const int64_t slots = static_cast<int64_t>(cu_count()) * per_cu;
     const int64_t target = std::max<int64_t>(1, slots / sets);
-    {
-        std::lock_guard<std::mutex> lock(plan->mu);
-        hipError_t e;
-        if (plan->latent_key != target) {
-            ItemMap m = build_item_map(p, target, int64_t{1} << 30);
-            if (plan->d_latent) {
-                e = hipDeviceSynchronize();  // earlier launches may read the old items
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-            }
-            if (m.bytes.size() > plan->latent_bytes) {
-                if (plan->d_latent) (void)hipFree(plan->d_latent);
-                plan->d_latent = nullptr;
-                plan->latent_bytes = 0;
-                e = hipMalloc(&plan->d_latent, m.bytes.size());
-                if (e != hipSuccess) {
-                    plan->d_latent = nullptr;
-                    return hip_fail(e, "hipMalloc (latent work items)");
-                }
-                plan->latent_bytes = m.bytes.size();
-            }
-            plan->latent_host = std::move(m.bytes);
-            e = hipMemcpyAsync(plan->d_latent, plan->latent_host.data(), plan->latent_host.size(),
-                               hipMemcpyHostToDevice, stream);
-            if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (latent work items)");
-            e = hipEventRecord(static_cast<hipEvent_t>(plan->upload_event), stream);
-            if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-            plan->latent_off_blocks = m.off_blocks;
-            plan->latent_off_items = m.off_items;
-            plan->latent_off_reqs = m.off_reqs;
-            plan->latent_off_tabs = m.off_tabs;
-            plan->latent_n_items = m.n_items;
-            plan->latent_n_blocks = m.n_blocks;
-            plan->latent_key = target;
-        }
-        const size_t need = static_cast<size_t>(plan->latent_n_items) *
-                            static_cast<size_t>(args->num_q_heads) *
-                            (static_cast<size_t>(kVDim) + 2) * sizeof(float);
-        if (plan->work_bytes < need) {
-            if (plan->d_work) {
-                e = hipDeviceSynchronize();  // earlier calls may use it
-                if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-                (void)hipFree(plan->d_work);
-                plan->d_work = nullptr;
-                plan->work_bytes = 0;
-            }
-            e = hipMalloc(&plan->d_work, need);
-            if (e != hipSuccess) {
-                plan->d_work = nullptr;
-                return hip_fail(e, "hipMalloc (attention workspace)");
-            }
-            plan->work_bytes = need;
-        }
-    }
+    const DevBlob *blob = nullptr;
+    st = plan_blob(plan, blob_key(kBlobLatent, target), stream_, [&](DevBlob &b) {
+        ItemMap m = build_item_map(p, target, int64_t{1} << 30);
+        b.host = std::move(m.bytes);
+        b.off[0] = m.off_blocks;
+        b.off[1] = m.off_items;
+        b.off[2] = m.off_reqs;
+        b.off[3] = m.off_tabs;
+        b.n[0] = m.n_items;
+        b.n[1] = m.n_blocks;
+    }, &blob);
+    if (st) return st;
+    const int32_t n_items = blob->n[0];
+    const size_t need = static_cast<size_t>(n_items) * static_cast<size_t>(args->num_q_heads) *
+                        (static_cast<size_t>(kVDim) + 2) * sizeof(float);
+    void *work = nullptr;
+    st = call_workspace(need, stream_, &work);
+    if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
-    const uint8_t *lm = static_cast<const uint8_t *>(plan->d_latent);
+    const uint8_t *lm = static_cast<const uint8_t *>(blob->dev);
     MlaArgs a{};
     a.tiles = reinterpret_cast<const AttnTile *>(lm);
-    a.blocks = reinterpret_cast<const AttnBlock *>(lm + plan->latent_off_blocks);
-    a.item_block0 = reinterpret_cast<const int32_t *>(lm + plan->latent_off_items);
-    a.req_item0 = reinterpret_cast<const int32_t *>(lm + plan->latent_off_reqs);
-    a.block_tabs = reinterpret_cast<const int32_t *>(lm + plan->latent_off_tabs);
+    a.blocks = reinterpret_cast<const AttnBlock *>(lm + blob->off[0]);
+    a.item_block0 = reinterpret_cast<const int32_t *>(lm + blob->off[1]);
+    a.req_item0 = reinterpret_cast<const int32_t *>(lm + blob->off[2]);
+    a.block_tabs = reinterpret_cast<const int32_t *>(lm + blob->off[3]);
     a.cs = reinterpret_cast<const double *>(dm + plan->staged.off_cs);
     a.pool_k = static_cast<const uint16_t *>(pool->k);
     a.cache_k = static_cast<const uint16_t *>(cache->k);
@@ -694,10 +663,10 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     a.o_req = args->out_request_stride;
     a.o_head = args->out_head_stride;
     const size_t acc_elems =
-        static_cast<size_t>(plan->latent_n_items) * static_cast<size_t>(args->num_q_heads) * kVDim;
-    a.part_acc = static_cast<float *>(plan->d_work);
-    a.part_ml = static_cast<float *>(plan->d_work) + acc_elems;
-    a.n_items = plan->latent_n_items;
+        static_cast<size_t>(n_items) * static_cast<size_t>(args->num_q_heads) * kVDim;
+    a.part_acc = static_cast<float *>(work);
+    a.part_ml = static_cast<float *>(work) + acc_elems;
+    a.n_items = n_items;
     a.n_sets = sets;
     a.num_q_heads = args->num_q_heads;
     a.scale = args->scale;
@@ -708,12 +677,15 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     hipError_t e = p.style == PIC_ROPE_HALF
                        ? launch_block<PIC_ROPE_HALF>(W, grid, stream, a, args->layer)
                        : launch_block<PIC_ROPE_INTERLEAVED>(W, grid, stream, a, args->layer);
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(mla_combine_kernel,
+                           dim3(static_cast<unsigned>(p.context.size()),
+                                static_cast<unsigned>(args->num_q_heads)),
+                           dim3(kCombineThreads), 0, stream, a);
+        e = hipGetLastError();
+    }
+    st = release_workspace(work, stream_);
     if (e != hipSuccess) return hip_fail(e, "latent attention kernel launch");
-    hipLaunchKernelGGL(mla_combine_kernel,
-                       dim3(static_cast<unsigned>(p.context.size()),
-                            static_cast<unsigned>(args->num_q_heads)),
-                       dim3(kCombineThreads), 0, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return hip_fail(e, "latent attention combine launch");
-    return PIC_OK;
+    if (st) return st;
+    return note_use(plan, stream_);
 }

@@ -49,6 +49,7 @@
 
 #include <cstdint>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <new>
 #include <string>
@@ -698,6 +699,20 @@ inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255);
 }  // namespace
 }  // namespace pic
 
+namespace pic {
+// One uploaded version of a registry's device table.  A version is never
+// written after its upload: a changed registry uploads a new one, and the
+// old one is freed once every pic_match that read it has run (its last-use
+// event per stream has completed).
+struct RegTable {
+    RegSlot *dev = nullptr;
+    std::vector<RegSlot> host;  // the uploaded slots (alive for the copy)
+    uint32_t mask = 0;
+    hipEvent_t ready = nullptr;
+    std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
+};
+}  // namespace pic
+
 // The opaque registry handle of the C ABI.
 struct pic_registry {
     uint32_t magic = 0x52454753u;
@@ -707,11 +722,8 @@ struct pic_registry {
     std::unordered_set<std::string> keys;  // fingerprint bytes + length, for duplicates
     bool dirty = true;
     int device = -1;
-    std::vector<pic::RegSlot> host_table;  // last uploaded table (kept alive for the copy)
-    pic::RegSlot *d_table = nullptr;
-    size_t d_slots = 0;
-    uint32_t mask = 0;
-    hipEvent_t upload_event = nullptr;
+    std::unique_ptr<pic::RegTable> table;                 // the current version
+    std::vector<std::unique_ptr<pic::RegTable>> retired;  // older versions still in use
 };
 
 namespace pic {
@@ -725,9 +737,32 @@ std::string reg_key(const uint64_t fp[4], int32_t length) {
     return k;
 }
 
+// Whether every launch that read table t has run (host check, no wait).
+bool table_idle(const RegTable &t) {
+    if (t.ready && hipEventQuery(t.ready) == hipErrorNotReady) return false;
+    for (const auto &u : t.uses)
+        if (hipEventQuery(u.second) == hipErrorNotReady) return false;
+    return true;
+}
+
+// Release table t; with `wait`, first wait for the launches that read it.
+void free_table(RegTable &t, bool wait) {
+    for (auto &u : t.uses) {
+        if (wait) (void)hipEventSynchronize(u.second);
+        (void)hipEventDestroy(u.second);
+    }
+    if (t.ready) {
+        if (wait) (void)hipEventSynchronize(t.ready);
+        (void)hipEventDestroy(t.ready);
+    }
+    if (t.dev) (void)hipFree(t.dev);
+    t = RegTable{};
+}
+
 // Bring the device table up to date on the current device, ordered on
-// `stream`.  A changed registry waits for the device first, since kernels of
-// earlier calls may still read the old table.
+// `stream`.  A changed registry uploads a new version (earlier calls on any
+// stream may still read the old one, which is retired, not overwritten);
+// an unchanged one makes `stream` wait for the current version's upload.
 pic_status sync_registry(pic_registry *reg, hipStream_t stream, const RegSlot **tab,
                          uint32_t *mask) {
     int dev = -1;
@@ -736,53 +771,67 @@ pic_status sync_registry(pic_registry *reg, hipStream_t stream, const RegSlot **
     if (reg->device >= 0 && dev != reg->device)
         return fail(PIC_ERR_STATE, "registry lives on device %d, current device is %d",
                     reg->device, dev);
-    if (reg->dirty) {
-        if (reg->d_table) {
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize (registry update)");
+    for (size_t i = 0; i < reg->retired.size();) {  // versions no call reads any more
+        if (table_idle(*reg->retired[i])) {
+            free_table(*reg->retired[i], false);
+            reg->retired.erase(reg->retired.begin() + static_cast<std::ptrdiff_t>(i));
+        } else {
+            i++;
         }
+    }
+    if (reg->dirty || !reg->table) {
+        std::unique_ptr<RegTable> t(new (std::nothrow) RegTable);
+        if (!t) return fail(PIC_ERR_NOMEM, "out of host memory");
         size_t slots = 16;
         while (slots < 2 * reg->entries.size()) slots *= 2;
-        reg->host_table.assign(slots, RegSlot{{0, 0, 0, 0}, 0, -1});
+        t->host.assign(slots, RegSlot{{0, 0, 0, 0}, 0, -1});
         const uint32_t m = static_cast<uint32_t>(slots - 1);
-        for (const RegSlot &s : reg->entries) {
-            uint32_t i = static_cast<uint32_t>(slot_hash(s.fp[0], s.length)) & m;
-            while (reg->host_table[i].chunk_id >= 0) i = (i + 1) & m;
-            reg->host_table[i] = s;
+        for (const RegSlot &sl : reg->entries) {
+            uint32_t i = static_cast<uint32_t>(slot_hash(sl.fp[0], sl.length)) & m;
+            while (t->host[i].chunk_id >= 0) i = (i + 1) & m;
+            t->host[i] = sl;
         }
-        if (slots > reg->d_slots) {
-            if (reg->d_table) (void)hipFree(reg->d_table);
-            reg->d_table = nullptr;
-            reg->d_slots = 0;
-            e = hipMalloc(&reg->d_table, slots * sizeof(RegSlot));
-            if (e != hipSuccess) {
-                reg->d_table = nullptr;
-                return hip_fail(e, "hipMalloc (registry table)");
-            }
-            reg->d_slots = slots;
+        t->mask = m;
+        e = hipMalloc(&t->dev, slots * sizeof(RegSlot));
+        if (e != hipSuccess) {
+            t->dev = nullptr;
+            return hip_fail(e, "hipMalloc (registry table)");
         }
-        e = hipMemcpyAsync(reg->d_table, reg->host_table.data(), slots * sizeof(RegSlot),
-                           hipMemcpyHostToDevice, stream);
-        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (registry table)");
-        if (!reg->upload_event) {
-            e = hipEventCreateWithFlags(&reg->upload_event, hipEventDisableTiming);
-            if (e != hipSuccess) {
-                reg->upload_event = nullptr;
-                return hip_fail(e, "hipEventCreate");
-            }
+        e = hipMemcpyAsync(t->dev, t->host.data(), slots * sizeof(RegSlot), hipMemcpyHostToDevice,
+                           stream);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&t->ready, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(t->ready, stream);
+        if (e != hipSuccess) {
+            (void)hipStreamSynchronize(stream);
+            free_table(*t, false);
+            return hip_fail(e, "registry table upload");
         }
-        e = hipEventRecord(reg->upload_event, stream);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-        reg->mask = m;
+        if (reg->table) reg->retired.push_back(std::move(reg->table));
+        reg->table = std::move(t);
         reg->device = dev;
         reg->dirty = false;
     } else {
-        e = hipStreamWaitEvent(stream, reg->upload_event, 0);
+        e = hipStreamWaitEvent(stream, reg->table->ready, 0);
         if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
     }
-    *tab = reg->d_table;
-    *mask = reg->mask;
+    *tab = reg->table->dev;
+    *mask = reg->table->mask;
     return PIC_OK;
+}
+
+// Record that launches on `stream` read the registry's current table.
+pic_status note_table_use(pic_registry *reg, hipStream_t stream) {
+    RegTable &t = *reg->table;
+    hipEvent_t ev = nullptr;
+    for (auto &u : t.uses)
+        if (u.first == stream) ev = u.second;
+    if (!ev) {
+        const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        t.uses.emplace_back(stream, ev);
+    }
+    const hipError_t e = hipEventRecord(ev, stream);
+    return e == hipSuccess ? PIC_OK : hip_fail(e, "hipEventRecord");
 }
 
 }  // namespace
@@ -831,11 +880,9 @@ pic_status pic_registry_add(pic_registry_t *reg, const uint8_t *fp, int32_t leng
 void pic_registry_destroy(pic_registry_t *reg) {
     if (!reg || reg->magic != pic::kRegMagic) return;
     reg->magic = 0;
-    if (reg->d_table) {
-        (void)hipDeviceSynchronize();
-        (void)hipFree(reg->d_table);
-    }
-    if (reg->upload_event) (void)hipEventDestroy(reg->upload_event);
+    // the registry's own work only: the launches that read any table version
+    if (reg->table) pic::free_table(*reg->table, true);
+    for (auto &t : reg->retired) pic::free_table(*t, true);
     delete reg;
 }
 
@@ -944,6 +991,7 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
     const hipError_t e2 = hipFreeAsync(mem, stream);
     if (e != hipSuccess) return hip_fail(e, "pic_match launch");
     if (e2 != hipSuccess) return hip_fail(e2, "hipFreeAsync (pic_match temporaries)");
+    if (reg) return note_table_use(reg, stream);  // the lock is still held
     return PIC_OK;
 }
 

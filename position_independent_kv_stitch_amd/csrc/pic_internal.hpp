@@ -3,6 +3,8 @@
 #pragma once
 
 #include <cstdint>
+#include <functional>
+#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -70,6 +72,19 @@ struct Launch {
     int32_t stream_loads = 0;  // 1: no pool row is read twice in a launch (non-temporal loads)
 };
 
+// What a plan's attention map is built from, copied from the caller's arrays
+// by pic_plan (pic_plan returns before the map exists; the first call that
+// needs it builds it).  requests[r] and chunks[c] point into the vectors
+// here.
+struct AttnSource {
+    std::vector<pic_chunk> chunks;
+    std::vector<int32_t> chunk_pages;  // pool page tables, chunk after chunk (paged pool)
+    std::vector<pic_entry> entries;    // request after request
+    std::vector<int32_t> req_pages;    // destination page tables, request after request
+    std::vector<pic_request> requests;
+    std::vector<int32_t> cs_of_entry;  // shift table of every entry (-1: delta 0)
+};
+
 struct Problem {
     pic_kv_shape shape{};
     int32_t rope_dim = 0;
@@ -88,6 +103,8 @@ struct Problem {
     std::vector<double> cs;       // [table][rope_dim/2][cos, sin]
     std::vector<int64_t> bounds;  // [entry][request, begin, end]
     std::vector<int64_t> recompute;
+    AttnSource attn_src;
+    bool attn_built = false;       // the members below exist once this is set
     std::vector<AttnTile> atiles;  // pic_attend map, request after request
     std::vector<AttnBlock> ablocks;
     std::vector<int64_t> context;  // context_len per request
@@ -98,11 +115,26 @@ struct Problem {
     pic_plan_info_t info{};
 };
 
-// Everything the device needs, packed into one upload.
+// Layout of a plan's stitch tiles and shift tables in one device buffer.
 struct Staged {
-    std::vector<uint8_t> bytes;
-    size_t off_tiles = 0, off_cs = 0, off_atiles = 0, off_ablocks = 0, off_rblock = 0;
+    size_t off_tiles = 0, off_cs = 0, total = 0;
 };
+
+// Metadata of one attention launch shape (the map in work blocks, or work
+// items of a kernel), packed for one upload: `host` stays alive with the
+// plan (the copy reads it asynchronously), `ready` is recorded after the
+// copy and every launch that reads `dev` waits for it on its own stream.
+// Blobs are never rebuilt or freed before the plan, so launches on other
+// streams can still read them.
+struct DevBlob {
+    std::vector<uint8_t> host;
+    void *dev = nullptr;
+    void *ready = nullptr;  // hipEvent_t
+    size_t off[8] = {};
+    int32_t n[4] = {};
+};
+enum BlobKind : int64_t { kBlobAttnMap = 1, kBlobGqa = 2, kBlobLatent = 3, kBlobBoundary = 4 };
+inline int64_t blob_key(BlobKind kind, int64_t shape_key) { return (int64_t{kind} << 56) | shape_key; }
 
 // Thread-local error reporting.
 void clear_error();
@@ -114,6 +146,9 @@ pic_status derive_units(const pic_kv_shape *shape, const pic_rope_config *rope, 
 
 // Slot shape of the kernel for a dtype and unit counts.
 Launch launch_shape_of(int32_t dtype, const Units &u);
+
+// The attention map of a copy-mode problem, from its AttnSource (host only).
+void build_attention(Problem *p);
 
 // Copy-mode and in-place problem builders (host only).
 pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
@@ -130,15 +165,36 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
                               const pic_page_segment *segments, int32_t n_segments,
                               Problem *turn, Problem *copy);
 Staged stage(const Problem &p);
+// The staged bytes of p written to `out` (stage(p).total bytes).
+void write_staged(const Problem &p, const Staged &s, uint8_t *out);
 
 // The matrix-core path of pic_attend (attend_gqa.hip): whether it takes a
 // plan at a GQA group size, and its launch (arguments checked by pic_attend).
 bool gqa_tile_path(const Problem &p, int group);
 
+// The plan's attention map, built on first use (host only; thread-safe).
+pic_status ensure_attention(struct ::pic_plan *plan);
+
 // Device side (stitch.hip): first-use upload of a plan's metadata, ordered on
 // `stream` (a hipStream_t); view checks shared by the launchers.
 pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream);
 pic_status check_view(const pic_kv_view *v, int vec, bool need_v, const char *name);
+
+// The plan's blob `key` on its device: built by `make` and uploaded ordered
+// on `stream` the first time, and waited for on `stream` every time
+// (ensure_device_plan must have succeeded first).
+pic_status plan_blob(struct ::pic_plan *plan, int64_t key, void *stream,
+                     const std::function<void(DevBlob &)> &make, const DevBlob **out);
+
+// Per-call workspace in stream-ordered device memory: allocated on `stream`
+// before the launches that use it and freed on `stream` after them, so calls
+// on different streams never share one.
+pic_status call_workspace(size_t bytes, void *stream, void **out);
+pic_status release_workspace(void *ptr, void *stream);
+
+// Record that work reading the plan is enqueued on `stream` (the plan keeps
+// one event per stream it was used on; pic_plan_destroy waits for them).
+pic_status note_use(struct ::pic_plan *plan, void *stream);
 }  // namespace pic
 
 // The opaque plan handle of the C ABI.
@@ -150,29 +206,6 @@ struct pic_plan {
     int device = -1;
     void *d_mem = nullptr;
     void *upload_event = nullptr;  // hipEvent_t
-    void *d_work = nullptr;        // pic_attend partial results
-    size_t work_bytes = 0;
-    // pic_attend_latent work items (attend_mla.hip): built for one launch
-    // shape, uploaded, and rebuilt when a call needs another shape
-    void *d_latent = nullptr;
-    size_t latent_bytes = 0;
-    int64_t latent_key = -1;
-    std::vector<uint8_t> latent_host;  // the uploaded bytes (alive for the copy)
-    size_t latent_off_blocks = 0, latent_off_items = 0, latent_off_reqs = 0, latent_off_tabs = 0;
-    int32_t latent_n_items = 0, latent_n_blocks = 0;
-    // pic_attend_boundary work items (attend_boundary.hip), the same way
-    void *d_bnd = nullptr;
-    size_t bnd_bytes = 0;
-    int64_t bnd_key = -1;
-    std::vector<uint8_t> bnd_host;
-    size_t bnd_off[6] = {0, 0, 0, 0, 0, 0};  // blocks, block positions, items, requests,
-                                             // limits, block shift tables
-    int32_t gqa_n_items = 0;
-    // pic_attend's matrix-core work items (attend_gqa.hip), the same way
-    void *d_gqa = nullptr;
-    size_t gqa_bytes = 0;
-    int64_t gqa_key = -1;
-    std::vector<uint8_t> gqa_host;
-    size_t gqa_off[4] = {0, 0, 0, 0};  // blocks, items, requests, block shift tables
-    int32_t bnd_n_items = 0, bnd_n_reqs = 0, bnd_max_rows = 0;
+    std::map<int64_t, pic::DevBlob> blobs;
+    std::vector<std::pair<void *, void *>> uses;  // (hipStream_t, hipEvent_t of its last use)
 };

@@ -143,16 +143,24 @@ Launch launch_shape_of(int32_t dtype, const Units &u) {
 
 namespace {
 
-// cos/sin of delta * theta_i for i < rope_dim/2, in fp64 (libm), appended to cs.
-void append_shift_table(const pic_rope_config &rope, int64_t delta, std::vector<double> &cs) {
+// theta_i = b^(-2i/d) for i < rope_dim/2 in fp64 (libm), or the caller's table.
+std::vector<double> plane_frequencies(const pic_rope_config &rope) {
     const int half_r = rope.rope_dim / 2;
-    for (int i = 0; i < half_r; i++) {
-        const double f = rope.inv_freq
-                             ? rope.inv_freq[i]
+    std::vector<double> f(static_cast<size_t>(half_r));
+    for (int i = 0; i < half_r; i++)
+        f[i] = rope.inv_freq ? rope.inv_freq[i]
                              : std::pow(rope.theta, -(2.0 * i) / static_cast<double>(rope.rope_dim));
-        const double phi = static_cast<double>(delta) * f;
-        cs.push_back(std::cos(phi));
-        cs.push_back(std::sin(phi));
+    return f;
+}
+
+// cos/sin of delta * theta_i for every plane i, in fp64 (libm), appended to cs.
+void append_shift_table(const std::vector<double> &freq, int64_t delta, std::vector<double> &cs) {
+    const size_t at = cs.size();
+    cs.resize(at + 2 * freq.size());
+    double *out = cs.data() + at;
+    for (size_t i = 0; i < freq.size(); i++) {
+        const double phi = static_cast<double>(delta) * freq[i];
+        sincos(phi, &out[2 * i + 1], &out[2 * i]);
     }
 }
 
@@ -169,6 +177,44 @@ bool any_overlap(std::vector<Interval> &v) {
         if (v[i].key == v[i - 1].key && v[i].lo < v[i - 1].hi) return true;
     return false;
 }
+
+// Claims on the slots of a pool of pages (a flat range of rows is one page),
+// for the checks that no slot is written twice or read twice.  A bit per
+// slot while the pool is not much larger than the claimed slots (about 1.5 M
+// bits for the batched-RAG destination), else the claimed runs, sorted once.
+class SlotClaims {
+  public:
+    SlotClaims(int64_t n_pages, int64_t page_size, int64_t expected_slots) : ps_(page_size) {
+        constexpr int64_t kMaxBits = int64_t{1} << 30;
+        use_bits_ = page_size > 0 && n_pages >= 0 && n_pages <= kMaxBits / page_size &&
+                    n_pages * page_size <= 64 * expected_slots + (int64_t{1} << 22);
+        if (use_bits_) words_.assign(static_cast<size_t>((n_pages * page_size + 63) / 64), 0);
+    }
+    void claim(int64_t page, int64_t lo, int64_t hi) {
+        if (!use_bits_) {
+            runs_.push_back(Interval{page, lo, hi});
+            return;
+        }
+        int64_t a = page * ps_ + lo;
+        const int64_t b = page * ps_ + hi;
+        while (a < b) {
+            const int sh = static_cast<int>(a & 63);
+            const int64_t n = std::min<int64_t>(64 - sh, b - a);
+            const uint64_t m = (n == 64 ? ~uint64_t{0} : ((uint64_t{1} << n) - 1)) << sh;
+            uint64_t &w = words_[static_cast<size_t>(a >> 6)];
+            clash_ |= (w & m) != 0;
+            w |= m;
+            a += n;
+        }
+    }
+    bool overlap() { return use_bits_ ? clash_ : any_overlap(runs_); }
+
+  private:
+    int64_t ps_;
+    bool use_bits_ = false, clash_ = false;
+    std::vector<uint64_t> words_;
+    std::vector<Interval> runs_;
+};
 
 void fill_info(Problem *p, int64_t tokens_written, int64_t tokens_masked, int64_t pool_need) {
     const int64_t es = p->shape.dtype == PIC_DTYPE_F32 ? 4 : 2;
@@ -195,23 +241,31 @@ void fill_info(Problem *p, int64_t tokens_written, int64_t tokens_masked, int64_
 // after them.
 void add_tiles(Problem *p, const HostEntry &e, const int32_t *dst_pages, const int32_t *src_pages,
                int32_t from, int32_t to) {
-    int32_t t = from;
-    while (t < to) {
+    if (from >= to) return;
+    const int64_t sps = p->src_page_size, ps = p->page_size;
+    // page and slot of the first token, then advanced tile by tile
+    int64_t s_pg = 0, d_pg = 0;
+    int32_t s_slot = 0, d_slot = 0;
+    if (src_pages) {
+        s_pg = (e.src_tok + from) / sps;
+        s_slot = static_cast<int32_t>((e.src_tok + from) % sps);
+    }
+    if (p->mode == kPaged) {
+        d_pg = (e.dst_pos + from) / ps;
+        d_slot = static_cast<int32_t>((e.dst_pos + from) % ps);
+    }
+    for (int32_t t = from; t < to;) {
         int32_t n = std::min(p->tile_tokens, to - t);
         DevTile tile{e.src_tok + t, 0, 0, 0, e.cs_idx, 0};
         if (src_pages) {
-            const int64_t at = e.src_tok + t;  // offset in the chunk's page list
-            const int32_t slot = static_cast<int32_t>(at % p->src_page_size);
-            n = std::min<int32_t>(n, p->src_page_size - slot);
-            tile.src_row = src_pages[at / p->src_page_size];
-            tile.src_slot = slot;
+            n = std::min<int32_t>(n, static_cast<int32_t>(sps) - s_slot);
+            tile.src_row = src_pages[s_pg];
+            tile.src_slot = s_slot;
         }
         if (p->mode == kPaged) {
-            const int64_t pos = e.dst_pos + t;
-            const int32_t slot = static_cast<int32_t>(pos % p->page_size);
-            n = std::min<int32_t>(n, p->page_size - slot);
-            tile.dst_a = dst_pages[pos / p->page_size];
-            tile.dst_b = slot;
+            n = std::min<int32_t>(n, static_cast<int32_t>(ps) - d_slot);
+            tile.dst_a = dst_pages[d_pg];
+            tile.dst_b = d_slot;
         } else if (p->mode == kContiguous) {
             tile.dst_a = e.request;
             tile.dst_b = static_cast<int32_t>(e.dst_pos + t);
@@ -219,6 +273,14 @@ void add_tiles(Problem *p, const HostEntry &e, const int32_t *dst_pages, const i
         tile.ntok = n;
         p->tiles.push_back(tile);
         t += n;
+        if (src_pages && (s_slot += n) == sps) {
+            s_slot = 0;
+            s_pg++;
+        }
+        if (p->mode == kPaged && (d_slot += n) == ps) {
+            d_slot = 0;
+            d_pg++;
+        }
     }
 }
 
@@ -336,9 +398,13 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             }
         if (any_overlap(iv)) return fail(PIC_ERR_OVERLAP, "entries of a request overlap");
     }
+    int64_t to_write = 0;  // tokens every entry writes, summed
+    for (int r = 0; r < n_requests; r++)
+        for (int j = 0; j < requests[r].n_entries; j++)
+            to_write += requests[r].entries[j].length - requests[r].entries[j].recompute_k;
     if (paged) {
-        std::vector<Interval> iv;
         const int64_t ps = geom->dst_page_size;
+        SlotClaims claims(geom->dst_num_pages, ps, to_write);
         for (int r = 0; r < n_requests; r++)
             for (int j = 0; j < requests[r].n_entries; j++) {
                 const pic_entry &e = requests[r].entries[j];
@@ -347,11 +413,11 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
                 while (pos < end) {
                     const int64_t lp = pos / ps, slot = pos % ps;
                     const int64_t run = std::min(ps - slot, end - pos);
-                    iv.push_back(Interval{requests[r].page_table[lp], slot, slot + run});
+                    claims.claim(requests[r].page_table[lp], slot, slot + run);
                     pos += run;
                 }
             }
-        if (any_overlap(iv))
+        if (claims.overlap())
             return fail(PIC_ERR_OVERLAP, "two placements write the same physical row");
     }
 
@@ -373,26 +439,38 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
         // Pool rows read more than once per layer (a chunk placed twice, or
         // chunks sharing rows) may be served from cache on the second read;
         // only a plan that reads every row once streams its loads.
-        std::vector<Interval> iv;
+        std::vector<Interval> iv;  // contiguous pool: one run per entry
+        SlotClaims claims(src_paged ? geom->src_num_pages : 0, src_paged ? sps : 1, to_write);
         for (int r = 0; r < n_requests; r++)
             for (int j = 0; j < requests[r].n_entries; j++) {
                 const pic_entry &e = requests[r].entries[j];
                 const pic_chunk &ch = chunks[e.chunk_id];
                 int64_t t = ch.token_start + e.recompute_k;
                 const int64_t end = ch.token_start + e.length;
-                while (t < end) {
-                    if (!src_paged) {
-                        iv.push_back(Interval{0, t, end});
-                        break;
-                    }
+                if (t < end && !src_paged) iv.push_back(Interval{0, t, end});
+                while (src_paged && t < end) {
                     const int64_t slot = t % sps;
                     const int64_t run = std::min(sps - slot, end - t);
-                    iv.push_back(Interval{ch.page_table[t / sps], slot, slot + run});
+                    claims.claim(ch.page_table[t / sps], slot, slot + run);
                     t += run;
                 }
             }
-        p.launch.stream_loads = any_overlap(iv) ? 0 : 1;
+        p.launch.stream_loads = (src_paged ? claims.overlap() : any_overlap(iv)) ? 0 : 1;
     }
+    {
+        // tiles end at tile_tokens and at destination and pool page ends
+        int64_t bound = 0;
+        for (int r = 0; r < n_requests; r++)
+            for (int j = 0; j < requests[r].n_entries; j++) {
+                const int64_t n = requests[r].entries[j].length - requests[r].entries[j].recompute_k;
+                if (n <= 0) continue;
+                bound += n / p.tile_tokens + 1;
+                if (paged) bound += n / geom->dst_page_size + 1;
+                if (src_paged) bound += n / sps + 1;
+            }
+        p.tiles.reserve(static_cast<size_t>(bound));
+    }
+    const std::vector<double> freq = plane_frequencies(*rope);
     std::unordered_map<int64_t, int32_t> table_of_delta;
     std::vector<int32_t> cs_of_entry;
     int64_t written = 0, masked = 0;
@@ -408,7 +486,7 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
                 if (it == table_of_delta.end()) {
                     cs_idx = static_cast<int32_t>(table_of_delta.size());
                     table_of_delta.emplace(delta, cs_idx);
-                    append_shift_table(*rope, delta, p.cs);
+                    append_shift_table(freq, delta, p.cs);
                 } else {
                     cs_idx = it->second;
                 }
@@ -424,19 +502,72 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             masked += e.recompute_k;
         }
     }
-    int32_t entry0 = 0;
     int64_t context_tokens = 0;
     for (int r = 0; r < n_requests; r++) {
-        build_attention_map(&p, chunks, requests[r], r, cs_of_entry, entry0);
-        entry0 += requests[r].n_entries;
-        context_tokens += p.context.back();
+        const pic_request &rq = requests[r];
+        int64_t L = rq.context_len;
+        for (int j = 0; j < rq.n_entries && rq.context_len == 0; j++)
+            L = std::max(L, rq.entries[j].dst_offset + rq.entries[j].length);
+        context_tokens += L;
     }
-    build_attention_blocks(&p);
+    // copies of what the attention map is built from, when a call needs it
+    AttnSource &as = p.attn_src;
+    as.cs_of_entry = std::move(cs_of_entry);
+    as.chunks.assign(chunks, chunks + n_chunks);
+    if (src_paged) {
+        size_t n = 0;
+        for (int c = 0; c < n_chunks; c++) n += static_cast<size_t>(chunks[c].n_pages);
+        as.chunk_pages.reserve(n);
+        for (int c = 0; c < n_chunks; c++)
+            as.chunk_pages.insert(as.chunk_pages.end(), chunks[c].page_table,
+                                  chunks[c].page_table + chunks[c].n_pages);
+    }
+    {
+        size_t ne = 0, np = 0;
+        for (int r = 0; r < n_requests; r++) {
+            ne += static_cast<size_t>(requests[r].n_entries);
+            if (paged) np += static_cast<size_t>(requests[r].n_pages);
+        }
+        as.entries.reserve(ne);
+        as.req_pages.reserve(np);
+        for (int r = 0; r < n_requests; r++) {
+            as.entries.insert(as.entries.end(), requests[r].entries,
+                              requests[r].entries + requests[r].n_entries);
+            if (paged)
+                as.req_pages.insert(as.req_pages.end(), requests[r].page_table,
+                                    requests[r].page_table + requests[r].n_pages);
+        }
+    }
+    size_t at = 0;
+    for (int c = 0; c < n_chunks; c++) {
+        as.chunks[c].page_table = src_paged ? as.chunk_pages.data() + at : nullptr;
+        if (src_paged) at += static_cast<size_t>(chunks[c].n_pages);
+    }
+    as.requests.assign(requests, requests + n_requests);
+    size_t e0 = 0, p0 = 0;
+    for (int r = 0; r < n_requests; r++) {
+        as.requests[r].entries = as.entries.data() + e0;
+        as.requests[r].page_table = paged ? as.req_pages.data() + p0 : nullptr;
+        e0 += static_cast<size_t>(requests[r].n_entries);
+        if (paged) p0 += static_cast<size_t>(requests[r].n_pages);
+    }
     fill_info(&p, written, masked, pool_need);
     p.info.context_tokens = context_tokens;
-    p.info.attend_blocks = static_cast<int64_t>(p.ablocks.size());
-    p.info.attend_block_tokens = p.attn_block_tokens;
     return PIC_OK;
+}
+
+void build_attention(Problem *p) {
+    const AttnSource &as = p->attn_src;
+    int32_t entry0 = 0;
+    for (size_t r = 0; r < as.requests.size(); r++) {
+        build_attention_map(p, as.chunks.data(), as.requests[r], static_cast<int32_t>(r),
+                            as.cs_of_entry, entry0);
+        entry0 += as.requests[r].n_entries;
+    }
+    build_attention_blocks(p);
+    p->info.attend_blocks = static_cast<int64_t>(p->ablocks.size());
+    p->info.attend_block_tokens = p->attn_block_tokens;
+    p->attn_built = true;
 }
 
 pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
@@ -476,6 +607,7 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.launch = launch_shape_of(shape->dtype, u);
     p.tile_tokens = kTileSteps * 4 * p.launch.g;
     p.launch.stream_loads = 1;  // segments never overlap: every row is read once
+    const std::vector<double> freq = plane_frequencies(*rope);
     std::unordered_map<int64_t, int32_t> table_of_delta;
     int64_t written = 0, masked = 0;
     for (int g = 0; g < n_segments; g++) {
@@ -489,7 +621,7 @@ pic_status build_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
         if (it == table_of_delta.end()) {
             cs_idx = static_cast<int32_t>(table_of_delta.size());
             table_of_delta.emplace(s.delta, cs_idx);
-            append_shift_table(*rope, s.delta, p.cs);
+            append_shift_table(freq, s.delta, p.cs);
         } else {
             cs_idx = it->second;
         }
@@ -605,13 +737,14 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
     turn->launch.stream_loads = 1;  // every turned slot is read once
     init(*copy, uc, kPaged);
     copy->launch.stream_loads = 0;  // a shared page may be copied for several segments
+    const std::vector<double> freq = plane_frequencies(*rope);
     std::unordered_map<int64_t, int32_t> tab_turn, tab_copy;
     auto table = [&](Problem &p, std::unordered_map<int64_t, int32_t> &m, int64_t delta) {
         auto it = m.find(delta);
         if (it != m.end()) return it->second;
         const int32_t idx = static_cast<int32_t>(m.size());
         m.emplace(delta, idx);
-        append_shift_table(*rope, delta, p.cs);
+        append_shift_table(freq, delta, p.cs);
         return idx;
     };
     int64_t turned = 0, copied = 0;
@@ -655,20 +788,24 @@ Staged stage(const Problem &p) {
     auto align = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
     s.off_tiles = 0;
     s.off_cs = align(p.tiles.size() * sizeof(DevTile));
-    s.off_atiles = align(s.off_cs + p.cs.size() * sizeof(double));
-    s.off_ablocks = align(s.off_atiles + p.atiles.size() * sizeof(AttnTile));
-    s.off_rblock = align(s.off_ablocks + p.ablocks.size() * sizeof(AttnBlock));
-    const size_t total = align(s.off_rblock + p.req_block0.size() * sizeof(int32_t));
-    s.bytes.assign(std::max<size_t>(total, 256), 0);
-    auto put = [&](size_t off, const void *src, size_t n) {
-        if (n) std::memcpy(&s.bytes[off], src, n);
-    };
-    put(s.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(DevTile));
-    put(s.off_cs, p.cs.data(), p.cs.size() * sizeof(double));
-    put(s.off_atiles, p.atiles.data(), p.atiles.size() * sizeof(AttnTile));
-    put(s.off_ablocks, p.ablocks.data(), p.ablocks.size() * sizeof(AttnBlock));
-    put(s.off_rblock, p.req_block0.data(), p.req_block0.size() * sizeof(int32_t));
+    s.total = std::max<size_t>(align(s.off_cs + p.cs.size() * sizeof(double)), 256);
     return s;
+}
+
+void write_staged(const Problem &p, const Staged &s, uint8_t *out) {
+    if (!p.tiles.empty()) std::memcpy(out + s.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(DevTile));
+    if (!p.cs.empty()) std::memcpy(out + s.off_cs, p.cs.data(), p.cs.size() * sizeof(double));
+}
+
+pic_status ensure_attention(struct ::pic_plan *plan) {
+    std::lock_guard<std::mutex> lock(plan->mu);
+    if (plan->prob.attn_built) return PIC_OK;
+    try {
+        build_attention(&plan->prob);
+    } catch (const std::bad_alloc &) {
+        return fail(PIC_ERR_NOMEM, "out of host memory (attention map)");
+    }
+    return PIC_OK;
 }
 
 }  // namespace pic
@@ -704,6 +841,9 @@ pic_status pic_plan_info(const pic_plan_t *plan, pic_plan_info_t *info) {
     if (!plan || plan->magic != pic::kPlanMagic)
         return pic::fail(PIC_ERR_STATE, "invalid or destroyed plan");
     if (!info) return pic::fail(PIC_ERR_INVALID_ARG, "info must not be NULL");
+    // the attention counts need the map: built here if no call has built it
+    pic_status st = pic::ensure_attention(const_cast<pic_plan_t *>(plan));
+    if (st) return st;
     *info = plan->prob.info;
     return PIC_OK;
 }

@@ -406,7 +406,8 @@ KArgs args_for(const Problem &p, const uint8_t *dmem, const Staged &stg) {
 
 // Upload the plan's metadata to the current device on first use, ordered on
 // `stream`; later uses on any stream wait for that upload.  A plan stays on
-// the device of its first use.
+// the device of its first use.  The copies read the plan's own tile and
+// table vectors, which live as long as the plan.
 pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream_) {
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     std::lock_guard<std::mutex> lock(plan->mu);
@@ -414,20 +415,30 @@ pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream_) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     if (!plan->d_mem) {
-        const size_t n = plan->staged.bytes.size();
-        e = hipMalloc(&plan->d_mem, n);
+        const Problem &p = plan->prob;
+        const Staged &stg = plan->staged;
+        e = hipMalloc(&plan->d_mem, stg.total);
         if (e != hipSuccess) {
             plan->d_mem = nullptr;
             return hip_fail(e, "hipMalloc (plan metadata)");
         }
-        e = hipMemcpyAsync(plan->d_mem, plan->staged.bytes.data(), n, hipMemcpyHostToDevice,
-                           stream);
-        if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync (plan metadata)");
-        hipEvent_t ev;
-        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
-        e = hipEventRecord(ev, stream);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+        uint8_t *d = static_cast<uint8_t *>(plan->d_mem);
+        if (!p.tiles.empty())
+            e = hipMemcpyAsync(d + stg.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(DevTile),
+                               hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess && !p.cs.empty())
+            e = hipMemcpyAsync(d + stg.off_cs, p.cs.data(), p.cs.size() * sizeof(double),
+                               hipMemcpyHostToDevice, stream);
+        hipEvent_t ev = nullptr;
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(ev, stream);
+        if (e != hipSuccess) {
+            if (ev) (void)hipEventDestroy(ev);
+            (void)hipStreamSynchronize(stream);  // nothing may still read or write d_mem
+            (void)hipFree(plan->d_mem);
+            plan->d_mem = nullptr;
+            return hip_fail(e, "plan metadata upload");
+        }
         plan->upload_event = ev;
         plan->device = dev;
         return PIC_OK;
@@ -437,6 +448,75 @@ pic_status ensure_device_plan(struct ::pic_plan *plan, void *stream_) {
                     plan->device, dev);
     e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(plan->upload_event), 0);
     if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    return PIC_OK;
+}
+
+pic_status plan_blob(struct ::pic_plan *plan, int64_t key, void *stream_,
+                     const std::function<void(DevBlob &)> &make, const DevBlob **out) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    auto it = plan->blobs.find(key);
+    if (it == plan->blobs.end()) {
+        DevBlob b;
+        try {
+            make(b);
+        } catch (const std::bad_alloc &) {
+            return fail(PIC_ERR_NOMEM, "out of host memory (attention metadata)");
+        }
+        const size_t n = std::max<size_t>(b.host.size(), 16);
+        b.host.resize(n);
+        hipError_t e = hipMalloc(&b.dev, n);
+        if (e != hipSuccess) return hip_fail(e, "hipMalloc (attention metadata)");
+        hipEvent_t ev = nullptr;
+        e = hipMemcpyAsync(b.dev, b.host.data(), n, hipMemcpyHostToDevice, stream);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(ev, stream);
+        if (e != hipSuccess) {
+            if (ev) (void)hipEventDestroy(ev);
+            (void)hipStreamSynchronize(stream);
+            (void)hipFree(b.dev);
+            return hip_fail(e, "attention metadata upload");
+        }
+        b.ready = ev;
+        it = plan->blobs.emplace(key, std::move(b)).first;
+    }
+    const hipError_t e = hipStreamWaitEvent(stream, static_cast<hipEvent_t>(it->second.ready), 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent");
+    *out = &it->second;  // map nodes never move, and blobs are never erased before the plan
+    return PIC_OK;
+}
+
+pic_status call_workspace(size_t bytes, void *stream, void **out) {
+    *out = nullptr;
+    const hipError_t e = hipMallocAsync(out, std::max<size_t>(bytes, 256),
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        *out = nullptr;
+        (void)hipGetLastError();
+        return hip_fail(e, "hipMallocAsync (attention workspace)");
+    }
+    return PIC_OK;
+}
+
+pic_status release_workspace(void *ptr, void *stream) {
+    if (!ptr) return PIC_OK;
+    const hipError_t e = hipFreeAsync(ptr, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipFreeAsync (attention workspace)");
+    return PIC_OK;
+}
+
+pic_status note_use(struct ::pic_plan *plan, void *stream) {
+    std::lock_guard<std::mutex> lock(plan->mu);
+    hipEvent_t ev = nullptr;
+    for (auto &u : plan->uses)
+        if (u.first == stream) ev = static_cast<hipEvent_t>(u.second);
+    if (!ev) {
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
+        plan->uses.emplace_back(stream, ev);
+    }
+    const hipError_t e = hipEventRecord(ev, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
     return PIC_OK;
 }
 
@@ -479,7 +559,7 @@ pic_status run_staged(const Problem &p, const KArgs &views, int32_t layer_begin,
                       hipStream_t stream, const char *what) {
     if (p.tiles.empty() || n_layers == 0) return PIC_OK;
     const Staged stg = stage(p);
-    const size_t n = stg.bytes.size();
+    const size_t n = stg.total;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
@@ -514,7 +594,7 @@ pic_status run_staged(const Problem &p, const KArgs &views, int32_t layer_begin,
             }
             slot.cap = cap;
         }
-        std::memcpy(slot.host, stg.bytes.data(), n);
+        write_staged(p, stg, static_cast<uint8_t *>(slot.host));
         e = hipMallocAsync(&dmem, n, stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();  // clear it
@@ -603,7 +683,7 @@ pic_status pic_stitch(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_vi
     a.layer_begin = layer_begin;
     const hipError_t e = launch(p, a, layer_end - layer_begin, stream);
     if (e != hipSuccess) return hip_fail(e, "stitch kernel launch");
-    return PIC_OK;
+    return note_use(plan, stream_);
 }
 
 pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *rope,
@@ -698,21 +778,28 @@ pic_status pic_stream_copy(void *dst, const void *src, int64_t nbytes, void *str
 void pic_plan_destroy(pic_plan_t *plan) {
     using namespace pic;
     if (!plan || plan->magic != kPlanMagic) return;
+    plan->magic = kDeadMagic;
     if (plan->d_mem) {
         int cur = -1;
         (void)hipGetDevice(&cur);
         if (cur != plan->device) (void)hipSetDevice(plan->device);
-        (void)hipDeviceSynchronize();
-        (void)hipFree(plan->d_mem);
-        if (plan->d_work) (void)hipFree(plan->d_work);
-        if (plan->d_latent) (void)hipFree(plan->d_latent);
-        if (plan->d_bnd) (void)hipFree(plan->d_bnd);
-        if (plan->d_gqa) (void)hipFree(plan->d_gqa);
-        if (plan->upload_event)
+        // the plan's own work only: the last use on every stream it ran on
+        for (auto &u : plan->uses) {
+            (void)hipEventSynchronize(static_cast<hipEvent_t>(u.second));
+            (void)hipEventDestroy(static_cast<hipEvent_t>(u.second));
+        }
+        for (auto &kv : plan->blobs) {
+            (void)hipEventSynchronize(static_cast<hipEvent_t>(kv.second.ready));
+            (void)hipEventDestroy(static_cast<hipEvent_t>(kv.second.ready));
+            (void)hipFree(kv.second.dev);
+        }
+        if (plan->upload_event) {
+            (void)hipEventSynchronize(static_cast<hipEvent_t>(plan->upload_event));
             (void)hipEventDestroy(static_cast<hipEvent_t>(plan->upload_event));
+        }
+        (void)hipFree(plan->d_mem);
         if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
     }
-    plan->magic = kDeadMagic;
     delete plan;
 }
 
