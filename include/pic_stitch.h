@@ -273,6 +273,29 @@ pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *
                               int32_t layer_begin, int32_t layer_end, void *stream);
 
 /*
+ * pic_rotate_inplace_noalloc -- pic_rotate_inplace for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, the same kernels
+ * and the same result, with nothing allocated by the call.  The tiles and
+ * shift tables, which pic_rotate_inplace stages in stream-ordered device
+ * memory, are written by small fill kernels (their bytes carried in the
+ * kernel arguments) into a static device array of 4 MiB that each device
+ * holds until the process ends; its address is taken once per device, on
+ * the first call with that device current.
+ * Limit: the staged metadata (32 bytes per tile of at most 16 tokens, plus
+ * rope_dim * 8 bytes per distinct nonzero delta, each part padded to 256
+ * bytes) must fit in 4 MiB, else PIC_ERR_RANGE before anything is enqueued
+ * (e.g. 64 segments of 2032 turned tokens with rope_dim 128 stage 318 KiB).
+ * Every call on a device shares that array: calls ordered on one stream
+ * are safe; calls that may overlap on one device (different streams) race.
+ * Errors otherwise as pic_rotate_inplace.
+ */
+pic_status pic_rotate_inplace_noalloc(const pic_kv_shape *shape, const pic_rope_config *rope,
+                                      const pic_kv_view *buf, int64_t buf_tokens,
+                                      const pic_segment *segments, int32_t n_segments,
+                                      int32_t layer_begin, int32_t layer_end, void *stream);
+
+/*
  * One segment of a paged KV buffer for pic_rotate_paged.  Token t of the
  * segment (t in [0, length)) sits at logical position first + t of the
  * segment's block table: slot (first + t) % page_size of physical page

@@ -31,7 +31,8 @@ EXPORTS = ("pic_plan", "pic_stitch", "pic_rotate_inplace", "pic_rotate_paged", "
            "pic_attend_latent",
            "pic_attend_boundary", "pic_plan_info",
            "pic_plan_ranges", "pic_plan_destroy", "pic_registry_create", "pic_registry_add",
-           "pic_registry_destroy", "pic_match", "pic_stream_copy", "pic_last_error")
+           "pic_registry_destroy", "pic_match", "pic_stream_copy", "pic_rotate_inplace_noalloc",
+           "pic_last_error")
 FP_KINDS = {"xxh64": 0, "sha256": 1}
 
 
@@ -192,6 +193,8 @@ def _configure(lib):
     lib.pic_rotate_inplace.argtypes = [P(KvShape), P(RopeConfig), P(KvView), C.c_int64,
                                        P(SegmentC), C.c_int32, C.c_int32, C.c_int32,
                                        C.c_void_p]
+    lib.pic_rotate_inplace_noalloc.restype = C.c_int
+    lib.pic_rotate_inplace_noalloc.argtypes = lib.pic_rotate_inplace.argtypes
     lib.pic_rotate_paged.restype = C.c_int
     lib.pic_rotate_paged.argtypes = [P(KvShape), P(RopeConfig), P(KvView), C.c_int32, C.c_int64,
                                      P(PageSegmentC), C.c_int32, C.c_int32, C.c_int32,
@@ -626,10 +629,14 @@ def attend_boundary(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: i
 
 def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
                    style: str = "half", rope_offset: int = 0, layer_begin: int = 0,
-                   layer_end: Optional[int] = None, inv_freq=None, stream=None, library=None):
+                   layer_end: Optional[int] = None, inv_freq=None, stream=None, library=None,
+                   noalloc: bool = False):
     """Enqueue pic_rotate_inplace on buf_k [L][T][H][D]; segments are
-    (token_start, length, delta, recompute_k) tuples or objects."""
+    (token_start, length, delta, recompute_k) tuples or objects.  With
+    noalloc, pic_rotate_inplace_noalloc (nothing allocated; calls on one
+    device that may overlap race)."""
     lib = load_library(library)
+    fn = lib.pic_rotate_inplace_noalloc if noalloc else lib.pic_rotate_inplace
     L, T, H, D = buf_k.shape
     le = L if layer_end is None else layer_end
     shape, rope, keep = _shape_and_rope(_dtype_name(buf_k), L, H, D, rope_offset, rope_dim,
@@ -639,9 +646,8 @@ def rotate_inplace(buf_k, segments: Sequence, *, rope_dim: int, theta: float,
         sarr[i] = SegmentC(int(_get(s, "token_start", 0)), int(_get(s, "delta", 2)),
                            int(_get(s, "length", 1)), int(_get(s, "recompute_k", 3)))
     view = _view(buf_k, None, "buf")
-    _check(lib.pic_rotate_inplace(C.byref(shape), C.byref(rope), C.byref(view), T, sarr,
-                                  len(segments), layer_begin, le, _stream_of(buf_k, stream)),
-           lib)
+    _check(fn(C.byref(shape), C.byref(rope), C.byref(view), T, sarr, len(segments),
+              layer_begin, le, _stream_of(buf_k, stream)), lib)
 
 
 def stream_copy(dst, src, stream=None, library=None):

@@ -552,6 +552,74 @@ PinnedRing *pinned_ring(int device) {
     return r.get();
 }
 
+// Kernel arguments of a per-call problem whose metadata sits at dmem, with
+// the pointers and strides of `views`.
+KArgs with_views(const Problem &p, const KArgs &views, const uint8_t *dmem, const Staged &stg,
+                 int32_t layer_begin) {
+    KArgs a = args_for(p, dmem, stg);
+    a.src_k = views.src_k;
+    a.src_v = views.src_v;
+    a.dst_k = views.dst_k;
+    a.dst_v = views.dst_v;
+    a.s_layer = views.s_layer;
+    a.s_tok = views.s_tok;
+    a.s_head = views.s_head;
+    a.s_page = views.s_page;
+    a.src_paged = views.src_paged;
+    a.d_layer = views.d_layer;
+    a.d_tok = views.d_tok;
+    a.d_head = views.d_head;
+    a.d_page = views.d_page;
+    a.d_req = views.d_req;
+    a.layer_begin = layer_begin;
+    return a;
+}
+
+// ------------------------------------------------- the no-allocation path
+//
+// pic_rotate_inplace_noalloc stages its tiles and shift tables in this
+// file-scope array instead of stream-ordered device memory.  In host code
+// the name `scratch` is a host-side stand-in, not a device address: the
+// device address is taken once per device with hipGetSymbolAddress (that
+// device current) and used wherever host code needs the array.  Every call
+// on a device shares its copy; calls that overlap on one device (different
+// streams) race.
+constexpr size_t kScratchBytes = size_t{4} << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The metadata reaches the array through kernel arguments, kFillBytes per
+// launch: the runtime copies arguments at launch, so no host buffer has to
+// outlive the call and nothing is allocated.
+constexpr int kFillBytes = 3584;
+struct FillArgs {
+    uint4 *dst;
+    uint32_t n16;  // 16-byte words in `words`
+    uint32_t pad;
+    uint4 words[kFillBytes / 16];
+};
+
+__global__ void __launch_bounds__(256) scratch_fill_kernel(const FillArgs a) {
+    for (uint32_t i = threadIdx.x; i < a.n16; i += 256) a.dst[i] = a.words[i];
+}
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on device `dev` (current), taken once.
+pic_status scratch_address(int dev, uint8_t **out) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    if (dev < 0 || dev >= kMaxDevices) return fail(PIC_ERR_DEVICE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return hip_fail(e, "hipGetSymbolAddress (scratch)");
+        addr[dev] = ptr;
+    }
+    *out = static_cast<uint8_t *>(addr[dev]);
+    return PIC_OK;
+}
+
 // Stage a per-call problem's tiles and shift tables in stream-ordered device
 // memory (freed on the same stream once the kernel has run) and launch it
 // over n_layers layers from layer_begin; views holds the pointers and strides.
@@ -608,23 +676,8 @@ pic_status run_staged(const Problem &p, const KArgs &views, int32_t layer_begin,
             return fail(PIC_ERR_DEVICE, "%s: hipMemcpyAsync (metadata): %s", what, hipGetErrorString(e));
         }
     }
-    KArgs a = args_for(p, static_cast<const uint8_t *>(dmem), stg);
-    a.src_k = views.src_k;
-    a.src_v = views.src_v;
-    a.dst_k = views.dst_k;
-    a.dst_v = views.dst_v;
-    a.s_layer = views.s_layer;
-    a.s_tok = views.s_tok;
-    a.s_head = views.s_head;
-    a.s_page = views.s_page;
-    a.src_paged = views.src_paged;
-    a.d_layer = views.d_layer;
-    a.d_tok = views.d_tok;
-    a.d_head = views.d_head;
-    a.d_page = views.d_page;
-    a.d_req = views.d_req;
-    a.layer_begin = layer_begin;
-    e = launch(p, a, n_layers, stream);
+    e = launch(p, with_views(p, views, static_cast<const uint8_t *>(dmem), stg, layer_begin),
+               n_layers, stream);
     const hipError_t e2 = hipFreeAsync(dmem, stream);
     if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s kernel launch: %s", what, hipGetErrorString(e));
     if (e2 != hipSuccess)
@@ -713,6 +766,70 @@ pic_status pic_rotate_inplace(const pic_kv_shape *shape, const pic_rope_config *
     v.s_head = v.d_head = buf->head_stride;
     return run_staged(p, v, layer_begin, layer_end - layer_begin, static_cast<hipStream_t>(stream_),
                       "rotate");
+}
+
+pic_status pic_rotate_inplace_noalloc(const pic_kv_shape *shape, const pic_rope_config *rope,
+                                      const pic_kv_view *buf, int64_t buf_tokens,
+                                      const pic_segment *segments, int32_t n_segments,
+                                      int32_t layer_begin, int32_t layer_end, void *stream_) {
+    using namespace pic;
+    clear_error();
+    Problem p;
+    pic_status st;
+    try {
+        st = build_inplace(shape, rope, buf_tokens, segments, n_segments, &p);
+    } catch (const std::bad_alloc &) {
+        return fail(PIC_ERR_NOMEM, "out of host memory");
+    }
+    if (st) return st;
+    if (layer_begin < 0 || layer_begin > layer_end || layer_end > p.shape.num_layers)
+        return fail(PIC_ERR_INVALID_ARG, "layer range [%d, %d) outside [0, %d)", layer_begin,
+                    layer_end, p.shape.num_layers);
+    st = check_view(buf, p.u.vec, false, "buf");
+    if (st) return st;
+    if (!slot_offsets_fit(p, buf->token_stride, buf->head_stride))
+        return fail(PIC_ERR_RANGE, "the view's token/head strides span 2^31 elements or more "
+                    "within one step");
+    const Staged stg = stage(p);
+    if (stg.total > kScratchBytes)
+        return fail(PIC_ERR_RANGE, "%zu bytes of tiles and shift tables (%zu tiles, %zu tables) "
+                    "exceed the %zu-byte static scratch", stg.total, p.tiles.size(),
+                    p.cs.size() / std::max(1, p.rope_dim), kScratchBytes);
+    if (p.tiles.empty() || layer_begin == layer_end) return PIC_OK;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    uint8_t *dmem = nullptr;
+    st = scratch_address(dev, &dmem);
+    if (st) return st;
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    FillArgs fa{};
+    for (size_t off = 0; off < stg.total; off += kFillBytes) {
+        const size_t n = std::min<size_t>(kFillBytes, stg.total - off);  // a multiple of 16
+        std::memset(fa.words, 0, sizeof fa.words);
+        auto put = [&](size_t at, const void *src, size_t len) {  // [at, at + len) of the layout
+            const size_t lo = std::max(at, off), hi = std::min(at + len, off + n);
+            if (lo < hi)
+                std::memcpy(reinterpret_cast<uint8_t *>(fa.words) + (lo - off),
+                            static_cast<const uint8_t *>(src) + (lo - at), hi - lo);
+        };
+        put(stg.off_tiles, p.tiles.data(), p.tiles.size() * sizeof(DevTile));
+        put(stg.off_cs, p.cs.data(), p.cs.size() * sizeof(double));
+        fa.dst = reinterpret_cast<uint4 *>(dmem + off);
+        fa.n16 = static_cast<uint32_t>(n / 16);
+        hipLaunchKernelGGL(scratch_fill_kernel, dim3(1), dim3(256), 0, stream, fa);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch fill launch");
+    }
+    KArgs v{};
+    v.src_k = buf->k;
+    v.dst_k = buf->k;
+    v.s_layer = v.d_layer = buf->layer_stride;
+    v.s_tok = v.d_tok = buf->token_stride;
+    v.s_head = v.d_head = buf->head_stride;
+    e = launch(p, with_views(p, v, dmem, stg, layer_begin), layer_end - layer_begin, stream);
+    if (e != hipSuccess) return hip_fail(e, "rotate kernel launch");
+    return PIC_OK;
 }
 
 pic_status pic_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *rope,

@@ -191,3 +191,21 @@ def test_runtime_guard_on_this_process():
     """The package imported here (with torch) maps at most one runtime."""
     from position_independent_kv_stitch_amd import _binding as B
     assert len(B.hip_runtimes()) <= 1
+
+
+def test_noalloc_refuses_metadata_beyond_its_array():
+    """pic_rotate_inplace_noalloc checks the size of its staged metadata
+    against its 4 MiB array before any device work: 140,000 one-token
+    segments (32-byte tiles) need more, and are refused with PIC_ERR_RANGE
+    (the view is a dummy: nothing is dereferenced)."""
+    lib = B.load_library()
+    shape, rope, keep = B._shape_and_rope("bf16", 1, 8, 128, 0, 128, "half", 1e6, False, None)
+    n = 140_000
+    segs = (B.SegmentC * n)()
+    for i in range(n):
+        segs[i] = B.SegmentC(2 * i, 1, 1, 0)
+    view = B.KvView(0x10000, None, 0, 8 * 128, 128, 0, 0)
+    st = lib.pic_rotate_inplace_noalloc(C.byref(shape), C.byref(rope), C.byref(view), 2 * n, segs,
+                                        n, 0, 1, None)
+    assert st == B.PIC_ERR_RANGE, lib.pic_last_error()
+    assert b"static scratch" in lib.pic_last_error()
