@@ -288,7 +288,7 @@ def setup_attend(name, torch, pic):
     return {"wl": wl, "step": run(plan), "plain_step": run(plain),
             "bytes": info["context_tokens"] * 2 * row * L,
             "token_layers": info["context_tokens"] * L, "launches": L,
-            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "gqa_tile_kernel + gqa_combine_kernel (one pic_attend)",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "gqa_tile_kernel + gqa_combine_kernel (one pic_attend)", "counters": "gqa",
             "plan": plan, "plans": [plain], "info": info, "config": cfg}
 
 
@@ -320,7 +320,7 @@ def setup_attend_mla(name, torch, pic):
            "parallelism": "single-gpu"}
     return {"wl": wl, "step": step, "bytes": info["context_tokens"] * row * L,
             "token_layers": info["context_tokens"] * L, "launches": L, "flops": flops,
-            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)", "counters": "mla",
             "plan": plan, "info": info, "config": cfg}
 
 
@@ -365,7 +365,7 @@ def setup_boundary(name, torch, pic):
            "sink_tokens": 4, "sink_bias": -15.0, "parallelism": "single-gpu"}
     return {"wl": wl, "step": step, "bytes": (ctx * row_bytes + qo_bytes) * L, "token_layers": n * L,
             "launches": L, "flops": flops,
-            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "bnd_block_kernel<half> + bnd_combine_kernel (one pic_attend_boundary)",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "bnd_block_kernel<half> + bnd_combine_kernel (one pic_attend_boundary)", "counters": "bnd",
             "plan": plan, "config": cfg}
 
 
