@@ -440,11 +440,15 @@ pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *pool, const pi
 
 /*
  * LegoLink's boundary reconnection (EPIC Guide, "2. Sparse Cross-Block
- * Reconnection"): the first boundary_k tokens of every chunk placed after
- * position 0 attend across the chunk boundary.  Boundary row b is token j <
- * min(boundary_k, length) of such an entry (entries request by request, in
- * each request's order; pic_plan_ranges lists them); it attends causally to
- * positions [0, dst_offset + j] of its request:
+ * Reconnection"): the boundary tokens of relocated chunks attend across the
+ * chunk boundary.  By default (rows NULL) boundary row b is token j <
+ * min(boundary_k, length) of an entry placed after position 0 (entries
+ * request by request, in each request's order; pic_plan_ranges lists them).
+ * The page leaves open how the "top-k" boundary tokens are chosen, so a
+ * caller may instead name them: rows[b] = {entry, j}, entry indexed in plan
+ * order (request by request, as pic_plan_ranges lists them), j < its
+ * length.  Either way row b attends causally to positions
+ * [0, dst_offset + j] of its request:
  *   out[b][jq] = sum_p w_p V_p / sum_p w_p,  w_p = exp(scale * q[b][jq] . K_p + b_p)
  * with the rows pic_attend reads (chunk keys turned by the entry's delta on
  * load, rounded to bf16 as pic_stitch stores them; other positions from the
@@ -464,21 +468,36 @@ typedef struct pic_attend_boundary_args {
                                listing: 16) */
     int32_t sink_tokens;    /* LegoLink damping (0 = off) */
     float sink_bias;
+    const int32_t *rows;    /* host [n_rows][2] {entry, token}, or NULL: the first
+                               boundary_k tokens of every relocated entry */
+    int32_t n_rows;         /* rows given (ignored when rows is NULL) */
+    int32_t reserved;       /* must be 0 */
 } pic_attend_boundary_args;
 
 /*
- * pic_attend_boundary -- enqueue the boundary reconnection of every
- * relocated entry of a plan at one layer (see above).  All boundary rows of
- * a request read its context together.  bf16 plans with K and V head rows
- * of 128 dims and a rotary slice on 8-dim pieces (PIC_ERR_INVALID_ARG,
- * PIC_ERR_ALIGN); q rows 16-byte aligned (PIC_ERR_ALIGN); every boundary
- * row's positions inside its request's context and mapped pages
- * (PIC_ERR_RANGE; also for more than 65535 requests with relocated entries
- * or a launch beyond 2^31 threads); in-place plans refused
- * (PIC_ERR_STATE).  A plan without relocated entries enqueues nothing.  The
- * work items for a launch shape (boundary_k and the device's CU count) are
- * built on the host and uploaded once per plan; workspace and metadata as
- * for pic_attend: calls on one plan from several streams may overlap.
+ * pic_attend_boundary -- enqueue the boundary reconnection of a plan at one
+ * layer, for the first boundary_k tokens of every relocated entry or for
+ * the rows the caller names (see above).  All boundary rows of a request
+ * read its context together.
+ * Requirements: bf16 plans with K and V head rows of 128 dims and a rotary
+ * slice on 8-dim pieces (PIC_ERR_INVALID_ARG, PIC_ERR_ALIGN); q rows
+ * 16-byte aligned (PIC_ERR_ALIGN); every boundary row's positions inside
+ * its request's context and mapped pages (PIC_ERR_RANGE; also for more
+ * than 65535 requests with boundary rows or a launch beyond 2^31 threads);
+ * in-place plans refused (PIC_ERR_STATE).
+ * Without rows: boundary_k >= 1 (PIC_ERR_INVALID_ARG); a plan without
+ * relocated entries enqueues nothing; the work items for a launch shape
+ * (boundary_k and the device's CU count) are built on the host and uploaded
+ * once per plan.
+ * With rows: n_rows >= 0 and reserved 0 (PIC_ERR_INVALID_ARG); rows come
+ * request by request -- the rows of one request together, requests in
+ * ascending order, any order and repeats within a request -- else
+ * PIC_ERR_INVALID_ARG; an entry outside the plan or a token outside its
+ * entry is PIC_ERR_RANGE; boundary_k is ignored.  The rows' work items are
+ * built and uploaded per call (stream-ordered memory filled from pinned
+ * staging), since a selection usually changes from call to call.
+ * Workspace and metadata as for pic_attend: calls on one plan from several
+ * streams may overlap.
  */
 pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *pool, const pic_kv_view *cache,
                                const pic_attend_boundary_args *args, void *stream);

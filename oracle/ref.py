@@ -498,28 +498,42 @@ def attend_latent(wl, pool_k, cache_k, q, layer, scale=None, sink_tokens=0, sink
     return out
 
 
-def boundary_rows(wl, boundary_k):
+def boundary_rows(wl, boundary_k, rows=None):
     """The boundary rows of a plan, in order: (request, entry index, token j,
-    position) for every entry placed after position 0 and j < min(k, length),
-    requests in order, each request's entries in the order given."""
-    rows = []
+    position).  Without `rows`: every entry placed after position 0 and
+    j < min(k, length), requests in order, each request's entries in the
+    order given.  With `rows`: the given (entry, token) pairs, entries
+    numbered across the requests in plan order (request by request), in the
+    order given; a token outside its entry raises ValueError."""
+    if rows is not None:
+        flat = [(r, i, e) for r, rq in enumerate(wl.requests) for i, e in enumerate(rq.entries)]
+        out = []
+        for ent, j in rows:
+            r, i, e = flat[int(ent)]
+            if not 0 <= int(j) < e.length:
+                raise ValueError(f"token {j} outside entry {ent} of length {e.length}")
+            out.append((r, i, int(j), e.dst_offset + int(j)))
+        return out
+    out = []
     for r, rq in enumerate(wl.requests):
         for i, e in enumerate(rq.entries):
             if e.dst_offset > 0:
                 for j in range(min(boundary_k, e.length)):
-                    rows.append((r, i, j, e.dst_offset + j))
-    return rows
+                    out.append((r, i, j, e.dst_offset + j))
+    return out
 
 
 def attend_boundary(wl, pool_k, pool_v, cache_k, cache_v, q, layer, boundary_k, scale=None,
-                    sink_tokens=0, sink_bias=0.0, layer_base=0, dtype=None):
+                    sink_tokens=0, sink_bias=0.0, layer_base=0, dtype=None, rows=None):
     """LegoLink's boundary reconnection (EPIC Guide, "2. Sparse Cross-Block
     Reconnection"), in fp64: boundary token j of every entry placed after
     position 0 (its first boundary_k tokens) attends causally to every
     position of its request up to and including its own, p = dst_offset + j:
     the preceding chunks and prefix (the cross-chunk part) and its own
-    chunk's earlier tokens.  q: [boundary rows][q heads][row_dim] in
-    boundary_rows() order; returns [boundary rows][q heads][row_dim].
+    chunk's earlier tokens.  With `rows`, the given (entry, token) pairs
+    instead (any token of any entry, each attending causally up to its own
+    position).  q: [boundary rows][q heads][row_dim] in boundary_rows()
+    order; returns [boundary rows][q heads][row_dim].
 
     The context rows are those this oracle's stitch leaves (chunk keys turned
     by the entry's shift and rounded to the storage type; dtype 'f64': not
@@ -532,7 +546,7 @@ def attend_boundary(wl, pool_k, pool_v, cache_k, cache_v, q, layer, boundary_k, 
     G = Hq // H
     sc = D ** -0.5 if scale is None else scale
     dt = dtype or wl.dtype
-    rows = boundary_rows(wl, boundary_k)
+    rows = boundary_rows(wl, boundary_k, rows)
     out = np.zeros((len(rows), Hq, D))
     pk, pv = pool_k[li:li + 1], pool_v[li:li + 1]
     if dt == "f64":

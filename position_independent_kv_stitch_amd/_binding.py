@@ -89,7 +89,8 @@ class BoundaryArgs(C.Structure):
                 ("out", C.c_void_p), ("out_row_stride", C.c_int64),
                 ("out_head_stride", C.c_int64), ("num_q_heads", C.c_int32),
                 ("layer", C.c_int32), ("scale", C.c_float), ("boundary_k", C.c_int32),
-                ("sink_tokens", C.c_int32), ("sink_bias", C.c_float)]
+                ("sink_tokens", C.c_int32), ("sink_bias", C.c_float),
+                ("rows", C.POINTER(C.c_int32)), ("n_rows", C.c_int32), ("reserved", C.c_int32)]
 
 
 class Geom(C.Structure):
@@ -584,15 +585,25 @@ def boundary_row_count(plan: Plan, boundary_k: int) -> int:
 
 def attend_boundary(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: int,
                     boundary_k: int = 16, out=None, scale: Optional[float] = None,
-                    sink_tokens: int = 0, sink_bias: float = 0.0, stream=None):
+                    sink_tokens: int = 0, sink_bias: float = 0.0, stream=None, rows=None):
     """Enqueue pic_attend_boundary (LegoLink boundary reconnection) at `layer`.
-    q: bf16 [boundary rows][q heads][row_dim] (rows as boundary_row_count
-    enumerates them); tensors as for attend().  Returns out, fp32 with q's
-    shape."""
+    q: bf16 [boundary rows][q heads][row_dim]: the first boundary_k tokens
+    of every relocated entry (as boundary_row_count enumerates them), or,
+    with `rows`, the given (entry, token) pairs (entries in plan order, the
+    rows of one request together, requests ascending); tensors as for
+    attend().  Returns out, fp32 with q's shape."""
     torch = _torch()
     if q.dtype != torch.bfloat16 or q.dim() != 3 or q.stride(-1) != 1:
         raise TypeError("q must be bf16 [boundary rows][q heads][row_dim]")
-    n = boundary_row_count(plan, boundary_k)
+    row_arr = None
+    if rows is not None:
+        row_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 2))
+        if row_arr.size and (row_arr.min() < -2 ** 31 or row_arr.max() >= 2 ** 31):
+            raise PicError(PIC_ERR_RANGE, "row entries and tokens must fit int32")
+        row_arr = row_arr.astype(np.int32)
+        n = len(row_arr)
+    else:
+        n = boundary_row_count(plan, boundary_k)
     if q.shape[0] != n or q.shape[2] != plan.row_dim:
         raise ValueError(f"q must have {n} boundary rows of {plan.row_dim} dims")
     if out is None:
@@ -620,7 +631,9 @@ def attend_boundary(plan: Plan, pool_k, pool_v, cache_k, cache_v, q, *, layer: i
     a = BoundaryArgs(q.data_ptr(), q.stride(0), q.stride(1), out.data_ptr(), out.stride(0),
                      out.stride(1), q.shape[1], layer,
                      float(plan.row_dim ** -0.5 if scale is None else scale), int(boundary_k),
-                     int(sink_tokens), float(sink_bias))
+                     int(sink_tokens), float(sink_bias),
+                     row_arr.ctypes.data_as(C.POINTER(C.c_int32)) if row_arr is not None else None,
+                     n if row_arr is not None else 0, 0)
     lib = plan._lib
     _check(lib.pic_attend_boundary(plan.handle, C.byref(pv), C.byref(cv), C.byref(a),
                                    _stream_of(q, stream)), lib)

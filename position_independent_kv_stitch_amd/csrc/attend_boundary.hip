@@ -695,20 +695,19 @@ struct BndMap {
     int32_t n_items = 0, n_reqs = 0, n_rows = 0, max_req_rows = 0;
 };
 
-// A relocated entry (dst_offset > 0): request, dst_offset, length.
-struct Reloc {
+// The boundary rows of one request, in the caller's row order: the last
+// context position each row sees.
+struct ReqRows {
     int32_t request;
-    int64_t dst;
-    int32_t length;
+    std::vector<int32_t> limit;
 };
 
-// Requests with relocated entries, in order; each request's context [0, L),
-// L = the last boundary position + 1, is cut into ceil(L / S) items of
+// Requests with boundary rows, in order; each request's context [0, L),
+// L = its last boundary position + 1, is cut into ceil(L / S) items of
 // about equal length, S the total over `target` (at least one step, at most
 // kMaxItems items per request).  Boundary rows are numbered request by
-// request, entry by entry, token by token: the order of the caller's q.
-BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t k,
-                     int64_t target) {
+// request in the order given: the order of the caller's q.
+BndMap build_bnd_map(const Problem &p, const std::vector<ReqRows> &groups, int64_t target) {
     std::vector<AttnTile> tiles;
     std::vector<AttnBlock> blocks;
     std::vector<int32_t> bpos;
@@ -716,17 +715,9 @@ BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t 
     std::vector<BndItem> items;
     std::vector<BndReq> reqs;
     std::vector<int32_t> limit;
-    // group the entries by request (they come request by request)
-    std::vector<std::pair<size_t, size_t>> groups;
-    for (size_t i = 0; i < order.size(); i++) {
-        if (groups.empty() || order[groups.back().first].request != order[i].request)
-            groups.push_back({i, i});
-        groups.back().second = i + 1;
-    }
-    auto ctx_of = [&](const std::pair<size_t, size_t> &gr) {
+    auto ctx_of = [&](const ReqRows &gr) {
         int64_t L = 0;
-        for (size_t i = gr.first; i < gr.second; i++)
-            L = std::max<int64_t>(L, order[i].dst + std::min(k, order[i].length));
+        for (int32_t x : gr.limit) L = std::max<int64_t>(L, int64_t{x} + 1);
         return L;
     };
     int64_t total = 0;
@@ -734,11 +725,9 @@ BndMap build_bnd_map(const Problem &p, const std::vector<Reloc> &order, int32_t 
     const int64_t per = std::max<int64_t>(kStepPos, (total + target - 1) / target);
     int32_t max_rows = 0;
     for (const auto &gr : groups) {
-        const int32_t r = order[gr.first].request;
+        const int32_t r = gr.request;
         BndReq R{static_cast<int32_t>(limit.size()), 0, static_cast<int32_t>(items.size()), 0};
-        for (size_t i = gr.first; i < gr.second; i++)
-            for (int32_t j = 0; j < std::min(k, order[i].length); j++)
-                limit.push_back(static_cast<int32_t>(order[i].dst + j));
+        limit.insert(limit.end(), gr.limit.begin(), gr.limit.end());
         R.n_tok = static_cast<int32_t>(limit.size()) - R.row0;
         max_rows = std::max(max_rows, R.n_tok);
         const int64_t L = ctx_of(gr);
@@ -855,7 +844,10 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
         return fail(PIC_ERR_INVALID_ARG, "num_q_heads %d: need a multiple of %d, at most 8x",
                     args->num_q_heads, H);
     const int G = args->num_q_heads / H;
-    if (args->boundary_k < 1) return fail(PIC_ERR_INVALID_ARG, "boundary_k %d < 1", args->boundary_k);
+    if (args->reserved != 0) return fail(PIC_ERR_INVALID_ARG, "reserved must be 0");
+    if (!args->rows && args->boundary_k < 1)
+        return fail(PIC_ERR_INVALID_ARG, "boundary_k %d < 1", args->boundary_k);
+    if (args->rows && args->n_rows < 0) return fail(PIC_ERR_INVALID_ARG, "n_rows %d < 0", args->n_rows);
     if (args->layer < 0 || args->layer >= p.shape.num_layers)
         return fail(PIC_ERR_INVALID_ARG, "layer %d outside [0, %d)", args->layer,
                     p.shape.num_layers);
@@ -868,16 +860,47 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     st = check_view(cache, 8, true, "cache");
     if (st) return st;
 
-    // relocated entries (dst_offset > 0), request by request, in each
-    // request's order: the plan's boundaries [request, begin, end]
-    std::vector<Reloc> order;
-    for (size_t i = 0; i + 2 < p.bounds.size(); i += 3)
-        if (p.bounds[i + 1] > 0)
-            order.push_back(Reloc{static_cast<int32_t>(p.bounds[i]), p.bounds[i + 1],
-                                  static_cast<int32_t>(p.bounds[i + 2] - p.bounds[i + 1])});
-    for (const Reloc &e : order) {
-        const int32_t r = e.request;
-        const int64_t need = e.dst + std::min(args->boundary_k, e.length);
+    // the boundary rows, request by request: the last position each row
+    // sees.  Default: tokens j < k of every relocated entry (dst_offset > 0),
+    // in each request's entry order; else the caller's (entry, token) rows.
+    // The plan's boundaries are [request, begin, end] per entry.
+    std::vector<ReqRows> groups;
+    try {
+        const int64_t n_entries = static_cast<int64_t>(p.bounds.size() / 3);
+        auto add = [&](int32_t r, int64_t pos) {
+            if (groups.empty() || groups.back().request != r) groups.push_back(ReqRows{r, {}});
+            groups.back().limit.push_back(static_cast<int32_t>(pos));
+        };
+        if (args->rows) {
+            for (int32_t b = 0; b < args->n_rows; b++) {
+                const int32_t e = args->rows[2 * b], j = args->rows[2 * b + 1];
+                if (e < 0 || e >= n_entries)
+                    return fail(PIC_ERR_RANGE, "row %d: entry %d outside the plan's %lld entries", b, e,
+                                static_cast<long long>(n_entries));
+                const int32_t r = static_cast<int32_t>(p.bounds[3 * e]);
+                const int64_t dst = p.bounds[3 * e + 1], len = p.bounds[3 * e + 2] - dst;
+                if (j < 0 || j >= len)
+                    return fail(PIC_ERR_RANGE, "row %d: token %d outside entry %d of length %lld", b, j,
+                                e, static_cast<long long>(len));
+                if (!groups.empty() && r < groups.back().request)
+                    return fail(PIC_ERR_INVALID_ARG, "row %d: request %d after request %d (rows must "
+                                "come request by request)", b, r, groups.back().request);
+                add(r, dst + j);
+            }
+        } else {
+            for (int64_t e = 0; e < n_entries; e++) {
+                const int64_t dst = p.bounds[3 * e + 1], len = p.bounds[3 * e + 2] - dst;
+                if (dst <= 0) continue;
+                for (int64_t j = 0; j < std::min<int64_t>(args->boundary_k, len); j++)
+                    add(static_cast<int32_t>(p.bounds[3 * e]), dst + j);
+            }
+        }
+    } catch (const std::bad_alloc &) {
+        return fail(PIC_ERR_NOMEM, "out of host memory");
+    }
+    for (const ReqRows &gr : groups) {
+        const int32_t r = gr.request;
+        const int64_t need = int64_t{*std::max_element(gr.limit.begin(), gr.limit.end())} + 1;
         if (need > p.context[r])
             return fail(PIC_ERR_RANGE, "request %d: boundary rows beyond its context", r);
         if (p.context_bad_page[r] >= 0 &&
@@ -885,7 +908,7 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
             return fail(PIC_ERR_RANGE, "request %d: context page %d maps outside the cache", r,
                         p.context_bad_page[r]);
     }
-    if (order.empty()) return PIC_OK;
+    if (groups.empty()) return PIC_OK;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_);
     st = ensure_device_plan(plan, stream_);
@@ -893,12 +916,8 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     // items: about two rounds of the CU slots (one workgroup of 8 waves per
     // CU and KV head at a time)
     const int64_t target = std::max<int64_t>(1, 2 * static_cast<int64_t>(cu_count()) / H);
-    const int64_t key = (target << 32) | static_cast<uint32_t>(args->boundary_k);
     int TT = 1, n_sets = 1, row_slots = 0;
-    const DevBlob *blob = nullptr;
-    st = plan_blob(plan, blob_key(kBlobBoundary, key), stream_, [&](DevBlob &b) {
-        BndMap m = build_bnd_map(p, order, args->boundary_k, target);
-        b.host = std::move(m.bytes);
+    auto fill_blob = [&](DevBlob &b, BndMap &m) {
         b.off[0] = m.off_blocks;
         b.off[1] = m.off_bpos;
         b.off[2] = m.off_items;
@@ -908,8 +927,37 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
         b.n[0] = m.n_items;
         b.n[1] = m.n_reqs;
         b.n[2] = m.max_req_rows;
-    }, &blob);
-    if (st) return st;
+    };
+    const DevBlob *blob = nullptr;
+    DevBlob call_blob;       // the caller's rows: metadata of this call only
+    void *call_dev = nullptr;
+    if (args->rows) {
+        BndMap m;
+        try {
+            m = build_bnd_map(p, groups, target);
+        } catch (const std::bad_alloc &) {
+            return fail(PIC_ERR_NOMEM, "out of host memory");
+        }
+        fill_blob(call_blob, m);
+        st = stage_per_call(std::max<size_t>(m.bytes.size(), 16),
+                            [&](uint8_t *host) { std::memcpy(host, m.bytes.data(), m.bytes.size()); },
+                            stream_, &call_dev, "boundary rows");
+        if (st) return st;
+        call_blob.dev = call_dev;
+        blob = &call_blob;
+    } else {
+        const int64_t key = (target << 32) | static_cast<uint32_t>(args->boundary_k);
+        st = plan_blob(plan, blob_key(kBlobBoundary, key), stream_, [&](DevBlob &b) {
+            BndMap m = build_bnd_map(p, groups, target);
+            b.host = std::move(m.bytes);
+            fill_blob(b, m);
+        }, &blob);
+        if (st) return st;
+    }
+    auto release_call = [&]() {
+        if (call_dev) (void)hipFreeAsync(call_dev, stream);
+        call_dev = nullptr;
+    };
     const int32_t n_items = blob->n[0], n_reqs = blob->n[1], max_rows = blob->n[2];
     // rows of a request's KV head: tokens x G, in as few sets of 8 waves x TT
     // tiles as the registers allow, TT as small as they then permit
@@ -919,13 +967,18 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     TT = static_cast<int>((rows + int64_t{n_sets} * kWaves * 16 - 1) / (int64_t{n_sets} * kWaves * 16));
     row_slots = n_sets * kWaves * TT * 16;
     if ((static_cast<int64_t>(n_items) * H + 7) / 8 * 8 * n_sets >= (int64_t{1} << 31) / (64 * kWaves) ||
-        static_cast<int64_t>(n_reqs) * rows * H >= (int64_t{1} << 31) / 64 || n_reqs > 65535)
+        static_cast<int64_t>(n_reqs) * rows * H >= (int64_t{1} << 31) / 64 || n_reqs > 65535) {
+        release_call();
         return fail(PIC_ERR_RANGE, "boundary rows x context too large for one launch");
+    }
     const size_t need = static_cast<size_t>(n_items) * H * row_slots *
                         (static_cast<size_t>(kDim) + 2) * sizeof(float);
     void *work = nullptr;
     st = call_workspace(need, stream_, &work);
-    if (st) return st;
+    if (st) {
+        release_call();
+        return st;
+    }
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
     const uint8_t *bm = static_cast<const uint8_t *>(blob->dev);
     BndArgs a{};
@@ -987,6 +1040,7 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
 #undef PIC_BND_LAUNCH
         default:
             (void)release_workspace(work, stream_);
+            release_call();
             return fail(PIC_ERR_INVALID_ARG, "internal: row tiles per wave %d", TT);
     }
     hipError_t e = hipGetLastError();
@@ -998,6 +1052,7 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
         e = hipGetLastError();
     }
     st = release_workspace(work, stream_);
+    release_call();
     if (e != hipSuccess) return hip_fail(e, "boundary attention kernel launch");
     if (st) return st;
     return note_use(plan, stream_);

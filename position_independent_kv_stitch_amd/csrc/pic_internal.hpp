@@ -192,6 +192,12 @@ pic_status plan_blob(struct ::pic_plan *plan, int64_t key, void *stream,
 pic_status call_workspace(size_t bytes, void *stream, void **out);
 pic_status release_workspace(void *ptr, void *stream);
 
+// n bytes written by `fill` into pinned staging, copied ordered on `stream`
+// into fresh stream-ordered device memory *dmem (the caller frees it with
+// hipFreeAsync on the same stream after the launches that read it).
+pic_status stage_per_call(size_t n, const std::function<void(uint8_t *)> &fill, void *stream,
+                          void **dmem, const char *what);
+
 // Record that work reading the plan is enqueued on `stream` (the plan keeps
 // one event per stream it was used on; pic_plan_destroy waits for them).
 pic_status note_use(struct ::pic_plan *plan, void *stream);

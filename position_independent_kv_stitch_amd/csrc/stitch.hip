@@ -620,6 +620,64 @@ pic_status scratch_address(int dev, uint8_t **out) {
     return PIC_OK;
 }
 
+}  // namespace
+
+pic_status stage_per_call(size_t n, const std::function<void(uint8_t *)> &fill, void *stream_,
+                          void **dmem, const char *what) {
+    hipStream_t stream = static_cast<hipStream_t>(stream_);
+    *dmem = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
+    PinnedRing *ring = pinned_ring(dev);
+    if (!ring) return fail(PIC_ERR_NOMEM, "out of host memory");
+    std::lock_guard<std::mutex> lock(ring->mu);
+    PinnedSlot &slot = ring->slots[ring->next];
+    ring->next = (ring->next + 1) % kPinnedSlots;
+    if (slot.done) {
+        e = hipEventSynchronize(slot.done);  // the copy that last read the slot has run
+        if (e != hipSuccess)
+            return fail(PIC_ERR_DEVICE, "%s: hipEventSynchronize: %s", what, hipGetErrorString(e));
+    } else {
+        e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
+        if (e != hipSuccess) {
+            slot.done = nullptr;
+            return fail(PIC_ERR_DEVICE, "%s: hipEventCreate: %s", what, hipGetErrorString(e));
+        }
+    }
+    if (slot.cap < n) {
+        if (slot.host) (void)hipHostFree(slot.host);
+        slot.host = nullptr;
+        slot.cap = 0;
+        const size_t cap = std::max<size_t>(n, size_t{1} << 20);
+        e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            slot.host = nullptr;
+            return fail(PIC_ERR_NOMEM, "%s: hipHostMalloc (%zu bytes): %s", what, cap,
+                        hipGetErrorString(e));
+        }
+        slot.cap = cap;
+    }
+    fill(static_cast<uint8_t *>(slot.host));
+    e = hipMallocAsync(dmem, n, stream);
+    if (e != hipSuccess) {
+        *dmem = nullptr;
+        (void)hipGetLastError();  // clear it
+        return fail(PIC_ERR_DEVICE, "%s: hipMallocAsync (metadata): %s", what, hipGetErrorString(e));
+    }
+    e = hipMemcpyAsync(*dmem, slot.host, n, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipEventRecord(slot.done, stream);
+    if (e != hipSuccess) {
+        (void)hipFreeAsync(*dmem, stream);
+        *dmem = nullptr;
+        (void)hipStreamSynchronize(stream);
+        return fail(PIC_ERR_DEVICE, "%s: hipMemcpyAsync (metadata): %s", what, hipGetErrorString(e));
+    }
+    return PIC_OK;
+}
+
+namespace {
+
 // Stage a per-call problem's tiles and shift tables in stream-ordered device
 // memory (freed on the same stream once the kernel has run) and launch it
 // over n_layers layers from layer_begin; views holds the pointers and strides.
@@ -627,57 +685,12 @@ pic_status run_staged(const Problem &p, const KArgs &views, int32_t layer_begin,
                       hipStream_t stream, const char *what) {
     if (p.tiles.empty() || n_layers == 0) return PIC_OK;
     const Staged stg = stage(p);
-    const size_t n = stg.total;
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s: hipGetDevice: %s", what, hipGetErrorString(e));
-    PinnedRing *ring = pinned_ring(dev);
-    if (!ring) return fail(PIC_ERR_NOMEM, "out of host memory");
     void *dmem = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(ring->mu);
-        PinnedSlot &slot = ring->slots[ring->next];
-        ring->next = (ring->next + 1) % kPinnedSlots;
-        if (slot.done) {
-            e = hipEventSynchronize(slot.done);  // the copy that last read the slot has run
-            if (e != hipSuccess)
-                return fail(PIC_ERR_DEVICE, "%s: hipEventSynchronize: %s", what, hipGetErrorString(e));
-        } else {
-            e = hipEventCreateWithFlags(&slot.done, hipEventDisableTiming);
-            if (e != hipSuccess) {
-                slot.done = nullptr;
-                return fail(PIC_ERR_DEVICE, "%s: hipEventCreate: %s", what, hipGetErrorString(e));
-            }
-        }
-        if (slot.cap < n) {
-            if (slot.host) (void)hipHostFree(slot.host);
-            slot.host = nullptr;
-            slot.cap = 0;
-            const size_t cap = std::max<size_t>(n, size_t{1} << 20);
-            e = hipHostMalloc(&slot.host, cap, hipHostMallocDefault);
-            if (e != hipSuccess) {
-                slot.host = nullptr;
-                return fail(PIC_ERR_NOMEM, "%s: hipHostMalloc (%zu bytes): %s", what, cap,
-                            hipGetErrorString(e));
-            }
-            slot.cap = cap;
-        }
-        write_staged(p, stg, static_cast<uint8_t *>(slot.host));
-        e = hipMallocAsync(&dmem, n, stream);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();  // clear it
-            return fail(PIC_ERR_DEVICE, "%s: hipMallocAsync (metadata): %s", what, hipGetErrorString(e));
-        }
-        e = hipMemcpyAsync(dmem, slot.host, n, hipMemcpyHostToDevice, stream);
-        if (e == hipSuccess) e = hipEventRecord(slot.done, stream);
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(dmem, stream);
-            (void)hipStreamSynchronize(stream);
-            return fail(PIC_ERR_DEVICE, "%s: hipMemcpyAsync (metadata): %s", what, hipGetErrorString(e));
-        }
-    }
-    e = launch(p, with_views(p, views, static_cast<const uint8_t *>(dmem), stg, layer_begin),
-               n_layers, stream);
+    pic_status st = stage_per_call(stg.total, [&](uint8_t *host) { write_staged(p, stg, host); },
+                                   stream, &dmem, what);
+    if (st) return st;
+    hipError_t e = launch(p, with_views(p, views, static_cast<const uint8_t *>(dmem), stg, layer_begin),
+                          n_layers, stream);
     const hipError_t e2 = hipFreeAsync(dmem, stream);
     if (e != hipSuccess) return fail(PIC_ERR_DEVICE, "%s kernel launch: %s", what, hipGetErrorString(e));
     if (e2 != hipSuccess)

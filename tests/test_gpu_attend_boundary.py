@@ -171,3 +171,112 @@ def test_errors(torch_cuda):
         B._check(fplan._lib.pic_attend_boundary(
             fplan.handle, C.byref(B._view(fk, fv, "pool")), C.byref(B._view(fc, fc, "contig")),
             C.byref(a), None), fplan._lib)
+
+
+# ------------------------------------------------------------ caller rows
+
+def pick_rows(wl, rng, per_request=24, spread=1.0):
+    """(entry, token) rows chosen at random, request by request: any entry
+    (those at position 0 too), tokens anywhere in the entry, shuffled within
+    the request, some repeated."""
+    rows, e0 = [], 0
+    for rq in wl.requests:
+        mine = []
+        for i, e in enumerate(rq.entries):
+            n = max(1, int(per_request * spread * e.length / max(1, sum(x.length for x in rq.entries))))
+            for j in rng.integers(0, e.length, size=n):
+                mine.append((e0 + i, int(j)))
+        if mine:
+            mine.append(mine[int(rng.integers(0, len(mine)))])  # a repeat
+        rng.shuffle(mine)
+        rows += mine
+        e0 += len(rq.entries)
+    return rows
+
+
+def run_rows_case(torch, wl, group, rows, seed, layer=0, sink_tokens=0, sink_bias=0.0, scale=0.09):
+    import position_independent_kv_stitch_amd as pic
+    pk, pv = pool_values(wl, seed=seed, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, seed + 10, "cuda:0")
+    cv = normal_values(wl.dst_shape(), wl.dtype, seed + 11, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    q = normal_values((len(rows), wl.n_heads * group, wl.row_dim), wl.dtype, seed + 12, "cuda:0")
+    out = pic.attend_boundary(plan, pk, pv, ck, cv, q, layer=layer, rows=rows, scale=scale,
+                              sink_tokens=sink_tokens, sink_bias=sink_bias)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    L1 = slice(layer, layer + 1)
+    hq = to_host(q)
+    want = oracle.attend_boundary(wl, to_host(pk[L1]), to_host(pv[L1]), to_host(ck[L1]),
+                                  to_host(cv[L1]), hq, layer, 0, scale=scale,
+                                  sink_tokens=sink_tokens, sink_bias=sink_bias, layer_base=layer,
+                                  rows=rows)
+    keys = np.concatenate([to_host(pk[L1]).reshape(-1, wl.row_dim),
+                           to_host(ck[L1]).reshape(-1, wl.row_dim)])
+    vals = np.concatenate([to_host(pv[L1]).reshape(-1, wl.row_dim),
+                           to_host(cv[L1]).reshape(-1, wl.row_dim)])
+    s = np.abs(f64(hq)).reshape(-1, wl.row_dim) @ np.abs(f64(keys)).T
+    dz = scale * (wl.row_dim + 1) * U * float(s.max())
+    tol = 2 * (2 * dz + 1e-5 + 2.0 ** -16 + 300 * U) * float(np.abs(f64(vals)).max())
+    err = float(np.abs(got - want).max())
+    plan.destroy()
+    return err, tol
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_caller_rows_random(torch_cuda, seed):
+    """Rows the caller names (the page leaves the choice of "top-k" boundary
+    tokens open): random tokens of every entry, repeats, shuffled within
+    each request, several requests, paged and contiguous caches, pools
+    paged or not, groups 1-8."""
+    rng = np.random.default_rng(seed)
+    wl = random_small(1500 + seed, dtype="bf16", style="interleaved" if seed % 4 == 3 else "half",
+                      paged=seed % 2 == 1, n_requests=1 + seed % 3, n_layers=2,
+                      max_len=60 + 40 * (seed % 3))
+    if seed % 4 == 2:
+        wl = with_paged_pool(wl, page_size=16, seed=seed)
+    group = (1, 2, 4, 8)[seed % 4]
+    rows = pick_rows(wl, rng, per_request=(8, 40, 120)[seed % 3])
+    sink = (4, -15.0) if seed % 2 == 0 else (0, 0.0)
+    say(f"caller rows seed={seed}: {len(rows)} rows, group {group}, sink {sink}")
+    err, tol = run_rows_case(torch_cuda, wl, group, rows, seed, layer=seed % 2,
+                             sink_tokens=sink[0], sink_bias=sink[1])
+    say(f"  max err {err:.3g} (bound {tol:.3g})")
+    assert err <= tol
+
+
+def test_caller_rows_top_k_of_decode_batch(torch_cuda):
+    """Two Llama-3-8B decode requests: for every relocated chunk 16 tokens
+    picked from its first 64 (a top-k selection as a caller would make
+    it), 32 query heads, LegoLink damping; and the first-16 selection given
+    as rows equals the default path bit for bit."""
+    import position_independent_kv_stitch_amd as pic
+    torch = torch_cuda
+    wl = decode_batch(n_requests=2, n_layers=2)
+    rng = np.random.default_rng(7)
+    rows, e0 = [], 0
+    for rq in wl.requests:
+        for i, e in enumerate(rq.entries):
+            for j in np.sort(rng.choice(64, size=16, replace=False)):
+                rows.append((e0 + i, int(j)))
+        e0 += len(rq.entries)
+    say(f"top-k rows of the decode batch: {len(rows)}")
+    err, tol = run_rows_case(torch, wl, 4, rows, 5, layer=1, sink_tokens=4, sink_bias=-15.0,
+                             scale=128 ** -0.5)
+    say(f"  max err {err:.3g} (bound {tol:.3g})")
+    assert err <= tol
+    # the default selection, given explicitly
+    pk, pv = pool_values(wl, seed=5, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), wl.dtype, 15, "cuda:0")
+    cv = normal_values(wl.dst_shape(), wl.dtype, 16, "cuda:0")
+    plan = pic.Plan.from_workload(wl)
+    first = [(e, j) for e, (_, b, end) in enumerate(plan.ranges()[0]) if b > 0
+             for j in range(min(16, int(end - b)))]
+    q = normal_values((len(first), 32, 128), wl.dtype, 17, "cuda:0")
+    a = pic.attend_boundary(plan, pk, pv, ck, cv, q, layer=0, boundary_k=16, sink_tokens=4,
+                            sink_bias=-15.0)
+    b = pic.attend_boundary(plan, pk, pv, ck, cv, q, layer=0, rows=first, sink_tokens=4,
+                            sink_bias=-15.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    plan.destroy()

@@ -845,6 +845,47 @@ def test_boundary_attention_equals_decode_attention_at_each_position(style):
         assert np.allclose(got[b], want[0], atol=1e-12)
 
 
+def test_boundary_rows_given_by_the_caller():
+    """Caller rows (entry, token), entries numbered in plan order: the
+    positions follow from each entry's offset; a token outside its entry is
+    refused."""
+    wl = Workload("b", "f64", 1, 1, 8, 0, 8, "half", 1e4, True, pool_tokens=30,
+                  chunks=[Chunk(0, 10), Chunk(10, 20)], capacity=60,
+                  requests=[Request([Entry(0, 0, 10), Entry(1, 12, 3)]), Request([Entry(1, 20, 20)])])
+    assert oracle.boundary_rows(wl, 0, rows=[(1, 2), (0, 9), (2, 17), (2, 0)]) == \
+        [(0, 1, 2, 14), (0, 0, 9, 9), (1, 0, 17, 37), (1, 0, 0, 20)]
+    with pytest.raises(ValueError):
+        oracle.boundary_rows(wl, 0, rows=[(1, 3)])
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_caller_boundary_rows_equal_decode_attention_at_their_positions(style):
+    """Caller rows anywhere in an entry (past the first k tokens, in the entry
+    at position 0, repeated, out of order within the request) each attend
+    exactly like a decode step whose context ends at the row's position
+    (the decode oracle)."""
+    H, D, G, L = 2, 8, 2, 40
+    rng = np.random.default_rng(41)
+    chunks = [Chunk(0, 9), Chunk(9, 12)]
+    entries = [Entry(1, 3, 12, 2), Entry(0, 20, 9), Entry(0, 0, 3)]
+    wl = Workload("b", "f64", 1, H, D, 0, D, style, 1e4, True, pool_tokens=21, chunks=chunks,
+                  requests=[Request(entries, None, L)], capacity=L)
+    pk = rng.standard_normal((1, 21, H, D))
+    pv = rng.standard_normal((1, 21, H, D))
+    ck = rng.standard_normal((1, 1, L, H, D))
+    cv = rng.standard_normal((1, 1, L, H, D))
+    given = [(1, 8), (0, 11), (2, 0), (2, 2), (0, 0), (1, 8), (0, 5)]
+    rows = oracle.boundary_rows(wl, 0, rows=given)
+    q = rng.standard_normal((len(rows), H * G, D))
+    got = oracle.attend_boundary(wl, pk, pv, ck, cv, q, 0, 0, sink_tokens=3, sink_bias=-4.0,
+                                 dtype="f64", rows=given)
+    for b, (_, _, _, p) in enumerate(rows):
+        dec = Workload("b", "f64", 1, H, D, 0, D, style, 1e4, True, pool_tokens=21,
+                       chunks=chunks, requests=[Request(entries, None, p + 1)], capacity=L)
+        want = oracle.attend(dec, pk, pv, ck, cv, q[b:b + 1], 0, sink_tokens=3, sink_bias=-4.0)
+        assert np.allclose(got[b], want[0], atol=1e-12)
+
+
 def test_boundary_attention_matches_library_sdpa_bf16():
     """bf16 storage: equals torch's scaled dot product attention (fp64, CPU)
     over the rows the oracle's stitch stores, with a causal limit per row."""
