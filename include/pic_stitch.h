@@ -219,8 +219,10 @@ typedef struct pic_plan pic_plan_t;
  *   0 <= chunk_id < n_chunks; 1 <= length <= chunk.length;
  *   0 <= recompute_k <= length; dst_offset >= 0;
  *   dst_offset + length <= dst_capacity (contiguous) or
- *     <= n_pages * dst_page_size (paged);
- *   chunk.token_start >= 0, chunk.length >= 1; in a paged pool
+ *     <= n_pages * dst_page_size (paged), and < 2^31 (positions are int32
+ *     on the device);
+ *   chunk.token_start >= 0, chunk.length >= 1, |chunk.base_pos| <= 2^62
+ *     (so delta = dst_offset - base_pos fits int64); in a paged pool
  *     token_start + length <= n_pages * src_page_size;
  *   every destination page written is in [0, dst_num_pages) and every
  *     pool page read in [0, src_num_pages);

@@ -285,6 +285,9 @@ int orc_validate_stitch(const orc_stitch_problem *p, int layer_begin, int layer_
 
     for (int c = 0; c < p->n_chunks; c++) {
         if (p->chunk_start[c] < 0 || p->chunk_len[c] < 1) return ORC_RANGE;
+        /* |base_pos| <= 2^62: delta = dst - base_pos stays inside int64 */
+        if (p->chunk_base[c] < -((int64_t)1 << 62) || p->chunk_base[c] > ((int64_t)1 << 62))
+            return ORC_RANGE;
         int64_t room = p->src_page_size > 0 ? (int64_t)p->chunk_pages[c] * p->src_page_size
                                             : p->pool_tokens;
         if (p->chunk_start[c] + p->chunk_len[c] > room) return ORC_RANGE;
@@ -299,6 +302,7 @@ int orc_validate_stitch(const orc_stitch_problem *p, int layer_begin, int layer_
             if (p->ent_len[e] < 1 || p->ent_len[e] > p->chunk_len[c]) return ORC_RANGE;
             if (p->ent_k[e] < 0 || p->ent_k[e] > p->ent_len[e]) return ORC_RANGE;
             if (p->ent_dst[e] < 0 || p->ent_dst[e] + p->ent_len[e] > span) return ORC_RANGE;
+            if (p->ent_dst[e] + p->ent_len[e] > 2147483647) return ORC_RANGE; /* positions < 2^31 */
             if (p->page_size > 0) {
                 for (int t = p->ent_k[e]; t < p->ent_len[e]; t++) {
                     int64_t pos = p->ent_dst[e] + t;

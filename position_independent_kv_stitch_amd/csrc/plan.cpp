@@ -28,6 +28,7 @@ namespace {
 thread_local std::string g_error;
 
 constexpr int64_t kMaxPosition = INT32_MAX;  // positions and in-chunk offsets fit int32
+constexpr int64_t kMaxBase = int64_t{1} << 62;  // |base_pos|: delta = dst - base_pos fits int64
 }  // namespace
 
 void clear_error() { g_error.clear(); }
@@ -329,6 +330,9 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             return fail(PIC_ERR_RANGE, "chunk %d: tokens [%lld, %lld)", c,
                         static_cast<long long>(ch.token_start),
                         static_cast<long long>(ch.token_start + ch.length));
+        if (ch.base_pos < -kMaxBase || ch.base_pos > kMaxBase)
+            return fail(PIC_ERR_RANGE, "chunk %d: base_pos %lld outside [-2^62, 2^62]", c,
+                        static_cast<long long>(ch.base_pos));
         if (!src_paged) pool_need = std::max(pool_need, ch.token_start + ch.length);
     }
     for (int r = 0; r < n_requests; r++) {

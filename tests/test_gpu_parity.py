@@ -65,6 +65,36 @@ def test_special_shifts(torch_cuda, dt, paged):
         check_stitch_case(wl, seed=seed)
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_huge_shifts(torch_cuda, dt):
+    """Shifts far beyond any context (chunks cached at base positions up to
+    +-2^61 away): angles of up to 2^61 radians on plane 0, tables from the
+    host's fp64 libm on both sides; copy mode on a paged destination and
+    the in-place rotation."""
+    torch = torch_cuda
+    import position_independent_kv_stitch_amd as pic
+    from pic_workloads import normal_values
+    huge = [2 ** 40, -(2 ** 40), 2 ** 52 + 7, -(2 ** 52) - 3, 2 ** 61, -(2 ** 61) + 11]
+    wl = random_small(77, dtype=dt, paged=True, n_requests=3, n_layers=2, max_len=200,
+                      deltas=huge)
+    say(f"huge shifts {dt}: copy mode")
+    check_stitch_case(wl, seed=9)
+    segs, at = [], 0
+    for i, d in enumerate(huge):
+        segs.append(Segment(at, 40 + 17 * i, d, i % 3))
+        at += 40 + 17 * i
+    ip = Workload("huge in place", dt, 2, 8, 128, 0, 128, "half", 1e6, False, inplace=True,
+                  n_tokens=at, segments=segs)
+    buf = normal_values(ip.buf_shape(), dt, 10, "cuda:0")
+    before = to_host(buf)
+    pic.rotate_workload(ip, buf)
+    torch.cuda.synchronize()
+    want = before.copy()
+    assert oracle.rotate_inplace(ip, want) == "ok"
+    stats = compare_k(to_host(buf), want, 0, 128, max_abs(before), what="huge in place")
+    say(f"  in place: {stats}")
+
+
 PAGED_POOL_CASES = [(seed, dt, paged, mla, ps)
                     for seed in range(2)
                     for dt in ("f32", "bf16")

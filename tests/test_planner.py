@@ -310,3 +310,21 @@ def test_attend_refuses_rows_too_narrow_for_the_group():
     args = B.AttendArgs(16, 256, 16, 16, 256, 16, 16, 0, 0.25, 0, 0.0, 0)
     st = lib.pic_attend(p.handle, C.byref(view), C.byref(view), C.byref(args), None)
     assert B.STATUS_NAMES[st] == "align" and b"row_dim" in lib.pic_last_error()
+
+
+@pytest.mark.parametrize("base,dst,want", [
+    (2 ** 62, 5, "ok"),                        # |base_pos| up to 2^62
+    (-(2 ** 62), 5, "ok"),
+    (2 ** 62 + 1, 5, "range"),                 # past it delta could overflow int64
+    (-(2 ** 62) - 1, 5, "range"),
+    (0, 2 ** 31 - 1 - 10, "ok"),               # the last positions below 2^31
+    (0, 2 ** 31 - 10, "range"),                # a position reaches 2^31
+])
+def test_extreme_bases_and_positions(base, dst, want):
+    """The library and the oracle agree at the bounds of base_pos and of
+    logical positions (contiguous destination wide enough for both)."""
+    wl = Workload("edge", "bf16", 1, 2, 128, 0, 128, "half", 5e5, True, pool_tokens=20,
+                  chunks=[Chunk(0, 10, base)], capacity=2 ** 31 + 64,
+                  requests=[Request([Entry(0, dst, 10, 2)])])
+    assert oracle.validate_stitch(wl) == want
+    assert ORACLE_TO_LIB[want] == plan_status(wl)
