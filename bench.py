@@ -208,15 +208,14 @@ def setup_rag(name, torch, pic):
     the destination as many layers (a divisor of 32) as fit beside it; a
     step is one pic_stitch per layer group, each reading its own pool
     layers and writing the destination's layers."""
-    from pic_workloads import config3, pool_values, sentinel_like
+    from pic_workloads import config3, layers_per_launch, pool_values, sentinel_like
     wl = config3()
     row = wl.n_heads * wl.row_dim * wl.esize
     pool_bytes = 2 * wl.n_layers * wl.pool_tokens * row
     dst_layer = 2 * wl.n_phys_pages * wl.page_size * row
     free, total = torch.cuda.mem_get_info()
-    margin = 6 << 30  # value generation, plan metadata, the runtime
-    group = next(g for g in (32, 16, 8, 4, 2, 1)
-                 if wl.n_layers % g == 0 and pool_bytes + g * dst_layer + margin <= free)
+    group = layers_per_launch(wl, free)  # 6 GiB kept for value generation and the runtime
+    assert group > 0, "HBM too small for the batched-RAG pool"
     log(f"workload {name}: {free / 2**30:.1f} of {total / 2**30:.1f} GiB free; pool "
         f"{pool_bytes / 2**30:.1f} GiB, destination {group} layers x {dst_layer / 2**30:.2f} GiB")
     pk, pv = pool_values(wl, seed=0, device="cuda:0")

@@ -421,6 +421,22 @@ def random_small(seed: int, dtype: str = "bf16", style: str = "half", paged: boo
                     requests=[Request(e) for e in reqs_entries], capacity=int(max(spans)))
 
 
+def layers_per_launch(wl: Workload, free_bytes: int, margin: int = 6 << 30) -> int:
+    """The most layers (a divisor of wl.n_layers) whose destination fits in
+    free_bytes beside the whole pool (K and V, all layers) and a margin: the
+    layer-group size of a stitch whose pool stays resident and whose
+    destination is reused by each group's launch."""
+    row = wl.n_heads * wl.row_dim * wl.esize * (2 if wl.has_v else 1)
+    pool = wl.n_layers * (wl.pool_tokens if not wl.src_page_size else
+                          wl.src_n_pages * wl.src_page_size) * row
+    dst_layer = (wl.n_phys_pages * wl.page_size if wl.page_size else
+                 len(wl.requests) * wl.capacity) * row
+    for g in range(wl.n_layers, 0, -1):
+        if wl.n_layers % g == 0 and pool + g * dst_layer + margin <= free_bytes:
+            return g
+    return 0
+
+
 # ------------------------------------------------------------ token streams
 
 # Mean content-defined chunk length of the chunking workloads: a boundary

@@ -387,16 +387,22 @@ def _subproblem(wl, req_ids):
 
 
 def test_config3_full_in_layer_groups(torch_cuda):
-    """Batched RAG: 64 requests over a 256-chunk pool, all 32 layers.  As the
-    benchmark runs it, the pool holds every layer and each launch stitches
-    one layer group (8 layers here) of all requests into a destination
-    holding that group.  Every group: on every layer, unwritten rows keep
-    the sentinel, no row is written twice and every written V row is its
-    pool row; 4 sampled requests on 2 layers are compared with the oracle."""
+    """Batched RAG: 64 requests over a 256-chunk pool, all 32 layers, in the
+    benchmark's launch configuration: the pool holds every layer and each
+    launch stitches one layer group of all requests into a destination
+    holding that group, the group as large as the free HBM allows (all 32
+    layers in one launch on a 288 GiB GPU).  Every group: on every layer,
+    unwritten rows keep the sentinel, no row is written twice and every
+    written V row is its pool row; 4 sampled requests on 2 layers are
+    compared with the oracle."""
     torch = torch_cuda
     import position_independent_kv_stitch_amd as pic
+    from pic_workloads import layers_per_launch
     wl = config3()
-    group = 8
+    torch.cuda.empty_cache()
+    group = layers_per_launch(wl, torch.cuda.mem_get_info()[0])
+    assert group > 0, "HBM too small for the batched-RAG pool"
+    say(f"config3: {group} layers per launch")
     gw = wl.with_layers(group)
     say("config3: generating the 32-layer pool")
     pk, pv = pool_values(wl, seed=0, device="cuda:0")

@@ -11,7 +11,8 @@ import oracle
 import position_independent_kv_stitch_amd as pic
 from position_independent_kv_stitch_amd import _binding as B
 from pic_workloads import (CONFIGS, Chunk, Entry, Request, Segment, Workload, config2,
-                           config3, decode_batch, random_small, with_paged_pool)
+                           config3, decode_batch, layers_per_launch, random_small,
+                           with_paged_pool)
 
 ORACLE_TO_LIB = {"ok": "ok", "bad_arg": "invalid_arg", "range": "range", "overlap": "overlap"}
 
@@ -196,6 +197,26 @@ def test_batched_rag_plan_scales():
     # every physical page is written by exactly one request (global permutation)
     pages = np.concatenate([r.page_table for r in wl.requests])
     assert len(np.unique(pages)) == len(pages) == wl.n_phys_pages
+
+
+
+def test_batched_rag_layers_per_launch():
+    """The layer group of the batched-RAG stitch: the pool (32 layers of K
+    and V over 562,245 tokens of 8 x 128 bf16 rows) stays resident and the
+    destination of g layers (96,341 pages of 16 tokens for K and V)
+    must fit beside it with 6 GiB to spare, g a divisor of 32."""
+    wl = config3()
+    row = 2 * 8 * 128 * 2
+    pool = 32 * wl.pool_tokens * row
+    dst = wl.n_phys_pages * 16 * row
+    gib = 1 << 30
+    assert layers_per_launch(wl, pool + 32 * dst + 6 * gib) == 32  # all layers, one launch
+    assert layers_per_launch(wl, pool + 32 * dst + 6 * gib - 1) == 16
+    assert layers_per_launch(wl, pool + 8 * dst + 6 * gib) == 8
+    assert layers_per_launch(wl, pool + 7 * dst + 6 * gib) == 4  # 7 does not divide 32
+    assert layers_per_launch(wl, pool + dst + 6 * gib - 1) == 0
+    # a 288 GiB GPU with the runtime's share taken holds all 32 layers
+    assert layers_per_launch(wl, int(286.6 * gib)) == 32
 
 
 # ------------------------------------------------------------- in-place
