@@ -16,8 +16,11 @@
 // position reads the request's own cache.  The EPIC Guide's LegoLink damping
 // is the same optional logit bias as in pic_attend.
 //
-// Work: a workgroup of W waves takes one work item (a run of positions of
-// one request) for W groups of 16 query heads, one group per wave.  The
+// Work: a workgroup takes one work item (a run of positions of one request)
+// for a set of query-head groups of 16: W waves of one group each, or, for
+// 128 heads, four waves of two groups each (one wave per SIMD, so that a
+// wave holds 512 registers and each fragment it reads from LDS feeds two
+// heads' groups of products).  The
 // items are cut for the launch: each request gets a share of the CU slots in
 // proportion to its context, so every workgroup has about the same number
 // of positions and the launch is one round.  An item's positions come in
@@ -31,9 +34,9 @@
 //     to bf16 by the stitch's own code, rotate.hpp);
 //   - S^T = K Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A = 16
 //     positions x 32 dims of K, one contiguous 1 KB LDS read per wave (the
-//     staging layout is the A-fragment layout); B = the wave's head group's
+//     staging layout is the A-fragment layout); B = the wave's head groups'
 //     queries, in registers for the whole item;
-//   - online softmax over the wave's 16 heads;
+//   - online softmax over each of the wave's groups of 16 heads;
 //   - O^T += V^T P^T: B = the weights straight from the D registers of the
 //     two S^T tiles (the product's k order is permuted to match), split into
 //     bf16 hi + lo so the weights lose nothing; A = V^T, eight 2-byte LDS
@@ -156,24 +159,47 @@ __device__ __forceinline__ StageTile stage_tile(const MlaArgs &a, const AttnTile
     return StageTile{off0, T.tok0, info};
 }
 
+// S^T = K Q^T of two-group waves on the matrix cores with VGPR results:
+// their 256 output accumulators fill the AGPRs, where the compiler would
+// otherwise also place these logits (it picks one register kind for every
+// product of a kernel) and then copy accumulators back and forth at every
+// step.  An accumulation into the same registers as the previous product's
+// result needs no wait states; a vector ALU read of the result does, which
+// vgpr_mfma_guard provides (its operands tie the logits, so no read of them
+// is scheduled before it).  The first k-step starts from zero.
+template <bool FIRST>
+__device__ __forceinline__ void mfma_v(f32x4 &c, const bf16x8 &a, const bf16x8 &b) {
+    if constexpr (FIRST)
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(c) : "v"(a), "v"(b));
+    else
+        asm("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void vgpr_mfma_guard(f32x4 &a, f32x4 &b, f32x4 &c, f32x4 &d) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
-// Two waves per SIMD: the register budget is 256 per lane (72 for the
-// queries, 128 accumulators, the rest for fragments in flight); scheduling
-// barriers keep the compiler from hoisting every LDS read of a phase ahead.
-// NB staging buffers: 2 overlap a step's loads with the previous step's
-// work inside the workgroup; 1 halves the LDS so that twice as many
-// workgroups share a CU and overlap each other instead.  TPS 16-position
-// tiles per step: 2 (the value product on 16x16x32 tiles), or 1 (on
-// 16x16x16 tiles), which halves a step's LDS so that a one-wave workgroup
-// can hold two steps and still share a CU with three others.
-template <int STYLE, int W, int NB, int TPS>
-__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
-mla_block_kernel(const MlaArgs a, int32_t layer) {
+// HT head groups of 16 per wave.  HT = 1 (two waves per SIMD): the register
+// budget is 256 per lane (72 for the queries, 128 accumulators, the rest for
+// fragments in flight).  HT = 2 (one wave per SIMD, 512 registers): 144 for
+// the queries, 256 accumulators (in AGPRs), and every staged fragment read
+// from LDS feeds twice the matrix-core work, which halves the LDS traffic
+// per product.  Scheduling barriers keep the compiler from hoisting every
+// LDS read of a phase ahead.  NB staging buffers: 4 keep three steps in
+// flight; 2 overlap a step's loads with the previous step's work inside the
+// workgroup; 1 halves the LDS so that twice as many workgroups share a CU
+// and overlap each other instead.  TPS 16-position tiles per step: 2 (the
+// value product on 16x16x32 tiles), or 1 (on 16x16x16 tiles), which halves a
+// step's LDS so that a one-wave workgroup can hold two steps and still share
+// a CU with three others.
+template <int STYLE, int W, int NB, int TPS, int HT>
+__device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) {
     static_assert(TPS == 1 || TPS == 2, "position tiles per step");
+    static_assert(HT == 1 || (HT == 2 && TPS == 2), "head groups per wave");
     constexpr int kStepPos = 16 * TPS;      // positions per step
     constexpr int kSlabs = TPS * kKSteps;   // 1 KB slabs of a staged step
     // staged step: slab j = (k-step j / TPS, position tile j % TPS); slot
@@ -193,26 +219,37 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
     if (item >= a.n_items) return;  // uniform over the workgroup
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
-    const int hg = set * W + wave;
+    const int hg0 = (set * W + wave) * HT;  // the wave's first head group
     const int b_lo = a.item_block0[item], b_hi = a.item_block0[item + 1];
     const int request = a.blocks[b_lo].request;
     const float scale2 = a.scale * kLog2e;  // logits in log2 units (exp2 weights)
     const float bias2 = a.sink_bias * kLog2e;
 
-    // ---- query fragments (B of S^T = K Q^T): head r16 of the wave's group,
+    // ---- query fragments (B of S^T = K Q^T): head r16 of group hg0 + h,
     // dims 32 s + 8 g .. + 8 of k-step s
-    bf16x8 qf[kKSteps];
-    {
-        const uint16_t *qrow = a.q + request * a.q_req + (hg * kGroupHeads + r16) * a.q_head;
+    bf16x8 qf[HT][kKSteps];
+#pragma unroll
+    for (int h = 0; h < HT; h++) {
+        const uint16_t *qrow = a.q + request * a.q_req + ((hg0 + h) * kGroupHeads + r16) * a.q_head;
 #pragma unroll
         for (int s = 0; s < kKSteps; s++)
-            qf[s] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g));
+            qf[h][s] = as_bf16x8(*reinterpret_cast<const uint4 *>(qrow + 32 * s + 8 * g));
     }
 
-    f32x4 acc[kDTiles];
+    f32x4 acc[HT][kDTiles];
 #pragma unroll
-    for (int t = 0; t < kDTiles; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int h = 0; h < HT; h++)
+#pragma unroll
+        for (int t = 0; t < kDTiles; t++) acc[h][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run[HT], l_run[HT];
+#pragma unroll
+    for (int h = 0; h < HT; h++) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+    }
+    // lane part of the transposing V^T reads (see the value product)
+    const int pq = r16 >> 2, dq = r16 & 3;
+    const int vt_lane = ((16 * (dq >> 1) + 4 * g + pq) * 16 + 8 * (dq & 1));
 
     for (int b = b_lo; b < b_hi; b++) {
         const AttnBlock B = a.blocks[b];
@@ -234,7 +271,6 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
             }
         }
         __syncthreads();
-
         // stage step p0 into buffer bf: wave w loads slabs TPS w + tau,
         // + TPS W, ... of position tile tau; lanes past the block's end repeat position p0
         // (their weights are 0).  The tile holding a lane's position is found
@@ -354,66 +390,87 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
 
             // ---- logits S^T for the wave's heads
             const uint4 *stg = s_stage[cb];
-            f32x4 st[TPS];
+            f32x4 st[HT][TPS];
 #pragma unroll
-            for (int tau = 0; tau < TPS; tau++) st[tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < HT; h++)
+#pragma unroll
+                for (int tau = 0; tau < TPS; tau++) st[h][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < kKSteps; s++) {
 #pragma unroll
-                for (int tau = 0; tau < TPS; tau++)
-                    st[tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        as_bf16x8(stg[(TPS * s + tau) * 64 + lane]), qf[s], st[tau], 0, 0, 0);
-                if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+                for (int tau = 0; tau < TPS; tau++) {
+                    const bf16x8 kf = as_bf16x8(stg[(TPS * s + tau) * 64 + lane]);
+#pragma unroll
+                    for (int h = 0; h < HT; h++) {
+                        if constexpr (HT == 1)
+                            st[h][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[h][s], st[h][tau], 0, 0, 0);
+                        else if (s == 0)
+                            mfma_v<true>(st[h][tau], kf, qf[h][s]);
+                        else
+                            mfma_v<false>(st[h][tau], kf, qf[h][s]);
+                    }
+                }
+                if (s % (6 / HT) == 6 / HT - 1) __builtin_amdgcn_sched_barrier(0);
             }
+            if constexpr (HT == 2) vgpr_mfma_guard(st[0][0], st[0][1], st[1][0], st[1][1]);
 
-            // ---- online softmax over head r16 (log2 units): this lane holds
-            // positions p0 + 16 tau + 4 g + i.  The running max is kept until a
-            // logit passes it by kLazy (weights stay below 2^kLazy; the merge
-            // uses the same reference), so the accumulator is seldom rescaled
-            constexpr int NV = 4 * TPS;  // logits per lane
-            float sc[NV];
+            // ---- online softmax over head r16 of each group (log2 units):
+            // this lane holds positions p0 + 16 tau + 4 g + i.  The running max
+            // is kept until a logit passes it by kLazy (weights stay below
+            // 2^kLazy; the merge uses the same reference), so the accumulator
+            // is seldom rescaled
+            constexpr int NV = 4 * TPS;  // logits per lane and group
+            float pb[NV];
 #pragma unroll
             for (int tau = 0; tau < TPS; tau++) {
-                const f32x4 pb = *reinterpret_cast<const f32x4 *>(&s_pbias[cb][16 * tau + 4 * g]);
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&s_pbias[cb][16 * tau + 4 * g]);
 #pragma unroll
-                for (int i = 0; i < 4; i++) sc[4 * tau + i] = fmaf(st[tau][i], scale2, pb[i]);
-            }
-            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-            if constexpr (TPS == 2) mx = fmaxf(mx, fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-            mx = row_max(mx);  // finite: position p0 is in the block
-            const bool bump = mx > m_run + kLazy;  // (-inf + kLazy stays -inf)
-            const float m_new = bump ? mx : m_run;
-            const float alpha = bump ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-            float pw[NV];
-#pragma unroll
-            for (int k = 0; k < NV; k++) pw[k] = __builtin_amdgcn_exp2f(sc[k] - m_new);
-            float psum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
-            if constexpr (TPS == 2) psum += (pw[4] + pw[5]) + (pw[6] + pw[7]);
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            if (__any(bump)) {
-                // one or two waves per workgroup: the accumulators live in
-                // AGPRs, and plain code paid their copies at every step
-                if constexpr (W <= 2) {
-                    acc_read_guard();
-#pragma unroll
-                    for (int t = 0; t < kDTiles; t++) scale_acc(acc[t], alpha);
-                } else {
-#pragma unroll
-                    for (int t = 0; t < kDTiles; t++) acc[t] *= alpha;
-                }
+                for (int i = 0; i < 4; i++) pb[4 * tau + i] = v[i];
             }
             // weights as B of O^T += V^T P^T: k index 8 g + j is position
             // 4 g + j (j < 4) or 16 + 4 g + j - 4 with two tiles, k index 4 g + j
             // position 4 g + j with one -- the order of pw; hi + lo bf16
-            uint32_t hi[NV / 2], lo[NV / 2];
+            uint32_t hi[HT][NV / 2], lo[HT][NV / 2];
 #pragma unroll
-            for (int k = 0; k < NV / 2; k++) {
-                const f32x2 pr = {pw[2 * k], pw[2 * k + 1]};
-                hi[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
-                const f32x2 rr = {pw[2 * k] - __uint_as_float(hi[k] << 16),
-                                  pw[2 * k + 1] - __uint_as_float(hi[k] & 0xFFFF0000u)};
-                lo[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
+            for (int h = 0; h < HT; h++) {
+                float sc[NV];
+#pragma unroll
+                for (int tau = 0; tau < TPS; tau++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) sc[4 * tau + i] = fmaf(st[h][tau][i], scale2, pb[4 * tau + i]);
+                float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+                if constexpr (TPS == 2) mx = fmaxf(mx, fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+                mx = row_max(mx);  // finite: position p0 is in the block
+                const bool bump = mx > m_run[h] + kLazy;  // (-inf + kLazy stays -inf)
+                const float m_new = bump ? mx : m_run[h];
+                const float alpha = bump ? __builtin_amdgcn_exp2f(m_run[h] - m_new) : 1.f;
+                float pw[NV];
+#pragma unroll
+                for (int k = 0; k < NV; k++) pw[k] = __builtin_amdgcn_exp2f(sc[k] - m_new);
+                float psum = (pw[0] + pw[1]) + (pw[2] + pw[3]);
+                if constexpr (TPS == 2) psum += (pw[4] + pw[5]) + (pw[6] + pw[7]);
+                l_run[h] = l_run[h] * alpha + psum;
+                m_run[h] = m_new;
+                if (__any(bump)) {
+                    // one wave per SIMD: the accumulators live in AGPRs, and
+                    // plain code paid their copies at every step
+                    if constexpr (W <= 2 || HT == 2) {
+                        acc_read_guard();
+#pragma unroll
+                        for (int t = 0; t < kDTiles; t++) scale_acc(acc[h][t], alpha);
+                    } else {
+#pragma unroll
+                        for (int t = 0; t < kDTiles; t++) acc[h][t] *= alpha;
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < NV / 2; k++) {
+                    const f32x2 pr = {pw[2 * k], pw[2 * k + 1]};
+                    hi[h][k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+                    const f32x2 rr = {pw[2 * k] - __uint_as_float(hi[h][k] << 16),
+                                      pw[2 * k + 1] - __uint_as_float(hi[h][k] & 0xFFFF0000u)};
+                    lo[h][k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(rr, bf16x2));
+                }
             }
 
             // ---- A = V^T (dim d = 16 t + r16; positions 4 g .. 4 g + 3, then
@@ -422,29 +479,57 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
             // lanes 4 j + i / 4 address (j = 0..3).  So lane i of group g
             // addresses position 4 g + i / 4 (+ 16 for the second tile), dims
             // 16 t + 4 (i % 4) .. + 4: slab (t / 2, tile), slot 16 g' + position
-            // % 16 with g' = 2 (t % 2) + (i % 4) / 2, second half when i is odd
-            const char *stg8 = reinterpret_cast<const char *>(stg);
-            const int pq = r16 >> 2, dq = r16 & 3;
+            // % 16 with g' = 2 (t % 2) + (i % 4) / 2, second half when i is odd.
+            // The lane's part of the address is vt_lane; tile t adds a constant.
+            const char *vt = reinterpret_cast<const char *>(stg) + vt_lane;
+            constexpr int kTileBytes = 64 * 16;  // one slab
+            auto vt_frag = [&](int t) {
+                const int tc = (TPS * (t >> 1)) * kTileBytes + 32 * 16 * (t & 1);
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + tc));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(vt + tc + kTileBytes));  // tile 1: the next slab
+                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                return as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+            };
+            if constexpr (HT == 2) {
+                // one fragment read ahead: tile t + 1's reads are issued before
+                // tile t's products (four per fragment)
+                bf16x8 va = vt_frag(0);
+#pragma unroll
+                for (int t = 0; t < kDTiles; t++) {
+                    const bf16x8 vn = vt_frag(t + 1 < kDTiles ? t + 1 : t);
+#pragma unroll
+                    for (int h = 0; h < HT; h++) {
+                        const bf16x8 phi = as_bf16x8(make_uint4(hi[h][0], hi[h][1], hi[h][2], hi[h][3]));
+                        const bf16x8 plo = as_bf16x8(make_uint4(lo[h][0], lo[h][1], lo[h][2], lo[h][3]));
+                        acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[h][t], 0, 0, 0);
+                        acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[h][t], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    va = vn;
+                }
+            } else
 #pragma unroll
             for (int t = 0; t < kDTiles; t++) {
-                const int gq = 2 * (t & 1) + (dq >> 1);
-                const int base = ((TPS * (t >> 1)) * 64 + 16 * gq + 4 * g + pq) * 16 + 8 * (dq & 1);
-                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(stg8 + base));
+                const int tc = (TPS * (t >> 1)) * kTileBytes + 32 * 16 * (t & 1);
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + tc));
                 if constexpr (TPS == 2) {
                     const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4 *)(stg8 + base + 64 * 16));  // tile 1: the next slab
+                        (lds_s16x4 *)(vt + tc + kTileBytes));  // tile 1: the next slab
                     const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
                     const bf16x8 va = as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-                    const bf16x8 phi = as_bf16x8(make_uint4(hi[0], hi[1], hi[2], hi[3]));
-                    const bf16x8 plo = as_bf16x8(make_uint4(lo[0], lo[1], lo[2], lo[3]));
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[t], 0, 0, 0);
+#pragma unroll
+                    for (int h = 0; h < HT; h++) {
+                        const bf16x8 phi = as_bf16x8(make_uint4(hi[h][0], hi[h][1], hi[h][2], hi[h][3]));
+                        const bf16x8 plo = as_bf16x8(make_uint4(lo[h][0], lo[h][1], lo[h][2], lo[h][3]));
+                        acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[h][t], 0, 0, 0);
+                        acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[h][t], 0, 0, 0);
+                    }
                 } else {
-                    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0], hi[1]));
-                    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0], lo[1]));
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, acc[t], 0, 0, 0);
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, acc[t], 0, 0, 0);
+                    const s16x4 phi = __builtin_bit_cast(s16x4, make_uint2(hi[0][0], hi[0][1]));
+                    const s16x4 plo = __builtin_bit_cast(s16x4, make_uint2(lo[0][0], lo[0][1]));
+                    acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, phi, acc[0][t], 0, 0, 0);
+                    acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, plo, acc[0][t], 0, 0, 0);
                 }
                 if (t % 4 == 3) __builtin_amdgcn_sched_barrier(0);
             }
@@ -456,19 +541,37 @@ mla_block_kernel(const MlaArgs a, int32_t layer) {
     }
 
     // ---- partial results: O^T D registers hold dims 16 t + 4 g + i of head r16
-    l_run += __shfl_xor(l_run, 16, 64);
-    l_run += __shfl_xor(l_run, 32, 64);
-    const int head = hg * kGroupHeads + r16;
-    const int64_t slot_id = static_cast<int64_t>(item) * a.num_q_heads + head;
-    float *pa = a.part_acc + slot_id * kVDim;
 #pragma unroll
-    for (int t = 0; t < kDTiles; t++)
-        *reinterpret_cast<float4 *>(pa + 16 * t + 4 * g) =
-            make_float4(acc[t][0], acc[t][1], acc[t][2], acc[t][3]);
-    if (g == 0) {
-        a.part_ml[2 * slot_id] = m_run;
-        a.part_ml[2 * slot_id + 1] = l_run;
+    for (int h = 0; h < HT; h++) {
+        float l = l_run[h];
+        l += __shfl_xor(l, 16, 64);
+        l += __shfl_xor(l, 32, 64);
+        const int head = (hg0 + h) * kGroupHeads + r16;
+        const int64_t slot_id = static_cast<int64_t>(item) * a.num_q_heads + head;
+        float *pa = a.part_acc + slot_id * kVDim;
+#pragma unroll
+        for (int t = 0; t < kDTiles; t++)
+            *reinterpret_cast<float4 *>(pa + 16 * t + 4 * g) =
+                make_float4(acc[h][t][0], acc[h][t][1], acc[h][t][2], acc[h][t][3]);
+        if (g == 0) {
+            a.part_ml[2 * slot_id] = m_run[h];
+            a.part_ml[2 * slot_id + 1] = l;
+        }
     }
+}
+
+template <int STYLE, int W, int NB, int TPS>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2)))
+mla_block_kernel(const MlaArgs a, int32_t layer) {
+    mla_block_body<STYLE, W, NB, TPS, 1>(a, layer);
+}
+
+// 128 query heads per workgroup: four waves of two head groups, one wave per
+// SIMD
+template <int STYLE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+mla_wide_kernel(const MlaArgs a, int32_t layer) {
+    mla_block_body<STYLE, 4, 4, 2, 2>(a, layer);
 }
 
 // out[r][j][d] = sum_b acc_b[d] e^{m_b - M} / sum_b l_b e^{m_b - M} over the
@@ -551,7 +654,7 @@ constexpr int kPerCu1 = std::min(8, 160 / (18 * kNb1 * kTps1 + 3));
 template <int STYLE>
 hipError_t launch_block(int w, dim3 grid, hipStream_t stream, const MlaArgs &a, int32_t layer) {
     switch (w) {
-        case 8: hipLaunchKernelGGL((mla_block_kernel<STYLE, 8, 4, 2>), grid, dim3(512), 0, stream, a, layer); break;
+        case 8: hipLaunchKernelGGL((mla_wide_kernel<STYLE>), grid, dim3(256), 0, stream, a, layer); break;
         case 4: hipLaunchKernelGGL((mla_block_kernel<STYLE, 4, 2, 2>), grid, dim3(256), 0, stream, a, layer); break;
         case 2: hipLaunchKernelGGL((mla_block_kernel<STYLE, 2, 2, 2>), grid, dim3(128), 0, stream, a, layer); break;
         default:
