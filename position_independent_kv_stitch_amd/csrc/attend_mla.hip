@@ -73,6 +73,8 @@ constexpr int kDTiles = kVDim / 16;       // output tiles of 16 dims
 constexpr int kGroupHeads = 16;           // query heads per wave
 constexpr int kItemTiles = kItemBlockTiles;  // map tiles per block at most
 constexpr int kCombineThreads = 256;
+constexpr int kSDepth = 4;  // logit fragments read ahead (two-group waves)
+constexpr int kVDepth = 3;  // V^T fragments read ahead (two-group waves)
 
 constexpr int kBlockTabs = kItemBlockTabs;  // shift tables per block at most (kept in LDS)
 constexpr int kHalfR = kRopeDim / 2;      // rotary planes
@@ -199,7 +201,7 @@ typedef void __attribute__((address_space(3))) *lptr_t;
 template <int STYLE, int W, int NB, int TPS, int HT>
 __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) {
     static_assert(TPS == 1 || TPS == 2, "position tiles per step");
-    static_assert(HT == 1 || (HT == 2 && TPS == 2), "head groups per wave");
+    static_assert(HT == 1 || (HT == 2 && TPS == 2 && NB == 4), "head groups per wave");
     constexpr int kStepPos = 16 * TPS;      // positions per step
     constexpr int kSlabs = TPS * kKSteps;   // 1 KB slabs of a staged step
     // staged step: slab j = (k-step j / TPS, position tile j % TPS); slot
@@ -304,7 +306,9 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
         // the group, with the stitch's fp64 turn and rounding
         auto turn = [&](int bb) {
             for (int u = tid; u < 16 * kStepPos; u += 64 * W) {
-                const int pos = u >> 4, gg = (u >> 2) & 3, qh = u & 3;
+                // a wave's lanes take 16 positions of one 8-plane group, so its
+                // LDS words are 256 contiguous bytes (no bank conflicts)
+                const int qh = u & 3, pos = (u >> 2) % kStepPos, gg = (u >> 2) / kStepPos;
                 const uint32_t slot1 = s_pslot[bb][pos];
                 if (slot1 == 0u) continue;
                 const double2 *tab = s_cs[slot1 - 1];
@@ -369,6 +373,7 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
         for (int i = 0; i < nsteps; i++) {
             const int p0 = i * kStepPos;
             int cb;  // the buffer computed on
+            bf16x8 kq[kSDepth];  // two-group waves: the first logit fragments
             if constexpr (NB == 4) {
                 // step i + 1's loads are in (i + 2's may not be); after the
                 // barrier every wave's are, step i is turned, step i - 1's
@@ -377,6 +382,11 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                 else wait_vm<0>();
                 __syncthreads();
                 cb = i & 3;
+                if constexpr (HT == 2) {
+                    // read ahead of the staging and the turn, which hide their latency
+#pragma unroll
+                    for (int f = 0; f < kSDepth; f++) kq[f] = as_bf16x8(s_stage[cb][f * 64 + lane]);
+                }
                 if (i + 3 < nsteps) stage(p0 + 3 * kStepPos, (i + 3) & 3);
                 if (i + 1 < nsteps) turn((i + 1) & 3);
             } else {
@@ -395,24 +405,35 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
             for (int h = 0; h < HT; h++)
 #pragma unroll
                 for (int tau = 0; tau < TPS; tau++) st[h][tau] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (HT == 2) {
+                // fragments f = TPS s + tau in slab order, the first kSDepth
+                // read at the top of the step, later ones kSDepth ahead
+                constexpr int kSFrags = TPS * kKSteps;
 #pragma unroll
-            for (int s = 0; s < kKSteps; s++) {
-#pragma unroll
-                for (int tau = 0; tau < TPS; tau++) {
-                    const bf16x8 kf = as_bf16x8(stg[(TPS * s + tau) * 64 + lane]);
+                for (int f = 0; f < kSFrags; f++) {
+                    const int s = f / TPS, tau = f % TPS;
+                    const bf16x8 kf = kq[f % kSDepth];
+                    if (f + kSDepth < kSFrags) kq[f % kSDepth] = as_bf16x8(stg[(f + kSDepth) * 64 + lane]);
 #pragma unroll
                     for (int h = 0; h < HT; h++) {
-                        if constexpr (HT == 1)
-                            st[h][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[h][s], st[h][tau], 0, 0, 0);
-                        else if (s == 0)
+                        if (s == 0)
                             mfma_v<true>(st[h][tau], kf, qf[h][s]);
                         else
                             mfma_v<false>(st[h][tau], kf, qf[h][s]);
                     }
+                    if (tau == TPS - 1) __builtin_amdgcn_sched_barrier(0);
                 }
-                if (s % (6 / HT) == 6 / HT - 1) __builtin_amdgcn_sched_barrier(0);
+                vgpr_mfma_guard(st[0][0], st[0][1], st[1][0], st[1][1]);
+            } else {
+#pragma unroll
+                for (int s = 0; s < kKSteps; s++) {
+#pragma unroll
+                    for (int tau = 0; tau < TPS; tau++)
+                        st[0][tau] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            as_bf16x8(stg[(TPS * s + tau) * 64 + lane]), qf[0][s], st[0][tau], 0, 0, 0);
+                    if (s % 6 == 5) __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            if constexpr (HT == 2) vgpr_mfma_guard(st[0][0], st[0][1], st[1][0], st[1][1]);
 
             // ---- online softmax over head r16 of each group (log2 units):
             // this lane holds positions p0 + 16 tau + 4 g + i.  The running max
@@ -426,6 +447,22 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                 const f32x4 v = *reinterpret_cast<const f32x4 *>(&s_pbias[cb][16 * tau + 4 * g]);
 #pragma unroll
                 for (int i = 0; i < 4; i++) pb[4 * tau + i] = v[i];
+            }
+            // the first V^T fragments (see the value product), read ahead of the softmax
+            const char *vt = reinterpret_cast<const char *>(stg) + vt_lane;
+            constexpr int kTileBytes = 64 * 16;  // one slab
+            auto vt_frag = [&](int t) {
+                const int tc = (TPS * (t >> 1)) * kTileBytes + 32 * 16 * (t & 1);
+                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + tc));
+                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (lds_s16x4 *)(vt + tc + kTileBytes));  // tile 1: the next slab
+                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+                return as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
+            };
+            bf16x8 vq[kVDepth];
+            if constexpr (HT == 2) {
+#pragma unroll
+                for (int t = 0; t < kVDepth; t++) vq[t] = vt_frag(t);
             }
             // weights as B of O^T += V^T P^T: k index 8 g + j is position
             // 4 g + j (j < 4) or 16 + 4 g + j - 4 with two tiles, k index 4 g + j
@@ -481,23 +518,13 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
             // 16 t + 4 (i % 4) .. + 4: slab (t / 2, tile), slot 16 g' + position
             // % 16 with g' = 2 (t % 2) + (i % 4) / 2, second half when i is odd.
             // The lane's part of the address is vt_lane; tile t adds a constant.
-            const char *vt = reinterpret_cast<const char *>(stg) + vt_lane;
-            constexpr int kTileBytes = 64 * 16;  // one slab
-            auto vt_frag = [&](int t) {
-                const int tc = (TPS * (t >> 1)) * kTileBytes + 32 * 16 * (t & 1);
-                const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(vt + tc));
-                const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (lds_s16x4 *)(vt + tc + kTileBytes));  // tile 1: the next slab
-                const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
-                return as_bf16x8(make_uint4(w0.x, w0.y, w1.x, w1.y));
-            };
             if constexpr (HT == 2) {
-                // one fragment read ahead: tile t + 1's reads are issued before
-                // tile t's products (four per fragment)
-                bf16x8 va = vt_frag(0);
+                // kVDepth fragments read ahead: tile t + kVDepth's reads are
+                // issued with tile t's products (four per fragment)
 #pragma unroll
                 for (int t = 0; t < kDTiles; t++) {
-                    const bf16x8 vn = vt_frag(t + 1 < kDTiles ? t + 1 : t);
+                    const bf16x8 va = vq[t % kVDepth];
+                    if (t + kVDepth < kDTiles) vq[t % kVDepth] = vt_frag(t + kVDepth);
 #pragma unroll
                     for (int h = 0; h < HT; h++) {
                         const bf16x8 phi = as_bf16x8(make_uint4(hi[h][0], hi[h][1], hi[h][2], hi[h][3]));
@@ -506,7 +533,6 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                         acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[h][t], 0, 0, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
-                    va = vn;
                 }
             } else
 #pragma unroll
