@@ -180,6 +180,21 @@ __device__ __forceinline__ void vgpr_mfma_guard(f32x4 &a, f32x4 &b, f32x4 &c, f3
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
+// A map tile as the two-group staging reads it: the byte address of the row
+// of block position 0 (pool or cache, layer included) and the token stride in
+// bytes, so that position pi's row starts at addr0 + pi * stride.
+struct StageRow {
+    uint64_t addr0;
+    int64_t stride;
+};
+
+__device__ __forceinline__ StageRow stage_row(const MlaArgs &a, const AttnTile &T, int32_t layer) {
+    const StageTile S = stage_tile(a, T, 0, layer);
+    const bool pool = S.info & kInfoPool;
+    const uint64_t base = reinterpret_cast<uint64_t>(pool ? a.pool_k : a.cache_k);
+    return StageRow{base + 2 * static_cast<uint64_t>(S.off0), 2 * (pool ? a.s_tok : a.c_tok)};
+}
+
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef const void __attribute__((address_space(1))) *gptr_t;
@@ -209,7 +224,13 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
     // i.e. the A fragment of lane 16 g + p
     __shared__ __attribute__((aligned(16))) uint4 s_stage[NB][kSlabs * 64];
     __shared__ __attribute__((aligned(16))) double2 s_cs[kBlockTabs][kHalfR];  // block's shift tables
-    __shared__ StageTile s_tiles[kItemTiles];
+    __shared__ StageTile s_tiles[HT == 1 ? kItemTiles : 1];
+    // two-group waves: every block position's tile (bits 0-5) and damping
+    // (bit 6), every tile's row address and stride and its table slot + 1
+    __shared__ uint8_t s_pinfo[HT == 2 ? kItemBlockPos : 1];
+    __shared__ __attribute__((aligned(16))) StageRow s_rows[HT == 2 ? kItemTiles : 1];
+    __shared__ uint8_t s_tslot[HT == 2 ? kItemTiles : 1];
+    static_assert(kItemTiles <= 64, "tile index in 6 bits");
     __shared__ uint32_t s_pslot[NB][kStepPos];                        // table slot + 1 (0: not turned)
     __shared__ __attribute__((aligned(16))) float s_pbias[NB][kStepPos];  // damping, -inf past the block
 
@@ -256,13 +277,33 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
     for (int b = b_lo; b < b_hi; b++) {
         const AttnBlock B = a.blocks[b];
         __syncthreads();  // the previous block's steps are done with s_tiles and s_stage
-        if (tid < B.ntiles) {
-            const AttnTile T = a.tiles[B.tile0 + tid];
-            int sl = -1;
+        if constexpr (HT == 1) {
+            if (tid < B.ntiles) {
+                const AttnTile T = a.tiles[B.tile0 + tid];
+                int sl = -1;
 #pragma unroll
-            for (int j = 0; j < kBlockTabs; j++)
-                if (T.cs_idx >= 0 && a.block_tabs[kBlockTabs * b + j] == T.cs_idx) sl = j;
-            s_tiles[tid] = stage_tile(a, T, sl, layer);
+                for (int j = 0; j < kBlockTabs; j++)
+                    if (T.cs_idx >= 0 && a.block_tabs[kBlockTabs * b + j] == T.cs_idx) sl = j;
+                s_tiles[tid] = stage_tile(a, T, sl, layer);
+            }
+        } else {
+            // four threads per tile fill its positions' bytes
+            const int t = tid >> 2;
+            if (t < B.ntiles) {
+                const AttnTile T = a.tiles[B.tile0 + t];
+                if ((tid & 3) == 0) {
+                    int sl = -1;
+#pragma unroll
+                    for (int j = 0; j < kBlockTabs; j++)
+                        if (T.cs_idx >= 0 && a.block_tabs[kBlockTabs * b + j] == T.cs_idx) sl = j;
+                    s_rows[t] = stage_row(a, T, layer);
+                    s_tslot[t] = static_cast<uint8_t>(sl + 1);
+                }
+                const int damp = static_cast<int>(std::min<int64_t>(
+                    std::max<int64_t>(int64_t{a.sink_tokens} - T.sink_dist, 0), T.ntok));
+                for (int k = tid & 3; k < T.ntok; k += 4)
+                    s_pinfo[T.tok0 + k] = static_cast<uint8_t>(t | (k < damp ? 64 : 0));
+            }
         }
         for (int i = tid; i < kBlockTabs * kHalfR; i += 64 * W) {
             const int j = i / kHalfR, pl = i - j * kHalfR;
@@ -278,7 +319,37 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
         // (their weights are 0).  The tile holding a lane's position is found
         // by a forward search (positions only grow within a block).
         int cur[2] = {0, 0};
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
         auto stage = [&](int p0, int bf) {
+            if constexpr (HT == 2) {
+                // wave w loads k-steps w, w + 4, ... (slabs 2 w + tau + 8 k) of
+                // both position tiles: one address per tile, the k-steps 256
+                // bytes apart in the row (the instruction's offset)
+                static_assert(TPS == 2 && W == 4 && kKSteps == 18, "two-group staging layout");
+#pragma unroll
+                for (int tau = 0; tau < TPS; tau++) {
+                    int pi = p0 + 16 * tau + r16;
+                    const bool valid = pi < B.ntok;
+                    if (!valid) pi = p0;
+                    const uint32_t info = s_pinfo[pi];
+                    const uint32_t t = info & 63u;
+                    const StageRow R = s_rows[t];
+                    if (wave == 0 && g == 0) {
+                        s_pslot[bf][16 * tau + r16] = valid ? s_tslot[t] : 0u;
+                        s_pbias[bf][16 * tau + r16] = valid ? ((info & 64u) ? bias2 : 0.f) : -INFINITY;
+                    }
+                    const char *row = reinterpret_cast<const char *>(
+                        R.addr0 + static_cast<uint64_t>(static_cast<int64_t>(pi) * R.stride)) +
+                        16 * g + 64 * wave_u;
+                    uint4 *slab = &s_stage[bf][(TPS * wave_u + tau) * 64];
+                    load_lds16<0>(row, slab);
+                    load_lds16<256>(row, slab + 8 * 64);
+                    load_lds16<512>(row, slab + 16 * 64);
+                    load_lds16<768>(row, slab + 24 * 64);
+                    if (TPS * wave_u + tau + 32 < kSlabs) load_lds16<1024>(row, slab + 32 * 64);
+                }
+                return;
+            }
 #pragma unroll
             for (int tau = 0; tau < TPS; tau++) {
                 int pi = p0 + 16 * tau + r16;
