@@ -75,6 +75,7 @@ constexpr int kItemTiles = kItemBlockTiles;  // map tiles per block at most
 constexpr int kCombineThreads = 256;
 constexpr int kSDepth = 4;  // logit fragments read ahead (two-group waves)
 constexpr int kVDepth = 3;  // V^T fragments read ahead (two-group waves)
+constexpr int kTurnAt0 = 8, kTurnAt1 = 20;  // value tiles that carry the next step's turn
 
 constexpr int kBlockTabs = kItemBlockTabs;  // shift tables per block at most (kept in LDS)
 constexpr int kHalfR = kRopeDim / 2;      // rotary planes
@@ -373,52 +374,61 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
         };
 
         // turn the rotary slots of moved chunk rows of buffer bb, in LDS: unit
-        // (position, 8-plane group gg, pair qh) turns planes 2 qh, 2 qh + 1 of
-        // the group, with the stitch's fp64 turn and rounding
+        // u = (position, 8-plane group gg, pair qh) turns planes 2 qh, 2 qh + 1
+        // of the group, with the stitch's fp64 turn and rounding.  A wave's
+        // lanes take 16 positions of one 8-plane group, so its LDS words are
+        // 256 contiguous bytes (no bank conflicts).  Without branches: a unit
+        // of a row that is not turned writes its words back unchanged.
+        auto turn_unit = [&](int bb, int u) {
+            const int qh = u & 3, pos = (u >> 2) % kStepPos, gg = (u >> 2) / kStepPos;
+            // (clamped: after a block's last step the buffer may hold any bits)
+            const uint32_t slot1 = min(s_pslot[bb][pos], static_cast<uint32_t>(kBlockTabs));
+            const bool on = slot1 != 0u;
+            const double2 *tab = s_cs[on ? slot1 - 1 : 0];
+            const int tau = pos >> 4, pp = pos & 15;
+            uint32_t *kx = reinterpret_cast<uint32_t *>(
+                &s_stage[bb][(TPS * kRopeStep + tau) * 64 + 16 * gg + pp]);
+            uint32_t *ky = reinterpret_cast<uint32_t *>(
+                &s_stage[bb][(TPS * (kRopeStep + 1) + tau) * 64 + 16 * gg + pp]);
+            if constexpr (STYLE == PIC_ROPE_HALF) {
+                // x of planes 8 gg + 2 qh, + 1 in word qh of the first rotary
+                // k-step's piece, their y (32 planes later) in the second's
+                const uint32_t ox = kx[qh], oy = ky[qh];
+                uint32_t wx = ox, wy = oy;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const double2 cs = tab[8 * gg + 2 * qh + h];
+                    const int sh = 16 * h;
+                    const double x = static_cast<double>(__uint_as_float(((ox >> sh) & 0xFFFFu) << 16));
+                    const double y = static_cast<double>(__uint_as_float(((oy >> sh) & 0xFFFFu) << 16));
+                    const uint32_t nx = f64_to_bf16(x * cs.x - y * cs.y);
+                    const uint32_t ny = f64_to_bf16(x * cs.y + y * cs.x);
+                    wx = (wx & ~(0xFFFFu << sh)) | (nx << sh);
+                    wy = (wy & ~(0xFFFFu << sh)) | (ny << sh);
+                }
+                kx[qh] = on ? wx : ox;
+                ky[qh] = on ? wy : oy;
+            } else {
+                // a whole pair per word: words 2 qh, 2 qh + 1 of the first
+                // piece hold planes 4 gg + 2 qh, + 1 (qh < 2); of the second,
+                // planes 16 + 4 gg + 2 qh - 4, + 1 (qh >= 2)
+                uint32_t *wp = qh < 2 ? kx + 2 * qh : ky + 2 * qh - 4;
+                const int plane0 = qh < 2 ? 4 * gg + 2 * qh : 16 + 4 * gg + 2 * qh - 4;
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const double2 cs = tab[plane0 + h];
+                    const uint32_t w = wp[h];
+                    const double x = bf16_lo(w), y = bf16_hi(w);
+                    const uint32_t n = f64_to_bf16(x * cs.x - y * cs.y) |
+                                       (f64_to_bf16(x * cs.y + y * cs.x) << 16);
+                    wp[h] = on ? n : w;
+                }
+            }
+        };
         auto turn = [&](int bb) {
             for (int u = tid; u < 16 * kStepPos; u += 64 * W) {
-                // a wave's lanes take 16 positions of one 8-plane group, so its
-                // LDS words are 256 contiguous bytes (no bank conflicts)
-                const int qh = u & 3, pos = (u >> 2) % kStepPos, gg = (u >> 2) / kStepPos;
-                const uint32_t slot1 = s_pslot[bb][pos];
-                if (slot1 == 0u) continue;
-                const double2 *tab = s_cs[slot1 - 1];
-                const int tau = pos >> 4, pp = pos & 15;
-                uint32_t *kx = reinterpret_cast<uint32_t *>(
-                    &s_stage[bb][(TPS * kRopeStep + tau) * 64 + 16 * gg + pp]);
-                uint32_t *ky = reinterpret_cast<uint32_t *>(
-                    &s_stage[bb][(TPS * (kRopeStep + 1) + tau) * 64 + 16 * gg + pp]);
-                if constexpr (STYLE == PIC_ROPE_HALF) {
-                    // x of planes 8 gg + 2 qh, + 1 in word qh of the first rotary
-                    // k-step's piece, their y (32 planes later) in the second's
-                    uint32_t wx = kx[qh], wy = ky[qh];
-#pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        const double2 cs = tab[8 * gg + 2 * qh + h];
-                        const int sh = 16 * h;
-                        const double x = static_cast<double>(__uint_as_float(((wx >> sh) & 0xFFFFu) << 16));
-                        const double y = static_cast<double>(__uint_as_float(((wy >> sh) & 0xFFFFu) << 16));
-                        const uint32_t nx = f64_to_bf16(x * cs.x - y * cs.y);
-                        const uint32_t ny = f64_to_bf16(x * cs.y + y * cs.x);
-                        wx = (wx & ~(0xFFFFu << sh)) | (nx << sh);
-                        wy = (wy & ~(0xFFFFu << sh)) | (ny << sh);
-                    }
-                    kx[qh] = wx;
-                    ky[qh] = wy;
-                } else {
-                    // a whole pair per word: words 2 qh, 2 qh + 1 of the first
-                    // piece hold planes 4 gg + 2 qh, + 1 (qh < 2); of the second,
-                    // planes 16 + 4 gg + 2 qh - 4, + 1 (qh >= 2)
-                    uint32_t *wp = qh < 2 ? kx + 2 * qh : ky + 2 * qh - 4;
-                    const int plane0 = qh < 2 ? 4 * gg + 2 * qh : 16 + 4 * gg + 2 * qh - 4;
-#pragma unroll
-                    for (int h = 0; h < 2; h++) {
-                        const double2 cs = tab[plane0 + h];
-                        const uint32_t w = wp[h];
-                        const double x = bf16_lo(w), y = bf16_hi(w);
-                        wp[h] = f64_to_bf16(x * cs.x - y * cs.y) | (f64_to_bf16(x * cs.y + y * cs.x) << 16);
-                    }
-                }
+                if (s_pslot[bb][(u >> 2) % kStepPos] == 0u) continue;
+                turn_unit(bb, u);
             }
         };
 
@@ -459,7 +469,8 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                     for (int f = 0; f < kSDepth; f++) kq[f] = as_bf16x8(s_stage[cb][f * 64 + lane]);
                 }
                 if (i + 3 < nsteps) stage(p0 + 3 * kStepPos, (i + 3) & 3);
-                if (i + 1 < nsteps) turn((i + 1) & 3);
+                // two-group waves turn step i + 1 among the value products
+                if (HT == 1 && i + 1 < nsteps) turn((i + 1) & 3);
             } else {
                 wait_vm<0>();
                 __syncthreads();  // the step is in LDS (every wave's share) and its meta written
@@ -603,7 +614,14 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                         acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[h][t], 0, 0, 0);
                         acc[h][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[h][t], 0, 0, 0);
                     }
-                    __builtin_amdgcn_sched_barrier(0);
+                    // the turn of the next step's buffer, one unit per thread
+                    // among tiles kTurnAt[k] .. + 3 (the vector work of a turn
+                    // takes about as long as their 16 products).  After the
+                    // block's last step it turns a buffer no step reads again.
+                    if (t == kTurnAt0 || t == kTurnAt1)
+                        turn_unit((i + 1) & 3, tid + (t == kTurnAt0 ? 0 : 64 * W));
+                    if (!((t >= kTurnAt0 && t < kTurnAt0 + 3) || (t >= kTurnAt1 && t < kTurnAt1 + 3)))
+                        __builtin_amdgcn_sched_barrier(0);
                 }
             } else
 #pragma unroll
