@@ -319,7 +319,7 @@ def setup_attend_mla(name, torch, pic):
            "parallelism": "single-gpu"}
     return {"wl": wl, "step": step, "bytes": info["context_tokens"] * row * L,
             "token_layers": info["context_tokens"] * L, "launches": L, "flops": flops,
-            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": "mla_block_kernel<half> + mla_combine_kernel (one pic_attend_latent)", "counters": "mla",
+            "arithmetic": "f32 softmax and accumulation, bf16 matrix-core products (vector f32 off the matrix-core shapes)", "kernel": ("mla_wide_kernel" if heads % 128 == 0 else "mla_block_kernel") + "<half> + mla_combine_kernel (one pic_attend_latent)", "counters": "mla",
             "plan": plan, "info": info, "config": cfg}
 
 
