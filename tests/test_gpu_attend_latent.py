@@ -21,7 +21,8 @@ import pytest
 
 import oracle
 from parity_util import to_host
-from pic_workloads import config4, normal_values, pool_values, random_small, with_paged_pool
+from pic_workloads import (Chunk, Entry, Request, Workload, config4, normal_values, pool_values,
+                           random_small, with_paged_pool)
 
 pytestmark = pytest.mark.gpu
 U = 2.0 ** -24
@@ -116,6 +117,37 @@ def test_deepseek_v3_request_full(torch_cuda, layer, heads):
     say(f"latent deepseek-v3 full layer={layer} heads={heads}")
     err, tol, vmax = run_case(torch_cuda, wl, heads, 7, layer=layer, sink_tokens=4,
                               sink_bias=-15.0)
+    say(f"  max err {err:.3g} (bound {tol:.3g})")
+    assert err <= tol
+
+
+def _many_chunk_request(n_chunks, seed):
+    """One request: a 64-token cache prefix, then n_chunks chunks of 64 tokens
+    from a paged pool of 8-token pages, each moved by its own shift (chunk c
+    cached at base 3 c), behind 16-token cache pages; every 4th chunk keeps
+    its first 8 tokens for recompute."""
+    n, length, prefix, ps = n_chunks, 64, 64, 16
+    chunks = [Chunk(i * length, length, 3 * i) for i in range(n)]
+    ctx = prefix + n * length
+    pages = np.random.default_rng(seed).permutation(-(-ctx // ps)).astype(np.int32)
+    entries = [Entry(c, prefix + c * length, length, 8 if c % 4 == 0 else 0) for c in range(n)]
+    wl = Workload("many-chunk MLA request", "bf16", 1, 1, 576, 512, 64, "half", 10000.0, False,
+                  pool_tokens=n * length, chunks=chunks, requests=[Request(entries, pages, ctx)],
+                  page_size=ps, n_phys_pages=len(pages))
+    return with_paged_pool(wl, page_size=8, seed=seed)
+
+
+@pytest.mark.parametrize("heads", [128, 256])
+def test_items_of_several_blocks(torch_cuda, heads):
+    """The 128-head kernel (four waves of two head groups) on work items of
+    several blocks: 1,024 chunks of 64 tokens, each with its own shift, so a
+    block (at most 4 shift tables) covers at most 4 chunks while an item
+    covers about 5 (128 heads: 256 items) or 9 (256 heads: two head-group
+    sets, 128 items) of them; pool pages of 8 tokens make tiles of 8
+    positions."""
+    wl = _many_chunk_request(1024, 40 + heads)
+    say(f"latent items of several blocks heads={heads}")
+    err, tol, vmax = run_case(torch_cuda, wl, heads, 40 + heads, sink_tokens=4, sink_bias=-15.0)
     say(f"  max err {err:.3g} (bound {tol:.3g})")
     assert err <= tol
 
