@@ -425,7 +425,88 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                 }
             }
         };
+        // one-wave workgroups (steps of one 16-position tile): lane 16 g + p
+        // turns the 8 planes of dim group g of position p, whose x and y (half
+        // pairing) or pairs (interleaved) are its two pieces of the rotary
+        // k-steps' slabs; in fp32 first, with the fp64 turn only for the
+        // planes where fp32 could round otherwise (rotate.hpp: turn_f32), each
+        // under its own branch, so a wave pays fp64 work for the planes some
+        // lane flagged.  The fp32 cos and sin are the fp64 table's, rounded.
+        auto turn8 = [&](int bb) {
+            const int p = r16;
+            const uint32_t slot1 = min(s_pslot[bb][p], static_cast<uint32_t>(kBlockTabs));
+            const bool on = slot1 != 0u;
+            const double2 *tab = s_cs[on ? slot1 - 1 : 0];
+            uint4 &ka = s_stage[bb][kRopeStep * 64 + 16 * g + p];
+            uint4 &kb = s_stage[bb][(kRopeStep + 1) * 64 + 16 * g + p];
+            const uint4 va = ka, vb = kb;
+            const uint32_t wa[4] = {va.x, va.y, va.z, va.w}, wb[4] = {vb.x, vb.y, vb.z, vb.w};
+            // planes of the lane: half pairing 8 g + e (x in piece a, y in b);
+            // interleaved 4 g + k (piece a, word k) and 16 + 4 g + k (piece b)
+            auto plane = [&](int e) {
+                return STYLE == PIC_ROPE_HALF ? 8 * g + e : (e < 4 ? 4 * g + e : 16 + 4 * g + e - 4);
+            };
+            uint32_t na[4], nb[4];
+            uint64_t redo[8];
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                if constexpr (STYLE == PIC_ROPE_HALF) {
+                    const double2 d0 = tab[plane(2 * k)], d1 = tab[plane(2 * k + 1)];
+                    float rx0, ry0, rx1, ry1;
+                    redo[2 * k] = __ballot(on && turn_f32(__uint_as_float(wa[k] << 16), __uint_as_float(wb[k] << 16),
+                                                          static_cast<float>(d0.x), static_cast<float>(d0.y), &rx0, &ry0));
+                    redo[2 * k + 1] = __ballot(on && turn_f32(__uint_as_float(wa[k] & 0xFFFF0000u),
+                                                              __uint_as_float(wb[k] & 0xFFFF0000u),
+                                                              static_cast<float>(d1.x), static_cast<float>(d1.y), &rx1, &ry1));
+                    na[k] = pack2_bf16(rx0, rx1);
+                    nb[k] = pack2_bf16(ry0, ry1);
+                } else {
+                    const double2 da = tab[plane(k)], db = tab[plane(4 + k)];
+                    float rx, ry;
+                    redo[k] = __ballot(on && turn_f32(__uint_as_float(wa[k] << 16), __uint_as_float(wa[k] & 0xFFFF0000u),
+                                                      static_cast<float>(da.x), static_cast<float>(da.y), &rx, &ry));
+                    na[k] = pack2_bf16(rx, ry);
+                    redo[4 + k] = __ballot(on && turn_f32(__uint_as_float(wb[k] << 16), __uint_as_float(wb[k] & 0xFFFF0000u),
+                                                          static_cast<float>(db.x), static_cast<float>(db.y), &rx, &ry));
+                    nb[k] = pack2_bf16(rx, ry);
+                }
+            }
+            uint64_t any_redo = 0;
+#pragma unroll
+            for (int e = 0; e < 8; e++) any_redo |= redo[e];
+            if (any_redo != 0) {  // uniform
+#pragma unroll
+                for (int e = 0; e < 8; e++) {
+                    if (!((redo[e] >> lane) & 1)) continue;
+                    const double2 cs = tab[plane(e)];
+                    if constexpr (STYLE == PIC_ROPE_HALF) {
+                        // plane e: half e % 2 of word e / 2 in both pieces
+                        const int k = e >> 1, sh = 16 * (e & 1);
+                        const double x = (e & 1) ? bf16_hi(wa[k]) : bf16_lo(wa[k]);
+                        const double y = (e & 1) ? bf16_hi(wb[k]) : bf16_lo(wb[k]);
+                        const uint32_t keep = 0xFFFF0000u >> sh;
+                        na[k] = (na[k] & keep) | (f64_to_bf16(x * cs.x - y * cs.y) << sh);
+                        nb[k] = (nb[k] & keep) | (f64_to_bf16(x * cs.y + y * cs.x) << sh);
+                    } else {
+                        // plane e: word e % 4 of piece a (e < 4) or b
+                        const uint32_t w = e < 4 ? wa[e & 3] : wb[e & 3];
+                        const double x = bf16_lo(w), y = bf16_hi(w);
+                        const uint32_t r = pack_bf16(x * cs.x - y * cs.y, x * cs.y + y * cs.x);
+                        if (e < 4) na[e & 3] = r;
+                        else nb[e & 3] = r;
+                    }
+                }
+            }
+            if (on) {
+                ka = make_uint4(na[0], na[1], na[2], na[3]);
+                kb = make_uint4(nb[0], nb[1], nb[2], nb[3]);
+            }
+        };
         auto turn = [&](int bb) {
+            if constexpr (W == 1 && TPS == 1) {
+                turn8(bb);
+                return;
+            }
             for (int u = tid; u < 16 * kStepPos; u += 64 * W) {
                 if (s_pslot[bb][(u >> 2) % kStepPos] == 0u) continue;
                 turn_unit(bb, u);
