@@ -909,13 +909,14 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     st = ensure_device_plan(plan, stream_);
     if (st) return st;
 
-    // head groups per workgroup (one wave each) and workgroups per item
+    // head groups per workgroup (W = 8: four waves of two groups, the rest
+    // one wave per group) and workgroups per item
     const int G = args->num_q_heads / kGroupHeads;
     const int W = G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1;
     const int sets = G / W;
-    // concurrent workgroups per CU: one of eight waves, two with two 37 KB
-    // staging buffers each, kPerCu1 one-wave workgroups; eight waves of up to
-    // 256 registers fill a CU's register file
+    // concurrent workgroups per CU: one of four 512-register waves (four
+    // 37 KB staging buffers), two with two staging buffers each, kPerCu1
+    // one-wave workgroups
     const int per_cu = W == 8 ? 1 : W == 1 ? kPerCu1 : 2;
     const int64_t slots = static_cast<int64_t>(cu_count()) * per_cu;
     const int64_t target = std::max<int64_t>(1, slots / sets);
