@@ -236,12 +236,82 @@ void fill_info(Problem *p, int64_t tokens_written, int64_t tokens_masked, int64_
     p->info.tile_tokens = p->tile_tokens;
 }
 
+// Launch order of a copy plan whose pool rows are read more than once (a
+// chunk placed into several requests).  In request order, the next read of a
+// repeated chunk lies a whole layer of traffic later, far past any cache.
+// Instead, the tiles of every placement of one chunk are merged by their
+// first token in the chunk, so that tiles reading the same rows are launched
+// together, and each chunk's merged run goes to one of eight queues (the
+// shortest so far) that are then interleaved: workgroup w of a launch runs on
+// XCD w % 8 (the same offset for every layer of a launch), so the placements
+// of a chunk share that XCD's L2 and all but the first read of a row hit it.
+// Tiles write disjoint rows, so the order changes no result.  ent_tile0[e]
+// is entry e's first tile (its tiles run to the next entry's first).
+constexpr int kXcds = 8;
+
+void order_tiles_by_source(Problem *p, int n_chunks, const std::vector<int32_t> &ent_chunk,
+                           const std::vector<int32_t> &ent_tile0,
+                           const std::vector<int32_t> &tile_off) {
+    const int32_t n_ent = static_cast<int32_t>(ent_chunk.size());
+    const int32_t n_tiles = static_cast<int32_t>(p->tiles.size());
+    if (n_ent < 2) return;
+    // entries grouped by chunk, chunks in the order of their first placement
+    std::vector<int32_t> first(static_cast<size_t>(n_chunks), -1), last(static_cast<size_t>(n_chunks), -1),
+        next(static_cast<size_t>(n_ent), -1), chunk_order;
+    for (int32_t e = 0; e < n_ent; e++) {
+        const int32_t c = ent_chunk[e];
+        if (first[c] < 0) {
+            first[c] = e;
+            chunk_order.push_back(c);
+        } else {
+            next[last[c]] = e;
+        }
+        last[c] = e;
+    }
+    auto tile_end = [&](int32_t e) { return e + 1 < n_ent ? ent_tile0[e + 1] : n_tiles; };
+    // each queue a list of tile indices
+    std::vector<std::vector<int32_t>> queue(kXcds);
+    for (auto &q : queue) q.reserve(static_cast<size_t>(n_tiles / kXcds + 1));
+    std::vector<int32_t> cur, end;
+    for (int32_t c : chunk_order) {
+        size_t j = 0;
+        for (size_t m = 1; m < queue.size(); m++)
+            if (queue[m].size() < queue[j].size()) j = m;
+        std::vector<int32_t> &q = queue[j];
+        if (next[first[c]] < 0) {  // placed once
+            for (int32_t t = ent_tile0[first[c]]; t < tile_end(first[c]); t++) q.push_back(t);
+            continue;
+        }
+        cur.clear();
+        end.clear();
+        for (int32_t e = first[c]; e >= 0; e = next[e]) {
+            cur.push_back(ent_tile0[e]);
+            end.push_back(tile_end(e));
+        }
+        // k-way merge by first token (k: the chunk's placements, a few)
+        for (;;) {
+            int best = -1;
+            for (size_t k = 0; k < cur.size(); k++)
+                if (cur[k] < end[k] && (best < 0 || tile_off[cur[k]] < tile_off[cur[best]]))
+                    best = static_cast<int>(k);
+            if (best < 0) break;
+            q.push_back(cur[best]++);
+        }
+    }
+    std::vector<DevTile> out;
+    out.reserve(p->tiles.size());
+    for (size_t i = 0; out.size() < p->tiles.size(); i++)
+        for (const auto &q : queue)
+            if (i < q.size()) out.push_back(p->tiles[q[i]]);
+    p->tiles.swap(out);
+}
+
 // Tiles of tokens [from, to) of one placement: at most tile_tokens tokens,
 // and never across a page of a paged destination or a paged pool, so each
 // tile has one source and one destination row base with consecutive rows
 // after them.
 void add_tiles(Problem *p, const HostEntry &e, const int32_t *dst_pages, const int32_t *src_pages,
-               int32_t from, int32_t to) {
+               int32_t from, int32_t to, std::vector<int32_t> *offs = nullptr) {
     if (from >= to) return;
     const int64_t sps = p->src_page_size, ps = p->page_size;
     // page and slot of the first token, then advanced tile by tile
@@ -273,6 +343,7 @@ void add_tiles(Problem *p, const HostEntry &e, const int32_t *dst_pages, const i
         }
         tile.ntok = n;
         p->tiles.push_back(tile);
+        if (offs) offs->push_back(t);
         t += n;
         if (src_pages && (s_slot += n) == sps) {
             s_slot = 0;
@@ -478,6 +549,12 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     std::unordered_map<int64_t, int32_t> table_of_delta;
     std::vector<int32_t> cs_of_entry;
     int64_t written = 0, masked = 0;
+    // chunk-relative first token of every tile, and every entry's tiles, for
+    // the launch order below
+    std::vector<int32_t> tile_off;
+    std::vector<int32_t> ent_chunk, ent_tile0;
+    const bool reorder = p.launch.stream_loads == 0;
+    if (reorder) tile_off.reserve(p.tiles.capacity());
     for (int r = 0; r < n_requests; r++) {
         const pic_request &rq = requests[r];
         for (int j = 0; j < rq.n_entries; j++) {
@@ -498,14 +575,20 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
             const HostEntry he{c.token_start, e.dst_offset, r, 0, cs_idx, 0};
             p.entries.push_back(he);
             cs_of_entry.push_back(cs_idx);
+            if (reorder) {
+                ent_chunk.push_back(e.chunk_id);
+                ent_tile0.push_back(static_cast<int32_t>(p.tiles.size()));
+            }
             add_tiles(&p, he, paged ? rq.page_table : nullptr,
-                      src_paged ? c.page_table : nullptr, e.recompute_k, e.length);
+                      src_paged ? c.page_table : nullptr, e.recompute_k, e.length,
+                      reorder ? &tile_off : nullptr);
             p.bounds.insert(p.bounds.end(), {r, e.dst_offset, e.dst_offset + e.length});
             p.recompute.insert(p.recompute.end(), {r, e.dst_offset, e.dst_offset + e.recompute_k});
             written += e.length - e.recompute_k;
             masked += e.recompute_k;
         }
     }
+    if (reorder) order_tiles_by_source(&p, n_chunks, ent_chunk, ent_tile0, tile_off);
     int64_t context_tokens = 0;
     for (int r = 0; r < n_requests; r++) {
         const pic_request &rq = requests[r];
