@@ -366,9 +366,15 @@ __device__ __forceinline__ void mla_block_body(const MlaArgs &a, int32_t layer) 
                     s_pbias[bf][16 * tau + r16] = valid ? (damp ? bias2 : 0.f) : -INFINITY;
                 }
                 const uint16_t *row = (pool ? a.pool_k : a.cache_k) + off + 8 * g;
-                for (int j = TPS * wave + tau; j < kSlabs; j += TPS * W) {
-                    const int s = j / TPS;
-                    load_lds16(row + 32 * s, &s_stage[bf][j * 64]);
+                if constexpr (W == 1 && TPS == 1) {
+                    // the row's 18 k-steps with one base address: slab s at
+                    // 1 KB s in LDS, k-step s 64 s bytes into the row
+                    load_lds16_row18(row, &s_stage[bf][0]);
+                } else {
+                    for (int j = TPS * wave + tau; j < kSlabs; j += TPS * W) {
+                        const int s = j / TPS;
+                        load_lds16(row + 32 * s, &s_stage[bf][j * 64]);
+                    }
                 }
             }
         };

@@ -38,6 +38,37 @@ __device__ __forceinline__ void load_lds16(const void *src, const void *lds) {
         : "memory");
 }
 
+// Eighteen such loads in one asm block: load k takes the 16 bytes at
+// src + 64 k (the instruction's offset field) into lds + 1024 k + 16 l, so a
+// 576-dim bf16 row's 18 k-steps of 32 dims land in 18 consecutive 1 KB
+// slabs.  M0 of load k is lds + 960 k (1024 k less the offset), computed by
+// the compiler into scalar registers, so the block itself only moves them
+// into M0 (no scalar arithmetic, which would clobber SCC); M0 is saved and
+// restored around the block.  lds must be the same for every lane.
+#define PIC_LDS_ROW_LOAD(k, o) \
+    "s_mov_b32 m0, %" #k "\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:" #o "\n\t"
+__device__ __forceinline__ void load_lds16_row18(const void *src, const void *lds) {
+    const uint32_t b = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)lds)));
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        PIC_LDS_ROW_LOAD(2, 0) PIC_LDS_ROW_LOAD(3, 64) PIC_LDS_ROW_LOAD(4, 128)
+        PIC_LDS_ROW_LOAD(5, 192) PIC_LDS_ROW_LOAD(6, 256) PIC_LDS_ROW_LOAD(7, 320)
+        PIC_LDS_ROW_LOAD(8, 384) PIC_LDS_ROW_LOAD(9, 448) PIC_LDS_ROW_LOAD(10, 512)
+        PIC_LDS_ROW_LOAD(11, 576) PIC_LDS_ROW_LOAD(12, 640) PIC_LDS_ROW_LOAD(13, 704)
+        PIC_LDS_ROW_LOAD(14, 768) PIC_LDS_ROW_LOAD(15, 832) PIC_LDS_ROW_LOAD(16, 896)
+        PIC_LDS_ROW_LOAD(17, 960) PIC_LDS_ROW_LOAD(18, 1024) PIC_LDS_ROW_LOAD(19, 1088)
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(b), "s"(b + 960), "s"(b + 2 * 960), "s"(b + 3 * 960), "s"(b + 4 * 960),
+          "s"(b + 5 * 960), "s"(b + 6 * 960), "s"(b + 7 * 960), "s"(b + 8 * 960), "s"(b + 9 * 960),
+          "s"(b + 10 * 960), "s"(b + 11 * 960), "s"(b + 12 * 960), "s"(b + 13 * 960),
+          "s"(b + 14 * 960), "s"(b + 15 * 960), "s"(b + 16 * 960), "s"(b + 17 * 960)
+        : "memory");
+}
+#undef PIC_LDS_ROW_LOAD
+
 // Wait until at most N of the wave's vector memory loads are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
