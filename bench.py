@@ -691,6 +691,10 @@ def main():
         out["tokens_per_s"] = round(W["token_layers"] * args.steps / (total_ms * 1e-3), 1)
     if launches > 1:
         out["roofline"]["launches_per_step"] = launches
+    if out["roofline"].get("traffic"):
+        # the HBM bandwidth the launch actually used (counter traffic over the
+        # same launch time): below `achieved` where repeated rows come from cache
+        out["roofline"]["traffic_gbps"] = round(out["roofline"]["traffic"] / (avg_kernel_ms * 1e-3) / 1e9, 1)
     if "flops" in W:  # matrix-core work beside the bytes: bf16 dense peak 2.5 PFLOP/s
         tf = W["flops"] / launches / (avg_kernel_ms * 1e-3) / 1e12
         out["roofline"]["mfma"] = {"achieved": round(tf, 1), "peak": 2500.0, "unit": "TFLOP/s",

@@ -191,6 +191,43 @@ def config3(seed: int = 0, n_layers: int = 32, n_requests: int = 64,
                     page_size=ps, n_phys_pages=total_pages)
 
 
+def repeat_heavy(seed: int, dtype: str = "bf16", style: str = "half", n_layers: int = 2,
+                 n_chunks: int = 24, n_requests: int = 20, max_len: int = 300,
+                 page_size: int = 16) -> Workload:
+    """Batched RAG in small: a pool of n_chunks chunks of ragged length
+    (1..max_len), n_requests requests each placing 3..8 of them drawn with
+    replacement (so every chunk is placed several times, at offsets with every
+    residue modulo the page), behind ragged prefixes, with recompute_k of 0,
+    1 or a random part of the entry and entries that place only a prefix of
+    their chunk; paged destination from one global random permutation."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, max_len, size=n_chunks, endpoint=True)
+    starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+    chunks = [Chunk(int(s), int(n)) for s, n in zip(starts, lens)]
+    reqs_entries, reqs_pages = [], []
+    for _ in range(n_requests):
+        k = int(rng.integers(3, 8, endpoint=True))
+        ids = rng.integers(0, n_chunks, size=k)
+        pos = int(rng.integers(0, 40))
+        entries = []
+        for c in ids:
+            ln = int(lens[c]) if rng.random() < 0.8 else int(rng.integers(1, lens[c], endpoint=True))
+            rk = int(rng.choice([0, 0, 1, int(rng.integers(0, ln + 1))]))
+            entries.append(Entry(int(c), pos, ln, rk))
+            pos += ln + int(rng.integers(0, 5))
+        reqs_entries.append(entries)
+        reqs_pages.append(-(-pos // page_size))
+    total_pages = int(sum(reqs_pages))
+    perm = rng.permutation(total_pages).astype(np.int32)
+    requests, at = [], 0
+    for entries, npg in zip(reqs_entries, reqs_pages):
+        requests.append(Request(entries, perm[at:at + npg].copy()))
+        at += npg
+    return Workload(f"repeat heavy {seed}", dtype, n_layers, 2, 128, 0, 128, style, 500000.0,
+                    True, pool_tokens=int(lens.sum()), chunks=chunks, requests=requests,
+                    page_size=page_size, n_phys_pages=total_pages)
+
+
 def config4(seed: int = 0, n_layers: int = 61) -> Workload:
     """MLA (DeepSeek-V3 shape): 61 layers, one 576-wide latent row per token
     (512 content dims copied, 64 rotary dims rotated, theta 1e4), bf16;

@@ -15,8 +15,8 @@ import pytest
 import oracle
 from parity_util import (check_stitch_case, compare_bits, compare_k, max_abs, to_host)
 from pic_workloads import (Chunk, Entry, Request, Segment, Workload, config1, config2, config3,
-                           config4, config5, pool_values, random_small, sentinel_like,
-                           with_paged_pool)
+                           config4, config5, pool_values, random_small, repeat_heavy,
+                           sentinel_like, with_paged_pool)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,22 @@ def test_random_small(torch_cuda, seed, dt, style, paged, mla):
     wl = random_small(seed, dtype=dt, style=style, paged=paged, mla=mla, n_requests=3,
                       n_layers=3, max_len=200)
     say(f"random_small seed={seed} {dt} {style} paged={paged} mla={mla}")
+    check_stitch_case(wl, seed=seed)
+
+
+@pytest.mark.parametrize("seed,dt,style,pool", [(0, "bf16", "half", False),
+                                               (1, "f32", "interleaved", False),
+                                               (2, "bf16", "interleaved", True),
+                                               (3, "f32", "half", True)])
+def test_repeated_chunks(torch_cuda, seed, dt, style, pool):
+    """Chunks placed many times over many requests: the planner launches the
+    placements of a chunk together, merged by source token and dealt to the
+    XCD queues, which must change no output.  Everything against the oracle."""
+    wl = repeat_heavy(seed, dtype=dt, style=style)
+    if pool:
+        wl = with_paged_pool(wl, page_size=16, seed=seed)
+    say(f"repeat_heavy seed={seed} {dt} {style} pool={pool}: "
+        f"{sum(len(r.entries) for r in wl.requests)} placements of {len(wl.chunks)} chunks")
     check_stitch_case(wl, seed=seed)
 
 
