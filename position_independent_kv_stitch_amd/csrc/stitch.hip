@@ -27,8 +27,11 @@
 // slice; INTERLEAVED: one word holding whole pairs), and copy units (the
 // non-rotary part of K, and V).  A lane owns the same units for every token,
 // so its unit offsets and its planes' cos/sin are computed once per tile and
-// kept in registers; all of a step's loads are issued before any store.
-// Consecutive lanes cover consecutive 16-byte words of a row, so a wave's
+// kept in registers.  A wave loads all of its steps of the tile first, each
+// step into registers of its own, and then turns and stores them step by
+// step, so its waits count down to the step they need instead of draining
+// the stores of the step before.  Consecutive lanes cover consecutive
+// 16-byte words of a row, so a wave's
 // accesses are fully coalesced (a bf16 GQA token row is 2 KiB of K and
 // 2 KiB of V).
 //
@@ -158,7 +161,7 @@ __device__ __forceinline__ void stw(void *base, int64_t elem, int esize, const u
 // destination rows; a wave step covers g tokens, whose rotary units (g * nr)
 // and copy units (g * (nck + nv)) are dealt to the 64 lanes, MAXR and MAXC
 // per lane.  Each lane's slot offsets and the cos/sin of its planes are set
-// up once per workgroup; all of a step's loads are issued before its stores.
+// up once per workgroup; all of the wave's loads are issued before its stores.
 template <typename E, int STYLE, int MAXR, int MAXC, int RB, int NTL>
 __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kernel(const KArgs a) {
     constexpr int VEC = Vec<E>::kElems;              // elements per 16-byte copy unit
@@ -204,7 +207,10 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
         d0 = layer * a.d_layer + T.dst_a * (a.mode == kPaged ? a.d_page : a.d_req) +
              static_cast<int64_t>(T.dst_b) * a.d_tok;
 
-    for (int blk = 0; blk < a.nblk; blk++) {
+    // the unit blocks of a step (one unless a row is very wide); with one,
+    // no loop, so that the compiler counts this step's memory operations
+    // exactly instead of assuming another iteration's are pending
+    auto do_blk = [&](const int blk) {
         int rs[MAXR], rd[MAXR];  // slot offsets from the step's first source/dest row
         int rq[MAXR];            // token of the step the slot belongs to
 #pragma unroll
@@ -251,35 +257,57 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
             }
         }
 
-        for (int t0 = wave * a.g; t0 < T.ntok; t0 += kWaves * a.g) {
+        // the wave's steps of the tile (at most kTileSteps: the planner cuts
+        // tiles of kTileSteps x 4 waves x g tokens) loaded first, each into
+        // registers of its own.  On gfx9 stores and loads share one counter,
+        // and a load into registers that a pending store still reads must
+        // wait for everything before it; with distinct registers every wait
+        // only counts down to the step it needs.
+        static_assert(kWaves >= 4, "a tile's steps per wave");
+        uint32_t A[kTileSteps][MAXR][NW], B[kTileSteps][MAXR][NW];
+        uint4 Cw[kTileSteps][MAXC];
+        // Loads are not predicated: a slot with no live token loads the
+        // tile's first row instead (always in bounds) and is not stored, so
+        // every wave issues the same loads in the same order and the waits
+        // can count them.
+#pragma unroll
+        for (int st = 0; st < kTileSteps; st++) {
+            const int t0 = (wave + kWaves * st) * a.g;
             const int lim = T.ntok - t0;  // slots of tokens q < lim are live
-            const int64_t sb = s0 + t0 * a.s_tok;
-            const int64_t db = d0 + t0 * a.d_tok;
-            uint32_t A[MAXR][NW], B[MAXR][NW];
-            uint4 Cw[MAXC];
+            const int64_t sb = s0 + static_cast<int64_t>(t0) * a.s_tok;
 #pragma unroll
             for (int i = 0; i < MAXR; i++) {
-                if (rq[i] < lim) {
-                    ldw<NW, NTL>(sk, sb + rs[i], ES, A[i]);
-                    if (STYLE == kHalf) ldw<NW, NTL>(sk, sb + rs[i] + half_off, ES, B[i]);
-                }
+                const int64_t o = rq[i] < lim ? sb + rs[i] : s0;
+                ldw<NW, NTL>(sk, o, ES, A[st][i]);
+                if (STYLE == kHalf) ldw<NW, NTL>(sk, rq[i] < lim ? o + half_off : s0, ES, B[st][i]);
             }
 #pragma unroll
             for (int i = 0; i < MAXC; i++)
-                if (cq[i] < lim) Cw[i] = ld16<NTL>(isv[i] ? sv : sk, sb + cs_[i], ES);
-#pragma unroll
-            for (int i = 0; i < MAXR; i++) {
-                if (rq[i] < lim) {
-                    if (turn) rotate_unit<E, STYLE, NW>(A[i], B[i], c, s);
-                    stw<NW>(dk, db + rd[i], ES, A[i]);
-                    if (STYLE == kHalf) stw<NW>(dk, db + rd[i] + half_off, ES, B[i]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < MAXC; i++)
-                if (cq[i] < lim) st16(isv[i] ? dv : dk, db + cd[i], ES, Cw[i]);
+                Cw[st][i] = ld16<NTL>(isv[i] ? sv : sk, cq[i] < lim ? sb + cs_[i] : s0, ES);
         }
+#pragma unroll
+        for (int st = 0; st < kTileSteps; st++) {
+            const int t0 = (wave + kWaves * st) * a.g;
+            const int lim = T.ntok - t0;
+            const int64_t db = d0 + static_cast<int64_t>(t0) * a.d_tok;
+#pragma unroll
+            for (int i = 0; i < MAXR; i++) {
+                if (rq[i] < lim) {
+                    if (turn) rotate_unit<E, STYLE, NW>(A[st][i], B[st][i], c, s);
+                    stw<NW>(dk, db + rd[i], ES, A[st][i]);
+                    if (STYLE == kHalf) stw<NW>(dk, db + rd[i] + half_off, ES, B[st][i]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < MAXC; i++)
+                if (cq[i] < lim) st16(isv[i] ? dv : dk, db + cd[i], ES, Cw[st][i]);
+        }
+    };
+    if (a.nblk == 1) {
+        do_blk(0);
+        return;
     }
+    for (int blk = 0; blk < a.nblk; blk++) do_blk(blk);
 }
 
 // The bandwidth reference of the library: a plain copy with the stitch's
