@@ -388,9 +388,12 @@ typedef struct pic_attend_args {
  * page it covers must be in [0, dst_num_pages) (PIC_ERR_RANGE).  In-place
  * plans are refused (PIC_ERR_STATE).
  *
- * Each call takes its partial-result workspace in stream-ordered device
- * memory (hipMallocAsync / hipFreeAsync on `stream`), so calls on one plan
- * from several streams may overlap.  The plan's attention map is built on
+ * The partial results go to a workspace that the plan keeps per stream
+ * for its whole life (allocated by the first call on that stream, replaced
+ * by a larger one when a call needs more, freed by pic_plan_destroy), so
+ * calls on one stream reuse it in stream order and calls on one plan from
+ * several streams may overlap.  A stream handle is taken to name one stream
+ * for the plan's life.  The plan's attention map is built on
  * the host by the first call that needs it, and its device metadata for a
  * launch shape is uploaded once, ordered on the stream of the call that
  * first needs it; calls on other streams wait for that upload on their own

@@ -591,7 +591,7 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     const size_t need = p.ablocks.size() * static_cast<size_t>(args->num_q_heads) *
                         (static_cast<size_t>(D) + 2) * sizeof(float);
     void *work = nullptr;
-    st = call_workspace(need, stream_, &work);
+    st = call_workspace(plan, need, stream_, &work);
     if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
     const uint8_t *bm = static_cast<const uint8_t *>(blob->dev);
@@ -642,11 +642,6 @@ extern "C" pic_status pic_attend(pic_plan_t *plan, const pic_kv_view *pool,
     else
         e = p.style == PIC_ROPE_HALF ? launch_attend<uint16_t, PIC_ROPE_HALF>(a, nb, nr, args->layer, stream)
                                      : launch_attend<uint16_t, PIC_ROPE_INTERLEAVED>(a, nb, nr, args->layer, stream);
-    if (e != hipSuccess) {
-        (void)release_workspace(work, stream_);
-        return hip_fail(e, "attention kernel launch");
-    }
-    st = release_workspace(work, stream_);
-    if (st) return st;
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
     return note_use(plan, stream_);
 }

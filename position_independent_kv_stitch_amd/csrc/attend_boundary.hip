@@ -974,7 +974,7 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
     const size_t need = static_cast<size_t>(n_items) * H * row_slots *
                         (static_cast<size_t>(kDim) + 2) * sizeof(float);
     void *work = nullptr;
-    st = call_workspace(need, stream_, &work);
+    st = call_workspace(plan, need, stream_, &work);
     if (st) {
         release_call();
         return st;
@@ -1039,7 +1039,6 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
         PIC_BND_LAUNCH(2)
 #undef PIC_BND_LAUNCH
         default:
-            (void)release_workspace(work, stream_);
             release_call();
             return fail(PIC_ERR_INVALID_ARG, "internal: row tiles per wave %d", TT);
     }
@@ -1051,9 +1050,7 @@ extern "C" pic_status pic_attend_boundary(pic_plan_t *plan, const pic_kv_view *p
                            dim3(64), 0, stream, a);
         e = hipGetLastError();
     }
-    st = release_workspace(work, stream_);
     release_call();
     if (e != hipSuccess) return hip_fail(e, "boundary attention kernel launch");
-    if (st) return st;
     return note_use(plan, stream_);
 }

@@ -630,7 +630,7 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
     const size_t need = static_cast<size_t>(n_items) * static_cast<size_t>(args->num_q_heads) *
                         (static_cast<size_t>(kDim) + 2) * sizeof(float);
     void *work = nullptr;
-    st = call_workspace(need, stream, &work);
+    st = call_workspace(plan, need, stream, &work);
     if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
     const uint8_t *gm = static_cast<const uint8_t *>(blob->dev);
@@ -696,9 +696,7 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
                            dim3(64), 0, stream, a);
         e = hipGetLastError();
     }
-    st = release_workspace(work, stream);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    if (st) return st;
     return note_use(plan, stream);
 }
 

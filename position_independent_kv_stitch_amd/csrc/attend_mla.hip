@@ -942,7 +942,7 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
     const size_t need = static_cast<size_t>(n_items) * static_cast<size_t>(args->num_q_heads) *
                         (static_cast<size_t>(kVDim) + 2) * sizeof(float);
     void *work = nullptr;
-    st = call_workspace(need, stream_, &work);
+    st = call_workspace(plan, need, stream_, &work);
     if (st) return st;
     const uint8_t *dm = static_cast<const uint8_t *>(plan->d_mem);
     const uint8_t *lm = static_cast<const uint8_t *>(blob->dev);
@@ -990,8 +990,6 @@ extern "C" pic_status pic_attend_latent(pic_plan_t *plan, const pic_kv_view *poo
                            dim3(kCombineThreads), 0, stream, a);
         e = hipGetLastError();
     }
-    st = release_workspace(work, stream_);
     if (e != hipSuccess) return hip_fail(e, "latent attention kernel launch");
-    if (st) return st;
     return note_use(plan, stream_);
 }

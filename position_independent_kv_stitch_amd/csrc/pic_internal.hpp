@@ -186,11 +186,20 @@ pic_status check_view(const pic_kv_view *v, int vec, bool need_v, const char *na
 pic_status plan_blob(struct ::pic_plan *plan, int64_t key, void *stream,
                      const std::function<void(DevBlob &)> &make, const DevBlob **out);
 
-// Per-call workspace in stream-ordered device memory: allocated on `stream`
-// before the launches that use it and freed on `stream` after them, so calls
-// on different streams never share one.
-pic_status call_workspace(size_t bytes, void *stream, void **out);
-pic_status release_workspace(void *ptr, void *stream);
+// A workspace of at least `bytes` for a call's launches on `stream`: the
+// plan keeps one buffer per stream for its whole life, so the calls on one
+// stream reuse it in stream order and calls on different streams never share
+// one.  A buffer too small is replaced by a larger one (at least 1.5 times
+// the size); the old one is kept, with an event recorded on the stream after
+// the work already queued there, until pic_plan_destroy frees it.
+pic_status call_workspace(struct ::pic_plan *plan, size_t bytes, void *stream, void **out);
+
+// One stream's workspace of a plan.
+struct Workspace {
+    void *stream;  // hipStream_t
+    void *ptr;
+    size_t bytes;
+};
 
 // n bytes written by `fill` into pinned staging, copied ordered on `stream`
 // into fresh stream-ordered device memory *dmem (the caller frees it with
@@ -214,4 +223,6 @@ struct pic_plan {
     void *upload_event = nullptr;  // hipEvent_t
     std::map<int64_t, pic::DevBlob> blobs;
     std::vector<std::pair<void *, void *>> uses;  // (hipStream_t, hipEvent_t of its last use)
+    std::vector<pic::Workspace> work;  // attention workspaces, one per stream
+    std::vector<std::pair<void *, void *>> retired_work;  // (buffer, hipEvent_t after its last use)
 };

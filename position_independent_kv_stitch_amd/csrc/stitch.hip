@@ -514,22 +514,44 @@ pic_status plan_blob(struct ::pic_plan *plan, int64_t key, void *stream_,
     return PIC_OK;
 }
 
-pic_status call_workspace(size_t bytes, void *stream, void **out) {
+pic_status call_workspace(struct ::pic_plan *plan, size_t bytes, void *stream, void **out) {
     *out = nullptr;
-    const hipError_t e = hipMallocAsync(out, std::max<size_t>(bytes, 256),
-                                        static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) {
-        *out = nullptr;
-        (void)hipGetLastError();
-        return hip_fail(e, "hipMallocAsync (attention workspace)");
+    bytes = std::max<size_t>(bytes, 256);
+    std::lock_guard<std::mutex> lock(plan->mu);
+    Workspace *w = nullptr;
+    for (auto &x : plan->work)
+        if (x.stream == stream) w = &x;
+    if (w && w->bytes >= bytes) {
+        *out = w->ptr;
+        return PIC_OK;
     }
-    return PIC_OK;
-}
-
-pic_status release_workspace(void *ptr, void *stream) {
-    if (!ptr) return PIC_OK;
-    const hipError_t e = hipFreeAsync(ptr, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "hipFreeAsync (attention workspace)");
+    if (w) {
+        // outgrown: the work already queued on the stream may still read it
+        hipEvent_t ev = nullptr;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
+        if (e == hipSuccess) e = hipEventRecord(ev, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) {
+            if (ev) (void)hipEventDestroy(ev);
+            return hip_fail(e, "attention workspace retirement");
+        }
+        plan->retired_work.emplace_back(w->ptr, ev);
+        bytes = std::max(bytes, w->bytes + w->bytes / 2);
+        w->ptr = nullptr;
+        w->bytes = 0;
+    }
+    void *p = nullptr;
+    const hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(e, "hipMalloc (attention workspace)");
+    }
+    if (w) {
+        w->ptr = p;
+        w->bytes = bytes;
+    } else {
+        plan->work.push_back(Workspace{stream, p, bytes});
+    }
+    *out = p;
     return PIC_OK;
 }
 
@@ -539,7 +561,8 @@ pic_status note_use(struct ::pic_plan *plan, void *stream) {
     for (auto &u : plan->uses)
         if (u.first == stream) ev = static_cast<hipEvent_t>(u.second);
     if (!ev) {
-        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        // completion is all that destroy waits for: no system-scope fence
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
         if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
         plan->uses.emplace_back(stream, ev);
     }
@@ -946,6 +969,12 @@ void pic_plan_destroy(pic_plan_t *plan) {
             (void)hipEventSynchronize(static_cast<hipEvent_t>(u.second));
             (void)hipEventDestroy(static_cast<hipEvent_t>(u.second));
         }
+        for (auto &r : plan->retired_work) {
+            (void)hipEventSynchronize(static_cast<hipEvent_t>(r.second));
+            (void)hipEventDestroy(static_cast<hipEvent_t>(r.second));
+            (void)hipFree(r.first);
+        }
+        for (auto &w : plan->work) (void)hipFree(w.ptr);
         for (auto &kv : plan->blobs) {
             (void)hipEventSynchronize(static_cast<hipEvent_t>(kv.second.ready));
             (void)hipEventDestroy(static_cast<hipEvent_t>(kv.second.ready));

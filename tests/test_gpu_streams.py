@@ -1,7 +1,7 @@
 """One plan used from two HIP streams at once: pic_attend (matrix-core and
 vector paths), pic_attend_latent and pic_attend_boundary calls on the same
 plan are enqueued alternately on two streams without waiting, so their
-kernels overlap.  Each call has its own partial-result workspace and the
+kernels overlap.  Each stream has its own partial-result workspace and the
 plan's metadata is uploaded once (on whichever stream first needs it, the
 other stream waiting for the upload), so every output must equal the
 oracle within the bounds the single-stream tests use.  Streams keep the
@@ -118,6 +118,45 @@ def test_attend_latent_one_plan_two_streams(torch_cuda):
         say(f"attend_latent stream {i}: max err {err:.3g} (tol {tol:.3g})")
         assert err <= tol, (i, err, tol)
     plan.destroy()
+
+
+def test_attend_latent_workspace_grows(torch_cuda):
+    """The plan keeps a partial-result workspace per stream and replaces it
+    by a larger one when a call needs more (the need grows with the query
+    heads): calls at 16, 128, 32 and 256 heads alternate over two streams
+    without waiting, and the plan is destroyed right after they are
+    enqueued.  Destroy must wait for every call, including those that used a
+    workspace since replaced, and every output must match the oracle."""
+    torch = torch_cuda
+    import position_independent_kv_stitch_amd as pic
+    rng = np.random.default_rng(6)
+    wl = with_context(random_small(65, dtype="bf16", mla=True, paged=True, n_requests=3,
+                                   n_layers=1, max_len=300), rng)
+    pk, _ = pool_values(wl, seed=3, device="cuda:0")
+    ck = normal_values(wl.dst_shape(), "bf16", 4, "cuda:0")
+    scale = 192 ** -0.5
+    heads = [16, 128, 32, 256, 16, 128]
+    qs = [normal_values((len(wl.requests), h, 576), "bf16", 40 + i, "cuda:0")
+          for i, h in enumerate(heads)]
+    outs = [torch.empty((len(wl.requests), h, 512), dtype=torch.float32, device="cuda:0")
+            for h in heads]
+    plan = pic.Plan.from_workload(wl)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for i, (q, out) in enumerate(zip(qs, outs)):
+        pic.attend_latent(plan, pk, ck, q, layer=0, out=out, scale=scale,
+                          stream=streams[(i // 2) % 2])
+    plan.destroy()
+    torch.cuda.synchronize()
+    hpk, hck = to_host(pk), to_host(ck)
+    rows = np.concatenate([hpk.reshape(-1, 576), hck.reshape(-1, 576)])
+    for i, (q, out) in enumerate(zip(qs, outs)):
+        hq = to_host(q)
+        want = oracle.attend_latent(wl, hpk, hck, hq, 0, scale=scale)
+        err = float(np.abs(out.cpu().numpy().astype(np.float64) - want).max())
+        tol = matrix_bound(hq, rows, rows[:, :512], scale)
+        say(f"attend_latent call {i} ({heads[i]} heads): max err {err:.3g} (tol {tol:.3g})")
+        assert err <= tol, (i, err, tol)
 
 
 def test_attend_boundary_one_plan_two_streams(torch_cuda):
