@@ -89,6 +89,9 @@ WORKLOADS = {
              "8 kv heads x 128, bf16, 16-token pages, recompute_k 0 (stitch, paged); the pool "
              "holds all 32 layers, the destination the layers of one group, written by each "
              "layer-group launch of the step",
+    "batched-rag-tp4": "one GPU's share of the batched-RAG workload under 4-way tensor "
+                       "parallelism: the same 64 requests, pool chunks and pages with 2 of the 8 "
+                       "kv heads (a 512-byte K row per token), all 32 layers in one launch",
     "llama3-8b-paged": "32 layers, 8 kv heads x 128, bf16, one request of 8 chunks x 2048 tokens "
                        "after a 128-token prefix, 16-token pages, recompute_k 32 (stitch, paged)",
     "llama3-8b-paged-pool": "the default workload with its chunks read from a paged pool of "
@@ -179,7 +182,7 @@ def setup_workload(name, torch, pic):
         return setup_boundary(name, torch, pic)
     if name.startswith("cdc-rag"):
         return setup_cdc(name, torch, pic)
-    if name == DEFAULT:
+    if name in (DEFAULT, "batched-rag-tp4"):
         return setup_rag(name, torch, pic)
     wl = {"llama3-8b-paged": config2, "mla": config4, "single-layer": config1,
           "llama3-8b-paged-pool": lambda: with_paged_pool(config2(), page_size=16, seed=1)}[name]()
@@ -208,8 +211,8 @@ def setup_rag(name, torch, pic):
     the destination as many layers (a divisor of 32) as fit beside it; a
     step is one pic_stitch per layer group, each reading its own pool
     layers and writing the destination's layers."""
-    from pic_workloads import config3, layers_per_launch, pool_values, sentinel_like
-    wl = config3()
+    from pic_workloads import config3, layers_per_launch, pool_values, sentinel_like, tp_share
+    wl = config3() if name == DEFAULT else tp_share(config3(), 4)
     row = wl.n_heads * wl.row_dim * wl.esize
     pool_bytes = 2 * wl.n_layers * wl.pool_tokens * row
     dst_layer = 2 * wl.n_phys_pages * wl.page_size * row
@@ -240,7 +243,7 @@ def setup_rag(name, torch, pic):
            "hbm_gib": {"total": round(total / 2**30, 1), "free_before": round(free / 2**30, 1),
                        "pool": round(pool_bytes / 2**30, 1),
                        "destination": round(group * dst_layer / 2**30, 1)},
-           "parallelism": "single-gpu"}
+           "parallelism": "single-gpu" if name == DEFAULT else "one GPU's share of tp4"}
     return {"wl": wl, "step": step, "bytes": step_bytes,
             "token_layers": info["tokens_written"] * wl.n_layers,
             "launches": wl.n_layers // group,

@@ -126,6 +126,15 @@ class Workload:
         return replace(self, n_layers=n_layers)
 
 
+def tp_share(wl: Workload, tp: int) -> Workload:
+    """One GPU's share of `wl` under tensor parallelism of degree tp: the same
+    chunks, requests and pages with n_heads / tp KV heads (each GPU stitches
+    its own heads with the same plan; no data crosses GPUs)."""
+    if tp < 1 or wl.n_heads % tp:
+        raise ValueError(f"{wl.n_heads} KV heads do not split {tp} ways")
+    return replace(wl, name=f"{wl.name}, 1/{tp} of the KV heads", n_heads=wl.n_heads // tp)
+
+
 # ---------------------------------------------------------------- workloads
 
 def config1() -> Workload:

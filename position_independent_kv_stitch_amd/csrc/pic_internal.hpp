@@ -68,6 +68,7 @@ struct Units {
 // nr of them per token, 2^uph_shift per head.
 struct Launch {
     int32_t maxr = 1, maxc = 2, g = 1, nblk = 1;
+    int32_t wpt = 4;  // waves per tile: a workgroup of 4 waves takes 4 / wpt tiles
     int32_t rb = 16, nr = 0, uph_shift = 0;
     int32_t stream_loads = 0;  // 1: no pool row is read twice in a launch (non-temporal loads)
 };

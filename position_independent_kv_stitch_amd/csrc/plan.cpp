@@ -144,6 +144,20 @@ Launch launch_shape_of(int32_t dtype, const Units &u) {
 
 namespace {
 
+// Waves per tile.  A tile holds at most tile_tokens tokens and never crosses
+// a page of a paged destination or pool (page_bound, 0 for none).  With
+// narrow rows a wave step spans several tokens, and one or two waves' steps
+// then cover the longest tile the plan can have: a workgroup of four waves
+// takes 4 / wpt tiles, each wave every step of its share, instead of one
+// tile whose page leaves most of its waves' steps empty.
+void set_tile_waves(Problem *p, int64_t page_bound) {
+    const int64_t per_wave = int64_t{kTileSteps} * p->launch.g;
+    const int64_t longest =
+        page_bound > 0 ? std::min<int64_t>(p->tile_tokens, page_bound) : p->tile_tokens;
+    p->launch.wpt = longest <= per_wave ? 1 : longest <= 2 * per_wave ? 2 : 4;
+    p->tile_tokens = static_cast<int32_t>(std::min<int64_t>(p->tile_tokens, p->launch.wpt * per_wave));
+}
+
 // theta_i = b^(-2i/d) for i < rope_dim/2 in fp64 (libm), or the caller's table.
 std::vector<double> plane_frequencies(const pic_rope_config &rope) {
     const int half_r = rope.rope_dim / 2;
@@ -298,11 +312,14 @@ void order_tiles_by_source(Problem *p, int n_chunks, const std::vector<int32_t> 
             q.push_back(cur[best]++);
         }
     }
+    // a workgroup takes `group` consecutive tiles, so each queue contributes
+    // that many at a time
+    const size_t group = static_cast<size_t>((kBlockThreads / 64) / p->launch.wpt);
     std::vector<DevTile> out;
     out.reserve(p->tiles.size());
-    for (size_t i = 0; out.size() < p->tiles.size(); i++)
+    for (size_t i = 0; out.size() < p->tiles.size(); i += group)
         for (const auto &q : queue)
-            if (i < q.size()) out.push_back(p->tiles[q[i]]);
+            for (size_t k = i; k < i + group && k < q.size(); k++) out.push_back(p->tiles[q[k]]);
     p->tiles.swap(out);
 }
 
@@ -510,6 +527,11 @@ pic_status build_stitch(const pic_kv_shape *shape, const pic_rope_config *rope,
     p.u = u;
     p.launch = launch_shape_of(shape->dtype, u);
     p.tile_tokens = kTileSteps * 4 * p.launch.g;
+    {
+        int64_t bound = paged ? geom->dst_page_size : 0;
+        if (src_paged) bound = bound > 0 ? std::min<int64_t>(bound, sps) : sps;
+        set_tile_waves(&p, bound);
+    }
     {
         // Pool rows read more than once per layer (a chunk placed twice, or
         // chunks sharing rows) may be served from cache on the second read;
@@ -818,6 +840,7 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
         p.u = u;
         p.launch = launch_shape_of(shape->dtype, u);
         p.tile_tokens = kTileSteps * 4 * p.launch.g;
+        set_tile_waves(&p, page_size);
     };
     init(*turn, ut, kInPlace);
     turn->shape.has_v = 0;

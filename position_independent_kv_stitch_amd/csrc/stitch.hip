@@ -78,6 +78,8 @@ struct KArgs {
     int32_t nv, vph;        // V units per token / per head
     int32_t g;              // tokens per wave step
     int32_t nblk;           // unit blocks per step (1 unless a row is very wide)
+    int32_t wpt;            // waves per tile (1, 2 or 4): a workgroup takes 4 / wpt tiles
+    int32_t n_tiles;
 };
 
 constexpr int kHalf = PIC_ROPE_HALF;
@@ -156,12 +158,14 @@ __device__ __forceinline__ void stw(void *base, int64_t elem, int esize, const u
 #define PIC_OCCUPANCY_HINT
 #endif
 
-// One workgroup of four wave64s per (tile, layer).  A tile is up to 16 wave
-// steps of consecutive tokens of one placed chunk landing in consecutive
-// destination rows; a wave step covers g tokens, whose rotary units (g * nr)
-// and copy units (g * (nck + nv)) are dealt to the 64 lanes, MAXR and MAXC
-// per lane.  Each lane's slot offsets and the cos/sin of its planes are set
-// up once per workgroup; all of the wave's loads are issued before its stores.
+// One workgroup of four wave64s per (4 / wpt tiles, layer): wpt waves take a
+// tile of up to 4 wpt wave steps of consecutive tokens of one placed chunk
+// landing in consecutive destination rows (wpt < 4 where rows are so narrow
+// that a page of them fills fewer than four waves' steps); a wave step covers
+// g tokens, whose rotary units (g * nr) and copy units (g * (nck + nv)) are
+// dealt to the 64 lanes, MAXR and MAXC per lane.  Each lane's slot offsets
+// and the cos/sin of its planes are set up once per tile; all of the wave's
+// loads are issued before its stores.
 template <typename E, int STYLE, int MAXR, int MAXC, int RB, int NTL>
 __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kernel(const KArgs a) {
     constexpr int VEC = Vec<E>::kElems;              // elements per 16-byte copy unit
@@ -172,11 +176,15 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
     constexpr int kWaves = kBlockThreads / 64;
     constexpr int kNone = 1 << 30;                       // slot token index: unused slot
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
     const int ncv = a.nck + a.nv;
     const int half_off = STYLE == kHalf ? a.half_r : 0;
 
-    const DevTile T = a.tiles[blockIdx.x];
+    // the wave's tile, and its place among the tile's waves
+    const int tile = static_cast<int>(blockIdx.x) * (kWaves / a.wpt) + wave / a.wpt;
+    if (tile >= a.n_tiles) return;  // the last workgroup's spare waves (no barriers here)
+    const int wv = wave % a.wpt;
+    const DevTile T = a.tiles[tile];
     const int64_t layer = a.layer_begin + static_cast<int64_t>(blockIdx.y);
     const bool turn = T.cs_idx >= 0;
 
@@ -272,7 +280,7 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
         // can count them.
 #pragma unroll
         for (int st = 0; st < kTileSteps; st++) {
-            const int t0 = (wave + kWaves * st) * a.g;
+            const int t0 = (wv + a.wpt * st) * a.g;
             const int lim = T.ntok - t0;  // slots of tokens q < lim are live
             const int64_t sb = s0 + static_cast<int64_t>(t0) * a.s_tok;
 #pragma unroll
@@ -287,7 +295,7 @@ __global__ void __launch_bounds__(kBlockThreads) PIC_OCCUPANCY_HINT stitch_kerne
         }
 #pragma unroll
         for (int st = 0; st < kTileSteps; st++) {
-            const int t0 = (wave + kWaves * st) * a.g;
+            const int t0 = (wv + a.wpt * st) * a.g;
             const int lim = T.ntok - t0;
             const int64_t db = d0 + static_cast<int64_t>(t0) * a.d_tok;
 #pragma unroll
@@ -348,7 +356,9 @@ bool slot_offsets_fit(const Problem &p, int64_t tok, int64_t head) {
 
 template <typename E, int STYLE, int MAXR, int MAXC, int RB, int NTL>
 hipError_t launch_kernel(const KArgs &a, int n_tiles, int n_layers, hipStream_t stream) {
-    dim3 grid(static_cast<unsigned>(n_tiles), static_cast<unsigned>(n_layers));
+    const int per_group = (kBlockThreads / 64) / a.wpt;  // tiles per workgroup
+    dim3 grid(static_cast<unsigned>((n_tiles + per_group - 1) / per_group),
+              static_cast<unsigned>(n_layers));
     hipLaunchKernelGGL((stitch_kernel<E, STYLE, MAXR, MAXC, RB, NTL>), grid, dim3(kBlockThreads),
                        0, stream, a);
     return hipGetLastError();
@@ -381,6 +391,8 @@ hipError_t launch_style(const Problem &p, const KArgs &a, int n_layers, hipStrea
 hipError_t launch(const Problem &p, KArgs a, int n_layers, hipStream_t stream) {
     a.g = p.launch.g;
     a.nblk = p.launch.nblk;
+    a.wpt = p.launch.wpt;
+    a.n_tiles = static_cast<int32_t>(p.tiles.size());
     a.nr = p.launch.nr;
     a.uph_shift = p.launch.uph_shift;
     if (p.shape.dtype == PIC_DTYPE_F32)

@@ -402,7 +402,8 @@ def _subproblem(wl, req_ids):
     return sub, np.concatenate(src_tok), pages
 
 
-def test_config3_full_in_layer_groups(torch_cuda):
+@pytest.mark.parametrize("tp", [1, 2, 4])
+def test_config3_full_in_layer_groups(torch_cuda, tp):
     """Batched RAG: 64 requests over a 256-chunk pool, all 32 layers, in the
     benchmark's launch configuration: the pool holds every layer and each
     launch stitches one layer group of all requests into a destination
@@ -410,15 +411,17 @@ def test_config3_full_in_layer_groups(torch_cuda):
     layers in one launch on a 288 GiB GPU).  Every group: on every layer,
     unwritten rows keep the sentinel, no row is written twice and every
     written V row is its pool row; 4 sampled requests on 2 layers are
-    compared with the oracle."""
+    compared with the oracle.  tp = 4: one GPU's share under 4-way tensor
+    parallelism (2 of the 8 KV heads), the shape its stitch has there; tp = 2
+    the share under 2-way parallelism (two waves per tile instead of one)."""
     torch = torch_cuda
     import position_independent_kv_stitch_amd as pic
-    from pic_workloads import layers_per_launch
-    wl = config3()
+    from pic_workloads import layers_per_launch, tp_share
+    wl = tp_share(config3(), tp)
     torch.cuda.empty_cache()
     group = layers_per_launch(wl, torch.cuda.mem_get_info()[0])
     assert group > 0, "HBM too small for the batched-RAG pool"
-    say(f"config3: {group} layers per launch")
+    say(f"config3 (tp share 1/{tp}): {group} layers per launch")
     gw = wl.with_layers(group)
     say("config3: generating the 32-layer pool")
     pk, pv = pool_values(wl, seed=0, device="cuda:0")

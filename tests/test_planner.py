@@ -12,7 +12,7 @@ import position_independent_kv_stitch_amd as pic
 from position_independent_kv_stitch_amd import _binding as B
 from pic_workloads import (CONFIGS, Chunk, Entry, Request, Segment, Workload, config2,
                            config3, decode_batch, layers_per_launch, random_small,
-                           with_paged_pool)
+                           tp_share, with_paged_pool)
 
 ORACLE_TO_LIB = {"ok": "ok", "bad_arg": "invalid_arg", "range": "range", "overlap": "overlap"}
 
@@ -198,6 +198,28 @@ def test_batched_rag_plan_scales():
     pages = np.concatenate([r.page_table for r in wl.requests])
     assert len(np.unique(pages)) == len(pages) == wl.n_phys_pages
 
+
+
+def test_tensor_parallel_share():
+    """One GPU's share under tensor parallelism keeps every chunk, request and
+    page and divides the KV heads; the plan's bytes divide with them and
+    every token is still written once."""
+    wl = config3()
+    share = tp_share(wl, 4)
+    assert share.n_heads == 2 and wl.n_heads == 8
+    assert share.requests is wl.requests and share.chunks is wl.chunks
+    assert share.pool_shape() == (32, wl.pool_tokens, 2, 128)
+    assert share.dst_shape() == (32, wl.n_phys_pages, 16, 2, 128)
+    full, part = pic.Plan.from_workload(wl), pic.Plan.from_workload(share)
+    assert part.info["tokens_written"] == full.info["tokens_written"]
+    for key in ("bytes_read_per_layer", "bytes_written_per_layer"):
+        assert 4 * part.info[key] == full.info[key]
+    assert oracle.validate_stitch(share) == "ok"
+    full.destroy()
+    part.destroy()
+    for tp in (3, 16, 0):
+        with pytest.raises(ValueError):
+            tp_share(wl, tp)
 
 
 def test_batched_rag_layers_per_launch():
