@@ -69,6 +69,27 @@ def test_repeated_chunks(torch_cuda, seed, dt, style, pool):
     check_stitch_case(wl, seed=seed)
 
 
+@pytest.mark.parametrize("seed,heads,dt,pool", [(10, 1, "bf16", False), (11, 4, "bf16", True),
+                                                (12, 4, "f32", False), (13, 1, "f32", True),
+                                                (14, 4, "bf16", False), (15, 8, "bf16", True)])
+def test_tiles_grouped_per_workgroup(torch_cuda, seed, heads, dt, pool):
+    """Narrow rows into paged destinations: one or two waves' steps cover a
+    page of tokens, so a workgroup takes four or two tiles (ragged tiles, a
+    last workgroup with spare waves); then chunks placed many times at 4 KV
+    heads, whose source-ordered launch deals tiles to its queues two at a
+    time.  Everything against the oracle."""
+    from dataclasses import replace
+    wl = random_small(seed, dtype=dt, paged=True, n_requests=3, n_layers=2, max_len=200,
+                      dims=(heads, 128, 0, 128))
+    if pool:
+        wl = with_paged_pool(wl, page_size=8, seed=seed)
+    say(f"grouped tiles seed={seed} {heads} heads {dt} pool={pool} page={wl.page_size}")
+    check_stitch_case(wl, seed=seed)
+    rh = replace(repeat_heavy(seed, dtype=dt, n_layers=1), n_heads=4)
+    say(f"repeat_heavy at 4 heads, seed={seed}")
+    check_stitch_case(rh, seed=seed)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("paged", [False, True])
 def test_special_shifts(torch_cuda, dt, paged):
