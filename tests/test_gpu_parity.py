@@ -90,6 +90,35 @@ def test_tiles_grouped_per_workgroup(torch_cuda, seed, heads, dt, pool):
     check_stitch_case(rh, seed=seed)
 
 
+SWEEP_HEADS = (1, 2, 4, 8)
+
+
+@pytest.mark.parametrize("seed", range(100, 148))
+def test_random_shape_sweep(torch_cuda, seed):
+    """Seeded random shapes: 1-8 KV heads of 64 or 128 dims (rotary slice
+    all or part of the row), or latent MLA rows; fp32 or bf16, both pairings;
+    contiguous or paged destination, contiguous or paged pool.  Every element
+    against the oracle."""
+    rng = np.random.default_rng(seed)
+    dt = str(rng.choice(["f32", "bf16"]))
+    mla = bool(rng.random() < 0.2)
+    style = "half" if mla else str(rng.choice(["half", "interleaved"]))
+    dims = None
+    if not mla:
+        heads = int(rng.choice(SWEEP_HEADS))
+        row = int(rng.choice([64, 128]))
+        rdim = int(rng.choice([row, row // 2])) if style == "half" or dt == "f32" else row
+        dims = (heads, row, row - rdim, rdim)
+    wl = random_small(seed, dtype=dt, style=style, paged=bool(rng.random() < 0.6), mla=mla,
+                      n_requests=int(rng.integers(1, 4)), n_layers=int(rng.integers(1, 4)),
+                      max_len=int(rng.choice([40, 120, 300])), dims=dims)
+    if rng.random() < 0.4:
+        wl = with_paged_pool(wl, page_size=int(rng.choice([4, 8, 16])), seed=seed)
+    say(f"sweep seed={seed}: {wl.n_heads} heads x {wl.row_dim} (rotary {wl.rope_offset}+"
+        f"{wl.rope_dim}) {dt} {style} dst pages {wl.page_size} pool pages {wl.src_page_size}")
+    check_stitch_case(wl, seed=seed)
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("paged", [False, True])
 def test_special_shifts(torch_cuda, dt, paged):
