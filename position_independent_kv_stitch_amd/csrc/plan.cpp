@@ -846,7 +846,17 @@ pic_status build_rotate_paged(const pic_kv_shape *shape, const pic_rope_config *
     turn->shape.has_v = 0;
     turn->launch.stream_loads = 1;  // every turned slot is read once
     init(*copy, uc, kPaged);
-    copy->launch.stream_loads = 0;  // a shared page may be copied for several segments
+    // a shared page may be copied for several segments: then its second read
+    // can come from cache; if every copied page is read once, loads stream
+    {
+        std::vector<uint8_t> seen(static_cast<size_t>(n_phys_pages), 0);
+        bool repeat = false;
+        for (int g = 0; g < n_segments && !repeat; g++)
+            for (int32_t i = 0; i < segments[g].n_pages && !repeat; i++)
+                if (segments[g].cow && segments[g].cow[i] >= 0)
+                    repeat = seen[static_cast<size_t>(segments[g].pages[i])]++ != 0;
+        copy->launch.stream_loads = repeat ? 0 : 1;
+    }
     const std::vector<double> freq = plane_frequencies(*rope);
     std::unordered_map<int64_t, int32_t> tab_turn, tab_copy;
     auto table = [&](Problem &p, std::unordered_map<int64_t, int32_t> &m, int64_t delta) {
