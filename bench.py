@@ -616,9 +616,10 @@ def main():
                          "others time the remaining paths")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures the single-GPU path only (asked for --gpus {args.gpus}); the "
-              "stitch has no cross-GPU exchange, see the sharding notes in DESIGN.md",
-              file=sys.stderr)
+        print(f"bench.py measures the single-GPU path only (asked for --gpus {args.gpus}): under "
+              "tensor, pipeline or data parallelism each GPU stitches its own KV heads, layers or "
+              "requests with the same plan and nothing crosses GPUs; --workload batched-rag-tp4 "
+              "times one GPU's share under 4-way tensor parallelism", file=sys.stderr)
         sys.exit(2)
 
     import torch
