@@ -588,7 +588,8 @@ pic_status pic_registry_add(pic_registry_t *reg, const uint8_t *fp, int32_t leng
                             int32_t chunk_id);
 
 /* pic_registry_destroy -- wait for the pic_match calls that read the
- * registry's tables, release it.  NULL is a no-op. */
+ * registry's tables, release it and its per-stream temporaries.  NULL is a
+ * no-op. */
 void pic_registry_destroy(pic_registry_t *reg);
 
 /*
@@ -606,9 +607,12 @@ void pic_registry_destroy(pic_registry_t *reg);
  * (PIC_ERR_ALIGN).  The registry's fingerprint kind must equal
  * cfg->fingerprint (PIC_ERR_INVALID_ARG).
  * Work is enqueued on `stream` and the call does not wait for it: counts
- * stay on the device.  Temporary device memory of about 8 bytes per token
- * plus 36 bytes per kept record (min(n_tokens, max_out)) is allocated and
- * freed on `stream` (stream-ordered).
+ * stay on the device.  Temporaries take about 8 bytes per token plus 36
+ * bytes per kept record (min(n_tokens, max_out)) of device memory: with a
+ * registry, from a buffer the registry keeps per stream until
+ * pic_registry_destroy (replaced by a larger one when a call needs more;
+ * a stream handle is taken to name one stream for the registry's life);
+ * without one, allocated and freed on `stream` (stream-ordered).
  */
 pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32_t *tokens,
                      int64_t n_tokens, pic_match_t *out, int64_t max_out, int64_t *n_out,

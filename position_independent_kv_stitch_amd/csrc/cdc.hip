@@ -724,6 +724,16 @@ struct pic_registry {
     int device = -1;
     std::unique_ptr<pic::RegTable> table;                 // the current version
     std::vector<std::unique_ptr<pic::RegTable>> retired;  // older versions still in use
+    // pic_match's temporaries, one buffer per stream kept between calls (the
+    // calls on one stream reuse it in stream order), and outgrown buffers
+    // with an event recorded after their last use; all freed by destroy
+    struct Scratch {
+        hipStream_t stream;
+        void *ptr;
+        size_t bytes;
+    };
+    std::vector<Scratch> scratch;
+    std::vector<std::pair<void *, hipEvent_t>> retired_scratch;
 };
 
 namespace pic {
@@ -826,12 +836,55 @@ pic_status note_table_use(pic_registry *reg, hipStream_t stream) {
     for (auto &u : t.uses)
         if (u.first == stream) ev = u.second;
     if (!ev) {
-        const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        // completion is all that is waited for: no system-scope fence
+        const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
         if (e != hipSuccess) return hip_fail(e, "hipEventCreate");
         t.uses.emplace_back(stream, ev);
     }
     const hipError_t e = hipEventRecord(ev, stream);
     return e == hipSuccess ? PIC_OK : hip_fail(e, "hipEventRecord");
+}
+
+// At least `bytes` of pic_match temporaries for launches on `stream`, from
+// the registry's buffer for that stream (reg->mu held).  A buffer too small
+// is replaced by a larger one (at least 1.5 times the size) and kept, with an
+// event recorded after the work already queued on the stream, until destroy.
+pic_status registry_scratch(pic_registry *reg, hipStream_t stream, size_t bytes, void **out) {
+    *out = nullptr;
+    pic_registry::Scratch *w = nullptr;
+    for (auto &x : reg->scratch)
+        if (x.stream == stream) w = &x;
+    if (w && w->bytes >= bytes) {
+        *out = w->ptr;
+        return PIC_OK;
+    }
+    if (w) {
+        hipEvent_t ev = nullptr;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming | hipEventDisableSystemFence);
+        if (e == hipSuccess) e = hipEventRecord(ev, stream);
+        if (e != hipSuccess) {
+            if (ev) (void)hipEventDestroy(ev);
+            return hip_fail(e, "pic_match temporaries retirement");
+        }
+        reg->retired_scratch.emplace_back(w->ptr, ev);
+        bytes = std::max(bytes, w->bytes + w->bytes / 2);
+        w->ptr = nullptr;
+        w->bytes = 0;
+    }
+    void *p = nullptr;
+    const hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(e, "hipMalloc (pic_match temporaries)");
+    }
+    if (w) {
+        w->ptr = p;
+        w->bytes = bytes;
+    } else {
+        reg->scratch.push_back(pic_registry::Scratch{stream, p, bytes});
+    }
+    *out = p;
+    return PIC_OK;
 }
 
 }  // namespace
@@ -883,6 +936,14 @@ void pic_registry_destroy(pic_registry_t *reg) {
     // the registry's own work only: the launches that read any table version
     if (reg->table) pic::free_table(*reg->table, true);
     for (auto &t : reg->retired) pic::free_table(*t, true);
+    // every pic_match that used the temporaries recorded a use of some table
+    // version after its launches, and those have all completed now
+    for (auto &r : reg->retired_scratch) {
+        (void)hipEventSynchronize(r.second);
+        (void)hipEventDestroy(r.second);
+        (void)hipFree(r.first);
+    }
+    for (auto &x : reg->scratch) (void)hipFree(x.ptr);
     delete reg;
 }
 
@@ -941,9 +1002,16 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
     const size_t o_cfp = off;   off = align256(off + sizeof(uint64_t) * 4 * keep);
     const size_t o_cid = off;   off = align256(off + sizeof(int32_t) * keep);
     const size_t o_own = off;   off = align256(off + sizeof(int32_t) * keep);
+    // temporaries: the registry's buffer for this stream, or stream-ordered
+    // memory when there is no registry
     void *mem = nullptr;
-    e = hipMallocAsync(&mem, off, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMallocAsync (pic_match temporaries)");
+    if (reg) {
+        pic_status st = registry_scratch(reg, stream, off, &mem);
+        if (st != PIC_OK) return st;
+    } else {
+        e = hipMallocAsync(&mem, off, stream);
+        if (e != hipSuccess) return hip_fail(e, "hipMallocAsync (pic_match temporaries)");
+    }
     uint8_t *base = static_cast<uint8_t *>(mem);
     auto *flags = reinterpret_cast<uint64_t *>(base + o_flags);
     auto *bcnt = reinterpret_cast<int32_t *>(base + o_bcnt);
@@ -988,7 +1056,7 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
     scan_apply_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum, a.owner, keep);
     if (keep > 0) cdc_emit_kernel<<<lane_grid(keep), kLaneThreads, 0, stream>>>(a);
     e = hipGetLastError();
-    const hipError_t e2 = hipFreeAsync(mem, stream);
+    const hipError_t e2 = reg ? hipSuccess : hipFreeAsync(mem, stream);
     if (e != hipSuccess) return hip_fail(e, "pic_match launch");
     if (e2 != hipSuccess) return hip_fail(e2, "hipFreeAsync (pic_match temporaries)");
     if (reg) return note_table_use(reg, stream);  // the lock is still held
