@@ -192,11 +192,11 @@ __device__ uint64_t xxh64_tokens(const int32_t *t, int64_t n, uint64_t seed) {
 }
 
 // xxHash64 of t[0, n) by a group of four consecutive lanes (q = lane % 4):
-// lane q runs accumulator q over the 8-byte word q of every stripe, eight
+// lane q runs accumulator q over the 8-byte word q of every stripe, kG
 // stripes per load group, then the group's accumulators meet in lane q = 0,
 // which alone returns the hash.  All four lanes must call it together.
+template <int kG>
 __device__ uint64_t xxh64_tokens_x4(const int32_t *t, int64_t n, uint64_t seed, int q) {
-    constexpr int kG = 8;
     const int64_t stripes = n / 8;
     uint64_t acc = xx_acc_seed(seed, q);
     const int32_t *base = t + 2 * q;
@@ -591,7 +591,7 @@ __global__ __launch_bounds__(kLaneThreads) void cdc_chunk_kernel(MatchArgs a) {
         const int64_t s = chunk_start(a.ends, c), len = a.ends[c] - s;
         uint64_t fp[4] = {0, 0, 0, 0};
         if constexpr (G == 4) {
-            fp[0] = xxh64_tokens_x4(a.tok + s, len, a.fp_seed, q);
+            fp[0] = xxh64_tokens_x4<8>(a.tok + s, len, a.fp_seed, q);
         } else {
             fingerprint(a.tok + s, len, a.kind, a.fp_seed, fp);
         }
@@ -659,13 +659,16 @@ __global__ __launch_bounds__(kThreads) void scan_apply_kernel(int32_t *__restric
     }
 }
 
-// One lane per output record (the first max_out segments); the owner map
-// names each slot's chunk.
+// G lanes per output record (the first max_out segments; G = 4 for
+// xxHash64, whose windows are hashed like chunks, 1 for SHA-256); the owner
+// map names each slot's chunk, and lane q = 0 of the group writes the record.
+template <int G>
 __global__ __launch_bounds__(kLaneThreads) void cdc_emit_kernel(MatchArgs a) {
     const int64_t m = min(static_cast<int64_t>(a.counts[1]), a.n);
     const int64_t lim = m < a.max_out ? m : a.max_out;
-    for (int64_t s = static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x; s < lim;
-         s += static_cast<int64_t>(gridDim.x) * kLaneThreads) {
+    const int q = threadIdx.x % G;
+    for (int64_t s = (static_cast<int64_t>(blockIdx.x) * kLaneThreads + threadIdx.x) / G; s < lim;
+         s += static_cast<int64_t>(gridDim.x) * (kLaneThreads / G)) {
         const int64_t c = a.owner[s], k = s - a.seg[c];
         const int64_t cs = chunk_start(a.ends, c), ce = a.ends[c];
         pic_match_t r;
@@ -678,14 +681,21 @@ __global__ __launch_bounds__(kLaneThreads) void cdc_emit_kernel(MatchArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) fp[j] = a.cfp[4 * c + j];
         } else {
+            // (uniform over the group: its lanes share s)
             const int64_t ws = cs + k * a.window;
             const int64_t wl = ce - ws < a.window ? ce - ws : a.window;
-            fingerprint(a.tok + ws, wl, a.kind, a.fp_seed, fp);
+            if constexpr (G == 4) {
+                fp[0] = xxh64_tokens_x4<16>(a.tok + ws, wl, a.fp_seed, q);
+                fp[1] = fp[2] = fp[3] = 0;
+            } else {
+                fingerprint(a.tok + ws, wl, a.kind, a.fp_seed, fp);
+            }
             r.start = ws;
             r.length = static_cast<int32_t>(wl);
             r.level = 1;
-            r.chunk_id = reg_lookup(a.tab, a.mask, fp, static_cast<int32_t>(wl));
+            r.chunk_id = q == 0 ? reg_lookup(a.tab, a.mask, fp, static_cast<int32_t>(wl)) : -1;
         }
+        if (q != 0) continue;
         r.reserved = 0;
         memcpy(r.fp, fp, 32);
         a.out[s] = r;
@@ -1054,7 +1064,12 @@ pic_status pic_match(pic_registry_t *reg, const pic_cdc_config *cfg, const int32
     scan_reduce_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum);
     scan_top_kernel<<<1, 1024, 0, stream>>>(ssum, 0, &counts[0], &counts[1], n_out);
     scan_apply_kernel<<<gb, kThreads, 0, stream>>>(a.seg, &counts[0], ssum, a.owner, keep);
-    if (keep > 0) cdc_emit_kernel<<<lane_grid(keep), kLaneThreads, 0, stream>>>(a);
+    if (keep > 0) {
+        if (cfg->fingerprint == PIC_FP_XXH64)
+            cdc_emit_kernel<4><<<lane_grid(4 * keep), kLaneThreads, 0, stream>>>(a);
+        else
+            cdc_emit_kernel<1><<<lane_grid(keep), kLaneThreads, 0, stream>>>(a);
+    }
     e = hipGetLastError();
     const hipError_t e2 = reg ? hipSuccess : hipFreeAsync(mem, stream);
     if (e != hipSuccess) return hip_fail(e, "pic_match launch");
