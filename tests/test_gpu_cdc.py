@@ -190,3 +190,33 @@ def test_rag_stream_full_size(torch_cuda, kind):
     hits = int((recs["chunk_id"][:m] >= 0).sum())
     say(f"  segments {m}, registered {hits}")
     assert hits > len(want) // 3
+
+
+def test_registry_temporaries_per_stream(torch_cuda):
+    """With a registry, pic_match keeps its temporaries in a buffer per
+    stream and replaces it by a larger one when a call needs more.  Calls of
+    growing and shrinking length alternate over two streams without waiting,
+    each with its own output, and the registry is destroyed right after they
+    are enqueued: destroy must wait for every call, also those whose buffer
+    was since replaced, and every call must equal the oracle."""
+    import position_independent_kv_stitch_amd as pic
+    torch = torch_cuda
+    th = 1 << 56
+    docs = [random_tokens(2500, seed=500 + i) for i in range(4)]
+    entries = registry_of(docs, th, "xxh64", 128)
+    reg = pic.Registry("xxh64", entries)
+    sizes = [3000, 20000, 500, 60000, 7000, 120000]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    inputs, outs = [], []
+    for i, n in enumerate(sizes):
+        toks = np.concatenate([random_tokens(n, seed=600 + i), docs[i % 4]])
+        inputs.append(toks)
+        t = torch.from_numpy(toks).to("cuda:0")
+        torch.cuda.synchronize()
+        outs.append((t,) + pic.match(t, th, reg, kind="xxh64", stream=streams[(i // 2) % 2]))
+    reg.destroy()
+    torch.cuda.synchronize()
+    for i, (toks, (_, out, n_out)) in enumerate(zip(inputs, outs)):
+        recs, m = pic.match_records(out, n_out)
+        say(f"cdc temporaries call {i}: {len(toks)} tokens, {m} segments")
+        assert_same(recs, m, cdc.match(toks, th, entries, kind="xxh64"))
