@@ -574,13 +574,29 @@ __global__ void __launch_bounds__(64) gqa_combine_kernel(const GqaArgs a) {
     const float f = mine ? __builtin_amdgcn_exp2f(m - M) : 0.f;
     float L = lsum * f;
     for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    // the items' rows read eight at a time, all eight loads in flight before
+    // the first is used (a request's items are summed by one wave, so the
+    // loop is latency-bound otherwise); a slot past the last item repeats it
+    // with weight 0, which adds exactly zero
+    constexpr int kInFlight = 8;
+    const float *acc = a.part_acc + (static_cast<int64_t>(i0) * hq + j) * kDim + 2 * lane;
+    const int64_t item_stride = hq * kDim;
     float2 O = make_float2(0.f, 0.f);
-    for (int t = 0; t < n; t++) {
-        const float ft = __shfl(f, t, 64);
-        const float2 v = *reinterpret_cast<const float2 *>(
-            a.part_acc + ((static_cast<int64_t>(i0) + t) * hq + j) * kDim + 2 * lane);
-        O.x += v.x * ft;
-        O.y += v.y * ft;
+    for (int t0 = 0; t0 < n; t0 += kInFlight) {
+        float2 v[kInFlight];
+        float ft[kInFlight];
+#pragma unroll
+        for (int k = 0; k < kInFlight; k++) {
+            const int t = min(t0 + k, n - 1);
+            ft[k] = __shfl(f, t, 64);
+            if (t0 + k >= n) ft[k] = 0.f;
+            v[k] = *reinterpret_cast<const float2 *>(acc + t * item_stride);
+        }
+#pragma unroll
+        for (int k = 0; k < kInFlight; k++) {
+            O.x += v[k].x * ft[k];
+            O.y += v[k].y * ft[k];
+        }
     }
     float *o = a.out + r * a.o_req + j * a.o_head + 2 * lane;
     o[0] = O.x / L;
