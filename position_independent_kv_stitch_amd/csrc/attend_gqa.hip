@@ -69,7 +69,7 @@ constexpr int kStages = PIC_GQA_STAGES;    // LDS stages per wave (steps in flig
 // waves whose rings (and ~3 KB of tables) fit a CU's 160 KB of LDS
 constexpr int kWavesPerCu = 160 * 1024 / (kStages * kSlabs * 1024 + 3 * 1024);
 constexpr int kMaxHalf = kDim / 2;         // rotary planes at most
-constexpr int kMaxItems = 64;              // items per request (the merge keeps them in lanes)
+constexpr int kMaxItems = 128;             // items per request (the merge keeps 64 per lane round)
 constexpr float kLazy = 12.f;              // running-max slack of the online softmax (log2 units)
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -559,43 +559,58 @@ __global__ void __launch_bounds__(64) gqa_tile_kernel(const GqaArgs a, int32_t l
 }
 
 // out[request][q head] = merge of the request's items (flash-decoding
-// rescaling, log2 units): one wave per (request, query head), lane t holds
-// item t's max and sum, every lane merges two dims.
+// rescaling, log2 units): one wave per (request, query head).  Lane l holds
+// the max and sum of items l, l + 64, ... (kMaxItems / 64 rounds); then
+// every lane merges two dims of the items' rows, reading them eight at a
+// time with all eight loads in flight before the first is used (the wave
+// alone sums its request, so the loop is latency-bound otherwise).  A slot
+// past the last item repeats it with weight 0, which adds exactly zero.
 __global__ void __launch_bounds__(64) gqa_combine_kernel(const GqaArgs a) {
+    constexpr int kRounds = kMaxItems / 64;
+    constexpr int kInFlight = 8;
+    static_assert(kMaxItems % 64 == 0 && 64 % kInFlight == 0, "item rounds of a wave");
     const int r = blockIdx.x, j = blockIdx.y, lane = threadIdx.x;
     const int i0 = a.req_item0[r], n = a.req_item0[r + 1] - i0;
     const int64_t hq = a.num_q_heads;
-    const bool mine = lane < n;
-    const int64_t slot = (static_cast<int64_t>(i0) + (mine ? lane : 0)) * hq + j;
-    const float m = mine ? a.part_ml[2 * slot] : -INFINITY;
-    const float lsum = mine ? a.part_ml[2 * slot + 1] : 0.f;
-    float M = m;
+    float m[kRounds], lsum[kRounds], f[kRounds];
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kRounds; q++) {
+        const int t = 64 * q + lane;
+        const bool mine = t < n;
+        const int64_t slot = (static_cast<int64_t>(i0) + (mine ? t : 0)) * hq + j;
+        m[q] = mine ? a.part_ml[2 * slot] : -INFINITY;
+        lsum[q] = mine ? a.part_ml[2 * slot + 1] : 0.f;
+        M = fmaxf(M, m[q]);
+    }
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float f = mine ? __builtin_amdgcn_exp2f(m - M) : 0.f;
-    float L = lsum * f;
+    float L = 0.f;
+#pragma unroll
+    for (int q = 0; q < kRounds; q++) {
+        f[q] = 64 * q + lane < n ? __builtin_amdgcn_exp2f(m[q] - M) : 0.f;
+        L += lsum[q] * f[q];
+    }
     for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-    // the items' rows read eight at a time, all eight loads in flight before
-    // the first is used (a request's items are summed by one wave, so the
-    // loop is latency-bound otherwise); a slot past the last item repeats it
-    // with weight 0, which adds exactly zero
-    constexpr int kInFlight = 8;
     const float *acc = a.part_acc + (static_cast<int64_t>(i0) * hq + j) * kDim + 2 * lane;
     const int64_t item_stride = hq * kDim;
     float2 O = make_float2(0.f, 0.f);
-    for (int t0 = 0; t0 < n; t0 += kInFlight) {
-        float2 v[kInFlight];
-        float ft[kInFlight];
 #pragma unroll
-        for (int k = 0; k < kInFlight; k++) {
-            const int t = min(t0 + k, n - 1);
-            ft[k] = __shfl(f, t, 64);
-            if (t0 + k >= n) ft[k] = 0.f;
-            v[k] = *reinterpret_cast<const float2 *>(acc + t * item_stride);
-        }
+    for (int q = 0; q < kRounds; q++) {
+        for (int t0 = 64 * q; t0 < min(n, 64 * q + 64); t0 += kInFlight) {
+            float2 v[kInFlight];
+            float ft[kInFlight];
 #pragma unroll
-        for (int k = 0; k < kInFlight; k++) {
-            O.x += v[k].x * ft[k];
-            O.y += v[k].y * ft[k];
+            for (int k = 0; k < kInFlight; k++) {
+                const int t = min(t0 + k, n - 1);
+                ft[k] = __shfl(f[q], (t0 + k) & 63, 64);
+                if (t0 + k >= n) ft[k] = 0.f;
+                v[k] = *reinterpret_cast<const float2 *>(acc + t * item_stride);
+            }
+#pragma unroll
+            for (int k = 0; k < kInFlight; k++) {
+                O.x += v[k].x * ft[k];
+                O.y += v[k].y * ft[k];
+            }
         }
     }
     float *o = a.out + r * a.o_req + j * a.o_head + 2 * lane;
@@ -631,9 +646,12 @@ pic_status attend_gqa(struct ::pic_plan *plan, const pic_kv_view *pool, const pi
     const int H = p.shape.num_heads;
     const int64_t slots = static_cast<int64_t>(cu_count()) * kWavesPerCu;
     const int64_t target = std::max<int64_t>(1, 2 * slots / H);  // about two rounds
+    // a request alone in the batch gets at most one round of items: two
+    // rounds of short items cost more in set-up than they gain
+    const int64_t per_request = std::min<int64_t>(kMaxItems, std::max<int64_t>(1, slots / H));
     const DevBlob *blob = nullptr;
     pic_status st = plan_blob(plan, blob_key(kBlobGqa, target), stream, [&](DevBlob &b) {
-        ItemMap m = build_item_map(p, target, kMaxItems);
+        ItemMap m = build_item_map(p, target, per_request);
         b.host = std::move(m.bytes);
         b.off[0] = m.off_blocks;
         b.off[1] = m.off_items;
